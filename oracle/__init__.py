@@ -1,0 +1,245 @@
+"""CPU oracle of the NVFP4 hot path -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline`` leg
+may import this package. It wraps the plain C reference ``nvfp4_oracle.c``
+(brute-force rounding, FP64 accumulation) with numpy arrays and composes its
+primitives into the three operations of the library:
+
+* ``quantize`` / ``quantize_aug``  -- NVFP4 quantization, optionally with RMSNorm,
+  channel gather and appended residue columns (ARCQuant article on zizhi168.cn,
+  sections 3.1-3.2; ResServe abstract);
+* ``gemm``                         -- y = S_a S_w deq(A) deq(W)^T in FP64;
+* ``gemm_residue``                 -- the same product over X_aug and
+  W_aug = [W' | W'[:, :S]] (ARCQuant article, section 3.1 formula and 3.2
+  "unified GEMM" over K+S).
+
+It shares no code with the HIP library. All inputs are host numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        L = C.CDLL(path)
+        f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+        f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+        u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+        i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+        i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+        i64 = C.c_int64
+        vp = C.c_void_p
+        L.or_e2m1_value.argtypes = [C.c_int]; L.or_e2m1_value.restype = C.c_double
+        L.or_e4m3_value.argtypes = [C.c_int]; L.or_e4m3_value.restype = C.c_double
+        L.or_e2m1_encode.argtypes = [C.c_float]; L.or_e2m1_encode.restype = C.c_int
+        L.or_e4m3_encode.argtypes = [C.c_float]; L.or_e4m3_encode.restype = C.c_int
+        L.or_tensor_scale.argtypes = [f32p, i64, i64, i64]; L.or_tensor_scale.restype = C.c_float
+        L.or_quantize.argtypes = [f32p, i64, i64, i64, vp, u8p, i64, u8p, i64, vp]
+        L.or_quantize.restype = i64
+        L.or_dequantize.argtypes = [u8p, i64, u8p, i64, C.c_float, i64, i64, f64p, i64]
+        L.or_dequantize_f32.argtypes = [u8p, i64, u8p, i64, C.c_float, i64, i64, f32p, i64]
+        L.or_rmsnorm.argtypes = [f32p, i64, i64, i64, f32p, C.c_float, f32p, i64]
+        L.or_channel_absmax.argtypes = [f32p, i64, i64, i64, vp, C.c_float, f32p]
+        L.or_perm_from_absmax.argtypes = [f32p, i64, i32p]
+        L.or_quantize_aug.argtypes = [f32p, i64, i64, i64, vp, C.c_float, vp, i64, vp,
+                                      u8p, i64, u8p, i64, vp]
+        L.or_quantize_aug.restype = i64
+        L.or_gemm.argtypes = [u8p, i64, u8p, i64, C.c_float, u8p, i64, u8p, i64, C.c_float,
+                              i64, i64, i64, f64p, i64]
+        L.or_gemm_pairs.argtypes = [u8p, i64, u8p, i64, C.c_float, u8p, i64, u8p, i64, C.c_float,
+                                    i64, i64p, i64p, i64, f64p]
+        L.or_gemm_exact.argtypes = [u8p, i64, u8p, i64, C.c_float, u8p, i64, u8p, i64, C.c_float,
+                                    i64, i64, i64, f64p, i64]
+        L.or_gemm_exact.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _f32(x) -> np.ndarray:
+    """Accept numpy arrays or torch tensors (any float dtype; bf16 is exact in fp32)."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").float().numpy()
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+class QTensor:
+    """An NVFP4 tensor in the canonical layout: codes [rows][K/2], scales [rows][K/16], S."""
+
+    def __init__(self, codes: np.ndarray, scales: np.ndarray, S: float, K: int):
+        self.codes, self.scales, self.S, self.K = codes, scales, np.float32(S), K
+        self.near_midpoint = 0
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+
+def e2m1_value(code: int) -> float:
+    return lib().or_e2m1_value(code)
+
+
+def e4m3_value(byte: int) -> float:
+    return lib().or_e4m3_value(byte)
+
+
+def e2m1_encode(q: float) -> int:
+    return lib().or_e2m1_encode(float(np.float32(q)))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().or_e4m3_encode(float(np.float32(v)))
+
+
+def tensor_scale(x) -> np.float32:
+    x = _f32(x)
+    rows, K = x.shape
+    return np.float32(lib().or_tensor_scale(x, rows, K, K))
+
+
+def _alloc(rows: int, K: int):
+    return np.zeros((rows, K // 2), np.uint8), np.zeros((rows, K // 16), np.uint8)
+
+
+def quantize(x, static_S=None) -> QTensor:
+    x = _f32(x)
+    rows, K = x.shape
+    assert K % 16 == 0
+    codes, scales = _alloc(rows, K)
+    S = np.zeros(1, np.float32)
+    sp = np.array([static_S], np.float32) if static_S is not None else None
+    near = lib().or_quantize(x, rows, K, K, sp.ctypes.data if sp is not None else None,
+                             codes, K // 2, scales, K // 16, S.ctypes.data)
+    q = QTensor(codes, scales, S[0], K)
+    q.near_midpoint = int(near)
+    return q
+
+
+def quantize_aug(x, gamma=None, eps: float = 1e-6, perm=None, S_cols: int = 0,
+                 static_S=None) -> QTensor:
+    x = _f32(x)
+    rows, K = x.shape
+    Ka = K + S_cols
+    assert K % 16 == 0 and S_cols % 16 == 0 and 0 <= S_cols <= K
+    codes, scales = _alloc(rows, Ka)
+    S = np.zeros(1, np.float32)
+    g = _f32(gamma) if gamma is not None else None
+    p = np.ascontiguousarray(perm, dtype=np.int32) if perm is not None else None
+    sp = np.array([static_S], np.float32) if static_S is not None else None
+    near = lib().or_quantize_aug(x, rows, K, K, g.ctypes.data if g is not None else None,
+                                 np.float32(eps), p.ctypes.data if p is not None else None,
+                                 S_cols, sp.ctypes.data if sp is not None else None,
+                                 codes, Ka // 2, scales, Ka // 16, S.ctypes.data)
+    q = QTensor(codes, scales, S[0], Ka)
+    q.near_midpoint = int(near)
+    return q
+
+
+def dequantize(q: QTensor) -> np.ndarray:
+    out = np.zeros((q.rows, q.K), np.float64)
+    lib().or_dequantize(q.codes, q.codes.shape[1], q.scales, q.scales.shape[1], q.S,
+                        q.rows, q.K, out, q.K)
+    return out
+
+
+def dequantize_f32(q: QTensor) -> np.ndarray:
+    out = np.zeros((q.rows, q.K), np.float32)
+    lib().or_dequantize_f32(q.codes, q.codes.shape[1], q.scales, q.scales.shape[1], q.S,
+                            q.rows, q.K, out, q.K)
+    return out
+
+
+def rmsnorm(x, gamma, eps: float = 1e-6) -> np.ndarray:
+    x = _f32(x)
+    g = _f32(gamma)
+    rows, K = x.shape
+    y = np.zeros((rows, K), np.float32)
+    lib().or_rmsnorm(x, rows, K, K, g, np.float32(eps), y, K)
+    return y
+
+
+def channel_absmax(x, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    x = _f32(x)
+    rows, K = x.shape
+    g = _f32(gamma) if gamma is not None else None
+    v = np.zeros(K, np.float32)
+    lib().or_channel_absmax(x, rows, K, K, g.ctypes.data if g is not None else None,
+                            np.float32(eps), v)
+    return v
+
+
+def perm_from_absmax(v) -> np.ndarray:
+    v = _f32(v)
+    perm = np.zeros(v.shape[0], np.int32)
+    lib().or_perm_from_absmax(v, v.shape[0], perm)
+    return perm
+
+
+def calibrate_perm(x_cal, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    """Channel order for the outlier reorder: descending calibration absmax."""
+    return perm_from_absmax(channel_absmax(x_cal, gamma, eps))
+
+
+def gemm(a: QTensor, w: QTensor) -> np.ndarray:
+    assert a.K == w.K
+    M, N, K = a.rows, w.rows, a.K
+    y = np.zeros((M, N), np.float64)
+    lib().or_gemm(a.codes, a.codes.shape[1], a.scales, a.scales.shape[1], a.S,
+                  w.codes, w.codes.shape[1], w.scales, w.scales.shape[1], w.S, M, N, K, y, N)
+    return y
+
+
+def gemm_pairs(a: QTensor, w: QTensor, ms, ns) -> np.ndarray:
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    y = np.zeros(ms.shape[0], np.float64)
+    lib().or_gemm_pairs(a.codes, a.codes.shape[1], a.scales, a.scales.shape[1], a.S,
+                        w.codes, w.codes.shape[1], w.scales, w.scales.shape[1], w.S,
+                        a.K, ms, ns, ms.shape[0], y)
+    return y
+
+
+def gemm_exact(a: QTensor, w: QTensor) -> np.ndarray:
+    M, N, K = a.rows, w.rows, a.K
+    y = np.zeros((M, N), np.float64)
+    rc = lib().or_gemm_exact(a.codes, a.codes.shape[1], a.scales, a.scales.shape[1], a.S,
+                             w.codes, w.codes.shape[1], w.scales, w.scales.shape[1], w.S,
+                             M, N, K, y, N)
+    if rc != 0:
+        raise OverflowError("exact accumulation out of range")
+    return y
+
+
+def weight_aug(w_perm, S_cols: int) -> QTensor:
+    """W_aug = [W' | W'[:, :S]] quantized as one tensor (W' already in channel order)."""
+    w = _f32(w_perm)
+    if S_cols:
+        w = np.ascontiguousarray(np.concatenate([w, w[:, :S_cols]], axis=1))
+    return quantize(w)
+
+
+def gemm_residue(x, w_perm, S_cols: int, gamma=None, eps: float = 1e-6, perm=None):
+    """Y = s_aug [Q(X') | Q(R)] [Q(W') | Q(W'_o)]^T; returns (y, X_aug, W_aug)."""
+    xa = quantize_aug(x, gamma, eps, perm, S_cols)
+    wa = weight_aug(w_perm, S_cols)
+    return gemm(xa, wa), xa, wa
+
+
+def gemm_error(y, y_ref) -> float:
+    """Max |y - y*| / max(|y*|, 1e-3 max|y*|): relative error floored near zero."""
+    y = np.asarray(y, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    if y_ref.size == 0:
+        return 0.0
+    floor = 1e-3 * np.max(np.abs(y_ref))
+    den = np.maximum(np.abs(y_ref), floor if floor > 0 else 1e-30)
+    return float(np.max(np.abs(y - y_ref) / den))

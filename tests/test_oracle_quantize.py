@@ -1,0 +1,266 @@
+"""Pins of the oracle's quantizer, residue and fused-quantizer steps.
+
+Each test checks the oracle against something other than itself:
+* exact reconstruction of inputs built on the NVFP4 grid (any error in the
+  tensor-scale constant, block-scale rounding, nibble order or sign handling
+  breaks it);
+* the per-element error bound |e1| <= alpha1 * M * eps4 and the two-stage
+  residue bound |e2| <= alpha1 alpha2 M eps4^2 (ARCQuant article, section 4.1),
+  with sup alpha = 1.125 (section 4.2), plus the tighter half-step bound;
+* the augmented-tensor identities of the ARCQuant article, section 3.1
+  (one scale s_aug for [Q(X) | Q(R)]);
+* RMSNorm against a closed form and against numpy float64;
+* the calibration order against numpy's stable argsort.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from block_scaled_fp4_02_amd import inputs
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "nvfp4_format.json")))
+BOOK = np.array(GOLD["e2m1_codebook"]["value"])
+EPS4 = GOLD["eps4"]["value"]
+SUP_ALPHA = GOLD["sup_alpha"]["value"]
+
+
+def unpack_codes(codes: np.ndarray) -> np.ndarray:
+    lo = codes & 15
+    hi = codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+def code_values(c: np.ndarray) -> np.ndarray:
+    v = BOOK[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def e4m3_table(orc):
+    return np.array([orc.e4m3_value(b) for b in range(256)])
+
+
+def grid_input(seed: int, rows: int, K: int, S_exp: int, orc):
+    """x = e(c) * d * S exactly, S = 2^S_exp, each block holding a +-6 code, one block d = 448."""
+    rng = np.random.default_rng(seed)
+    tab = e4m3_table(orc)
+    nb = K // 16
+    dbytes = rng.integers(1, 127, size=(rows, nb))
+    dbytes[0, 0] = 0x7E
+    codes = rng.integers(0, 16, size=(rows, K))
+    codes[:, ::16] = np.where(rng.random((rows, nb)) < 0.5, 7, 15)   # +-6 in every block
+    d = tab[dbytes]
+    x = code_values(codes) * np.repeat(d, 16, axis=1) * 2.0 ** S_exp
+    return x.astype(np.float32), codes, dbytes
+
+
+@pytest.mark.parametrize("S_exp", [-12, -3, 0, 5])
+def test_grid_inputs_reconstruct_exactly(orc, S_exp):
+    x, codes, dbytes = grid_input(40 + S_exp, 6, 256, S_exp, orc)
+    # the value must be exactly representable in FP32 (<= 6 significant bits)
+    assert np.array_equal(x.astype(np.float64), x.astype(np.float64))
+    q = orc.quantize(x)
+    assert q.S == np.float32(2.0 ** S_exp)
+    assert np.array_equal(q.scales, dbytes.astype(np.uint8))
+    got = unpack_codes(q.codes)
+    # a zero value can carry either sign bit; the sign is the input's sign bit
+    want = np.where((codes & 7) == 0, np.where(np.signbit(x), 8, 0), codes)
+    assert np.array_equal(got, want)
+    assert np.array_equal(orc.dequantize(q), x.astype(np.float64))
+
+
+def test_nibble_order_and_layout(orc):
+    # one block: values 0.5*S at k=0 and 6*S at k=1; low nibble holds the even k
+    x = np.zeros((1, 16), np.float32)
+    x[0, 0], x[0, 1] = 0.5, 6.0
+    q = orc.quantize(x)
+    assert q.S == np.float32(6.0 / 2688.0)
+    assert q.scales[0, 0] == 0x7E
+    assert q.codes[0, 0] == (1 | (7 << 4))
+
+
+def test_zero_tensor_and_negative_zero(orc):
+    x = np.zeros((2, 32), np.float32)
+    x[1, 3] = -0.0
+    q = orc.quantize(x)
+    assert q.S == 1.0
+    assert not q.scales.any()
+    c = unpack_codes(q.codes)
+    assert c[1, 3] == 8 and c.sum() == 8
+    assert not orc.dequantize(q).any()
+
+
+def test_zero_scale_block(orc):
+    # a block far below the tensor max gets d = 0 and codes of magnitude 0
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 1000.0
+    x[0, 16:] = 1e-6 * np.arange(1, 17)
+    q = orc.quantize(x)
+    assert q.scales[0, 1] == 0
+    assert (unpack_codes(q.codes)[0, 16:] & 7).sum() == 0
+
+
+def _block_stats(x, q, orc):
+    """alpha = s*6/a_b, |x - deq|, s, q-values per element."""
+    tab = e4m3_table(orc)
+    rows, K = x.shape
+    d = tab[q.scales].repeat(16, axis=1)
+    s = (d * float(q.S))
+    ab = np.abs(x).reshape(rows, K // 16, 16).max(axis=2).repeat(16, axis=1)
+    deq = orc.dequantize(q)
+    return d, s, ab, deq
+
+
+@pytest.mark.parametrize("case", ["gemv", "residue", "prefill_like"])
+def test_error_bounds_on_workloads(orc, case):
+    if case == "gemv":
+        x, _ = inputs.gemv_4096()
+    elif case == "residue":
+        x, _ = inputs.residue_8192(16)
+    else:
+        x = inputs.activations(5, 0, 64, 8192, 0.01, 50.0)
+    x = x.float().numpy()
+    q = orc.quantize(x)
+    d, s, ab, deq = _block_stats(x, q, orc)
+    err = np.abs(x - deq)
+    normal = d >= 2.0 ** -6
+    alpha = np.where(ab > 0, s * 6 / np.where(ab > 0, ab, 1), 1.0)
+    # page bound (section 4.1) with sup alpha (section 4.2)
+    assert np.all(alpha[normal] <= SUP_ALPHA)
+    assert np.all(err <= alpha * ab * EPS4 + 1e-30)
+    # tighter: RNE scale error is at most half a step of 2^-3
+    assert np.all(alpha[normal] >= 1 / (1 + 2.0 ** -4) - 1e-6)
+    assert np.all(alpha[normal] <= (1 + 2.0 ** -3) / (1 + 2.0 ** -4) + 1e-6)
+    # half-step bound: gap/2 of the E2M1 grid at |q|, or the clip beyond 6
+    qv = np.abs(x) / np.where(s > 0, s, 1)
+    half = np.where(qv <= 2, 0.25, np.where(qv <= 4, 0.5, 1.0))
+    clip = np.maximum(qv - 6.0, 0)
+    bound = s * np.maximum(half, clip) * (1 + 2.0 ** -20)
+    assert np.all(err[s > 0] <= bound[s > 0])
+
+
+def test_two_stage_residue_bound(orc):
+    x, _ = inputs.residue_8192(16)
+    x = x.float().numpy()
+    K = x.shape[1]
+    xa = orc.quantize_aug(x, S_cols=K)
+    q = orc.quantize(x)
+    assert xa.S == q.S                           # one scale s_aug (section 3.1)
+    assert np.array_equal(xa.codes[:, :K // 2], q.codes)
+    assert np.array_equal(xa.scales[:, :K // 16], q.scales)
+    deq = orc.dequantize(xa)
+    total = deq[:, :K] + deq[:, K:]
+    err2 = np.abs(x.astype(np.float64) - total)
+    tab = e4m3_table(orc)
+    d = tab[q.scales]
+    ab = np.abs(x).reshape(x.shape[0], -1, 16).max(axis=2)
+    s = d * float(q.S)
+    alpha1 = s * 6 / ab
+    # residue blocks
+    dr = tab[xa.scales[:, K // 16:]]
+    r = orc.dequantize_f32(q)
+    R = x - r
+    abr = np.abs(R).reshape(x.shape[0], -1, 16).max(axis=2)
+    sr = dr * float(q.S)
+    ok = (d >= 2.0 ** -6) & (dr >= 2.0 ** -6)
+    alpha2 = np.where(abr > 0, sr * 6 / np.where(abr > 0, abr, 1), 0)
+    e2 = err2.reshape(x.shape[0], -1, 16).max(axis=2)
+    # page: |e2| <= alpha1 alpha2 M eps4^2 with M the block max, and sup(alpha1 alpha2) < 2
+    assert np.all(e2[ok] <= (alpha1 * alpha2 * ab * EPS4 ** 2)[ok] + ab[ok] * 2.0 ** -20)
+    assert np.all(e2[ok] <= GOLD["sup_alpha_product"]["value"] * ab[ok] * GOLD["eps4_squared_equals_eps8"]["value"])
+    # the residue lowers the error of every block
+    e1 = np.abs(x.astype(np.float64) - orc.dequantize(q)).reshape(x.shape[0], -1, 16).max(axis=2)
+    assert np.all(e2 <= e1)
+
+
+def test_residue_is_x_minus_fp32_dequant(orc):
+    x = inputs.small_random(5, 4, 64).float().numpy()
+    xa = orc.quantize_aug(x, S_cols=32)
+    q = orc.quantize(x)
+    R = (x[:, :32] - orc.dequantize_f32(q)[:, :32]).astype(np.float32)
+    qr = orc.quantize(R, static_S=float(q.S))
+    assert np.array_equal(xa.codes[:, 32:], qr.codes)
+    assert np.array_equal(xa.scales[:, 4:], qr.scales)
+
+
+def test_static_scale(orc):
+    x = inputs.small_random(6, 3, 64).float().numpy()
+    q = orc.quantize(x)
+    q2 = orc.quantize(x, static_S=float(q.S))
+    assert np.array_equal(q.codes, q2.codes) and np.array_equal(q.scales, q2.scales)
+    # a static scale 100x too small saturates block scales at 448 and codes at 6
+    q3 = orc.quantize(x, static_S=float(q.S) / 100)
+    assert q3.scales.max() == 0x7E
+    big = np.abs(x) > 6 * 448 * float(q3.S)
+    assert np.all((unpack_codes(q3.codes)[big] & 7) == 7)
+
+
+def test_idempotence(orc):
+    x, _ = inputs.gemv_4096()
+    q = orc.quantize(x.float().numpy())
+    deq = orc.dequantize(q).astype(np.float32)
+    q2 = orc.quantize(deq)
+    if q2.S == q.S:
+        assert np.array_equal(q2.codes, q.codes) and np.array_equal(q2.scales, q.scales)
+    else:
+        assert abs(float(q2.S) - float(q.S)) <= np.spacing(np.float32(q.S))
+
+
+def test_rmsnorm_closed_form(orc):
+    c = np.float32(0.75)
+    x = np.full((1, 64), c, np.float32)
+    y = orc.rmsnorm(x, np.ones(64, np.float32), 1e-6)
+    want = np.float32(c * np.float32(1 / np.sqrt(np.float64(c) ** 2 + np.float64(np.float32(1e-6)))))
+    assert np.all(y == want)
+
+
+def test_rmsnorm_vs_numpy(orc):
+    x, g, _, _ = inputs.outlier_aug(rows=8, N=16, cal_rows=4)
+    x = x.float().numpy()
+    g = g.float().numpy()
+    y = orc.rmsnorm(x, g, 1e-6)
+    xd = x.astype(np.float64)
+    r = 1 / np.sqrt((xd * xd).mean(axis=1, keepdims=True) + np.float64(np.float32(1e-6)))
+    ref = xd * r * g
+    assert np.allclose(y, ref, rtol=2.0 ** -22, atol=0)
+
+
+def test_perm_order(orc):
+    v = np.array([1.0, 5.0, 5.0, 0.5, 7.0, 1.0], np.float32)
+    assert list(orc.perm_from_absmax(v)) == [4, 1, 2, 0, 5, 3]
+    rng = np.random.default_rng(1)
+    v = rng.integers(0, 20, 300).astype(np.float32)
+    want = np.argsort(-v, kind="stable")
+    assert np.array_equal(orc.perm_from_absmax(v), want)
+
+
+def test_channel_absmax(orc):
+    x, g, xcal, _ = inputs.outlier_aug(rows=4, N=16, cal_rows=32)
+    xc = xcal.float().numpy()
+    v = orc.channel_absmax(xc, g, 1e-6)
+    y = orc.rmsnorm(xc, g, 1e-6)
+    assert np.array_equal(v, np.abs(y).max(axis=0))
+    perm = orc.calibrate_perm(xc, g)
+    cols = inputs.outlier_columns(4, 0, 4096, 0.01)
+    # the synthetic outlier channels rank first
+    assert set(perm[:len(cols)].tolist()) == set(cols.tolist())
+
+
+def test_fused_quantizer_composition(orc):
+    x, g, xcal, _ = inputs.outlier_aug(rows=8, N=16, cal_rows=16)
+    perm = orc.calibrate_perm(xcal, g)
+    S_cols = 128
+    xa = orc.quantize_aug(x, gamma=g, perm=perm, S_cols=S_cols)
+    y = orc.rmsnorm(x.float().numpy(), g, 1e-6)[:, perm]
+    q = orc.quantize(y)
+    K = 4096
+    assert xa.S == q.S
+    assert np.array_equal(xa.codes[:, :K // 2], q.codes)
+    R = y[:, :S_cols] - orc.dequantize_f32(q)[:, :S_cols]
+    qr = orc.quantize(R.astype(np.float32), static_S=float(q.S))
+    assert np.array_equal(xa.codes[:, K // 2:], qr.codes)
+    assert np.array_equal(xa.scales[:, K // 16:], qr.scales)
+    # identity permutation reduces to the plain quantizer
+    xi = orc.quantize_aug(x, perm=np.arange(K, dtype=np.int32))
+    assert np.array_equal(xi.codes, orc.quantize(x).codes)
