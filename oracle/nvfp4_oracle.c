@@ -60,6 +60,10 @@ int or_e2m1_encode(float q)
 {
     double a = fabs((double)q), best_d = INFINITY;
     int best = 0;
+    /* Saturation: at or above the largest magnitude the nearest value is that
+     * magnitude. Checked first because far above it the double distances below
+     * would all round to the same number and tie. */
+    if (a >= or_e2m1_value(7)) return 7 | (signbit(q) ? 8 : 0);
     for (int c = 0; c < 8; ++c) {
         double d = fabs(a - or_e2m1_value(c));
         if (d < best_d || (d == best_d && (c & 1) == 0)) { best_d = d; best = c; }
@@ -71,6 +75,7 @@ int or_e4m3_encode(float v)
 {
     double a = (double)v, best_d = INFINITY;
     int best = 0;
+    if (a >= or_e4m3_value(126)) return 126;           /* saturation, as above */
     for (int c = 0; c < 127; ++c) {                    /* all finite non-negative */
         double d = fabs(a - or_e4m3_value(c));
         if (d < best_d || (d == best_d && (c & 1) == 0)) { best_d = d; best = c; }

@@ -60,8 +60,15 @@ def test_e4m3_encode_matches_torch(orc):
 
 
 def test_e4m3_encode_saturates(orc):
-    for v in [448.0, 449.0, 463.9, 464.0, 480.0, 1e6, 3e38]:
+    for v in [448.0, 449.0, 463.9, 464.0, 480.0, 1e6, 1e20, 3e38]:
         assert orc.e4m3_encode(v) == 0x7E
+
+
+def test_e2m1_encode_saturates_far_above(orc):
+    # far above 6 every double distance rounds alike; the result must still be 6
+    for q in [6.0, 7.0, 1e9, 1e20, 1e30, 3e38]:
+        assert orc.e2m1_encode(q) == 7
+        assert orc.e2m1_encode(-q) == 15
 
 
 def _rint_e2m1(q: np.ndarray) -> np.ndarray:
