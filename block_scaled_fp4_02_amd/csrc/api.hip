@@ -1,0 +1,290 @@
+// api.hip -- extern "C" entry points of libnvfp4 (declared in include/nvfp4.h).
+//
+// Every argument is validated before anything is enqueued; on error the call
+// returns a status and no output is touched. The library allocates nothing:
+// scratch space comes from the caller's workspace, carved up here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/nvfp4.h"
+#include "internal.h"
+#include "nvfp4_device.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+nvfp4_status hip_fail(hipError_t e) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return NVFP4_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The skinny (decode) path takes M up to this many rows; larger M is tiled.
+constexpr int64_t kSkinnyMaxM = 32;
+
+int64_t ldc_for(int64_t K) { return (int64_t)up((size_t)(K / 2), 16); }
+int64_t lds_for(int64_t K) { return (int64_t)up((size_t)(K / 16), 8); }
+
+size_t quant_ws(int64_t rows) {
+    return up(kAmaxPartials * sizeof(float), kAlign) + up((size_t)std::max<int64_t>(rows, 1) * sizeof(float), kAlign);
+}
+
+size_t tensor_ws(int64_t rows, int64_t K) {
+    return up((size_t)(rows * ldc_for(K)), kAlign) + up((size_t)(rows * lds_for(K)), kAlign) + kAlign;
+}
+
+size_t gemm_ws(int64_t M, int64_t N, int64_t K, int64_t S) {
+    size_t part = 0;
+    if (M <= kSkinnyMaxM) part = up(skinny_workspace_bytes(M, N, K, S), kAlign);
+    return part;
+}
+
+struct Carver {
+    uint8_t *p; size_t left; bool ok = true;
+    uint8_t *take(size_t n) {
+        n = up(n, kAlign);
+        if (n > left) { ok = false; return nullptr; }
+        uint8_t *r = p; p += n; left -= n; return r;
+    }
+};
+
+int elem_size(int xt) { return xt == NVFP4_BF16 ? 2 : 4; }
+
+nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t K) {
+    if (!t || !t->codes || !t->scales || !t->tensor_scale) return NVFP4_ERR_NULL;
+    if (t->rows != rows || t->K != K) return NVFP4_ERR_SHAPE;
+    if (t->ld_codes < K / 2 || t->ld_scales < K / 16) return NVFP4_ERR_SHAPE;
+    if (t->ld_codes % 16 || t->ld_scales % 8 || !aligned(t->codes, 16) || !aligned(t->scales, 8) ||
+        !aligned(t->tensor_scale, 4))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+nvfp4_status check_x(const void *x, int xt, int64_t rows, int64_t K, int64_t ldx) {
+    if (!x) return NVFP4_ERR_NULL;
+    if (xt != NVFP4_BF16 && xt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
+    if (rows < 0 || K < 0 || K % 16 || ldx < K) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || (ldx * elem_size(xt)) % 16) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+nvfp4_status check_opts(const nvfp4_quant_opts *o, int64_t K_in) {
+    if (!o) return NVFP4_OK;
+    if (o->residue_cols < 0 || o->residue_cols > K_in || o->residue_cols % 16) return NVFP4_ERR_SHAPE;
+    if (o->gamma && !aligned(o->gamma, 16)) return NVFP4_ERR_ALIGN;
+    if (o->perm && K_in > 16384) return NVFP4_ERR_UNSUPPORTED;
+    if (o->perm && !aligned(o->perm, 4)) return NVFP4_ERR_ALIGN;
+    if (o->gamma && !(o->eps >= 0.0f)) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+#define CHECK(expr) do { nvfp4_status s_ = (expr); if (s_ != NVFP4_OK) return s_; } while (0)
+
+// Enqueue the quantizer writing into `out` (validated by the caller).
+nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in, int64_t ldx,
+                              const nvfp4_quant_opts *opts, const nvfp4_tensor &out,
+                              float *partials, float *rscale, hipStream_t st) {
+    QuantLaunch q;
+    q.x = x; q.xt = xt; q.rows = rows; q.K_in = K_in; q.ldx = ldx;
+    q.gamma = opts ? static_cast<const uint16_t *>(opts->gamma) : nullptr;
+    q.eps = opts ? opts->eps : 0.0f;
+    q.perm = opts ? opts->perm : nullptr;
+    q.res_cols = opts ? opts->residue_cols : 0;
+    q.static_S = opts ? opts->static_tensor_scale : nullptr;
+    q.codes = out.codes; q.ldc = out.ld_codes; q.scales = out.scales; q.lds = out.ld_scales;
+    q.S_out = out.tensor_scale;
+    q.partials = partials; q.rscale = rscale;
+    hipError_t e = launch_quantize(q, st);
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status enqueue_gemm(const nvfp4_tensor &a, const nvfp4_tensor &w, int64_t M, int64_t K, int64_t S,
+                          void *y, int yt, int64_t ldy, uint8_t *part, size_t part_bytes, hipStream_t st) {
+    hipError_t e;
+    if (M <= kSkinnyMaxM) {
+        SkinnyLaunch g;
+        g.a_codes = a.codes; g.a_ldc = a.ld_codes; g.a_scales = a.scales; g.a_lds = a.ld_scales; g.a_S = a.tensor_scale;
+        g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
+        g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
+        g.y = y; g.yt = yt; g.ldy = ldy;
+        g.partials = reinterpret_cast<float *>(part); g.partial_bytes = part_bytes;
+        e = launch_skinny(g, st);
+    } else {
+        PrefillLaunch g;
+        g.a_codes = a.codes; g.a_ldc = a.ld_codes; g.a_scales = a.scales; g.a_lds = a.ld_scales; g.a_S = a.tensor_scale;
+        g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
+        g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
+        g.y = y; g.yt = yt; g.ldy = ldy;
+        e = launch_prefill(g, st);
+    }
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S) {
+    if (M < 0 || N < 0 || K < 0 || S < 0) return 0;
+    switch (op) {
+        case 0: return quant_ws(M);
+        case 1: return tensor_ws(M, K) + quant_ws(M) + gemm_ws(M, N, K, 0);
+        case 2: return tensor_ws(M, K + S) + quant_ws(M) + gemm_ws(M, N, K, S);
+        case 3: return up((size_t)std::max<int64_t>(M, 1) * sizeof(float), kAlign);
+        default: return 0;
+    }
+}
+
+nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, int64_t ldx,
+                            const nvfp4_quant_opts *opts, const nvfp4_tensor *out,
+                            void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_x(x, xt, rows, K_in, ldx));
+    CHECK(check_opts(opts, K_in));
+    const int64_t S = opts ? opts->residue_cols : 0;
+    CHECK(check_tensor(out, rows, K_in + S));
+    const size_t need = nvfp4_workspace_size(0, rows, 0, K_in, S);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    Carver c{static_cast<uint8_t *>(ws), ws_bytes};
+    float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
+    float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(rows, 1) * sizeof(float)));
+    if (!c.ok) return NVFP4_ERR_WORKSPACE;
+    return enqueue_quantize(x, xt, rows, K_in, ldx, opts, *out, partials, rscale,
+                            static_cast<hipStream_t>(stream));
+}
+
+nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
+                        int64_t M, int64_t K, int64_t ldx,
+                        const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
+                        void *ws, size_t ws_bytes, void *stream) {
+    if ((a_q == nullptr) == (x == nullptr)) return NVFP4_ERR_NULL;
+    if (!w || !y) return NVFP4_ERR_NULL;
+    if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
+    if (M < 0 || K < 0 || K % 16) return NVFP4_ERR_SHAPE;
+    CHECK(check_tensor(w, w->rows, K));
+    const int64_t N = w->rows;
+    if (ldy < N) return NVFP4_ERR_SHAPE;
+    if (a_q) CHECK(check_tensor(a_q, M, K));
+    else CHECK(check_x(x, xt, M, K, ldx));
+    const size_t need = a_q ? gemm_ws(M, N, K, 0) : nvfp4_workspace_size(1, M, N, K, 0);
+    if (need && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (M == 0 || N == 0) return NVFP4_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Carver c{static_cast<uint8_t *>(ws), ws_bytes};
+    nvfp4_tensor aq;
+    if (a_q) {
+        aq = *a_q;
+    } else {
+        aq.rows = M; aq.K = K; aq.ld_codes = ldc_for(K); aq.ld_scales = lds_for(K);
+        aq.codes = c.take((size_t)(M * aq.ld_codes));
+        aq.scales = c.take((size_t)(M * aq.ld_scales));
+        aq.tensor_scale = reinterpret_cast<float *>(c.take(sizeof(float)));
+        float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
+        float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(M, 1) * sizeof(float)));
+        if (!c.ok) return NVFP4_ERR_WORKSPACE;
+        CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, st));
+    }
+    const size_t pb = gemm_ws(M, N, K, 0);
+    uint8_t *part = pb ? c.take(pb) : nullptr;
+    if (!c.ok) return NVFP4_ERR_WORKSPACE;
+    return enqueue_gemm(aq, *w, M, K, 0, y, yt, ldy, part, pb, st);
+}
+
+nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int64_t ldx,
+                                const nvfp4_quant_opts *opts, const nvfp4_tensor *w,
+                                void *y, int yt, int64_t ldy, const nvfp4_tensor *a_aug_out,
+                                void *ws, size_t ws_bytes, void *stream) {
+    if (!w || !y) return NVFP4_ERR_NULL;
+    if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
+    CHECK(check_x(x, xt, M, K, ldx));
+    CHECK(check_opts(opts, K));
+    const int64_t S = opts ? opts->residue_cols : 0;
+    CHECK(check_tensor(w, w->rows, K));
+    const int64_t N = w->rows;
+    if (ldy < N) return NVFP4_ERR_SHAPE;
+    if (a_aug_out) CHECK(check_tensor(a_aug_out, M, K + S));
+    const size_t need = nvfp4_workspace_size(2, M, N, K, S);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (M == 0) return NVFP4_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Carver c{static_cast<uint8_t *>(ws), ws_bytes};
+    nvfp4_tensor aq;
+    if (a_aug_out) {
+        aq = *a_aug_out;
+        c.take(tensor_ws(M, K + S) - kAlign);
+    } else {
+        aq.rows = M; aq.K = K + S; aq.ld_codes = ldc_for(K + S); aq.ld_scales = lds_for(K + S);
+        aq.codes = c.take((size_t)(M * aq.ld_codes));
+        aq.scales = c.take((size_t)(M * aq.ld_scales));
+        aq.tensor_scale = reinterpret_cast<float *>(c.take(sizeof(float)));
+    }
+    float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
+    float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(M, 1) * sizeof(float)));
+    if (!c.ok) return NVFP4_ERR_WORKSPACE;
+    CHECK(enqueue_quantize(x, xt, M, K, ldx, opts, aq, partials, rscale, st));
+    if (N == 0) return NVFP4_OK;
+    const size_t pb = gemm_ws(M, N, K, S);
+    uint8_t *part = pb ? c.take(pb) : nullptr;
+    if (!c.ok) return NVFP4_ERR_WORKSPACE;
+    return enqueue_gemm(aq, *w, M, K, S, y, yt, ldy, part, pb, st);
+}
+
+nvfp4_status nvfp4_channel_absmax(const void *x, int xt, int64_t rows, int64_t K, int64_t ldx,
+                                  const void *gamma, float eps, float *absmax_out,
+                                  void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_x(x, xt, rows, K, ldx));
+    if (!absmax_out) return NVFP4_ERR_NULL;
+    if (gamma && !aligned(gamma, 16)) return NVFP4_ERR_ALIGN;
+    if (gamma && !(eps >= 0.0f)) return NVFP4_ERR_SHAPE;
+    if (gamma && (!ws || ws_bytes < nvfp4_workspace_size(3, rows, 0, K, 0))) return NVFP4_ERR_WORKSPACE;
+    if (K == 0) return NVFP4_OK;
+    ChannelAbsmaxLaunch cl;
+    cl.x = x; cl.xt = xt; cl.rows = rows; cl.K = K; cl.ldx = ldx;
+    cl.gamma = static_cast<const uint16_t *>(gamma); cl.eps = eps;
+    cl.rscale = static_cast<float *>(ws); cl.out = absmax_out;
+    hipError_t e = launch_channel_absmax(cl, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_perm_from_absmax(const float *absmax_host, int64_t K, int32_t *perm_host) {
+    if (K < 0) return NVFP4_ERR_SHAPE;
+    if (K > 0 && (!absmax_host || !perm_host)) return NVFP4_ERR_NULL;
+    std::vector<int32_t> idx((size_t)K);
+    for (int64_t i = 0; i < K; ++i) idx[(size_t)i] = (int32_t)i;
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int32_t a, int32_t b) { return absmax_host[a] > absmax_host[b]; });
+    std::memcpy(perm_host, idx.data(), sizeof(int32_t) * (size_t)K);
+    return NVFP4_OK;
+}
+
+const char *nvfp4_status_string(nvfp4_status s) {
+    switch (s) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_ERR_NULL: return "null pointer";
+        case NVFP4_ERR_SHAPE: return "bad shape";
+        case NVFP4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+        case NVFP4_ERR_DTYPE: return "bad dtype";
+        case NVFP4_ERR_WORKSPACE: return "workspace too small";
+        case NVFP4_ERR_UNSUPPORTED: return "unsupported";
+        case NVFP4_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *nvfp4_last_error(void) { return g_last_error; }
+int nvfp4_version(void) { return 10000; }
+
+int nvfp4_host_e4m3_encode(float v) { return (int)e4m3_rne_sat(v); }
+int nvfp4_host_e2m1_encode(float q) { return (int)(e2m1_rne_sat(std::fabs(q)) | ((f2u(q) >> 31) << 3)); }
+
+}  // extern "C"

@@ -1,0 +1,244 @@
+// gemm_tiled.hip -- tiled W4A4 product for large M (prefill) on gfx950 matrix cores.
+//
+// Only here is the product a dense contraction, so only here is it tiled for
+// MFMA. NVFP4's 16-element E4M3 block scales do not map onto CDNA4's scaled
+// FP4 MFMA (E8M0 scales per 32 elements), and e(c)*d needs up to 6 significant
+// bits, so each 16-element block is decoded to exact f16 e*d values in LDS and
+// multiplied with v_mfma_f32_16x16x32_f16 (FP32 accumulation). The epilogue
+// applies S_a S_w once and stores FP32 or BF16 (one write, no second pass).
+//
+// Residue columns (ARCQuant article, sections 3.1-3.2: one GEMM over K+S whose
+// weight tail repeats the weight's first S columns) are handled by decoding the
+// residue activation tile of the same K step and issuing a second set of MFMAs
+// against the already-decoded weight tile, so the weights are read once.
+//
+// Tile: BM x BN output per workgroup of 4 waves (2 x 2), BK = 64 per step,
+// LDS double-buffered; tiles are stored in MFMA operand order (each operand
+// fetch is 1 KB contiguous per wave).
+#include "internal.h"
+#include "nvfp4_device.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int BK = 64;
+
+struct TArgs {
+    const uint8_t *a_codes; int64_t a_ldc;
+    const uint8_t *a_scales; int64_t a_lds;
+    const float *a_S;
+    const uint8_t *w_codes; int64_t w_ldc;
+    const uint8_t *w_scales; int64_t w_lds;
+    const float *w_S;
+    int64_t M, N, K, res_cols;
+    void *y; int yt; int64_t ldy;
+    int tiles_m, tiles_n;
+};
+
+__device__ inline uint16_t f2bf(float f) {
+    uint32_t u = f2u(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// 32 consecutive k of one row (codes + the two block scales), zero beyond kend.
+struct RowChunk { uint4 c; uint32_t s; };
+
+__device__ inline RowChunk load_chunk(const uint8_t *codes, int64_t ldc, const uint8_t *scales, int64_t lds,
+                                      int64_t row, int64_t nrows, int64_t k, int64_t kend) {
+    RowChunk rc;
+    rc.c = make_uint4(0, 0, 0, 0);
+    rc.s = 0;
+    if (row < nrows) {
+        const uint8_t *cp = codes + row * ldc + k / 2;
+        const uint8_t *sp = scales + row * lds + k / 16;
+        if (k + 32 <= kend) {
+            rc.c = *reinterpret_cast<const uint4 *>(cp);
+            rc.s = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+        } else if (k + 16 <= kend) {
+            const uint2 h = *reinterpret_cast<const uint2 *>(cp);
+            rc.c.x = h.x; rc.c.y = h.y;
+            rc.s = sp[0];
+        }
+    }
+    return rc;
+}
+
+// Decode a chunk into 4 fragments (8 k each) and store them at LDS slots
+// base + 16 q (q = 0..3): the lane (r16 + 16 q) of k-chunk `base`.
+__device__ inline void store_chunk(half8 *lds, int slot, const RowChunk &rc) {
+    const half2v d0 = scale_pair(rc.s & 0xFFu), d1 = scale_pair((rc.s >> 8) & 0xFFu);
+    lds[slot + 0] = decode8(rc.c.x, d0);
+    lds[slot + 16] = decode8(rc.c.y, d0);
+    lds[slot + 32] = decode8(rc.c.z, d1);
+    lds[slot + 48] = decode8(rc.c.w, d1);
+}
+
+template <int BM, int BN, bool RES>
+__global__ __launch_bounds__(256) void tiled_kernel(TArgs a) {
+    constexpr int RT = BM / 16, CT = BN / 16;               // 16-row tiles per operand
+    constexpr int A_SLOTS = RT * 2 * 64, B_SLOTS = CT * 2 * 64;
+    constexpr int STAGE = A_SLOTS * (RES ? 2 : 1) + B_SLOTS;
+    constexpr int WRT = RT / 2, WCT = CT / 2;               // per-wave tiles (2 x 2 waves)
+    extern __shared__ half8 lds[];                           // [2][STAGE]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    // XCD-aware order: consecutive blocks go to different XCDs; regroup so that
+    // blocks sharing a weight tile column land on the same XCD.
+    const int nblk = a.tiles_m * a.tiles_n;
+    int bid = blockIdx.x;
+    if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+    const int tn = bid / a.tiles_m, tm = bid % a.tiles_m;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    const int64_t ksteps = (a.K + BK - 1) / BK;
+    const int64_t rsteps = RES ? (a.res_cols + BK - 1) / BK : 0;
+
+    // loader mapping: thread -> (row, half) ; BM/BN rows x 2 halves
+    constexpr int A_ITERS = (BM * 2 + 255) / 256, B_ITERS = (BN * 2 + 255) / 256;
+    RowChunk ra[A_ITERS], rr[RES ? A_ITERS : 1], rb[B_ITERS];
+
+    auto gload = [&](int64_t s) {
+        const int64_t k = s * BK;
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx >> 1, h = idx & 1;
+            if (r < BM) {
+                ra[it] = load_chunk(a.a_codes, a.a_ldc, a.a_scales, a.a_lds, m0 + r, a.M, k + 32 * h, a.K);
+                if (RES) {
+                    if (s < rsteps) {
+                        RowChunk t = load_chunk(a.a_codes, a.a_ldc, a.a_scales, a.a_lds, m0 + r, a.M,
+                                                a.K + k + 32 * h, a.K + a.res_cols);
+                        rr[it] = t;
+                    } else {
+                        rr[it].c = make_uint4(0, 0, 0, 0); rr[it].s = 0;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < B_ITERS; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx >> 1, h = idx & 1;
+            if (r < BN) rb[it] = load_chunk(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K);
+        }
+    };
+    auto lstore = [&](half8 *st) {
+#pragma unroll
+        for (int it = 0; it < A_ITERS; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx >> 1, h = idx & 1;
+            if (r < BM) {
+                const int slot = ((r >> 4) * 2 + h) * 64 + (r & 15);
+                store_chunk(st, slot, ra[it]);
+                if (RES) store_chunk(st + A_SLOTS + B_SLOTS, slot, rr[it]);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < B_ITERS; ++it) {
+            const int idx = tid + 256 * it;
+            const int r = idx >> 1, h = idx & 1;
+            if (r < BN) store_chunk(st + A_SLOTS, ((r >> 4) * 2 + h) * 64 + (r & 15), rb[it]);
+        }
+    };
+
+    float4v acc[WRT][WCT];
+#pragma unroll
+    for (int i = 0; i < WRT; ++i)
+#pragma unroll
+        for (int j = 0; j < WCT; ++j) acc[i][j] = float4v{0, 0, 0, 0};
+
+    gload(0);
+    lstore(lds);
+    __syncthreads();
+    for (int64_t s = 0; s < ksteps; ++s) {
+        half8 *cur = lds + (s & 1) * STAGE;
+        half8 *nxt = lds + ((s + 1) & 1) * STAGE;
+        if (s + 1 < ksteps) gload(s + 1);
+        const bool res_step = RES && s < rsteps;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            half8 bf[WCT];
+#pragma unroll
+            for (int j = 0; j < WCT; ++j) bf[j] = cur[A_SLOTS + ((wn * WCT + j) * 2 + kc) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < WRT; ++i) {
+                const half8 af = cur[((wm * WRT + i) * 2 + kc) * 64 + lane];
+#pragma unroll
+                for (int j = 0; j < WCT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+            }
+            if (res_step) {
+#pragma unroll
+                for (int i = 0; i < WRT; ++i) {
+                    const half8 af = cur[A_SLOTS + B_SLOTS + ((wm * WRT + i) * 2 + kc) * 64 + lane];
+#pragma unroll
+                    for (int j = 0; j < WCT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+        if (s + 1 < ksteps) lstore(nxt);
+        __syncthreads();
+    }
+
+    const float scale = a.a_S[0] * a.w_S[0];
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < WRT; ++i) {
+#pragma unroll
+        for (int j = 0; j < WCT; ++j) {
+            const int64_t n = n0 + (wn * WCT + j) * 16 + c16;
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + (wm * WRT + i) * 16 + 4 * g + e;
+                if (m < a.M) {
+                    const float v = acc[i][j][e] * scale;
+                    if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
+                    else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f2bf(v);
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN, bool RES>
+hipError_t run(const TArgs &a0, hipStream_t st) {
+    TArgs a = a0;
+    a.tiles_m = (int)((a.M + BM - 1) / BM);
+    a.tiles_n = (int)((a.N + BN - 1) / BN);
+    constexpr int STAGE = (BM / 16) * 2 * 64 * (RES ? 2 : 1) + (BN / 16) * 2 * 64;
+    const size_t lds = 2 * (size_t)STAGE * sizeof(half8);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled_kernel<BM, BN, RES>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int blocks = a.tiles_m * a.tiles_n;
+    tiled_kernel<BM, BN, RES><<<blocks, 256, lds, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st) {
+    TArgs a;
+    a.a_codes = g.a_codes; a.a_ldc = g.a_ldc; a.a_scales = g.a_scales; a.a_lds = g.a_lds; a.a_S = g.a_S;
+    a.w_codes = g.w_codes; a.w_ldc = g.w_ldc; a.w_scales = g.w_scales; a.w_lds = g.w_lds; a.w_S = g.w_S;
+    a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
+    a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
+    a.tiles_m = a.tiles_n = 0;
+    if (g.res_cols > 0) {
+        if (g.M <= 64) return run<64, 128, true>(a, st);
+        return run<128, 128, true>(a, st);
+    }
+    if (g.M <= 64) return run<64, 128, false>(a, st);
+    return run<128, 128, false>(a, st);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,82 @@
+// nvfp4_device.h -- scalar rounding helpers and FP4 decoding for gfx950.
+//
+// The rounding helpers reproduce, with integer arithmetic on the float bit
+// pattern, round-to-nearest-even onto the E4M3 and E2M1 grids with saturation
+// (the NVFP4 element/scale formats of the ARCQuant article, section 1). They
+// are __host__ __device__ so that the same source can be checked on the CPU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline uint32_t f2u(float f) { union { float f; uint32_t u; } c; c.f = f; return c.u; }
+__host__ __device__ inline float u2f(uint32_t u) { union { float f; uint32_t u; } c; c.u = u; return c.f; }
+
+// E4M3 byte of sf >= 0 (finite): nearest of the 127 finite non-negative values,
+// ties to the even code, everything >= 448 -> 448 (0x7E).
+__host__ __device__ inline uint32_t e4m3_rne_sat(float sf) {
+    if (sf >= 448.0f) return 0x7Eu;
+    if (sf < 0.015625f) {                     // below 2^-6: subnormal grid, step 2^-9
+        return (uint32_t)rintf(sf * 512.0f);  // exact scaling; 8 becomes 2^-6 = 0x08
+    }
+    uint32_t u = f2u(sf);
+    uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);   // round mantissa to 3 bits, ties even
+    uint32_t c = (r >> 20) - (120u << 3);           // exponent bias 127 -> 7
+    return c > 0x7Eu ? 0x7Eu : c;
+}
+
+// Value of a non-negative E4M3 byte (0..0x7E) as float, exact.
+__host__ __device__ inline float e4m3_to_float(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 0) return (float)m * 0.001953125f;     // m * 2^-9
+    return u2f(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 magnitude index (0..7) of a = |q|: nearest of {0,.5,1,1.5,2,3,4,6},
+// ties to the even index, everything >= 6 -> 7.
+__host__ __device__ inline uint32_t e2m1_rne_sat(float a) {
+    if (a >= 6.0f) return 7u;
+    if (a < 1.0f) return (uint32_t)rintf(a * 2.0f);  // 0, 0.5, 1.0 -> 0, 1, 2
+    uint32_t u = f2u(a);
+    uint32_t r = u + 0x1FFFFFu + ((u >> 22) & 1u);   // round mantissa to 1 bit, ties even
+    uint32_t c = (r >> 22) - (126u << 1);            // exponent bias 127 -> 1
+    return c > 7u ? 7u : c;
+}
+
+// Value e(code) of a 4-bit code, exact.
+__host__ __device__ inline float e2m1_to_float(uint32_t c) {
+    uint32_t e = (c >> 1) & 3u, m = c & 1u;
+    float mag = (e == 0) ? 0.5f * (float)m : u2f(((e + 126u) << 23) | (m << 22));
+    return (c & 8u) ? -mag : mag;
+}
+
+// 8 packed E2M1 codes (one dword, low nibble first) times an E4M3 block scale,
+// as 8 f16 values e(c) * d. The hardware convert applies only the exponent of
+// its f32 scale, so it produces e * 2^8 and the multiply by the f16 whose bits
+// are (byte << 7) -- the E4M3 value times 2^-8, exact in f16 -- gives e * d.
+// Both factors and the product are exact in f16 (<= 6 significant bits,
+// 2^-10 <= |e d| <= 2688).
+__device__ inline half8 decode8(uint32_t codes, half2v dd) {
+    half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 0);
+    half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 1);
+    half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 2);
+    half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 256.0f, 3);
+    p0 *= dd; p1 *= dd; p2 *= dd; p3 *= dd;
+    half8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    return r;
+}
+
+// f16 pair (d * 2^-8, d * 2^-8) from an E4M3 byte.
+__device__ inline half2v scale_pair(uint32_t b) {
+    uint32_t h = (b & 0x7Fu) << 7;
+    uint32_t v = h | (h << 16);
+    return __builtin_bit_cast(half2v, v);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,448 @@
+// quantize.hip -- NVFP4 quantizer kernels for gfx950.
+//
+// Steps of the fused quantizer (ARCQuant article on zizhi168.cn, section 3.2:
+// channel reorder, RMSNorm, main quantization and residual quantization in one
+// kernel; ResServe abstract: FP4 base plus FP4-quantized residue):
+//   amax pass    per-tensor |x| maximum (of the RMSNorm output when normalizing),
+//                as one partial maximum per workgroup -- no atomics, so the
+//                result does not depend on scheduling;
+//   quant pass   every workgroup folds the partials into S, then quantizes
+//                groups of 64 columns (4 blocks of 16) per thread: block absmax,
+//                E4M3 block scale, E2M1 codes, nibble packing, and the residue
+//                R = x - fl(fl(e d) S) of columns below res_cols, quantized
+//                against the same S and stored after column K_in.
+// All rounding follows the FP32 order of nvfp4.h; contraction into FMA is off
+// so every product and difference rounds exactly once.
+#include "internal.h"
+#include "nvfp4_device.h"
+
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline float bf16f(uint32_t h) { return u2f(h << 16); }
+
+// 16 consecutive elements starting at element `off` of a bf16 or f32 array.
+template <int XT>
+__device__ inline void load16(const void *base, int64_t off, float *v) {
+    if constexpr (XT == IN_BF16) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+        uint4 a = p[0], b = p[1];
+        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = u2f(w[i] << 16);
+            v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 q = p[i];
+            v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+        }
+    }
+}
+
+__device__ inline void gamma16(const uint16_t *g, int64_t off, float *v) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(g + off);
+    uint4 a = p[0], b = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[2 * i] = u2f(w[i] << 16);
+        v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+    }
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Maximum over the workgroup (kThreads threads); result valid in every thread.
+__device__ inline float block_max(float v, float *sh) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) sh[w] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, sh[i]);
+    return r;
+}
+
+__device__ inline double block_sum_d(double v, double *sh) {
+    v = wave_sum_d(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) sh[w] = v;
+    __syncthreads();
+    double r = sh[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) r += sh[i];
+    return r;
+}
+
+// ---------------------------------------------------------------- amax pass
+
+template <int XT>
+__global__ __launch_bounds__(kThreads) void amax_plain_kernel(const void *x, int64_t rows, int64_t K,
+                                                             int64_t ldx, float *partials) {
+    __shared__ float sh[kThreads / 64];
+    const int64_t nb = K / 16, total = rows * nb;
+    float m = 0.0f;
+    for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total;
+         c += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = c / nb, b = c - r * nb;
+        float v[16];
+        load16<XT>(x, r * ldx + 16 * b, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+    m = block_max(m, sh);
+    if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// Row-parallel pass for RMSNorm: r = fl32(1 / sqrt(sum(x^2)/K + eps)) with the
+// sum in FP64, then max |fl(fl(x r) gamma)| over the row.
+template <int XT>
+__device__ inline float row_rms_scale(const void *x, int64_t row, int64_t K, int64_t ldx, float eps,
+                                      double *shd) {
+    double ss = 0.0;
+    for (int64_t b = threadIdx.x; b < K / 16; b += kThreads) {
+        float v[16];
+        load16<XT>(x, row * ldx + 16 * b, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += (double)v[i] * (double)v[i];
+    }
+    ss = block_sum_d(ss, shd);
+    return (float)(1.0 / sqrt(ss / (double)K + (double)eps));
+}
+
+template <int XT>
+__global__ __launch_bounds__(kThreads) void amax_rmsnorm_kernel(const void *x, int64_t rows, int64_t K,
+                                                               int64_t ldx, const uint16_t *gamma,
+                                                               float eps, float *rscale, float *partials) {
+    __shared__ float sh[kThreads / 64];
+    __shared__ double shd[kThreads / 64];
+    float m = 0.0f;
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const float r = row_rms_scale<XT>(x, row, K, ldx, eps, shd);
+        if (threadIdx.x == 0) rscale[row] = r;
+        for (int64_t b = threadIdx.x; b < K / 16; b += kThreads) {
+            float v[16], g[16];
+            load16<XT>(x, row * ldx + 16 * b, v);
+            gamma16(gamma, 16 * b, g);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float y = v[i] * r;
+                y = y * g[i];
+                m = fmaxf(m, fabsf(y));
+            }
+        }
+    }
+    m = block_max(m, sh);
+    if (threadIdx.x == 0) partials[blockIdx.x] = m;
+}
+
+// -------------------------------------------------------------- quant pass
+
+struct QArgs {
+    const void *x; int64_t rows, K_in, ldx;
+    const uint16_t *gamma;
+    const int32_t *perm;
+    int64_t res_cols;
+    const float *static_S;
+    uint8_t *codes; int64_t ldc;
+    uint8_t *scales; int64_t lds;
+    float *S_out;
+    const float *partials; int npart;
+    const float *rscale;
+};
+
+__device__ inline float tensor_scale(const QArgs &a, float *sh) {
+    if (a.static_S) return *a.static_S;
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < a.npart; i += kThreads) m = fmaxf(m, a.partials[i]);
+    m = block_max(m, sh);
+    return m > 0.0f ? m / 2688.0f : 1.0f;
+}
+
+// Encode one block of 16 values against tensor scale S (t = 6 S): returns the
+// E4M3 byte, fills two dwords of packed codes, and d (the decoded scale).
+__device__ inline uint32_t encode_block(const float *v, float S, float t, uint32_t *cw, float &d) {
+    float ab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+    const float sf = ab / t;
+    const uint32_t db = e4m3_rne_sat(sf);
+    d = e4m3_to_float(db);
+    const float s = d * S;
+    const float rcp = (s > 0.0f) ? 1.0f / s : 0.0f;
+    cw[0] = 0; cw[1] = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float q = v[i] * rcp;
+        const uint32_t c = e2m1_rne_sat(fabsf(q)) | ((f2u(v[i]) >> 31) << 3);
+        cw[i >> 3] |= c << (4 * (i & 7));
+    }
+    return db;
+}
+
+// Quantize `nb` (1..4) blocks of row `row` starting at column col0 from v[64].
+__device__ inline void process_group(const QArgs &a, const float *v, int nb, int64_t row, int64_t col0,
+                                     float S, float t) {
+    uint32_t cw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t sw = 0;
+    float dblk[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        if (b < nb) {
+            const uint32_t db = encode_block(v + 16 * b, S, t, cw + 2 * b, dblk[b]);
+            sw |= db << (8 * b);
+        }
+    }
+    uint8_t *cp = a.codes + row * a.ldc + col0 / 2;
+    uint8_t *sp = a.scales + row * a.lds + col0 / 16;
+    if (nb == 4) {
+        reinterpret_cast<uint4 *>(cp)[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        reinterpret_cast<uint4 *>(cp)[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+        *reinterpret_cast<uint32_t *>(sp) = sw;
+    } else {
+        for (int b = 0; b < nb; ++b) {
+            reinterpret_cast<uint2 *>(cp)[b] = make_uint2(cw[2 * b], cw[2 * b + 1]);
+            sp[b] = (uint8_t)(sw >> (8 * b));
+        }
+    }
+    if (col0 >= a.res_cols) return;
+    // residue R = x - fl(fl(e d) S) on the columns below res_cols
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        if (b < nb && col0 + 16 * b < a.res_cols) {
+            float rv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t c = (cw[2 * b + (i >> 3)] >> (4 * (i & 7))) & 15u;
+                const float ed = e2m1_to_float(c) * dblk[b];
+                const float deq = ed * S;
+                rv[i] = v[16 * b + i] - deq;
+            }
+            uint32_t rc[2];
+            float dr;
+            const uint32_t rdb = encode_block(rv, S, t, rc, dr);
+            const int64_t col = a.K_in + col0 + 16 * b;
+            *reinterpret_cast<uint2 *>(a.codes + row * a.ldc + col / 2) = make_uint2(rc[0], rc[1]);
+            a.scales[row * a.lds + col / 16] = (uint8_t)rdb;
+        }
+    }
+}
+
+template <int XT, bool NORM>
+__global__ __launch_bounds__(kThreads) void quantize_flat_kernel(QArgs a) {
+    __shared__ float sh[kThreads / 64];
+    const float S = tensor_scale(a, sh);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.S_out = S;
+    const float t = 6.0f * S;
+    const int64_t ng = (a.K_in + 63) / 64, total = a.rows * ng;
+    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total;
+         g += (int64_t)gridDim.x * kThreads) {
+        const int64_t row = g / ng, gi = g - row * ng, col0 = 64 * gi;
+        const int64_t rem = a.K_in - col0;
+        const int nb = rem >= 64 ? 4 : (int)(rem / 16);
+        float v[64];
+        float r = 1.0f;
+        if (NORM) r = a.rscale[row];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (b < nb) {
+                load16<XT>(a.x, row * a.ldx + col0 + 16 * b, v + 16 * b);
+                if (NORM) {
+                    float gm[16];
+                    gamma16(a.gamma, col0 + 16 * b, gm);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float y = v[16 * b + i] * r;
+                        v[16 * b + i] = y * gm[i];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[16 * b + i] = 0.0f;
+            }
+        }
+        process_group(a, v, nb, row, col0, S, t);
+    }
+}
+
+// Channel-gather variant: one workgroup per row stages the (normalized) row in
+// LDS, then each thread gathers its 64 columns through perm.
+template <int XT, bool NORM>
+__global__ __launch_bounds__(kThreads) void quantize_perm_kernel(QArgs a) {
+    extern __shared__ float rowbuf[];
+    __shared__ float sh[kThreads / 64];
+    const float S = tensor_scale(a, sh);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.S_out = S;
+    const float t = 6.0f * S;
+    const int64_t ng = (a.K_in + 63) / 64;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const float r = NORM ? a.rscale[row] : 1.0f;
+        for (int64_t b = threadIdx.x; b < a.K_in / 16; b += kThreads) {
+            float v[16];
+            load16<XT>(a.x, row * a.ldx + 16 * b, v);
+            if (NORM) {
+                float gm[16];
+                gamma16(a.gamma, 16 * b, gm);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float y = v[i] * r;
+                    v[i] = y * gm[i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rowbuf[16 * b + i] = v[i];
+        }
+        __syncthreads();
+        for (int64_t gi = threadIdx.x; gi < ng; gi += kThreads) {
+            const int64_t col0 = 64 * gi, rem = a.K_in - col0;
+            const int nb = rem >= 64 ? 4 : (int)(rem / 16);
+            float v[64];
+#pragma unroll
+            for (int i = 0; i < 64; ++i) v[i] = (i < 16 * nb) ? rowbuf[a.perm[col0 + i]] : 0.0f;
+            process_group(a, v, nb, row, col0, S, t);
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------ calibration absmax
+
+template <int XT>
+__global__ __launch_bounds__(kThreads) void rms_scale_kernel(const void *x, int64_t rows, int64_t K,
+                                                            int64_t ldx, float eps, float *rscale) {
+    __shared__ double shd[kThreads / 64];
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const float r = row_rms_scale<XT>(x, row, K, ldx, eps, shd);
+        if (threadIdx.x == 0) rscale[row] = r;
+    }
+}
+
+// Column maxima: thread per group of 16 columns, loop over all rows.
+template <int XT, bool NORM>
+__global__ __launch_bounds__(kThreads) void channel_absmax_kernel(const void *x, int64_t rows, int64_t K,
+                                                                 int64_t ldx, const uint16_t *gamma,
+                                                                 const float *rscale, float *out) {
+    const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (b >= K / 16) return;
+    float m[16], g[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { m[i] = 0.0f; g[i] = 1.0f; }
+    if (NORM) gamma16(gamma, 16 * b, g);
+    for (int64_t row = 0; row < rows; ++row) {
+        float v[16];
+        load16<XT>(x, row * ldx + 16 * b, v);
+        const float r = NORM ? rscale[row] : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float y = v[i];
+            if (NORM) { y = y * r; y = y * g[i]; }
+            m[i] = fmaxf(m[i], fabsf(y));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[16 * b + i] = m[i];
+}
+
+int amax_grid(int64_t rows, int64_t K) {
+    const int64_t chunks = rows * (K / 16);
+    int64_t g = (chunks + kThreads * 4 - 1) / (kThreads * 4);
+    if (g < 1) g = 1;
+    if (g > kAmaxPartials) g = kAmaxPartials;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
+    const bool norm = q.gamma != nullptr, perm = q.perm != nullptr;
+    int npart = 0;
+    if (!q.static_S) {
+        if (norm) {
+            npart = (int)(q.rows < kAmaxPartials ? q.rows : kAmaxPartials);
+            if (npart < 1) npart = 1;
+            if (q.xt == IN_BF16)
+                amax_rmsnorm_kernel<IN_BF16><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.gamma, q.eps, q.rscale, q.partials);
+            else
+                amax_rmsnorm_kernel<IN_F32><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.gamma, q.eps, q.rscale, q.partials);
+        } else {
+            npart = amax_grid(q.rows, q.K_in);
+            if (q.xt == IN_BF16)
+                amax_plain_kernel<IN_BF16><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.partials);
+            else
+                amax_plain_kernel<IN_F32><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.partials);
+        }
+    } else if (norm) {
+        const int g = (int)(q.rows < 4096 ? (q.rows > 0 ? q.rows : 1) : 4096);
+        if (q.xt == IN_BF16)
+            rms_scale_kernel<IN_BF16><<<g, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.eps, q.rscale);
+        else
+            rms_scale_kernel<IN_F32><<<g, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.eps, q.rscale);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    QArgs a;
+    a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
+    a.gamma = q.gamma; a.perm = q.perm; a.res_cols = q.res_cols; a.static_S = q.static_S;
+    a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
+    a.partials = q.partials; a.npart = npart; a.rscale = q.rscale;
+
+    if (perm) {
+        const int g = (int)(q.rows < 2048 ? (q.rows > 0 ? q.rows : 1) : 2048);
+        const size_t lds = (size_t)q.K_in * sizeof(float);
+#define QP(XT, NM) quantize_perm_kernel<XT, NM><<<g, kThreads, lds, st>>>(a)
+        if (q.xt == IN_BF16) { if (norm) QP(IN_BF16, true); else QP(IN_BF16, false); }
+        else { if (norm) QP(IN_F32, true); else QP(IN_F32, false); }
+#undef QP
+    } else {
+        const int64_t groups = q.rows * ((q.K_in + 63) / 64);
+        int64_t g = (groups + kThreads - 1) / kThreads;
+        if (g > 8192) g = 8192;
+        if (g < 1) g = 1;
+#define QF(XT, NM) quantize_flat_kernel<XT, NM><<<(int)g, kThreads, 0, st>>>(a)
+        if (q.xt == IN_BF16) { if (norm) QF(IN_BF16, true); else QF(IN_BF16, false); }
+        else { if (norm) QF(IN_F32, true); else QF(IN_F32, false); }
+#undef QF
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st) {
+    const bool norm = c.gamma != nullptr;
+    if (norm) {
+        const int g = (int)(c.rows < 4096 ? (c.rows > 0 ? c.rows : 1) : 4096);
+        if (c.xt == IN_BF16)
+            rms_scale_kernel<IN_BF16><<<g, kThreads, 0, st>>>(c.x, c.rows, c.K, c.ldx, c.eps, c.rscale);
+        else
+            rms_scale_kernel<IN_F32><<<g, kThreads, 0, st>>>(c.x, c.rows, c.K, c.ldx, c.eps, c.rscale);
+    }
+    const int g = (int)((c.K / 16 + kThreads - 1) / kThreads);
+#define CA(XT, NM) channel_absmax_kernel<XT, NM><<<g > 0 ? g : 1, kThreads, 0, st>>>(c.x, c.rows, c.K, c.ldx, c.gamma, c.rscale, c.out)
+    if (c.xt == IN_BF16) { if (norm) CA(IN_BF16, true); else CA(IN_BF16, false); }
+    else { if (norm) CA(IN_F32, true); else CA(IN_F32, false); }
+#undef CA
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,253 @@
+"""Thin ctypes binding of libnvfp4 (include/nvfp4.h) for torch tensors.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. Loading fails loudly when ``libnvfp4.so`` is missing; there is no
+fallback path. Device memory (outputs, workspace) comes from torch, and every
+call is enqueued on torch's current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+BF16, FP32 = 0, 1
+_STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "misaligned", 4: "bad dtype",
+           5: "workspace too small", 6: "unsupported", 7: "HIP error"}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_STATUS.get(status, '?')})")
+
+
+class _CTensor(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("ld_codes", C.c_int64), ("scales", C.c_void_p),
+                ("ld_scales", C.c_int64), ("tensor_scale", C.c_void_p), ("rows", C.c_int64),
+                ("K", C.c_int64)]
+
+
+class _COpts(C.Structure):
+    _fields_ = [("gamma", C.c_void_p), ("eps", C.c_float), ("perm", C.c_void_p),
+                ("residue_cols", C.c_int64), ("static_tensor_scale", C.c_void_p)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_channel_absmax",
+           "nvfp4_perm_from_absmax", "nvfp4_workspace_size", "nvfp4_status_string",
+           "nvfp4_last_error", "nvfp4_version", "nvfp4_host_e4m3_encode", "nvfp4_host_e2m1_encode"]
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+            L = C.CDLL(LIB_PATH)
+            vp, i64, sz = C.c_void_p, C.c_int64, C.c_size_t
+            L.nvfp4_quantize.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, sz, vp]
+            L.nvfp4_gemm.argtypes = [vp, vp, C.c_int, i64, i64, i64, vp, vp, C.c_int, i64, vp, sz, vp]
+            L.nvfp4_gemm_residue.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, C.c_int, i64, vp,
+                                             vp, sz, vp]
+            L.nvfp4_channel_absmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, C.c_float, vp, vp, sz, vp]
+            L.nvfp4_perm_from_absmax.argtypes = [vp, i64, vp]
+            L.nvfp4_workspace_size.argtypes = [C.c_int, i64, i64, i64, i64]
+            L.nvfp4_workspace_size.restype = sz
+            L.nvfp4_status_string.argtypes = [C.c_int]
+            L.nvfp4_status_string.restype = C.c_char_p
+            L.nvfp4_last_error.restype = C.c_char_p
+            L.nvfp4_host_e4m3_encode.argtypes = [C.c_float]
+            L.nvfp4_host_e2m1_encode.argtypes = [C.c_float]
+            for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_channel_absmax",
+                         "nvfp4_perm_from_absmax"):
+                getattr(L, name).restype = C.c_int
+            _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().nvfp4_last_error().decode() if status == 7 else ""
+        err = NVFP4Error(status, what + (f" [{msg}]" if msg else ""))
+        raise err
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _round_up(v: int, a: int) -> int:
+    return (v + a - 1) // a * a
+
+
+class NVFP4Tensor:
+    """Device NVFP4 tensor: codes [rows, ld_codes] u8, scales [rows, ld_scales] u8, scale [1] f32."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, scale: torch.Tensor, K: int):
+        self.codes, self.scales, self.scale, self.K = codes, scales, scale, K
+
+    @staticmethod
+    def empty(rows: int, K: int, device="cuda") -> "NVFP4Tensor":
+        ldc, lds = _round_up(max(K // 2, 1), 16), _round_up(max(K // 16, 1), 8)
+        codes = torch.empty((rows, ldc), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, lds), dtype=torch.uint8, device=device)
+        scale = torch.empty((1,), dtype=torch.float32, device=device)
+        return NVFP4Tensor(codes, scales, scale, K)
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    def c(self) -> _CTensor:
+        return _CTensor(self.codes.data_ptr(), self.codes.stride(0), self.scales.data_ptr(),
+                        self.scales.stride(0), self.scale.data_ptr(), self.rows, self.K)
+
+    def host(self):
+        """(codes [rows, K/2], scales [rows, K/16], S) as numpy arrays on the host."""
+        return (self.codes[:, : self.K // 2].cpu().numpy(), self.scales[:, : self.K // 16].cpu().numpy(),
+                self.scale.cpu().numpy()[0])
+
+
+_ws = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A per-(device, stream) scratch buffer, grown on demand (plumbing, not compute)."""
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf
+
+
+def _opts(gamma, eps, perm, residue_cols, static_scale):
+    if gamma is None and perm is None and not residue_cols and static_scale is None:
+        return None, []
+    keep = []
+    if gamma is not None:
+        assert gamma.dtype == torch.bfloat16 and gamma.is_contiguous()
+        keep.append(gamma)
+    if perm is not None:
+        assert perm.dtype == torch.int32 and perm.is_contiguous()
+        keep.append(perm)
+    if static_scale is not None:
+        if not torch.is_tensor(static_scale):
+            static_scale = torch.tensor([float(static_scale)], dtype=torch.float32,
+                                        device=(gamma if gamma is not None else perm).device
+                                        if (gamma is not None or perm is not None) else "cuda")
+        keep.append(static_scale)
+    o = _COpts(_ptr(gamma), C.c_float(eps), _ptr(perm), int(residue_cols), _ptr(static_scale))
+    return o, keep
+
+
+def quantize(x: torch.Tensor, gamma=None, eps: float = 1e-6, perm=None, residue_cols: int = 0,
+             static_scale=None) -> NVFP4Tensor:
+    """NVFP4-quantize rows of x (bf16/f32, 2-D), optionally fused with RMSNorm, a channel
+    gather and residue columns; returns rows x (K + residue_cols)."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, K = x.shape
+    out = NVFP4Tensor.empty(rows, K + residue_cols, x.device)
+    o, keep = _opts(gamma, eps, perm, residue_cols, static_scale)
+    n = lib().nvfp4_workspace_size(0, rows, 0, K, residue_cols)
+    ws = workspace(n, x.device)
+    ct = out.c()
+    _check(lib().nvfp4_quantize(_ptr(x), _dtype_code(x), rows, K, x.stride(0),
+                                C.byref(o) if o is not None else None, C.byref(ct),
+                                _ptr(ws), ws.numel(), _stream()), "nvfp4_quantize")
+    return out
+
+
+def gemm(a, w: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = Q(a) Q(w)^T; a is an NVFP4Tensor or a raw bf16/f32 [M, K] tensor (quantized in the call)."""
+    N, K = w.rows, w.K
+    if isinstance(a, NVFP4Tensor):
+        M, dev = a.rows, a.codes.device
+    else:
+        assert a.dim() == 2 and a.stride(1) == 1
+        M, dev = a.shape[0], a.device
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    yt = _dtype_code(out)
+    if isinstance(a, NVFP4Tensor):
+        ac = a.c()
+        n = lib().nvfp4_workspace_size(1, M, N, K, 0)
+        ws = workspace(n, dev)
+        _check(lib().nvfp4_gemm(C.byref(ac), None, 0, M, K, 0, C.byref(w.c()), _ptr(out), yt, out.stride(0),
+                                _ptr(ws), ws.numel(), _stream()), "nvfp4_gemm")
+    else:
+        n = lib().nvfp4_workspace_size(1, M, N, K, 0)
+        ws = workspace(n, dev)
+        _check(lib().nvfp4_gemm(None, _ptr(a), _dtype_code(a), M, K, a.stride(0), C.byref(w.c()), _ptr(out),
+                                yt, out.stride(0), _ptr(ws), ws.numel(), _stream()), "nvfp4_gemm")
+    return out
+
+
+def gemm_residue(x: torch.Tensor, w: NVFP4Tensor, residue_cols: int, gamma=None, eps: float = 1e-6,
+                 perm=None, static_scale=None, out_dtype=torch.float32, return_aug: bool = False,
+                 out: torch.Tensor | None = None):
+    """Y = s_aug [Q(X') | Q(R)] [Q(W) | Q(W[:, :S])]^T with X' = perm/RMSNorm(x), R its residue
+    on columns [0, S). w must already be in the channel order of perm."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    M, K = x.shape
+    N = w.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    o, keep = _opts(gamma, eps, perm, residue_cols, static_scale)
+    if o is None:
+        o = _COpts(None, C.c_float(eps), None, 0, None)
+    aug = NVFP4Tensor.empty(M, K + residue_cols, x.device) if return_aug else None
+    augc = aug.c() if aug is not None else None
+    n = lib().nvfp4_workspace_size(2, M, N, K, residue_cols)
+    ws = workspace(n, x.device)
+    _check(lib().nvfp4_gemm_residue(_ptr(x), _dtype_code(x), M, K, x.stride(0), C.byref(o), C.byref(w.c()),
+                                    _ptr(out), _dtype_code(out), out.stride(0),
+                                    C.byref(augc) if augc is not None else None,
+                                    _ptr(ws), ws.numel(), _stream()), "nvfp4_gemm_residue")
+    return (out, aug) if return_aug else out
+
+
+def channel_absmax(x: torch.Tensor, gamma=None, eps: float = 1e-6) -> torch.Tensor:
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, K = x.shape
+    out = torch.empty((K,), dtype=torch.float32, device=x.device)
+    n = lib().nvfp4_workspace_size(3, rows, 0, K, 0)
+    ws = workspace(n, x.device)
+    _check(lib().nvfp4_channel_absmax(_ptr(x), _dtype_code(x), rows, K, x.stride(0), _ptr(gamma),
+                                      C.c_float(eps), _ptr(out), _ptr(ws), ws.numel(), _stream()),
+           "nvfp4_channel_absmax")
+    return out
+
+
+def perm_from_absmax(v: torch.Tensor) -> torch.Tensor:
+    """Host sort: channels by descending absmax, ties by ascending index (int32, on v's device)."""
+    vh = v.detach().float().cpu().contiguous()
+    p = torch.empty(vh.numel(), dtype=torch.int32)
+    _check(lib().nvfp4_perm_from_absmax(C.c_void_p(vh.data_ptr()), vh.numel(), C.c_void_p(p.data_ptr())),
+           "nvfp4_perm_from_absmax")
+    return p.to(v.device)
+
+
+def calibrate_perm(x_cal: torch.Tensor, gamma=None, eps: float = 1e-6) -> torch.Tensor:
+    return perm_from_absmax(channel_absmax(x_cal, gamma, eps))

@@ -1,0 +1,161 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 hot path: block-scaled FP4
+ * quantization and the W4A4 matrix product it feeds.
+ *
+ * Format (ARCQuant article on zizhi168.cn, section 1; abstract of "Replay the
+ * Curvature: Accurate and Scalable NVFP4 Quantization for Large Language Model
+ * Inference"): each value is an E2M1 code, every 16 consecutive values along K
+ * share one E4M3 block scale, and one FP32 scale S covers the whole tensor.
+ *
+ * Canonical storage of an NVFP4 tensor with `rows` rows and K columns:
+ *   codes  : rows x ld_codes bytes; byte j of a row holds code(2j) in its low
+ *            nibble and code(2j+1) in its high nibble; a code is
+ *            sign (bit 3) | E2M1 magnitude index (bits 2..0; 0,0.5,1,1.5,2,3,4,6)
+ *   scales : rows x ld_scales bytes; byte b of a row is the E4M3 scale of
+ *            columns [16b, 16b+16)
+ *   S      : one float in device memory (so a dynamic scale needs no host sync)
+ * The value of an element is e(code) * d(scale) * S.
+ *
+ * Quantization rule (the pages fix the format, not the rounding; this is the
+ * reading implemented, and the CPU oracle implements the same rule):
+ *   S  = amax(tensor) / 2688 (2688 = 6 * 448), or 1 for an all-zero tensor,
+ *        or the caller's static scale;
+ *   d  = E4M3(amax(block) / (6 S)), round to nearest even, saturating at 448;
+ *   q  = x * (1 / (d S)) in FP32 (0 when d S = 0);
+ *   code = E2M1(|q|) round to nearest even, saturating at 6, sign bit of x.
+ *
+ * Conventions for every entry point:
+ *  - All buffer pointers are DEVICE pointers unless the name says host.
+ *    `stream` is a hipStream_t (NULL = the default stream); every call only
+ *    enqueues work on it and returns without synchronizing.
+ *  - The caller owns and allocates every buffer, including the workspace
+ *    (size from nvfp4_workspace_size). The library never allocates device
+ *    memory and keeps no device state between calls.
+ *  - Argument errors are detected before anything is enqueued; the call then
+ *    returns a status != NVFP4_OK and leaves every output untouched. Launch
+ *    failures return NVFP4_ERR_HIP; nvfp4_last_error() gives the HIP text.
+ *  - Alignment: codes rows must start on 16-byte boundaries (codes pointer and
+ *    ld_codes multiples of 16) and scales rows on 8-byte boundaries (pointer
+ *    and ld_scales multiples of 8), else NVFP4_ERR_ALIGN (the ARCQuant article,
+ *    section 6.3, asks for 16-byte aligned tensor dimensions). Activation
+ *    rows (x, ldx) must be 16-byte aligned; K must be a multiple of 16.
+ *  - Inputs must be finite; inputs and outputs must not alias. Calls on one
+ *    workspace must be ordered (same stream or synchronized).
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,         /* a required pointer is NULL                        */
+    NVFP4_ERR_SHAPE = 2,        /* inconsistent or unsupported sizes                 */
+    NVFP4_ERR_ALIGN = 3,        /* pointer or leading dimension misaligned           */
+    NVFP4_ERR_DTYPE = 4,        /* unknown dtype code                                */
+    NVFP4_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required        */
+    NVFP4_ERR_UNSUPPORTED = 6,  /* valid request this build does not implement       */
+    NVFP4_ERR_HIP = 7           /* the HIP runtime reported an error                 */
+} nvfp4_status;
+
+typedef enum { NVFP4_BF16 = 0, NVFP4_FP32 = 1 } nvfp4_dtype;
+
+/* One NVFP4 tensor in the canonical layout above (rows x K, K % 16 == 0). */
+typedef struct {
+    uint8_t *codes;        /* device, rows x ld_codes bytes                  */
+    int64_t  ld_codes;     /* bytes between rows, >= K/2, multiple of 16     */
+    uint8_t *scales;       /* device, rows x ld_scales bytes                 */
+    int64_t  ld_scales;    /* bytes between rows, >= K/16, multiple of 8     */
+    float   *tensor_scale; /* device, 1 float                                */
+    int64_t  rows;
+    int64_t  K;
+} nvfp4_tensor;
+
+/* Options of the fused quantizer (ARCQuant article, section 3.2: channel
+ * reorder + RMSNorm + main quantization + residual quantization in one kernel). */
+typedef struct {
+    const void    *gamma;          /* RMSNorm weight, bf16 device [K_in], or NULL = no norm.
+                                      y = fl(fl(x*r)*gamma), r = 1/sqrt(mean(x^2)+eps) with
+                                      the sum of squares in FP64 and r rounded to FP32   */
+    float          eps;            /* RMSNorm epsilon (e.g. 1e-6)                         */
+    const int32_t *perm;           /* device [K_in] channel order x'[:, j] = y[:, perm[j]],
+                                      or NULL (ARCQuant article, section 3.1: outliers
+                                      ranked by calibration absmax come first)           */
+    int64_t        residue_cols;   /* S: residue of columns [0, S) appended after column
+                                      K_in, quantized against the same tensor scale
+                                      (ARCQuant section 3.1; ResServe abstract). 0 = none,
+                                      S = K_in gives K -> 2K. Multiple of 16.             */
+    const float   *static_tensor_scale; /* device float, or NULL = dynamic amax / 2688   */
+} nvfp4_quant_opts;
+
+/* Quantize x (rows x K_in, dtype xt, leading dimension ldx elements) into
+ * `out`, which must have rows == rows and K == K_in + opts->residue_cols.
+ * opts may be NULL (plain quantization with a dynamic tensor scale). K_in with
+ * a permutation is limited to 16384. Workspace: nvfp4_workspace_size(0, rows, 0, K_in, S). */
+nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, int64_t ldx,
+                            const nvfp4_quant_opts *opts, const nvfp4_tensor *out,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* W4A4 product y[m][n] = S_a S_w sum_k e(a)d(a) e(w)d(w) over k < K, accumulated
+ * in FP32 (ARCQuant article, section 3.1: Y ~ Q(X) Q(W)^T).
+ * Exactly one of a_q (pre-quantized activations, M x K) and x (raw activations,
+ * dtype xt, leading dimension ldx, quantized inside the call with a dynamic
+ * tensor scale) is non-NULL. w is N x K. y is M x N with leading dimension ldy,
+ * dtype yt (FP32, or BF16 rounded to nearest even).
+ * Small M (<= 64) streams the packed weights once with wide loads; large M
+ * uses the tiled matrix-core path. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
+nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
+                        int64_t M, int64_t K, int64_t ldx,
+                        const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Residue-compensated product (ARCQuant article, sections 3.1-3.2; ResServe abstract):
+ *   X' = perm/RMSNorm(x) per opts, R = X' - deq(Q(X')) on columns [0, S),
+ *   Y  = s_aug [Q(X') | Q(R)] [Q(W) | Q(W[:, :S])]^T,  s_aug = S_x S_w,
+ * one GEMM over K + S columns in which the weight tail reuses the weight's own
+ * first S columns (the same codes and scales; it is never materialized). w must
+ * already be in the channel order of opts->perm. S = opts->residue_cols in
+ * [0, K]; S = 0 gives the plain product of the normalized/reordered input.
+ * a_aug_out (optional, M x (K + S)) receives the quantized X_aug.
+ * Workspace: nvfp4_workspace_size(2, M, N, K, S). */
+nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int64_t ldx,
+                                const nvfp4_quant_opts *opts, const nvfp4_tensor *w,
+                                void *y, int yt, int64_t ldy, const nvfp4_tensor *a_aug_out,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* Calibration statistic for the outlier reorder (ARCQuant article, sections 3.1
+ * and 6.1): absmax_out[j] = max over rows of |RMSNorm(x)[:, j]| (|x| when
+ * gamma == NULL). x is rows x K (dtype xt, ldx); absmax_out is a device float[K].
+ * Workspace: nvfp4_workspace_size(3, rows, 0, K, 0). */
+nvfp4_status nvfp4_channel_absmax(const void *x, int xt, int64_t rows, int64_t K, int64_t ldx,
+                                  const void *gamma, float eps, float *absmax_out,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* Host helper: perm_host = channels sorted by absmax_host descending, ties by
+ * ascending index (host arrays of K elements). */
+nvfp4_status nvfp4_perm_from_absmax(const float *absmax_host, int64_t K, int32_t *perm_host);
+
+/* Bytes of workspace an operation needs: op 0 = quantize (M = rows), 1 = gemm,
+ * 2 = gemm_residue, 3 = channel_absmax (M = rows). S is the residue column count. */
+size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S);
+
+const char *nvfp4_status_string(nvfp4_status s);
+const char *nvfp4_last_error(void);   /* thread-local text of the last HIP error */
+int         nvfp4_version(void);      /* major * 10000 + minor * 100 + patch      */
+
+/* Host-side builds of the kernels' scalar rounding helpers, exported so the
+ * rounding logic itself can be checked on a machine without a GPU.
+ * nvfp4_host_e4m3_encode: v >= 0 -> E4M3 byte; nvfp4_host_e2m1_encode: q -> 4-bit code. */
+int nvfp4_host_e4m3_encode(float v);
+int nvfp4_host_e2m1_encode(float q);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

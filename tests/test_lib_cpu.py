@@ -1,0 +1,127 @@
+"""Host-side checks of libnvfp4 that need no GPU: the library loads, exports every
+entry point declared in include/nvfp4.h, its argument checks reject bad calls
+before touching the device, and the kernels' scalar rounding helpers (built for
+the host from the same source) agree bit for bit with the oracle."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from block_scaled_fp4_02_amd import build, nvfp4
+    build.build(force=False)
+    return nvfp4.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    from block_scaled_fp4_02_amd import nvfp4
+    assert sorted(nvfp4.EXPORTS) == names
+
+
+def test_version_and_strings(L):
+    assert L.nvfp4_version() == 10000
+    assert L.nvfp4_status_string(0) == b"ok"
+    assert L.nvfp4_status_string(5) == b"workspace too small"
+
+
+def test_host_e4m3_matches_oracle(L, orc):
+    rng = np.random.default_rng(5)
+    finite = np.array([orc.e4m3_value(b) for b in range(127)])
+    mids = (finite[:-1] + finite[1:]) / 2
+    vals = np.concatenate([finite, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                           2.0 ** rng.uniform(-30, 12, 20000), rng.uniform(0, 500, 5000),
+                           [0.0, 1e-45, 2.0 ** -10, 448.0, 463.99, 464.0, 1e30]]).astype(np.float32)
+    for v in vals:
+        assert L.nvfp4_host_e4m3_encode(C.c_float(v)) == orc.e4m3_encode(v), v
+
+
+def test_host_e2m1_matches_oracle(L, orc):
+    rng = np.random.default_rng(6)
+    book = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    mids = (book[:-1] + book[1:]) / 2
+    q = np.concatenate([book, mids, np.nextafter(mids, 0), np.nextafter(mids, 9), rng.uniform(-8, 8, 20000),
+                        [0.0, -0.0, 6.4, 1e30, -1e30, 1e-40]]).astype(np.float32)
+    q = np.concatenate([q, -q])
+    for v in q:
+        assert L.nvfp4_host_e2m1_encode(C.c_float(v)) == orc.e2m1_encode(v), v
+
+
+def test_workspace_sizes(L):
+    assert L.nvfp4_workspace_size(0, 4, 0, 64, 0) > 0
+    assert L.nvfp4_workspace_size(1, 16, 14336, 4096, 0) >= 16 * 2048
+    assert L.nvfp4_workspace_size(2, 16, 8192, 8192, 8192) > L.nvfp4_workspace_size(1, 16, 8192, 8192, 0)
+    assert L.nvfp4_workspace_size(9, 1, 1, 16, 0) == 0
+
+
+def _tensor(rows, K, codes=16, scales=16, scale=16, ldc=None, lds=None):
+    from block_scaled_fp4_02_amd.nvfp4 import _CTensor
+    return _CTensor(codes, ldc if ldc is not None else max(16, (K // 2 + 15) // 16 * 16), scales,
+                    lds if lds is not None else max(8, (K // 16 + 7) // 8 * 8), scale, rows, K)
+
+
+def test_argument_errors_before_launch(L):
+    """Bad arguments come back as status codes; fake (never dereferenced) pointers."""
+    vp = C.c_void_p
+    fake = vp(1 << 20)
+    out = _tensor(4, 64, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    ws, wsn = fake, 1 << 20
+    # null input
+    assert L.nvfp4_quantize(None, 0, 4, 64, 64, None, C.byref(out), ws, wsn, None) == 1
+    # K not a multiple of 16
+    assert L.nvfp4_quantize(fake, 0, 4, 60, 64, None, C.byref(out), ws, wsn, None) == 2
+    # bad dtype
+    assert L.nvfp4_quantize(fake, 7, 4, 64, 64, None, C.byref(out), ws, wsn, None) == 4
+    # misaligned input
+    assert L.nvfp4_quantize(vp((1 << 20) + 2), 0, 4, 64, 64, None, C.byref(out), ws, wsn, None) == 3
+    # output shape mismatch
+    bad = _tensor(5, 64, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    assert L.nvfp4_quantize(fake, 0, 4, 64, 64, None, C.byref(bad), ws, wsn, None) == 2
+    # misaligned leading dimension of codes
+    bad = _tensor(4, 64, codes=1 << 20, scales=1 << 21, scale=1 << 22, ldc=40)
+    assert L.nvfp4_quantize(fake, 0, 4, 64, 64, None, C.byref(bad), ws, wsn, None) == 3
+    # workspace too small
+    assert L.nvfp4_quantize(fake, 0, 4, 64, 64, None, C.byref(out), ws, 16, None) == 5
+    # gemm: both or neither activation source
+    w = _tensor(32, 64, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    assert L.nvfp4_gemm(None, None, 0, 4, 64, 64, C.byref(w), fake, 1, 32, ws, wsn, None) == 1
+    assert L.nvfp4_gemm(C.byref(out), fake, 0, 4, 64, 64, C.byref(w), fake, 1, 32, ws, wsn, None) == 1
+    # gemm: K mismatch between activation and weight
+    w2 = _tensor(32, 48, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    assert L.nvfp4_gemm(C.byref(out), None, 0, 4, 64, 0, C.byref(w2), fake, 1, 32, ws, wsn, None) == 2
+    # gemm: ldy too small, bad output dtype
+    assert L.nvfp4_gemm(C.byref(out), None, 0, 4, 64, 0, C.byref(w), fake, 1, 16, ws, wsn, None) == 2
+    assert L.nvfp4_gemm(C.byref(out), None, 0, 4, 64, 0, C.byref(w), fake, 3, 32, ws, wsn, None) == 4
+    # residue: S not a multiple of 16 / larger than K
+    from block_scaled_fp4_02_amd.nvfp4 import _COpts
+    o = _COpts(None, C.c_float(1e-6), None, 24, None)
+    assert L.nvfp4_gemm_residue(fake, 0, 4, 64, 64, C.byref(o), C.byref(w), fake, 1, 32, None, ws, wsn, None) == 2
+    o = _COpts(None, C.c_float(1e-6), None, 80, None)
+    assert L.nvfp4_gemm_residue(fake, 0, 4, 64, 64, C.byref(o), C.byref(w), fake, 1, 32, None, ws, wsn, None) == 2
+    # permutation beyond the staged-row limit
+    o = _COpts(None, C.c_float(1e-6), fake, 0, None)
+    assert L.nvfp4_quantize(fake, 0, 4, 32768, 32768, C.byref(o),
+                            C.byref(_tensor(4, 32768, codes=1 << 20, scales=1 << 21, scale=1 << 22)),
+                            ws, 1 << 30, None) == 6
+
+
+def test_perm_from_absmax_host(L, orc):
+    rng = np.random.default_rng(9)
+    v = rng.integers(0, 30, 500).astype(np.float32)
+    p = np.zeros(500, np.int32)
+    assert L.nvfp4_perm_from_absmax(C.c_void_p(v.ctypes.data), 500, C.c_void_p(p.ctypes.data)) == 0
+    assert np.array_equal(p, orc.perm_from_absmax(v))
