@@ -46,7 +46,7 @@ size_t tensor_ws(int64_t rows, int64_t K) {
 
 size_t gemm_ws(int64_t M, int64_t N, int64_t K, int64_t S) {
     size_t part = 0;
-    if (M <= kSkinnyMaxM) part = up(skinny_workspace_bytes(M, N, K, S), kAlign);
+    if (M <= kSkinnyMaxM && K > 0) part = up(skinny_workspace_bytes(M, N, K, S), kAlign);
     return part;
 }
 
@@ -61,9 +61,13 @@ struct Carver {
 
 int elem_size(int xt) { return xt == NVFP4_BF16 ? 2 : 4; }
 
+// A tensor with no elements may carry null code/scale pointers; its scale
+// pointer is still required (the quantizer writes S = 1 for it).
 nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t K) {
-    if (!t || !t->codes || !t->scales || !t->tensor_scale) return NVFP4_ERR_NULL;
-    if (t->rows != rows || t->K != K) return NVFP4_ERR_SHAPE;
+    if (!t || !t->tensor_scale) return NVFP4_ERR_NULL;
+    if (t->rows != rows || t->K != K || rows < 0 || K < 0 || K % 16) return NVFP4_ERR_SHAPE;
+    if (rows == 0 || K == 0) return aligned(t->tensor_scale, 4) ? NVFP4_OK : NVFP4_ERR_ALIGN;
+    if (!t->codes || !t->scales) return NVFP4_ERR_NULL;
     if (t->ld_codes < K / 2 || t->ld_scales < K / 16) return NVFP4_ERR_SHAPE;
     if (t->ld_codes % 16 || t->ld_scales % 8 || !aligned(t->codes, 16) || !aligned(t->scales, 8) ||
         !aligned(t->tensor_scale, 4))
@@ -72,9 +76,11 @@ nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t K) {
 }
 
 nvfp4_status check_x(const void *x, int xt, int64_t rows, int64_t K, int64_t ldx) {
-    if (!x) return NVFP4_ERR_NULL;
     if (xt != NVFP4_BF16 && xt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
-    if (rows < 0 || K < 0 || K % 16 || ldx < K) return NVFP4_ERR_SHAPE;
+    if (rows < 0 || K < 0 || K % 16) return NVFP4_ERR_SHAPE;
+    if (rows == 0 || K == 0) return NVFP4_OK;          // nothing is read
+    if (!x) return NVFP4_ERR_NULL;
+    if (ldx < K) return NVFP4_ERR_SHAPE;
     if (!aligned(x, 16) || (ldx * elem_size(xt)) % 16) return NVFP4_ERR_ALIGN;
     return NVFP4_OK;
 }
@@ -112,7 +118,7 @@ nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in,
 nvfp4_status enqueue_gemm(const nvfp4_tensor &a, const nvfp4_tensor &w, int64_t M, int64_t K, int64_t S,
                           void *y, int yt, int64_t ldy, uint8_t *part, size_t part_bytes, hipStream_t st) {
     hipError_t e;
-    if (M <= kSkinnyMaxM) {
+    if (M <= kSkinnyMaxM && K > 0) {
         SkinnyLaunch g;
         g.a_codes = a.codes; g.a_ldc = a.ld_codes; g.a_scales = a.scales; g.a_lds = a.ld_scales; g.a_S = a.tensor_scale;
         g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
@@ -167,8 +173,10 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
                         int64_t M, int64_t K, int64_t ldx,
                         const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
                         void *ws, size_t ws_bytes, void *stream) {
-    if ((a_q == nullptr) == (x == nullptr)) return NVFP4_ERR_NULL;
-    if (!w || !y) return NVFP4_ERR_NULL;
+    if (!w) return NVFP4_ERR_NULL;
+    if (a_q == nullptr && x == nullptr && !(M == 0 || K == 0)) return NVFP4_ERR_NULL;
+    if (a_q != nullptr && x != nullptr) return NVFP4_ERR_NULL;
+    if (!y && M > 0 && w->rows > 0) return NVFP4_ERR_NULL;
     if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
     if (M < 0 || K < 0 || K % 16) return NVFP4_ERR_SHAPE;
     CHECK(check_tensor(w, w->rows, K));
@@ -176,6 +184,10 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
     if (ldy < N) return NVFP4_ERR_SHAPE;
     if (a_q) CHECK(check_tensor(a_q, M, K));
     else CHECK(check_x(x, xt, M, K, ldx));
+    if (M > 0 && N > 0 && K == 0 && !a_q) {
+        // empty contraction: y = 0 through the tiled path with an all-zero operand
+        a_q = w;  // any K == 0 tensor works: nothing of it is read
+    }
     const size_t need = a_q ? gemm_ws(M, N, K, 0) : nvfp4_workspace_size(1, M, N, K, 0);
     if (need && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
     if (M == 0 || N == 0) return NVFP4_OK;
@@ -204,7 +216,8 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
                                 const nvfp4_quant_opts *opts, const nvfp4_tensor *w,
                                 void *y, int yt, int64_t ldy, const nvfp4_tensor *a_aug_out,
                                 void *ws, size_t ws_bytes, void *stream) {
-    if (!w || !y) return NVFP4_ERR_NULL;
+    if (!w) return NVFP4_ERR_NULL;
+    if (!y && M > 0 && w->rows > 0) return NVFP4_ERR_NULL;
     if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
     CHECK(check_x(x, xt, M, K, ldx));
     CHECK(check_opts(opts, K));

@@ -319,7 +319,12 @@ __global__ __launch_bounds__(kThreads) void quantize_perm_kernel(QArgs a) {
             const int nb = rem >= 64 ? 4 : (int)(rem / 16);
             float v[64];
 #pragma unroll
-            for (int i = 0; i < 64; ++i) v[i] = (i < 16 * nb) ? rowbuf[a.perm[col0 + i]] : 0.0f;
+            for (int i = 0; i < 64; ++i) {
+                // indices outside [0, K_in) are clamped so a bad permutation cannot leave the row
+                int32_t pi = (i < 16 * nb) ? a.perm[col0 + i] : 0;
+                pi = pi < 0 ? 0 : (pi >= a.K_in ? (int32_t)(a.K_in - 1) : pi);
+                v[i] = (i < 16 * nb) ? rowbuf[pi] : 0.0f;
+            }
             process_group(a, v, nb, row, col0, S, t);
         }
         __syncthreads();

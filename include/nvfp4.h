@@ -86,7 +86,8 @@ typedef struct {
     float          eps;            /* RMSNorm epsilon (e.g. 1e-6)                         */
     const int32_t *perm;           /* device [K_in] channel order x'[:, j] = y[:, perm[j]],
                                       or NULL (ARCQuant article, section 3.1: outliers
-                                      ranked by calibration absmax come first)           */
+                                      ranked by calibration absmax come first). Must be a
+                                      permutation of [0, K_in); other values are clamped */
     int64_t        residue_cols;   /* S: residue of columns [0, S) appended after column
                                       K_in, quantized against the same tensor scale
                                       (ARCQuant section 3.1; ResServe abstract). 0 = none,
@@ -108,8 +109,8 @@ nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, i
  * dtype xt, leading dimension ldx, quantized inside the call with a dynamic
  * tensor scale) is non-NULL. w is N x K. y is M x N with leading dimension ldy,
  * dtype yt (FP32, or BF16 rounded to nearest even).
- * Small M (<= 64) streams the packed weights once with wide loads; large M
- * uses the tiled matrix-core path. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
+ * Small M (<= 32) streams the packed weights once with wide loads; larger M
+ * uses the tiled matrix-core path. K == 0 gives y = 0. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
                         int64_t M, int64_t K, int64_t ldx,
                         const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
