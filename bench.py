@@ -1,0 +1,336 @@
+"""Benchmark of the NVFP4 decode hot path on one MI355X.
+
+Workload (one "step"): the small-M decode sweep -- for every M in {1,2,4,8,16}
+and every (K, N) in {(4096,14336), (14336,4096), (4096,6144)}, one nvfp4_gemm
+call on bf16 activations X[M x K] (1% outlier channels x50, quantized to NVFP4
+inside the call: amax, block scales, codes) against pre-quantized NVFP4
+weights W[N x K] (from N(0, 0.02)), FP32 output. 15 calls per step.
+
+Timing: each step is captured once in a HIP graph and replayed, so host launch
+overhead is not measured. Every call reads a different copy of its weight
+(ring of copies, > 512 MB between reuses) so the 256 MB last-level cache
+cannot serve the weights; inputs are resident in HBM before timing starts.
+
+value = algorithmic bytes of the step (weight codes + scales once, bf16 X once,
+FP32 y once) / step time, in GB/s.
+
+Also reported (same JSON line):
+  roofline     the decode GEMM kernel alone (pre-quantized activations), HIP
+               events over graph replays of that kernel, against 8 TB/s;
+  cpu_baseline the CPU oracle (activation quantize + FP64 GEMM) on a bounded
+               sample of the same sweep, on the host cores;
+  detail       per (M, K, N) us/call and GB/s for the whole call and the kernel,
+               the residue-compensated variant, the M=64 augmented-channel
+               product and the prefill TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_scaled_fp4_02_amd import inputs  # noqa: E402
+
+METRIC = "NVFP4 GEMM µs & HBM GB/s at M=1–16; prefill TFLOP/s; % of roofline"
+HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0
+RING_BYTES = 640 << 20
+
+
+def wbytes(N, K):
+    return N * K // 2 + N * K // 16
+
+
+def call_bytes(M, N, K):
+    """Algorithmic bytes of one fused call: W once, bf16 X once, FP32 y once."""
+    return wbytes(N, K) + 2 * M * K + 4 * M * N
+
+
+def kernel_bytes(M, N, K):
+    """Algorithmic bytes of the GEMM kernel on pre-quantized activations."""
+    return wbytes(N, K) + M * K // 2 + M * K // 16 + 4 * M * N
+
+
+class Ring:
+    """Copies of one quantized weight, enough that reuse distance exceeds the MALL."""
+
+    def __init__(self, wq, copies):
+        from block_scaled_fp4_02_amd import nvfp4
+        self.items = [wq]
+        for _ in range(copies - 1):
+            self.items.append(nvfp4.NVFP4Tensor(wq.codes.clone(), wq.scales.clone(), wq.scale.clone(), wq.K))
+        self.i = 0
+
+    def next(self):
+        t = self.items[self.i % len(self.items)]
+        self.i += 1
+        return t
+
+
+def graph_time(fn, reps: int, inner: int = 1):
+    """Capture fn() (inner calls) in a graph; replay `reps` times; return seconds per inner call."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                       # warm (first-call attributes, workspace growth)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(reps):
+        g.replay()
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) / 1e3 / reps / inner, g
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip residue/augmented/prefill detail")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode path shards along N with no collective, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    from block_scaled_fp4_02_amd import nvfp4
+    nvfp4.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------- inputs, resident in HBM
+    shapes = inputs.DECODE_SHAPES
+    xs, rings, ys = {}, {}, {}
+    for si, (K, N) in enumerate(shapes):
+        x, w = inputs.decode_sweep(si)
+        xs[si] = x.to(dev)
+        wq = nvfp4.quantize(w.to(dev))
+        copies = max(2, -(-RING_BYTES // wbytes(N, K)))
+        rings[si] = Ring(wq, copies)
+        for M in inputs.DECODE_MS:
+            ys[(si, M)] = torch.empty((M, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for M in inputs.DECODE_MS:
+            for si in range(len(shapes)):
+                nvfp4.gemm(xs[si][:M], rings[si].next(), out=ys[(si, M)])
+
+    step_bytes = sum(call_bytes(M, N, K) for M in inputs.DECODE_MS for (K, N) in shapes)
+
+    # One graph per ring phase, each holding exactly one step; step t replays graph t % phases,
+    # so every call of consecutive steps reads a different weight copy.
+    phases = max(len(r.items) for r in rings.values())
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        for _ in range(phases):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                step()
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s)
+    for t in range(args.warmup):
+        graphs[t % phases].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for t in range(args.steps):
+        graphs[(args.warmup + t) % phases].replay()
+    en.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timed_steps = args.steps
+    sec_per_step = st.elapsed_time(en) / 1e3 / timed_steps
+    value = step_bytes / sec_per_step / 1e9
+    del graphs
+
+    # ---------------- per-case detail: whole call and kernel alone
+    detail = {"decode": []}
+    kern_bytes_total, kern_time_total = 0.0, 0.0
+    for si, (K, N) in enumerate(shapes):
+        ring = rings[si]
+        n = len(ring.items)
+        for M in inputs.DECODE_MS:
+            y = ys[(si, M)]
+            x = xs[si][:M]
+            aq = nvfp4.quantize(x)
+
+            def fused():
+                for _ in range(n):
+                    nvfp4.gemm(x, ring.next(), out=y)
+
+            def kern():
+                for _ in range(n):
+                    nvfp4.gemm(aq, ring.next(), out=y)
+
+            tf, _ = graph_time(fused, reps=20, inner=n)
+            tk, _ = graph_time(kern, reps=20, inner=n)
+            kern_bytes_total += kernel_bytes(M, N, K)
+            kern_time_total += tk
+            detail["decode"].append({
+                "M": M, "K": K, "N": N,
+                "us_call": round(tf * 1e6, 3), "GBs_call": round(call_bytes(M, N, K) / tf / 1e9, 1),
+                "us_kernel": round(tk * 1e6, 3), "GBs_kernel": round(kernel_bytes(M, N, K) / tk / 1e9, 1),
+                "frac_hbm_kernel": round(kernel_bytes(M, N, K) / tk / 1e9 / HBM_PEAK_GBS, 4),
+            })
+    achieved = kern_bytes_total / kern_time_total / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "skinny_kernel (decode W4A4 GEMM, pre-quantized activations)",
+                "per_launch_bytes": round(kern_bytes_total / len(detail["decode"])),
+                "per_launch_us": round(kern_time_total / len(detail["decode"]) * 1e6, 3)}
+
+    if not args.no_extra:
+        detail.update(extra_detail(nvfp4, dev))
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": timed_steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1/e4m3 (f16 MFMA, f32 acc)",
+        "data": "synthetic (seeded; Llama-3.1-8B linear-layer shapes)",
+        "config": {"workload": "small-M decode GEMM sweep M in {1,2,4,8,16} x (K,N) in "
+                               "{(4096,14336),(14336,4096),(4096,6144)}, bf16 activations quantized in the call",
+                   "calls_per_step": 15, "bytes_per_step": step_bytes, "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+def extra_detail(nvfp4, dev):
+    """Residue K->2K overhead, M=64 augmented product, prefill TFLOP/s (one number each)."""
+    res = {"residue": [], "augmented": [], "prefill": []}
+    # residue-compensated decode, K = N = 8192
+    x, w = inputs.residue_8192(16)
+    xd = x.to(dev)
+    wq = nvfp4.quantize(w.to(dev))
+    ring = Ring(wq, max(2, -(-RING_BYTES // wbytes(8192, 8192))))
+    n = len(ring.items)
+    for M in inputs.RESIDUE_MS:
+        y = torch.empty((M, 8192), dtype=torch.float32, device=dev)
+        xm = xd[:M]
+
+        def base():
+            for _ in range(n):
+                nvfp4.gemm(xm, ring.next(), out=y)
+
+        def comp():
+            for _ in range(n):
+                nvfp4.gemm_residue(xm, ring.next(), 8192, out=y)
+
+        tb, _ = graph_time(base, 20, n)
+        tc, _ = graph_time(comp, 20, n)
+        res["residue"].append({"M": M, "K": 8192, "N": 8192, "us_plain": round(tb * 1e6, 3),
+                               "us_residue": round(tc * 1e6, 3), "overhead": round(tc / tb - 1, 4),
+                               "GBs_residue": round(call_bytes(M, 8192, 8192) / tc / 1e9, 1)})
+    del ring
+    # augmented channels, M = 64, K = 4096, N = 14336
+    x, g, xcal, w = inputs.outlier_aug()
+    xd, gd = x.to(dev), g.to(dev)
+    perm = nvfp4.calibrate_perm(xcal.to(dev), gd)
+    wq = nvfp4.quantize(w.to(dev)[:, perm.long()].contiguous())
+    ring = Ring(wq, max(2, -(-RING_BYTES // wbytes(14336, 4096))))
+    n = len(ring.items)
+    y = torch.empty((64, 14336), dtype=torch.float32, device=dev)
+    t0 = None
+    for S in [0] + inputs.AUG_S:
+        def aug():
+            for _ in range(n):
+                nvfp4.gemm_residue(xd, ring.next(), S, gamma=gd, eps=1e-6, perm=perm, out=y)
+        t, _ = graph_time(aug, 20, n)
+        t0 = t if S == 0 else t0
+        flops = 2 * 64 * 14336 * (4096 + S)
+        res["augmented"].append({"M": 64, "K": 4096, "S": S, "N": 14336, "us_call": round(t * 1e6, 3),
+                                 "overhead_vs_S0": round(t / t0 - 1, 4),
+                                 "GBs": round(call_bytes(64, 14336, 4096) / t / 1e9, 1),
+                                 "TFLOPs": round(flops / t / 1e12, 2)})
+    del ring
+    # prefill: bf16 out, activation quantize in the call
+    torch.manual_seed(0)
+    for si, (K, N) in enumerate(inputs.PREFILL_SHAPES):
+        xall = torch.randn((8192, K), device=dev, dtype=torch.float32)
+        cols = torch.from_numpy(inputs.outlier_columns(5, si, K, 0.01)).to(dev)
+        xall[:, cols] *= 50.0
+        xall = xall.to(torch.bfloat16)
+        w = (torch.randn((N, K), device=dev, dtype=torch.float32) * 0.015).to(torch.bfloat16)
+        wq = nvfp4.quantize(w)
+        del w
+        aq_cache = {}
+        for M in inputs.PREFILL_MS:
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            xm = xall[:M]
+            aq = nvfp4.quantize(xm)
+            aq_cache[M] = aq
+
+            def full():
+                nvfp4.gemm(xm, wq, out=y)
+
+            def kern():
+                nvfp4.gemm(aq, wq, out=y)
+
+            reps = 10 if M < 8192 else 4
+            tf, _ = graph_time(full, reps, 1)
+            tk, _ = graph_time(kern, reps, 1)
+            flops = 2.0 * M * N * K
+            res["prefill"].append({"M": M, "K": K, "N": N, "us_call": round(tf * 1e6, 1),
+                                   "TFLOPs_call": round(flops / tf / 1e12, 1),
+                                   "us_kernel": round(tk * 1e6, 1), "TFLOPs_kernel": round(flops / tk / 1e12, 1),
+                                   "frac_f16_mfma_kernel": round(flops / tk / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
+        del xall, wq, aq_cache
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(budget_s: float):
+    """The CPU oracle (unchanged) on a bounded sample of the decode sweep: for each case in
+    sweep order, quantize X and run the FP64 GEMM against the oracle-quantized weight, until
+    the time budget is spent. Value = algorithmic bytes of the cases done / their time."""
+    import oracle
+    oracle.lib()
+    done, t_total, b_total = [], 0.0, 0
+    for si, (K, N) in enumerate(inputs.DECODE_SHAPES):
+        x, w = inputs.decode_sweep(si)
+        ow = oracle.quantize(w)
+        for M in inputs.DECODE_MS:
+            t0 = time.perf_counter()
+            oracle.gemm(oracle.quantize(x[:M]), ow)
+            dt = time.perf_counter() - t0
+            t_total += dt
+            b_total += call_bytes(M, N, K)
+            done.append(f"M={M},K={K},N={N}")
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    return {"value": round(b_total / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(done)} of 15 sweep calls ({', '.join(done)}), {t_total:.1f} s, single thread",
+            "us_call_mean": round(t_total / len(done) * 1e6, 1)}
+
+
+if __name__ == "__main__":
+    main()

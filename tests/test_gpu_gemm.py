@@ -186,3 +186,34 @@ def test_deterministic(nv):
     d = nv.gemm_residue(xd, wq, 4096)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d)
+
+
+def test_graph_replay_matches_eager(nv):
+    """The decode call captured in a HIP graph gives the eager result on every replay,
+    with unrelated eager work and synchronizations between replays."""
+    x, w = inputs.decode_sweep(0)
+    xd = x.to(DEV)
+    wq = nv.quantize(w.to(DEV))
+    y = torch.empty((16, 14336), dtype=torch.float32, device=DEV)
+    yr = torch.empty((4, 14336), dtype=torch.float32, device=DEV)
+    eager = nv.gemm(xd, wq).clone()
+    eager_r = nv.gemm_residue(xd[:4], wq, 4096).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        nv.gemm(xd, wq, out=y)
+        nv.gemm_residue(xd[:4], wq, 4096, out=yr)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            nv.gemm(xd, wq, out=y)
+            nv.gemm_residue(xd[:4], wq, 4096, out=yr)
+    torch.cuda.current_stream().wait_stream(s)
+    for i in range(4):
+        note(f"graph replay {i}")
+        y.zero_(); yr.zero_()
+        g.replay()
+        other = nv.gemm(xd[:2], wq)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager) and torch.equal(yr, eager_r), i
+        assert other.shape == (2, 14336)
