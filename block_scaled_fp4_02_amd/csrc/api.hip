@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -45,9 +46,14 @@ size_t tensor_ws(int64_t rows, int64_t K) {
 }
 
 size_t gemm_ws(int64_t M, int64_t N, int64_t K, int64_t S) {
-    size_t part = 0;
-    if (M <= kSkinnyMaxM && K > 0) part = up(skinny_workspace_bytes(M, N, K, S), kAlign);
-    return part;
+    if (M <= kSkinnyMaxM && K > 0) return up(decode_workspace_bytes(M, N, K, S), kAlign);
+    return 0;
+}
+
+unsigned spin_limit() {
+    const char *e = std::getenv("NVFP4_SPIN_LIMIT");
+    if (e && *e) return (unsigned)std::strtoul(e, nullptr, 10);
+    return 1u << 20;
 }
 
 struct Carver {
@@ -115,17 +121,21 @@ nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in,
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
+// Product on an already quantized activation tensor `a` (K + S columns).
 nvfp4_status enqueue_gemm(const nvfp4_tensor &a, const nvfp4_tensor &w, int64_t M, int64_t K, int64_t S,
-                          void *y, int yt, int64_t ldy, uint8_t *part, size_t part_bytes, hipStream_t st) {
+                          void *y, int yt, int64_t ldy, unsigned *header, uint8_t *scratch, size_t scratch_bytes,
+                          hipStream_t st) {
     hipError_t e;
     if (M <= kSkinnyMaxM && K > 0) {
-        SkinnyLaunch g;
-        g.a_codes = a.codes; g.a_ldc = a.ld_codes; g.a_scales = a.scales; g.a_lds = a.ld_scales; g.a_S = a.tensor_scale;
+        DecodeLaunch g{};
+        g.x = nullptr;
+        g.q_codes = a.codes; g.q_ldc = a.ld_codes; g.q_scales = a.scales; g.q_lds = a.ld_scales; g.q_S = a.tensor_scale;
         g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
         g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
         g.y = y; g.yt = yt; g.ldy = ldy;
-        g.partials = reinterpret_cast<float *>(part); g.partial_bytes = part_bytes;
-        e = launch_skinny(g, st);
+        g.header = header; g.scratch = scratch; g.scratch_bytes = scratch_bytes;
+        g.spin_limit = spin_limit();
+        e = launch_decode(g, st);
     } else {
         PrefillLaunch g;
         g.a_codes = a.codes; g.a_ldc = a.ld_codes; g.a_scales = a.scales; g.a_lds = a.ld_scales; g.a_S = a.tensor_scale;
@@ -137,6 +147,22 @@ nvfp4_status enqueue_gemm(const nvfp4_tensor &a, const nvfp4_tensor &w, int64_t 
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
+// Quantize-and-multiply in one launch (decode shapes, no RMSNorm or gather).
+nvfp4_status enqueue_fused(const void *x, int xt, int64_t ldx, const float *static_S, const nvfp4_tensor &q,
+                           const nvfp4_tensor &w, int64_t M, int64_t K, int64_t S, void *y, int yt, int64_t ldy,
+                           unsigned *header, uint8_t *scratch, size_t scratch_bytes, hipStream_t st) {
+    DecodeLaunch g{};
+    g.x = x; g.x_bf16 = xt == NVFP4_BF16; g.ldx = ldx; g.static_S = static_S;
+    g.q_codes = q.codes; g.q_ldc = q.ld_codes; g.q_scales = q.scales; g.q_lds = q.ld_scales; g.q_S = q.tensor_scale;
+    g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
+    g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
+    g.y = y; g.yt = yt; g.ldy = ldy;
+    g.header = header; g.scratch = scratch; g.scratch_bytes = scratch_bytes;
+    g.spin_limit = spin_limit();
+    const hipError_t e = launch_decode(g, st);
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,10 +170,10 @@ extern "C" {
 size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S) {
     if (M < 0 || N < 0 || K < 0 || S < 0) return 0;
     switch (op) {
-        case 0: return quant_ws(M);
-        case 1: return tensor_ws(M, K) + quant_ws(M) + gemm_ws(M, N, K, 0);
-        case 2: return tensor_ws(M, K + S) + quant_ws(M) + gemm_ws(M, N, K, S);
-        case 3: return up((size_t)std::max<int64_t>(M, 1) * sizeof(float), kAlign);
+        case 0: return kHeaderBytes + quant_ws(M);
+        case 1: return kHeaderBytes + tensor_ws(M, K) + quant_ws(M) + gemm_ws(M, N, K, 0);
+        case 2: return kHeaderBytes + tensor_ws(M, K + S) + quant_ws(M) + gemm_ws(M, N, K, S);
+        case 3: return kHeaderBytes + up((size_t)std::max<int64_t>(M, 1) * sizeof(float), kAlign);
         default: return 0;
     }
 }
@@ -161,7 +187,7 @@ nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, i
     CHECK(check_tensor(out, rows, K_in + S));
     const size_t need = nvfp4_workspace_size(0, rows, 0, K_in, S);
     if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
-    Carver c{static_cast<uint8_t *>(ws), ws_bytes};
+    Carver c{static_cast<uint8_t *>(ws) + kHeaderBytes, ws_bytes - kHeaderBytes};
     float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
     float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(rows, 1) * sizeof(float)));
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
@@ -184,32 +210,31 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
     if (ldy < N) return NVFP4_ERR_SHAPE;
     if (a_q) CHECK(check_tensor(a_q, M, K));
     else CHECK(check_x(x, xt, M, K, ldx));
-    if (M > 0 && N > 0 && K == 0 && !a_q) {
-        // empty contraction: y = 0 through the tiled path with an all-zero operand
-        a_q = w;  // any K == 0 tensor works: nothing of it is read
-    }
-    const size_t need = a_q ? gemm_ws(M, N, K, 0) : nvfp4_workspace_size(1, M, N, K, 0);
-    if (need && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    const size_t need = nvfp4_workspace_size(1, M, N, K, 0);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (M == 0 || N == 0) return NVFP4_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    Carver c{static_cast<uint8_t *>(ws), ws_bytes};
+    unsigned *header = static_cast<unsigned *>(ws);
+    Carver c{static_cast<uint8_t *>(ws) + kHeaderBytes, ws_bytes - kHeaderBytes};
     nvfp4_tensor aq;
     if (a_q) {
         aq = *a_q;
     } else {
         aq.rows = M; aq.K = K; aq.ld_codes = ldc_for(K); aq.ld_scales = lds_for(K);
-        aq.codes = c.take((size_t)(M * aq.ld_codes));
-        aq.scales = c.take((size_t)(M * aq.ld_scales));
+        aq.codes = c.take((size_t)std::max<int64_t>(M * aq.ld_codes, 1));
+        aq.scales = c.take((size_t)std::max<int64_t>(M * aq.ld_scales, 1));
         aq.tensor_scale = reinterpret_cast<float *>(c.take(sizeof(float)));
-        float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
-        float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(M, 1) * sizeof(float)));
-        if (!c.ok) return NVFP4_ERR_WORKSPACE;
-        CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, st));
     }
-    const size_t pb = gemm_ws(M, N, K, 0);
-    uint8_t *part = pb ? c.take(pb) : nullptr;
+    float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
+    float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(M, 1) * sizeof(float)));
+    const size_t sb = gemm_ws(M, N, K, 0);
+    uint8_t *scratch = sb ? c.take(sb) : nullptr;
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
-    return enqueue_gemm(aq, *w, M, K, 0, y, yt, ldy, part, pb, st);
+    const bool skinny = M <= kSkinnyMaxM && K > 0;
+    if (!a_q && skinny && decode_can_fuse(M, N, K, 0))
+        return enqueue_fused(x, xt, ldx, nullptr, aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
+    if (!a_q) CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, st));
+    return enqueue_gemm(aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
 }
 
 nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int64_t ldx,
@@ -230,26 +255,31 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
     if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
     if (M == 0) return NVFP4_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    Carver c{static_cast<uint8_t *>(ws), ws_bytes};
+    unsigned *header = static_cast<unsigned *>(ws);
+    Carver c{static_cast<uint8_t *>(ws) + kHeaderBytes, ws_bytes - kHeaderBytes};
     nvfp4_tensor aq;
     if (a_aug_out) {
         aq = *a_aug_out;
         c.take(tensor_ws(M, K + S) - kAlign);
     } else {
         aq.rows = M; aq.K = K + S; aq.ld_codes = ldc_for(K + S); aq.ld_scales = lds_for(K + S);
-        aq.codes = c.take((size_t)(M * aq.ld_codes));
-        aq.scales = c.take((size_t)(M * aq.ld_scales));
+        aq.codes = c.take((size_t)std::max<int64_t>(M * aq.ld_codes, 1));
+        aq.scales = c.take((size_t)std::max<int64_t>(M * aq.ld_scales, 1));
         aq.tensor_scale = reinterpret_cast<float *>(c.take(sizeof(float)));
     }
     float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
     float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(M, 1) * sizeof(float)));
+    const size_t sb = gemm_ws(M, N, K, S);
+    uint8_t *scratch = sb ? c.take(sb) : nullptr;
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
+    const bool plain = !opts || (!opts->gamma && !opts->perm);
+    const bool skinny = M <= kSkinnyMaxM && K > 0;
+    if (N > 0 && plain && skinny && decode_can_fuse(M, N, K, S))
+        return enqueue_fused(x, xt, ldx, opts ? opts->static_tensor_scale : nullptr, aq, *w, M, K, S, y, yt, ldy,
+                             header, scratch, sb, st);
     CHECK(enqueue_quantize(x, xt, M, K, ldx, opts, aq, partials, rscale, st));
     if (N == 0) return NVFP4_OK;
-    const size_t pb = gemm_ws(M, N, K, S);
-    uint8_t *part = pb ? c.take(pb) : nullptr;
-    if (!c.ok) return NVFP4_ERR_WORKSPACE;
-    return enqueue_gemm(aq, *w, M, K, S, y, yt, ldy, part, pb, st);
+    return enqueue_gemm(aq, *w, M, K, S, y, yt, ldy, header, scratch, sb, st);
 }
 
 nvfp4_status nvfp4_channel_absmax(const void *x, int xt, int64_t rows, int64_t K, int64_t ldx,
@@ -259,12 +289,12 @@ nvfp4_status nvfp4_channel_absmax(const void *x, int xt, int64_t rows, int64_t K
     if (!absmax_out) return NVFP4_ERR_NULL;
     if (gamma && !aligned(gamma, 16)) return NVFP4_ERR_ALIGN;
     if (gamma && !(eps >= 0.0f)) return NVFP4_ERR_SHAPE;
-    if (gamma && (!ws || ws_bytes < nvfp4_workspace_size(3, rows, 0, K, 0))) return NVFP4_ERR_WORKSPACE;
+    if (!ws || ws_bytes < nvfp4_workspace_size(3, rows, 0, K, 0)) return NVFP4_ERR_WORKSPACE;
     if (K == 0) return NVFP4_OK;
     ChannelAbsmaxLaunch cl;
     cl.x = x; cl.xt = xt; cl.rows = rows; cl.K = K; cl.ldx = ldx;
     cl.gamma = static_cast<const uint16_t *>(gamma); cl.eps = eps;
-    cl.rscale = static_cast<float *>(ws); cl.out = absmax_out;
+    cl.rscale = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + kHeaderBytes); cl.out = absmax_out;
     hipError_t e = launch_channel_absmax(cl, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }

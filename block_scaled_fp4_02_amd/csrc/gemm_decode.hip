@@ -1,0 +1,485 @@
+// gemm_decode.hip -- decode-shaped W4A4 product (M <= 32) in one launch, gfx950.
+//
+// y[m][n] = S_a S_w sum_k e(a)d(a) e(w)d(w)            (ARCQuant article, section 3.1)
+// plus the residue columns of the augmented-K product (ARCQuant sections
+// 3.1-3.2; ResServe abstract: the residue contribution is computed in the
+// spare capacity of the narrow product and combined on chip).
+//
+// At small M the product is bound by streaming the packed weights once (the
+// small-batch decode kernel discussion of the ReSET page on zingnex.cn,
+// section "CUDA内核优化"). The whole weight of a call (<= ~40 MB) fits in
+// flight across the chip's waves, so the kernel is organized around issuing
+// every weight load as early as possible and doing everything else -- the
+// activation quantization, the operand decode, the split-K combine -- while
+// those loads are in flight, in a single launch:
+//
+//  phase 0  each wave issues the loads of its first (up to 4) weight items
+//           (16 rows x 512 columns: 4 x 16 B codes + 8 B scales per lane);
+//  phase 1  (raw activations only) the grid quantizes X cooperatively: each
+//           workgroup takes 1/G of X's 16-element blocks, publishes its
+//           |x| maximum, waits for all G (grid-wide counter), derives
+//           S = amax / 2688, encodes its blocks (and their residue blocks)
+//           into the quantized-activation buffer, publishes, and waits again;
+//  phase 2  the workgroup decodes the activation operand of its K range
+//           into LDS (f16 e*d, exact) in v_mfma_f32_16x16x32_f16 A-operand
+//           lane order;
+//  phase 3  waves decode weight items in registers and run the MFMAs,
+//           refilling the 4-item ring as they go; residue columns reuse the
+//           decoded weight registers for a second MFMA;
+//  phase 4  with more than one K range, partial tiles go to the workspace
+//           and the last-arriving workgroup of each tile group sums them in
+//           fixed order (deterministic) and writes y.
+//
+// Grid-wide waits need every workgroup resident; the host sizes the grid from
+// the occupancy query. Each wait is bounded: past the spin limit a workgroup
+// computes what it waited for from X itself (same arithmetic, same result),
+// so no wait can hang. Counters live in the caller's workspace, start at zero
+// and are returned to zero by the last workgroup of each call.
+#include "internal.h"
+#include "nvfp4_device.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 4;
+constexpr int64_t kMaxTileCounters = kHeaderCounters - 4;
+
+struct DArgs {
+    const void *x; int x_bf16; int64_t ldx;   // raw activations (fused quantize) or nullptr
+    const float *static_S;
+    uint8_t *q_codes; int64_t q_ldc;          // quantized activations [M][K + res]
+    uint8_t *q_scales; int64_t q_lds;
+    float *q_S;
+    const uint8_t *w_codes; int64_t w_ldc;
+    const uint8_t *w_scales; int64_t w_lds;
+    const float *w_S;
+    int64_t M, N, K, res_cols;
+    void *y; int yt; int64_t ldy;
+    float *partials;
+    float *amax_slots;                         // G floats
+    unsigned *counters;                        // [0] amax published [1] codes published [2] done
+    unsigned *tile_cnt;                        // Q counters
+    int U, P, T, tw, G;
+    int64_t NT;
+    unsigned spin_limit;
+};
+
+struct WLoad {
+    uint4 c[4];
+    uint2 s;
+};
+
+__device__ inline void load_w(const DArgs &a, int64_t n, int64_t kb, int g, WLoad &w) {
+    const uint8_t *crow = a.w_codes + n * a.w_ldc;
+    const uint8_t *srow = a.w_scales + n * a.w_lds;
+    const int64_t k0 = kb + 128 * g;
+    if (k0 + 128 <= a.K) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(crow + k0 / 2);
+        w.c[0] = p[0]; w.c[1] = p[1]; w.c[2] = p[2]; w.c[3] = p[3];
+        w.s = *reinterpret_cast<const uint2 *>(srow + k0 / 16);
+    } else {
+        uint32_t sc[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t ki = k0 + 32 * i;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (ki + 32 <= a.K) {
+                v = *reinterpret_cast<const uint4 *>(crow + ki / 2);
+            } else if (ki + 16 <= a.K) {
+                const uint2 h = *reinterpret_cast<const uint2 *>(crow + ki / 2);
+                v.x = h.x; v.y = h.y;
+            }
+            w.c[i] = v;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int64_t kk = ki + 16 * b;
+                if (kk + 16 <= a.K) sc[(2 * i + b) >> 2] |= (uint32_t)srow[kk / 16] << (8 * ((2 * i + b) & 3));
+            }
+        }
+        w.s = make_uint2(sc[0], sc[1]);
+    }
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ inline float block_max(float v, float *sh) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
+    return r;
+}
+
+// Wait until counter >= target (thread 0 polls, bounded); returns true on success.
+__device__ inline bool grid_wait(unsigned *counter, unsigned target, unsigned limit, int *sh_flag) {
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        unsigned it = 0;
+        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++it > limit) { ok = 0; break; }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        *sh_flag = ok;
+    }
+    __syncthreads();
+    const bool ok = *sh_flag != 0;
+    __threadfence();                       // acquire: see what the publishers wrote
+    return ok;
+}
+
+// Publish: every thread's prior stores reach agent scope, then one increment.
+__device__ inline void grid_signal(unsigned *counter) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(counter, 1u);
+}
+
+// Tensor scale from the raw activations (slow path, every workgroup alone).
+__device__ inline float scale_from_x(const DArgs &a, float *sh) {
+    const int64_t KB = a.K / 16, NB = a.M * KB;
+    float m = 0.0f;
+    for (int64_t b = threadIdx.x; b < NB; b += kThreads) {
+        const int64_t row = b / KB, blk = b - row * KB;
+        float v[16];
+        load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+    m = block_max(m, sh);
+    return m > 0.0f ? m / 2688.0f : 1.0f;
+}
+
+// 8 codes + scale of the quantized activation at (row m, column k, k % 8 == 0),
+// either read from the quantized buffer or, on the slow path, re-encoded from X.
+// Residue columns are k >= K (residue of column k - K).
+__device__ inline half8 act_slot(const DArgs &a, int64_t m, int64_t k, bool from_x, float S) {
+    if (!from_x) {
+        const uint32_t cw = *reinterpret_cast<const uint32_t *>(a.q_codes + m * a.q_ldc + k / 2);
+        const uint32_t sb = a.q_scales[m * a.q_lds + k / 16];
+        return decode8(cw, scale_pair(sb));
+    }
+    const bool res = k >= a.K;
+    const int64_t kk = res ? k - a.K : k;
+    float v[16];
+    load16_any(a.x, a.x_bf16, m * a.ldx + (kk & ~(int64_t)15), v);
+    uint32_t cw[2];
+    float d;
+    const float t = 6.0f * S;
+    uint32_t db = encode_block(v, S, t, cw, d);
+    if (res) {
+        float r[16];
+        block_residue(v, cw, d, S, r);
+        db = encode_block(r, S, t, cw, d);
+    }
+    return decode8(cw[(kk >> 3) & 1], scale_pair(db));
+}
+
+template <int MT, bool RES, bool FUSED>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
+    extern __shared__ half8 lds_a[];          // [U][16][MT][64] (+ residue copy)
+    __shared__ float sh_red[kWaves];
+    __shared__ int sh_flag;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int p = blockIdx.x % a.P;
+    const int64_t q = blockIdx.x / a.P;
+    const int64_t kbeg = (int64_t)p * a.U * 512;
+    const int64_t kend = kbeg + (int64_t)a.U * 512 < a.K ? kbeg + (int64_t)a.U * 512 : a.K;
+    const int units = (int)((kend - kbeg + 511) / 512);
+    const int64_t rend = RES ? (a.res_cols < kend ? a.res_cols : kend) : kbeg;
+    const int res_units = RES ? (rend > kbeg ? (int)((rend - kbeg + 511) / 512) : 0) : 0;
+    const int slots = a.U * 16 * MT * 64;
+
+    // ---- phase 0: this wave's weight items (tile-major, then unit) into the ring
+    const int64_t t_lo = q * a.T, t_hi = (q + 1) * a.T < a.NT ? (q + 1) * a.T : a.NT;
+    const int64_t t_first = t_lo + wave;
+    const int ntiles = t_first < t_hi ? (int)((t_hi - t_first + kWaves - 1) / kWaves) : 0;
+    const int nitems = ntiles * units;
+    auto item_row = [&](int it) -> int64_t {
+        const int64_t n = 16 * (t_first + (int64_t)(it / units) * kWaves) + r16;
+        return n < a.N ? n : a.N - 1;
+    };
+    WLoad ring[kRing];
+#pragma unroll
+    for (int s = 0; s < kRing; ++s)
+        if (s < nitems) load_w(a, item_row(s), kbeg + 512 * (s % units), g, ring[s]);
+
+    // ---- phase 1: cooperative activation quantization
+    bool from_x = false;
+    float S = 0.0f;
+    if (FUSED) {
+        const int64_t KB = a.K / 16, NB = a.M * KB;
+        const int64_t b0 = (int64_t)blockIdx.x * NB / a.G, b1 = ((int64_t)blockIdx.x + 1) * NB / a.G;
+        const int64_t mine = b0 + threadIdx.x;           // host guarantees b1 - b0 <= kThreads
+        const bool have = mine < b1;
+        float v[16];
+        float lmax = 0.0f;
+        int64_t row = 0, blk = 0;
+        if (have) {
+            row = mine / KB; blk = mine - row * KB;
+            load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
+        }
+        if (a.static_S) {
+            S = *a.static_S;
+        } else {
+            lmax = block_max(lmax, sh_red);
+            if (threadIdx.x == 0) a.amax_slots[blockIdx.x] = lmax;
+            grid_signal(&a.counters[0]);
+            if (grid_wait(&a.counters[0], (unsigned)a.G, a.spin_limit, &sh_flag)) {
+                float m = 0.0f;
+                for (int i = threadIdx.x; i < a.G; i += kThreads) m = fmaxf(m, a.amax_slots[i]);
+                m = block_max(m, sh_red);
+                S = m > 0.0f ? m / 2688.0f : 1.0f;
+            } else {
+                S = scale_from_x(a, sh_red);
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) *a.q_S = S;
+        if (have) {
+            const float t = 6.0f * S;
+            uint32_t cw[2];
+            float d;
+            const uint32_t db = encode_block(v, S, t, cw, d);
+            *reinterpret_cast<uint2 *>(a.q_codes + row * a.q_ldc + 8 * blk) = make_uint2(cw[0], cw[1]);
+            a.q_scales[row * a.q_lds + blk] = (uint8_t)db;
+            if (RES && 16 * blk < a.res_cols) {
+                float r[16];
+                block_residue(v, cw, d, S, r);
+                uint32_t rc[2];
+                float dr;
+                const uint32_t rdb = encode_block(r, S, t, rc, dr);
+                *reinterpret_cast<uint2 *>(a.q_codes + row * a.q_ldc + 8 * (KB + blk)) = make_uint2(rc[0], rc[1]);
+                a.q_scales[row * a.q_lds + KB + blk] = (uint8_t)rdb;
+            }
+        }
+        grid_signal(&a.counters[1]);
+        from_x = !grid_wait(&a.counters[1], (unsigned)a.G, a.spin_limit, &sh_flag);
+    }
+
+    // ---- phase 2: activation operand of this K range into LDS
+    for (int s = threadIdx.x; s < (units + res_units) * 16 * MT * 64; s += kThreads) {
+        const bool is_res = s >= units * 16 * MT * 64;
+        const int s2 = is_res ? s - units * 16 * MT * 64 : s;
+        const int l = s2 & 63, mt = (s2 >> 6) % MT, ij = ((s2 >> 6) / MT) & 15, u = ((s2 >> 6) / MT) >> 4;
+        const int m = 16 * mt + (l & 15), gg = l >> 4, i = ij >> 2, j = ij & 3;
+        const int64_t k = kbeg + 512 * u + 128 * gg + 32 * i + 8 * j;
+        half8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (m < a.M && k < (is_res ? rend : kend)) v = act_slot(a, m, is_res ? a.K + k : k, from_x, S);
+        lds_a[(is_res ? slots : 0) + s2] = v;
+    }
+    __syncthreads();
+
+    // ---- phase 3: decode weights, MFMA
+    const float scale = (FUSED ? S : a.q_S[0]) * a.w_S[0];
+    float4v acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+    for (int base = 0; base < nitems; base += kRing) {
+#pragma unroll
+        for (int s = 0; s < kRing; ++s) {
+            const int it = base + s;
+            if (it < nitems) {
+                const int u = it % units;
+                const half8 *abase = lds_a + (size_t)u * 16 * MT * 64 + lane;
+                const bool res_u = RES && u < res_units;
+                const WLoad cur = ring[s];
+                if (it + kRing < nitems)
+                    load_w(a, item_row(it + kRing), kbeg + 512 * ((it + kRing) % units), g, ring[s]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t sw = (i < 2) ? cur.s.x : cur.s.y;
+                    const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
+                    const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
+                    const uint32_t cws[4] = {cur.c[i].x, cur.c[i].y, cur.c[i].z, cur.c[i].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+                            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64], b,
+                                                                             acc[mt], 0, 0, 0);
+                            if (res_u)
+                                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, acc[mt], 0, 0, 0);
+                        }
+                    }
+                }
+                if (u == units - 1) {
+                    // tile done: lane holds rows 16 mt + 4 g + e of column n
+                    const int64_t n = 16 * (t_first + (int64_t)(it / units) * kWaves) + r16;
+                    if (n < a.N) {
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int64_t m = 16 * mt + 4 * g + e;
+                                if (m < a.M) {
+                                    if (a.P == 1) {
+                                        const float v = acc[mt][e] * scale;
+                                        if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
+                                        else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
+                                    } else {
+                                        a.partials[((int64_t)p * a.M + m) * a.N + n] = acc[mt][e];
+                                    }
+                                }
+                            }
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+                }
+            }
+        }
+    }
+
+    // ---- phase 4: split-K combine by the last workgroup of the tile group
+    if (a.P > 1) {
+        __threadfence();                   // partial tiles reach agent scope
+        __syncthreads();
+        if (threadIdx.x == 0) sh_flag = atomicAdd(&a.tile_cnt[q], 1u) == (unsigned)a.P - 1;
+        __syncthreads();
+        if (sh_flag) {
+            __threadfence();               // acquire the other ranges' partials
+            const int64_t ncols = (t_hi - t_lo) * 16;
+            for (int64_t idx = threadIdx.x; idx < a.M * ncols; idx += kThreads) {
+                const int64_t m = idx / ncols, n = 16 * t_lo + (idx - m * ncols);
+                if (n >= a.N) continue;
+                float sum = 0.0f;
+                for (int pp = 0; pp < a.P; ++pp) sum += a.partials[((int64_t)pp * a.M + m) * a.N + n];
+                const float v = sum * scale;
+                if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
+                else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(&a.tile_cnt[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // ---- phase 5: the last workgroup of a fused call returns the grid counters to zero
+    if (FUSED) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned old = atomicAdd(&a.counters[2], 1u);
+            if (old == (unsigned)a.G - 1) {
+                __hip_atomic_store(&a.counters[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.counters[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.counters[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+struct Plan { int MT, U, P, T, tw, G; int64_t NT, Q; size_t lds; bool fused_ok; };
+
+int max_resident(const void *fn, size_t lds) {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 1;                       // no device: size conservatively, do not cache
+    }
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kThreads, lds) != hipSuccess || per < 1) per = 1;
+    return per * cus;
+}
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t res_cols, int cap) {
+    Plan pl;
+    pl.MT = M <= 16 ? 1 : 2;
+    const bool res = res_cols > 0;
+    const int umax = (pl.MT == 1 ? 4 : 2) / (res ? 2 : 1) > 0 ? (pl.MT == 1 ? 4 : 2) / (res ? 2 : 1) : 1;
+    pl.NT = (N + 15) / 16;
+    const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
+    // pick (U, tw): fewest items per wave that keeps the grid resident, preferring fewer K ranges
+    int bestU = 1, besttw = 1;
+    double best = 1e30;
+    for (int U = 1; U <= umax; U *= 2) {
+        for (int tw = 1; tw <= 8; ++tw) {
+            const int64_t P = (ku + U - 1) / U, Q = (pl.NT + 4 * tw - 1) / (4 * tw);
+            const int64_t G = P * Q;
+            if (G > cap - cap / 8 || Q > kMaxTileCounters) continue;
+            const int items = tw * (int)(U < ku ? U : ku);
+            // cost: items per wave (time per wave), plus a small charge per K range (partials)
+            const double cost = items + 0.15 * (double)P + (G < 192 ? 4.0 : 0.0);
+            if (cost < best) { best = cost; bestU = U; besttw = tw; }
+        }
+    }
+    pl.U = bestU > ku ? (int)ku : bestU;
+    pl.tw = besttw;
+    pl.T = 4 * pl.tw;
+    pl.P = (int)((ku + pl.U - 1) / pl.U);
+    pl.Q = (pl.NT + pl.T - 1) / pl.T;
+    pl.G = (int)(pl.P * pl.Q);
+    pl.lds = (size_t)pl.U * 16 * pl.MT * 64 * sizeof(half8) * (res ? 2 : 1);
+    pl.fused_ok = pl.G <= cap - cap / 8 && pl.Q <= kMaxTileCounters &&
+                  (M * (K / 16)) <= (int64_t)pl.G * kThreads;
+    return pl;
+}
+
+const void *kernel_ptr(int MT, bool res, bool fused) {
+#define KP(A, B, C) reinterpret_cast<const void *>(&decode_kernel<A, B, C>)
+    if (MT == 1) return res ? (fused ? KP(1, true, true) : KP(1, true, false)) : (fused ? KP(1, false, true) : KP(1, false, false));
+    return res ? (fused ? KP(2, true, true) : KP(2, true, false)) : (fused ? KP(2, false, true) : KP(2, false, false));
+#undef KP
+}
+
+Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
+    const int MT = M <= 16 ? 1 : 2;
+    const bool res = res_cols > 0;
+    // capacity with the largest LDS the plan may choose
+    const size_t lds_max = (size_t)((MT == 1 ? 4 : 2)) * 16 * MT * 64 * 16;
+    const int cap = max_resident(kernel_ptr(MT, res, true), lds_max);
+    return make_plan(M, N, K, res_cols, cap);
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
+    const Plan pl = plan_for(M, N, K, res_cols);
+    const size_t part = pl.P > 1 ? (size_t)pl.P * M * N * sizeof(float) : 0;
+    return part + ((size_t)pl.G * sizeof(float) + 255) / 256 * 256;
+}
+
+bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
+    return plan_for(M, N, K, res_cols).fused_ok;
+}
+
+hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
+    const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols);
+    const bool fused = g.x != nullptr;
+    if (fused && !pl.fused_ok) return hipErrorInvalidValue;
+    DArgs a;
+    a.x = g.x; a.x_bf16 = g.x_bf16; a.ldx = g.ldx; a.static_S = g.static_S;
+    a.q_codes = g.q_codes; a.q_ldc = g.q_ldc; a.q_scales = g.q_scales; a.q_lds = g.q_lds; a.q_S = g.q_S;
+    a.w_codes = g.w_codes; a.w_ldc = g.w_ldc; a.w_scales = g.w_scales; a.w_lds = g.w_lds; a.w_S = g.w_S;
+    a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
+    a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
+    // counters live in the zero-kept header; amax slots and partials in the scratch region
+    if (!g.header || !g.scratch || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols))
+        return hipErrorInvalidValue;
+    if (pl.Q > kMaxTileCounters) return hipErrorInvalidValue;
+    a.counters = g.header;
+    a.tile_cnt = g.header + 4;
+    a.amax_slots = static_cast<float *>(g.scratch);
+    a.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(g.scratch) +
+                                           ((size_t)pl.G * sizeof(float) + 255) / 256 * 256);
+    a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.G = pl.G; a.NT = pl.NT;
+    a.spin_limit = g.spin_limit;
+    const bool res = g.res_cols > 0;
+    const void *fn = kernel_ptr(pl.MT, res, fused);
+    void *args[] = {&a};
+    return hipLaunchKernel(fn, dim3(pl.G), dim3(kThreads), args, pl.lds, st);
+}
+
+}  // namespace nvfp4

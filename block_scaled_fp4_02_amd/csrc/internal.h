@@ -36,23 +36,34 @@ struct ChannelAbsmaxLaunch {
 };
 hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 
-// Decode-shaped (small M) product; A is a canonical NVFP4 tensor whose first K
-// columns are the main part and, when res_cols > 0, columns [K, K + res_cols)
-// hold the residue of columns [0, res_cols).
-struct SkinnyLaunch {
-    const uint8_t *a_codes; int64_t a_ldc;
-    const uint8_t *a_scales; int64_t a_lds;
-    const float *a_S;
+// Every workspace starts with a header of counters used by the grid-wide
+// waits and the split-K combine. It must be zero before the first call on a
+// workspace; every call leaves it zero.
+constexpr size_t kHeaderBytes = 8192;
+constexpr int64_t kHeaderCounters = (int64_t)(kHeaderBytes / sizeof(unsigned));
+
+// Decode-shaped (M <= 32) product in one launch. With x != nullptr the raw
+// activations are quantized inside the kernel into q_* (canonical NVFP4 layout,
+// K + res_cols columns: the residue of columns [0, res_cols) after column K);
+// with x == nullptr q_* already hold them.
+struct DecodeLaunch {
+    const void *x; int x_bf16; int64_t ldx;
+    const float *static_S;
+    uint8_t *q_codes; int64_t q_ldc;
+    uint8_t *q_scales; int64_t q_lds;
+    float *q_S;
     const uint8_t *w_codes; int64_t w_ldc;
     const uint8_t *w_scales; int64_t w_lds;
     const float *w_S;
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
-    float *partials;                        // split-K partial sums (workspace)
-    size_t partial_bytes;
+    unsigned *header;                       // kHeaderBytes, zero-kept
+    void *scratch; size_t scratch_bytes;    // decode_workspace_bytes()
+    unsigned spin_limit;                    // bound on each grid-wide wait (polls)
 };
-size_t skinny_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t res_cols);
-hipError_t launch_skinny(const SkinnyLaunch &g, hipStream_t st);
+size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t res_cols);
+bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols);
+hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st);
 
 // Large-M tiled matrix-core product (no residue columns in this path unless
 // res_cols > 0 is requested through the same tensor layout).

@@ -79,4 +79,66 @@ __device__ inline half2v scale_pair(uint32_t b) {
     return __builtin_bit_cast(half2v, v);
 }
 
+// Quantize one block of 16 values against tensor scale S (t = 6 S, both FP32):
+// returns the E4M3 byte, fills two dwords of packed codes (low nibble first)
+// and sets d to the decoded block scale. FP32 order: sf = a_b / t,
+// d = E4M3(sf), s = d * S, r = 1 / s (0 when s == 0), q = x * r.
+// Callers compile with contraction off so each step rounds once.
+__device__ inline uint32_t encode_block(const float *v, float S, float t, uint32_t *cw, float &d) {
+    float ab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+    const float sf = ab / t;
+    const uint32_t db = e4m3_rne_sat(sf);
+    d = e4m3_to_float(db);
+    const float s = d * S;
+    const float rcp = (s > 0.0f) ? 1.0f / s : 0.0f;
+    cw[0] = 0; cw[1] = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float q = v[i] * rcp;
+        const uint32_t c = e2m1_rne_sat(fabsf(q)) | ((f2u(v[i]) >> 31) << 3);
+        cw[i >> 3] |= c << (4 * (i & 7));
+    }
+    return db;
+}
+
+// Residue of a block: R = x - fl(fl(e d) S) for the 16 values and their codes.
+__device__ inline void block_residue(const float *v, const uint32_t *cw, float d, float S, float *r) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t c = (cw[i >> 3] >> (4 * (i & 7))) & 15u;
+        const float ed = e2m1_to_float(c) * d;
+        const float deq = ed * S;
+        r[i] = v[i] - deq;
+    }
+}
+
+// 16 consecutive elements (bf16 when is_bf16, else f32) starting at element off.
+__device__ inline void load16_any(const void *base, bool is_bf16, int64_t off, float *v) {
+    if (is_bf16) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+        const uint4 a = p[0], b = p[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = u2f(w[i] << 16);
+            v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 q = p[i];
+            v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+        }
+    }
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = f2u(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
 }  // namespace nvfp4

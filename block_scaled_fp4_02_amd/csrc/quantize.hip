@@ -180,27 +180,6 @@ __device__ inline float tensor_scale(const QArgs &a, float *sh) {
     return m > 0.0f ? m / 2688.0f : 1.0f;
 }
 
-// Encode one block of 16 values against tensor scale S (t = 6 S): returns the
-// E4M3 byte, fills two dwords of packed codes, and d (the decoded scale).
-__device__ inline uint32_t encode_block(const float *v, float S, float t, uint32_t *cw, float &d) {
-    float ab = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
-    const float sf = ab / t;
-    const uint32_t db = e4m3_rne_sat(sf);
-    d = e4m3_to_float(db);
-    const float s = d * S;
-    const float rcp = (s > 0.0f) ? 1.0f / s : 0.0f;
-    cw[0] = 0; cw[1] = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float q = v[i] * rcp;
-        const uint32_t c = e2m1_rne_sat(fabsf(q)) | ((f2u(v[i]) >> 31) << 3);
-        cw[i >> 3] |= c << (4 * (i & 7));
-    }
-    return db;
-}
-
 // Quantize `nb` (1..4) blocks of row `row` starting at column col0 from v[64].
 __device__ inline void process_group(const QArgs &a, const float *v, int nb, int64_t row, int64_t col0,
                                      float S, float t) {
@@ -232,13 +211,7 @@ __device__ inline void process_group(const QArgs &a, const float *v, int nb, int
     for (int b = 0; b < 4; ++b) {
         if (b < nb && col0 + 16 * b < a.res_cols) {
             float rv[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t c = (cw[2 * b + (i >> 3)] >> (4 * (i & 7))) & 15u;
-                const float ed = e2m1_to_float(c) * dblk[b];
-                const float deq = ed * S;
-                rv[i] = v[16 * b + i] - deq;
-            }
+            block_residue(v + 16 * b, cw + 2 * b, dblk[b], S, rv);
             uint32_t rc[2];
             float dr;
             const uint32_t rdb = encode_block(rv, S, t, rc, dr);

@@ -133,11 +133,14 @@ _ws = {}
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A per-(device, stream) scratch buffer, grown on demand (plumbing, not compute)."""
+    """A per-(device, stream) workspace, grown on demand (plumbing, not compute).
+
+    Zero-filled when allocated: its first 8 KiB hold the library's synchronization
+    counters, which must start at zero and which every call leaves at zero."""
     key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        buf = torch.zeros(max(nbytes, 16384), dtype=torch.uint8, device=device)
         _ws[key] = buf
     return buf
 

@@ -30,7 +30,10 @@
  *    enqueues work on it and returns without synchronizing.
  *  - The caller owns and allocates every buffer, including the workspace
  *    (size from nvfp4_workspace_size). The library never allocates device
- *    memory and keeps no device state between calls.
+ *    memory. The first 8 KiB of every workspace hold synchronization counters
+ *    (grid-wide waits of the one-launch decode product, split-K combine): they
+ *    must be zero before the first call on a workspace, and every call leaves
+ *    them zero. A workspace must not be used by two calls at the same time.
  *  - Argument errors are detected before anything is enqueued; the call then
  *    returns a status != NVFP4_OK and leaves every output untouched. Launch
  *    failures return NVFP4_ERR_HIP; nvfp4_last_error() gives the HIP text.
@@ -109,8 +112,9 @@ nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, i
  * dtype xt, leading dimension ldx, quantized inside the call with a dynamic
  * tensor scale) is non-NULL. w is N x K. y is M x N with leading dimension ldy,
  * dtype yt (FP32, or BF16 rounded to nearest even).
- * Small M (<= 32) streams the packed weights once with wide loads; larger M
- * uses the tiled matrix-core path. K == 0 gives y = 0. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
+ * Small M (<= 32) runs as one launch that quantizes x cooperatively across
+ * the grid while the packed weights stream in with wide loads; larger M
+ * quantizes x first and uses the tiled matrix-core path. K == 0 gives y = 0. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
                         int64_t M, int64_t K, int64_t ldx,
                         const nvfp4_tensor *w, void *y, int yt, int64_t ldy,

@@ -217,3 +217,25 @@ def test_graph_replay_matches_eager(nv):
         torch.cuda.synchronize()
         assert torch.equal(y, eager) and torch.equal(yr, eager_r), i
         assert other.shape == (2, 14336)
+
+
+@pytest.mark.parametrize("shape_idx", [0, 1])
+def test_wait_fallback_identical(nv, orc, shape_idx, monkeypatch):
+    """Force every grid-wide wait of the one-launch decode product to give up at once
+    (spin limit 0, set from the host): workgroups then recompute the tensor scale and
+    their activation operand from X themselves. Results must equal the normal path's."""
+    x, w = inputs.decode_sweep(shape_idx)
+    xd = x.to(DEV)
+    wq = nv.quantize(w.to(DEV))
+    y0 = nv.gemm(xd, wq).clone()
+    r0 = nv.gemm_residue(xd[:5], wq, 2048).clone()
+    torch.cuda.synchronize()
+    monkeypatch.setenv("NVFP4_SPIN_LIMIT", "0")
+    note(f"fallback path shape {shape_idx}")
+    y1 = nv.gemm(xd, wq)
+    r1 = nv.gemm_residue(xd[:5], wq, 2048)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("NVFP4_SPIN_LIMIT")
+    assert torch.equal(y0, y1) and torch.equal(r0, r1)
+    ref = orc.gemm(orc.quantize(x), orc.quantize(w))
+    assert gemm_error(y1.cpu().numpy(), ref) <= TOL
