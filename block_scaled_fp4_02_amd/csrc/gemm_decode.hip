@@ -119,28 +119,38 @@ __device__ inline float block_max(float v, float *sh) {
     return r;
 }
 
-// Wait until counter >= target (thread 0 polls, bounded); returns true on success.
+// Cross-workgroup data goes through device-coherent (sc1) accesses -- relaxed
+// agent-scope atomic loads and stores -- so no cache-wide writeback or
+// invalidate is ever needed: a publisher waits for its own stores to complete
+// (s_waitcnt vmcnt(0), which on gfx9 also waits for its earlier loads, so only
+// the waves that stored shared data wait) and then increments a counter;
+// readers poll the counter and read the data with sc1 loads.
+template <typename T>
+__device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+__device__ inline void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Every wave that stored shared data has called wait_own_stores(); count once.
+__device__ inline void grid_signal(unsigned *counter) {
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until counter >= target (thread 0 polls, bounded); true on success.
 __device__ inline bool grid_wait(unsigned *counter, unsigned target, unsigned limit, int *sh_flag) {
     if (threadIdx.x == 0) {
         int ok = 1;
         unsigned it = 0;
-        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while (ld_dev(counter) < target) {
             if (++it > limit) { ok = 0; break; }
             __builtin_amdgcn_s_sleep(2);
         }
         *sh_flag = ok;
     }
     __syncthreads();
-    const bool ok = *sh_flag != 0;
-    __threadfence();                       // acquire: see what the publishers wrote
-    return ok;
-}
-
-// Publish: every thread's prior stores reach agent scope, then one increment.
-__device__ inline void grid_signal(unsigned *counter) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(counter, 1u);
+    return *sh_flag != 0;
 }
 
 // Tensor scale from the raw activations (slow path, every workgroup alone).
@@ -161,10 +171,13 @@ __device__ inline float scale_from_x(const DArgs &a, float *sh) {
 // 8 codes + scale of the quantized activation at (row m, column k, k % 8 == 0),
 // either read from the quantized buffer or, on the slow path, re-encoded from X.
 // Residue columns are k >= K (residue of column k - K).
+template <bool COHERENT>
 __device__ inline half8 act_slot(const DArgs &a, int64_t m, int64_t k, bool from_x, float S) {
     if (!from_x) {
-        const uint32_t cw = *reinterpret_cast<const uint32_t *>(a.q_codes + m * a.q_ldc + k / 2);
-        const uint32_t sb = a.q_scales[m * a.q_lds + k / 16];
+        const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.q_codes + m * a.q_ldc + k / 2);
+        const uint8_t *sp = a.q_scales + m * a.q_lds + k / 16;
+        const uint32_t cw = COHERENT ? ld_dev(cp) : *cp;
+        const uint32_t sb = COHERENT ? (uint32_t)ld_dev(sp) : (uint32_t)*sp;
         return decode8(cw, scale_pair(sb));
     }
     const bool res = k >= a.K;
@@ -234,11 +247,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
             S = *a.static_S;
         } else {
             lmax = block_max(lmax, sh_red);
-            if (threadIdx.x == 0) a.amax_slots[blockIdx.x] = lmax;
+            if (threadIdx.x == 0) {
+                st_dev(&a.amax_slots[blockIdx.x], lmax);
+                wait_own_stores();
+            }
             grid_signal(&a.counters[0]);
             if (grid_wait(&a.counters[0], (unsigned)a.G, a.spin_limit, &sh_flag)) {
                 float m = 0.0f;
-                for (int i = threadIdx.x; i < a.G; i += kThreads) m = fmaxf(m, a.amax_slots[i]);
+                for (int i = threadIdx.x; i < a.G; i += kThreads) m = fmaxf(m, ld_dev(&a.amax_slots[i]));
                 m = block_max(m, sh_red);
                 S = m > 0.0f ? m / 2688.0f : 1.0f;
             } else {
@@ -251,18 +267,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
             uint32_t cw[2];
             float d;
             const uint32_t db = encode_block(v, S, t, cw, d);
-            *reinterpret_cast<uint2 *>(a.q_codes + row * a.q_ldc + 8 * blk) = make_uint2(cw[0], cw[1]);
-            a.q_scales[row * a.q_lds + blk] = (uint8_t)db;
+            uint32_t *cp = reinterpret_cast<uint32_t *>(a.q_codes + row * a.q_ldc + 8 * blk);
+            st_dev(cp, cw[0]);
+            st_dev(cp + 1, cw[1]);
+            st_dev(a.q_scales + row * a.q_lds + blk, (uint8_t)db);
             if (RES && 16 * blk < a.res_cols) {
                 float r[16];
                 block_residue(v, cw, d, S, r);
                 uint32_t rc[2];
                 float dr;
                 const uint32_t rdb = encode_block(r, S, t, rc, dr);
-                *reinterpret_cast<uint2 *>(a.q_codes + row * a.q_ldc + 8 * (KB + blk)) = make_uint2(rc[0], rc[1]);
-                a.q_scales[row * a.q_lds + KB + blk] = (uint8_t)rdb;
+                uint32_t *rp = reinterpret_cast<uint32_t *>(a.q_codes + row * a.q_ldc + 8 * (KB + blk));
+                st_dev(rp, rc[0]);
+                st_dev(rp + 1, rc[1]);
+                st_dev(a.q_scales + row * a.q_lds + KB + blk, (uint8_t)rdb);
             }
         }
+        if (__any(have)) wait_own_stores();      // only waves that stored shared codes
         grid_signal(&a.counters[1]);
         from_x = !grid_wait(&a.counters[1], (unsigned)a.G, a.spin_limit, &sh_flag);
     }
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
         const int m = 16 * mt + (l & 15), gg = l >> 4, i = ij >> 2, j = ij & 3;
         const int64_t k = kbeg + 512 * u + 128 * gg + 32 * i + 8 * j;
         half8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (m < a.M && k < (is_res ? rend : kend)) v = act_slot(a, m, is_res ? a.K + k : k, from_x, S);
+        if (m < a.M && k < (is_res ? rend : kend)) v = act_slot<FUSED>(a, m, is_res ? a.K + k : k, from_x, S);
         lds_a[(is_res ? slots : 0) + s2] = v;
     }
     __syncthreads();
@@ -330,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
                                         if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
                                         else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
                                     } else {
-                                        a.partials[((int64_t)p * a.M + m) * a.N + n] = acc[mt][e];
+                                        st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], acc[mt][e]);
                                     }
                                 }
                             }
@@ -344,18 +365,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
 
     // ---- phase 4: split-K combine by the last workgroup of the tile group
     if (a.P > 1) {
-        __threadfence();                   // partial tiles reach agent scope
+        wait_own_stores();                 // this wave's partial tiles are visible
         __syncthreads();
-        if (threadIdx.x == 0) sh_flag = atomicAdd(&a.tile_cnt[q], 1u) == (unsigned)a.P - 1;
+        if (threadIdx.x == 0)
+            sh_flag = __hip_atomic_fetch_add(&a.tile_cnt[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      (unsigned)a.P - 1;
         __syncthreads();
         if (sh_flag) {
-            __threadfence();               // acquire the other ranges' partials
             const int64_t ncols = (t_hi - t_lo) * 16;
             for (int64_t idx = threadIdx.x; idx < a.M * ncols; idx += kThreads) {
                 const int64_t m = idx / ncols, n = 16 * t_lo + (idx - m * ncols);
                 if (n >= a.N) continue;
                 float sum = 0.0f;
-                for (int pp = 0; pp < a.P; ++pp) sum += a.partials[((int64_t)pp * a.M + m) * a.N + n];
+                for (int pp = 0; pp < a.P; ++pp) sum += ld_dev(&a.partials[((int64_t)pp * a.M + m) * a.N + n]);
                 const float v = sum * scale;
                 if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
                 else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
@@ -369,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
     if (FUSED) {
         __syncthreads();
         if (threadIdx.x == 0) {
-            const unsigned old = atomicAdd(&a.counters[2], 1u);
+            const unsigned old = __hip_atomic_fetch_add(&a.counters[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (old == (unsigned)a.G - 1) {
                 __hip_atomic_store(&a.counters[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(&a.counters[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
