@@ -7,47 +7,56 @@
 //
 // At small M the product is bound by streaming the packed weights once (the
 // small-batch decode kernel discussion of the ReSET page on zingnex.cn,
-// section "CUDA内核优化"). The whole weight of a call (<= ~40 MB) fits in
-// flight across the chip's waves, so the kernel is organized around issuing
-// every weight load as early as possible and doing everything else -- the
-// activation quantization, the operand decode, the split-K combine -- while
-// those loads are in flight, in a single launch:
+// section "CUDA内核优化"). A call's whole weight (<= ~40 MB) fits in flight
+// across the chip, so the kernel is built around issuing every weight load at
+// once and doing everything else while those loads are in flight:
 //
-//  phase 0  each wave issues the loads of its first (up to 4) weight items
-//           (16 rows x 512 columns: 4 x 16 B codes + 8 B scales per lane);
-//  phase 1  (raw activations only) the grid quantizes X cooperatively: each
-//           workgroup takes 1/G of X's 16-element blocks, publishes its
-//           |x| maximum, waits for all G (grid-wide counter), derives
-//           S = amax / 2688, encodes its blocks (and their residue blocks)
-//           into the quantized-activation buffer, publishes, and waits again;
-//  phase 2  the workgroup decodes the activation operand of its K range
-//           into LDS (f16 e*d, exact) in v_mfma_f32_16x16x32_f16 A-operand
-//           lane order;
-//  phase 3  waves decode weight items in registers and run the MFMAs,
-//           refilling the 4-item ring as they go; residue columns reuse the
-//           decoded weight registers for a second MFMA;
-//  phase 4  with more than one K range, partial tiles go to the workspace
-//           and the last-arriving workgroup of each tile group sums them in
-//           fixed order (deterministic) and writes y.
+//  * a workgroup owns a K range of U 512-column units and T 16-row weight
+//    tiles; it has four consumer waves and one producer wave;
+//  * consumer waves issue the loads of their (tile, unit) items at once
+//    (ring of 4 items: 4 x 16 B codes + 8 B scales per lane each), wait at one
+//    barrier for the activation operand, then decode each weight item in
+//    registers (v_cvt_scalef32_pk_f16_fp4 + v_pk_mul_f16, exact) and issue 16
+//    v_mfma_f32_16x16x32_f16 per item, refilling the ring; residue columns
+//    reuse the decoded weight registers for a second MFMA;
+//  * the producer wave has no weight loads in flight, so its waits are its own
+//    (vmcnt is in order on gfx9): it quantizes the activations and writes the
+//    K range's operand into LDS as exact f16 e*d values in A-operand lane order;
+//  * with more than one K range, partial tiles go to the workspace through
+//    device-coherent stores and the last workgroup of each tile group sums
+//    them in fixed order (deterministic) and writes y.
 //
-// Grid-wide waits need every workgroup resident; the host sizes the grid from
-// the occupancy query. Each wait is bounded: past the spin limit a workgroup
-// computes what it waited for from X itself (same arithmetic, same result),
-// so no wait can hang. Counters live in the caller's workspace, start at zero
-// and are returned to zero by the last workgroup of each call.
+// Activation quantization (raw activations in the call), chosen per shape:
+//  LOCAL  X is small: every workgroup computes amax(X) itself and quantizes
+//         its own K range -- no communication at all;
+//  SYNC1  the grid agrees on amax(X) (each workgroup publishes the maximum of
+//         1/G of X, one grid-wide wait), then each quantizes its own K range;
+//  SYNC2  as SYNC1, then each workgroup quantizes 1/G of X's blocks into the
+//         quantized-activation buffer and a second wait makes them visible.
+// Cross-workgroup data moves through relaxed device-scope (sc1) loads and
+// stores; a publisher waits for its own stores (s_waitcnt vmcnt(0)) and then
+// counts. Grid-wide counters are hierarchical (16 sub-counters, then one top
+// counter) because same-address device atomics serialize, and carry a call
+// index in their upper half so they never need resetting. Every wait is
+// bounded: past the spin limit a workgroup recomputes what it waited for from
+// X itself (same arithmetic, same result), so no wait can hang.
 #include "internal.h"
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kCons = 4;                       // consumer waves
+constexpr int kThreads = 64 * (kCons + 1);     // plus one producer wave
 constexpr int kRing = 4;
-constexpr int64_t kMaxTileCounters = kHeaderCounters - 4;
+constexpr int kGroups = 16;                    // sub-counters per grid-wide wait
+constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
+constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
+
+enum Mode { MODE_PRE = 0, MODE_LOCAL = 1, MODE_SYNC1 = 2, MODE_SYNC2 = 3 };
 
 struct DArgs {
-    const void *x; int x_bf16; int64_t ldx;   // raw activations (fused quantize) or nullptr
+    const void *x; int x_bf16; int64_t ldx;   // raw activations (modes LOCAL/SYNC1/SYNC2)
     const float *static_S;
     uint8_t *q_codes; int64_t q_ldc;          // quantized activations [M][K + res]
     uint8_t *q_scales; int64_t q_lds;
@@ -57,15 +66,66 @@ struct DArgs {
     const float *w_S;
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
-    float *partials;
-    float *amax_slots;                         // G floats
-    unsigned *counters;                        // [0] amax published [1] codes published [2] done
-    unsigned *tile_cnt;                        // Q counters
-    int U, P, T, tw, G;
+    uint8_t *header;                          // zero-kept counters
+    float *amax_slots;                        // G floats
+    float *partials;                          // P x M x N floats
+    int U, P, T, tw, G, mode;
     int64_t NT;
     unsigned spin_limit;
 };
 
+template <typename T>
+__device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ inline T add_dev(T *p, T v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+__device__ inline void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// ------------------------------------------------------------ grid-wide wait
+// Counter word: upper 32 bits = call index, lower = arrivals in this call.
+struct Sync { unsigned long long *top, *sub; };
+
+__device__ inline Sync sync_at(uint8_t *header, int s) {
+    Sync y;
+    y.top = reinterpret_cast<unsigned long long *>(header + 1024 * s);
+    y.sub = reinterpret_cast<unsigned long long *>(header + 1024 * s + 64);
+    return y;
+}
+
+// One lane per workgroup: count this workgroup in; returns the call index to wait past.
+__device__ inline unsigned sync_arrive(Sync y, int G) {
+    const int NG = G < kGroups ? G : kGroups;
+    const int grp = (int)(blockIdx.x % NG);
+    const unsigned members = (unsigned)((G - grp + NG - 1) / NG);
+    const unsigned mine = (unsigned)(ld_dev(y.top) >> 32);   // cannot advance before we arrive
+    unsigned long long *sc = y.sub + 8 * grp;                 // 64 bytes apart
+    const unsigned long long old = add_dev(sc, 1ull);
+    if ((unsigned)old + 1 == members) {
+        add_dev(sc, (1ull << 32) - members);                  // next call, zero arrivals
+        const unsigned long long ot = add_dev(y.top, 1ull);
+        if ((unsigned)ot + 1 == (unsigned)NG) add_dev(y.top, (1ull << 32) - (unsigned long long)NG);
+    }
+    return mine;
+}
+
+__device__ inline bool sync_wait(Sync y, unsigned mine, unsigned limit) {
+    unsigned it = 0;
+    while ((unsigned)(ld_dev(y.top) >> 32) == mine) {
+        if (++it > limit) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+}
+
+// ------------------------------------------------------------ weight items
 struct WLoad {
     uint4 c[4];
     uint2 s;
@@ -102,105 +162,98 @@ __device__ inline void load_w(const DArgs &a, int64_t n, int64_t kb, int g, WLoa
     }
 }
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ inline float block_max(float v, float *sh) {
-    v = wave_max(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = sh[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
-    return r;
-}
-
-// Cross-workgroup data goes through device-coherent (sc1) accesses -- relaxed
-// agent-scope atomic loads and stores -- so no cache-wide writeback or
-// invalidate is ever needed: a publisher waits for its own stores to complete
-// (s_waitcnt vmcnt(0), which on gfx9 also waits for its earlier loads, so only
-// the waves that stored shared data wait) and then increments a counter;
-// readers poll the counter and read the data with sc1 loads.
-template <typename T>
-__device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-template <typename T>
-__device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-
-__device__ inline void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Every wave that stored shared data has called wait_own_stores(); count once.
-__device__ inline void grid_signal(unsigned *counter) {
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until counter >= target (thread 0 polls, bounded); true on success.
-__device__ inline bool grid_wait(unsigned *counter, unsigned target, unsigned limit, int *sh_flag) {
-    if (threadIdx.x == 0) {
-        int ok = 1;
-        unsigned it = 0;
-        while (ld_dev(counter) < target) {
-            if (++it > limit) { ok = 0; break; }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        *sh_flag = ok;
-    }
-    __syncthreads();
-    return *sh_flag != 0;
-}
-
-// Tensor scale from the raw activations (slow path, every workgroup alone).
-__device__ inline float scale_from_x(const DArgs &a, float *sh) {
+// ------------------------------------------------------------ producer wave
+// amax(X) over all rows and columns by one wave.
+__device__ inline float wave_amax_x(const DArgs &a) {
+    const int lane = threadIdx.x & 63;
     const int64_t KB = a.K / 16, NB = a.M * KB;
     float m = 0.0f;
-    for (int64_t b = threadIdx.x; b < NB; b += kThreads) {
+    for (int64_t b = lane; b < NB; b += 64) {
         const int64_t row = b / KB, blk = b - row * KB;
         float v[16];
         load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
 #pragma unroll
         for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
     }
-    m = block_max(m, sh);
-    return m > 0.0f ? m / 2688.0f : 1.0f;
+    return wave_max(m);
 }
 
-// 8 codes + scale of the quantized activation at (row m, column k, k % 8 == 0),
-// either read from the quantized buffer or, on the slow path, re-encoded from X.
-// Residue columns are k >= K (residue of column k - K).
-template <bool COHERENT>
-__device__ inline half8 act_slot(const DArgs &a, int64_t m, int64_t k, bool from_x, float S) {
-    if (!from_x) {
-        const uint32_t *cp = reinterpret_cast<const uint32_t *>(a.q_codes + m * a.q_ldc + k / 2);
-        const uint8_t *sp = a.q_scales + m * a.q_lds + k / 16;
-        const uint32_t cw = COHERENT ? ld_dev(cp) : *cp;
-        const uint32_t sb = COHERENT ? (uint32_t)ld_dev(sp) : (uint32_t)*sp;
-        return decode8(cw, scale_pair(sb));
-    }
-    const bool res = k >= a.K;
-    const int64_t kk = res ? k - a.K : k;
-    float v[16];
-    load16_any(a.x, a.x_bf16, m * a.ldx + (kk & ~(int64_t)15), v);
-    uint32_t cw[2];
-    float d;
+__device__ inline float scale_of(float amax) { return amax > 0.0f ? amax / 2688.0f : 1.0f; }
+
+// A 32-column chunk of one activation row as codes + 2 block scales.
+struct Chunk { uint32_t c[4]; uint32_t s0, s1; };
+
+// Quantize columns [k, k + 32) of row m from X (blocks beyond K stay zero);
+// res selects the residue of those columns.
+__device__ inline Chunk chunk_from_x(const DArgs &a, int64_t m, int64_t k, bool res, float S) {
+    Chunk ch = {{0, 0, 0, 0}, 0, 0};
     const float t = 6.0f * S;
-    uint32_t db = encode_block(v, S, t, cw, d);
-    if (res) {
-        float r[16];
-        block_residue(v, cw, d, S, r);
-        db = encode_block(r, S, t, cw, d);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int64_t kb = k + 16 * b;
+        if (kb + 16 <= a.K) {
+            float v[16];
+            load16_any(a.x, a.x_bf16, m * a.ldx + kb, v);
+            uint32_t cw[2];
+            float d;
+            uint32_t db = encode_block(v, S, t, cw, d);
+            if (res) {
+                float r[16];
+                block_residue(v, cw, d, S, r);
+                db = encode_block(r, S, t, cw, d);
+            }
+            ch.c[2 * b] = cw[0];
+            ch.c[2 * b + 1] = cw[1];
+            if (b == 0) ch.s0 = db; else ch.s1 = db;
+        }
     }
-    return decode8(cw[(kk >> 3) & 1], scale_pair(db));
+    return ch;
 }
 
-template <int MT, bool RES, bool FUSED>
+// The same chunk read from the quantized-activation buffer (column kc of the
+// stored tensor; residue columns are stored after column K).
+template <bool COHERENT>
+__device__ inline Chunk chunk_from_q(const DArgs &a, int64_t m, int64_t kc, int64_t kend_cols) {
+    Chunk ch = {{0, 0, 0, 0}, 0, 0};
+    const uint8_t *cp = a.q_codes + m * a.q_ldc + kc / 2;
+    const uint8_t *sp = a.q_scales + m * a.q_lds + kc / 16;
+    if (kc + 32 <= kend_cols) {
+        const unsigned long long *p = reinterpret_cast<const unsigned long long *>(cp);
+        const unsigned long long lo = COHERENT ? ld_dev(p) : p[0];
+        const unsigned long long hi = COHERENT ? ld_dev(p + 1) : p[1];
+        ch.c[0] = (uint32_t)lo; ch.c[1] = (uint32_t)(lo >> 32);
+        ch.c[2] = (uint32_t)hi; ch.c[3] = (uint32_t)(hi >> 32);
+        ch.s0 = COHERENT ? ld_dev(sp) : sp[0];
+        ch.s1 = COHERENT ? ld_dev(sp + 1) : sp[1];
+    } else if (kc + 16 <= kend_cols) {
+        const unsigned long long *p = reinterpret_cast<const unsigned long long *>(cp);
+        const unsigned long long lo = COHERENT ? ld_dev(p) : p[0];
+        ch.c[0] = (uint32_t)lo; ch.c[1] = (uint32_t)(lo >> 32);
+        ch.s0 = COHERENT ? ld_dev(sp) : sp[0];
+    }
+    return ch;
+}
+
+// Write a chunk's 4 fragments to the LDS operand: columns kc..kc+31 of row m.
+template <int MT>
+__device__ inline void chunk_to_lds(half8 *lds, int64_t kbeg, int64_t m, int64_t kc, const Chunk &ch) {
+    const int64_t off = kc - kbeg;
+    const int u = (int)(off >> 9), gg = (int)((off >> 7) & 3), i = (int)((off >> 5) & 3);
+    const int mt = (int)(m >> 4), l = (int)(m & 15) + 16 * gg;
+    const half2v d0 = scale_pair(ch.s0), d1 = scale_pair(ch.s1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int slot = (((u * 16) + 4 * i + j) * MT + mt) * 64 + l;
+        lds[slot] = decode8(ch.c[j], j < 2 ? d0 : d1);
+    }
+}
+
+// ---------------------------------------------------------------- kernel
+template <int MT, bool RES>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
     extern __shared__ half8 lds_a[];          // [U][16][MT][64] (+ residue copy)
-    __shared__ float sh_red[kWaves];
-    __shared__ int sh_flag;
+    __shared__ float sh_S;
+    __shared__ int sh_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const int p = blockIdx.x % a.P;
@@ -211,167 +264,206 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
     const int64_t rend = RES ? (a.res_cols < kend ? a.res_cols : kend) : kbeg;
     const int res_units = RES ? (rend > kbeg ? (int)((rend - kbeg + 511) / 512) : 0) : 0;
     const int slots = a.U * 16 * MT * 64;
-
-    // ---- phase 0: this wave's weight items (tile-major, then unit) into the ring
     const int64_t t_lo = q * a.T, t_hi = (q + 1) * a.T < a.NT ? (q + 1) * a.T : a.NT;
+
+    // consumer work: tiles t_lo + wave + kCons * j
     const int64_t t_first = t_lo + wave;
-    const int ntiles = t_first < t_hi ? (int)((t_hi - t_first + kWaves - 1) / kWaves) : 0;
+    const int ntiles = (wave < kCons && t_first < t_hi) ? (int)((t_hi - t_first + kCons - 1) / kCons) : 0;
     const int nitems = ntiles * units;
     auto item_row = [&](int it) -> int64_t {
-        const int64_t n = 16 * (t_first + (int64_t)(it / units) * kWaves) + r16;
+        const int64_t n = 16 * (t_first + (int64_t)(it / units) * kCons) + r16;
         return n < a.N ? n : a.N - 1;
     };
+
     WLoad ring[kRing];
+    if (wave < kCons) {
+        // ---- consumers: every weight load of the first items, right away
 #pragma unroll
-    for (int s = 0; s < kRing; ++s)
-        if (s < nitems) load_w(a, item_row(s), kbeg + 512 * (s % units), g, ring[s]);
-
-    // ---- phase 1: cooperative activation quantization
-    bool from_x = false;
-    float S = 0.0f;
-    if (FUSED) {
-        const int64_t KB = a.K / 16, NB = a.M * KB;
-        const int64_t b0 = (int64_t)blockIdx.x * NB / a.G, b1 = ((int64_t)blockIdx.x + 1) * NB / a.G;
-        const int64_t mine = b0 + threadIdx.x;           // host guarantees b1 - b0 <= kThreads
-        const bool have = mine < b1;
-        float v[16];
-        float lmax = 0.0f;
-        int64_t row = 0, blk = 0;
-        if (have) {
-            row = mine / KB; blk = mine - row * KB;
-            load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
+        for (int s = 0; s < kRing; ++s)
+            if (s < nitems) load_w(a, item_row(s), kbeg + 512 * (s % units), g, ring[s]);
+    } else {
+        // ---- producer: activation operand of this K range into LDS
+        const half8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int s = lane; s < (units + res_units) * 16 * MT * 64; s += 64) {
+            const bool is_res = s >= units * 16 * MT * 64;
+            lds_a[is_res ? slots + (s - units * 16 * MT * 64) : s] = zero;
         }
-        if (a.static_S) {
-            S = *a.static_S;
-        } else {
-            lmax = block_max(lmax, sh_red);
-            if (threadIdx.x == 0) {
-                st_dev(&a.amax_slots[blockIdx.x], lmax);
-                wait_own_stores();
-            }
-            grid_signal(&a.counters[0]);
-            if (grid_wait(&a.counters[0], (unsigned)a.G, a.spin_limit, &sh_flag)) {
-                float m = 0.0f;
-                for (int i = threadIdx.x; i < a.G; i += kThreads) m = fmaxf(m, ld_dev(&a.amax_slots[i]));
-                m = block_max(m, sh_red);
-                S = m > 0.0f ? m / 2688.0f : 1.0f;
+        float S = 0.0f;
+        bool from_x = a.mode == MODE_LOCAL || a.mode == MODE_SYNC1;
+        if (a.mode != MODE_PRE) {
+            if (a.static_S) {
+                S = *a.static_S;
+            } else if (a.mode == MODE_LOCAL) {
+                S = scale_of(wave_amax_x(a));
             } else {
-                S = scale_from_x(a, sh_red);
+                // publish the maximum of this workgroup's 1/G of X's blocks
+                const int64_t KB = a.K / 16, NB = a.M * KB;
+                const int64_t b0 = (int64_t)blockIdx.x * NB / a.G, b1 = ((int64_t)blockIdx.x + 1) * NB / a.G;
+                float lmax = 0.0f;
+                for (int64_t b = b0 + lane; b < b1; b += 64) {
+                    const int64_t row = b / KB, blk = b - row * KB;
+                    float v[16];
+                    load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
+                }
+                lmax = wave_max(lmax);
+                const Sync y0 = sync_at(a.header, 0);
+                int ok = 1;
+                if (lane == 0) {
+                    st_dev(&a.amax_slots[blockIdx.x], lmax);
+                    wait_own_stores();
+                    ok = sync_wait(y0, sync_arrive(y0, a.G), a.spin_limit) ? 1 : 0;
+                }
+                ok = __shfl(ok, 0);
+                if (ok) {
+                    float m = 0.0f;
+                    for (int i = lane; i < a.G; i += 64) m = fmaxf(m, ld_dev(&a.amax_slots[i]));
+                    S = scale_of(wave_max(m));
+                } else {
+                    S = scale_of(wave_amax_x(a));
+                }
+            }
+            if (blockIdx.x == 0 && lane == 0) *a.q_S = S;
+            if (a.mode == MODE_SYNC2) {
+                // quantize this workgroup's 1/G of X's blocks into the shared buffer
+                const int64_t KB = a.K / 16, NB = a.M * KB;
+                const int64_t b0 = (int64_t)blockIdx.x * NB / a.G, b1 = ((int64_t)blockIdx.x + 1) * NB / a.G;
+                const float t = 6.0f * S;
+                for (int64_t b = b0 + lane; b < b1; b += 64) {
+                    const int64_t row = b / KB, blk = b - row * KB;
+                    float v[16];
+                    load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
+                    uint32_t cw[2];
+                    float d;
+                    const uint32_t db = encode_block(v, S, t, cw, d);
+                    unsigned long long *cp = reinterpret_cast<unsigned long long *>(a.q_codes + row * a.q_ldc + 8 * blk);
+                    st_dev(cp, (unsigned long long)cw[0] | ((unsigned long long)cw[1] << 32));
+                    st_dev(a.q_scales + row * a.q_lds + blk, (uint8_t)db);
+                    if (RES && 16 * blk < a.res_cols) {
+                        float r[16];
+                        block_residue(v, cw, d, S, r);
+                        uint32_t rc[2];
+                        float dr;
+                        const uint32_t rdb = encode_block(r, S, t, rc, dr);
+                        unsigned long long *rp =
+                            reinterpret_cast<unsigned long long *>(a.q_codes + row * a.q_ldc + 8 * (KB + blk));
+                        st_dev(rp, (unsigned long long)rc[0] | ((unsigned long long)rc[1] << 32));
+                        st_dev(a.q_scales + row * a.q_lds + KB + blk, (uint8_t)rdb);
+                    }
+                }
+                wait_own_stores();
+                const Sync y1 = sync_at(a.header, 1);
+                int ok = 1;
+                if (lane == 0) ok = sync_wait(y1, sync_arrive(y1, a.G), a.spin_limit) ? 1 : 0;
+                from_x = __shfl(ok, 0) == 0;
             }
         }
-        if (blockIdx.x == 0 && threadIdx.x == 0) *a.q_S = S;
-        if (have) {
-            const float t = 6.0f * S;
-            uint32_t cw[2];
-            float d;
-            const uint32_t db = encode_block(v, S, t, cw, d);
-            uint32_t *cp = reinterpret_cast<uint32_t *>(a.q_codes + row * a.q_ldc + 8 * blk);
-            st_dev(cp, cw[0]);
-            st_dev(cp + 1, cw[1]);
-            st_dev(a.q_scales + row * a.q_lds + blk, (uint8_t)db);
-            if (RES && 16 * blk < a.res_cols) {
-                float r[16];
-                block_residue(v, cw, d, S, r);
-                uint32_t rc[2];
-                float dr;
-                const uint32_t rdb = encode_block(r, S, t, rc, dr);
-                uint32_t *rp = reinterpret_cast<uint32_t *>(a.q_codes + row * a.q_ldc + 8 * (KB + blk));
-                st_dev(rp, rc[0]);
-                st_dev(rp + 1, rc[1]);
-                st_dev(a.q_scales + row * a.q_lds + KB + blk, (uint8_t)rdb);
+        // the K range's chunks (32 columns of one row each), main and residue
+        const int64_t nch = (kend - kbeg + 31) / 32, nrch = RES ? (rend - kbeg + 31) / 32 : 0;
+        const bool writer = from_x && q == 0 && a.mode != MODE_PRE;   // keeps the quantized buffer complete
+        for (int64_t c = lane; c < a.M * (nch + nrch); c += 64) {
+            const int64_t m = c / (nch + nrch), cc = c - m * (nch + nrch);
+            const bool is_res = cc >= nch;
+            const int64_t kc = kbeg + 32 * (is_res ? cc - nch : cc);
+            Chunk ch;
+            if (from_x) {
+                ch = chunk_from_x(a, m, kc, is_res, S);
+                if (writer) {
+                    const int64_t col = is_res ? a.K + kc : kc;
+                    uint32_t *cp = reinterpret_cast<uint32_t *>(a.q_codes + m * a.q_ldc + col / 2);
+                    if (kc + 32 <= a.K) {
+                        cp[0] = ch.c[0]; cp[1] = ch.c[1]; cp[2] = ch.c[2]; cp[3] = ch.c[3];
+                        a.q_scales[m * a.q_lds + col / 16] = (uint8_t)ch.s0;
+                        a.q_scales[m * a.q_lds + col / 16 + 1] = (uint8_t)ch.s1;
+                    } else if (kc + 16 <= a.K) {
+                        cp[0] = ch.c[0]; cp[1] = ch.c[1];
+                        a.q_scales[m * a.q_lds + col / 16] = (uint8_t)ch.s0;
+                    }
+                }
+            } else {
+                const int64_t col = is_res ? a.K + kc : kc;
+                const int64_t lim = is_res ? a.K + rend : kend;
+                ch = a.mode == MODE_PRE ? chunk_from_q<false>(a, m, col, lim) : chunk_from_q<true>(a, m, col, lim);
             }
+            chunk_to_lds<MT>(lds_a + (is_res ? slots : 0), kbeg, m, kc, ch);
         }
-        if (__any(have)) wait_own_stores();      // only waves that stored shared codes
-        grid_signal(&a.counters[1]);
-        from_x = !grid_wait(&a.counters[1], (unsigned)a.G, a.spin_limit, &sh_flag);
+        if (lane == 0) sh_S = a.mode == MODE_PRE ? a.q_S[0] : S;
     }
+    __syncthreads();                           // activation operand ready
 
-    // ---- phase 2: activation operand of this K range into LDS
-    for (int s = threadIdx.x; s < (units + res_units) * 16 * MT * 64; s += kThreads) {
-        const bool is_res = s >= units * 16 * MT * 64;
-        const int s2 = is_res ? s - units * 16 * MT * 64 : s;
-        const int l = s2 & 63, mt = (s2 >> 6) % MT, ij = ((s2 >> 6) / MT) & 15, u = ((s2 >> 6) / MT) >> 4;
-        const int m = 16 * mt + (l & 15), gg = l >> 4, i = ij >> 2, j = ij & 3;
-        const int64_t k = kbeg + 512 * u + 128 * gg + 32 * i + 8 * j;
-        half8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (m < a.M && k < (is_res ? rend : kend)) v = act_slot<FUSED>(a, m, is_res ? a.K + k : k, from_x, S);
-        lds_a[(is_res ? slots : 0) + s2] = v;
-    }
-    __syncthreads();
-
-    // ---- phase 3: decode weights, MFMA
-    const float scale = (FUSED ? S : a.q_S[0]) * a.w_S[0];
-    float4v acc[MT];
+    // ---- consumers: decode weights, MFMA
+    const float scale = sh_S * a.w_S[0];
+    if (wave < kCons) {
+        float4v acc[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
-    for (int base = 0; base < nitems; base += kRing) {
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+        for (int base = 0; base < nitems; base += kRing) {
 #pragma unroll
-        for (int s = 0; s < kRing; ++s) {
-            const int it = base + s;
-            if (it < nitems) {
-                const int u = it % units;
-                const half8 *abase = lds_a + (size_t)u * 16 * MT * 64 + lane;
-                const bool res_u = RES && u < res_units;
-                const WLoad cur = ring[s];
-                if (it + kRing < nitems)
-                    load_w(a, item_row(it + kRing), kbeg + 512 * ((it + kRing) % units), g, ring[s]);
+            for (int s = 0; s < kRing; ++s) {
+                const int it = base + s;
+                if (it < nitems) {
+                    const int u = it % units;
+                    const half8 *abase = lds_a + (size_t)u * 16 * MT * 64 + lane;
+                    const bool res_u = RES && u < res_units;
+                    const WLoad cur = ring[s];
+                    if (it + kRing < nitems)
+                        load_w(a, item_row(it + kRing), kbeg + 512 * ((it + kRing) % units), g, ring[s]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t sw = (i < 2) ? cur.s.x : cur.s.y;
-                    const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
-                    const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
-                    const uint32_t cws[4] = {cur.c[i].x, cur.c[i].y, cur.c[i].z, cur.c[i].w};
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t sw = (i < 2) ? cur.s.x : cur.s.y;
+                        const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
+                        const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
+                        const uint32_t cws[4] = {cur.c[i].x, cur.c[i].y, cur.c[i].z, cur.c[i].w};
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
+                        for (int j = 0; j < 4; ++j) {
+                            const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) {
-                            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64], b,
-                                                                             acc[mt], 0, 0, 0);
-                            if (res_u)
-                                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                    abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, acc[mt], 0, 0, 0);
+                            for (int mt = 0; mt < MT; ++mt) {
+                                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64],
+                                                                                 b, acc[mt], 0, 0, 0);
+                                if (res_u)
+                                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                        abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, acc[mt], 0, 0, 0);
+                            }
                         }
                     }
-                }
-                if (u == units - 1) {
-                    // tile done: lane holds rows 16 mt + 4 g + e of column n
-                    const int64_t n = 16 * (t_first + (int64_t)(it / units) * kWaves) + r16;
-                    if (n < a.N) {
+                    if (u == units - 1) {
+                        // tile done: lane holds rows 16 mt + 4 g + e of column n
+                        const int64_t n = 16 * (t_first + (int64_t)(it / units) * kCons) + r16;
+                        if (n < a.N) {
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
+                            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int64_t m = 16 * mt + 4 * g + e;
-                                if (m < a.M) {
-                                    if (a.P == 1) {
-                                        const float v = acc[mt][e] * scale;
-                                        if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
-                                        else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
-                                    } else {
-                                        st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], acc[mt][e]);
+                                for (int e = 0; e < 4; ++e) {
+                                    const int64_t m = 16 * mt + 4 * g + e;
+                                    if (m < a.M) {
+                                        if (a.P == 1) {
+                                            const float v = acc[mt][e] * scale;
+                                            if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
+                                            else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
+                                        } else {
+                                            st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], acc[mt][e]);
+                                        }
                                     }
                                 }
-                            }
-                    }
+                        }
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+                        for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+                    }
                 }
             }
         }
     }
 
-    // ---- phase 4: split-K combine by the last workgroup of the tile group
+    // ---- split-K combine by the last workgroup of the tile group
     if (a.P > 1) {
-        wait_own_stores();                 // this wave's partial tiles are visible
+        wait_own_stores();                     // this wave's partial tiles are visible
         __syncthreads();
-        if (threadIdx.x == 0)
-            sh_flag = __hip_atomic_fetch_add(&a.tile_cnt[q], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                      (unsigned)a.P - 1;
+        unsigned *tile_cnt = reinterpret_cast<unsigned *>(a.header + kTileCntOffset);
+        if (threadIdx.x == 0) sh_last = add_dev(&tile_cnt[q], 1u) == (unsigned)a.P - 1;
         __syncthreads();
-        if (sh_flag) {
+        if (sh_last) {
             const int64_t ncols = (t_hi - t_lo) * 16;
             for (int64_t idx = threadIdx.x; idx < a.M * ncols; idx += kThreads) {
                 const int64_t m = idx / ncols, n = 16 * t_lo + (idx - m * ncols);
@@ -382,126 +474,106 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
                 if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
                 else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
             }
-            if (threadIdx.x == 0)
-                __hip_atomic_store(&a.tile_cnt[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-
-    // ---- phase 5: the last workgroup of a fused call returns the grid counters to zero
-    if (FUSED) {
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const unsigned old = __hip_atomic_fetch_add(&a.counters[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (old == (unsigned)a.G - 1) {
-                __hip_atomic_store(&a.counters[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.counters[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.counters[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (threadIdx.x == 0) st_dev(&tile_cnt[q], 0u);
         }
     }
 }
 
-struct Plan { int MT, U, P, T, tw, G; int64_t NT, Q; size_t lds; bool fused_ok; };
+// ---------------------------------------------------------------- planning
+struct Plan { int MT, U, P, T, tw, G, mode; int64_t NT, Q; size_t lds; };
 
-int max_resident(const void *fn, size_t lds) {
-    static int cus = 0;
-    if (!cus) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return 1;                       // no device: size conservatively, do not cache
-    }
+int resident_capacity(const void *fn, size_t lds) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 1;                       // no device: plan conservatively
     int per = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kThreads, lds) != hipSuccess || per < 1) per = 1;
     return per * cus;
 }
 
-Plan make_plan(int64_t M, int64_t N, int64_t K, int64_t res_cols, int cap) {
+const void *kernel_ptr(int MT, bool res) {
+    if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true>)
+                            : reinterpret_cast<const void *>(&decode_kernel<1, false>);
+    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, false>);
+}
+
+Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
     Plan pl;
     pl.MT = M <= 16 ? 1 : 2;
     const bool res = res_cols > 0;
-    const int umax = (pl.MT == 1 ? 4 : 2) / (res ? 2 : 1) > 0 ? (pl.MT == 1 ? 4 : 2) / (res ? 2 : 1) : 1;
+    int umax = (pl.MT == 1 ? 4 : 2) / (res ? 2 : 1);
+    if (umax < 1) umax = 1;
+    const size_t lds_max = (size_t)umax * 16 * pl.MT * 64 * sizeof(half8) * (res ? 2 : 1);
+    static int cap_cache[2][2] = {{0, 0}, {0, 0}};
+    int &capc = cap_cache[pl.MT - 1][res ? 1 : 0];
+    if (capc <= 1) capc = resident_capacity(kernel_ptr(pl.MT, res), lds_max);
+    const int cap = capc - capc / 8;
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
-    // pick (U, tw): fewest items per wave that keeps the grid resident, preferring fewer K ranges
     int bestU = 1, besttw = 1;
     double best = 1e30;
     for (int U = 1; U <= umax; U *= 2) {
-        for (int tw = 1; tw <= 8; ++tw) {
-            const int64_t P = (ku + U - 1) / U, Q = (pl.NT + 4 * tw - 1) / (4 * tw);
+        for (int tw = 1; tw <= 16; ++tw) {
+            const int64_t P = (ku + U - 1) / U, Q = (pl.NT + kCons * tw - 1) / (kCons * tw);
             const int64_t G = P * Q;
-            if (G > cap - cap / 8 || Q > kMaxTileCounters) continue;
+            if (G > cap || Q > kMaxTileCounters) continue;
             const int items = tw * (int)(U < ku ? U : ku);
-            // cost: items per wave (time per wave), plus a small charge per K range (partials)
             const double cost = items + 0.15 * (double)P + (G < 192 ? 4.0 : 0.0);
             if (cost < best) { best = cost; bestU = U; besttw = tw; }
         }
     }
     pl.U = bestU > ku ? (int)ku : bestU;
     pl.tw = besttw;
-    pl.T = 4 * pl.tw;
+    pl.T = kCons * pl.tw;
     pl.P = (int)((ku + pl.U - 1) / pl.U);
     pl.Q = (pl.NT + pl.T - 1) / pl.T;
     pl.G = (int)(pl.P * pl.Q);
     pl.lds = (size_t)pl.U * 16 * pl.MT * 64 * sizeof(half8) * (res ? 2 : 1);
-    pl.fused_ok = pl.G <= cap - cap / 8 && pl.Q <= kMaxTileCounters &&
-                  (M * (K / 16)) <= (int64_t)pl.G * kThreads;
+    // activation handling
+    const int64_t kc = (int64_t)pl.U * 512 < K ? (int64_t)pl.U * 512 : K;
+    if (!raw_x || norm_or_perm) pl.mode = MODE_PRE;
+    else if (M * kc <= 8192 && M * K <= 16384) pl.mode = MODE_LOCAL;
+    else if (M * kc <= 8192) pl.mode = MODE_SYNC1;
+    else pl.mode = MODE_SYNC2;
     return pl;
 }
 
-const void *kernel_ptr(int MT, bool res, bool fused) {
-#define KP(A, B, C) reinterpret_cast<const void *>(&decode_kernel<A, B, C>)
-    if (MT == 1) return res ? (fused ? KP(1, true, true) : KP(1, true, false)) : (fused ? KP(1, false, true) : KP(1, false, false));
-    return res ? (fused ? KP(2, true, true) : KP(2, true, false)) : (fused ? KP(2, false, true) : KP(2, false, false));
-#undef KP
-}
-
-Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
-    const int MT = M <= 16 ? 1 : 2;
-    const bool res = res_cols > 0;
-    // capacity with the largest LDS the plan may choose
-    const size_t lds_max = (size_t)((MT == 1 ? 4 : 2)) * 16 * MT * 64 * 16;
-    const int cap = max_resident(kernel_ptr(MT, res, true), lds_max);
-    return make_plan(M, N, K, res_cols, cap);
-}
+bool plan_ok(const Plan &pl) { return pl.Q <= kMaxTileCounters && pl.G >= 1; }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
-    const Plan pl = plan_for(M, N, K, res_cols);
+    const Plan pl = plan_for(M, N, K, res_cols, true, false);
     const size_t part = pl.P > 1 ? (size_t)pl.P * M * N * sizeof(float) : 0;
     return part + ((size_t)pl.G * sizeof(float) + 255) / 256 * 256;
 }
 
 bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
-    return plan_for(M, N, K, res_cols).fused_ok;
+    return plan_ok(plan_for(M, N, K, res_cols, true, false));
 }
 
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
-    const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols);
-    const bool fused = g.x != nullptr;
-    if (fused && !pl.fused_ok) return hipErrorInvalidValue;
+    const bool raw = g.x != nullptr;
+    const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols, raw, false);
+    if (!plan_ok(pl)) return hipErrorInvalidValue;
+    if (!g.header || !g.scratch || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols))
+        return hipErrorInvalidValue;
     DArgs a;
     a.x = g.x; a.x_bf16 = g.x_bf16; a.ldx = g.ldx; a.static_S = g.static_S;
     a.q_codes = g.q_codes; a.q_ldc = g.q_ldc; a.q_scales = g.q_scales; a.q_lds = g.q_lds; a.q_S = g.q_S;
     a.w_codes = g.w_codes; a.w_ldc = g.w_ldc; a.w_scales = g.w_scales; a.w_lds = g.w_lds; a.w_S = g.w_S;
     a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
-    // counters live in the zero-kept header; amax slots and partials in the scratch region
-    if (!g.header || !g.scratch || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols))
-        return hipErrorInvalidValue;
-    if (pl.Q > kMaxTileCounters) return hipErrorInvalidValue;
-    a.counters = g.header;
-    a.tile_cnt = g.header + 4;
+    a.header = reinterpret_cast<uint8_t *>(g.header);
     a.amax_slots = static_cast<float *>(g.scratch);
     a.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(g.scratch) +
                                            ((size_t)pl.G * sizeof(float) + 255) / 256 * 256);
-    a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.G = pl.G; a.NT = pl.NT;
+    a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
     a.spin_limit = g.spin_limit;
-    const bool res = g.res_cols > 0;
-    const void *fn = kernel_ptr(pl.MT, res, fused);
     void *args[] = {&a};
-    return hipLaunchKernel(fn, dim3(pl.G), dim3(kThreads), args, pl.lds, st);
+    return hipLaunchKernel(kernel_ptr(pl.MT, g.res_cols > 0), dim3(pl.G), dim3(kThreads), args, pl.lds, st);
 }
 
 }  // namespace nvfp4
