@@ -93,10 +93,16 @@ __device__ inline float wave_max(float v) {
 // Counter word: upper 32 bits = call index, lower = arrivals in this call.
 struct Sync { unsigned long long *top, *sub; };
 
+// Header bytes [2048 s, 2048 s + 64 (kGroups + 1)) belong to sync s (s = 0, 1):
+// the top counter, then one 64-byte line per sub-counter.
+constexpr size_t kSyncBytes = 2048;
+static_assert(64 * (kGroups + 1) <= (int)kSyncBytes, "sub-counters overflow their sync's region");
+static_assert(2 * kSyncBytes <= kTileCntOffset, "sync regions overlap the tile counters");
+
 __device__ inline Sync sync_at(uint8_t *header, int s) {
     Sync y;
-    y.top = reinterpret_cast<unsigned long long *>(header + 1024 * s);
-    y.sub = reinterpret_cast<unsigned long long *>(header + 1024 * s + 64);
+    y.top = reinterpret_cast<unsigned long long *>(header + kSyncBytes * s);
+    y.sub = reinterpret_cast<unsigned long long *>(header + kSyncBytes * s + 64);
     return y;
 }
 
