@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
             }
         }
         // the K range's chunks (32 columns of one row each), main and residue
-        const int64_t nch = (kend - kbeg + 31) / 32, nrch = RES ? (rend - kbeg + 31) / 32 : 0;
+        const int64_t nch = (kend - kbeg + 31) / 32, nrch = (RES && rend > kbeg) ? (rend - kbeg + 31) / 32 : 0;
         const bool writer = from_x && q == 0 && a.mode != MODE_PRE;   // keeps the quantized buffer complete
         for (int64_t c = lane; c < a.M * (nch + nrch); c += 64) {
             const int64_t m = c / (nch + nrch), cc = c - m * (nch + nrch);
