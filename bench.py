@@ -45,6 +45,10 @@ F16_MFMA_PEAK_TFLOPS = 2500.0
 RING_BYTES = 640 << 20
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def wbytes(N, K):
     return N * K // 2 + N * K // 16
 
@@ -136,6 +140,7 @@ def main():
 
     step_bytes = sum(call_bytes(M, N, K) for M in inputs.DECODE_MS for (K, N) in shapes)
 
+    log(f"inputs ready; capturing step graphs")
     # One graph per ring phase, each holding exactly one step; step t replays graph t % phases,
     # so every call of consecutive steps reads a different weight copy.
     phases = max(len(r.items) for r in rings.values())
@@ -166,6 +171,8 @@ def main():
     sec_per_step = st.elapsed_time(en) / 1e3 / timed_steps
     value = step_bytes / sec_per_step / 1e9
     del graphs
+    log(f"timed {timed_steps} steps: {sec_per_step * 1e6:.1f} us/step, {value:.1f} GB/s; "
+        f"sync timeouts so far {nvfp4.sync_timeouts()}")
 
     # ---------------- per-case detail: whole call and kernel alone
     detail = {"decode": []}
@@ -188,6 +195,8 @@ def main():
 
             tf, _ = graph_time(fused, reps=20, inner=n)
             tk, _ = graph_time(kern, reps=20, inner=n)
+            log(f"case M={M} K={K} N={N}: call {tf * 1e6:.2f} us, kernel {tk * 1e6:.2f} us, "
+                f"timeouts {nvfp4.sync_timeouts()}")
             kern_bytes_total += kernel_bytes(M, N, K)
             kern_time_total += tk
             detail["decode"].append({

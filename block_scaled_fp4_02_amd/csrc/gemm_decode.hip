@@ -93,11 +93,11 @@ __device__ inline float wave_max(float v) {
 // Counter word: upper 32 bits = call index, lower = arrivals in this call.
 struct Sync { unsigned long long *top, *sub; };
 
-// Header bytes [2048 s, 2048 s + 64 (kGroups + 1)) belong to sync s (s = 0, 1):
+// Header bytes [1536 s, 1536 s + 64 (kGroups + 1)) belong to sync s (s = 0, 1):
 // the top counter, then one 64-byte line per sub-counter.
-constexpr size_t kSyncBytes = 2048;
+constexpr size_t kSyncBytes = 1536;
 static_assert(64 * (kGroups + 1) <= (int)kSyncBytes, "sub-counters overflow their sync's region");
-static_assert(2 * kSyncBytes <= kTileCntOffset, "sync regions overlap the tile counters");
+static_assert(2 * kSyncBytes <= kTileCntOffset - 64, "sync regions overlap the timeout counter");
 
 __device__ inline Sync sync_at(uint8_t *header, int s) {
     Sync y;
@@ -122,10 +122,16 @@ __device__ inline unsigned sync_arrive(Sync y, int G) {
     return mine;
 }
 
-__device__ inline bool sync_wait(Sync y, unsigned mine, unsigned limit) {
+// Header word counting waits that gave up (diagnostics; read by the host).
+constexpr size_t kTimeoutCounterOffset = 4096 - 64;
+
+__device__ inline bool sync_wait(Sync y, unsigned mine, unsigned limit, uint8_t *header) {
     unsigned it = 0;
     while ((unsigned)(ld_dev(y.top) >> 32) == mine) {
-        if (++it > limit) return false;
+        if (++it > limit) {
+            add_dev(reinterpret_cast<unsigned *>(header + kTimeoutCounterOffset), 1u);
+            return false;
+        }
         __builtin_amdgcn_s_sleep(2);
     }
     return true;
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
                 if (lane == 0) {
                     st_dev(&a.amax_slots[blockIdx.x], lmax);
                     wait_own_stores();
-                    ok = sync_wait(y0, sync_arrive(y0, a.G), a.spin_limit) ? 1 : 0;
+                    ok = sync_wait(y0, sync_arrive(y0, a.G), a.spin_limit, a.header) ? 1 : 0;
                 }
                 ok = __shfl(ok, 0);
                 if (ok) {
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
                 wait_own_stores();
                 const Sync y1 = sync_at(a.header, 1);
                 int ok = 1;
-                if (lane == 0) ok = sync_wait(y1, sync_arrive(y1, a.G), a.spin_limit) ? 1 : 0;
+                if (lane == 0) ok = sync_wait(y1, sync_arrive(y1, a.G), a.spin_limit, a.header) ? 1 : 0;
                 from_x = __shfl(ok, 0) == 0;
             }
         }

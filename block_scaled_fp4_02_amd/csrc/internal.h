@@ -40,6 +40,8 @@ hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 // waits and the split-K combine. It must be zero before the first call on a
 // workspace; every call leaves it zero.
 constexpr size_t kHeaderBytes = 8192;
+// Byte offset (in the header) of a u32 counting grid-wide waits that gave up.
+constexpr size_t kHeaderTimeoutCounter = 4096 - 64;
 constexpr int64_t kHeaderCounters = (int64_t)(kHeaderBytes / sizeof(unsigned));
 
 // Decode-shaped (M <= 32) product in one launch. With x != nullptr the raw

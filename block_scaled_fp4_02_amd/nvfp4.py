@@ -145,6 +145,17 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return buf
 
 
+HEADER_TIMEOUT_OFFSET = 4096 - 64
+
+
+def sync_timeouts() -> int:
+    """Total grid-wide waits that gave up (and recomputed locally) on this process's workspaces."""
+    total = 0
+    for buf in _ws.values():
+        total += int(buf[HEADER_TIMEOUT_OFFSET:HEADER_TIMEOUT_OFFSET + 4].cpu().view(torch.int32)[0])
+    return total
+
+
 def _opts(gamma, eps, perm, residue_cols, static_scale):
     if gamma is None and perm is None and not residue_cols and static_scale is None:
         return None, []
