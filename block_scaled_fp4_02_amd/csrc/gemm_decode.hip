@@ -40,6 +40,9 @@
 // index in their upper half so they never need resetting. Every wait is
 // bounded: past the spin limit a workgroup recomputes what it waited for from
 // X itself (same arithmetic, same result), so no wait can hang.
+#include <cstdio>
+#include <cstdlib>
+
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -521,7 +524,11 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     static int cap_cache[2][2] = {{0, 0}, {0, 0}};
     int &capc = cap_cache[pl.MT - 1][res ? 1 : 0];
     if (capc <= 1) capc = resident_capacity(kernel_ptr(pl.MT, res), lds_max);
-    const int cap = capc - capc / 8;
+    int cap = capc - capc / 8;
+    if (const char *e = std::getenv("NVFP4_DECODE_MAX_GRID")) {      // tuning override
+        const int v = std::atoi(e);
+        if (v > 0 && v < cap) cap = v;
+    }
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
     int bestU = 1, besttw = 1;
@@ -549,6 +556,10 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     else if (M * kc <= 8192 && M * K <= 16384) pl.mode = MODE_LOCAL;
     else if (M * kc <= 8192) pl.mode = MODE_SYNC1;
     else pl.mode = MODE_SYNC2;
+    if (std::getenv("NVFP4_DEBUG_PLAN"))
+        std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d T=%d G=%d mode=%d "
+                     "(resident capacity %d)\n", (long long)M, (long long)N, (long long)K, (long long)res_cols,
+                     pl.MT, pl.U, pl.P, pl.T, pl.G, pl.mode, capc);
     return pl;
 }
 
