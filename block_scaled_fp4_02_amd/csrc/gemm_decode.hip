@@ -14,7 +14,7 @@
 //  * a workgroup owns a K range of U 512-column units and T 16-row weight
 //    tiles; it has four consumer waves and one producer wave;
 //  * consumer waves issue the loads of their (tile, unit) items at once
-//    (ring of 4 items: 4 x 16 B codes + 8 B scales per lane each), wait at one
+//    (a ring of 4 items: 4 x 16 B codes + 8 B scales per lane each), wait at one
 //    barrier for the activation operand, then decode each weight item in
 //    registers (v_cvt_scalef32_pk_f16_fp4 + v_pk_mul_f16, exact) and issue 16
 //    v_mfma_f32_16x16x32_f16 per item, refilling the ring; residue columns
@@ -51,8 +51,8 @@ namespace {
 
 constexpr int kCons = 4;                       // consumer waves
 constexpr int kThreads = 64 * (kCons + 1);     // plus one producer wave
-constexpr int kRing = 4;
 constexpr int kGroups = 16;                    // sub-counters per grid-wide wait
+constexpr int kMaxItems = 8;                   // (tile, unit) items per consumer wave
 constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
 constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
 
@@ -146,35 +146,22 @@ struct WLoad {
     uint2 s;
 };
 
+// Always the same five loads, so the compiler can count them (vmcnt) across the
+// ring. Addresses past K are clamped to the row start: such weight lanes meet
+// an activation operand that is exactly zero there, and any code/scale byte
+// decodes to a finite f16, so they contribute 0. A 16 B load at a chunk start
+// below K stays inside the row's padded stride (ld_codes is a multiple of 16
+// and >= K/2), and so does an 8 B scale load at a unit start below K.
 __device__ inline void load_w(const DArgs &a, int64_t n, int64_t kb, int g, WLoad &w) {
     const uint8_t *crow = a.w_codes + n * a.w_ldc;
     const uint8_t *srow = a.w_scales + n * a.w_lds;
     const int64_t k0 = kb + 128 * g;
-    if (k0 + 128 <= a.K) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(crow + k0 / 2);
-        w.c[0] = p[0]; w.c[1] = p[1]; w.c[2] = p[2]; w.c[3] = p[3];
-        w.s = *reinterpret_cast<const uint2 *>(srow + k0 / 16);
-    } else {
-        uint32_t sc[2] = {0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t ki = k0 + 32 * i;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (ki + 32 <= a.K) {
-                v = *reinterpret_cast<const uint4 *>(crow + ki / 2);
-            } else if (ki + 16 <= a.K) {
-                const uint2 h = *reinterpret_cast<const uint2 *>(crow + ki / 2);
-                v.x = h.x; v.y = h.y;
-            }
-            w.c[i] = v;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int64_t kk = ki + 16 * b;
-                if (kk + 16 <= a.K) sc[(2 * i + b) >> 2] |= (uint32_t)srow[kk / 16] << (8 * ((2 * i + b) & 3));
-            }
-        }
-        w.s = make_uint2(sc[0], sc[1]);
+    for (int i = 0; i < 4; ++i) {
+        const int64_t ki = k0 + 32 * i;
+        w.c[i] = *reinterpret_cast<const uint4 *>(crow + (ki < a.K ? ki / 2 : 0));
     }
+    w.s = *reinterpret_cast<const uint2 *>(srow + (k0 < a.K ? k0 / 16 : 0));
 }
 
 // ------------------------------------------------------------ producer wave
@@ -249,23 +236,17 @@ __device__ inline Chunk chunk_from_q(const DArgs &a, int64_t m, int64_t kc, int6
     return ch;
 }
 
-// Write a chunk's 4 fragments to the LDS operand: columns kc..kc+31 of row m.
-template <int MT>
-__device__ inline void chunk_to_lds(half8 *lds, int64_t kbeg, int64_t m, int64_t kc, const Chunk &ch) {
-    const int64_t off = kc - kbeg;
-    const int u = (int)(off >> 9), gg = (int)((off >> 7) & 3), i = (int)((off >> 5) & 3);
-    const int mt = (int)(m >> 4), l = (int)(m & 15) + 16 * gg;
+__device__ inline void chunk_to_slots(half8 *lds, int base_slot, int stride, const Chunk &ch) {
     const half2v d0 = scale_pair(ch.s0), d1 = scale_pair(ch.s1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int slot = (((u * 16) + 4 * i + j) * MT + mt) * 64 + l;
-        lds[slot] = decode8(ch.c[j], j < 2 ? d0 : d1);
-    }
+    for (int j = 0; j < 4; ++j) lds[base_slot + j * stride] = decode8(ch.c[j], j < 2 ? d0 : d1);
 }
 
 // ---------------------------------------------------------------- kernel
 template <int MT, bool RES>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_kernel(DArgs a) {
+    constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
     extern __shared__ half8 lds_a[];          // [U][16][MT][64] (+ residue copy)
     __shared__ float sh_S;
     __shared__ int sh_last;
@@ -290,6 +271,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
         return n < a.N ? n : a.N - 1;
     };
 
+    // Loaded before the weight ring: vmcnt is in order, so anything loaded after
+    // the ring and used early would wait for the whole ring.
+    const float w_scale = a.w_S[0];
     WLoad ring[kRing];
     if (wave < kCons) {
         // ---- consumers: every weight load of the first items, right away
@@ -298,11 +282,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
             if (s < nitems) load_w(a, item_row(s), kbeg + 512 * (s % units), g, ring[s]);
     } else {
         // ---- producer: activation operand of this K range into LDS
-        const half8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int s = lane; s < (units + res_units) * 16 * MT * 64; s += 64) {
-            const bool is_res = s >= units * 16 * MT * 64;
-            lds_a[is_res ? slots + (s - units * 16 * MT * 64) : s] = zero;
-        }
         float S = 0.0f;
         bool from_x = a.mode == MODE_LOCAL || a.mode == MODE_SYNC1;
         if (a.mode != MODE_PRE) {
@@ -374,72 +353,83 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
                 from_x = __shfl(ok, 0) == 0;
             }
         }
-        // the K range's chunks (32 columns of one row each), main and residue
-        const int64_t nch = (kend - kbeg + 31) / 32, nrch = (RES && rend > kbeg) ? (rend - kbeg + 31) / 32 : 0;
+        // The K range's operand: for each (unit u, sub-block i, m-tile mt) the 64
+        // lanes take row 16 mt + (lane & 15) and quarter g = lane >> 4, i.e. the
+        // 32 columns kbeg + 512 u + 128 g + 32 i, and write slots
+        // ((u * 16 + 4 i + j) * MT + mt) * 64 + lane: consecutive lanes, consecutive
+        // slots. Every slot of the range is written once (zero outside the data).
         const bool writer = from_x && q == 0 && a.mode != MODE_PRE;   // keeps the quantized buffer complete
-        for (int64_t c = lane; c < a.M * (nch + nrch); c += 64) {
-            const int64_t m = c / (nch + nrch), cc = c - m * (nch + nrch);
-            const bool is_res = cc >= nch;
-            const int64_t kc = kbeg + 32 * (is_res ? cc - nch : cc);
-            Chunk ch;
-            if (from_x) {
-                ch = chunk_from_x(a, m, kc, is_res, S);
-                if (writer) {
-                    const int64_t col = is_res ? a.K + kc : kc;
-                    uint32_t *cp = reinterpret_cast<uint32_t *>(a.q_codes + m * a.q_ldc + col / 2);
-                    if (kc + 32 <= a.K) {
-                        cp[0] = ch.c[0]; cp[1] = ch.c[1]; cp[2] = ch.c[2]; cp[3] = ch.c[3];
-                        a.q_scales[m * a.q_lds + col / 16] = (uint8_t)ch.s0;
-                        a.q_scales[m * a.q_lds + col / 16 + 1] = (uint8_t)ch.s1;
-                    } else if (kc + 16 <= a.K) {
-                        cp[0] = ch.c[0]; cp[1] = ch.c[1];
-                        a.q_scales[m * a.q_lds + col / 16] = (uint8_t)ch.s0;
+        const int passes = (units + res_units) * 4 * MT;
+        for (int w = 0; w < passes; ++w) {
+            const bool is_res = w >= units * 4 * MT;
+            const int w2 = is_res ? w - units * 4 * MT : w;
+            const int mt = w2 % MT, i = (w2 / MT) & 3, u = (w2 / MT) >> 2;
+            const int64_t row = r16 + 16 * mt;
+            const int64_t kc = kbeg + 512 * u + 128 * g + 32 * i;
+            Chunk ch = {{0, 0, 0, 0}, 0, 0};
+            if (row < a.M && kc < (is_res ? rend : kend)) {
+                if (from_x) {
+                    ch = chunk_from_x(a, row, kc, is_res, S);
+                    if (writer) {
+                        const int64_t col = is_res ? a.K + kc : kc;
+                        uint32_t *cp = reinterpret_cast<uint32_t *>(a.q_codes + row * a.q_ldc + col / 2);
+                        if (kc + 32 <= a.K) {
+                            cp[0] = ch.c[0]; cp[1] = ch.c[1]; cp[2] = ch.c[2]; cp[3] = ch.c[3];
+                            a.q_scales[row * a.q_lds + col / 16] = (uint8_t)ch.s0;
+                            a.q_scales[row * a.q_lds + col / 16 + 1] = (uint8_t)ch.s1;
+                        } else {
+                            cp[0] = ch.c[0]; cp[1] = ch.c[1];
+                            a.q_scales[row * a.q_lds + col / 16] = (uint8_t)ch.s0;
+                        }
                     }
+                } else {
+                    const int64_t col = is_res ? a.K + kc : kc;
+                    const int64_t lim = is_res ? a.K + rend : kend;
+                    ch = a.mode == MODE_PRE ? chunk_from_q<false>(a, row, col, lim)
+                                            : chunk_from_q<true>(a, row, col, lim);
                 }
-            } else {
-                const int64_t col = is_res ? a.K + kc : kc;
-                const int64_t lim = is_res ? a.K + rend : kend;
-                ch = a.mode == MODE_PRE ? chunk_from_q<false>(a, m, col, lim) : chunk_from_q<true>(a, m, col, lim);
             }
-            chunk_to_lds<MT>(lds_a + (is_res ? slots : 0), kbeg, m, kc, ch);
+            chunk_to_slots(lds_a + (is_res ? slots : 0), ((u * 16 + 4 * i) * MT + mt) * 64 + lane, MT * 64, ch);
         }
         if (lane == 0) sh_S = a.mode == MODE_PRE ? a.q_S[0] : S;
     }
     __syncthreads();                           // activation operand ready
 
     // ---- consumers: decode weights, MFMA
-    const float scale = sh_S * a.w_S[0];
+    const float scale = sh_S * w_scale;
     if (wave < kCons) {
-        float4v acc[MT];
+        float4v acc[MT], acc2[MT];                 // two MFMA chains: even / odd fragments
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
-        for (int base = 0; base < nitems; base += kRing) {
+        for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+        // Fully unrolled over at most kMaxItems items (no loop back-edge): each slot
+        // is consumed in place and refilled right after, always with the same five
+        // loads (past the last item it re-reads the current one, a cache hit), so
+        // the load stream is uniform and vmcnt is tracked exactly.
 #pragma unroll
-            for (int s = 0; s < kRing; ++s) {
-                const int it = base + s;
+        for (int it = 0; it < kMaxItems; ++it) {
+            const int s = it % kRing;
+            {
                 if (it < nitems) {
                     const int u = it % units;
                     const half8 *abase = lds_a + (size_t)u * 16 * MT * 64 + lane;
                     const bool res_u = RES && u < res_units;
-                    const WLoad cur = ring[s];
-                    if (it + kRing < nitems)
-                        load_w(a, item_row(it + kRing), kbeg + 512 * ((it + kRing) % units), g, ring[s]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t sw = (i < 2) ? cur.s.x : cur.s.y;
+                        const uint32_t sw = (i < 2) ? ring[s].s.x : ring[s].s.y;
                         const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
                         const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
-                        const uint32_t cws[4] = {cur.c[i].x, cur.c[i].y, cur.c[i].z, cur.c[i].w};
+                        const uint32_t cws[4] = {ring[s].c[i].x, ring[s].c[i].y, ring[s].c[i].z, ring[s].c[i].w};
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) {
-                                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64],
-                                                                                 b, acc[mt], 0, 0, 0);
+                                float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
+                                ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64], b,
+                                                                            ac, 0, 0, 0);
                                 if (res_u)
-                                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                        abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, acc[mt], 0, 0, 0);
+                                    ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                        abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, ac, 0, 0, 0);
                             }
                         }
                     }
@@ -452,20 +442,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
 #pragma unroll
                                 for (int e = 0; e < 4; ++e) {
                                     const int64_t m = 16 * mt + 4 * g + e;
+                                    const float tot = acc[mt][e] + acc2[mt][e];
                                     if (m < a.M) {
                                         if (a.P == 1) {
-                                            const float v = acc[mt][e] * scale;
+                                            const float v = tot * scale;
                                             if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
                                             else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
                                         } else {
-                                            st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], acc[mt][e]);
+                                            st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], tot);
                                         }
                                     }
                                 }
                         }
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+                        for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
                     }
+                }
+                if (it + kRing < kMaxItems) {
+                    const int nx = it + kRing < nitems ? it + kRing : (it < nitems ? it : nitems - 1);
+                    __builtin_amdgcn_sched_barrier(0);   // keep: consume slot s, then refill it
+                    load_w(a, item_row(nx), kbeg + 512 * (nx % units), g, ring[s]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
@@ -479,15 +476,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DArgs a) {
         if (threadIdx.x == 0) sh_last = add_dev(&tile_cnt[q], 1u) == (unsigned)a.P - 1;
         __syncthreads();
         if (sh_last) {
-            const int64_t ncols = (t_hi - t_lo) * 16;
-            for (int64_t idx = threadIdx.x; idx < a.M * ncols; idx += kThreads) {
-                const int64_t m = idx / ncols, n = 16 * t_lo + (idx - m * ncols);
+            const int64_t ncols = (t_hi - t_lo) * 16;   // multiple of 16: whole column pairs
+            for (int64_t idx = threadIdx.x; idx < a.M * (ncols / 2); idx += kThreads) {
+                const int64_t m = idx / (ncols / 2), n = 16 * t_lo + 2 * (idx - m * (ncols / 2));
                 if (n >= a.N) continue;
-                float sum = 0.0f;
-                for (int pp = 0; pp < a.P; ++pp) sum += ld_dev(&a.partials[((int64_t)pp * a.M + m) * a.N + n]);
-                const float v = sum * scale;
-                if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
-                else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
+                float s0 = 0.0f, s1 = 0.0f;
+                for (int pp = 0; pp < a.P; ++pp) {
+                    const float *src = &a.partials[((int64_t)pp * a.M + m) * a.N + n];
+                    if (n + 1 < a.N && ((a.N & 1) == 0)) {
+                        const unsigned long long v = ld_dev(reinterpret_cast<const unsigned long long *>(src));
+                        s0 += u2f((uint32_t)v);
+                        s1 += u2f((uint32_t)(v >> 32));
+                    } else {
+                        s0 += ld_dev(src);
+                        if (n + 1 < a.N) s1 += ld_dev(src + 1);
+                    }
+                }
+                for (int c = 0; c < 2 && n + c < a.N; ++c) {
+                    const float v = (c ? s1 : s0) * scale;
+                    if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n + c] = v;
+                    else static_cast<uint16_t *>(a.y)[m * a.ldy + n + c] = f32_to_bf16_rne(v);
+                }
             }
             if (threadIdx.x == 0) st_dev(&tile_cnt[q], 0u);
         }
@@ -539,6 +548,7 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
             const int64_t G = P * Q;
             if (G > cap || Q > kMaxTileCounters) continue;
             const int items = tw * (int)(U < ku ? U : ku);
+            if (items > kMaxItems) continue;
             const double cost = items + 0.15 * (double)P + (G < 192 ? 4.0 : 0.0);
             if (cost < best) { best = cost; bestU = U; besttw = tw; }
         }
