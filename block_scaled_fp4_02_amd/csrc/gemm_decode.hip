@@ -266,9 +266,9 @@ void decode_kernel(DArgs a) {
     const int64_t t_first = t_lo + wave;
     const int ntiles = (wave < kCons && t_first < t_hi) ? (int)((t_hi - t_first + kCons - 1) / kCons) : 0;
     const int nitems = ntiles * units;
-    auto item_row = [&](int it) -> int64_t {
+    auto item_row = [&](int it) -> int64_t {     // clamped into [0, N): loads never leave W
         const int64_t n = 16 * (t_first + (int64_t)(it / units) * kCons) + r16;
-        return n < a.N ? n : a.N - 1;
+        return n < 0 ? 0 : (n < a.N ? n : a.N - 1);
     };
 
     // Loaded before the weight ring: vmcnt is in order, so anything loaded after
@@ -397,7 +397,7 @@ void decode_kernel(DArgs a) {
 
     // ---- consumers: decode weights, MFMA
     const float scale = sh_S * w_scale;
-    if (wave < kCons) {
+    if (wave < kCons && nitems > 0) {            // waves without tiles issue no loads at all
         float4v acc[MT], acc2[MT];                 // two MFMA chains: even / odd fragments
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
