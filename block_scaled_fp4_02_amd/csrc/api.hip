@@ -50,12 +50,6 @@ size_t gemm_ws(int64_t M, int64_t N, int64_t K, int64_t S) {
     return 0;
 }
 
-unsigned spin_limit() {
-    const char *e = std::getenv("NVFP4_SPIN_LIMIT");
-    if (e && *e) return (unsigned)std::strtoul(e, nullptr, 10);
-    return 4096;      // polls of ~1 us: a wait gives up after a few ms
-}
-
 struct Carver {
     uint8_t *p; size_t left; bool ok = true;
     uint8_t *take(size_t n) {
@@ -69,11 +63,22 @@ int elem_size(int xt) { return xt == NVFP4_BF16 ? 2 : 4; }
 
 // A tensor with no elements may carry null code/scale pointers; its scale
 // pointer is still required (the quantizer writes S = 1 for it).
-nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t K) {
+// Tiled layout (weights only): strips of 16 rows, strides fixed by K.
+int64_t tiled_ldc(int64_t K) { return (K + 511) / 512 * 4096; }
+int64_t tiled_lds(int64_t K) { return (K + 511) / 512 * 512; }
+
+nvfp4_status check_tensor(const nvfp4_tensor *t, int64_t rows, int64_t K, bool allow_tiled = false) {
     if (!t || !t->tensor_scale) return NVFP4_ERR_NULL;
+    if (t->layout != NVFP4_LAYOUT_ROWMAJOR && t->layout != NVFP4_LAYOUT_TILED) return NVFP4_ERR_SHAPE;
+    if (t->layout == NVFP4_LAYOUT_TILED && !allow_tiled) return NVFP4_ERR_UNSUPPORTED;
     if (t->rows != rows || t->K != K || rows < 0 || K < 0 || K % 16) return NVFP4_ERR_SHAPE;
     if (rows == 0 || K == 0) return aligned(t->tensor_scale, 4) ? NVFP4_OK : NVFP4_ERR_ALIGN;
     if (!t->codes || !t->scales) return NVFP4_ERR_NULL;
+    if (t->layout == NVFP4_LAYOUT_TILED) {
+        if (t->ld_codes != tiled_ldc(K) || t->ld_scales != tiled_lds(K)) return NVFP4_ERR_SHAPE;
+        if (!aligned(t->codes, 16) || !aligned(t->scales, 8) || !aligned(t->tensor_scale, 4)) return NVFP4_ERR_ALIGN;
+        return NVFP4_OK;
+    }
     if (t->ld_codes < K / 2 || t->ld_scales < K / 16) return NVFP4_ERR_SHAPE;
     if (t->ld_codes % 16 || t->ld_scales % 8 || !aligned(t->codes, 16) || !aligned(t->scales, 8) ||
         !aligned(t->tensor_scale, 4))
@@ -131,15 +136,16 @@ nvfp4_status enqueue_gemm(const nvfp4_tensor &a, const nvfp4_tensor &w, int64_t 
         g.x = nullptr;
         g.q_codes = a.codes; g.q_ldc = a.ld_codes; g.q_scales = a.scales; g.q_lds = a.ld_scales; g.q_S = a.tensor_scale;
         g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
+        g.w_tiled = w.layout == NVFP4_LAYOUT_TILED;
         g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
         g.y = y; g.yt = yt; g.ldy = ldy;
         g.header = header; g.scratch = scratch; g.scratch_bytes = scratch_bytes;
-        g.spin_limit = spin_limit();
         e = launch_decode(g, st);
     } else {
         PrefillLaunch g;
         g.a_codes = a.codes; g.a_ldc = a.ld_codes; g.a_scales = a.scales; g.a_lds = a.ld_scales; g.a_S = a.tensor_scale;
         g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
+        g.w_tiled = w.layout == NVFP4_LAYOUT_TILED;
         g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
         g.y = y; g.yt = yt; g.ldy = ldy;
         e = launch_prefill(g, st);
@@ -152,13 +158,14 @@ nvfp4_status enqueue_fused(const void *x, int xt, int64_t ldx, const float *stat
                            const nvfp4_tensor &w, int64_t M, int64_t K, int64_t S, void *y, int yt, int64_t ldy,
                            unsigned *header, uint8_t *scratch, size_t scratch_bytes, hipStream_t st) {
     DecodeLaunch g{};
-    g.x = x; g.x_bf16 = xt == NVFP4_BF16; g.ldx = ldx; g.static_S = static_S;
+    (void)xt;                                   // decode_can_fuse admitted bf16 only
+    g.x = x; g.ldx = ldx; g.static_S = static_S;
     g.q_codes = q.codes; g.q_ldc = q.ld_codes; g.q_scales = q.scales; g.q_lds = q.ld_scales; g.q_S = q.tensor_scale;
     g.w_codes = w.codes; g.w_ldc = w.ld_codes; g.w_scales = w.scales; g.w_lds = w.ld_scales; g.w_S = w.tensor_scale;
+    g.w_tiled = w.layout == NVFP4_LAYOUT_TILED;
     g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
     g.y = y; g.yt = yt; g.ldy = ldy;
     g.header = header; g.scratch = scratch; g.scratch_bytes = scratch_bytes;
-    g.spin_limit = spin_limit();
     const hipError_t e = launch_decode(g, st);
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
@@ -205,7 +212,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
     if (!y && M > 0 && w->rows > 0) return NVFP4_ERR_NULL;
     if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
     if (M < 0 || K < 0 || K % 16) return NVFP4_ERR_SHAPE;
-    CHECK(check_tensor(w, w->rows, K));
+    CHECK(check_tensor(w, w->rows, K, true));
     const int64_t N = w->rows;
     if (ldy < N) return NVFP4_ERR_SHAPE;
     if (a_q) CHECK(check_tensor(a_q, M, K));
@@ -231,7 +238,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
     uint8_t *scratch = sb ? c.take(sb) : nullptr;
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
     const bool skinny = M <= kSkinnyMaxM && K > 0;
-    if (!a_q && skinny && decode_can_fuse(M, N, K, 0))
+    if (!a_q && skinny && decode_can_fuse(M, N, K, 0, xt == NVFP4_BF16))
         return enqueue_fused(x, xt, ldx, nullptr, aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
     if (!a_q) CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, st));
     return enqueue_gemm(aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
@@ -247,7 +254,7 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
     CHECK(check_x(x, xt, M, K, ldx));
     CHECK(check_opts(opts, K));
     const int64_t S = opts ? opts->residue_cols : 0;
-    CHECK(check_tensor(w, w->rows, K));
+    CHECK(check_tensor(w, w->rows, K, true));
     const int64_t N = w->rows;
     if (ldy < N) return NVFP4_ERR_SHAPE;
     if (a_aug_out) CHECK(check_tensor(a_aug_out, M, K + S));
@@ -274,12 +281,28 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
     const bool plain = !opts || (!opts->gamma && !opts->perm);
     const bool skinny = M <= kSkinnyMaxM && K > 0;
-    if (N > 0 && plain && skinny && decode_can_fuse(M, N, K, S))
+    if (N > 0 && plain && skinny && decode_can_fuse(M, N, K, S, xt == NVFP4_BF16))
         return enqueue_fused(x, xt, ldx, opts ? opts->static_tensor_scale : nullptr, aq, *w, M, K, S, y, yt, ldy,
                              header, scratch, sb, st);
     CHECK(enqueue_quantize(x, xt, M, K, ldx, opts, aq, partials, rscale, st));
     if (N == 0) return NVFP4_OK;
     return enqueue_gemm(aq, *w, M, K, S, y, yt, ldy, header, scratch, sb, st);
+}
+
+nvfp4_status nvfp4_pack_tiled(const nvfp4_tensor *src, const nvfp4_tensor *dst, void *stream) {
+    if (!src || !dst) return NVFP4_ERR_NULL;
+    CHECK(check_tensor(src, src->rows, src->K));
+    if (dst->layout != NVFP4_LAYOUT_TILED) return NVFP4_ERR_SHAPE;
+    CHECK(check_tensor(dst, src->rows, src->K, true));
+    if (src->tensor_scale == dst->tensor_scale && src->rows > 0 && src->K > 0) return NVFP4_ERR_SHAPE;
+    PackLaunch g;
+    g.src_codes = src->codes; g.src_ldc = src->ld_codes; g.src_scales = src->scales; g.src_lds = src->ld_scales;
+    g.src_S = src->tensor_scale;
+    g.dst_codes = dst->codes; g.dst_ldc = dst->ld_codes; g.dst_scales = dst->scales; g.dst_lds = dst->ld_scales;
+    g.dst_S = dst->tensor_scale;
+    g.rows = src->rows; g.K = src->K;
+    const hipError_t e = launch_pack_tiled(g, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
 nvfp4_status nvfp4_channel_absmax(const void *x, int xt, int64_t rows, int64_t K, int64_t ldx,

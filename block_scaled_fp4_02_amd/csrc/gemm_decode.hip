@@ -12,34 +12,27 @@
 // once and doing everything else while those loads are in flight:
 //
 //  * a workgroup owns a K range of U 512-column units and T 16-row weight
-//    tiles; it has four consumer waves and one producer wave;
-//  * consumer waves issue the loads of their (tile, unit) items at once
-//    (a ring of 4 items: 4 x 16 B codes + 8 B scales per lane each), wait at one
-//    barrier for the activation operand, then decode each weight item in
+//    tiles; it has four consumer waves and four producer waves;
+//  * producer waves issue their (small) activation loads first; after one
+//    barrier the consumer waves issue the loads of their (tile, unit) items at
+//    once (a ring of up to 4 items: 4 x 16 B codes + 8 B scales per lane
+//    each), so the activation data is ahead of the weights in the CU's memory
+//    queue and the operand is ready long before the weights have landed;
+//  * producers write the K range's operand into LDS as exact f16 e*d values
+//    in A-operand lane order; consumers then decode each weight item in
 //    registers (v_cvt_scalef32_pk_f16_fp4 + v_pk_mul_f16, exact) and issue 16
-//    v_mfma_f32_16x16x32_f16 per item, refilling the ring; residue columns
-//    reuse the decoded weight registers for a second MFMA;
-//  * the producer wave has no weight loads in flight, so its waits are its own
-//    (vmcnt is in order on gfx9): it quantizes the activations and writes the
-//    K range's operand into LDS as exact f16 e*d values in A-operand lane order;
+//    v_mfma_f32_16x16x32_f16 per item as items land, refilling the ring;
+//    residue columns reuse the decoded weight registers for a second MFMA;
 //  * with more than one K range, partial tiles go to the workspace through
 //    device-coherent stores and the last workgroup of each tile group sums
 //    them in fixed order (deterministic) and writes y.
 //
-// Activation quantization (raw activations in the call), chosen per shape:
-//  LOCAL  X is small: every workgroup computes amax(X) itself and quantizes
-//         its own K range -- no communication at all;
-//  SYNC1  the grid agrees on amax(X) (each workgroup publishes the maximum of
-//         1/G of X, one grid-wide wait), then each quantizes its own K range;
-//  SYNC2  as SYNC1, then each workgroup quantizes 1/G of X's blocks into the
-//         quantized-activation buffer and a second wait makes them visible.
-// Cross-workgroup data moves through relaxed device-scope (sc1) loads and
-// stores; a publisher waits for its own stores (s_waitcnt vmcnt(0)) and then
-// counts. Grid-wide counters are hierarchical (16 sub-counters, then one top
-// counter) because same-address device atomics serialize, and carry a call
-// index in their upper half so they never need resetting. Every wait is
-// bounded: past the spin limit a workgroup recomputes what it waited for from
-// X itself (same arithmetic, same result), so no wait can hang.
+// Activations: PRE reads an already quantized tensor; LOCAL (raw bf16 X with
+// M K <= 16384) has every workgroup read all of X, take amax(X) itself and
+// quantize its own K range -- no communication between workgroups. Larger raw
+// activations are quantized by the quantize kernels first: a grid-wide wait
+// inside a kernel that saturates HBM costs several microseconds, since every
+// round trip queues behind the weight stream.
 #include <cstdio>
 #include <cstdlib>
 
@@ -49,17 +42,30 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kCons = 4;                       // consumer waves
-constexpr int kThreads = 64 * (kCons + 1);     // plus one producer wave
-constexpr int kGroups = 16;                    // sub-counters per grid-wide wait
+constexpr int kCons = 4;                       // consumer waves: weights and MFMA
+constexpr int kProd = 4;                       // producer waves: the activation operand
+constexpr int kThreads = 64 * (kCons + kProd);
+constexpr int kPThreads = 64 * kProd;
 constexpr int kMaxItems = 8;                   // (tile, unit) items per consumer wave
+constexpr int kPreItems = 2;                   // items each consumer issues before the operand barrier
 constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
 constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
+constexpr int64_t kLocalMaxElems = 16384;      // LOCAL: X read by every workgroup (8 units of 8 per lane)
+constexpr int kLocalLoads = (int)(kLocalMaxElems / 8 / kPThreads);
 
-enum Mode { MODE_PRE = 0, MODE_LOCAL = 1, MODE_SYNC1 = 2, MODE_SYNC2 = 3 };
+enum Mode { MODE_PRE = 0, MODE_LOCAL = 1 };
+
+#ifdef NVFP4_TIMELINE
+// Profiling builds only: per (workgroup, wave, point) s_memrealtime stamps (100 MHz).
+__device__ unsigned long long g_timeline[1024 * 8 * 8];
+#define TL(point) do { if ((threadIdx.x & 63) == 0 && blockIdx.x < 1024) \
+    g_timeline[(blockIdx.x * 8 + (threadIdx.x >> 6)) * 8 + (point)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define TL(point) do { } while (0)
+#endif
 
 struct DArgs {
-    const void *x; int x_bf16; int64_t ldx;   // raw activations (modes LOCAL/SYNC1/SYNC2)
+    const void *x; int64_t ldx;               // raw bf16 activations (LOCAL)
     const float *static_S;
     uint8_t *q_codes; int64_t q_ldc;          // quantized activations [M][K + res]
     uint8_t *q_scales; int64_t q_lds;
@@ -69,12 +75,10 @@ struct DArgs {
     const float *w_S;
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
-    uint8_t *header;                          // zero-kept counters
-    float *amax_slots;                        // G floats
+    uint8_t *header;                          // zero-kept tile counters
     float *partials;                          // P x M x N floats
     int U, P, T, tw, G, mode;
     int64_t NT;
-    unsigned spin_limit;
 };
 
 template <typename T>
@@ -85,60 +89,6 @@ template <typename T>
 __device__ inline T add_dev(T *p, T v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 __device__ inline void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-// ------------------------------------------------------------ grid-wide wait
-// Counter word: upper 32 bits = call index, lower = arrivals in this call.
-struct Sync { unsigned long long *top, *sub; };
-
-// Header bytes [1536 s, 1536 s + 64 (kGroups + 1)) belong to sync s (s = 0, 1):
-// the top counter, then one 64-byte line per sub-counter.
-constexpr size_t kSyncBytes = 1536;
-static_assert(64 * (kGroups + 1) <= (int)kSyncBytes, "sub-counters overflow their sync's region");
-static_assert(2 * kSyncBytes <= kTileCntOffset - 64, "sync regions overlap the timeout counter");
-
-__device__ inline Sync sync_at(uint8_t *header, int s) {
-    Sync y;
-    y.top = reinterpret_cast<unsigned long long *>(header + kSyncBytes * s);
-    y.sub = reinterpret_cast<unsigned long long *>(header + kSyncBytes * s + 64);
-    return y;
-}
-
-// One lane per workgroup: count this workgroup in; returns the call index to wait past.
-__device__ inline unsigned sync_arrive(Sync y, int G) {
-    const int NG = G < kGroups ? G : kGroups;
-    const int grp = (int)(blockIdx.x % NG);
-    const unsigned members = (unsigned)((G - grp + NG - 1) / NG);
-    const unsigned mine = (unsigned)(ld_dev(y.top) >> 32);   // cannot advance before we arrive
-    unsigned long long *sc = y.sub + 8 * grp;                 // 64 bytes apart
-    const unsigned long long old = add_dev(sc, 1ull);
-    if ((unsigned)old + 1 == members) {
-        add_dev(sc, (1ull << 32) - members);                  // next call, zero arrivals
-        const unsigned long long ot = add_dev(y.top, 1ull);
-        if ((unsigned)ot + 1 == (unsigned)NG) add_dev(y.top, (1ull << 32) - (unsigned long long)NG);
-    }
-    return mine;
-}
-
-// Header word counting waits that gave up (diagnostics; read by the host).
-constexpr size_t kTimeoutCounterOffset = 4096 - 64;
-
-__device__ inline bool sync_wait(Sync y, unsigned mine, unsigned limit, uint8_t *header) {
-    unsigned it = 0;
-    while ((unsigned)(ld_dev(y.top) >> 32) == mine) {
-        if (++it > limit) {
-            add_dev(reinterpret_cast<unsigned *>(header + kTimeoutCounterOffset), 1u);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-    return true;
-}
 
 // ------------------------------------------------------------ weight items
 struct WLoad {
@@ -164,101 +114,238 @@ __device__ inline void load_w(const DArgs &a, int64_t n, int64_t kb, int g, WLoa
     w.s = *reinterpret_cast<const uint2 *>(srow + (k0 < a.K ? k0 / 16 : 0));
 }
 
-// ------------------------------------------------------------ producer wave
-// amax(X) over all rows and columns by one wave.
-__device__ inline float wave_amax_x(const DArgs &a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t KB = a.K / 16, NB = a.M * KB;
-    float m = 0.0f;
-    for (int64_t b = lane; b < NB; b += 64) {
-        const int64_t row = b / KB, blk = b - row * KB;
-        float v[16];
-        load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
+// The same item from tiled weights: lane p's 4 x 16 B and 8 B are stored in
+// lane order, so every load of the wave is one contiguous run (padding is zero).
+__device__ inline void load_w_tiled(const DArgs &a, int64_t tile, int64_t unit, int lane, WLoad &w) {
+    const uint8_t *c = a.w_codes + tile * a.w_ldc + unit * 4096 + 16 * lane;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-    }
-    return wave_max(m);
+    for (int i = 0; i < 4; ++i) w.c[i] = *reinterpret_cast<const uint4 *>(c + 1024 * i);
+    w.s = *reinterpret_cast<const uint2 *>(a.w_scales + tile * a.w_lds + unit * 512 + 8 * lane);
 }
+
+// ------------------------------------------------------------ activation operand
+// The K range's operand lives in LDS as exact f16 values e*d in MFMA A-operand
+// order: slot ((u * 16 + 4 i + j) * MT + mt) * 64 + 16 g + r holds row
+// 16 mt + r, columns kbeg + 512 u + 128 g + 32 i + 8 j .. + 8 (u: 512-column
+// unit, g: lane quarter, i: 32-column step, j: 8-column fragment). A "chunk" is
+// 32 columns of one row, i.e. the four slots j = 0..3. The residue columns'
+// operand is a second copy of the same layout, `slots` further on.
 
 __device__ inline float scale_of(float amax) { return amax > 0.0f ? amax / 2688.0f : 1.0f; }
 
-// A 32-column chunk of one activation row as codes + 2 block scales.
-struct Chunk { uint32_t c[4]; uint32_t s0, s1; };
+__device__ inline unsigned wave_max_u(unsigned v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o));
+    return v;
+}
 
-// Quantize columns [k, k + 32) of row m from X (blocks beyond K stay zero);
-// res selects the residue of those columns.
-__device__ inline Chunk chunk_from_x(const DArgs &a, int64_t m, int64_t k, bool res, float S) {
-    Chunk ch = {{0, 0, 0, 0}, 0, 0};
+// The workgroup's K range and its chunk counts.
+struct Range {
+    int64_t kbeg, kend, rend;   // columns [kbeg, kend); residue columns [kbeg, rend)
+    int units, res_units;       // 512-column units of each
+    int npm, npr;               // chunk positions per row (32 columns each)
+};
+
+// Slot of the j = 0 fragment of the chunk of row m starting at column kc.
+template <int MT>
+__device__ inline int chunk_slot(int64_t kbeg, int m, int64_t kc) {
+    const int off = (int)(kc - kbeg);
+    const int u = off >> 9, w = (off >> 5) & 15;
+    return ((u * 16 + 4 * (w & 3)) * MT + (m >> 4)) * 64 + 16 * (w >> 2) + (m & 15);
+}
+
+// Chunk c of the range (rows fastest): main chunks, then residue chunks.
+// key = LDS slot of fragment j = 0, plus kV1 when the chunk's second 16-column
+// block is inside the data; -1 past the chunk list.
+constexpr int kV1 = 1 << 30;
+struct ChunkPos {
+    int64_t m, col;   // row; stored column of the chunk start (residue columns follow column K)
+    int key;
+};
+
+template <int MT>
+__device__ inline ChunkPos chunk_pos(const DArgs &a, const Range &r, int c, int slots) {
+    ChunkPos f;
+    const unsigned M = (unsigned)a.M;
+    const unsigned nch = M * (unsigned)(r.npm + r.npr);
+    if ((unsigned)c >= nch) { f.m = 0; f.col = 0; f.key = -1; return f; }
+    const unsigned m = (unsigned)c % M, pos = (unsigned)c / M;
+    const bool res = (int)pos >= r.npm;
+    const int64_t kc = r.kbeg + 32 * (int64_t)(res ? (int)pos - r.npm : (int)pos);
+    f.m = m;
+    f.col = res ? a.K + kc : kc;
+    f.key = chunk_slot<MT>(r.kbeg, (int)m, kc) + (res ? slots : 0) + (kc + 16 < (res ? r.rend : r.kend) ? kV1 : 0);
+    return f;
+}
+
+// A chunk of the quantized-activation buffer: codes (low nibble = even column)
+// and the two block scales.
+struct QChunk { unsigned long long lo, hi; uint32_t s0, s1; int key; };
+
+// Always the same four loads; a chunk past the list, or a second block past the
+// data, reads row 0's first bytes instead and is zeroed when stored.
+__device__ inline QChunk qchunk_load(const DArgs &a, const ChunkPos &f) {
+    const bool v1 = f.key >= 0 && (f.key & kV1);
+    const uint8_t *crow = a.q_codes + f.m * a.q_ldc;
+    const uint8_t *srow = a.q_scales + f.m * a.q_lds;
+    const unsigned long long *p0 = reinterpret_cast<const unsigned long long *>(crow + f.col / 2);
+    const unsigned long long *p1 =
+        reinterpret_cast<const unsigned long long *>(crow + (v1 ? f.col / 2 + 8 : f.col / 2));
+    const uint8_t *q0 = srow + f.col / 16, *q1 = srow + (v1 ? f.col / 16 + 1 : f.col / 16);
+    QChunk q;
+    q.lo = *p0;
+    q.hi = *p1;
+    q.s0 = *q0;
+    q.s1 = *q1;
+    q.key = f.key;
+    return q;
+}
+
+template <int MT>
+__device__ inline void qchunk_store(half8 *lds, const QChunk &q) {
+    if (q.key < 0) return;
+    const bool v1 = q.key & kV1;
+    const int slot = q.key & (kV1 - 1);
+    const half2v d0 = scale_pair(q.s0), d1 = scale_pair(v1 ? q.s1 : 0u);
+    const uint32_t hi0 = v1 ? (uint32_t)q.hi : 0u, hi1 = v1 ? (uint32_t)(q.hi >> 32) : 0u;
+    lds[slot] = decode8((uint32_t)q.lo, d0);
+    lds[slot + MT * 64] = decode8((uint32_t)(q.lo >> 32), d0);
+    lds[slot + 2 * MT * 64] = decode8(hi0, d1);
+    lds[slot + 3 * MT * 64] = decode8(hi1, d1);
+}
+
+// 32 bf16 activations of one row (a raw chunk); the second block is read only
+// inside the data (else the first block again).
+struct XChunk { uint4 w[4]; };
+
+__device__ inline XChunk xchunk_load(const DArgs &a, int64_t m, int64_t kc, bool v1) {
+    const uint16_t *row = static_cast<const uint16_t *>(a.x) + m * a.ldx;
+    XChunk x;
+    x.w[0] = *reinterpret_cast<const uint4 *>(row + kc);
+    x.w[1] = *reinterpret_cast<const uint4 *>(row + kc + 8);
+    x.w[2] = *reinterpret_cast<const uint4 *>(row + (v1 ? kc + 16 : kc));
+    x.w[3] = *reinterpret_cast<const uint4 *>(row + (v1 ? kc + 24 : kc + 8));
+    return x;
+}
+
+__device__ inline void bf16x16(const uint4 &p, const uint4 &q, float *v) {
+    const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[2 * i] = u2f(w[i] << 16);
+        v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+    }
+}
+
+// Quantize a raw chunk (row m, columns kc..) against S into its LDS slots and,
+// for columns below the residue bound, the residue's slots; the writer also
+// stores codes and scales into the quantized-activation buffer.
+template <int MT, bool RES>
+__device__ inline void xchunk_quantize(const DArgs &a, half8 *lds, int slots, int64_t kbeg, int64_t rend,
+                                       int64_t m, int64_t kc, bool v1, const XChunk &x, float S, bool writer) {
     const float t = 6.0f * S;
+    uint32_t mc[4] = {0, 0, 0, 0}, ms[2] = {0, 0}, rc[4] = {0, 0, 0, 0}, rs[2] = {0, 0};
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-        const int64_t kb = k + 16 * b;
-        if (kb + 16 <= a.K) {
-            float v[16];
-            load16_any(a.x, a.x_bf16, m * a.ldx + kb, v);
-            uint32_t cw[2];
-            float d;
-            uint32_t db = encode_block(v, S, t, cw, d);
-            if (res) {
-                float r[16];
-                block_residue(v, cw, d, S, r);
-                db = encode_block(r, S, t, cw, d);
-            }
-            ch.c[2 * b] = cw[0];
-            ch.c[2 * b + 1] = cw[1];
-            if (b == 0) ch.s0 = db; else ch.s1 = db;
+        if (b == 1 && !v1) break;
+        float v[16];
+        bf16x16(x.w[2 * b], x.w[2 * b + 1], v);
+        uint32_t cw[2];
+        float d;
+        ms[b] = encode_block(v, S, t, cw, d);
+        mc[2 * b] = cw[0];
+        mc[2 * b + 1] = cw[1];
+        if (RES && kc + 16 * b < rend) {
+            block_residue(v, cw, d, S, v);          // element-wise, in place
+            rs[b] = encode_block(v, S, t, cw, d);
+            rc[2 * b] = cw[0];
+            rc[2 * b + 1] = cw[1];
         }
     }
-    return ch;
-}
-
-// The same chunk read from the quantized-activation buffer (column kc of the
-// stored tensor; residue columns are stored after column K).
-template <bool COHERENT>
-__device__ inline Chunk chunk_from_q(const DArgs &a, int64_t m, int64_t kc, int64_t kend_cols) {
-    Chunk ch = {{0, 0, 0, 0}, 0, 0};
-    const uint8_t *cp = a.q_codes + m * a.q_ldc + kc / 2;
-    const uint8_t *sp = a.q_scales + m * a.q_lds + kc / 16;
-    if (kc + 32 <= kend_cols) {
-        const unsigned long long *p = reinterpret_cast<const unsigned long long *>(cp);
-        const unsigned long long lo = COHERENT ? ld_dev(p) : p[0];
-        const unsigned long long hi = COHERENT ? ld_dev(p + 1) : p[1];
-        ch.c[0] = (uint32_t)lo; ch.c[1] = (uint32_t)(lo >> 32);
-        ch.c[2] = (uint32_t)hi; ch.c[3] = (uint32_t)(hi >> 32);
-        ch.s0 = COHERENT ? ld_dev(sp) : sp[0];
-        ch.s1 = COHERENT ? ld_dev(sp + 1) : sp[1];
-    } else if (kc + 16 <= kend_cols) {
-        const unsigned long long *p = reinterpret_cast<const unsigned long long *>(cp);
-        const unsigned long long lo = COHERENT ? ld_dev(p) : p[0];
-        ch.c[0] = (uint32_t)lo; ch.c[1] = (uint32_t)(lo >> 32);
-        ch.s0 = COHERENT ? ld_dev(sp) : sp[0];
-    }
-    return ch;
-}
-
-__device__ inline void chunk_to_slots(half8 *lds, int base_slot, int stride, const Chunk &ch) {
-    const half2v d0 = scale_pair(ch.s0), d1 = scale_pair(ch.s1);
+    const int slot = chunk_slot<MT>(kbeg, (int)m, kc);
+    {
+        const half2v d0 = scale_pair(ms[0]), d1 = scale_pair(ms[1]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds[base_slot + j * stride] = decode8(ch.c[j], j < 2 ? d0 : d1);
+        for (int j = 0; j < 4; ++j) lds[slot + j * MT * 64] = decode8(mc[j], j < 2 ? d0 : d1);
+    }
+    const bool has_res = RES && kc < rend;
+    if (has_res) {
+        const half2v d0 = scale_pair(rs[0]), d1 = scale_pair(rs[1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lds[slots + slot + j * MT * 64] = decode8(rc[j], j < 2 ? d0 : d1);
+    }
+    if (writer) {
+        uint8_t *crow = a.q_codes + m * a.q_ldc;
+        uint8_t *srow = a.q_scales + m * a.q_lds;
+        unsigned long long *cp = reinterpret_cast<unsigned long long *>(crow + kc / 2);
+        cp[0] = (unsigned long long)mc[0] | ((unsigned long long)mc[1] << 32);
+        srow[kc / 16] = (uint8_t)ms[0];
+        if (v1) {
+            cp[1] = (unsigned long long)mc[2] | ((unsigned long long)mc[3] << 32);
+            srow[kc / 16 + 1] = (uint8_t)ms[1];
+        }
+        if (has_res) {
+            unsigned long long *rp = reinterpret_cast<unsigned long long *>(crow + (a.K + kc) / 2);
+            rp[0] = (unsigned long long)rc[0] | ((unsigned long long)rc[1] << 32);
+            srow[(a.K + kc) / 16] = (uint8_t)rs[0];
+            if (kc + 16 < rend) {
+                rp[1] = (unsigned long long)rc[2] | ((unsigned long long)rc[3] << 32);
+                srow[(a.K + kc) / 16 + 1] = (uint8_t)rs[1];
+            }
+        }
+    }
+}
+
+// Zero every operand slot that no chunk writes: rows >= M and chunk positions
+// past the data (LDS only).
+template <int MT>
+__device__ inline void zero_unwritten(half8 *lds, const Range &r, int slots, int64_t M) {
+    const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) - kCons;   // producer waves
+    constexpr int nwaves = kProd;
+    const int row = lane & 15, g = lane >> 4;
+    const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int reg = 0; reg < 2; ++reg) {
+        const int n = (reg == 0 ? r.units : r.res_units) * 16 * MT;   // 64-slot groups
+        const int64_t lim = reg == 0 ? r.kend : r.rend;
+        half8 *base = lds + (reg == 0 ? 0 : slots);
+        for (int grp = wave; grp < n; grp += nwaves) {
+            const int mt = grp % MT, q4 = grp / MT;
+            const int64_t kc = r.kbeg + 512 * (q4 >> 4) + 128 * g + 32 * ((q4 >> 2) & 3);
+            if (16 * mt + row >= M || kc >= lim) base[grp * 64 + lane] = z;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- kernel
-template <int MT, bool RES>
+template <int MT, bool RES, bool TILED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
     constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
+    // Items issued before the operand barrier; the rest of the ring is issued
+    // after it, so that computing on landed items overlaps the (throttled)
+    // issue of later loads.
+    constexpr int kPre = kPreItems < kRing ? kPreItems : kRing;
     extern __shared__ half8 lds_a[];          // [U][16][MT][64] (+ residue copy)
     __shared__ float sh_S;
+    __shared__ float sh_part[kProd];
+    __shared__ unsigned sh_cnt;
     __shared__ int sh_last;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave index as a scalar: branches on it are uniform (barriers inside them stay per wave)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r16 = lane & 15;
     const int p = blockIdx.x % a.P;
     const int64_t q = blockIdx.x / a.P;
-    const int64_t kbeg = (int64_t)p * a.U * 512;
-    const int64_t kend = kbeg + (int64_t)a.U * 512 < a.K ? kbeg + (int64_t)a.U * 512 : a.K;
-    const int units = (int)((kend - kbeg + 511) / 512);
-    const int64_t rend = RES ? (a.res_cols < kend ? a.res_cols : kend) : kbeg;
-    const int res_units = RES ? (rend > kbeg ? (int)((rend - kbeg + 511) / 512) : 0) : 0;
+    Range rg;
+    rg.kbeg = (int64_t)p * a.U * 512;
+    rg.kend = rg.kbeg + (int64_t)a.U * 512 < a.K ? rg.kbeg + (int64_t)a.U * 512 : a.K;
+    rg.units = (int)((rg.kend - rg.kbeg + 511) / 512);
+    rg.rend = RES ? (a.res_cols < rg.kend ? a.res_cols : rg.kend) : rg.kbeg;
+    if (rg.rend < rg.kbeg) rg.rend = rg.kbeg;
+    rg.res_units = (int)((rg.rend - rg.kbeg + 511) / 512);
+    rg.npm = (int)((rg.kend - rg.kbeg + 31) / 32);
+    rg.npr = (int)((rg.rend - rg.kbeg + 31) / 32);
+    const int64_t kbeg = rg.kbeg;
+    const int units = rg.units, res_units = rg.res_units;
     const int slots = a.U * 16 * MT * 64;
     const int64_t t_lo = q * a.T, t_hi = (q + 1) * a.T < a.NT ? (q + 1) * a.T : a.NT;
 
@@ -266,134 +353,107 @@ void decode_kernel(DArgs a) {
     const int64_t t_first = t_lo + wave;
     const int ntiles = (wave < kCons && t_first < t_hi) ? (int)((t_hi - t_first + kCons - 1) / kCons) : 0;
     const int nitems = ntiles * units;
-    auto item_row = [&](int it) -> int64_t {     // clamped into [0, N): loads never leave W
-        const int64_t n = 16 * (t_first + (int64_t)(it / units) * kCons) + r16;
-        return n < 0 ? 0 : (n < a.N ? n : a.N - 1);
+    // Item it = (tile t_first + kCons * (it / units), unit it % units of the
+    // range); rows and tiles are clamped into W, so loads never leave it.
+    auto load_item = [&](int it, WLoad &w) {
+        const int64_t t = t_first + (int64_t)(it / units) * kCons;
+        if (TILED) {
+            load_w_tiled(a, t < 0 ? 0 : (t < a.NT ? t : a.NT - 1), kbeg / 512 + it % units, lane, w);
+        } else {
+            const int64_t n = 16 * t + r16;
+            load_w(a, n < 0 ? 0 : (n < a.N ? n : a.N - 1), kbeg + 512 * (it % units), g, w);
+        }
     };
 
-    // Loaded before the weight ring: vmcnt is in order, so anything loaded after
-    // the ring and used early would wait for the whole ring.
+    // The two kinds of wave meet at two workgroup barriers (the producers'
+    // loads are out; the operand is complete); the producers' work sits in its
+    // own branch so that it never shares registers with the consumers' loads in
+    // flight.
+    TL(0);
     const float w_scale = a.w_S[0];
     WLoad ring[kRing];
+    if (tid == 0) sh_cnt = 0;
     if (wave < kCons) {
-        // ---- consumers: every weight load of the first items, right away
+        __syncthreads();                       // the producers' loads are out
+        if (nitems > 0) {
 #pragma unroll
-        for (int s = 0; s < kRing; ++s)
-            if (s < nitems) load_w(a, item_row(s), kbeg + 512 * (s % units), g, ring[s]);
+            for (int s = 0; s < kPre; ++s) load_item(s < nitems ? s : nitems - 1, ring[s]);
+        }
+        TL(1);
+        __syncthreads();                       // operand complete
     } else {
-        // ---- producer: activation operand of this K range into LDS
-        float S = 0.0f;
-        bool from_x = a.mode == MODE_LOCAL || a.mode == MODE_SYNC1;
-        if (a.mode != MODE_PRE) {
+        const int ptid = tid - 64 * kCons, pw = wave - kCons;
+        if (a.mode == MODE_PRE) {
+            // chunks ptid + 256 t of the quantized activations
+            const float S = ptid == 0 ? a.q_S[0] : 0.0f;
+            QChunk qc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                qc[t] = qchunk_load(a, chunk_pos<MT>(a, rg, ptid + kPThreads * t, slots));
+            __syncthreads();                   // loads out: consumers may issue theirs
+            zero_unwritten<MT>(lds_a, rg, slots, a.M);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) qchunk_store<MT>(lds_a, qc[t]);
+            if (ptid == 0) sh_S = S;
+            TL(1);
+            __syncthreads();                   // operand complete
+        } else {
+            // LOCAL: raw chunk ptid of the range, and this wave's quarter of X for amax(X)
+            const int nraw = (int)a.M * rg.npm;
+            const ChunkPos f = chunk_pos<MT>(a, rg, ptid < nraw ? ptid : 1 << 30, slots);
+            const bool v1 = f.key >= 0 && (f.key & kV1);
+            const XChunk xc = xchunk_load(a, f.m, f.col, v1);
+            const int64_t NU = a.M * (a.K / 8);
+            const int64_t u0 = NU * pw / kProd, u1 = NU * (pw + 1) / kProd;
+            uint4 av[kLocalLoads];
+            if (!a.static_S) {
+                const uint32_t KU = (uint32_t)(a.K / 8);
+                const uint16_t *x = static_cast<const uint16_t *>(a.x);
+#pragma unroll
+                for (int t = 0; t < kLocalLoads; ++t) {
+                    const int64_t idx = u0 + lane + 64 * t < u1 ? u0 + lane + 64 * t : u0;
+                    const uint32_t row = (uint32_t)idx / KU, cu = (uint32_t)idx - row * KU;
+                    av[t] = *reinterpret_cast<const uint4 *>(x + (int64_t)row * a.ldx + 8 * (int64_t)cu);
+                }
+            }
+            __syncthreads();                   // loads out: consumers may issue theirs
+            zero_unwritten<MT>(lds_a, rg, slots, a.M);
+            if (!a.static_S) {
+                // for finite values the order of |bf16| bit patterns is that of the magnitudes
+                unsigned mx = 0;
+#pragma unroll
+                for (int t = 0; t < kLocalLoads; ++t) {
+                    const uint32_t w[4] = {av[t].x, av[t].y, av[t].z, av[t].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mx = max(mx, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+                }
+                mx = wave_max_u(mx);
+                if (lane == 0) {
+                    sh_part[pw] = u2f(mx << 16);
+                    __hip_atomic_fetch_add(&sh_cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                }
+                // the producers alone meet here: the consumers may still be issuing loads
+                while (__hip_atomic_load(&sh_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < (unsigned)kProd)
+                    __builtin_amdgcn_s_sleep(1);
+            }
+            float S;
             if (a.static_S) {
                 S = *a.static_S;
-            } else if (a.mode == MODE_LOCAL) {
-                S = scale_of(wave_amax_x(a));
             } else {
-                // publish the maximum of this workgroup's 1/G of X's blocks
-                const int64_t KB = a.K / 16, NB = a.M * KB;
-                const int64_t b0 = (int64_t)blockIdx.x * NB / a.G, b1 = ((int64_t)blockIdx.x + 1) * NB / a.G;
-                float lmax = 0.0f;
-                for (int64_t b = b0 + lane; b < b1; b += 64) {
-                    const int64_t row = b / KB, blk = b - row * KB;
-                    float v[16];
-                    load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
+                float m = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, fabsf(v[i]));
-                }
-                lmax = wave_max(lmax);
-                const Sync y0 = sync_at(a.header, 0);
-                int ok = 1;
-                if (lane == 0) {
-                    st_dev(&a.amax_slots[blockIdx.x], lmax);
-                    wait_own_stores();
-                    ok = sync_wait(y0, sync_arrive(y0, a.G), a.spin_limit, a.header) ? 1 : 0;
-                }
-                ok = __shfl(ok, 0);
-                if (ok) {
-                    float m = 0.0f;
-                    for (int i = lane; i < a.G; i += 64) m = fmaxf(m, ld_dev(&a.amax_slots[i]));
-                    S = scale_of(wave_max(m));
-                } else {
-                    S = scale_of(wave_amax_x(a));
-                }
+                for (int w = 0; w < kProd; ++w) m = fmaxf(m, sh_part[w]);
+                S = scale_of(m);
             }
-            if (blockIdx.x == 0 && lane == 0) *a.q_S = S;
-            if (a.mode == MODE_SYNC2) {
-                // quantize this workgroup's 1/G of X's blocks into the shared buffer
-                const int64_t KB = a.K / 16, NB = a.M * KB;
-                const int64_t b0 = (int64_t)blockIdx.x * NB / a.G, b1 = ((int64_t)blockIdx.x + 1) * NB / a.G;
-                const float t = 6.0f * S;
-                for (int64_t b = b0 + lane; b < b1; b += 64) {
-                    const int64_t row = b / KB, blk = b - row * KB;
-                    float v[16];
-                    load16_any(a.x, a.x_bf16, row * a.ldx + 16 * blk, v);
-                    uint32_t cw[2];
-                    float d;
-                    const uint32_t db = encode_block(v, S, t, cw, d);
-                    unsigned long long *cp = reinterpret_cast<unsigned long long *>(a.q_codes + row * a.q_ldc + 8 * blk);
-                    st_dev(cp, (unsigned long long)cw[0] | ((unsigned long long)cw[1] << 32));
-                    st_dev(a.q_scales + row * a.q_lds + blk, (uint8_t)db);
-                    if (RES && 16 * blk < a.res_cols) {
-                        float r[16];
-                        block_residue(v, cw, d, S, r);
-                        uint32_t rc[2];
-                        float dr;
-                        const uint32_t rdb = encode_block(r, S, t, rc, dr);
-                        unsigned long long *rp =
-                            reinterpret_cast<unsigned long long *>(a.q_codes + row * a.q_ldc + 8 * (KB + blk));
-                        st_dev(rp, (unsigned long long)rc[0] | ((unsigned long long)rc[1] << 32));
-                        st_dev(a.q_scales + row * a.q_lds + KB + blk, (uint8_t)rdb);
-                    }
-                }
-                wait_own_stores();
-                const Sync y1 = sync_at(a.header, 1);
-                int ok = 1;
-                if (lane == 0) ok = sync_wait(y1, sync_arrive(y1, a.G), a.spin_limit, a.header) ? 1 : 0;
-                from_x = __shfl(ok, 0) == 0;
-            }
+            if (blockIdx.x == 0 && ptid == 0) *a.q_S = S;
+            if (ptid == 0) sh_S = S;
+            if (ptid < nraw)
+                xchunk_quantize<MT, RES>(a, lds_a, slots, kbeg, rg.rend, f.m, f.col, v1, xc, S, q == 0);
+            TL(1);
+            __syncthreads();                   // operand complete
         }
-        // The K range's operand: for each (unit u, sub-block i, m-tile mt) the 64
-        // lanes take row 16 mt + (lane & 15) and quarter g = lane >> 4, i.e. the
-        // 32 columns kbeg + 512 u + 128 g + 32 i, and write slots
-        // ((u * 16 + 4 i + j) * MT + mt) * 64 + lane: consecutive lanes, consecutive
-        // slots. Every slot of the range is written once (zero outside the data).
-        const bool writer = from_x && q == 0 && a.mode != MODE_PRE;   // keeps the quantized buffer complete
-        const int passes = (units + res_units) * 4 * MT;
-        for (int w = 0; w < passes; ++w) {
-            const bool is_res = w >= units * 4 * MT;
-            const int w2 = is_res ? w - units * 4 * MT : w;
-            const int mt = w2 % MT, i = (w2 / MT) & 3, u = (w2 / MT) >> 2;
-            const int64_t row = r16 + 16 * mt;
-            const int64_t kc = kbeg + 512 * u + 128 * g + 32 * i;
-            Chunk ch = {{0, 0, 0, 0}, 0, 0};
-            if (row < a.M && kc < (is_res ? rend : kend)) {
-                if (from_x) {
-                    ch = chunk_from_x(a, row, kc, is_res, S);
-                    if (writer) {
-                        const int64_t col = is_res ? a.K + kc : kc;
-                        uint32_t *cp = reinterpret_cast<uint32_t *>(a.q_codes + row * a.q_ldc + col / 2);
-                        if (kc + 32 <= a.K) {
-                            cp[0] = ch.c[0]; cp[1] = ch.c[1]; cp[2] = ch.c[2]; cp[3] = ch.c[3];
-                            a.q_scales[row * a.q_lds + col / 16] = (uint8_t)ch.s0;
-                            a.q_scales[row * a.q_lds + col / 16 + 1] = (uint8_t)ch.s1;
-                        } else {
-                            cp[0] = ch.c[0]; cp[1] = ch.c[1];
-                            a.q_scales[row * a.q_lds + col / 16] = (uint8_t)ch.s0;
-                        }
-                    }
-                } else {
-                    const int64_t col = is_res ? a.K + kc : kc;
-                    const int64_t lim = is_res ? a.K + rend : kend;
-                    ch = a.mode == MODE_PRE ? chunk_from_q<false>(a, row, col, lim)
-                                            : chunk_from_q<true>(a, row, col, lim);
-                }
-            }
-            chunk_to_slots(lds_a + (is_res ? slots : 0), ((u * 16 + 4 * i) * MT + mt) * 64 + lane, MT * 64, ch);
-        }
-        if (lane == 0) sh_S = a.mode == MODE_PRE ? a.q_S[0] : S;
     }
-    __syncthreads();                           // activation operand ready
+    TL(2);
 
     // ---- consumers: decode weights, MFMA
     const float scale = sh_S * w_scale;
@@ -401,6 +461,8 @@ void decode_kernel(DArgs a) {
         float4v acc[MT], acc2[MT];                 // two MFMA chains: even / odd fragments
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+#pragma unroll
+        for (int s = kPre; s < kRing; ++s) load_item(s < nitems ? s : nitems - 1, ring[s]);
         // Fully unrolled over at most kMaxItems items (no loop back-edge): each slot
         // is consumed in place and refilled right after, always with the same five
         // loads (past the last item it re-reads the current one, a cache hit), so
@@ -461,13 +523,14 @@ void decode_kernel(DArgs a) {
                 if (it + kRing < kMaxItems) {
                     const int nx = it + kRing < nitems ? it + kRing : (it < nitems ? it : nitems - 1);
                     __builtin_amdgcn_sched_barrier(0);   // keep: consume slot s, then refill it
-                    load_w(a, item_row(nx), kbeg + 512 * (nx % units), g, ring[s]);
+                    load_item(nx, ring[s]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
     }
 
+    TL(3);
     // ---- split-K combine by the last workgroup of the tile group
     if (a.P > 1) {
         wait_own_stores();                     // this wave's partial tiles are visible
@@ -501,6 +564,7 @@ void decode_kernel(DArgs a) {
             if (threadIdx.x == 0) st_dev(&tile_cnt[q], 0u);
         }
     }
+    TL(4);
 }
 
 // ---------------------------------------------------------------- planning
@@ -516,11 +580,16 @@ int resident_capacity(const void *fn, size_t lds) {
     return per * cus;
 }
 
-const void *kernel_ptr(int MT, bool res) {
-    if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true>)
-                            : reinterpret_cast<const void *>(&decode_kernel<1, false>);
-    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true>)
-               : reinterpret_cast<const void *>(&decode_kernel<2, false>);
+template <bool TILED>
+const void *kernel_ptr_t(int MT, bool res) {
+    if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED>)
+                            : reinterpret_cast<const void *>(&decode_kernel<1, false, TILED>);
+    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED>);
+}
+
+const void *kernel_ptr(int MT, bool res, bool tiled = false) {
+    return tiled ? kernel_ptr_t<true>(MT, res) : kernel_ptr_t<false>(MT, res);
 }
 
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
@@ -533,10 +602,10 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     static int cap_cache[2][2] = {{0, 0}, {0, 0}};
     int &capc = cap_cache[pl.MT - 1][res ? 1 : 0];
     if (capc <= 1) capc = resident_capacity(kernel_ptr(pl.MT, res), lds_max);
-    int cap = capc - capc / 8;
+    int cap = capc;                  // one round of resident workgroups
     if (const char *e = std::getenv("NVFP4_DECODE_MAX_GRID")) {      // tuning override
         const int v = std::atoi(e);
-        if (v > 0 && v < cap) cap = v;
+        if (v > 0) cap = v;
     }
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
@@ -553,6 +622,14 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
             if (cost < best) { best = cost; bestU = U; besttw = tw; }
         }
     }
+    if (const char *e = std::getenv("NVFP4_DECODE_FORCE")) {         // tuning override "U,tw"
+        int fu = 0, ft = 0;
+        if (std::sscanf(e, "%d,%d", &fu, &ft) == 2 && fu >= 1 && fu <= umax && ft >= 1 &&
+            ft * (fu < ku ? fu : (int)ku) <= kMaxItems && (pl.NT + kCons * ft - 1) / (kCons * ft) <= kMaxTileCounters) {
+            bestU = fu;
+            besttw = ft;
+        }
+    }
     pl.U = bestU > ku ? (int)ku : bestU;
     pl.tw = besttw;
     pl.T = kCons * pl.tw;
@@ -561,11 +638,12 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     pl.G = (int)(pl.P * pl.Q);
     pl.lds = (size_t)pl.U * 16 * pl.MT * 64 * sizeof(half8) * (res ? 2 : 1);
     // activation handling
+    // Raw activations are quantized in the kernel only when every workgroup can
+    // read all of X and each producer thread holds at most one 32-column chunk.
     const int64_t kc = (int64_t)pl.U * 512 < K ? (int64_t)pl.U * 512 : K;
-    if (!raw_x || norm_or_perm) pl.mode = MODE_PRE;
-    else if (M * kc <= 8192 && M * K <= 16384) pl.mode = MODE_LOCAL;
-    else if (M * kc <= 8192) pl.mode = MODE_SYNC1;
-    else pl.mode = MODE_SYNC2;
+    const int64_t raw_chunks = M * ((kc + 31) / 32);
+    pl.mode = (raw_x && !norm_or_perm && raw_chunks <= kPThreads && M * K <= kLocalMaxElems) ? MODE_LOCAL
+                                                                                            : MODE_PRE;
     if (std::getenv("NVFP4_DEBUG_PLAN"))
         std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d T=%d G=%d mode=%d "
                      "(resident capacity %d)\n", (long long)M, (long long)N, (long long)K, (long long)res_cols,
@@ -578,35 +656,40 @@ bool plan_ok(const Plan &pl) { return pl.Q <= kMaxTileCounters && pl.G >= 1; }
 }  // namespace
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
-    const Plan pl = plan_for(M, N, K, res_cols, true, false);
-    const size_t part = pl.P > 1 ? (size_t)pl.P * M * N * sizeof(float) : 0;
-    return part + ((size_t)pl.G * sizeof(float) + 255) / 256 * 256;
+    const Plan pl = plan_for(M, N, K, res_cols, false, false);
+    return pl.P > 1 ? (size_t)pl.P * M * N * sizeof(float) : 0;
 }
 
-bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
-    return plan_ok(plan_for(M, N, K, res_cols, true, false));
+bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool x_bf16) {
+    const Plan pl = plan_for(M, N, K, res_cols, true, false);
+    return x_bf16 && plan_ok(pl) && pl.mode == MODE_LOCAL;
 }
+
+#ifdef NVFP4_TIMELINE
+extern "C" int nvfp4_debug_timeline(void *host, size_t bytes) {
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), bytes < sizeof(g_timeline) ? bytes : sizeof(g_timeline));
+}
+#endif
 
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     const bool raw = g.x != nullptr;
     const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols, raw, false);
-    if (!plan_ok(pl)) return hipErrorInvalidValue;
-    if (!g.header || !g.scratch || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols))
+    if (!plan_ok(pl) || (raw && pl.mode != MODE_LOCAL)) return hipErrorInvalidValue;
+    if (!g.header || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols) ||
+        (pl.P > 1 && !g.scratch))
         return hipErrorInvalidValue;
     DArgs a;
-    a.x = g.x; a.x_bf16 = g.x_bf16; a.ldx = g.ldx; a.static_S = g.static_S;
+    a.x = g.x; a.ldx = g.ldx; a.static_S = g.static_S;
     a.q_codes = g.q_codes; a.q_ldc = g.q_ldc; a.q_scales = g.q_scales; a.q_lds = g.q_lds; a.q_S = g.q_S;
     a.w_codes = g.w_codes; a.w_ldc = g.w_ldc; a.w_scales = g.w_scales; a.w_lds = g.w_lds; a.w_S = g.w_S;
     a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
     a.header = reinterpret_cast<uint8_t *>(g.header);
-    a.amax_slots = static_cast<float *>(g.scratch);
-    a.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(g.scratch) +
-                                           ((size_t)pl.G * sizeof(float) + 255) / 256 * 256);
+    a.partials = static_cast<float *>(g.scratch);
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
-    a.spin_limit = g.spin_limit;
     void *args[] = {&a};
-    return hipLaunchKernel(kernel_ptr(pl.MT, g.res_cols > 0), dim3(pl.G), dim3(kThreads), args, pl.lds, st);
+    return hipLaunchKernel(kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0), dim3(pl.G), dim3(kThreads), args,
+                           pl.lds, st);
 }
 
 }  // namespace nvfp4

@@ -30,6 +30,7 @@ struct TArgs {
     const uint8_t *w_codes; int64_t w_ldc;
     const uint8_t *w_scales; int64_t w_lds;
     const float *w_S;
+    int w_tiled;
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
     int tiles_m, tiles_n;
@@ -60,6 +61,23 @@ __device__ inline RowChunk load_chunk(const uint8_t *codes, int64_t ldc, const u
             rc.c.x = h.x; rc.c.y = h.y;
             rc.s = sp[0];
         }
+    }
+    return rc;
+}
+
+// The same chunk of a tiled weight (16 x 512 items in decode lane order: the
+// 32 columns at k of row n are lane 16 g + r, step i of item (n / 16, k / 512)).
+__device__ inline RowChunk load_chunk_tiled(const uint8_t *codes, int64_t ldc, const uint8_t *scales, int64_t lds,
+                                            int64_t row, int64_t nrows, int64_t k, int64_t kend) {
+    RowChunk rc;
+    rc.c = make_uint4(0, 0, 0, 0);
+    rc.s = 0;
+    if (row < nrows && k < kend) {                // tiled padding is zero: no half-chunk case
+        const int64_t t = row >> 4, u = k >> 9;
+        const int lane = (int)(16 * ((k >> 7) & 3) + (row & 15)), i = (int)((k >> 5) & 3);
+        rc.c = *reinterpret_cast<const uint4 *>(codes + t * ldc + u * 4096 + 1024 * i + 16 * lane);
+        const uint8_t *sp = scales + t * lds + u * 512 + 8 * lane + 2 * i;
+        rc.s = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
     }
     return rc;
 }
@@ -122,7 +140,9 @@ __global__ __launch_bounds__(256) void tiled_kernel(TArgs a) {
         for (int it = 0; it < B_ITERS; ++it) {
             const int idx = tid + 256 * it;
             const int r = idx >> 1, h = idx & 1;
-            if (r < BN) rb[it] = load_chunk(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K);
+            if (r < BN)
+                rb[it] = a.w_tiled ? load_chunk_tiled(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K)
+                                   : load_chunk(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K);
         }
     };
     auto lstore = [&](half8 *st) {
@@ -230,6 +250,7 @@ hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st) {
     TArgs a;
     a.a_codes = g.a_codes; a.a_ldc = g.a_ldc; a.a_scales = g.a_scales; a.a_lds = g.a_lds; a.a_S = g.a_S;
     a.w_codes = g.w_codes; a.w_ldc = g.w_ldc; a.w_scales = g.w_scales; a.w_lds = g.w_lds; a.w_S = g.w_S;
+    a.w_tiled = g.w_tiled;
     a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
     a.tiles_m = a.tiles_n = 0;

@@ -36,49 +36,60 @@ struct ChannelAbsmaxLaunch {
 };
 hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 
-// Every workspace starts with a header of counters used by the grid-wide
-// waits and the split-K combine. It must be zero before the first call on a
-// workspace; every call leaves it zero.
+// Every workspace starts with a header of counters used by the split-K
+// combine. It must be zero before the first call on a workspace; every call
+// leaves it zero.
 constexpr size_t kHeaderBytes = 8192;
-// Byte offset (in the header) of a u32 counting grid-wide waits that gave up.
-constexpr size_t kHeaderTimeoutCounter = 4096 - 64;
-constexpr int64_t kHeaderCounters = (int64_t)(kHeaderBytes / sizeof(unsigned));
 
-// Decode-shaped (M <= 32) product in one launch. With x != nullptr the raw
-// activations are quantized inside the kernel into q_* (canonical NVFP4 layout,
-// K + res_cols columns: the residue of columns [0, res_cols) after column K);
-// with x == nullptr q_* already hold them.
+// Decode-shaped (M <= 32) product in one launch. With x != nullptr (bf16, and
+// decode_can_fuse true) the raw activations are quantized inside the kernel and
+// also stored into q_* (canonical NVFP4 layout, K + res_cols columns: the
+// residue of columns [0, res_cols) after column K); with x == nullptr q_*
+// already hold them.
 struct DecodeLaunch {
-    const void *x; int x_bf16; int64_t ldx;
+    const void *x; int64_t ldx;
     const float *static_S;
     uint8_t *q_codes; int64_t q_ldc;
     uint8_t *q_scales; int64_t q_lds;
     float *q_S;
-    const uint8_t *w_codes; int64_t w_ldc;
+    const uint8_t *w_codes; int64_t w_ldc;  // row-major, or tiled (w_tiled: strip strides)
     const uint8_t *w_scales; int64_t w_lds;
     const float *w_S;
+    int w_tiled;
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
     unsigned *header;                       // kHeaderBytes, zero-kept
     void *scratch; size_t scratch_bytes;    // decode_workspace_bytes()
-    unsigned spin_limit;                    // bound on each grid-wide wait (polls)
 };
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t res_cols);
-bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols);
+bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool x_bf16);
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st);
 
-// Large-M tiled matrix-core product (no residue columns in this path unless
-// res_cols > 0 is requested through the same tensor layout).
+// Large-M matrix-core product over 128 x 128 (or 64 x 128) output tiles; the
+// residue columns (res_cols > 0) follow column K in the activation tensor.
 struct PrefillLaunch {
     const uint8_t *a_codes; int64_t a_ldc;
     const uint8_t *a_scales; int64_t a_lds;
     const float *a_S;
-    const uint8_t *w_codes; int64_t w_ldc;
+    const uint8_t *w_codes; int64_t w_ldc;  // row-major, or tiled (w_tiled)
     const uint8_t *w_scales; int64_t w_lds;
     const float *w_S;
+    int w_tiled;
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
 };
 hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st);
+
+// Row-major -> tiled weight layout (16 x 512 items in decode lane order).
+struct PackLaunch {
+    const uint8_t *src_codes; int64_t src_ldc;
+    const uint8_t *src_scales; int64_t src_lds;
+    const float *src_S;
+    uint8_t *dst_codes; int64_t dst_ldc;
+    uint8_t *dst_scales; int64_t dst_lds;
+    float *dst_S;
+    int64_t rows, K;
+};
+hipError_t launch_pack_tiled(const PackLaunch &g, hipStream_t st);
 
 }  // namespace nvfp4

@@ -14,7 +14,7 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+LIB_PATH = os.environ.get("NVFP4_LIB") or os.path.join(_HERE, "libnvfp4.so")  # override: alternative build
 
 BF16, FP32 = 0, 1
 _STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "misaligned", 4: "bad dtype",
@@ -27,10 +27,13 @@ class NVFP4Error(RuntimeError):
         super().__init__(f"{what}: status {status} ({_STATUS.get(status, '?')})")
 
 
+ROWMAJOR, TILED = 0, 1
+
+
 class _CTensor(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("ld_codes", C.c_int64), ("scales", C.c_void_p),
                 ("ld_scales", C.c_int64), ("tensor_scale", C.c_void_p), ("rows", C.c_int64),
-                ("K", C.c_int64)]
+                ("K", C.c_int64), ("layout", C.c_int32)]
 
 
 class _COpts(C.Structure):
@@ -41,7 +44,7 @@ class _COpts(C.Structure):
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_channel_absmax",
+EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
            "nvfp4_perm_from_absmax", "nvfp4_workspace_size", "nvfp4_status_string",
            "nvfp4_last_error", "nvfp4_version", "nvfp4_host_e4m3_encode", "nvfp4_host_e2m1_encode"]
 
@@ -58,6 +61,7 @@ def lib():
             L.nvfp4_gemm.argtypes = [vp, vp, C.c_int, i64, i64, i64, vp, vp, C.c_int, i64, vp, sz, vp]
             L.nvfp4_gemm_residue.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, C.c_int, i64, vp,
                                              vp, sz, vp]
+            L.nvfp4_pack_tiled.argtypes = [vp, vp, vp]
             L.nvfp4_channel_absmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, C.c_float, vp, vp, sz, vp]
             L.nvfp4_perm_from_absmax.argtypes = [vp, i64, vp]
             L.nvfp4_workspace_size.argtypes = [C.c_int, i64, i64, i64, i64]
@@ -67,8 +71,8 @@ def lib():
             L.nvfp4_last_error.restype = C.c_char_p
             L.nvfp4_host_e4m3_encode.argtypes = [C.c_float]
             L.nvfp4_host_e2m1_encode.argtypes = [C.c_float]
-            for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_channel_absmax",
-                         "nvfp4_perm_from_absmax"):
+            for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_pack_tiled",
+                         "nvfp4_channel_absmax", "nvfp4_perm_from_absmax"):
                 getattr(L, name).restype = C.c_int
             _lib = L
     return _lib
@@ -102,10 +106,16 @@ def _round_up(v: int, a: int) -> int:
 
 
 class NVFP4Tensor:
-    """Device NVFP4 tensor: codes [rows, ld_codes] u8, scales [rows, ld_scales] u8, scale [1] f32."""
+    """Device NVFP4 tensor: codes u8, scales u8, scale [1] f32, in one of two layouts.
 
-    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, scale: torch.Tensor, K: int):
-        self.codes, self.scales, self.scale, self.K = codes, scales, scale, K
+    Row-major: codes [rows, ld_codes], scales [rows, ld_scales]. Tiled (weights
+    for the products): codes [ceil(rows/16), KU*4096], scales [ceil(rows/16),
+    KU*512], KU = ceil(K/512), as documented in include/nvfp4.h."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, scale: torch.Tensor, K: int,
+                 layout: int = ROWMAJOR, rows: int | None = None):
+        self.codes, self.scales, self.scale, self.K, self.layout = codes, scales, scale, K, layout
+        self._rows = codes.shape[0] if rows is None else rows
 
     @staticmethod
     def empty(rows: int, K: int, device="cuda") -> "NVFP4Tensor":
@@ -115,18 +125,42 @@ class NVFP4Tensor:
         scale = torch.empty((1,), dtype=torch.float32, device=device)
         return NVFP4Tensor(codes, scales, scale, K)
 
+    @staticmethod
+    def empty_tiled(rows: int, K: int, device="cuda") -> "NVFP4Tensor":
+        nt, ku = (rows + 15) // 16, (K + 511) // 512
+        codes = torch.empty((nt, ku * 4096), dtype=torch.uint8, device=device)
+        scales = torch.empty((nt, ku * 512), dtype=torch.uint8, device=device)
+        scale = torch.empty((1,), dtype=torch.float32, device=device)
+        return NVFP4Tensor(codes, scales, scale, K, TILED, rows)
+
     @property
     def rows(self) -> int:
-        return self.codes.shape[0]
+        return self._rows
+
+    def clone(self) -> "NVFP4Tensor":
+        return NVFP4Tensor(self.codes.clone(), self.scales.clone(), self.scale.clone(), self.K, self.layout,
+                           self._rows)
 
     def c(self) -> _CTensor:
-        return _CTensor(self.codes.data_ptr(), self.codes.stride(0), self.scales.data_ptr(),
-                        self.scales.stride(0), self.scale.data_ptr(), self.rows, self.K)
+        ldc = self.codes.stride(0) if self.codes.dim() == 2 else 0
+        lds = self.scales.stride(0) if self.scales.dim() == 2 else 0
+        return _CTensor(self.codes.data_ptr(), ldc, self.scales.data_ptr(), lds, self.scale.data_ptr(),
+                        self.rows, self.K, self.layout)
 
     def host(self):
-        """(codes [rows, K/2], scales [rows, K/16], S) as numpy arrays on the host."""
+        """(codes [rows, K/2], scales [rows, K/16], S) as numpy arrays on the host (row-major only)."""
+        if self.layout != ROWMAJOR:
+            raise ValueError("host() reads row-major tensors")
         return (self.codes[:, : self.K // 2].cpu().numpy(), self.scales[:, : self.K // 16].cpu().numpy(),
                 self.scale.cpu().numpy()[0])
+
+
+def pack_tiled(w: NVFP4Tensor) -> NVFP4Tensor:
+    """The tiled copy of a row-major weight (nvfp4_pack_tiled), on the current stream."""
+    out = NVFP4Tensor.empty_tiled(w.rows, w.K, device=w.codes.device)
+    src, dst = w.c(), out.c()
+    _check(lib().nvfp4_pack_tiled(C.byref(src), C.byref(dst), _stream()), "nvfp4_pack_tiled")
+    return out
 
 
 _ws = {}
@@ -135,7 +169,7 @@ _ws = {}
 def workspace(nbytes: int, device) -> torch.Tensor:
     """A per-(device, stream) workspace, grown on demand (plumbing, not compute).
 
-    Zero-filled when allocated: its first 8 KiB hold the library's synchronization
+    Zero-filled when allocated: its first 8 KiB hold the library's split-K
     counters, which must start at zero and which every call leaves at zero."""
     key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
     buf = _ws.get(key)
@@ -143,17 +177,6 @@ def workspace(nbytes: int, device) -> torch.Tensor:
         buf = torch.zeros(max(nbytes, 16384), dtype=torch.uint8, device=device)
         _ws[key] = buf
     return buf
-
-
-HEADER_TIMEOUT_OFFSET = 4096 - 64
-
-
-def sync_timeouts() -> int:
-    """Total grid-wide waits that gave up (and recomputed locally) on this process's workspaces."""
-    total = 0
-    for buf in _ws.values():
-        total += int(buf[HEADER_TIMEOUT_OFFSET:HEADER_TIMEOUT_OFFSET + 4].cpu().view(torch.int32)[0])
-    return total
 
 
 def _opts(gamma, eps, perm, residue_cols, static_scale):

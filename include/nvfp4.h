@@ -16,6 +16,19 @@
  *   S      : one float in device memory (so a dynamic scale needs no host sync)
  * The value of an element is e(code) * d(scale) * S.
  *
+ * Tiled storage (weights; layout = NVFP4_LAYOUT_TILED), the order in which the
+ * decode product reads them, so that each of its loads is one contiguous 1 KiB
+ * run. The tensor is cut into items of 16 rows x 512 columns; item (t, u)
+ * (rows [16t, 16t+16), columns [512u, 512u+512)) lives at codes + t*ld_codes +
+ * u*4096 and scales + t*ld_scales + u*512, with ld_codes = KU*4096,
+ * ld_scales = KU*512, KU = ceil(K/512). Inside an item, for p = 0..63 with
+ * r = p % 16, g = p / 16:
+ *   codes  byte 1024*i + 16*p + j  (i, j < 4 / 16) = byte j of the canonical
+ *          codes of row 16t+r starting at column 512u + 128g + 32i;
+ *   scales byte 8*p + b  (b < 8) = the block scale of row 16t+r, columns
+ *          512u + 128g + 16b .. +16.
+ * Rows >= rows and columns >= K are zero codes with zero scales.
+ *
  * Quantization rule (the pages fix the format, not the rounding; this is the
  * reading implemented, and the CPU oracle implements the same rule):
  *   S  = amax(tensor) / 2688 (2688 = 6 * 448), or 1 for an all-zero tensor,
@@ -30,10 +43,10 @@
  *    enqueues work on it and returns without synchronizing.
  *  - The caller owns and allocates every buffer, including the workspace
  *    (size from nvfp4_workspace_size). The library never allocates device
- *    memory. The first 8 KiB of every workspace hold synchronization counters
- *    (grid-wide waits of the one-launch decode product, split-K combine): they
- *    must be zero before the first call on a workspace, and every call leaves
- *    them zero. A workspace must not be used by two calls at the same time.
+ *    memory. The first 8 KiB of every workspace hold the counters of the
+ *    decode product's split-K combine: they must be zero before the first
+ *    call on a workspace, and every call leaves them zero. A workspace must
+ *    not be used by two calls at the same time.
  *  - Argument errors are detected before anything is enqueued; the call then
  *    returns a status != NVFP4_OK and leaves every output untouched. Launch
  *    failures return NVFP4_ERR_HIP; nvfp4_last_error() gives the HIP text.
@@ -69,15 +82,20 @@ typedef enum {
 
 typedef enum { NVFP4_BF16 = 0, NVFP4_FP32 = 1 } nvfp4_dtype;
 
-/* One NVFP4 tensor in the canonical layout above (rows x K, K % 16 == 0). */
+typedef enum { NVFP4_LAYOUT_ROWMAJOR = 0, NVFP4_LAYOUT_TILED = 1 } nvfp4_layout;
+
+/* One NVFP4 tensor (rows x K, K % 16 == 0) in the canonical (row-major)
+ * layout, or -- for the weight operand of the products only -- the tiled one. */
 typedef struct {
-    uint8_t *codes;        /* device, rows x ld_codes bytes                  */
-    int64_t  ld_codes;     /* bytes between rows, >= K/2, multiple of 16     */
-    uint8_t *scales;       /* device, rows x ld_scales bytes                 */
-    int64_t  ld_scales;    /* bytes between rows, >= K/16, multiple of 8     */
+    uint8_t *codes;        /* device; row-major: rows x ld_codes bytes       */
+    int64_t  ld_codes;     /* row-major: bytes between rows, >= K/2, multiple
+                              of 16; tiled: KU*4096 (bytes per 16-row strip) */
+    uint8_t *scales;       /* device; row-major: rows x ld_scales bytes      */
+    int64_t  ld_scales;    /* row-major: >= K/16, multiple of 8; tiled: KU*512 */
     float   *tensor_scale; /* device, 1 float                                */
     int64_t  rows;
     int64_t  K;
+    int32_t  layout;       /* nvfp4_layout                                    */
 } nvfp4_tensor;
 
 /* Options of the fused quantizer (ARCQuant article, section 3.2: channel
@@ -112,9 +130,12 @@ nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, i
  * dtype xt, leading dimension ldx, quantized inside the call with a dynamic
  * tensor scale) is non-NULL. w is N x K. y is M x N with leading dimension ldy,
  * dtype yt (FP32, or BF16 rounded to nearest even).
- * Small M (<= 32) runs as one launch that quantizes x cooperatively across
- * the grid while the packed weights stream in with wide loads; larger M
- * quantizes x first and uses the tiled matrix-core path. K == 0 gives y = 0. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
+ * w may be row-major or tiled; a_q must be row-major.
+ * Small M (<= 32) runs as one decode launch that streams the weights once
+ * (x small enough: quantized inside that launch; else by the quantize kernels
+ * first). Larger M quantizes x first and uses the matrix-core tile path, which
+ * takes row-major weights only (NVFP4_ERR_UNSUPPORTED for tiled ones).
+ * K == 0 gives y = 0. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
                         int64_t M, int64_t K, int64_t ldx,
                         const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
@@ -133,6 +154,12 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
                                 const nvfp4_quant_opts *opts, const nvfp4_tensor *w,
                                 void *y, int yt, int64_t ldy, const nvfp4_tensor *a_aug_out,
                                 void *ws, size_t ws_bytes, void *stream);
+
+/* Rewrite the row-major weight `src` into the tiled layout `dst` (same rows
+ * and K; dst->ld_codes = KU*4096, dst->ld_scales = KU*512; its codes and
+ * scales buffers hold ceil(rows/16) strips). The tensor scale is copied.
+ * A one-time layout change of static weights: values are not touched. */
+nvfp4_status nvfp4_pack_tiled(const nvfp4_tensor *src, const nvfp4_tensor *dst, void *stream);
 
 /* Calibration statistic for the outlier reorder (ARCQuant article, sections 3.1
  * and 6.1): absmax_out[j] = max over rows of |RMSNorm(x)[:, j]| (|x| when

@@ -44,3 +44,19 @@ def bf16_bound_ok(y_bf16, y_ref, tol=2e-3) -> bool:
     floor = 1e-3 * np.max(np.abs(y_ref))
     bound = tol * np.maximum(np.abs(y_ref), floor) + 2.0 ** -8 * np.abs(y_ref)
     return bool(np.all(np.abs(y - y_ref) <= bound))
+
+
+def untile(codes_t, scales_t, rows: int, K: int):
+    """Row-major (codes [rows, K/2], scales [rows, K/16]) of a tiled NVFP4 tensor, and
+    whether its padding is zero, following the layout as documented in include/nvfp4.h
+    (item (t, u) of 16 rows x 512 columns; byte 1024 i + 16 p + j of its codes is byte j
+    of row 16 t + p % 16 from column 512 u + 128 (p // 16) + 32 i; scale byte 8 p + b is
+    the block of columns 512 u + 128 (p // 16) + 16 b)."""
+    nt, ku = (rows + 15) // 16, (K + 511) // 512
+    c = np.asarray(codes_t).reshape(nt, ku, 4, 4, 16, 16)     # t, u, i, g, r, j
+    s = np.asarray(scales_t).reshape(nt, ku, 4, 16, 8)        # t, u, g, r, b
+    codes = c.transpose(0, 4, 1, 3, 2, 5).reshape(nt * 16, ku * 512 // 2)   # rows, (u, g, i, j)
+    scales = s.transpose(0, 3, 1, 2, 4).reshape(nt * 16, ku * 32)          # rows, (u, g, b)
+    pad_zero = (not codes[rows:].any() and not codes[:, K // 2:].any() and not scales[rows:].any()
+                and not scales[:, K // 16:].any())
+    return codes[:rows, :K // 2], scales[:rows, :K // 16], pad_zero

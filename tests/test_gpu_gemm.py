@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from block_scaled_fp4_02_amd import inputs
-from helpers import assert_qtensor_equal, bf16_bound_ok, gemm_error, note
+from helpers import assert_qtensor_equal, bf16_bound_ok, gemm_error, note, untile
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -219,23 +219,38 @@ def test_graph_replay_matches_eager(nv):
         assert other.shape == (2, 14336)
 
 
-@pytest.mark.parametrize("shape_idx", [0, 1])
-def test_wait_fallback_identical(nv, orc, shape_idx, monkeypatch):
-    """Force every grid-wide wait of the one-launch decode product to give up at once
-    (spin limit 0, set from the host): workgroups then recompute the tensor scale and
-    their activation operand from X themselves. Results must equal the normal path's."""
-    x, w = inputs.decode_sweep(shape_idx)
+@pytest.mark.parametrize("N,K", [(47, 528), (300, 1040), (4096, 4096), (33, 16)])
+def test_pack_tiled_layout(nv, N, K):
+    """nvfp4_pack_tiled is the documented byte permutation (checked on the host)."""
+    w = inputs.small_random(70 + N, N, K)
+    note(f"pack tiled N={N} K={K}")
+    wq = nv.quantize(w.to(DEV))
+    wt = nv.pack_tiled(wq)
+    torch.cuda.synchronize()
+    codes, scales, S = wq.host()
+    tc, ts, pad_zero = untile(wt.codes.cpu().numpy(), wt.scales.cpu().numpy(), N, K)
+    assert np.array_equal(tc, codes) and np.array_equal(ts, scales) and pad_zero
+    assert wt.scale.cpu().numpy()[0] == S
+
+
+@pytest.mark.parametrize("M,N,K,S", [(1, 14336, 4096, 0), (16, 4096, 14336, 0), (5, 6144, 4096, 0),
+                                     (32, 300, 1040, 0), (16, 8192, 8192, 8192), (8, 1000, 4112, 2048),
+                                     (64, 300, 1040, 0), (130, 47, 528, 528), (3, 15, 48, 48)])
+def test_tiled_weights_same_result(nv, M, N, K, S):
+    """Products with tiled weights equal those with row-major weights bit for bit
+    (same arithmetic, only the load order of the weight bytes changes)."""
+    x = inputs.small_random(90 + M, M, K)
+    w = inputs.small_random(91 + N, N, K)
     xd = x.to(DEV)
     wq = nv.quantize(w.to(DEV))
-    y0 = nv.gemm(xd, wq).clone()
-    r0 = nv.gemm_residue(xd[:5], wq, 2048).clone()
+    wt = nv.pack_tiled(wq)
+    note(f"tiled weights M={M} N={N} K={K} S={S}")
+    if S == 0:
+        y0, y1 = nv.gemm(xd, wq), nv.gemm(xd, wt)
+        aq = nv.quantize(xd)
+        z0, z1 = nv.gemm(aq, wq, out_dtype=torch.bfloat16), nv.gemm(aq, wt, out_dtype=torch.bfloat16)
+    else:
+        y0, y1 = nv.gemm_residue(xd, wq, S), nv.gemm_residue(xd, wt, S)
+        z0, z1 = y0, y1
     torch.cuda.synchronize()
-    monkeypatch.setenv("NVFP4_SPIN_LIMIT", "0")
-    note(f"fallback path shape {shape_idx}")
-    y1 = nv.gemm(xd, wq)
-    r1 = nv.gemm_residue(xd[:5], wq, 2048)
-    torch.cuda.synchronize()
-    monkeypatch.delenv("NVFP4_SPIN_LIMIT")
-    assert torch.equal(y0, y1) and torch.equal(r0, r1)
-    ref = orc.gemm(orc.quantize(x), orc.quantize(w))
-    assert gemm_error(y1.cpu().numpy(), ref) <= TOL
+    assert torch.equal(y0, y1) and torch.equal(z0, z1)

@@ -68,10 +68,15 @@ def test_workspace_sizes(L):
     assert L.nvfp4_workspace_size(9, 1, 1, 16, 0) == 0
 
 
-def _tensor(rows, K, codes=16, scales=16, scale=16, ldc=None, lds=None):
+def _tensor(rows, K, codes=16, scales=16, scale=16, ldc=None, lds=None, layout=0):
     from block_scaled_fp4_02_amd.nvfp4 import _CTensor
-    return _CTensor(codes, ldc if ldc is not None else max(16, (K // 2 + 15) // 16 * 16), scales,
-                    lds if lds is not None else max(8, (K // 16 + 7) // 8 * 8), scale, rows, K)
+    if layout == 1:
+        ku = (K + 511) // 512
+        dl, ds = ku * 4096, ku * 512
+    else:
+        dl, ds = max(16, (K // 2 + 15) // 16 * 16), max(8, (K // 16 + 7) // 8 * 8)
+    return _CTensor(codes, ldc if ldc is not None else dl, scales, lds if lds is not None else ds, scale, rows, K,
+                    layout)
 
 
 def test_argument_errors_before_launch(L):
@@ -117,6 +122,35 @@ def test_argument_errors_before_launch(L):
     assert L.nvfp4_quantize(fake, 0, 4, 32768, 32768, C.byref(o),
                             C.byref(_tensor(4, 32768, codes=1 << 20, scales=1 << 21, scale=1 << 22)),
                             ws, 1 << 30, None) == 6
+
+
+def test_tiled_layout_argument_errors(L):
+    """The tiled layout is accepted for weights only, with its fixed strides."""
+    vp = C.c_void_p
+    fake = vp(1 << 20)
+    ws, wsn = fake, 1 << 20
+    a = _tensor(4, 1024, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    wt = _tensor(32, 1024, codes=1 << 23, scales=1 << 24, scale=1 << 25, layout=1)
+    # tiled activations are not supported
+    at = _tensor(4, 1024, codes=1 << 20, scales=1 << 21, scale=1 << 22, layout=1)
+    assert L.nvfp4_gemm(C.byref(at), None, 0, 4, 1024, 0, C.byref(wt), fake, 1, 32, ws, wsn, None) == 6
+    # wrong strip strides / unknown layout code
+    bad = _tensor(32, 1024, codes=1 << 23, scales=1 << 24, scale=1 << 25, layout=1, ldc=4096)
+    assert L.nvfp4_gemm(C.byref(a), None, 0, 4, 1024, 0, C.byref(bad), fake, 1, 32, ws, wsn, None) == 2
+    bad = _tensor(32, 1024, codes=1 << 23, scales=1 << 24, scale=1 << 25, layout=1, lds=8192)
+    assert L.nvfp4_gemm(C.byref(a), None, 0, 4, 1024, 0, C.byref(bad), fake, 1, 32, ws, wsn, None) == 2
+    bad = _tensor(32, 1024, codes=1 << 23, scales=1 << 24, scale=1 << 25, layout=5)
+    assert L.nvfp4_gemm(C.byref(a), None, 0, 4, 1024, 0, C.byref(bad), fake, 1, 32, ws, wsn, None) == 2
+    # misaligned tiled codes
+    bad = _tensor(32, 1024, codes=(1 << 23) + 8, scales=1 << 24, scale=1 << 25, layout=1)
+    assert L.nvfp4_gemm(C.byref(a), None, 0, 4, 1024, 0, C.byref(bad), fake, 1, 32, ws, wsn, None) == 3
+    # pack: source must be row-major, destination tiled with the same shape
+    w = _tensor(32, 1024, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    assert L.nvfp4_pack_tiled(C.byref(wt), C.byref(wt), None) == 6
+    assert L.nvfp4_pack_tiled(C.byref(w), C.byref(a), None) == 2
+    assert L.nvfp4_pack_tiled(C.byref(w), C.byref(_tensor(48, 1024, codes=1 << 23, scales=1 << 24,
+                                                           scale=1 << 25, layout=1)), None) == 2
+    assert L.nvfp4_pack_tiled(None, C.byref(wt), None) == 1
 
 
 def test_perm_from_absmax_host(L, orc):
