@@ -45,6 +45,23 @@ F16_MFMA_PEAK_TFLOPS = 2500.0
 RING_BYTES = 640 << 20
 
 
+def profiled_traffic():
+    """HBM bytes per decode-kernel launch from the committed pmc summary, or None once the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        md = open(os.path.join(ROOT, "profiles", "decode_kernel_decode_sweep.md")).read()
+        src = open(os.path.join(ROOT, "block_scaled_fp4_02_amd", "csrc", "gemm_decode.hip"), "rb").read()
+    except OSError:
+        return None
+    t = re.search(r"^traffic_bytes_per_launch: (\d+)$", md, re.M)
+    h = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", md, re.M)
+    if not t or not h or h.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(t.group(1))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -111,6 +128,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--layout", choices=["tiled", "rowmajor"], default="tiled",
                     help="weight storage: tiled (packed once, before timing) or canonical row-major")
+    ap.add_argument("--reps", type=int, default=20, help="graph replays per case in the per-case legs")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first copy this many MiB device-to-device (a plain copy of known size, for "
+                         "scaling hardware byte counters)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="run only the kernel-alone leg behind the roofline figure (for profiling: then every "
+                         "decode-kernel launch of the process belongs to that figure, equally per case)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -122,16 +146,27 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.copy_calibration_mib > 0:
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
+
     # ---------------- inputs, resident in HBM
     shapes = inputs.DECODE_SHAPES
     xs, rings, ys = {}, {}, {}
+    # the same ring length for every shape (the smallest weight's count), so every case
+    # launches the same number of kernels
+    copies = max(max(2, -(-RING_BYTES // wbytes(N, K))) for (K, N) in shapes)
     for si, (K, N) in enumerate(shapes):
         x, w = inputs.decode_sweep(si)
         xs[si] = x.to(dev)
         wq = nvfp4.quantize(w.to(dev))
         if args.layout == "tiled":
             wq = nvfp4.pack_tiled(wq)       # one-time layout change of the static weight
-        copies = max(2, -(-RING_BYTES // wbytes(N, K)))
         rings[si] = Ring(wq, copies)
         for M in inputs.DECODE_MS:
             ys[(si, M)] = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -144,40 +179,43 @@ def main():
 
     step_bytes = sum(call_bytes(M, N, K) for M in inputs.DECODE_MS for (K, N) in shapes)
 
-    log(f"inputs ready; capturing step graphs")
-    # One graph per ring phase, each holding exactly one step; step t replays graph t % phases,
-    # so every call of consecutive steps reads a different weight copy.
-    phases = max(len(r.items) for r in rings.values())
-    graphs = []
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()
+    value = sec_per_step = wall = None
+    if not args.roofline_only:
+        log("inputs ready; capturing step graphs")
+        # One graph per ring phase, each holding exactly one step; step t replays graph t % phases,
+        # so every call of consecutive steps reads a different weight copy.
+        phases = copies
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+            torch.cuda.synchronize()
+            for _ in range(phases):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    step()
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(s)
+        for t in range(args.warmup):
+            graphs[t % phases].replay()
         torch.cuda.synchronize()
-        for _ in range(phases):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                step()
-            graphs.append(g)
-    torch.cuda.current_stream().wait_stream(s)
-    for t in range(args.warmup):
-        graphs[t % phases].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    st.record()
-    for t in range(args.steps):
-        graphs[(args.warmup + t) % phases].replay()
-    en.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    timed_steps = args.steps
-    sec_per_step = st.elapsed_time(en) / 1e3 / timed_steps
-    value = step_bytes / sec_per_step / 1e9
-    del graphs
-    log(f"timed {timed_steps} steps: {sec_per_step * 1e6:.1f} us/step, {value:.1f} GB/s")
+        t0 = time.perf_counter()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for t in range(args.steps):
+            graphs[(args.warmup + t) % phases].replay()
+        en.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        sec_per_step = st.elapsed_time(en) / 1e3 / args.steps
+        value = step_bytes / sec_per_step / 1e9
+        del graphs
+        log(f"timed {args.steps} steps: {sec_per_step * 1e6:.1f} us/step, {value:.1f} GB/s")
 
-    # ---------------- per-case detail: whole call and kernel alone
+    # ---------------- per-case detail: whole call and kernel alone. The kernel-alone leg
+    # (pre-quantized activations) launches only the decode kernel, the same number of times
+    # for every case, so a profiler's average over that kernel equals per_launch_us.
     detail = {"decode": []}
     kern_bytes_total, kern_time_total = 0.0, 0.0
     for si, (K, N) in enumerate(shapes):
@@ -196,40 +234,47 @@ def main():
                 for _ in range(n):
                     nvfp4.gemm(aq, ring.next(), out=y)
 
-            tf, _ = graph_time(fused, reps=20, inner=n)
-            tk, _ = graph_time(kern, reps=20, inner=n)
-            log(f"case M={M} K={K} N={N}: call {tf * 1e6:.2f} us, kernel {tk * 1e6:.2f} us")
+            tf = None if args.roofline_only else graph_time(fused, reps=args.reps, inner=n)[0]
+            tk, _ = graph_time(kern, reps=args.reps, inner=n)
+            log(f"case M={M} K={K} N={N}: call " + ("-" if tf is None else f"{tf * 1e6:.2f} us") +
+                f", kernel {tk * 1e6:.2f} us")
             kern_bytes_total += kernel_bytes(M, N, K)
             kern_time_total += tk
-            detail["decode"].append({
-                "M": M, "K": K, "N": N,
-                "us_call": round(tf * 1e6, 3), "GBs_call": round(call_bytes(M, N, K) / tf / 1e9, 1),
-                "us_kernel": round(tk * 1e6, 3), "GBs_kernel": round(kernel_bytes(M, N, K) / tk / 1e9, 1),
-                "frac_hbm_kernel": round(kernel_bytes(M, N, K) / tk / 1e9 / HBM_PEAK_GBS, 4),
-            })
+            row = {"M": M, "K": K, "N": N,
+                   "us_kernel": round(tk * 1e6, 3), "GBs_kernel": round(kernel_bytes(M, N, K) / tk / 1e9, 1),
+                   "frac_hbm_kernel": round(kernel_bytes(M, N, K) / tk / 1e9 / HBM_PEAK_GBS, 4)}
+            if tf is not None:
+                row.update({"us_call": round(tf * 1e6, 3), "GBs_call": round(call_bytes(M, N, K) / tf / 1e9, 1)})
+            detail["decode"].append(row)
     achieved = kern_bytes_total / kern_time_total / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "skinny_kernel (decode W4A4 GEMM, pre-quantized activations)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
+                "kernel": "decode_kernel<1,false,true> (M<=16 W4A4 decode product, pre-quantized "
+                          "activations, tiled weights)" if args.layout == "tiled" else
+                          "decode_kernel<1,false,false> (row-major weights)",
                 "per_launch_bytes": round(kern_bytes_total / len(detail["decode"])),
                 "per_launch_us": round(kern_time_total / len(detail["decode"]) * 1e6, 3)}
 
-    if not args.no_extra:
+    if not args.no_extra and not args.roofline_only:
         detail.update(extra_detail(nvfp4, dev, args.layout == "tiled"))
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    cpu = None if (args.no_cpu_baseline or args.roofline_only) else cpu_baseline(args.cpu_seconds)
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": timed_steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp4-e2m1/e4m3 (f16 MFMA, f32 acc)",
-        "data": "synthetic (seeded; Llama-3.1-8B linear-layer shapes)",
+        "metric": METRIC, "value": None if value is None else round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None if sec_per_step is None else round(sec_per_step * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded; Llama-like linear-layer shapes)",
         "config": {"workload": "small-M decode GEMM sweep M in {1,2,4,8,16} x (K,N) in "
-                               "{(4096,14336),(14336,4096),(4096,6144)}, bf16 activations quantized in the call",
+                               "{(4096,14336),(14336,4096),(4096,6144)}, bf16 activations quantized in the call, "
+                               f"{args.layout} NVFP4 weights",
                    "calls_per_step": 15, "bytes_per_step": step_bytes, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": None if wall is None else round(wall, 3),
     }
+    if args.roofline_only:
+        out["mode"] = "roofline-only (kernel-alone leg; value is reported by the default run)"
     print(json.dumps(out))
 
 

@@ -35,6 +35,7 @@
 // round trip queues behind the weight stream.
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 #include "internal.h"
 #include "nvfp4_device.h"
@@ -317,7 +318,7 @@ __device__ inline void zero_unwritten(half8 *lds, const Range &r, int slots, int
 }
 
 // ---------------------------------------------------------------- kernel
-template <int MT, bool RES, bool TILED>
+template <int MT, bool RES, bool TILED, bool REFILL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
     constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
@@ -463,71 +464,79 @@ void decode_kernel(DArgs a) {
         for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
 #pragma unroll
         for (int s = kPre; s < kRing; ++s) load_item(s < nitems ? s : nitems - 1, ring[s]);
-        // Fully unrolled over at most kMaxItems items (no loop back-edge): each slot
-        // is consumed in place and refilled right after, always with the same five
-        // loads (past the last item it re-reads the current one, a cache hit), so
-        // the load stream is uniform and vmcnt is tracked exactly.
+        // Fully unrolled over NI items (no loop back-edge), NI = kRing when the
+        // plan's items per wave fit the ring (no refills at all; a kernel of its
+        // own, so the two loop shapes never share a register allocation) and
+        // kMaxItems otherwise:
+        // each slot is consumed in place and refilled right after, always with the
+        // same five loads (past the last item -- only in ragged waves -- it
+        // re-reads the current one), so vmcnt is tracked exactly and the common
+        // plans (4 or 8 items per wave) issue no redundant loads.
+        auto run = [&](auto ni) {
+            constexpr int NI = decltype(ni)::value;
 #pragma unroll
-        for (int it = 0; it < kMaxItems; ++it) {
-            const int s = it % kRing;
-            {
-                if (it < nitems) {
-                    const int u = it % units;
-                    const half8 *abase = lds_a + (size_t)u * 16 * MT * 64 + lane;
-                    const bool res_u = RES && u < res_units;
+            for (int it = 0; it < NI; ++it) {
+                const int s = it % kRing;
+                {
+                    if (it < nitems) {
+                        const int u = it % units;
+                        const half8 *abase = lds_a + (size_t)u * 16 * MT * 64 + lane;
+                        const bool res_u = RES && u < res_units;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t sw = (i < 2) ? ring[s].s.x : ring[s].s.y;
-                        const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
-                        const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
-                        const uint32_t cws[4] = {ring[s].c[i].x, ring[s].c[i].y, ring[s].c[i].z, ring[s].c[i].w};
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t sw = (i < 2) ? ring[s].s.x : ring[s].s.y;
+                            const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
+                            const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
+                            const uint32_t cws[4] = {ring[s].c[i].x, ring[s].c[i].y, ring[s].c[i].z, ring[s].c[i].w};
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
+                            for (int j = 0; j < 4; ++j) {
+                                const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
 #pragma unroll
-                            for (int mt = 0; mt < MT; ++mt) {
-                                float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
-                                ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64], b,
-                                                                            ac, 0, 0, 0);
-                                if (res_u)
-                                    ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                        abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, ac, 0, 0, 0);
+                                for (int mt = 0; mt < MT; ++mt) {
+                                    float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
+                                    ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64], b,
+                                                                                ac, 0, 0, 0);
+                                    if (res_u)
+                                        ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                            abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, ac, 0, 0, 0);
+                                }
                             }
                         }
-                    }
-                    if (u == units - 1) {
-                        // tile done: lane holds rows 16 mt + 4 g + e of column n
-                        const int64_t n = 16 * (t_first + (int64_t)(it / units) * kCons) + r16;
-                        if (n < a.N) {
+                        if (u == units - 1) {
+                            // tile done: lane holds rows 16 mt + 4 g + e of column n
+                            const int64_t n = 16 * (t_first + (int64_t)(it / units) * kCons) + r16;
+                            if (n < a.N) {
 #pragma unroll
-                            for (int mt = 0; mt < MT; ++mt)
+                                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const int64_t m = 16 * mt + 4 * g + e;
-                                    const float tot = acc[mt][e] + acc2[mt][e];
-                                    if (m < a.M) {
-                                        if (a.P == 1) {
-                                            const float v = tot * scale;
-                                            if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
-                                            else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
-                                        } else {
-                                            st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], tot);
+                                    for (int e = 0; e < 4; ++e) {
+                                        const int64_t m = 16 * mt + 4 * g + e;
+                                        const float tot = acc[mt][e] + acc2[mt][e];
+                                        if (m < a.M) {
+                                            if (a.P == 1) {
+                                                const float v = tot * scale;
+                                                if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
+                                                else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
+                                            } else {
+                                                st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], tot);
+                                            }
                                         }
                                     }
-                                }
-                        }
+                            }
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+                            for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // items stay in order (no hoisted decodes)
+                    if (it + kRing < NI) {
+                        const int nx = it + kRing < nitems ? it + kRing : (it < nitems ? it : nitems - 1);
+                        load_item(nx, ring[s]);          // consume slot s, then refill it
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-                if (it + kRing < kMaxItems) {
-                    const int nx = it + kRing < nitems ? it + kRing : (it < nitems ? it : nitems - 1);
-                    __builtin_amdgcn_sched_barrier(0);   // keep: consume slot s, then refill it
-                    load_item(nx, ring[s]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             }
-        }
+        };
+        run(std::integral_constant<int, REFILL ? kMaxItems : kRing>{});
     }
 
     TL(3);
@@ -568,7 +577,7 @@ void decode_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------- planning
-struct Plan { int MT, U, P, T, tw, G, mode; int64_t NT, Q; size_t lds; };
+struct Plan { int MT, U, P, T, tw, G, mode; bool refill; int64_t NT, Q; size_t lds; };
 
 int resident_capacity(const void *fn, size_t lds) {
     int dev = 0, cus = 0;
@@ -580,16 +589,17 @@ int resident_capacity(const void *fn, size_t lds) {
     return per * cus;
 }
 
-template <bool TILED>
+template <bool TILED, bool REFILL>
 const void *kernel_ptr_t(int MT, bool res) {
-    if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED>)
-                            : reinterpret_cast<const void *>(&decode_kernel<1, false, TILED>);
-    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED>)
-               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED>);
+    if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL>)
+                            : reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, REFILL>);
+    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL>);
 }
 
-const void *kernel_ptr(int MT, bool res, bool tiled = false) {
-    return tiled ? kernel_ptr_t<true>(MT, res) : kernel_ptr_t<false>(MT, res);
+const void *kernel_ptr(int MT, bool res, bool tiled = false, bool refill = true) {
+    if (tiled) return refill ? kernel_ptr_t<true, true>(MT, res) : kernel_ptr_t<true, false>(MT, res);
+    return refill ? kernel_ptr_t<false, true>(MT, res) : kernel_ptr_t<false, false>(MT, res);
 }
 
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
@@ -637,6 +647,8 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     pl.Q = (pl.NT + pl.T - 1) / pl.T;
     pl.G = (int)(pl.P * pl.Q);
     pl.lds = (size_t)pl.U * 16 * pl.MT * 64 * sizeof(half8) * (res ? 2 : 1);
+    // items per consumer wave: at most tw tiles x the units of a range
+    pl.refill = pl.tw * (pl.U < ku ? pl.U : (int)ku) > (pl.MT == 1 ? 4 : 3);
     // activation handling
     // Raw activations are quantized in the kernel only when every workgroup can
     // read all of X and each producer thread holds at most one 32-column chunk.
@@ -688,8 +700,8 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.partials = static_cast<float *>(g.scratch);
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
     void *args[] = {&a};
-    return hipLaunchKernel(kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0), dim3(pl.G), dim3(kThreads), args,
-                           pl.lds, st);
+    return hipLaunchKernel(kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill), dim3(pl.G), dim3(kThreads),
+                           args, pl.lds, st);
 }
 
 }  // namespace nvfp4
