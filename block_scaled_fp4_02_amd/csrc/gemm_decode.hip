@@ -53,6 +53,9 @@ constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile c
 constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
 constexpr int64_t kLocalMaxElems = 16384;      // LOCAL: X read by every workgroup (8 units of 8 per lane)
 constexpr int kLocalLoads = (int)(kLocalMaxElems / 8 / kPThreads);
+constexpr int kLocalChunks = 2;                // LOCAL: raw 32-column chunks per producer thread
+constexpr int kPreChunks = 8;                  // PRE: quantized chunks per producer thread and batch
+constexpr int kMaxP = 8;                       // split-K partials loaded at once by the combine
 
 enum Mode { MODE_PRE = 0, MODE_LOCAL = 1 };
 
@@ -78,7 +81,7 @@ struct DArgs {
     void *y; int yt; int64_t ldy;
     uint8_t *header;                          // zero-kept tile counters
     float *partials;                          // P x M x N floats
-    int U, P, T, tw, G, mode;
+    int U, P, T, tw, KW, G, mode;
     int64_t NT;
 };
 
@@ -147,12 +150,14 @@ struct Range {
     int npm, npr;               // chunk positions per row (32 columns each)
 };
 
-// Slot of the j = 0 fragment of the chunk of row m starting at column kc.
-template <int MT>
-__device__ inline int chunk_slot(int64_t kbeg, int m, int64_t kc) {
+// Operand layout (only the M real rows): slot (((u * 4 + i) * 4 + j) * 4 + g) * M + m
+// holds row m, columns kbeg + 512 u + 128 g + 32 i + 8 j .. + 8. This returns the
+// slot of fragment j = 0 of the chunk of row m starting at column kc; fragment j
+// adds 4 M j.
+__device__ inline int chunk_slot(int64_t kbeg, int M, int m, int64_t kc) {
     const int off = (int)(kc - kbeg);
-    const int u = off >> 9, w = (off >> 5) & 15;
-    return ((u * 16 + 4 * (w & 3)) * MT + (m >> 4)) * 64 + 16 * (w >> 2) + (m & 15);
+    const int u = off >> 9, w = (off >> 5) & 15;     // w = 4 g + i
+    return ((u * 4 + (w & 3)) * 16 + (w >> 2)) * M + m;
 }
 
 // Chunk c of the range (rows fastest): main chunks, then residue chunks.
@@ -164,7 +169,6 @@ struct ChunkPos {
     int key;
 };
 
-template <int MT>
 __device__ inline ChunkPos chunk_pos(const DArgs &a, const Range &r, int c, int slots) {
     ChunkPos f;
     const unsigned M = (unsigned)a.M;
@@ -175,7 +179,8 @@ __device__ inline ChunkPos chunk_pos(const DArgs &a, const Range &r, int c, int 
     const int64_t kc = r.kbeg + 32 * (int64_t)(res ? (int)pos - r.npm : (int)pos);
     f.m = m;
     f.col = res ? a.K + kc : kc;
-    f.key = chunk_slot<MT>(r.kbeg, (int)m, kc) + (res ? slots : 0) + (kc + 16 < (res ? r.rend : r.kend) ? kV1 : 0);
+    f.key = chunk_slot(r.kbeg, (int)M, (int)m, kc) + (res ? slots : 0) +
+            (kc + 16 < (res ? r.rend : r.kend) ? kV1 : 0);
     return f;
 }
 
@@ -202,17 +207,17 @@ __device__ inline QChunk qchunk_load(const DArgs &a, const ChunkPos &f) {
     return q;
 }
 
-template <int MT>
-__device__ inline void qchunk_store(half8 *lds, const QChunk &q) {
+// Decode a chunk into its four fragments (j stride js = 4 M slots).
+__device__ inline void qchunk_store(half8 *lds, int js, const QChunk &q) {
     if (q.key < 0) return;
     const bool v1 = q.key & kV1;
     const int slot = q.key & (kV1 - 1);
     const half2v d0 = scale_pair(q.s0), d1 = scale_pair(v1 ? q.s1 : 0u);
     const uint32_t hi0 = v1 ? (uint32_t)q.hi : 0u, hi1 = v1 ? (uint32_t)(q.hi >> 32) : 0u;
     lds[slot] = decode8((uint32_t)q.lo, d0);
-    lds[slot + MT * 64] = decode8((uint32_t)(q.lo >> 32), d0);
-    lds[slot + 2 * MT * 64] = decode8(hi0, d1);
-    lds[slot + 3 * MT * 64] = decode8(hi1, d1);
+    lds[slot + js] = decode8((uint32_t)(q.lo >> 32), d0);
+    lds[slot + 2 * js] = decode8(hi0, d1);
+    lds[slot + 3 * js] = decode8(hi1, d1);
 }
 
 // 32 bf16 activations of one row (a raw chunk); the second block is read only
@@ -241,7 +246,7 @@ __device__ inline void bf16x16(const uint4 &p, const uint4 &q, float *v) {
 // Quantize a raw chunk (row m, columns kc..) against S into its LDS slots and,
 // for columns below the residue bound, the residue's slots; the writer also
 // stores codes and scales into the quantized-activation buffer.
-template <int MT, bool RES>
+template <bool RES>
 __device__ inline void xchunk_quantize(const DArgs &a, half8 *lds, int slots, int64_t kbeg, int64_t rend,
                                        int64_t m, int64_t kc, bool v1, const XChunk &x, float S, bool writer) {
     const float t = 6.0f * S;
@@ -263,17 +268,18 @@ __device__ inline void xchunk_quantize(const DArgs &a, half8 *lds, int slots, in
             rc[2 * b + 1] = cw[1];
         }
     }
-    const int slot = chunk_slot<MT>(kbeg, (int)m, kc);
+    const int M = (int)a.M, js = 4 * M;
+    const int slot = chunk_slot(kbeg, M, (int)m, kc);
     {
         const half2v d0 = scale_pair(ms[0]), d1 = scale_pair(ms[1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lds[slot + j * MT * 64] = decode8(mc[j], j < 2 ? d0 : d1);
+        for (int j = 0; j < 4; ++j) lds[slot + j * js] = decode8(mc[j], j < 2 ? d0 : d1);
     }
     const bool has_res = RES && kc < rend;
     if (has_res) {
         const half2v d0 = scale_pair(rs[0]), d1 = scale_pair(rs[1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lds[slots + slot + j * MT * 64] = decode8(rc[j], j < 2 ? d0 : d1);
+        for (int j = 0; j < 4; ++j) lds[slots + slot + j * js] = decode8(rc[j], j < 2 ? d0 : d1);
     }
     if (writer) {
         uint8_t *crow = a.q_codes + m * a.q_ldc;
@@ -297,22 +303,21 @@ __device__ inline void xchunk_quantize(const DArgs &a, half8 *lds, int slots, in
     }
 }
 
-// Zero every operand slot that no chunk writes: rows >= M and chunk positions
-// past the data (LDS only).
-template <int MT>
-__device__ inline void zero_unwritten(half8 *lds, const Range &r, int slots, int64_t M) {
-    const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) - kCons;   // producer waves
-    constexpr int nwaves = kProd;
-    const int row = lane & 15, g = lane >> 4;
+// Zero the operand slots that no chunk writes: chunk positions past the data
+// at the end of a ragged range (LDS only; producer waves).
+__device__ inline void zero_unwritten(half8 *lds, const Range &r, int slots, int M) {
+    const int ptid = (int)threadIdx.x - 64 * kCons;
     const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
     for (int reg = 0; reg < 2; ++reg) {
-        const int n = (reg == 0 ? r.units : r.res_units) * 16 * MT;   // 64-slot groups
-        const int64_t lim = reg == 0 ? r.kend : r.rend;
+        const int first = reg == 0 ? r.npm : r.npr;                     // first position past the data
+        const int npos = (reg == 0 ? r.units : r.res_units) * 16;       // 32-column positions
         half8 *base = lds + (reg == 0 ? 0 : slots);
-        for (int grp = wave; grp < n; grp += nwaves) {
-            const int mt = grp % MT, q4 = grp / MT;
-            const int64_t kc = r.kbeg + 512 * (q4 >> 4) + 128 * g + 32 * ((q4 >> 2) & 3);
-            if (16 * mt + row >= M || kc >= lim) base[grp * 64 + lane] = z;
+        const int total = (npos - first) * 4 * M;                        // (position, j, row)
+        for (int e = ptid; e < total; e += kPThreads) {
+            const int m = e % M, rest = e / M, j = rest & 3, pos = first + (rest >> 2);
+            const int u = pos >> 4, w = pos & 15;
+            base[(((u * 4 + (w & 3)) * 4 + j) * 4 + (w >> 2)) * M + m] = z;
         }
     }
 }
@@ -326,7 +331,7 @@ void decode_kernel(DArgs a) {
     // after it, so that computing on landed items overlaps the (throttled)
     // issue of later loads.
     constexpr int kPre = kPreItems < kRing ? kPreItems : kRing;
-    extern __shared__ half8 lds_a[];          // [U][16][MT][64] (+ residue copy)
+    extern __shared__ half8 lds_a[];          // operand [U][4 i][4 j][4 g][M] (+ residue copy); then tile sums
     __shared__ float sh_S;
     __shared__ float sh_part[kProd];
     __shared__ unsigned sh_cnt;
@@ -334,6 +339,7 @@ void decode_kernel(DArgs a) {
     // wave index as a scalar: branches on it are uniform (barriers inside them stay per wave)
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r16 = lane & 15;
+    const int M = (int)a.M;
     const int p = blockIdx.x % a.P;
     const int64_t q = blockIdx.x / a.P;
     Range rg;
@@ -347,22 +353,28 @@ void decode_kernel(DArgs a) {
     rg.npr = (int)((rg.rend - rg.kbeg + 31) / 32);
     const int64_t kbeg = rg.kbeg;
     const int units = rg.units, res_units = rg.res_units;
-    const int slots = a.U * 16 * MT * 64;
+    const int slots = a.U * 64 * M;              // operand slots of a full range; the residue copy follows
     const int64_t t_lo = q * a.T, t_hi = (q + 1) * a.T < a.NT ? (q + 1) * a.T : a.NT;
 
-    // consumer work: tiles t_lo + wave + kCons * j
-    const int64_t t_first = t_lo + wave;
-    const int ntiles = (wave < kCons && t_first < t_hi) ? (int)((t_hi - t_first + kCons - 1) / kCons) : 0;
-    const int nitems = ntiles * units;
-    // Item it = (tile t_first + kCons * (it / units), unit it % units of the
-    // range); rows and tiles are clamped into W, so loads never leave it.
+    // Consumer wave w takes tiles t_lo + w / KW + TW i_t (i_t < ntw) and units
+    // w % KW + KW i_u (i_u < nuw) of the range: KW waves share each tile, each
+    // summing its own units, and their parts are added in LDS at the end.
+    const int KW = a.KW, TW = kCons / KW;
+    const int tg = wave / KW, uo = wave % KW;
+    const int ntw = (wave < kCons && t_lo + tg < t_hi) ? (int)((t_hi - t_lo - tg + TW - 1) / TW) : 0;
+    const int nuw = (wave < kCons && uo < units) ? (units - uo + KW - 1) / KW : 0;
+    const int nitems = ntw * nuw;
+    // Item it = (tile i_t = it / nuw, unit i_u = it % nuw); tiles and rows are
+    // clamped into W, so loads never leave it.
     auto load_item = [&](int it, WLoad &w) {
-        const int64_t t = t_first + (int64_t)(it / units) * kCons;
+        const int at = it / nuw, bu = it - at * nuw;
+        const int64_t t = t_lo + tg + (int64_t)TW * at;
+        const int64_t ul = uo + (int64_t)KW * bu;
         if (TILED) {
-            load_w_tiled(a, t < 0 ? 0 : (t < a.NT ? t : a.NT - 1), kbeg / 512 + it % units, lane, w);
+            load_w_tiled(a, t < a.NT ? t : a.NT - 1, kbeg / 512 + ul, lane, w);
         } else {
             const int64_t n = 16 * t + r16;
-            load_w(a, n < 0 ? 0 : (n < a.N ? n : a.N - 1), kbeg + 512 * (it % units), g, w);
+            load_w(a, n < a.N ? n : a.N - 1, kbeg + 512 * ul, g, w);
         }
     };
 
@@ -385,25 +397,38 @@ void decode_kernel(DArgs a) {
     } else {
         const int ptid = tid - 64 * kCons, pw = wave - kCons;
         if (a.mode == MODE_PRE) {
-            // chunks ptid + 256 t of the quantized activations
+            // chunks ptid + 256 t of the quantized activations, kPreChunks per
+            // thread before the barrier; larger ranges take further batches after it
             const float S = ptid == 0 ? a.q_S[0] : 0.0f;
-            QChunk qc[4];
+            const int nch = M * (rg.npm + rg.npr);
+            QChunk qc[kPreChunks];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                qc[t] = qchunk_load(a, chunk_pos<MT>(a, rg, ptid + kPThreads * t, slots));
+            for (int t = 0; t < kPreChunks; ++t) qc[t] = qchunk_load(a, chunk_pos(a, rg, ptid + kPThreads * t, slots));
             __syncthreads();                   // loads out: consumers may issue theirs
-            zero_unwritten<MT>(lds_a, rg, slots, a.M);
+            zero_unwritten(lds_a, rg, slots, M);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) qchunk_store<MT>(lds_a, qc[t]);
+            for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * M, qc[t]);
+            for (int c0 = kPreChunks * kPThreads; c0 < nch; c0 += kPreChunks * kPThreads) {
+#pragma unroll
+                for (int t = 0; t < kPreChunks; ++t)
+                    qc[t] = qchunk_load(a, chunk_pos(a, rg, c0 + ptid + kPThreads * t, slots));
+#pragma unroll
+                for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * M, qc[t]);
+            }
             if (ptid == 0) sh_S = S;
             TL(1);
             __syncthreads();                   // operand complete
         } else {
-            // LOCAL: raw chunk ptid of the range, and this wave's quarter of X for amax(X)
-            const int nraw = (int)a.M * rg.npm;
-            const ChunkPos f = chunk_pos<MT>(a, rg, ptid < nraw ? ptid : 1 << 30, slots);
-            const bool v1 = f.key >= 0 && (f.key & kV1);
-            const XChunk xc = xchunk_load(a, f.m, f.col, v1);
+            // LOCAL: raw chunks ptid and ptid + 256 of the range, and this wave's
+            // quarter of X for amax(X)
+            const int nraw = M * rg.npm;
+            XChunk xc[kLocalChunks];
+#pragma unroll
+            for (int t = 0; t < kLocalChunks; ++t) {
+                const int c = ptid + kPThreads * t;
+                const ChunkPos f = chunk_pos(a, rg, c < nraw ? c : 1 << 30, slots);
+                xc[t] = xchunk_load(a, f.m, f.col, f.key >= 0 && (f.key & kV1));
+            }
             const int64_t NU = a.M * (a.K / 8);
             const int64_t u0 = NU * pw / kProd, u1 = NU * (pw + 1) / kProd;
             uint4 av[kLocalLoads];
@@ -418,7 +443,7 @@ void decode_kernel(DArgs a) {
                 }
             }
             __syncthreads();                   // loads out: consumers may issue theirs
-            zero_unwritten<MT>(lds_a, rg, slots, a.M);
+            zero_unwritten(lds_a, rg, slots, M);
             if (!a.static_S) {
                 // for finite values the order of |bf16| bit patterns is that of the magnitudes
                 unsigned mx = 0;
@@ -448,8 +473,15 @@ void decode_kernel(DArgs a) {
             }
             if (blockIdx.x == 0 && ptid == 0) *a.q_S = S;
             if (ptid == 0) sh_S = S;
-            if (ptid < nraw)
-                xchunk_quantize<MT, RES>(a, lds_a, slots, kbeg, rg.rend, f.m, f.col, v1, xc, S, q == 0);
+#pragma unroll
+            for (int t = 0; t < kLocalChunks; ++t) {
+                const int c = ptid + kPThreads * t;
+                if (c < nraw) {
+                    const ChunkPos f = chunk_pos(a, rg, c, slots);
+                    xchunk_quantize<RES>(a, lds_a, slots, kbeg, rg.rend, f.m, f.col, (f.key & kV1) != 0, xc[t], S,
+                                         q == 0);
+                }
+            }
             TL(1);
             __syncthreads();                   // operand complete
         }
@@ -458,7 +490,36 @@ void decode_kernel(DArgs a) {
 
     // ---- consumers: decode weights, MFMA
     const float scale = sh_S * w_scale;
-    if (wave < kCons && nitems > 0) {            // waves without tiles issue no loads at all
+    // Output tile t of this workgroup: lane holds rows 16 mt + 4 g + e of column
+    // 16 t + r16; only rows < M are stored.
+    auto store_tile = [&](int64_t t, const float4v *v) {
+        const int64_t n = 16 * t + r16;
+        if (n >= a.N) return;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = 16 * mt + 4 * g + e;
+                if (m < a.M) {
+                    if (a.P == 1) {
+                        const float val = v[mt][e] * scale;
+                        if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = val;
+                        else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(val);
+                    } else {
+                        st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], v[mt][e]);
+                    }
+                }
+            }
+    };
+    // A-operand rows 16 mt + r16 >= M read row M - 1 instead: the MFMA output
+    // rows they feed are never stored.
+    int arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) arow[mt] = 16 * mt + r16 < M ? 16 * mt + r16 : M - 1;
+    float4v ts0[MT], ts1[MT];                  // this wave's parts of its first two tiles (KW > 1)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) { ts0[mt] = float4v{0, 0, 0, 0}; ts1[mt] = float4v{0, 0, 0, 0}; }
+    if (wave < kCons && nitems > 0) {            // waves without items issue no loads at all
         float4v acc[MT], acc2[MT];                 // two MFMA chains: even / odd fragments
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
@@ -467,76 +528,97 @@ void decode_kernel(DArgs a) {
         // Fully unrolled over NI items (no loop back-edge), NI = kRing when the
         // plan's items per wave fit the ring (no refills at all; a kernel of its
         // own, so the two loop shapes never share a register allocation) and
-        // kMaxItems otherwise:
-        // each slot is consumed in place and refilled right after, always with the
-        // same five loads (past the last item -- only in ragged waves -- it
-        // re-reads the current one), so vmcnt is tracked exactly and the common
-        // plans (4 or 8 items per wave) issue no redundant loads.
+        // kMaxItems otherwise: each slot is consumed in place and refilled right
+        // after, always with the same five loads (past the last item -- only in
+        // ragged waves -- it re-reads the current one), so vmcnt is tracked
+        // exactly and the common plans issue no redundant loads.
         auto run = [&](auto ni) {
             constexpr int NI = decltype(ni)::value;
+            int at = 0, bu = 0;                    // tile and unit of the current item (wave-uniform)
 #pragma unroll
             for (int it = 0; it < NI; ++it) {
                 const int s = it % kRing;
-                {
-                    if (it < nitems) {
-                        const int u = it % units;
-                        const half8 *abase = lds_a + (size_t)u * 16 * MT * 64 + lane;
-                        const bool res_u = RES && u < res_units;
+                if (it < nitems) {
+                    const int ul = uo + KW * bu;
+                    const half8 *abase = lds_a + ul * 64 * M + g * M;
+                    const bool res_u = RES && ul < res_units;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const uint32_t sw = (i < 2) ? ring[s].s.x : ring[s].s.y;
-                            const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
-                            const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
-                            const uint32_t cws[4] = {ring[s].c[i].x, ring[s].c[i].y, ring[s].c[i].z, ring[s].c[i].w};
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t sw = (i < 2) ? ring[s].s.x : ring[s].s.y;
+                        const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
+                        const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
+                        const uint32_t cws[4] = {ring[s].c[i].x, ring[s].c[i].y, ring[s].c[i].z, ring[s].c[i].w};
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
+                        for (int j = 0; j < 4; ++j) {
+                            const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
+                            const int fo = (4 * i + j) * 4 * M;
 #pragma unroll
-                                for (int mt = 0; mt < MT; ++mt) {
-                                    float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
-                                    ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[(4 * i + j) * MT * 64 + mt * 64], b,
-                                                                                ac, 0, 0, 0);
-                                    if (res_u)
-                                        ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                            abase[slots + (4 * i + j) * MT * 64 + mt * 64], b, ac, 0, 0, 0);
-                                }
+                            for (int mt = 0; mt < MT; ++mt) {
+                                float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
+                                ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt]], b, ac, 0, 0, 0);
+                                if (res_u)
+                                    ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[slots + fo + arow[mt]], b, ac,
+                                                                                0, 0, 0);
                             }
                         }
-                        if (u == units - 1) {
-                            // tile done: lane holds rows 16 mt + 4 g + e of column n
-                            const int64_t n = 16 * (t_first + (int64_t)(it / units) * kCons) + r16;
-                            if (n < a.N) {
+                    }
+                    if (bu == nuw - 1) {
+                        // this wave's part of tile t_lo + tg + TW at is complete
+                        float4v tot[MT];
 #pragma unroll
-                                for (int mt = 0; mt < MT; ++mt)
+                        for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt] + acc2[mt];
+                        if (KW == 1) {
+                            store_tile(t_lo + tg + (int64_t)TW * at, tot);
+                        } else if (at == 0) {
 #pragma unroll
-                                    for (int e = 0; e < 4; ++e) {
-                                        const int64_t m = 16 * mt + 4 * g + e;
-                                        const float tot = acc[mt][e] + acc2[mt][e];
-                                        if (m < a.M) {
-                                            if (a.P == 1) {
-                                                const float v = tot * scale;
-                                                if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
-                                                else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(v);
-                                            } else {
-                                                st_dev(&a.partials[((int64_t)p * a.M + m) * a.N + n], tot);
-                                            }
-                                        }
-                                    }
-                            }
+                            for (int mt = 0; mt < MT; ++mt) ts0[mt] = tot[mt];
+                        } else {
 #pragma unroll
-                            for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+                            for (int mt = 0; mt < MT; ++mt) ts1[mt] = tot[mt];
                         }
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+                        bu = 0;
+                        ++at;
+                    } else {
+                        ++bu;
                     }
-                    __builtin_amdgcn_sched_barrier(0);   // items stay in order (no hoisted decodes)
-                    if (it + kRing < NI) {
-                        const int nx = it + kRing < nitems ? it + kRing : (it < nitems ? it : nitems - 1);
-                        load_item(nx, ring[s]);          // consume slot s, then refill it
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);   // items stay in order (no hoisted decodes)
+                if (it + kRing < NI) {
+                    const int nx = it + kRing < nitems ? it + kRing : (it < nitems ? it : nitems - 1);
+                    load_item(nx, ring[s]);          // consume slot s, then refill it
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
         run(std::integral_constant<int, REFILL ? kMaxItems : kRing>{});
+    }
+
+    // ---- tiles shared by KW waves: their parts are added in LDS, in wave order
+    if (a.KW > 1) {
+        __syncthreads();                       // every consumer is done with the operand
+        float4v *red = reinterpret_cast<float4v *>(lds_a);   // [2 tiles][kCons][MT][64]
+        if (wave < kCons && nitems > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                red[((0 * kCons + wave) * MT + mt) * 64 + lane] = ts0[mt];
+                if (ntw > 1) red[((1 * kCons + wave) * MT + mt) * 64 + lane] = ts1[mt];
+            }
+        }
+        __syncthreads();
+        if (wave < kCons && uo == 0) {
+            for (int at = 0; at < ntw && at < 2; ++at) {
+                float4v sum[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) sum[mt] = float4v{0, 0, 0, 0};
+                for (int k = 0; k < KW && k < units; ++k) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) sum[mt] += red[((at * kCons + tg * KW + k) * MT + mt) * 64 + lane];
+                }
+                store_tile(t_lo + tg + (int64_t)TW * at, sum);
+            }
+        }
     }
 
     TL(3);
@@ -549,20 +631,33 @@ void decode_kernel(DArgs a) {
         __syncthreads();
         if (sh_last) {
             const int64_t ncols = (t_hi - t_lo) * 16;   // multiple of 16: whole column pairs
+            const bool pairs = (a.N & 1) == 0;
             for (int64_t idx = threadIdx.x; idx < a.M * (ncols / 2); idx += kThreads) {
                 const int64_t m = idx / (ncols / 2), n = 16 * t_lo + 2 * (idx - m * (ncols / 2));
                 if (n >= a.N) continue;
                 float s0 = 0.0f, s1 = 0.0f;
-                for (int pp = 0; pp < a.P; ++pp) {
-                    const float *src = &a.partials[((int64_t)pp * a.M + m) * a.N + n];
-                    if (n + 1 < a.N && ((a.N & 1) == 0)) {
-                        const unsigned long long v = ld_dev(reinterpret_cast<const unsigned long long *>(src));
-                        s0 += u2f((uint32_t)v);
-                        s1 += u2f((uint32_t)(v >> 32));
-                    } else {
-                        s0 += ld_dev(src);
-                        if (n + 1 < a.N) s1 += ld_dev(src + 1);
+                // kMaxP partials loaded at once, then added in order p = 0, 1, ...
+                for (int p0 = 0; p0 < a.P; p0 += kMaxP) {
+                    float v0[kMaxP], v1[kMaxP];
+#pragma unroll
+                    for (int k = 0; k < kMaxP; ++k) {
+                        v0[k] = 0.0f;
+                        v1[k] = 0.0f;
+                        if (p0 + k < a.P) {
+                            const float *src = &a.partials[((int64_t)(p0 + k) * a.M + m) * a.N + n];
+                            if (pairs) {
+                                const unsigned long long v = ld_dev(reinterpret_cast<const unsigned long long *>(src));
+                                v0[k] = u2f((uint32_t)v);
+                                v1[k] = u2f((uint32_t)(v >> 32));
+                            } else {
+                                v0[k] = ld_dev(src);
+                                if (n + 1 < a.N) v1[k] = ld_dev(src + 1);
+                            }
+                        }
                     }
+#pragma unroll
+                    for (int k = 0; k < kMaxP; ++k)
+                        if (p0 + k < a.P) { s0 += v0[k]; s1 += v1[k]; }
                 }
                 for (int c = 0; c < 2 && n + c < a.N; ++c) {
                     const float v = (c ? s1 : s0) * scale;
@@ -577,16 +672,22 @@ void decode_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------- planning
-struct Plan { int MT, U, P, T, tw, G, mode; bool refill; int64_t NT, Q; size_t lds; };
+struct Plan { int MT, U, P, T, tw, KW, G, mode; bool refill; int64_t NT, Q; size_t lds; };
 
-int resident_capacity(const void *fn, size_t lds) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 1;                       // no device: plan conservatively
-    int per = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kThreads, lds) != hipSuccess || per < 1) per = 1;
-    return per * cus;
+constexpr size_t kLdsPerCu = 160 * 1024;       // gfx950
+constexpr size_t kLdsStatic = 256;             // the kernel's own __shared__ words, rounded up
+
+int cu_count() {
+    static int cus = 0;
+    if (cus <= 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+            cus = c;
+        else
+            return 256;                        // no device: plan for MI355X
+    }
+    return cus;
 }
 
 template <bool TILED, bool REFILL>
@@ -597,69 +698,81 @@ const void *kernel_ptr_t(int MT, bool res) {
                : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL>);
 }
 
-const void *kernel_ptr(int MT, bool res, bool tiled = false, bool refill = true) {
+const void *kernel_ptr(int MT, bool res, bool tiled, bool refill) {
     if (tiled) return refill ? kernel_ptr_t<true, true>(MT, res) : kernel_ptr_t<true, false>(MT, res);
     return refill ? kernel_ptr_t<false, true>(MT, res) : kernel_ptr_t<false, false>(MT, res);
 }
 
+// Work split of one call. A K range of U units (P ranges) costs its operand in
+// LDS (U x 1 KiB per activation row, twice with residue columns); KW consumer
+// waves share each tile (TW = 4 / KW tiles at a time, ntw per wave). The
+// estimate charges each item (16 rows x 512 columns of W) its streaming time
+// on the busiest CU -- a CU streams ~0.23 us per item with its loads in flight
+// -- plus ~1.5 us for a split-K combine, which costs three dependent
+// round trips through the memory system.
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
     Plan pl;
     pl.MT = M <= 16 ? 1 : 2;
     const bool res = res_cols > 0;
-    int umax = (pl.MT == 1 ? 4 : 2) / (res ? 2 : 1);
-    if (umax < 1) umax = 1;
-    const size_t lds_max = (size_t)umax * 16 * pl.MT * 64 * sizeof(half8) * (res ? 2 : 1);
-    static int cap_cache[2][2] = {{0, 0}, {0, 0}};
-    int &capc = cap_cache[pl.MT - 1][res ? 1 : 0];
-    if (capc <= 1) capc = resident_capacity(kernel_ptr(pl.MT, res), lds_max);
-    int cap = capc;                  // one round of resident workgroups
-    if (const char *e = std::getenv("NVFP4_DECODE_MAX_GRID")) {      // tuning override
-        const int v = std::atoi(e);
-        if (v > 0) cap = v;
-    }
+    const int ring = pl.MT == 1 ? 4 : 3;
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
-    int bestU = 1, besttw = 1;
+    const int ncu = cu_count();
     double best = 1e30;
-    for (int U = 1; U <= umax; U *= 2) {
-        for (int tw = 1; tw <= 16; ++tw) {
-            const int64_t P = (ku + U - 1) / U, Q = (pl.NT + kCons * tw - 1) / (kCons * tw);
-            const int64_t G = P * Q;
-            if (G > cap || Q > kMaxTileCounters) continue;
-            const int items = tw * (int)(U < ku ? U : ku);
-            if (items > kMaxItems) continue;
-            const double cost = items + 0.15 * (double)P + (G < 192 ? 4.0 : 0.0);
-            if (cost < best) { best = cost; bestU = U; besttw = tw; }
+    int bU = 1, bKW = 1, bntw = 1;
+    bool found = false;
+    for (int64_t P0 = 1; P0 <= ku && P0 <= 64; ++P0) {
+        const int64_t U = (ku + P0 - 1) / P0, P = (ku + U - 1) / U;
+        if (P != P0) continue;                 // each split once
+        const size_t lds_a = (size_t)U * 1024 * (size_t)M * (res ? 2 : 1);
+        for (int KW = 1; KW <= kCons; KW *= 2) {
+            const int TW = kCons / KW;
+            const int64_t nuw = (U + KW - 1) / KW;
+            for (int ntw = 1; ntw <= kMaxItems; ++ntw) {
+                if (ntw * nuw > kMaxItems || (KW > 1 && ntw > 2)) break;
+                const int64_t T = (int64_t)TW * ntw, Q = (pl.NT + T - 1) / T, G = P * Q;
+                size_t lds = lds_a > (KW > 1 ? (size_t)8192 * pl.MT : 0) ? lds_a : (size_t)8192 * pl.MT;
+                lds = (lds + 255) / 256 * 256;
+                const int per_cu = lds + kLdsStatic <= kLdsPerCu / 2 ? 2 : (lds + kLdsStatic <= kLdsPerCu ? 1 : 0);
+                if (per_cu == 0 || Q > kMaxTileCounters) continue;   // more than one round is allowed
+                const double items_wg = (double)T * (double)U;
+                const double cost = 0.23 * items_wg * (double)((G + ncu - 1) / ncu) +
+                                    (P > 1 ? 1.5 + 0.1 * (double)P : 0.0) + (KW > 1 ? 0.1 : 0.0);
+                if (cost < best) { best = cost; bU = (int)U; bKW = KW; bntw = ntw; found = true; }
+            }
         }
     }
-    if (const char *e = std::getenv("NVFP4_DECODE_FORCE")) {         // tuning override "U,tw"
-        int fu = 0, ft = 0;
-        if (std::sscanf(e, "%d,%d", &fu, &ft) == 2 && fu >= 1 && fu <= umax && ft >= 1 &&
-            ft * (fu < ku ? fu : (int)ku) <= kMaxItems && (pl.NT + kCons * ft - 1) / (kCons * ft) <= kMaxTileCounters) {
-            bestU = fu;
-            besttw = ft;
+    if (const char *e = std::getenv("NVFP4_DECODE_FORCE")) {         // tuning override "U,KW,ntw"
+        int fu = 0, fk = 0, ft = 0;
+        if (std::sscanf(e, "%d,%d,%d", &fu, &fk, &ft) == 3 && fu >= 1 && (fk == 1 || fk == 2 || fk == 4) &&
+            ft >= 1 && ft * ((fu + fk - 1) / fk) <= kMaxItems && (fk == 1 || ft <= 2)) {
+            bU = fu; bKW = fk; bntw = ft; found = true;
         }
     }
-    pl.U = bestU > ku ? (int)ku : bestU;
-    pl.tw = besttw;
-    pl.T = kCons * pl.tw;
+    if (!found) { bU = 1; bKW = 1; bntw = 1; }
+    pl.U = bU > ku ? (int)ku : bU;
+    pl.KW = bKW;
+    pl.tw = bntw;
+    pl.T = (kCons / pl.KW) * pl.tw;
     pl.P = (int)((ku + pl.U - 1) / pl.U);
     pl.Q = (pl.NT + pl.T - 1) / pl.T;
     pl.G = (int)(pl.P * pl.Q);
-    pl.lds = (size_t)pl.U * 16 * pl.MT * 64 * sizeof(half8) * (res ? 2 : 1);
-    // items per consumer wave: at most tw tiles x the units of a range
-    pl.refill = pl.tw * (pl.U < ku ? pl.U : (int)ku) > (pl.MT == 1 ? 4 : 3);
-    // activation handling
+    {
+        const size_t lds_a = (size_t)pl.U * 1024 * (size_t)M * (res ? 2 : 1);
+        const size_t red = pl.KW > 1 ? (size_t)8192 * pl.MT : 0;
+        pl.lds = ((lds_a > red ? lds_a : red) + 255) / 256 * 256;
+    }
+    pl.refill = (int64_t)pl.tw * ((pl.U + pl.KW - 1) / pl.KW) > ring;
     // Raw activations are quantized in the kernel only when every workgroup can
-    // read all of X and each producer thread holds at most one 32-column chunk.
+    // read all of X and each producer thread holds at most kLocalChunks chunks.
     const int64_t kc = (int64_t)pl.U * 512 < K ? (int64_t)pl.U * 512 : K;
     const int64_t raw_chunks = M * ((kc + 31) / 32);
-    pl.mode = (raw_x && !norm_or_perm && raw_chunks <= kPThreads && M * K <= kLocalMaxElems) ? MODE_LOCAL
-                                                                                            : MODE_PRE;
+    pl.mode = (raw_x && !norm_or_perm && raw_chunks <= (int64_t)kLocalChunks * kPThreads && M * K <= kLocalMaxElems)
+                  ? MODE_LOCAL : MODE_PRE;
     if (std::getenv("NVFP4_DEBUG_PLAN"))
-        std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d T=%d G=%d mode=%d "
-                     "(resident capacity %d)\n", (long long)M, (long long)N, (long long)K, (long long)res_cols,
-                     pl.MT, pl.U, pl.P, pl.T, pl.G, pl.mode, capc);
+        std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d KW=%d T=%d G=%d "
+                     "lds=%zu refill=%d mode=%d cost=%.2f\n", (long long)M, (long long)N, (long long)K,
+                     (long long)res_cols, pl.MT, pl.U, pl.P, pl.KW, pl.T, pl.G, pl.lds, (int)pl.refill, pl.mode, best);
     return pl;
 }
 
@@ -698,10 +811,14 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
     a.header = reinterpret_cast<uint8_t *>(g.header);
     a.partials = static_cast<float *>(g.scratch);
-    a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
+    a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.KW = pl.KW; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
+    const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill);
+    if (pl.lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
+        if (e != hipSuccess) return e;
+    }
     void *args[] = {&a};
-    return hipLaunchKernel(kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill), dim3(pl.G), dim3(kThreads),
-                           args, pl.lds, st);
+    return hipLaunchKernel(fn, dim3(pl.G), dim3(kThreads), args, pl.lds, st);
 }
 
 }  // namespace nvfp4
