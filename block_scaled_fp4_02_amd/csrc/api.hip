@@ -50,6 +50,15 @@ size_t gemm_ws(int64_t M, int64_t N, int64_t K, int64_t S) {
     return 0;
 }
 
+// Bound on the small quantizer's arrival wait, in polls of ~0.1 us (a few ms).
+// NVFP4_SPIN_LIMIT overrides it from the host (0 = give up at once), so the
+// recompute fallback can be exercised without any fault or hang.
+unsigned spin_limit() {
+    const char *e = std::getenv("NVFP4_SPIN_LIMIT");
+    if (e && *e) return (unsigned)std::strtoul(e, nullptr, 10);
+    return 1u << 16;
+}
+
 struct Carver {
     uint8_t *p; size_t left; bool ok = true;
     uint8_t *take(size_t n) {
@@ -111,7 +120,7 @@ nvfp4_status check_opts(const nvfp4_quant_opts *o, int64_t K_in) {
 // Enqueue the quantizer writing into `out` (validated by the caller).
 nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in, int64_t ldx,
                               const nvfp4_quant_opts *opts, const nvfp4_tensor &out,
-                              float *partials, float *rscale, hipStream_t st) {
+                              float *partials, float *rscale, unsigned *header, hipStream_t st) {
     QuantLaunch q;
     q.x = x; q.xt = xt; q.rows = rows; q.K_in = K_in; q.ldx = ldx;
     q.gamma = opts ? static_cast<const uint16_t *>(opts->gamma) : nullptr;
@@ -122,6 +131,8 @@ nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in,
     q.codes = out.codes; q.ldc = out.ld_codes; q.scales = out.scales; q.lds = out.ld_scales;
     q.S_out = out.tensor_scale;
     q.partials = partials; q.rscale = rscale;
+    q.bar = header;                            // header words 0 and 1
+    q.spin = spin_limit();
     hipError_t e = launch_quantize(q, st);
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
@@ -198,7 +209,7 @@ nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, i
     float *partials = reinterpret_cast<float *>(c.take(kAmaxPartials * sizeof(float)));
     float *rscale = reinterpret_cast<float *>(c.take((size_t)std::max<int64_t>(rows, 1) * sizeof(float)));
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
-    return enqueue_quantize(x, xt, rows, K_in, ldx, opts, *out, partials, rscale,
+    return enqueue_quantize(x, xt, rows, K_in, ldx, opts, *out, partials, rscale, static_cast<unsigned *>(ws),
                             static_cast<hipStream_t>(stream));
 }
 
@@ -240,7 +251,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
     const bool skinny = M <= kSkinnyMaxM && K > 0;
     if (!a_q && skinny && decode_can_fuse(M, N, K, 0, xt == NVFP4_BF16))
         return enqueue_fused(x, xt, ldx, nullptr, aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
-    if (!a_q) CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, st));
+    if (!a_q) CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, header, st));
     return enqueue_gemm(aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
 }
 
@@ -284,7 +295,7 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
     if (N > 0 && plain && skinny && decode_can_fuse(M, N, K, S, xt == NVFP4_BF16))
         return enqueue_fused(x, xt, ldx, opts ? opts->static_tensor_scale : nullptr, aq, *w, M, K, S, y, yt, ldy,
                              header, scratch, sb, st);
-    CHECK(enqueue_quantize(x, xt, M, K, ldx, opts, aq, partials, rscale, st));
+    CHECK(enqueue_quantize(x, xt, M, K, ldx, opts, aq, partials, rscale, header, st));
     if (N == 0) return NVFP4_OK;
     return enqueue_gemm(aq, *w, M, K, S, y, yt, ldy, header, scratch, sb, st);
 }

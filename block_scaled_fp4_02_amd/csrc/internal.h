@@ -23,6 +23,8 @@ struct QuantLaunch {
     // workspace
     float *partials;                        // kAmaxPartials floats
     float *rscale;                          // rows floats (RMSNorm factors)
+    unsigned *bar;                          // 2 header words (arrival count, generation), or nullptr
+    unsigned spin;                          // bound on the arrival wait (polls)
 };
 
 // Enqueue the amax pass (if the scale is dynamic) and the quantize pass.
@@ -36,9 +38,11 @@ struct ChannelAbsmaxLaunch {
 };
 hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 
-// Every workspace starts with a header of counters used by the split-K
-// combine. It must be zero before the first call on a workspace; every call
-// leaves it zero.
+// Every workspace starts with a header of counters: the small quantizer's
+// arrival count and generation (bytes 0..7) and the decode product's split-K
+// tile counters (from byte 4096). It must be zero before the first call on a
+// workspace; calls keep it valid (counts return to zero, the generation only
+// advances), so it never needs clearing again.
 constexpr size_t kHeaderBytes = 8192;
 
 // Decode-shaped (M <= 32) product in one launch. With x != nullptr (bf16, and

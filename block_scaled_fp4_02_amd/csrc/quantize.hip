@@ -259,6 +259,110 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(QArgs a) {
     }
 }
 
+// ------------------------------------------------- small activations, one launch
+// Decode-sized activations (rows <= 32, no RMSNorm or reorder) in one launch of
+// G <= 64 workgroups, a thread per 16-element block (up to kSmallPer each):
+// partial maxima, one grid-wide arrival, then each workgroup encodes its blocks
+// from registers. Between launches the GPU is otherwise idle, so the arrival is
+// short; it is bounded, and a workgroup whose wait gives up recomputes amax(X)
+// itself (same result).
+constexpr int kSmallPer = 4;
+constexpr int kSmallMaxG = 64;
+
+template <typename T>
+__device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+template <typename T>
+__device__ inline T add_dev(T *p, T v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int XT>
+__global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsigned *bar, float *part, int G,
+                                                                   unsigned spin) {
+    __shared__ float sh[kThreads / 64];
+    __shared__ int sh_ok;
+    const int64_t KB = a.K_in / 16, NB = a.rows * KB;
+    const int64_t b0 = (int64_t)blockIdx.x * NB / G, b1 = ((int64_t)blockIdx.x + 1) * NB / G;
+    float v[kSmallPer][16];
+    float m = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kSmallPer; ++t) {
+        const int64_t b = b0 + threadIdx.x + (int64_t)kThreads * t;
+        if (b < b1) {
+            const int64_t row = b / KB, blk = b - row * KB;
+            load16<XT>(a.x, row * a.ldx + 16 * blk, v[t]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[t][i]));
+        }
+    }
+    float S;
+    if (a.static_S) {
+        S = *a.static_S;
+    } else {
+        m = block_max(m, sh);
+        if (G > 1) {
+            if (threadIdx.x == 0) {
+                // sense-reversing arrival: bar[0] counts, bar[1] is the generation
+                st_dev(&part[blockIdx.x], m);
+                const unsigned gen = ld_dev(&bar[1]);
+                wait_vm();                     // the partial is visible and gen read before arriving
+                int ok = 1;
+                if (add_dev(&bar[0], 1u) == (unsigned)G - 1) {
+                    st_dev(&bar[0], 0u);
+                    wait_vm();
+                    add_dev(&bar[1], 1u);
+                } else {
+                    unsigned it = 0;
+                    while (ld_dev(&bar[1]) == gen) {
+                        if (++it > spin) { ok = 0; break; }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                sh_ok = ok;
+            }
+            __syncthreads();
+            float mm = 0.0f;
+            if (sh_ok) {
+                for (int i = threadIdx.x; i < G; i += kThreads) mm = fmaxf(mm, ld_dev(&part[i]));
+            } else {                           // the wait gave up: all of X here
+                for (int64_t b = threadIdx.x; b < NB; b += kThreads) {
+                    const int64_t row = b / KB, blk = b - row * KB;
+                    float w[16];
+                    load16<XT>(a.x, row * a.ldx + 16 * blk, w);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) mm = fmaxf(mm, fabsf(w[i]));
+                }
+            }
+            m = block_max(mm, sh);
+        }
+        S = m > 0.0f ? m / 2688.0f : 1.0f;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.S_out = S;
+    const float t6 = 6.0f * S;
+#pragma unroll
+    for (int t = 0; t < kSmallPer; ++t) {
+        const int64_t b = b0 + threadIdx.x + (int64_t)kThreads * t;
+        if (b < b1) {
+            const int64_t row = b / KB, blk = b - row * KB;
+            uint32_t cw[2];
+            float d;
+            const uint32_t db = encode_block(v[t], S, t6, cw, d);
+            *reinterpret_cast<uint2 *>(a.codes + row * a.ldc + 8 * blk) = make_uint2(cw[0], cw[1]);
+            a.scales[row * a.lds + blk] = (uint8_t)db;
+            if (16 * blk < a.res_cols) {
+                float rv[16];
+                block_residue(v[t], cw, d, S, rv);
+                uint32_t rc[2];
+                float dr;
+                const uint32_t rdb = encode_block(rv, S, t6, rc, dr);
+                *reinterpret_cast<uint2 *>(a.codes + row * a.ldc + a.K_in / 2 + 8 * blk) = make_uint2(rc[0], rc[1]);
+                a.scales[row * a.lds + KB + blk] = (uint8_t)rdb;
+            }
+        }
+    }
+}
+
 // Channel-gather variant: one workgroup per row stages the (normalized) row in
 // LDS, then each thread gathers its 64 columns through perm.
 template <int XT, bool NORM>
@@ -354,6 +458,21 @@ int amax_grid(int64_t rows, int64_t K) {
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
     const bool norm = q.gamma != nullptr, perm = q.perm != nullptr;
+    const int64_t nb = q.rows * (q.K_in / 16);
+    if (!norm && !perm && q.bar && q.rows <= 32 && nb > 0 && nb <= (int64_t)kSmallMaxG * kThreads * kSmallPer) {
+        int G = (int)((nb + kThreads - 1) / kThreads);
+        if (G > kSmallMaxG) G = kSmallMaxG;
+        QArgs a;
+        a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
+        a.gamma = nullptr; a.perm = nullptr; a.res_cols = q.res_cols; a.static_S = q.static_S;
+        a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
+        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale;
+        if (q.xt == IN_BF16)
+            quantize_small_kernel<IN_BF16><<<G, kThreads, 0, st>>>(a, q.bar, q.partials, G, q.spin);
+        else
+            quantize_small_kernel<IN_F32><<<G, kThreads, 0, st>>>(a, q.bar, q.partials, G, q.spin);
+        return hipGetLastError();
+    }
     int npart = 0;
     if (!q.static_S) {
         if (norm) {

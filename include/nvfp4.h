@@ -43,10 +43,11 @@
  *    enqueues work on it and returns without synchronizing.
  *  - The caller owns and allocates every buffer, including the workspace
  *    (size from nvfp4_workspace_size). The library never allocates device
- *    memory. The first 8 KiB of every workspace hold the counters of the
- *    decode product's split-K combine: they must be zero before the first
- *    call on a workspace, and every call leaves them zero. A workspace must
- *    not be used by two calls at the same time.
+ *    memory. The first 8 KiB of every workspace hold counters (the small
+ *    quantizer's arrival count and generation, the decode product's split-K
+ *    tile counters): they must be zero before the first call on a workspace;
+ *    calls keep them valid, so they never need clearing again. A workspace
+ *    must not be used by two calls at the same time.
  *  - Argument errors are detected before anything is enqueued; the call then
  *    returns a status != NVFP4_OK and leaves every output untouched. Launch
  *    failures return NVFP4_ERR_HIP; nvfp4_last_error() gives the HIP text.

@@ -156,3 +156,22 @@ def test_deterministic(nv):
     b = nv.quantize(x.to(DEV), residue_cols=256)
     torch.cuda.synchronize()
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales) and torch.equal(a.scale, b.scale)
+
+
+@pytest.mark.parametrize("rows,K,S", [(16, 14336, 0), (7, 4112, 2048), (32, 8192, 8192)])
+def test_small_quantizer_wait_fallback(nv, orc, rows, K, S, monkeypatch):
+    """The one-launch quantizer of decode-sized activations, with its grid-wide
+    arrival forced to give up at once (spin limit 0, set from the host): every
+    workgroup then recomputes amax(X) itself. Codes must equal the oracle's."""
+    x = inputs.small_random(300 + rows, rows, K)
+    ox = orc.quantize_aug(x, S_cols=S) if S else orc.quantize(x)
+    note(f"small quantizer rows={rows} K={K} S={S}: normal")
+    q0 = nv.quantize(x.to(DEV), residue_cols=S)
+    torch.cuda.synchronize()
+    assert_qtensor_equal(q0, ox, "normal")
+    monkeypatch.setenv("NVFP4_SPIN_LIMIT", "0")
+    note(f"small quantizer rows={rows} K={K} S={S}: fallback")
+    q1 = nv.quantize(x.to(DEV), residue_cols=S)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("NVFP4_SPIN_LIMIT")
+    assert_qtensor_equal(q1, ox, "fallback")
