@@ -28,7 +28,7 @@
 //    them in fixed order (deterministic) and writes y.
 //
 // Activations: PRE reads an already quantized tensor; LOCAL (raw bf16 X with
-// M K <= 16384) has every workgroup read all of X, take amax(X) itself and
+// M K <= 32768) has every workgroup read all of X, take amax(X) itself and
 // quantize its own K range -- no communication between workgroups. Larger raw
 // activations are quantized by the quantize kernels first: a grid-wide wait
 // inside a kernel that saturates HBM costs several microseconds, since every
@@ -51,9 +51,9 @@ constexpr int kMaxItems = 8;                   // (tile, unit) items per consume
 constexpr int kPreItems = 2;                   // items each consumer issues before the operand barrier
 constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
 constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
-constexpr int64_t kLocalMaxElems = 16384;      // LOCAL: X read by every workgroup (8 units of 8 per lane)
-constexpr int kLocalLoads = (int)(kLocalMaxElems / 8 / kPThreads);
-constexpr int kLocalChunks = 2;                // LOCAL: raw 32-column chunks per producer thread
+constexpr int64_t kLocalMaxElems = 32768;      // LOCAL: X read by every workgroup
+constexpr int kLocalLoads = 8;                 // LOCAL: amax loads per lane and batch (K split over workgroups)
+constexpr int kLocalChunks = 4;                // LOCAL: raw 32-column chunks per producer thread
 constexpr int kPreChunks = 8;                  // PRE: quantized chunks per producer thread and batch
 constexpr int kMaxP = 8;                       // split-K partials loaded at once by the combine
 
@@ -419,39 +419,57 @@ void decode_kernel(DArgs a) {
             TL(1);
             __syncthreads();                   // operand complete
         } else {
-            // LOCAL: raw chunks ptid and ptid + 256 of the range, and this wave's
-            // quarter of X for amax(X)
+            // LOCAL: raw chunks ptid + 256 t (t < kLocalChunks) of the range. When the
+            // range is all of K (P == 1) they are all of X and give amax(X) directly;
+            // otherwise each producer wave also reads its quarter of X for amax, in
+            // batches of kLocalLoads loads per lane (the first before the barrier).
             const int nraw = M * rg.npm;
+            const bool full = a.P == 1;
             XChunk xc[kLocalChunks];
 #pragma unroll
             for (int t = 0; t < kLocalChunks; ++t) {
                 const int c = ptid + kPThreads * t;
                 const ChunkPos f = chunk_pos(a, rg, c < nraw ? c : 1 << 30, slots);
-                xc[t] = xchunk_load(a, f.m, f.col, f.key >= 0 && (f.key & kV1));
+                xc[t] = xchunk_load(a, f.m, f.col, f.key >= 0 && (f.key & kV1));   // past the list: row 0 again
             }
             const int64_t NU = a.M * (a.K / 8);
             const int64_t u0 = NU * pw / kProd, u1 = NU * (pw + 1) / kProd;
-            uint4 av[kLocalLoads];
-            if (!a.static_S) {
-                const uint32_t KU = (uint32_t)(a.K / 8);
-                const uint16_t *x = static_cast<const uint16_t *>(a.x);
+            const uint32_t KU = (uint32_t)(a.K / 8);
+            const uint16_t *xb = static_cast<const uint16_t *>(a.x);
+            auto amax_batch = [&](int64_t base, uint4 *av) {
 #pragma unroll
                 for (int t = 0; t < kLocalLoads; ++t) {
-                    const int64_t idx = u0 + lane + 64 * t < u1 ? u0 + lane + 64 * t : u0;
+                    const int64_t idx = base + lane + 64 * t < u1 ? base + lane + 64 * t : u0;
                     const uint32_t row = (uint32_t)idx / KU, cu = (uint32_t)idx - row * KU;
-                    av[t] = *reinterpret_cast<const uint4 *>(x + (int64_t)row * a.ldx + 8 * (int64_t)cu);
+                    av[t] = *reinterpret_cast<const uint4 *>(xb + (int64_t)row * a.ldx + 8 * (int64_t)cu);
                 }
-            }
+            };
+            // for finite values the order of |bf16| bit patterns is that of the magnitudes
+            auto bits_max = [](unsigned mx, const uint4 &v) {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = max(mx, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+                return mx;
+            };
+            uint4 av[kLocalLoads];
+            if (!a.static_S && !full) amax_batch(u0, av);
             __syncthreads();                   // loads out: consumers may issue theirs
             zero_unwritten(lds_a, rg, slots, M);
             if (!a.static_S) {
-                // for finite values the order of |bf16| bit patterns is that of the magnitudes
                 unsigned mx = 0;
+                if (full) {
 #pragma unroll
-                for (int t = 0; t < kLocalLoads; ++t) {
-                    const uint32_t w[4] = {av[t].x, av[t].y, av[t].z, av[t].w};
+                    for (int t = 0; t < kLocalChunks; ++t)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) mx = max(mx, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+                        for (int h = 0; h < 4; ++h) mx = bits_max(mx, xc[t].w[h]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < kLocalLoads; ++t) mx = bits_max(mx, av[t]);
+                    for (int64_t base = u0 + 64 * kLocalLoads; base < u1; base += 64 * kLocalLoads) {
+                        amax_batch(base, av);
+#pragma unroll
+                        for (int t = 0; t < kLocalLoads; ++t) mx = bits_max(mx, av[t]);
+                    }
                 }
                 mx = wave_max_u(mx);
                 if (lane == 0) {

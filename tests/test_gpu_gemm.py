@@ -254,3 +254,19 @@ def test_tiled_weights_same_result(nv, M, N, K, S):
         z0, z1 = y0, y1
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(z0, z1)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 512, 28672), (2, 256, 16384), (8, 700, 4096), (3, 40, 10000 // 16 * 16)])
+def test_in_launch_quantization_shapes(nv, orc, M, N, K):
+    """Raw activations small enough to be quantized inside the decode launch, including
+    K ranges split over workgroups (amax then read separately from the range's chunks):
+    the product must match the oracle's on the oracle-quantized operands."""
+    x = inputs.small_random(500 + M, M, K)
+    w = inputs.small_random(501 + N, N, K, scale=0.02)
+    note(f"in-launch quantization M={M} N={N} K={K}")
+    wq = nv.quantize(w.to(DEV))
+    y = nv.gemm(x.to(DEV), wq)
+    torch.cuda.synchronize()
+    ref = orc.gemm(orc.quantize(x), orc.quantize(w))
+    err = gemm_error(y.cpu().numpy(), ref)
+    assert err <= TOL, err
