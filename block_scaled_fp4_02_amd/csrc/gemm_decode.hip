@@ -82,6 +82,8 @@ struct DArgs {
     uint8_t *header;                          // zero-kept tile counters
     float *partials;                          // P x M x N floats
     int U, P, T, tw, KW, G, mode;
+    int Rr;                                   // operand rows per slot group (M, or 2 Mp when stacked)
+    int Mp;                                   // stacked residue: residue row of m is Mp + m; else 0
     int64_t NT;
 };
 
@@ -150,14 +152,17 @@ struct Range {
     int npm, npr;               // chunk positions per row (32 columns each)
 };
 
-// Operand layout (only the M real rows): slot (((u * 4 + i) * 4 + j) * 4 + g) * M + m
-// holds row m, columns kbeg + 512 u + 128 g + 32 i + 8 j .. + 8. This returns the
-// slot of fragment j = 0 of the chunk of row m starting at column kc; fragment j
-// adds 4 M j.
-__device__ inline int chunk_slot(int64_t kbeg, int M, int m, int64_t kc) {
+// Operand layout (R rows per slot group): slot (((u * 4 + i) * 4 + j) * 4 + g) * R + rho
+// holds operand row rho, columns kbeg + 512 u + 128 g + 32 i + 8 j .. + 8. The rows
+// are the M activation rows (R = M), or -- residue columns with M <= 8 -- the M rows
+// at 0.. and their residue rows at Mp.. (Mp = M rounded up to a power of two,
+// R = 2 Mp): one 16-row MFMA then covers both, and output rows m and Mp + m are
+// added when the tile is stored. This returns the slot of fragment j = 0 of the
+// chunk of row rho starting at column kc; fragment j adds 4 R j.
+__device__ inline int chunk_slot(int64_t kbeg, int R, int rho, int64_t kc) {
     const int off = (int)(kc - kbeg);
     const int u = off >> 9, w = (off >> 5) & 15;     // w = 4 g + i
-    return ((u * 4 + (w & 3)) * 16 + (w >> 2)) * M + m;
+    return ((u * 4 + (w & 3)) * 16 + (w >> 2)) * R + rho;
 }
 
 // Chunk c of the range (rows fastest): main chunks, then residue chunks.
@@ -179,7 +184,8 @@ __device__ inline ChunkPos chunk_pos(const DArgs &a, const Range &r, int c, int 
     const int64_t kc = r.kbeg + 32 * (int64_t)(res ? (int)pos - r.npm : (int)pos);
     f.m = m;
     f.col = res ? a.K + kc : kc;
-    f.key = chunk_slot(r.kbeg, (int)M, (int)m, kc) + (res ? slots : 0) +
+    // residue chunks: stacked rows Mp + m, or the second copy `slots` further on
+    f.key = chunk_slot(r.kbeg, a.Rr, res && a.Mp ? a.Mp + (int)m : (int)m, kc) + (res && !a.Mp ? slots : 0) +
             (kc + 16 < (res ? r.rend : r.kend) ? kV1 : 0);
     return f;
 }
@@ -207,7 +213,7 @@ __device__ inline QChunk qchunk_load(const DArgs &a, const ChunkPos &f) {
     return q;
 }
 
-// Decode a chunk into its four fragments (j stride js = 4 M slots).
+// Decode a chunk into its four fragments (j stride js = 4 R slots).
 __device__ inline void qchunk_store(half8 *lds, int js, const QChunk &q) {
     if (q.key < 0) return;
     const bool v1 = q.key & kV1;
@@ -268,8 +274,9 @@ __device__ inline void xchunk_quantize(const DArgs &a, half8 *lds, int slots, in
             rc[2 * b + 1] = cw[1];
         }
     }
-    const int M = (int)a.M, js = 4 * M;
-    const int slot = chunk_slot(kbeg, M, (int)m, kc);
+    const int js = 4 * a.Rr;
+    const int slot = chunk_slot(kbeg, a.Rr, (int)m, kc);
+    const int rslot = a.Mp ? chunk_slot(kbeg, a.Rr, a.Mp + (int)m, kc) : slots + slot;
     {
         const half2v d0 = scale_pair(ms[0]), d1 = scale_pair(ms[1]);
 #pragma unroll
@@ -279,7 +286,7 @@ __device__ inline void xchunk_quantize(const DArgs &a, half8 *lds, int slots, in
     if (has_res) {
         const half2v d0 = scale_pair(rs[0]), d1 = scale_pair(rs[1]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lds[slots + slot + j * js] = decode8(rc[j], j < 2 ? d0 : d1);
+        for (int j = 0; j < 4; ++j) lds[rslot + j * js] = decode8(rc[j], j < 2 ? d0 : d1);
     }
     if (writer) {
         uint8_t *crow = a.q_codes + m * a.q_ldc;
@@ -304,20 +311,25 @@ __device__ inline void xchunk_quantize(const DArgs &a, half8 *lds, int slots, in
 }
 
 // Zero the operand slots that no chunk writes: chunk positions past the data
-// at the end of a ragged range (LDS only; producer waves).
-__device__ inline void zero_unwritten(half8 *lds, const Range &r, int slots, int M) {
+// at the end of a ragged range, for the M activation rows and the residue rows
+// (LDS only; producer waves). Padding rows between them are never read into a
+// stored output row and stay as they are.
+__device__ inline void zero_unwritten(half8 *lds, const DArgs &a, const Range &r, int slots) {
     const int ptid = (int)threadIdx.x - 64 * kCons;
+    const int M = (int)a.M, R = a.Rr;
     const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int reg = 0; reg < 2; ++reg) {
         const int first = reg == 0 ? r.npm : r.npr;                     // first position past the data
-        const int npos = (reg == 0 ? r.units : r.res_units) * 16;       // 32-column positions
-        half8 *base = lds + (reg == 0 ? 0 : slots);
+        // stacked residue rows span every unit of the range; a separate copy only its own
+        const int npos = (reg == 0 || a.Mp ? r.units : r.res_units) * 16;
+        half8 *base = lds + (reg == 1 && !a.Mp ? slots : 0);
+        const int row0 = reg == 1 && a.Mp ? a.Mp : 0;
         const int total = (npos - first) * 4 * M;                        // (position, j, row)
         for (int e = ptid; e < total; e += kPThreads) {
             const int m = e % M, rest = e / M, j = rest & 3, pos = first + (rest >> 2);
             const int u = pos >> 4, w = pos & 15;
-            base[(((u * 4 + (w & 3)) * 4 + j) * 4 + (w >> 2)) * M + m] = z;
+            base[(((u * 4 + (w & 3)) * 4 + j) * 4 + (w >> 2)) * R + row0 + m] = z;
         }
     }
 }
@@ -353,7 +365,8 @@ void decode_kernel(DArgs a) {
     rg.npr = (int)((rg.rend - rg.kbeg + 31) / 32);
     const int64_t kbeg = rg.kbeg;
     const int units = rg.units, res_units = rg.res_units;
-    const int slots = a.U * 64 * M;              // operand slots of a full range; the residue copy follows
+    const int R = a.Rr;                          // operand rows per slot group
+    const int slots = a.U * 64 * R;              // operand slots of a full range; a residue copy follows
     const int64_t t_lo = q * a.T, t_hi = (q + 1) * a.T < a.NT ? (q + 1) * a.T : a.NT;
 
     // Consumer wave w takes tiles t_lo + w / KW + TW i_t (i_t < ntw) and units
@@ -405,15 +418,15 @@ void decode_kernel(DArgs a) {
 #pragma unroll
             for (int t = 0; t < kPreChunks; ++t) qc[t] = qchunk_load(a, chunk_pos(a, rg, ptid + kPThreads * t, slots));
             __syncthreads();                   // loads out: consumers may issue theirs
-            zero_unwritten(lds_a, rg, slots, M);
+            zero_unwritten(lds_a, a, rg, slots);
 #pragma unroll
-            for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * M, qc[t]);
+            for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
             for (int c0 = kPreChunks * kPThreads; c0 < nch; c0 += kPreChunks * kPThreads) {
 #pragma unroll
                 for (int t = 0; t < kPreChunks; ++t)
                     qc[t] = qchunk_load(a, chunk_pos(a, rg, c0 + ptid + kPThreads * t, slots));
 #pragma unroll
-                for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * M, qc[t]);
+                for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
             }
             if (ptid == 0) sh_S = S;
             TL(1);
@@ -454,7 +467,7 @@ void decode_kernel(DArgs a) {
             uint4 av[kLocalLoads];
             if (!a.static_S && !full) amax_batch(u0, av);
             __syncthreads();                   // loads out: consumers may issue theirs
-            zero_unwritten(lds_a, rg, slots, M);
+            zero_unwritten(lds_a, a, rg, slots);
             if (!a.static_S) {
                 unsigned mx = 0;
                 if (full) {
@@ -510,7 +523,24 @@ void decode_kernel(DArgs a) {
     const float scale = sh_S * w_scale;
     // Output tile t of this workgroup: lane holds rows 16 mt + 4 g + e of column
     // 16 t + r16; only rows < M are stored.
-    auto store_tile = [&](int64_t t, const float4v *v) {
+    auto store_tile = [&](int64_t t, const float4v *vin) {
+        float4v v[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) v[mt] = vin[mt];
+        if (RES && MT == 1 && a.Mp) {
+            // stacked residue (MT == 1): output row m += row Mp + m. Row 4 g + e sits
+            // in lane group g, element e; Mp >= 4 puts the residue row in lane + 4 Mp.
+            const int mp = a.Mp;
+            float4v o;
+            if (mp >= 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = __shfl(v[0][e], (lane + 4 * mp) & 63);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = e + mp < 4 ? v[0][(e + mp) & 3] : 0.0f;
+            }
+            v[0] += o;
+        }
         const int64_t n = 16 * t + r16;
         if (n >= a.N) return;
 #pragma unroll
@@ -529,18 +559,23 @@ void decode_kernel(DArgs a) {
                 }
             }
     };
-    // A-operand rows 16 mt + r16 >= M read row M - 1 instead: the MFMA output
+    // A-operand rows 16 mt + r16 >= R read row R - 1 instead: the MFMA output
     // rows they feed are never stored.
     int arow[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) arow[mt] = 16 * mt + r16 < M ? 16 * mt + r16 : M - 1;
+    for (int mt = 0; mt < MT; ++mt) arow[mt] = 16 * mt + r16 < R ? 16 * mt + r16 : R - 1;
     float4v ts0[MT], ts1[MT];                  // this wave's parts of its first two tiles (KW > 1)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) { ts0[mt] = float4v{0, 0, 0, 0}; ts1[mt] = float4v{0, 0, 0, 0}; }
     if (wave < kCons && nitems > 0) {            // waves without items issue no loads at all
-        float4v acc[MT], acc2[MT];                 // two MFMA chains: even / odd fragments
+        // independent MFMA chains: even / odd fragments, and (MT == 1; for MT == 2 the
+        // registers are not there) the residue columns' own two
+        constexpr bool kSepRes = RES && MT == 1;
+        float4v acc[MT], acc2[MT], accr[1], accr2[1];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+#pragma unroll
+        for (int mt = 0; mt < 1; ++mt) { accr[mt] = float4v{0, 0, 0, 0}; accr2[mt] = float4v{0, 0, 0, 0}; }
 #pragma unroll
         for (int s = kPre; s < kRing; ++s) load_item(s < nitems ? s : nitems - 1, ring[s]);
         // Fully unrolled over NI items (no loop back-edge), NI = kRing when the
@@ -558,8 +593,8 @@ void decode_kernel(DArgs a) {
                 const int s = it % kRing;
                 if (it < nitems) {
                     const int ul = uo + KW * bu;
-                    const half8 *abase = lds_a + ul * 64 * M + g * M;
-                    const bool res_u = RES && ul < res_units;
+                    const half8 *abase = lds_a + ul * 64 * R + g * R;
+                    const bool res_u = RES && !a.Mp && ul < res_units;   // a separate residue copy
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t sw = (i < 2) ? ring[s].s.x : ring[s].s.y;
@@ -569,14 +604,16 @@ void decode_kernel(DArgs a) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
-                            const int fo = (4 * i + j) * 4 * M;
+                            const int fo = (4 * i + j) * 4 * R;
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) {
                                 float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
                                 ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt]], b, ac, 0, 0, 0);
-                                if (res_u)
-                                    ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[slots + fo + arow[mt]], b, ac,
+                                if (RES && res_u) {
+                                    float4v &ar = kSepRes ? ((j & 1) ? accr2[0] : accr[0]) : ac;
+                                    ar = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[slots + fo + arow[mt]], b, ar,
                                                                                 0, 0, 0);
+                                }
                             }
                         }
                     }
@@ -584,7 +621,10 @@ void decode_kernel(DArgs a) {
                         // this wave's part of tile t_lo + tg + TW at is complete
                         float4v tot[MT];
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt) tot[mt] = acc[mt] + acc2[mt];
+                        for (int mt = 0; mt < MT; ++mt) {
+                            tot[mt] = acc[mt] + acc2[mt];
+                            if (kSepRes) tot[mt] += accr[0] + accr2[0];
+                        }
                         if (KW == 1) {
                             store_tile(t_lo + tg + (int64_t)TW * at, tot);
                         } else if (at == 0) {
@@ -596,6 +636,8 @@ void decode_kernel(DArgs a) {
                         }
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
+                        accr[0] = float4v{0, 0, 0, 0};
+                        accr2[0] = float4v{0, 0, 0, 0};
                         bu = 0;
                         ++at;
                     } else {
@@ -690,7 +732,7 @@ void decode_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------- planning
-struct Plan { int MT, U, P, T, tw, KW, G, mode; bool refill; int64_t NT, Q; size_t lds; };
+struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool refill; int64_t NT, Q; size_t lds; };
 
 constexpr size_t kLdsPerCu = 160 * 1024;       // gfx950
 constexpr size_t kLdsStatic = 256;             // the kernel's own __shared__ words, rounded up
@@ -736,13 +778,18 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
     const int ncu = cu_count();
+    // operand rows: residue rows stacked under the activation rows when M <= 8
+    pl.Mp = 0;
+    if (res && M <= 8) { pl.Mp = 1; while (pl.Mp < M) pl.Mp *= 2; }
+    pl.Rr = pl.Mp ? 2 * pl.Mp : (int)M;
+    const int64_t op_rows = pl.Mp ? 2 * pl.Mp : (res ? 2 * M : M);   // rows of operand per unit
     double best = 1e30;
     int bU = 1, bKW = 1, bntw = 1;
     bool found = false;
     for (int64_t P0 = 1; P0 <= ku && P0 <= 64; ++P0) {
         const int64_t U = (ku + P0 - 1) / P0, P = (ku + U - 1) / U;
         if (P != P0) continue;                 // each split once
-        const size_t lds_a = (size_t)U * 1024 * (size_t)M * (res ? 2 : 1);
+        const size_t lds_a = (size_t)U * 1024 * (size_t)op_rows;
         for (int KW = 1; KW <= kCons; KW *= 2) {
             const int TW = kCons / KW;
             const int64_t nuw = (U + KW - 1) / KW;
@@ -776,7 +823,7 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     pl.Q = (pl.NT + pl.T - 1) / pl.T;
     pl.G = (int)(pl.P * pl.Q);
     {
-        const size_t lds_a = (size_t)pl.U * 1024 * (size_t)M * (res ? 2 : 1);
+        const size_t lds_a = (size_t)pl.U * 1024 * (size_t)op_rows;
         const size_t red = pl.KW > 1 ? (size_t)8192 * pl.MT : 0;
         pl.lds = ((lds_a > red ? lds_a : red) + 255) / 256 * 256;
     }
@@ -830,6 +877,7 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.header = reinterpret_cast<uint8_t *>(g.header);
     a.partials = static_cast<float *>(g.scratch);
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.KW = pl.KW; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
+    a.Rr = pl.Rr; a.Mp = pl.Mp;
     const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill);
     if (pl.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
