@@ -52,7 +52,7 @@ constexpr int kPreItems = 2;                   // items each consumer issues bef
 constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
 constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
 constexpr int64_t kLocalMaxElems = 32768;      // LOCAL: X read by every workgroup
-constexpr int kLocalLoads = 8;                 // LOCAL: amax loads per lane and batch (K split over workgroups)
+constexpr int kLocalLoads = 4;                 // LOCAL: amax loads per lane and batch (K split over workgroups)
 constexpr int kLocalChunks = 4;                // LOCAL: raw 32-column chunks per producer thread
 constexpr int kPreChunks = 8;                  // PRE: quantized chunks per producer thread and batch
 constexpr int kMaxP = 8;                       // split-K partials loaded at once by the combine
@@ -61,7 +61,8 @@ enum Mode { MODE_PRE = 0, MODE_LOCAL = 1 };
 
 #ifdef NVFP4_TIMELINE
 // Profiling builds only: per (workgroup, wave, point) s_memrealtime stamps (100 MHz).
-__device__ unsigned long long g_timeline[1024 * 8 * 8];
+// Internal linkage: the kernel addresses it PC-relative, with no load of its address.
+static __device__ unsigned long long g_timeline[1024 * 8 * 8];
 #define TL(point) do { if ((threadIdx.x & 63) == 0 && blockIdx.x < 1024) \
     g_timeline[(blockIdx.x * 8 + (threadIdx.x >> 6)) * 8 + (point)] = __builtin_amdgcn_s_memrealtime(); } while (0)
 #else
@@ -146,6 +147,13 @@ __device__ inline unsigned wave_max_u(unsigned v) {
 }
 
 // The workgroup's K range and its chunk counts.
+// A load through the vector memory path: counted by vmcnt, in order with the
+// weight loads, so it never holds up the scalar/LDS waits before the barriers
+// (a scalar load of a value in HBM would: every lgkmcnt wait covers it).
+__device__ inline float load_vmem(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct Range {
     int64_t kbeg, kend, rend;   // columns [kbeg, kend); residue columns [kbeg, rend)
     int units, res_units;       // 512-column units of each
@@ -165,51 +173,71 @@ __device__ inline int chunk_slot(int64_t kbeg, int R, int rho, int64_t kc) {
     return ((u * 4 + (w & 3)) * 16 + (w >> 2)) * R + rho;
 }
 
-// Chunk c of the range (rows fastest): main chunks, then residue chunks.
-// key = LDS slot of fragment j = 0, plus kV1 when the chunk's second 16-column
-// block is inside the data; -1 past the chunk list.
+// Producer thread ptid takes operand row m = ptid % M and the chunk positions
+// p0 + step t of the range (step = 256 / M, p0 = ptid / M): rows are fastest
+// across a wave, so each load instruction covers consecutive columns of each
+// row, and a thread's addresses need one division in all. Threads at or past
+// M * step have no positions (p0 is set past every list).
+struct PMap { int m, p0, step; };
+__device__ inline PMap prod_map(int ptid, int M) {
+    PMap r;
+    r.step = kPThreads / M;
+    r.m = ptid % M;
+    r.p0 = ptid < M * r.step ? ptid / M : 1 << 20;
+    return r;
+}
+
+// Chunk position pos of the range: 32 columns of one row; the npm main
+// positions come first, then the npr residue positions. key = LDS slot of
+// fragment j = 0, plus kV1 when the chunk's second 16-column block is inside
+// the data; -1 past the list.
 constexpr int kV1 = 1 << 30;
 struct ChunkPos {
-    int64_t m, col;   // row; stored column of the chunk start (residue columns follow column K)
+    int64_t col;   // stored column of the chunk start (residue columns follow column K)
     int key;
 };
 
-__device__ inline ChunkPos chunk_pos(const DArgs &a, const Range &r, int c, int slots) {
+__device__ inline ChunkPos chunk_at(const DArgs &a, const Range &r, int m, int pos, int slots) {
     ChunkPos f;
-    const unsigned M = (unsigned)a.M;
-    const unsigned nch = M * (unsigned)(r.npm + r.npr);
-    if ((unsigned)c >= nch) { f.m = 0; f.col = 0; f.key = -1; return f; }
-    const unsigned m = (unsigned)c % M, pos = (unsigned)c / M;
-    const bool res = (int)pos >= r.npm;
-    const int64_t kc = r.kbeg + 32 * (int64_t)(res ? (int)pos - r.npm : (int)pos);
-    f.m = m;
+    if (pos >= r.npm + r.npr) { f.col = 0; f.key = -1; return f; }
+    const bool res = pos >= r.npm;
+    const int lp = res ? pos - r.npm : pos;
+    const int64_t kc = r.kbeg + 32 * (int64_t)lp;
     f.col = res ? a.K + kc : kc;
     // residue chunks: stacked rows Mp + m, or the second copy `slots` further on
-    f.key = chunk_slot(r.kbeg, a.Rr, res && a.Mp ? a.Mp + (int)m : (int)m, kc) + (res && !a.Mp ? slots : 0) +
-            (kc + 16 < (res ? r.rend : r.kend) ? kV1 : 0);
+    const int w = lp & 15;
+    f.key = (((lp >> 4) * 4 + (w & 3)) * 16 + (w >> 2)) * a.Rr + (res && a.Mp ? a.Mp + m : m) +
+            (res && !a.Mp ? slots : 0) + (kc + 16 < (res ? r.rend : r.kend) ? kV1 : 0);
     return f;
 }
 
-// A chunk of the quantized-activation buffer: codes (low nibble = even column)
-// and the two block scales.
-struct QChunk { unsigned long long lo, hi; uint32_t s0, s1; int key; };
+// A chunk of the quantized-activation buffer: 16 bytes of codes (low nibble =
+// even column) and the two block scales.
+struct QChunk { uint4 c; uint32_t s; int key; };
 
-// Always the same four loads; a chunk past the list, or a second block past the
-// data, reads row 0's first bytes instead and is zeroed when stored.
-__device__ inline QChunk qchunk_load(const DArgs &a, const ChunkPos &f) {
-    const bool v1 = f.key >= 0 && (f.key & kV1);
-    const uint8_t *crow = a.q_codes + f.m * a.q_ldc;
-    const uint8_t *srow = a.q_scales + f.m * a.q_lds;
-    const unsigned long long *p0 = reinterpret_cast<const unsigned long long *>(crow + f.col / 2);
-    const unsigned long long *p1 =
-        reinterpret_cast<const unsigned long long *>(crow + (v1 ? f.col / 2 + 8 : f.col / 2));
-    const uint8_t *q0 = srow + f.col / 16, *q1 = srow + (v1 ? f.col / 16 + 1 : f.col / 16);
+// Without residue columns every chunk starts at a multiple of 32 columns: one
+// 16-byte and one 2-byte load. Row-major rows hold at least K/2 bytes of codes
+// and K/16 of scales, padded to multiples of 16 and 8, so both stay inside the
+// row's pitch even where the second block lies past the data (those bytes are
+// dropped when stored). Residue chunks start at column K + kc, only 8-byte
+// aligned when K is an odd multiple of 16, so with residue columns every chunk
+// takes two 8-byte and two 1-byte loads, the second of each only inside the
+// data (one code path: a branch on alignment would diverge within a wave).
+// Past the list it reads the row's start.
+template <bool RES>
+__device__ inline QChunk qchunk_load(const uint8_t *crow, const uint8_t *srow, const ChunkPos &f) {
     QChunk q;
-    q.lo = *p0;
-    q.hi = *p1;
-    q.s0 = *q0;
-    q.s1 = *q1;
     q.key = f.key;
+    if (!RES) {
+        q.c = *reinterpret_cast<const uint4 *>(crow + f.col / 2);
+        q.s = *reinterpret_cast<const uint16_t *>(srow + f.col / 16);
+    } else {
+        const bool v1 = f.key >= 0 && (f.key & kV1);
+        const uint2 lo = *reinterpret_cast<const uint2 *>(crow + f.col / 2);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(crow + (v1 ? f.col / 2 + 8 : f.col / 2));
+        q.c = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        q.s = (uint32_t)srow[f.col / 16] | ((uint32_t)srow[v1 ? f.col / 16 + 1 : f.col / 16] << 8);
+    }
     return q;
 }
 
@@ -218,12 +246,11 @@ __device__ inline void qchunk_store(half8 *lds, int js, const QChunk &q) {
     if (q.key < 0) return;
     const bool v1 = q.key & kV1;
     const int slot = q.key & (kV1 - 1);
-    const half2v d0 = scale_pair(q.s0), d1 = scale_pair(v1 ? q.s1 : 0u);
-    const uint32_t hi0 = v1 ? (uint32_t)q.hi : 0u, hi1 = v1 ? (uint32_t)(q.hi >> 32) : 0u;
-    lds[slot] = decode8((uint32_t)q.lo, d0);
-    lds[slot + js] = decode8((uint32_t)(q.lo >> 32), d0);
-    lds[slot + 2 * js] = decode8(hi0, d1);
-    lds[slot + 3 * js] = decode8(hi1, d1);
+    const half2v d0 = scale_pair(q.s & 0xFFu), d1 = scale_pair(v1 ? (q.s >> 8) & 0xFFu : 0u);
+    lds[slot] = decode8(q.c.x, d0);
+    lds[slot + js] = decode8(q.c.y, d0);
+    lds[slot + 2 * js] = decode8(v1 ? q.c.z : 0u, d1);
+    lds[slot + 3 * js] = decode8(v1 ? q.c.w : 0u, d1);
 }
 
 // 32 bf16 activations of one row (a raw chunk); the second block is read only
@@ -396,7 +423,7 @@ void decode_kernel(DArgs a) {
     // own branch so that it never shares registers with the consumers' loads in
     // flight.
     TL(0);
-    const float w_scale = a.w_S[0];
+    const float w_scale = load_vmem(a.w_S);
     WLoad ring[kRing];
     if (tid == 0) sh_cnt = 0;
     if (wave < kCons) {
@@ -410,21 +437,25 @@ void decode_kernel(DArgs a) {
     } else {
         const int ptid = tid - 64 * kCons, pw = wave - kCons;
         if (a.mode == MODE_PRE) {
-            // chunks ptid + 256 t of the quantized activations, kPreChunks per
-            // thread before the barrier; larger ranges take further batches after it
+            // the thread's chunk positions of the quantized activations, kPreChunks
+            // before the barrier; larger ranges take further batches after it
             const float S = ptid == 0 ? a.q_S[0] : 0.0f;
-            const int nch = M * (rg.npm + rg.npr);
+            const PMap pm = prod_map(ptid, M);
+            const uint8_t *crow = a.q_codes + (int64_t)pm.m * a.q_ldc;
+            const uint8_t *srow = a.q_scales + (int64_t)pm.m * a.q_lds;
+            const int npos = rg.npm + rg.npr;
             QChunk qc[kPreChunks];
 #pragma unroll
-            for (int t = 0; t < kPreChunks; ++t) qc[t] = qchunk_load(a, chunk_pos(a, rg, ptid + kPThreads * t, slots));
+            for (int t = 0; t < kPreChunks; ++t)
+                qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * t, slots));
             __syncthreads();                   // loads out: consumers may issue theirs
             zero_unwritten(lds_a, a, rg, slots);
 #pragma unroll
             for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
-            for (int c0 = kPreChunks * kPThreads; c0 < nch; c0 += kPreChunks * kPThreads) {
+            for (int b = kPreChunks; pm.p0 + pm.step * b < npos; b += kPreChunks) {
 #pragma unroll
                 for (int t = 0; t < kPreChunks; ++t)
-                    qc[t] = qchunk_load(a, chunk_pos(a, rg, c0 + ptid + kPThreads * t, slots));
+                    qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * (b + t), slots));
 #pragma unroll
                 for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
             }
@@ -432,27 +463,29 @@ void decode_kernel(DArgs a) {
             TL(1);
             __syncthreads();                   // operand complete
         } else {
-            // LOCAL: raw chunks ptid + 256 t (t < kLocalChunks) of the range. When the
-            // range is all of K (P == 1) they are all of X and give amax(X) directly;
-            // otherwise each producer wave also reads its quarter of X for amax, in
-            // batches of kLocalLoads loads per lane (the first before the barrier).
-            const int nraw = M * rg.npm;
+            // LOCAL: the thread's main chunk positions p0 + step t (t < kLocalChunks;
+            // the plan makes them cover the range). When the range is all of K
+            // (P == 1) they are all of X and give amax(X) directly; otherwise each
+            // producer wave also reads its quarter of X for amax, in batches of
+            // kLocalLoads loads per lane (the first before the barrier).
+            const PMap pm = prod_map(ptid, M);
             const bool full = a.P == 1;
             XChunk xc[kLocalChunks];
 #pragma unroll
             for (int t = 0; t < kLocalChunks; ++t) {
-                const int c = ptid + kPThreads * t;
-                const ChunkPos f = chunk_pos(a, rg, c < nraw ? c : 1 << 30, slots);
-                xc[t] = xchunk_load(a, f.m, f.col, f.key >= 0 && (f.key & kV1));   // past the list: row 0 again
+                const int pos = pm.p0 + pm.step * t;
+                const ChunkPos f = chunk_at(a, rg, pm.m, pos < rg.npm ? pos : 1 << 20, slots);
+                xc[t] = xchunk_load(a, pm.m, f.col, f.key >= 0 && (f.key & kV1));   // past the list: the row's start
             }
-            const int64_t NU = a.M * (a.K / 8);
-            const int64_t u0 = NU * pw / kProd, u1 = NU * (pw + 1) / kProd;
+            // 16-byte units of X: M K / 8 <= 4096 here, so 32-bit indices
+            const int NU = (int)(a.M * (a.K / 8));
+            const int u0 = NU * pw / kProd, u1 = NU * (pw + 1) / kProd;
             const uint32_t KU = (uint32_t)(a.K / 8);
             const uint16_t *xb = static_cast<const uint16_t *>(a.x);
-            auto amax_batch = [&](int64_t base, uint4 *av) {
+            auto amax_batch = [&](int base, uint4 *av) {
 #pragma unroll
                 for (int t = 0; t < kLocalLoads; ++t) {
-                    const int64_t idx = base + lane + 64 * t < u1 ? base + lane + 64 * t : u0;
+                    const int idx = base + lane + 64 * t < u1 ? base + lane + 64 * t : u0;
                     const uint32_t row = (uint32_t)idx / KU, cu = (uint32_t)idx - row * KU;
                     av[t] = *reinterpret_cast<const uint4 *>(xb + (int64_t)row * a.ldx + 8 * (int64_t)cu);
                 }
@@ -478,7 +511,7 @@ void decode_kernel(DArgs a) {
                 } else {
 #pragma unroll
                     for (int t = 0; t < kLocalLoads; ++t) mx = bits_max(mx, av[t]);
-                    for (int64_t base = u0 + 64 * kLocalLoads; base < u1; base += 64 * kLocalLoads) {
+                    for (int base = u0 + 64 * kLocalLoads; base < u1; base += 64 * kLocalLoads) {
                         amax_batch(base, av);
 #pragma unroll
                         for (int t = 0; t < kLocalLoads; ++t) mx = bits_max(mx, av[t]);
@@ -506,10 +539,10 @@ void decode_kernel(DArgs a) {
             if (ptid == 0) sh_S = S;
 #pragma unroll
             for (int t = 0; t < kLocalChunks; ++t) {
-                const int c = ptid + kPThreads * t;
-                if (c < nraw) {
-                    const ChunkPos f = chunk_pos(a, rg, c, slots);
-                    xchunk_quantize<RES>(a, lds_a, slots, kbeg, rg.rend, f.m, f.col, (f.key & kV1) != 0, xc[t], S,
+                const int pos = pm.p0 + pm.step * t;
+                if (pos < rg.npm) {
+                    const ChunkPos f = chunk_at(a, rg, pm.m, pos, slots);
+                    xchunk_quantize<RES>(a, lds_a, slots, kbeg, rg.rend, pm.m, f.col, (f.key & kV1) != 0, xc[t], S,
                                          q == 0);
                 }
             }
@@ -831,8 +864,9 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     // Raw activations are quantized in the kernel only when every workgroup can
     // read all of X and each producer thread holds at most kLocalChunks chunks.
     const int64_t kc = (int64_t)pl.U * 512 < K ? (int64_t)pl.U * 512 : K;
-    const int64_t raw_chunks = M * ((kc + 31) / 32);
-    pl.mode = (raw_x && !norm_or_perm && raw_chunks <= (int64_t)kLocalChunks * kPThreads && M * K <= kLocalMaxElems)
+    const int64_t step = M > 0 ? kPThreads / M : 1;   // chunk positions per pass (prod_map)
+    const int64_t per_thread = ((kc + 31) / 32 + step - 1) / step;
+    pl.mode = (raw_x && !norm_or_perm && per_thread <= kLocalChunks && M * K <= kLocalMaxElems)
                   ? MODE_LOCAL : MODE_PRE;
     if (std::getenv("NVFP4_DEBUG_PLAN"))
         std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d KW=%d T=%d G=%d "
@@ -863,6 +897,7 @@ extern "C" int nvfp4_debug_timeline(void *host, size_t bytes) {
 
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     const bool raw = g.x != nullptr;
+    if (g.M < 1 || g.M > 32 || g.N < 1 || g.K < 1) return hipErrorInvalidValue;   // the kernel's row bound
     const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols, raw, false);
     if (!plan_ok(pl) || (raw && pl.mode != MODE_LOCAL)) return hipErrorInvalidValue;
     if (!g.header || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols) ||
