@@ -85,6 +85,7 @@ struct DArgs {
     int U, P, T, tw, KW, G, mode;
     int Rr;                                   // operand rows per slot group (M, or 2 Mp when stacked)
     int Mp;                                   // stacked residue: residue row of m is Mp + m; else 0
+    int ordered;                              // consumers issue their loads after the producers' (barrier)
     int64_t NT;
 };
 
@@ -213,7 +214,7 @@ __device__ inline ChunkPos chunk_at(const DArgs &a, const Range &r, int m, int p
 
 // A chunk of the quantized-activation buffer: 16 bytes of codes (low nibble =
 // even column) and the two block scales.
-struct QChunk { uint4 c; uint32_t s; int key; };
+struct QChunk { uint4 c; uint16_t s; uint8_t s1; int key; };   // s: both scales (no residue), else the first; s1: the second
 
 // Without residue columns every chunk starts at a multiple of 32 columns: one
 // 16-byte and one 2-byte load. Row-major rows hold at least K/2 bytes of codes
@@ -223,30 +224,33 @@ struct QChunk { uint4 c; uint32_t s; int key; };
 // aligned when K is an odd multiple of 16, so with residue columns every chunk
 // takes two 8-byte and two 1-byte loads, the second of each only inside the
 // data (one code path: a branch on alignment would diverge within a wave).
-// Past the list it reads the row's start.
+// Past the list it reads the row's start (dropped when stored).
 template <bool RES>
 __device__ inline QChunk qchunk_load(const uint8_t *crow, const uint8_t *srow, const ChunkPos &f) {
     QChunk q;
     q.key = f.key;
     if (!RES) {
-        q.c = *reinterpret_cast<const uint4 *>(crow + f.col / 2);
-        q.s = *reinterpret_cast<const uint16_t *>(srow + f.col / 16);
+        q.c = *reinterpret_cast<const uint4 *>(crow + (f.col >> 1));
+        q.s = *reinterpret_cast<const uint16_t *>(srow + (f.col >> 4));
     } else {
         const bool v1 = f.key >= 0 && (f.key & kV1);
-        const uint2 lo = *reinterpret_cast<const uint2 *>(crow + f.col / 2);
-        const uint2 hi = *reinterpret_cast<const uint2 *>(crow + (v1 ? f.col / 2 + 8 : f.col / 2));
+        const uint2 lo = *reinterpret_cast<const uint2 *>(crow + (f.col >> 1));
+        const uint2 hi = *reinterpret_cast<const uint2 *>(crow + (f.col >> 1) + (v1 ? 8 : 0));
         q.c = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        q.s = (uint32_t)srow[f.col / 16] | ((uint32_t)srow[v1 ? f.col / 16 + 1 : f.col / 16] << 8);
+        q.s = srow[f.col >> 4];            // combined only when stored: no wait here
+        q.s1 = srow[(f.col >> 4) + (v1 ? 1 : 0)];
     }
     return q;
 }
 
 // Decode a chunk into its four fragments (j stride js = 4 R slots).
+template <bool RES>
 __device__ inline void qchunk_store(half8 *lds, int js, const QChunk &q) {
     if (q.key < 0) return;
     const bool v1 = q.key & kV1;
     const int slot = q.key & (kV1 - 1);
-    const half2v d0 = scale_pair(q.s & 0xFFu), d1 = scale_pair(v1 ? (q.s >> 8) & 0xFFu : 0u);
+    const uint32_t s0 = RES ? (uint32_t)q.s : q.s & 0xFFu, s1 = RES ? (uint32_t)q.s1 : (uint32_t)q.s >> 8;
+    const half2v d0 = scale_pair(s0), d1 = scale_pair(v1 ? s1 : 0u);
     lds[slot] = decode8(q.c.x, d0);
     lds[slot + js] = decode8(q.c.y, d0);
     lds[slot + 2 * js] = decode8(v1 ? q.c.z : 0u, d1);
@@ -371,7 +375,7 @@ void decode_kernel(DArgs a) {
     // issue of later loads.
     constexpr int kPre = kPreItems < kRing ? kPreItems : kRing;
     extern __shared__ half8 lds_a[];          // operand [U][4 i][4 j][4 g][M] (+ residue copy); then tile sums
-    __shared__ float sh_S;
+    __shared__ float sh_S, sh_wS;             // activation and weight tensor scales
     __shared__ float sh_part[kProd];
     __shared__ unsigned sh_cnt;
     __shared__ int sh_last;
@@ -423,11 +427,14 @@ void decode_kernel(DArgs a) {
     // own branch so that it never shares registers with the consumers' loads in
     // flight.
     TL(0);
-    const float w_scale = load_vmem(a.w_S);
     WLoad ring[kRing];
     if (tid == 0) sh_cnt = 0;
     if (wave < kCons) {
-        __syncthreads();                       // the producers' loads are out
+        // Ordered launches wait until the producers' loads are out, so that the
+        // operand lands ahead of the weight stream (LOCAL always: the barrier
+        // also orders the counter reset above before the producers' arrivals).
+        // Otherwise the producers' few loads race the consumers' first items.
+        if (a.ordered) __syncthreads();
         if (nitems > 0) {
 #pragma unroll
             for (int s = 0; s < kPre; ++s) load_item(s < nitems ? s : nitems - 1, ring[s]);
@@ -439,27 +446,39 @@ void decode_kernel(DArgs a) {
         if (a.mode == MODE_PRE) {
             // the thread's chunk positions of the quantized activations, kPreChunks
             // before the barrier; larger ranges take further batches after it
-            const float S = ptid == 0 ? a.q_S[0] : 0.0f;
             const PMap pm = prod_map(ptid, M);
             const uint8_t *crow = a.q_codes + (int64_t)pm.m * a.q_ldc;
             const uint8_t *srow = a.q_scales + (int64_t)pm.m * a.q_lds;
             const int npos = rg.npm + rg.npr;
-            QChunk qc[kPreChunks];
-#pragma unroll
-            for (int t = 0; t < kPreChunks; ++t)
-                qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * t, slots));
-            __syncthreads();                   // loads out: consumers may issue theirs
-            zero_unwritten(lds_a, a, rg, slots);
-#pragma unroll
-            for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
-            for (int b = kPreChunks; pm.p0 + pm.step * b < npos; b += kPreChunks) {
+            // A wave whose first position (lane 0's) is past the list holds no chunk
+            // and issues nothing; the others issue the whole batch back to back. The
+            // two paths share no values (each meets the barrier itself), so nothing
+            // loaded has to be settled where they join.
+            float S = 0.0f, wS = 0.0f;
+            if (__builtin_amdgcn_readfirstlane(pm.p0) < npos) {
+                QChunk qc[kPreChunks];
 #pragma unroll
                 for (int t = 0; t < kPreChunks; ++t)
-                    qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * (b + t), slots));
+                    qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * t, slots));
+                if (a.ordered) __syncthreads();    // loads out: consumers may issue theirs
+                // the two tensor scales (lane 0 of the first producer wave, which
+                // always holds chunks), after the batch is out
+                if (ptid == 0) { S = load_vmem(a.q_S); wS = load_vmem(a.w_S); }
+                zero_unwritten(lds_a, a, rg, slots);
 #pragma unroll
-                for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
+                for (int t = 0; t < kPreChunks; ++t) qchunk_store<RES>(lds_a, 4 * R, qc[t]);
+                for (int b = kPreChunks; pm.p0 + pm.step * b < npos; b += kPreChunks) {
+#pragma unroll
+                    for (int t = 0; t < kPreChunks; ++t)
+                        qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * (b + t), slots));
+#pragma unroll
+                    for (int t = 0; t < kPreChunks; ++t) qchunk_store<RES>(lds_a, 4 * R, qc[t]);
+                }
+            } else {
+                if (a.ordered) __syncthreads();
+                zero_unwritten(lds_a, a, rg, slots);
             }
-            if (ptid == 0) sh_S = S;
+            if (ptid == 0) { sh_S = S; sh_wS = wS; }
             TL(1);
             __syncthreads();                   // operand complete
         } else {
@@ -470,13 +489,22 @@ void decode_kernel(DArgs a) {
             // kLocalLoads loads per lane (the first before the barrier).
             const PMap pm = prod_map(ptid, M);
             const bool full = a.P == 1;
+            // chunk slots of this wave that hold a chunk for some lane (wave-uniform);
+            // a lane past its list in such a slot reads its row's start, which leaves
+            // amax(X) unchanged; empty slots issue no loads and stay zero
+            const int p0w = __builtin_amdgcn_readfirstlane(pm.p0);
+            const int nt = p0w < rg.npm ? (rg.npm - p0w + pm.step - 1) / pm.step : 0;
             XChunk xc[kLocalChunks];
 #pragma unroll
             for (int t = 0; t < kLocalChunks; ++t) {
-                const int pos = pm.p0 + pm.step * t;
-                const ChunkPos f = chunk_at(a, rg, pm.m, pos < rg.npm ? pos : 1 << 20, slots);
-                xc[t] = xchunk_load(a, pm.m, f.col, f.key >= 0 && (f.key & kV1));   // past the list: the row's start
+                xc[t] = XChunk{};
+                if (t < nt) {
+                    const int pos = pm.p0 + pm.step * t;
+                    const ChunkPos f = chunk_at(a, rg, pm.m, pos < rg.npm ? pos : 1 << 20, slots);
+                    xc[t] = xchunk_load(a, pm.m, f.col, f.key >= 0 && (f.key & kV1));
+                }
             }
+            const float wS = ptid == 0 ? load_vmem(a.w_S) : 0.0f;   // behind the chunk loads
             // 16-byte units of X: M K / 8 <= 4096 here, so 32-bit indices
             const int NU = (int)(a.M * (a.K / 8));
             const int u0 = NU * pw / kProd, u1 = NU * (pw + 1) / kProd;
@@ -536,7 +564,7 @@ void decode_kernel(DArgs a) {
                 S = scale_of(m);
             }
             if (blockIdx.x == 0 && ptid == 0) *a.q_S = S;
-            if (ptid == 0) sh_S = S;
+            if (ptid == 0) { sh_S = S; sh_wS = wS; }
 #pragma unroll
             for (int t = 0; t < kLocalChunks; ++t) {
                 const int pos = pm.p0 + pm.step * t;
@@ -553,7 +581,7 @@ void decode_kernel(DArgs a) {
     TL(2);
 
     // ---- consumers: decode weights, MFMA
-    const float scale = sh_S * w_scale;
+    const float scale = sh_S * sh_wS;
     // Output tile t of this workgroup: lane holds rows 16 mt + 4 g + e of column
     // 16 t + r16; only rows < M are stored.
     auto store_tile = [&](int64_t t, const float4v *vin) {
@@ -765,7 +793,7 @@ void decode_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------- planning
-struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool refill; int64_t NT, Q; size_t lds; };
+struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool refill, ordered; int64_t NT, Q; size_t lds; };
 
 constexpr size_t kLdsPerCu = 160 * 1024;       // gfx950
 constexpr size_t kLdsStatic = 256;             // the kernel's own __shared__ words, rounded up
@@ -868,10 +896,15 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     const int64_t per_thread = ((kc + 31) / 32 + step - 1) / step;
     pl.mode = (raw_x && !norm_or_perm && per_thread <= kLocalChunks && M * K <= kLocalMaxElems)
                   ? MODE_LOCAL : MODE_PRE;
+    // PRE producers with more than two chunks per thread put enough loads in
+    // the CU's queue that the operand lands late behind the consumers' first
+    // items; then the consumers wait for them (measured crossover: two chunks).
+    const int64_t pre_per_thread = (((kc + 31) / 32) * (res_cols > 0 ? 2 : 1) + step - 1) / step;
+    pl.ordered = pl.mode == MODE_LOCAL || pre_per_thread > 2;
     if (std::getenv("NVFP4_DEBUG_PLAN"))
         std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d KW=%d T=%d G=%d "
-                     "lds=%zu refill=%d mode=%d cost=%.2f\n", (long long)M, (long long)N, (long long)K,
-                     (long long)res_cols, pl.MT, pl.U, pl.P, pl.KW, pl.T, pl.G, pl.lds, (int)pl.refill, pl.mode, best);
+                     "lds=%zu refill=%d mode=%d ordered=%d cost=%.2f\n", (long long)M, (long long)N, (long long)K,
+                     (long long)res_cols, pl.MT, pl.U, pl.P, pl.KW, pl.T, pl.G, pl.lds, (int)pl.refill, pl.mode, (int)pl.ordered, best);
     return pl;
 }
 
@@ -912,7 +945,7 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.header = reinterpret_cast<uint8_t *>(g.header);
     a.partials = static_cast<float *>(g.scratch);
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.KW = pl.KW; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
-    a.Rr = pl.Rr; a.Mp = pl.Mp;
+    a.Rr = pl.Rr; a.Mp = pl.Mp; a.ordered = pl.ordered ? 1 : 0;
     const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill);
     if (pl.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
