@@ -829,8 +829,9 @@ const void *kernel_ptr(int MT, bool res, bool tiled, bool refill) {
 // waves share each tile (TW = 4 / KW tiles at a time, ntw per wave). The
 // estimate charges each item (16 rows x 512 columns of W) its streaming time
 // on the busiest CU -- a CU streams ~0.23 us per item with its loads in flight
-// -- plus ~1.5 us for a split-K combine, which costs three dependent
-// round trips through the memory system.
+// -- plus ~2 us for each further round of workgroups (a workgroup's start-up:
+// arguments, operand, first items), plus ~1.5 us for a split-K combine, which
+// costs three dependent round trips through the memory system.
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
     Plan pl;
     pl.MT = M <= 16 ? 1 : 2;
@@ -862,7 +863,8 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
                 const int per_cu = lds + kLdsStatic <= kLdsPerCu / 2 ? 2 : (lds + kLdsStatic <= kLdsPerCu ? 1 : 0);
                 if (per_cu == 0 || Q > kMaxTileCounters) continue;   // more than one round is allowed
                 const double items_wg = (double)T * (double)U;
-                const double cost = 0.23 * items_wg * (double)((G + ncu - 1) / ncu) +
+                const int64_t rounds = (G + ncu - 1) / ncu;
+                const double cost = 0.23 * items_wg * (double)rounds + 2.0 * (double)(rounds - 1) +
                                     (P > 1 ? 1.5 + 0.1 * (double)P : 0.0) + (KW > 1 ? 0.1 : 0.0);
                 if (cost < best) { best = cost; bU = (int)U; bKW = KW; bntw = ntw; found = true; }
             }
@@ -871,7 +873,8 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     if (const char *e = std::getenv("NVFP4_DECODE_FORCE")) {         // tuning override "U,KW,ntw"
         int fu = 0, fk = 0, ft = 0;
         if (std::sscanf(e, "%d,%d,%d", &fu, &fk, &ft) == 3 && fu >= 1 && (fk == 1 || fk == 2 || fk == 4) &&
-            ft >= 1 && ft * ((fu + fk - 1) / fk) <= kMaxItems && (fk == 1 || ft <= 2)) {
+            ft >= 1 && ft * ((fu + fk - 1) / fk) <= kMaxItems && (fk == 1 || ft <= 2) &&
+            (size_t)fu * 1024 * (size_t)op_rows + kLdsStatic <= kLdsPerCu) {
             bU = fu; bKW = fk; bntw = ft; found = true;
         }
     }
@@ -896,11 +899,12 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     const int64_t per_thread = ((kc + 31) / 32 + step - 1) / step;
     pl.mode = (raw_x && !norm_or_perm && per_thread <= kLocalChunks && M * K <= kLocalMaxElems)
                   ? MODE_LOCAL : MODE_PRE;
-    // PRE producers with more than two chunks per thread put enough loads in
-    // the CU's queue that the operand lands late behind the consumers' first
-    // items; then the consumers wait for them (measured crossover: two chunks).
+    // PRE producers with more than one chunk per thread put enough loads in the
+    // CU's queue that the operand lands late behind the consumers' first items;
+    // then the consumers wait for them (measured: ordering wins from two chunks
+    // per thread on, racing wins at one).
     const int64_t pre_per_thread = (((kc + 31) / 32) * (res_cols > 0 ? 2 : 1) + step - 1) / step;
-    pl.ordered = pl.mode == MODE_LOCAL || pre_per_thread > 2;
+    pl.ordered = pl.mode == MODE_LOCAL || pre_per_thread > 1;
     if (std::getenv("NVFP4_DEBUG_PLAN"))
         std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d KW=%d T=%d G=%d "
                      "lds=%zu refill=%d mode=%d ordered=%d cost=%.2f\n", (long long)M, (long long)N, (long long)K,
