@@ -15,6 +15,8 @@
 // Tile: BM x BN output per workgroup of 4 waves (2 x 2), BK = 64 per step,
 // LDS double-buffered; tiles are stored in MFMA operand order (each operand
 // fetch is 1 KB contiguous per wave).
+#include <type_traits>
+
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -225,6 +227,199 @@ __global__ __launch_bounds__(256) void tiled_kernel(TArgs a) {
     }
 }
 
+// Chunk loads for the large-tile product: the scale pair is one 2-byte load
+// (k is a multiple of 32, so the pair is 2-byte aligned in both layouts).
+__device__ inline RowChunk load_chunk2(const uint8_t *codes, int64_t ldc, const uint8_t *scales, int64_t lds,
+                                       int64_t row, int64_t nrows, int64_t k, int64_t kend) {
+    RowChunk rc;
+    rc.c = make_uint4(0, 0, 0, 0);
+    rc.s = 0;
+    if (row < nrows) {
+        const uint8_t *cp = codes + row * ldc + k / 2;
+        const uint8_t *sp = scales + row * lds + k / 16;
+        if (k + 32 <= kend) {
+            rc.c = *reinterpret_cast<const uint4 *>(cp);
+            rc.s = *reinterpret_cast<const uint16_t *>(sp);
+        } else if (k + 16 <= kend) {
+            const uint2 h = *reinterpret_cast<const uint2 *>(cp);
+            rc.c.x = h.x; rc.c.y = h.y;
+            rc.s = sp[0];
+        }
+    }
+    return rc;
+}
+
+__device__ inline RowChunk load_chunk2_tiled(const uint8_t *codes, int64_t ldc, const uint8_t *scales, int64_t lds,
+                                             int64_t row, int64_t nrows, int64_t k, int64_t kend) {
+    RowChunk rc;
+    rc.c = make_uint4(0, 0, 0, 0);
+    rc.s = 0;
+    if (row < nrows && k < kend) {                // tiled padding is zero: no half-chunk case
+        const int64_t t = row >> 4, u = k >> 9;
+        const int lane = (int)(16 * ((k >> 7) & 3) + (row & 15)), i = (int)((k >> 5) & 3);
+        rc.c = *reinterpret_cast<const uint4 *>(codes + t * ldc + u * 4096 + 1024 * i + 16 * lane);
+        rc.s = *reinterpret_cast<const uint16_t *>(scales + t * lds + u * 512 + 8 * lane + 2 * i);
+    }
+    return rc;
+}
+
+// Large tiles (no residue columns): BM x 256 per workgroup of NW waves (2
+// along M x NW/2 along N), each wave a BM/2 x 512/NW block of 16 x 16 tiles,
+// so every fragment read from LDS feeds 4 to 8 MFMAs (against 4 for the 64 x 64
+// wave tile above). BM = 256 runs 8 waves (two per SIMD, 128 accumulator
+// registers each); BM = 128 runs 4. Two LDS stages; within a wave the stages
+// overlap as a software pipeline, in source order:
+//  * a 2-deep register queue: the global loads of step s + 2 go out at the
+//    start of step s and are decoded during step s + 1;
+//  * the decode and LDS stores of step s + 1 (into the other stage) are spread
+//    over the MFMA groups of step s;
+//  * A fragments are read from LDS four MFMA groups ahead, the second
+//    k-chunk's B fragments during the last groups of the first.
+template <int BM, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void tiled2_kernel(TArgs a) {
+    constexpr int BN = 256, NT = 64 * NW;                    // threads
+    constexpr int RT = BM / 16, CT = BN / 16;
+    constexpr int A_SLOTS = RT * 2 * 64, B_SLOTS = CT * 2 * 64;
+    constexpr int STAGE = A_SLOTS + B_SLOTS;
+    constexpr int WN = NW / 2;                               // waves: 2 along M x WN along N
+    constexpr int WRT = RT / 2, WCT = CT / WN;
+    constexpr int A_ITERS = BM * 2 / NT, B_ITERS = BN * 2 / NT, NCH = A_ITERS + B_ITERS;
+    static_assert(A_ITERS * NT == BM * 2 && B_ITERS * NT == BN * 2, "whole chunks per thread");
+    constexpr int NG = 2 * WRT, NU = 4 * NCH;                // MFMA groups and decode units per step
+    extern __shared__ half8 lds[];                           // [2][STAGE]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int nblk = a.tiles_m * a.tiles_n;
+    int bid = blockIdx.x;
+    if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+    const int tn = bid / a.tiles_m, tm = bid % a.tiles_m;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t ksteps = (a.K + BK - 1) / BK;
+
+    // chunk c of this thread: A chunks (c < A_ITERS), then B chunks; (row, half) of the tile
+    auto crow = [&](int c) { return ((tid + NT * (c < A_ITERS ? c : c - A_ITERS)) >> 1); };
+    auto chalf = [&](int c) { return (tid + NT * (c < A_ITERS ? c : c - A_ITERS)) & 1; };
+    auto cslot = [&](int c) {
+        const int r = crow(c), h = chalf(c);
+        return (c < A_ITERS ? 0 : A_SLOTS) + ((r >> 4) * 2 + h) * 64 + (r & 15);
+    };
+    RowChunk rq0[NCH], rq1[NCH];
+    auto gload = [&](int64_t s, RowChunk *q) {
+        const int64_t k = s * BK;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int r = crow(c), h = chalf(c);
+            if (c < A_ITERS)
+                q[c] = load_chunk2(a.a_codes, a.a_ldc, a.a_scales, a.a_lds, m0 + r, a.M, k + 32 * h, a.K);
+            else
+                q[c] = a.w_tiled ? load_chunk2_tiled(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K)
+                                 : load_chunk2(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K);
+        }
+    };
+    // decode unit u = fragment (u & 3) of chunk (u >> 2) into stage st
+    auto unit = [&](half8 *st, const RowChunk *q, int u) {
+        const int c = u >> 2, f = u & 3;
+        const uint32_t sb = f < 2 ? (q[c].s & 0xFFu) : ((q[c].s >> 8) & 0xFFu);
+        const uint32_t w = f == 0 ? q[c].c.x : f == 1 ? q[c].c.y : f == 2 ? q[c].c.z : q[c].c.w;
+        st[cslot(c) + 16 * f] = decode8(w, scale_pair(sb));
+    };
+
+    float4v acc[WRT][WCT];
+#pragma unroll
+    for (int i = 0; i < WRT; ++i)
+#pragma unroll
+        for (int j = 0; j < WCT; ++j) acc[i][j] = float4v{0, 0, 0, 0};
+
+    gload(0, rq0);
+    if (ksteps > 1) gload(1, rq1);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) unit(lds, rq0, u);
+    __syncthreads();
+
+    // step s (parity P): MFMAs on stage P; decode the queue entry of step s + 1
+    // (rq[P ^ 1]) into stage P ^ 1; load step s + 2 into rq[P]
+    auto step = [&](int64_t s, auto parity) {
+        constexpr int P = decltype(parity)::value;
+        RowChunk *qload = P == 0 ? rq0 : rq1;
+        const RowChunk *qdec = P == 0 ? rq1 : rq0;
+        const half8 *cur = lds + P * STAGE;
+        half8 *nxt = lds + (P ^ 1) * STAGE;
+        const bool dec = s + 1 < ksteps;
+        if (s + 2 < ksteps) gload(s + 2, qload);
+        // A fragments of the step's groups, read kPD groups ahead; B fragments of
+        // the second k-chunk read during the last groups of the first
+        constexpr int kPD = 4;
+        auto aslot = [&](int gi) { return ((wm * WRT + gi % WRT) * 2 + gi / WRT) * 64 + lane; };
+        half8 afr[NG];
+        half8 bf[WCT], bn[WCT];
+#pragma unroll
+        for (int j = 0; j < WCT; ++j) bf[j] = cur[A_SLOTS + ((wn * WCT + j) * 2 + 0) * 64 + lane];
+#pragma unroll
+        for (int gi = 0; gi < kPD && gi < NG; ++gi) afr[gi] = cur[aslot(gi)];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int kc = gi / WRT, i = gi % WRT;
+            if (gi + kPD < NG) afr[gi + kPD] = cur[aslot(gi + kPD)];
+            if (kc == 0 && i == (WRT > 2 ? WRT - 2 : 0)) {
+#pragma unroll
+                for (int j = 0; j < WCT; ++j) bn[j] = cur[A_SLOTS + ((wn * WCT + j) * 2 + 1) * 64 + lane];
+            }
+#pragma unroll
+            for (int j = 0; j < WCT; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afr[gi], kc == 0 ? bf[j] : bn[j], acc[i][j], 0, 0, 0);
+            if (dec) {
+#pragma unroll
+                for (int u = gi * NU / NG; u < (gi + 1) * NU / NG; ++u) unit(nxt, qdec, u);
+            }
+        }
+        __syncthreads();
+    };
+    for (int64_t s = 0; s < ksteps; s += 2) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < ksteps) step(s + 1, std::integral_constant<int, 1>{});
+    }
+
+    const float scale = a.a_S[0] * a.w_S[0];
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < WRT; ++i) {
+#pragma unroll
+        for (int j = 0; j < WCT; ++j) {
+            const int64_t n = n0 + (wn * WCT + j) * 16 + c16;
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + (wm * WRT + i) * 16 + 4 * g + e;
+                if (m < a.M) {
+                    const float v = acc[i][j][e] * scale;
+                    if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = v;
+                    else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f2bf(v);
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int NW>
+hipError_t run2(const TArgs &a0, hipStream_t st) {
+    TArgs a = a0;
+    a.tiles_m = (int)((a.M + BM - 1) / BM);
+    a.tiles_n = (int)((a.N + 255) / 256);
+    constexpr int STAGE = (BM / 16) * 2 * 64 + 16 * 2 * 64;
+    const size_t lds = 2 * (size_t)STAGE * sizeof(half8);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled2_kernel<BM, NW>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    tiled2_kernel<BM, NW><<<a.tiles_m * a.tiles_n, 64 * NW, lds, st>>>(a);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, bool RES>
 hipError_t run(const TArgs &a0, hipStream_t st) {
     TArgs a = a0;
@@ -259,6 +454,10 @@ hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st) {
         return run<128, 128, true>(a, st);
     }
     if (g.M <= 64) return run<64, 128, false>(a, st);
+    // large tiles when they still give the chip a workgroup per CU or more
+    const int64_t tn = (g.N + 255) / 256;
+    if (((g.M + 255) / 256) * tn >= 192) return run2<256, 8>(a, st);
+    if (((g.M + 127) / 128) * tn >= 192) return run2<128, 4>(a, st);
     return run<128, 128, false>(a, st);
 }
 

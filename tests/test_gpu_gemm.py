@@ -270,3 +270,31 @@ def test_in_launch_quantization_shapes(nv, orc, M, N, K):
     ref = orc.gemm(orc.quantize(x), orc.quantize(w))
     err = gemm_error(y.cpu().numpy(), ref)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M,N,K", [(700, 16400, 1040), (300, 16400, 1040), (520, 12304, 2064)])
+def test_prefill_large_tiles_ragged(nv, orc, M, N, K):
+    """Shapes that take the large-tile product (BM x 256 tiles, chosen when they
+    still give one workgroup per CU): ragged M, N, and a K ending in a half
+    chunk. Sampled outputs against the oracle; row-major and tiled weights
+    give identical bits."""
+    x = inputs.small_random(800 + M, M, K)
+    w = inputs.small_random(801 + N, N, K, scale=0.02)
+    note(f"large-tile prefill M={M} N={N} K={K}")
+    xd = x.to(DEV)
+    wq = nv.quantize(w.to(DEV))
+    wt = nv.pack_tiled(wq)
+    y = nv.gemm(xd, wq)
+    yt = nv.gemm(xd, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yt)
+    rng = np.random.default_rng(M + N)
+    ms = np.concatenate([rng.integers(0, M, 1500), [M - 1, M - 1, 0]])
+    ns = np.concatenate([rng.integers(0, N, 1500), [N - 1, 0, N - 1]])
+    xq = orc.quantize(x)
+    rows = np.unique(ns)
+    wsub = orc.quantize(w[rows], static_S=float(orc.tensor_scale(w)))
+    wpos = {r: i for i, r in enumerate(rows)}
+    ref = orc.gemm_pairs(xq, wsub, ms, np.array([wpos[n] for n in ns]))
+    err = gemm_error(y.cpu().numpy()[ms, ns], ref)
+    assert err <= TOL, err
