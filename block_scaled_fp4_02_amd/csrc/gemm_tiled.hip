@@ -263,22 +263,23 @@ __device__ inline RowChunk load_chunk2_tiled(const uint8_t *codes, int64_t ldc, 
     return rc;
 }
 
-// Large tiles (no residue columns): BM x 256 per workgroup of NW waves (2
-// along M x NW/2 along N), each wave a BM/2 x 512/NW block of 16 x 16 tiles,
-// so every fragment read from LDS feeds 4 to 8 MFMAs (against 4 for the 64 x 64
-// wave tile above). BM = 256 runs 8 waves (two per SIMD, 128 accumulator
-// registers each); BM = 128 runs 4. Two LDS stages; within a wave the stages
-// overlap as a software pipeline, in source order:
+// Large tiles (no residue columns): BM x BN per workgroup of NW waves (2 along
+// M x NW/2 along N), each wave a BM/2 x 2 BN/NW block of 16 x 16 tiles, so
+// every fragment read from LDS feeds 4 to 8 MFMAs (against 4 for the 64 x 64
+// wave tile above). 256 x 256 runs 8 waves (two per SIMD, 128 accumulator
+// registers each), 128 x 256 runs 4, 128 x 128 runs 4 with two workgroups per
+// CU. Two LDS stages; within a wave the stages overlap as a software
+// pipeline, in source order:
 //  * a 2-deep register queue: the global loads of step s + 2 go out at the
 //    start of step s and are decoded during step s + 1;
 //  * the decode and LDS stores of step s + 1 (into the other stage) are spread
 //    over the MFMA groups of step s;
 //  * A fragments are read from LDS four MFMA groups ahead, the second
 //    k-chunk's B fragments during the last groups of the first.
-template <int BM, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+template <int BM, int BN, int NW, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void tiled2_kernel(TArgs a) {
-    constexpr int BN = 256, NT = 64 * NW;                    // threads
+    constexpr int NT = 64 * NW;                              // threads
     constexpr int RT = BM / 16, CT = BN / 16;
     constexpr int A_SLOTS = RT * 2 * 64, B_SLOTS = CT * 2 * 64;
     constexpr int STAGE = A_SLOTS + B_SLOTS;
@@ -402,21 +403,21 @@ void tiled2_kernel(TArgs a) {
     }
 }
 
-template <int BM, int NW>
+template <int BM, int BN, int NW, int WPE>
 hipError_t run2(const TArgs &a0, hipStream_t st) {
     TArgs a = a0;
     a.tiles_m = (int)((a.M + BM - 1) / BM);
-    a.tiles_n = (int)((a.N + 255) / 256);
-    constexpr int STAGE = (BM / 16) * 2 * 64 + 16 * 2 * 64;
+    a.tiles_n = (int)((a.N + BN - 1) / BN);
+    constexpr int STAGE = (BM / 16) * 2 * 64 + (BN / 16) * 2 * 64;
     const size_t lds = 2 * (size_t)STAGE * sizeof(half8);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled2_kernel<BM, NW>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tiled2_kernel<BM, BN, NW, WPE>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    tiled2_kernel<BM, NW><<<a.tiles_m * a.tiles_n, 64 * NW, lds, st>>>(a);
+    tiled2_kernel<BM, BN, NW, WPE><<<a.tiles_m * a.tiles_n, 64 * NW, lds, st>>>(a);
     return hipGetLastError();
 }
 
@@ -456,9 +457,9 @@ hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st) {
     if (g.M <= 64) return run<64, 128, false>(a, st);
     // large tiles when they still give the chip a workgroup per CU or more
     const int64_t tn = (g.N + 255) / 256;
-    if (((g.M + 255) / 256) * tn >= 192) return run2<256, 8>(a, st);
-    if (((g.M + 127) / 128) * tn >= 192) return run2<128, 4>(a, st);
-    return run<128, 128, false>(a, st);
+    if (((g.M + 255) / 256) * tn >= 192) return run2<256, 256, 8, 2>(a, st);
+    if (((g.M + 127) / 128) * tn >= 192) return run2<128, 256, 4, 1>(a, st);
+    return run2<128, 128, 4, 2>(a, st);             // 128 x 128 tiles, two workgroups per CU
 }
 
 }  // namespace nvfp4
