@@ -32,7 +32,11 @@ inline size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // The skinny (decode) path takes M up to this many rows; larger M is tiled.
-constexpr int64_t kSkinnyMaxM = 32;
+constexpr int64_t kSkinnyMaxM = 64;
+// The decode product takes M <= 32, and M <= 64 without residue columns: with
+// them, four row tiles need a second operand copy that halves the K range a
+// workgroup holds, and the tiled product is faster there.
+inline bool skinny_rows(int64_t M, int64_t K, int64_t S) { return K > 0 && (M <= 32 || (M <= kSkinnyMaxM && S == 0)); }
 
 int64_t ldc_for(int64_t K) { return (int64_t)up((size_t)(K / 2), 16); }
 int64_t lds_for(int64_t K) { return (int64_t)up((size_t)(K / 16), 8); }
@@ -46,7 +50,7 @@ size_t tensor_ws(int64_t rows, int64_t K) {
 }
 
 size_t gemm_ws(int64_t M, int64_t N, int64_t K, int64_t S) {
-    if (M <= kSkinnyMaxM && K > 0) return up(decode_workspace_bytes(M, N, K, S), kAlign);
+    if (skinny_rows(M, K, S)) return up(decode_workspace_bytes(M, N, K, S), kAlign);
     return 0;
 }
 
@@ -142,7 +146,7 @@ nvfp4_status enqueue_gemm(const nvfp4_tensor &a, const nvfp4_tensor &w, int64_t 
                           void *y, int yt, int64_t ldy, unsigned *header, uint8_t *scratch, size_t scratch_bytes,
                           hipStream_t st) {
     hipError_t e;
-    if (M <= kSkinnyMaxM && K > 0) {
+    if (skinny_rows(M, K, S)) {
         DecodeLaunch g{};
         g.x = nullptr;
         g.q_codes = a.codes; g.q_ldc = a.ld_codes; g.q_scales = a.scales; g.q_lds = a.ld_scales; g.q_S = a.tensor_scale;
@@ -248,7 +252,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
     const size_t sb = gemm_ws(M, N, K, 0);
     uint8_t *scratch = sb ? c.take(sb) : nullptr;
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
-    const bool skinny = M <= kSkinnyMaxM && K > 0;
+    const bool skinny = skinny_rows(M, K, 0);
     if (!a_q && skinny && decode_can_fuse(M, N, K, 0, xt == NVFP4_BF16))
         return enqueue_fused(x, xt, ldx, nullptr, aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
     if (!a_q) CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, header, st));
@@ -291,7 +295,7 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
     uint8_t *scratch = sb ? c.take(sb) : nullptr;
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
     const bool plain = !opts || (!opts->gamma && !opts->perm);
-    const bool skinny = M <= kSkinnyMaxM && K > 0;
+    const bool skinny = skinny_rows(M, K, S);
     if (N > 0 && plain && skinny && decode_can_fuse(M, N, K, S, xt == NVFP4_BF16))
         return enqueue_fused(x, xt, ldx, opts ? opts->static_tensor_scale : nullptr, aq, *w, M, K, S, y, yt, ldy,
                              header, scratch, sb, st);

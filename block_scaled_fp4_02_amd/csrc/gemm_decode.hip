@@ -1,4 +1,4 @@
-// gemm_decode.hip -- decode-shaped W4A4 product (M <= 32) in one launch, gfx950.
+// gemm_decode.hip -- decode-shaped W4A4 product (M <= 64) in one launch, gfx950.
 //
 // y[m][n] = S_a S_w sum_k e(a)d(a) e(w)d(w)            (ARCQuant article, section 3.1)
 // plus the residue columns of the augmented-K product (ARCQuant sections
@@ -48,6 +48,7 @@ constexpr int kProd = 4;                       // producer waves: the activation
 constexpr int kThreads = 64 * (kCons + kProd);
 constexpr int kPThreads = 64 * kProd;
 constexpr int kMaxItems = 8;                   // (tile, unit) items per consumer wave
+__host__ __device__ constexpr int max_items(int MT) { return MT == 4 ? 4 : kMaxItems; }   // registers
 constexpr int kPreItems = 2;                   // items each consumer issues before the operand barrier
 constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
 constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
@@ -369,7 +370,7 @@ __device__ inline void zero_unwritten(half8 *lds, const DArgs &a, const Range &r
 template <int MT, bool RES, bool TILED, bool REFILL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
-    constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
+    constexpr int kRing = MT == 1 ? 4 : (MT == 2 ? 3 : 2);   // weight items in flight per consumer wave
     // Items issued before the operand barrier; the rest of the ring is issued
     // after it, so that computing on landed items overlaps the (throttled)
     // issue of later loads.
@@ -403,7 +404,7 @@ void decode_kernel(DArgs a) {
     // Consumer wave w takes tiles t_lo + w / KW + TW i_t (i_t < ntw) and units
     // w % KW + KW i_u (i_u < nuw) of the range: KW waves share each tile, each
     // summing its own units, and their parts are added in LDS at the end.
-    const int KW = a.KW, TW = kCons / KW;
+    const int KW = MT == 4 ? 1 : a.KW, TW = kCons / KW;   // four row tiles: the plan keeps KW = 1
     const int tg = wave / KW, uo = wave % KW;
     const int ntw = (wave < kCons && t_lo + tg < t_hi) ? (int)((t_hi - t_lo - tg + TW - 1) / TW) : 0;
     const int nuw = (wave < kCons && uo < units) ? (units - uo + KW - 1) / KW : 0;
@@ -642,7 +643,7 @@ void decode_kernel(DArgs a) {
         // Fully unrolled over NI items (no loop back-edge), NI = kRing when the
         // plan's items per wave fit the ring (no refills at all; a kernel of its
         // own, so the two loop shapes never share a register allocation) and
-        // kMaxItems otherwise: each slot is consumed in place and refilled right
+        // max_items(MT) otherwise: each slot is consumed in place and refilled right
         // after, always with the same five loads (past the last item -- only in
         // ragged waves -- it re-reads the current one), so vmcnt is tracked
         // exactly and the common plans issue no redundant loads.
@@ -668,7 +669,7 @@ void decode_kernel(DArgs a) {
                             const int fo = (4 * i + j) * 4 * R;
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) {
-                                float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
+                                float4v &ac = (MT < 4 && (j & 1)) ? acc2[mt] : acc[mt];   // four row tiles: one chain each
                                 ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt]], b, ac, 0, 0, 0);
                                 if (RES && res_u) {
                                     float4v &ar = kSepRes ? ((j & 1) ? accr2[0] : accr[0]) : ac;
@@ -713,7 +714,7 @@ void decode_kernel(DArgs a) {
                 }
             }
         };
-        run(std::integral_constant<int, REFILL ? kMaxItems : kRing>{});
+        run(std::integral_constant<int, REFILL ? max_items(MT) : kRing>{});
     }
 
     // ---- tiles shared by KW waves: their parts are added in LDS, in wave order
@@ -815,8 +816,10 @@ template <bool TILED, bool REFILL>
 const void *kernel_ptr_t(int MT, bool res) {
     if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL>)
                             : reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, REFILL>);
-    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL>)
-               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL>);
+    if (MT == 2) return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL>)
+                            : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL>);
+    return res ? reinterpret_cast<const void *>(&decode_kernel<4, true, TILED, REFILL>)
+               : reinterpret_cast<const void *>(&decode_kernel<4, false, TILED, REFILL>);
 }
 
 const void *kernel_ptr(int MT, bool res, bool tiled, bool refill) {
@@ -834,9 +837,9 @@ const void *kernel_ptr(int MT, bool res, bool tiled, bool refill) {
 // costs three dependent round trips through the memory system.
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
     Plan pl;
-    pl.MT = M <= 16 ? 1 : 2;
+    pl.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     const bool res = res_cols > 0;
-    const int ring = pl.MT == 1 ? 4 : 3;
+    const int ring = pl.MT == 1 ? 4 : (pl.MT == 2 ? 3 : 2);
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
     const int ncu = cu_count();
@@ -852,19 +855,20 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
         const int64_t U = (ku + P0 - 1) / P0, P = (ku + U - 1) / U;
         if (P != P0) continue;                 // each split once
         const size_t lds_a = (size_t)U * 1024 * (size_t)op_rows;
-        for (int KW = 1; KW <= kCons; KW *= 2) {
+        for (int KW = 1; KW <= (pl.MT == 4 ? 1 : kCons); KW *= 2) {   // four row tiles: KW = 1 only
             const int TW = kCons / KW;
             const int64_t nuw = (U + KW - 1) / KW;
-            for (int ntw = 1; ntw <= kMaxItems; ++ntw) {
-                if (ntw * nuw > kMaxItems || (KW > 1 && ntw > 2)) break;
+            for (int ntw = 1; ntw <= max_items(pl.MT); ++ntw) {
+                if (ntw * nuw > max_items(pl.MT) || (KW > 1 && ntw > 2)) break;
                 const int64_t T = (int64_t)TW * ntw, Q = (pl.NT + T - 1) / T, G = P * Q;
                 size_t lds = lds_a > (KW > 1 ? (size_t)8192 * pl.MT : 0) ? lds_a : (size_t)8192 * pl.MT;
                 lds = (lds + 255) / 256 * 256;
                 const int per_cu = lds + kLdsStatic <= kLdsPerCu / 2 ? 2 : (lds + kLdsStatic <= kLdsPerCu ? 1 : 0);
                 if (per_cu == 0 || Q > kMaxTileCounters) continue;   // more than one round is allowed
                 const double items_wg = (double)T * (double)U;
-                const int64_t rounds = (G + ncu - 1) / ncu;
-                const double cost = 0.23 * items_wg * (double)rounds + 2.0 * (double)(rounds - 1) +
+                // work of the busiest CU, and rounds of workgroups (per_cu of them fit a CU at once)
+                const int64_t per_cu_wgs = (G + ncu - 1) / ncu, rounds = (G + ncu * per_cu - 1) / (ncu * per_cu);
+                const double cost = 0.23 * items_wg * (double)per_cu_wgs + 2.0 * (double)(rounds - 1) +
                                     (P > 1 ? 1.5 + 0.1 * (double)P : 0.0) + (KW > 1 ? 0.1 : 0.0);
                 if (cost < best) { best = cost; bU = (int)U; bKW = KW; bntw = ntw; found = true; }
             }
@@ -873,7 +877,7 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     if (const char *e = std::getenv("NVFP4_DECODE_FORCE")) {         // tuning override "U,KW,ntw"
         int fu = 0, fk = 0, ft = 0;
         if (std::sscanf(e, "%d,%d,%d", &fu, &fk, &ft) == 3 && fu >= 1 && (fk == 1 || fk == 2 || fk == 4) &&
-            ft >= 1 && ft * ((fu + fk - 1) / fk) <= kMaxItems && (fk == 1 || ft <= 2) &&
+            ft >= 1 && ft * ((fu + fk - 1) / fk) <= max_items(pl.MT) && (fk == 1 || ft <= 2) && (pl.MT < 4 || fk == 1) &&
             (size_t)fu * 1024 * (size_t)op_rows + kLdsStatic <= kLdsPerCu) {
             bU = fu; bKW = fk; bntw = ft; found = true;
         }
@@ -934,7 +938,7 @@ extern "C" int nvfp4_debug_timeline(void *host, size_t bytes) {
 
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     const bool raw = g.x != nullptr;
-    if (g.M < 1 || g.M > 32 || g.N < 1 || g.K < 1) return hipErrorInvalidValue;   // the kernel's row bound
+    if (g.M < 1 || g.M > 64 || g.N < 1 || g.K < 1) return hipErrorInvalidValue;   // the kernel's row bound
     const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols, raw, false);
     if (!plan_ok(pl) || (raw && pl.mode != MODE_LOCAL)) return hipErrorInvalidValue;
     if (!g.header || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols) ||

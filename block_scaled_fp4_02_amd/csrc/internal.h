@@ -45,7 +45,7 @@ hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 // advances), so it never needs clearing again.
 constexpr size_t kHeaderBytes = 8192;
 
-// Decode-shaped (M <= 32) product in one launch. With x != nullptr (bf16, and
+// Decode-shaped (M <= 64) product in one launch. With x != nullptr (bf16, and
 // decode_can_fuse true) the raw activations are quantized inside the kernel and
 // also stored into q_* (canonical NVFP4 layout, K + res_cols columns: the
 // residue of columns [0, res_cols) after column K); with x == nullptr q_*
