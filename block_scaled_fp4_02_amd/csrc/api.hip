@@ -33,10 +33,7 @@ inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 
 // The skinny (decode) path takes M up to this many rows; larger M is tiled.
 constexpr int64_t kSkinnyMaxM = 64;
-// The decode product takes M <= 32, and M <= 64 without residue columns: with
-// them, four row tiles need a second operand copy that halves the K range a
-// workgroup holds, and the tiled product is faster there.
-inline bool skinny_rows(int64_t M, int64_t K, int64_t S) { return K > 0 && (M <= 32 || (M <= kSkinnyMaxM && S == 0)); }
+inline bool skinny_rows(int64_t M, int64_t K, int64_t) { return K > 0 && M <= kSkinnyMaxM; }
 
 int64_t ldc_for(int64_t K) { return (int64_t)up((size_t)(K / 2), 16); }
 int64_t lds_for(int64_t K) { return (int64_t)up((size_t)(K / 16), 8); }

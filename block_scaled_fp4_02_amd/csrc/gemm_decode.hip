@@ -48,7 +48,6 @@ constexpr int kProd = 4;                       // producer waves: the activation
 constexpr int kThreads = 64 * (kCons + kProd);
 constexpr int kPThreads = 64 * kProd;
 constexpr int kMaxItems = 8;                   // (tile, unit) items per consumer wave
-__host__ __device__ constexpr int max_items(int MT) { return MT == 4 ? 4 : kMaxItems; }   // registers
 constexpr int kPreItems = 2;                   // items each consumer issues before the operand barrier
 constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
 constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
@@ -370,7 +369,7 @@ __device__ inline void zero_unwritten(half8 *lds, const DArgs &a, const Range &r
 template <int MT, bool RES, bool TILED, bool REFILL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
-    constexpr int kRing = MT == 1 ? 4 : (MT == 2 ? 3 : 2);   // weight items in flight per consumer wave
+    constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
     // Items issued before the operand barrier; the rest of the ring is issued
     // after it, so that computing on landed items overlaps the (throttled)
     // issue of later loads.
@@ -404,7 +403,7 @@ void decode_kernel(DArgs a) {
     // Consumer wave w takes tiles t_lo + w / KW + TW i_t (i_t < ntw) and units
     // w % KW + KW i_u (i_u < nuw) of the range: KW waves share each tile, each
     // summing its own units, and their parts are added in LDS at the end.
-    const int KW = MT == 4 ? 1 : a.KW, TW = kCons / KW;   // four row tiles: the plan keeps KW = 1
+    const int KW = a.KW, TW = kCons / KW;
     const int tg = wave / KW, uo = wave % KW;
     const int ntw = (wave < kCons && t_lo + tg < t_hi) ? (int)((t_hi - t_lo - tg + TW - 1) / TW) : 0;
     const int nuw = (wave < kCons && uo < units) ? (units - uo + KW - 1) / KW : 0;
@@ -643,7 +642,7 @@ void decode_kernel(DArgs a) {
         // Fully unrolled over NI items (no loop back-edge), NI = kRing when the
         // plan's items per wave fit the ring (no refills at all; a kernel of its
         // own, so the two loop shapes never share a register allocation) and
-        // max_items(MT) otherwise: each slot is consumed in place and refilled right
+        // kMaxItems otherwise: each slot is consumed in place and refilled right
         // after, always with the same five loads (past the last item -- only in
         // ragged waves -- it re-reads the current one), so vmcnt is tracked
         // exactly and the common plans issue no redundant loads.
@@ -669,7 +668,7 @@ void decode_kernel(DArgs a) {
                             const int fo = (4 * i + j) * 4 * R;
 #pragma unroll
                             for (int mt = 0; mt < MT; ++mt) {
-                                float4v &ac = (MT < 4 && (j & 1)) ? acc2[mt] : acc[mt];   // four row tiles: one chain each
+                                float4v &ac = (j & 1) ? acc2[mt] : acc[mt];
                                 ac = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt]], b, ac, 0, 0, 0);
                                 if (RES && res_u) {
                                     float4v &ar = kSepRes ? ((j & 1) ? accr2[0] : accr[0]) : ac;
@@ -714,7 +713,7 @@ void decode_kernel(DArgs a) {
                 }
             }
         };
-        run(std::integral_constant<int, REFILL ? max_items(MT) : kRing>{});
+        run(std::integral_constant<int, REFILL ? kMaxItems : kRing>{});
     }
 
     // ---- tiles shared by KW waves: their parts are added in LDS, in wave order
@@ -793,6 +792,165 @@ void decode_kernel(DArgs a) {
     TL(4);
 }
 
+// ---------------------------------------------------------------- M = 33..64
+// Four row tiles take 64 rows x 1 KiB of operand per 512-column unit, so a
+// whole K range does not fit in LDS. Here the operand streams through a window
+// of two unit slots instead: every consumer wave owns one 16-row weight tile
+// over all of K (no split-K, no combine), producers fill the slot of unit k + 2
+// as soon as the consumers are done with unit k, one workgroup barrier per
+// unit. Residue columns (ARCQuant article, sections 3.1-3.2) are further
+// "virtual units" after the K / 512 main ones: their operand is the residue
+// rows, their weights W's first units again (read a second time: S / K more
+// weight bytes, against twice the LDS for a second operand copy).
+//
+// Barriers: both kinds of wave pass exactly NV = KU + RU of them. Barrier 0:
+// units 0 and 1 are in their slots. Barrier k >= 1: the consumers are done with
+// unit k - 1, and the producers have stored unit k (k >= 2) into the slot unit
+// k - 2 left. Consumers work on unit k between barriers k and k + 1.
+constexpr int kWinChunks = 4;                  // operand chunks per producer thread and unit (64 x 16)
+constexpr int kWinRows = 64;                   // operand rows of a window slot: fixed, so every fragment
+                                               // offset is an immediate of the LDS read
+
+template <bool RES>
+__device__ inline QChunk win_chunk_load(const DArgs &a, int v, int KU, int c) {
+    QChunk q;
+    q.key = -1;
+    q.c = make_uint4(0, 0, 0, 0);
+    q.s = 0;
+    q.s1 = 0;
+    const int m = c >> 4, p = c & 15;
+    const bool resv = RES && v >= KU;
+    const int64_t u = resv ? v - KU : v;
+    const int64_t kc = 512 * u + 32 * p;                              // operand column
+    const int64_t cend = resv ? (a.res_cols < 512 * u + 512 ? a.res_cols : 512 * u + 512)
+                              : (a.K < 512 * u + 512 ? a.K : 512 * u + 512);
+    if (m >= a.M) return q;
+    if (kc < cend) {
+        const ChunkPos f{(resv ? a.K : 0) + kc, ((p & 3) * 16 + (p >> 2)) * kWinRows + m + (kc + 16 < cend ? kV1 : 0)};
+        q = qchunk_load<RES>(a.q_codes + (int64_t)m * a.q_ldc, a.q_scales + (int64_t)m * a.q_lds, f);
+    } else {
+        q.key = ((p & 3) * 16 + (p >> 2)) * kWinRows + m;               // past the data: a zero chunk
+    }
+    return q;
+}
+
+template <bool TILED, bool RES>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_win_kernel(DArgs a) {
+    constexpr int MT = 4;
+    constexpr int R = kWinRows, SLOT = 64 * kWinRows;
+    extern __shared__ half8 lds_a[];           // [2 slots][64 R]: rows >= M are never read
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r16 = lane & 15;
+    const int M = (int)a.M;
+    const int KU = (int)((a.K + 511) / 512), RU = RES ? (int)((a.res_cols + 511) / 512) : 0, NV = KU + RU;
+
+    if (wave < kCons) {
+        // ---- consumer: tile t over all (virtual) units
+        const int64_t t = 4 * (int64_t)blockIdx.x + wave;
+        const bool has = t < a.NT;
+        const int64_t tc = has ? t : a.NT - 1;
+        const float qS = load_vmem(a.q_S), wS = load_vmem(a.w_S);   // first: no wait holds a weight load on them
+        auto issue = [&](int v, WLoad &w) {
+            const int64_t wu = v < KU ? v : v - KU;
+            if (TILED) {
+                load_w_tiled(a, tc, wu, lane, w);
+            } else {
+                const int64_t n = 16 * tc + r16;
+                load_w(a, n < a.N ? n : a.N - 1, 512 * wu, g, w);
+            }
+        };
+        int arow[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) arow[mt] = 16 * mt + r16 < M ? 16 * mt + r16 : M - 1;
+        float4v acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
+        WLoad ring0, ring1;
+        if (has) {
+            issue(0, ring0);
+            if (NV > 1) issue(1, ring1);
+        }
+        __syncthreads();                       // barrier 0: units 0 and 1 are in their slots
+        auto step = [&](int v, WLoad &w) {
+            if (has) {
+                const half8 *abase = lds_a + (v & 1) * SLOT + g * R;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t sw = (i < 2) ? w.s.x : w.s.y;
+                    const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
+                    const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
+                    const uint32_t cws[4] = {w.c[i].x, w.c[i].y, w.c[i].z, w.c[i].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
+                        const int fo = (4 * i + j) * 4 * R;
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt]], b, acc[mt], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // one 32-column step's fragments live at a time
+                }
+                if (v + 2 < NV) issue(v + 2, w);
+            }
+            if (v + 1 < NV) __syncthreads();   // barrier v + 1: done with unit v
+        };
+        for (int v = 0; v < NV; v += 2) {
+            step(v, ring0);
+            if (v + 1 < NV) step(v + 1, ring1);
+        }
+        if (has) {
+            const float scale = qS * wS;
+            const int64_t n = 16 * t + r16;
+            if (n < a.N) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t m = 16 * mt + 4 * g + e;
+                        if (m < a.M) {
+                            const float val = acc[mt][e] * scale;
+                            if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = val;
+                            else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(val);
+                        }
+                    }
+            }
+        }
+    } else {
+        // ---- producers: unit v's chunks (row c / 16, position c % 16) into slot v & 1;
+        // the loads of unit k + 1 go out while unit k is stored
+        const int ptid = tid - 64 * kCons;
+        QChunk q0[kWinChunks], q1[kWinChunks];
+        auto load_unit = [&](int v, QChunk *q) {
+#pragma unroll
+            for (int i = 0; i < kWinChunks; ++i) q[i] = win_chunk_load<RES>(a, v, KU, ptid + kPThreads * i);
+        };
+        auto store_unit = [&](int v, const QChunk *q) {
+            half8 *dst = lds_a + (v & 1) * SLOT;
+#pragma unroll
+            for (int i = 0; i < kWinChunks; ++i) qchunk_store<RES>(dst, 4 * R, q[i]);
+        };
+        load_unit(0, q0);
+        if (NV > 1) load_unit(1, q1);
+        store_unit(0, q0);
+        if (NV > 1) store_unit(1, q1);
+        if (NV > 2) load_unit(2, q0);
+        __syncthreads();                       // barrier 0
+        auto pstep = [&](int k, QChunk *qs, QChunk *ql) {
+            // barrier k: store unit k (k >= 2; loaded one step ago into qs), load unit k + 1 into ql
+            if (k >= 2) {
+                store_unit(k, qs);
+                if (k + 1 < NV) load_unit(k + 1, ql);
+            }
+            __syncthreads();
+        };
+        for (int k = 1; k < NV; k += 2) {
+            pstep(k, q1, q0);                  // k odd: unit k's data sits in q1
+            if (k + 1 < NV) pstep(k + 1, q0, q1);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- planning
 struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool refill, ordered; int64_t NT, Q; size_t lds; };
 
@@ -816,10 +974,8 @@ template <bool TILED, bool REFILL>
 const void *kernel_ptr_t(int MT, bool res) {
     if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL>)
                             : reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, REFILL>);
-    if (MT == 2) return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL>)
-                            : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL>);
-    return res ? reinterpret_cast<const void *>(&decode_kernel<4, true, TILED, REFILL>)
-               : reinterpret_cast<const void *>(&decode_kernel<4, false, TILED, REFILL>);
+    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL>);
 }
 
 const void *kernel_ptr(int MT, bool res, bool tiled, bool refill) {
@@ -837,9 +993,9 @@ const void *kernel_ptr(int MT, bool res, bool tiled, bool refill) {
 // costs three dependent round trips through the memory system.
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
     Plan pl;
-    pl.MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    pl.MT = M <= 16 ? 1 : 2;
     const bool res = res_cols > 0;
-    const int ring = pl.MT == 1 ? 4 : (pl.MT == 2 ? 3 : 2);
+    const int ring = pl.MT == 1 ? 4 : 3;
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
     const int ncu = cu_count();
@@ -855,11 +1011,11 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
         const int64_t U = (ku + P0 - 1) / P0, P = (ku + U - 1) / U;
         if (P != P0) continue;                 // each split once
         const size_t lds_a = (size_t)U * 1024 * (size_t)op_rows;
-        for (int KW = 1; KW <= (pl.MT == 4 ? 1 : kCons); KW *= 2) {   // four row tiles: KW = 1 only
+        for (int KW = 1; KW <= kCons; KW *= 2) {
             const int TW = kCons / KW;
             const int64_t nuw = (U + KW - 1) / KW;
-            for (int ntw = 1; ntw <= max_items(pl.MT); ++ntw) {
-                if (ntw * nuw > max_items(pl.MT) || (KW > 1 && ntw > 2)) break;
+            for (int ntw = 1; ntw <= kMaxItems; ++ntw) {
+                if (ntw * nuw > kMaxItems || (KW > 1 && ntw > 2)) break;
                 const int64_t T = (int64_t)TW * ntw, Q = (pl.NT + T - 1) / T, G = P * Q;
                 size_t lds = lds_a > (KW > 1 ? (size_t)8192 * pl.MT : 0) ? lds_a : (size_t)8192 * pl.MT;
                 lds = (lds + 255) / 256 * 256;
@@ -877,7 +1033,7 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     if (const char *e = std::getenv("NVFP4_DECODE_FORCE")) {         // tuning override "U,KW,ntw"
         int fu = 0, fk = 0, ft = 0;
         if (std::sscanf(e, "%d,%d,%d", &fu, &fk, &ft) == 3 && fu >= 1 && (fk == 1 || fk == 2 || fk == 4) &&
-            ft >= 1 && ft * ((fu + fk - 1) / fk) <= max_items(pl.MT) && (fk == 1 || ft <= 2) && (pl.MT < 4 || fk == 1) &&
+            ft >= 1 && ft * ((fu + fk - 1) / fk) <= kMaxItems && (fk == 1 || ft <= 2) &&
             (size_t)fu * 1024 * (size_t)op_rows + kLdsStatic <= kLdsPerCu) {
             bU = fu; bKW = fk; bntw = ft; found = true;
         }
@@ -921,11 +1077,13 @@ bool plan_ok(const Plan &pl) { return pl.Q <= kMaxTileCounters && pl.G >= 1; }
 }  // namespace
 
 size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t res_cols) {
+    if (M > 32) return 0;                      // the windowed kernel: no split-K
     const Plan pl = plan_for(M, N, K, res_cols, false, false);
     return pl.P > 1 ? (size_t)pl.P * M * N * sizeof(float) : 0;
 }
 
 bool decode_can_fuse(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool x_bf16) {
+    if (M > 32) return false;                  // the windowed kernel reads quantized activations
     const Plan pl = plan_for(M, N, K, res_cols, true, false);
     return x_bf16 && plan_ok(pl) && pl.mode == MODE_LOCAL;
 }
@@ -936,9 +1094,37 @@ extern "C" int nvfp4_debug_timeline(void *host, size_t bytes) {
 }
 #endif
 
+// M = 33..64: the windowed kernel, one 16-row weight tile per consumer wave
+// over all of K (and the residue units), quantized activations only.
+hipError_t launch_decode_win(const DecodeLaunch &g, hipStream_t st) {
+    if (g.x != nullptr || !g.header) return hipErrorInvalidValue;
+    DArgs a{};
+    a.q_codes = g.q_codes; a.q_ldc = g.q_ldc; a.q_scales = g.q_scales; a.q_lds = g.q_lds; a.q_S = g.q_S;
+    a.w_codes = g.w_codes; a.w_ldc = g.w_ldc; a.w_scales = g.w_scales; a.w_lds = g.w_lds; a.w_S = g.w_S;
+    a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
+    a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
+    a.header = reinterpret_cast<uint8_t *>(g.header);
+    a.NT = (g.N + 15) / 16;
+    a.Rr = (int)g.M;
+    a.U = 1; a.P = 1; a.T = 4; a.tw = 1; a.KW = 1; a.G = (int)((a.NT + 3) / 4); a.mode = MODE_PRE; a.Mp = 0;
+    const bool res = g.res_cols > 0, tiled = g.w_tiled != 0;
+    const void *fn = tiled ? (res ? reinterpret_cast<const void *>(&decode_win_kernel<true, true>)
+                                  : reinterpret_cast<const void *>(&decode_win_kernel<true, false>))
+                           : (res ? reinterpret_cast<const void *>(&decode_win_kernel<false, true>)
+                                  : reinterpret_cast<const void *>(&decode_win_kernel<false, false>));
+    const size_t lds = 2 * 64 * (size_t)kWinRows * sizeof(half8);
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    void *args[] = {&a};
+    return hipLaunchKernel(fn, dim3((unsigned)a.G), dim3(kThreads), args, lds, st);
+}
+
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     const bool raw = g.x != nullptr;
-    if (g.M < 1 || g.M > 64 || g.N < 1 || g.K < 1) return hipErrorInvalidValue;   // the kernel's row bound
+    if (g.M < 1 || g.M > 64 || g.N < 1 || g.K < 1) return hipErrorInvalidValue;   // the kernels' row bound
+    if (g.M > 32) return launch_decode_win(g, st);
     const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols, raw, false);
     if (!plan_ok(pl) || (raw && pl.mode != MODE_LOCAL)) return hipErrorInvalidValue;
     if (!g.header || g.scratch_bytes < decode_workspace_bytes(g.M, g.N, g.K, g.res_cols) ||
