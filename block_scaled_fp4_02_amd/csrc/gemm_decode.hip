@@ -798,7 +798,8 @@ void decode_kernel(DArgs a) {
 // of two unit slots instead: every consumer wave owns one 16-row weight tile
 // over all of K (no split-K, no combine), producers fill the slot of unit k + 2
 // as soon as the consumers are done with unit k, one workgroup barrier per
-// unit. Residue columns (ARCQuant article, sections 3.1-3.2) are further
+// unit (loads run three units ahead on both sides). Residue columns (ARCQuant
+// article, sections 3.1-3.2) are further
 // "virtual units" after the K / 512 main ones: their operand is the residue
 // rows, their weights W's first units again (read a second time: S / K more
 // weight bytes, against twice the LDS for a second operand copy).
@@ -845,6 +846,7 @@ void decode_win_kernel(DArgs a) {
     const int M = (int)a.M;
     const int KU = (int)((a.K + 511) / 512), RU = RES ? (int)((a.res_cols + 511) / 512) : 0, NV = KU + RU;
 
+    TL(0);
     if (wave < kCons) {
         // ---- consumer: tile t over all (virtual) units
         const int64_t t = 4 * (int64_t)blockIdx.x + wave;
@@ -866,12 +868,14 @@ void decode_win_kernel(DArgs a) {
         float4v acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
-        WLoad ring0, ring1;
+        WLoad ring0, ring1, ring2;             // units v, v + 1, v + 2 in flight (v mod 3)
         if (has) {
             issue(0, ring0);
             if (NV > 1) issue(1, ring1);
+            if (NV > 2) issue(2, ring2);
         }
         __syncthreads();                       // barrier 0: units 0 and 1 are in their slots
+        TL(1);
         auto step = [&](int v, WLoad &w) {
             if (has) {
                 const half8 *abase = lds_a + (v & 1) * SLOT + g * R;
@@ -891,14 +895,18 @@ void decode_win_kernel(DArgs a) {
                     }
                     __builtin_amdgcn_sched_barrier(0);   // one 32-column step's fragments live at a time
                 }
-                if (v + 2 < NV) issue(v + 2, w);
+                if (v + 3 < NV) issue(v + 3, w);
             }
             if (v + 1 < NV) __syncthreads();   // barrier v + 1: done with unit v
+            if (v == 2) TL(2);
+            if (v == 5) TL(3);
         };
-        for (int v = 0; v < NV; v += 2) {
+        for (int v = 0; v < NV; v += 3) {
             step(v, ring0);
             if (v + 1 < NV) step(v + 1, ring1);
+            if (v + 2 < NV) step(v + 2, ring2);
         }
+        TL(4);
         if (has) {
             const float scale = qS * wS;
             const int64_t n = 16 * t + r16;
@@ -917,10 +925,10 @@ void decode_win_kernel(DArgs a) {
             }
         }
     } else {
-        // ---- producers: unit v's chunks (row c / 16, position c % 16) into slot v & 1;
-        // the loads of unit k + 1 go out while unit k is stored
+        // ---- producers: unit v's chunks (row c / 16, position c % 16) into slot v & 1,
+        // from register set v mod 3; the loads of unit k + 2 go out while unit k is stored
         const int ptid = tid - 64 * kCons;
-        QChunk q0[kWinChunks], q1[kWinChunks];
+        QChunk q0[kWinChunks], q1[kWinChunks], q2[kWinChunks];
         auto load_unit = [&](int v, QChunk *q) {
 #pragma unroll
             for (int i = 0; i < kWinChunks; ++i) q[i] = win_chunk_load<RES>(a, v, KU, ptid + kPThreads * i);
@@ -932,21 +940,26 @@ void decode_win_kernel(DArgs a) {
         };
         load_unit(0, q0);
         if (NV > 1) load_unit(1, q1);
+        if (NV > 2) load_unit(2, q2);
         store_unit(0, q0);
         if (NV > 1) store_unit(1, q1);
-        if (NV > 2) load_unit(2, q0);
+        if (NV > 3) load_unit(3, q0);
+        TL(5);
         __syncthreads();                       // barrier 0
+        TL(6);
         auto pstep = [&](int k, QChunk *qs, QChunk *ql) {
-            // barrier k: store unit k (k >= 2; loaded one step ago into qs), load unit k + 1 into ql
+            // barrier k: store unit k (k >= 2; its set qs = k mod 3), load unit k + 2 into ql
+            // (set (k + 2) mod 3, whose unit k - 1 is stored)
             if (k >= 2) {
                 store_unit(k, qs);
-                if (k + 1 < NV) load_unit(k + 1, ql);
+                if (k + 2 < NV) load_unit(k + 2, ql);
             }
             __syncthreads();
         };
-        for (int k = 1; k < NV; k += 2) {
-            pstep(k, q1, q0);                  // k odd: unit k's data sits in q1
-            if (k + 1 < NV) pstep(k + 1, q0, q1);
+        for (int k = 1; k < NV; k += 3) {      // k = 1 mod 3 at the top
+            pstep(k, q1, q0);
+            if (k + 1 < NV) pstep(k + 1, q2, q1);
+            if (k + 2 < NV) pstep(k + 2, q0, q2);
         }
     }
 }
