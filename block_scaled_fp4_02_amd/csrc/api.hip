@@ -48,7 +48,7 @@ size_t tensor_ws(int64_t rows, int64_t K) {
 
 size_t gemm_ws(int64_t M, int64_t N, int64_t K, int64_t S) {
     if (skinny_rows(M, K, S)) return up(decode_workspace_bytes(M, N, K, S), kAlign);
-    return 0;
+    return up(prefill_workspace_bytes(M, N, K, S), kAlign);
 }
 
 // Bound on the small quantizer's arrival wait, in polls of ~0.1 us (a few ms).
@@ -160,6 +160,7 @@ nvfp4_status enqueue_gemm(const nvfp4_tensor &a, const nvfp4_tensor &w, int64_t 
         g.w_tiled = w.layout == NVFP4_LAYOUT_TILED;
         g.M = M; g.N = w.rows; g.K = K; g.res_cols = S;
         g.y = y; g.yt = yt; g.ldy = ldy;
+        g.scratch = scratch; g.scratch_bytes = scratch_bytes;
         e = launch_prefill(g, st);
     }
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);

@@ -36,6 +36,9 @@ struct TArgs {
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
     int tiles_m, tiles_n;
+    // split-K (tiled2 only): range p = blockIdx.y of P, kchunk k-steps each;
+    // part != nullptr: unscaled fp32 partial tiles to part[p][M][N] instead of y
+    int P; int64_t kchunk; float *part;
 };
 
 __device__ inline uint16_t f2bf(float f) {
@@ -297,7 +300,10 @@ void tiled2_kernel(TArgs a) {
     if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
     const int tn = bid / a.tiles_m, tm = bid % a.tiles_m;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    const int64_t ksteps = (a.K + BK - 1) / BK;
+    // this workgroup's k-steps [s0, s0 + ksteps) (split-K: range blockIdx.y)
+    const int64_t kall = (a.K + BK - 1) / BK;
+    const int64_t s0 = (int64_t)blockIdx.y * a.kchunk;
+    const int64_t ksteps = (s0 + a.kchunk < kall ? s0 + a.kchunk : kall) - s0;
 
     // chunk c of this thread: A chunks (c < A_ITERS), then B chunks; (row, half) of the tile
     auto crow = [&](int c) { return ((tid + NT * (c < A_ITERS ? c : c - A_ITERS)) >> 1); };
@@ -308,7 +314,7 @@ void tiled2_kernel(TArgs a) {
     };
     RowChunk rq0[NCH], rq1[NCH];
     auto gload = [&](int64_t s, RowChunk *q) {
-        const int64_t k = s * BK;
+        const int64_t k = (s0 + s) * BK;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int r = crow(c), h = chalf(c);
@@ -382,8 +388,24 @@ void tiled2_kernel(TArgs a) {
         if (s + 1 < ksteps) step(s + 1, std::integral_constant<int, 1>{});
     }
 
-    const float scale = a.a_S[0] * a.w_S[0];
     const int g = lane >> 4, c16 = lane & 15;
+    if (a.part) {                              // split-K: the unscaled partial tile
+        float *part = a.part + (int64_t)blockIdx.y * a.M * a.N;
+#pragma unroll
+        for (int i = 0; i < WRT; ++i)
+#pragma unroll
+            for (int j = 0; j < WCT; ++j) {
+                const int64_t n = n0 + (wn * WCT + j) * 16 + c16;
+                if (n >= a.N) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t m = m0 + (wm * WRT + i) * 16 + 4 * g + e;
+                    if (m < a.M) part[m * a.N + n] = acc[i][j][e];
+                }
+            }
+        return;
+    }
+    const float scale = a.a_S[0] * a.w_S[0];
 #pragma unroll
     for (int i = 0; i < WRT; ++i) {
 #pragma unroll
@@ -403,6 +425,21 @@ void tiled2_kernel(TArgs a) {
     }
 }
 
+// Split-K combine: y[m][n] = S_a S_w sum_p part[p][m][n], in order p = 0, 1, ...
+// (deterministic); one thread per element.
+__global__ __launch_bounds__(256) void prefill_combine_kernel(const float *part, int P, int64_t M, int64_t N,
+                                                              const float *a_S, const float *w_S, void *y, int yt,
+                                                              int64_t ldy) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * N) return;
+    const int64_t m = idx / N, n = idx - m * N;
+    float s = 0.0f;
+    for (int p = 0; p < P; ++p) s += part[(int64_t)p * M * N + idx];
+    const float v = s * (a_S[0] * w_S[0]);
+    if (yt == 1) static_cast<float *>(y)[m * ldy + n] = v;
+    else static_cast<uint16_t *>(y)[m * ldy + n] = f2bf(v);
+}
+
 template <int BM, int BN, int NW, int WPE>
 hipError_t run2(const TArgs &a0, hipStream_t st) {
     TArgs a = a0;
@@ -417,7 +454,12 @@ hipError_t run2(const TArgs &a0, hipStream_t st) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    tiled2_kernel<BM, BN, NW, WPE><<<a.tiles_m * a.tiles_n, 64 * NW, lds, st>>>(a);
+    tiled2_kernel<BM, BN, NW, WPE><<<dim3(a.tiles_m * a.tiles_n, a.P), 64 * NW, lds, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.part) return e;
+    const int64_t total = a.M * a.N;
+    prefill_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a.part, a.P, a.M, a.N, a.a_S, a.w_S, a.y,
+                                                                            a.yt, a.ldy);
     return hipGetLastError();
 }
 
@@ -440,9 +482,20 @@ hipError_t run(const TArgs &a0, hipStream_t st) {
     return hipGetLastError();
 }
 
-}  // namespace
+// Split-K ranges for the large-tile product: only when even 256 x 256 tiles
+// leave most of the chip idle and K is long; P ranges of at least 32 k-steps
+// until the chip holds ~one workgroup per CU.
+int prefill_splits(int64_t M, int64_t N, int64_t K, int64_t S) {
+    if (S > 0 || M <= 64) return 1;
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t ksteps = (K + BK - 1) / BK;
+    if (tiles * 2 >= 192 || ksteps < 256) return 1;     // large enough for the unsplit plans
+    int P = 1;
+    while (P < 8 && tiles * P < 224 && ksteps / (2 * P) >= 32) P *= 2;
+    return P;
+}
 
-hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st) {
+hipError_t launch_prefill_impl(const PrefillLaunch &g, hipStream_t st) {
     TArgs a;
     a.a_codes = g.a_codes; a.a_ldc = g.a_ldc; a.a_scales = g.a_scales; a.a_lds = g.a_lds; a.a_S = g.a_S;
     a.w_codes = g.w_codes; a.w_ldc = g.w_ldc; a.w_scales = g.w_scales; a.w_lds = g.w_lds; a.w_S = g.w_S;
@@ -450,16 +503,35 @@ hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st) {
     a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
     a.tiles_m = a.tiles_n = 0;
+    a.P = 1; a.kchunk = (g.K + BK - 1) / BK; a.part = nullptr;
     if (g.res_cols > 0) {
         if (g.M <= 64) return run<64, 128, true>(a, st);
         return run<128, 128, true>(a, st);
     }
     if (g.M <= 64) return run<64, 128, false>(a, st);
+    const int P = prefill_splits(g.M, g.N, g.K, g.res_cols);
+    if (P > 1) {
+        if (!g.scratch || g.scratch_bytes < (size_t)P * (size_t)g.M * (size_t)g.N * sizeof(float))
+            return hipErrorInvalidValue;
+        a.P = P;
+        a.kchunk = ((g.K + BK - 1) / BK + P - 1) / P;
+        a.part = static_cast<float *>(g.scratch);
+        return run2<256, 256, 8, 2>(a, st);
+    }
     // large tiles when they still give the chip a workgroup per CU or more
     const int64_t tn = (g.N + 255) / 256;
     if (((g.M + 255) / 256) * tn >= 192) return run2<256, 256, 8, 2>(a, st);
     if (((g.M + 127) / 128) * tn >= 192) return run2<128, 256, 4, 1>(a, st);
     return run2<128, 128, 4, 2>(a, st);             // 128 x 128 tiles, two workgroups per CU
 }
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t S) {
+    const int P = prefill_splits(M, N, K, S);
+    return P > 1 ? (size_t)P * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st) { return launch_prefill_impl(g, st); }
 
 }  // namespace nvfp4

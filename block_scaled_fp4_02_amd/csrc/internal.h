@@ -81,7 +81,11 @@ struct PrefillLaunch {
     int w_tiled;
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
+    void *scratch; size_t scratch_bytes;    // split-K partials (prefill_workspace_bytes), or nullptr
 };
+// Workspace bytes of the prefill product: fp32 split-K partials when the plan
+// splits K (long K, too few output tiles to fill the chip), else 0.
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t S);
 hipError_t launch_prefill(const PrefillLaunch &g, hipStream_t st);
 
 // Row-major -> tiled weight layout (16 x 512 items in decode lane order).
