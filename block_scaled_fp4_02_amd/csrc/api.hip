@@ -132,7 +132,7 @@ nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in,
     q.codes = out.codes; q.ldc = out.ld_codes; q.scales = out.scales; q.lds = out.ld_scales;
     q.S_out = out.tensor_scale;
     q.partials = partials; q.rscale = rscale;
-    q.bar = header;                            // header words 0 and 1
+    q.slots = reinterpret_cast<unsigned long long *>(header) + kSlotsOffset / 8;   // header bytes 512..1023
     q.spin = spin_limit();
     hipError_t e = launch_quantize(q, st);
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);

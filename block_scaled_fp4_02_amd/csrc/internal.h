@@ -23,7 +23,7 @@ struct QuantLaunch {
     // workspace
     float *partials;                        // kAmaxPartials floats
     float *rscale;                          // rows floats (RMSNorm factors)
-    unsigned *bar;                          // 2 header words (arrival count, generation), or nullptr
+    unsigned long long *slots;              // 64 arrival slots of the small quantizer (header), or nullptr
     unsigned spin;                          // bound on the arrival wait (polls)
 };
 
@@ -38,12 +38,13 @@ struct ChannelAbsmaxLaunch {
 };
 hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 
-// Every workspace starts with a header of counters: the small quantizer's
-// arrival count and generation (bytes 0..7) and the decode product's split-K
-// tile counters (from byte 4096). It must be zero before the first call on a
-// workspace; calls keep it valid (counts return to zero, the generation only
-// advances), so it never needs clearing again.
+// Every workspace starts with a header of counters: the small quantizer's 64
+// arrival slots (bytes 512..1023: partial maximum and epoch) and the decode
+// product's split-K tile counters (from byte 4096). It must be zero before the
+// first call on a workspace; calls keep it valid (counts return to zero, all
+// slots advance to the same epoch), so it never needs clearing again.
 constexpr size_t kHeaderBytes = 8192;
+constexpr size_t kSlotsOffset = 512;
 
 // Decode-shaped (M <= 64) product in one launch. With x != nullptr (bf16, and
 // decode_can_fuse true) the raw activations are quantized inside the kernel and

@@ -263,9 +263,17 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(QArgs a) {
 // Decode-sized activations (rows <= 32, no RMSNorm or reorder) in one launch of
 // G <= 64 workgroups, a thread per 16-element block (up to kSmallPer each):
 // partial maxima, one grid-wide arrival, then each workgroup encodes its blocks
-// from registers. Between launches the GPU is otherwise idle, so the arrival is
-// short; it is bounded, and a workgroup whose wait gives up recomputes amax(X)
-// itself (same result).
+// from registers.
+//
+// The arrival uses no read-modify-write (atomics on one word from many
+// workgroups serialize in the memory system and cost microseconds): 64 slots
+// of 8 bytes, each (partial maximum | epoch << 32). Between calls every slot
+// holds the same epoch; workgroup b reads its own slot's epoch e at start,
+// writes (partial, e + 1) into the slots l = b mod G, and waits until all 64
+// slots carry e + 1, so the 64 partials it then holds are those of this call
+// (slots l >= G repeat a real partial). The wait is bounded; a workgroup whose
+// wait gives up recomputes amax(X) itself (same result), and it has still
+// written its slots, so the epochs stay in step.
 constexpr int kSmallPer = 4;
 constexpr int kSmallMaxG = 64;
 
@@ -273,17 +281,18 @@ template <typename T>
 __device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 template <typename T>
 __device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-template <typename T>
-__device__ inline T add_dev(T *p, T v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int XT>
-__global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsigned *bar, float *part, int G,
+__global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsigned long long *slot, int G,
                                                                    unsigned spin) {
     __shared__ float sh[kThreads / 64];
     __shared__ int sh_ok;
     const int64_t KB = a.K_in / 16, NB = a.rows * KB;
     const int64_t b0 = (int64_t)blockIdx.x * NB / G, b1 = ((int64_t)blockIdx.x + 1) * NB / G;
+    // this call's epoch, read ahead of the data (its latency overlaps theirs)
+    const bool arrive = !a.static_S && G > 1;
+    unsigned ep = 0;
+    if (arrive && threadIdx.x < 64) ep = (unsigned)(ld_dev(&slot[blockIdx.x]) >> 32) + 1u;
     float v[kSmallPer][16];
     float m = 0.0f;
 #pragma unroll
@@ -301,30 +310,26 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
         S = *a.static_S;
     } else {
         m = block_max(m, sh);
-        if (G > 1) {
-            if (threadIdx.x == 0) {
-                // sense-reversing arrival: bar[0] counts, bar[1] is the generation
-                st_dev(&part[blockIdx.x], m);
-                const unsigned gen = ld_dev(&bar[1]);
-                wait_vm();                     // the partial is visible and gen read before arriving
+        if (arrive) {
+            if (threadIdx.x < 64) {            // wave 0: lane l owns slot l
+                const int l = threadIdx.x;
+                if (l % G == (int)blockIdx.x)
+                    st_dev(&slot[l], (unsigned long long)ep << 32 | __float_as_uint(m));
+                unsigned long long sv = ld_dev(&slot[l]);
+                unsigned it = 0;
                 int ok = 1;
-                if (add_dev(&bar[0], 1u) == (unsigned)G - 1) {
-                    st_dev(&bar[0], 0u);
-                    wait_vm();
-                    add_dev(&bar[1], 1u);
-                } else {
-                    unsigned it = 0;
-                    while (ld_dev(&bar[1]) == gen) {
-                        if (++it > spin) { ok = 0; break; }
-                        __builtin_amdgcn_s_sleep(2);
-                    }
+                while (!__all((unsigned)(sv >> 32) == ep)) {
+                    if (++it > spin) { ok = 0; break; }
+                    __builtin_amdgcn_s_sleep(2);
+                    sv = ld_dev(&slot[l]);
                 }
-                sh_ok = ok;
+                const float pm = wave_max(__uint_as_float((unsigned)sv));
+                if (l == 0) { sh_ok = ok; sh[0] = pm; }
             }
             __syncthreads();
             float mm = 0.0f;
             if (sh_ok) {
-                for (int i = threadIdx.x; i < G; i += kThreads) mm = fmaxf(mm, ld_dev(&part[i]));
+                mm = sh[0];
             } else {                           // the wait gave up: all of X here
                 for (int64_t b = threadIdx.x; b < NB; b += kThreads) {
                     const int64_t row = b / KB, blk = b - row * KB;
@@ -459,7 +464,7 @@ int amax_grid(int64_t rows, int64_t K) {
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
     const bool norm = q.gamma != nullptr, perm = q.perm != nullptr;
     const int64_t nb = q.rows * (q.K_in / 16);
-    if (!norm && !perm && q.bar && q.rows <= 32 && nb > 0 && nb <= (int64_t)kSmallMaxG * kThreads * kSmallPer) {
+    if (!norm && !perm && q.slots && q.rows <= 32 && nb > 0 && nb <= (int64_t)kSmallMaxG * kThreads * kSmallPer) {
         int G = (int)((nb + kThreads - 1) / kThreads);
         if (G > kSmallMaxG) G = kSmallMaxG;
         QArgs a;
@@ -468,9 +473,9 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
         a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
         a.partials = q.partials; a.npart = 0; a.rscale = q.rscale;
         if (q.xt == IN_BF16)
-            quantize_small_kernel<IN_BF16><<<G, kThreads, 0, st>>>(a, q.bar, q.partials, G, q.spin);
+            quantize_small_kernel<IN_BF16><<<G, kThreads, 0, st>>>(a, q.slots, G, q.spin);
         else
-            quantize_small_kernel<IN_F32><<<G, kThreads, 0, st>>>(a, q.bar, q.partials, G, q.spin);
+            quantize_small_kernel<IN_F32><<<G, kThreads, 0, st>>>(a, q.slots, G, q.spin);
         return hipGetLastError();
     }
     int npart = 0;

@@ -44,7 +44,7 @@
  *  - The caller owns and allocates every buffer, including the workspace
  *    (size from nvfp4_workspace_size). The library never allocates device
  *    memory. The first 8 KiB of every workspace hold counters (the small
- *    quantizer's arrival count and generation, the decode product's split-K
+ *    quantizer's arrival slots, the decode product's split-K
  *    tile counters): they must be zero before the first call on a workspace;
  *    calls keep them valid, so they never need clearing again. A workspace
  *    must not be used by two calls at the same time.
