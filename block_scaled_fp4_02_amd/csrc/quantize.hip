@@ -170,6 +170,7 @@ struct QArgs {
     float *S_out;
     const float *partials; int npart;
     const float *rscale;
+    float eps;
 };
 
 __device__ inline float tensor_scale(const QArgs &a, float *sh) {
@@ -276,11 +277,41 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(QArgs a) {
 // written its slots, so the epochs stay in step.
 constexpr int kSmallPer = 4;
 constexpr int kSmallMaxG = 64;
+constexpr int64_t kRowsMaxK = 16384;           // row kernel: the row (f32) in LDS
 
 template <typename T>
 __device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 template <typename T>
 __device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// This call's epoch, read by wave 0 at the start of the kernel.
+__device__ inline unsigned slot_epoch(const unsigned long long *slot) {
+    return (unsigned)(ld_dev(&slot[blockIdx.x]) >> 32) + 1u;
+}
+
+// Arrival of workgroup blockIdx.x < G <= 64 with partial m (after block_max:
+// the same in every thread). Wave 0 writes the slots and waits; the grid
+// maximum is returned in every thread, and *sh_ok says whether the wait
+// completed (0: it gave up after `spin` polls, the caller recomputes).
+__device__ inline float slot_max(unsigned long long *slot, int G, unsigned ep, float m, unsigned spin,
+                                 float *sh, int *sh_ok) {
+    if (threadIdx.x < 64) {                    // wave 0: lane l owns slot l
+        const int l = threadIdx.x;
+        if (l % G == (int)blockIdx.x) st_dev(&slot[l], (unsigned long long)ep << 32 | __float_as_uint(m));
+        unsigned long long sv = ld_dev(&slot[l]);
+        unsigned it = 0;
+        int ok = 1;
+        while (!__all((unsigned)(sv >> 32) == ep)) {
+            if (++it > spin) { ok = 0; break; }
+            __builtin_amdgcn_s_sleep(2);
+            sv = ld_dev(&slot[l]);
+        }
+        const float pm = wave_max(__uint_as_float((unsigned)sv));
+        if (l == 0) { *sh_ok = ok; sh[0] = pm; }
+    }
+    __syncthreads();
+    return sh[0];
+}
 
 template <int XT>
 __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsigned long long *slot, int G,
@@ -292,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
     // this call's epoch, read ahead of the data (its latency overlaps theirs)
     const bool arrive = !a.static_S && G > 1;
     unsigned ep = 0;
-    if (arrive && threadIdx.x < 64) ep = (unsigned)(ld_dev(&slot[blockIdx.x]) >> 32) + 1u;
+    if (arrive && threadIdx.x < 64) ep = slot_epoch(slot);
     float v[kSmallPer][16];
     float m = 0.0f;
 #pragma unroll
@@ -311,26 +342,9 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
     } else {
         m = block_max(m, sh);
         if (arrive) {
-            if (threadIdx.x < 64) {            // wave 0: lane l owns slot l
-                const int l = threadIdx.x;
-                if (l % G == (int)blockIdx.x)
-                    st_dev(&slot[l], (unsigned long long)ep << 32 | __float_as_uint(m));
-                unsigned long long sv = ld_dev(&slot[l]);
-                unsigned it = 0;
-                int ok = 1;
-                while (!__all((unsigned)(sv >> 32) == ep)) {
-                    if (++it > spin) { ok = 0; break; }
-                    __builtin_amdgcn_s_sleep(2);
-                    sv = ld_dev(&slot[l]);
-                }
-                const float pm = wave_max(__uint_as_float((unsigned)sv));
-                if (l == 0) { sh_ok = ok; sh[0] = pm; }
-            }
-            __syncthreads();
-            float mm = 0.0f;
-            if (sh_ok) {
-                mm = sh[0];
-            } else {                           // the wait gave up: all of X here
+            float mm = slot_max(slot, G, ep, m, spin, sh, &sh_ok);
+            if (!sh_ok) {
+                mm = 0.0f;                           // the wait gave up: all of X here
                 for (int64_t b = threadIdx.x; b < NB; b += kThreads) {
                     const int64_t row = b / KB, blk = b - row * KB;
                     float w[16];
@@ -365,6 +379,105 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
                 a.scales[row * a.lds + KB + blk] = (uint8_t)rdb;
             }
         }
+    }
+}
+
+// ------------------------------------------- few rows with RMSNorm / reorder
+// Rows <= 64 with RMSNorm and/or the calibration reorder, in one launch of one
+// workgroup per row: the row, normalized, goes to LDS (the FP64 sum of squares
+// in the order of row_rms_scale), its maximum meets the other rows' in the slot
+// arrival, then each thread gathers a 16-column block through perm and encodes
+// it (and its residue block below res_cols). A workgroup whose wait gives up
+// recomputes every row's maximum itself (same values, same result).
+// Column c sits at rowbuf[(c % 16) KB + c / 16]: a thread's 16 columns are 16
+// rows of that table, so the lanes of a wave touch consecutive words.
+template <int XT, bool NORM, bool PERM>
+__global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QArgs a, unsigned long long *slot, unsigned spin) {
+    extern __shared__ float rowbuf[];
+    __shared__ float sh[kThreads / 64];
+    __shared__ double shd[kThreads / 64];
+    __shared__ int sh_ok;
+    const int G = (int)gridDim.x;
+    const int64_t row = blockIdx.x, K = a.K_in, KB = K / 16;
+    const bool arrive = !a.static_S && G > 1;
+    unsigned ep = 0;
+    if (arrive && threadIdx.x < 64) ep = slot_epoch(slot);
+    double ss = 0.0;
+    float m = 0.0f;
+    for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
+        float v[16];
+        load16<XT>(a.x, row * a.ldx + 16 * b, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (NORM) ss += (double)v[i] * (double)v[i];
+            else m = fmaxf(m, fabsf(v[i]));
+            rowbuf[i * KB + b] = v[i];
+        }
+    }
+    if (NORM) {
+        ss = block_sum_d(ss, shd);
+        const float r = (float)(1.0 / sqrt(ss / (double)K + (double)a.eps));
+        for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
+            float g[16];
+            gamma16(a.gamma, 16 * b, g);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float y = rowbuf[i * KB + b] * r;
+                y = y * g[i];
+                rowbuf[i * KB + b] = y;
+                m = fmaxf(m, fabsf(y));
+            }
+        }
+    }
+    m = block_max(m, sh);                      // also: the row is complete in LDS
+    float S;
+    if (a.static_S) {
+        S = *a.static_S;
+    } else {
+        if (arrive) {
+            float mm = slot_max(slot, G, ep, m, spin, sh, &sh_ok);
+            if (!sh_ok) {                      // the wait gave up: every row here
+                mm = 0.0f;
+                for (int64_t rr = 0; rr < a.rows; ++rr) {
+                    float rs = 1.0f;
+                    if (NORM) rs = row_rms_scale<XT>(a.x, rr, K, a.ldx, a.eps, shd);
+                    for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
+                        float v[16], g[16];
+                        load16<XT>(a.x, rr * a.ldx + 16 * b, v);
+                        if (NORM) gamma16(a.gamma, 16 * b, g);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            float y = v[i];
+                            if (NORM) { y = y * rs; y = y * g[i]; }
+                            mm = fmaxf(mm, fabsf(y));
+                        }
+                    }
+                }
+            }
+            m = block_max(mm, sh);
+        }
+        S = m > 0.0f ? m / 2688.0f : 1.0f;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.S_out = S;
+    const float t = 6.0f * S;
+    for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
+        float v[16];
+        if (PERM) {
+            const int4 *pp = reinterpret_cast<const int4 *>(a.perm + 16 * b);
+            const int4 p4[4] = {pp[0], pp[1], pp[2], pp[3]};
+            const int32_t pi[16] = {p4[0].x, p4[0].y, p4[0].z, p4[0].w, p4[1].x, p4[1].y, p4[1].z, p4[1].w,
+                                    p4[2].x, p4[2].y, p4[2].z, p4[2].w, p4[3].x, p4[3].y, p4[3].z, p4[3].w};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                // indices outside [0, K) are clamped so a bad permutation cannot leave the row
+                const int32_t c = pi[i] < 0 ? 0 : (pi[i] >= K ? (int32_t)(K - 1) : pi[i]);
+                v[i] = rowbuf[(c & 15) * KB + (c >> 4)];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = rowbuf[i * KB + b];
+        }
+        process_group(a, v, 1, row, 16 * b, S, t);
     }
 }
 
@@ -464,6 +577,23 @@ int amax_grid(int64_t rows, int64_t K) {
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
     const bool norm = q.gamma != nullptr, perm = q.perm != nullptr;
     const int64_t nb = q.rows * (q.K_in / 16);
+    if ((norm || perm) && q.slots && q.rows >= 1 && q.rows <= kSmallMaxG && q.K_in > 0 && q.K_in <= kRowsMaxK) {
+        QArgs a;
+        a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
+        a.gamma = q.gamma; a.perm = q.perm; a.res_cols = q.res_cols; a.static_S = q.static_S;
+        a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
+        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps;
+        const size_t lds = (size_t)q.K_in * sizeof(float);
+        const int g = (int)q.rows;
+#define QR(XT, NM, PM) quantize_rows_kernel<XT, NM, PM><<<g, kThreads, lds, st>>>(a, q.slots, q.spin)
+        if (q.xt == IN_BF16) {
+            if (norm && perm) QR(IN_BF16, true, true); else if (norm) QR(IN_BF16, true, false); else QR(IN_BF16, false, true);
+        } else {
+            if (norm && perm) QR(IN_F32, true, true); else if (norm) QR(IN_F32, true, false); else QR(IN_F32, false, true);
+        }
+#undef QR
+        return hipGetLastError();
+    }
     if (!norm && !perm && q.slots && q.rows <= 32 && nb > 0 && nb <= (int64_t)kSmallMaxG * kThreads * kSmallPer) {
         int G = (int)((nb + kThreads - 1) / kThreads);
         if (G > kSmallMaxG) G = kSmallMaxG;
@@ -471,7 +601,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
         a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
         a.gamma = nullptr; a.perm = nullptr; a.res_cols = q.res_cols; a.static_S = q.static_S;
         a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
-        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale;
+        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps;
         if (q.xt == IN_BF16)
             quantize_small_kernel<IN_BF16><<<G, kThreads, 0, st>>>(a, q.slots, G, q.spin);
         else
@@ -508,7 +638,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
     a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
     a.gamma = q.gamma; a.perm = q.perm; a.res_cols = q.res_cols; a.static_S = q.static_S;
     a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
-    a.partials = q.partials; a.npart = npart; a.rscale = q.rscale;
+    a.partials = q.partials; a.npart = npart; a.rscale = q.rscale; a.eps = q.eps;
 
     if (perm) {
         const int g = (int)(q.rows < 2048 ? (q.rows > 0 ? q.rows : 1) : 2048);

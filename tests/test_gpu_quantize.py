@@ -175,3 +175,31 @@ def test_small_quantizer_wait_fallback(nv, orc, rows, K, S, monkeypatch):
     torch.cuda.synchronize()
     monkeypatch.delenv("NVFP4_SPIN_LIMIT")
     assert_qtensor_equal(q1, ox, "fallback")
+
+
+@pytest.mark.parametrize("rows,norm,use_perm,S", [(64, True, True, 256), (7, True, True, 0), (1, True, False, 64),
+                                                  (33, False, True, 512)])
+def test_rows_quantizer_wait_fallback(nv, orc, rows, norm, use_perm, S, monkeypatch):
+    """The one-launch quantizer of <= 64 rows with RMSNorm and/or reorder (one
+    workgroup per row), normally and with its grid-wide arrival forced to give
+    up at once (spin limit 0, set from the host): every workgroup then
+    recomputes each row's maximum itself. Codes must equal the oracle's."""
+    x, g, xcal, _ = inputs.outlier_aug(rows=64, N=16, cal_rows=64)
+    x = x[:rows].contiguous()
+    perm = orc.perm_from_absmax(orc.channel_absmax(xcal, g, 1e-6)) if use_perm else None
+    kw = dict(residue_cols=S)
+    if norm:
+        kw.update(gamma=g.to(DEV), eps=1e-6)
+    if use_perm:
+        kw.update(perm=torch.from_numpy(perm).to(DEV))
+    ref = orc.quantize_aug(x, gamma=g if norm else None, eps=1e-6, perm=perm, S_cols=S)
+    note(f"row quantizer rows={rows} norm={norm} perm={use_perm} S={S}: normal")
+    q0 = nv.quantize(x.to(DEV), **kw)
+    torch.cuda.synchronize()
+    assert_qtensor_equal(q0, ref, "normal")
+    monkeypatch.setenv("NVFP4_SPIN_LIMIT", "0")
+    note(f"row quantizer rows={rows} norm={norm} perm={use_perm} S={S}: fallback")
+    q1 = nv.quantize(x.to(DEV), **kw)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("NVFP4_SPIN_LIMIT")
+    assert_qtensor_equal(q1, ref, "fallback")
