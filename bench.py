@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--roofline-only", action="store_true",
                     help="run only the kernel-alone leg behind the roofline figure (for profiling: then every "
                          "decode-kernel launch of the process belongs to that figure, equally per case)")
+    ap.add_argument("--prefill-case", default="",
+                    help="M,K,N: run only the prefill product on pre-quantized activations, --reps launches "
+                         "(for profiling the MFMA kernel; prints one line with its time)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -154,6 +157,10 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
+
+    if args.prefill_case:
+        prefill_case(nvfp4, dev, args.layout == "tiled", [int(v) for v in args.prefill_case.split(",")], args.reps)
+        return
 
     # ---------------- inputs, resident in HBM
     shapes = inputs.DECODE_SHAPES
@@ -361,6 +368,33 @@ def extra_detail(nvfp4, dev, tiled):
         del xall, wq, aq_cache
         torch.cuda.empty_cache()
     return res
+
+
+def prefill_case(nvfp4, dev, tiled, mkn, reps):
+    """One prefill shape, kernel-alone (activations quantized before), `reps` launches."""
+    M, K, N = mkn
+    torch.manual_seed(0)
+    x = torch.randn((M, K), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn((N, K), device=dev, dtype=torch.float32) * 0.015).to(torch.bfloat16)
+    wq = nvfp4.quantize(w)
+    if tiled:
+        wq = nvfp4.pack_tiled(wq)
+    del w
+    aq = nvfp4.quantize(x)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    nvfp4.gemm(aq, wq, out=y)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        nvfp4.gemm(aq, wq, out=y)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / max(reps, 1)
+    flops = 2.0 * M * N * K
+    print(json.dumps({"prefill_case": [M, K, N], "reps": reps, "us_per_call": round(us, 1),
+                      "TFLOPs": round(flops / us / 1e6, 1),
+                      "frac_f16_mfma": round(flops / us / 1e6 / F16_MFMA_PEAK_TFLOPS, 4)}), flush=True)
 
 
 def cpu_baseline(budget_s: float):
