@@ -366,7 +366,9 @@ __device__ inline void zero_unwritten(half8 *lds, const DArgs &a, const Range &r
 }
 
 // ---------------------------------------------------------------- kernel
-template <int MT, bool RES, bool TILED, bool REFILL>
+// STK: residue rows stacked under the activation rows (RES, MT == 1, M <= 8);
+// an instance of its own, so that its MFMA loop carries no residue branch.
+template <int MT, bool RES, bool TILED, bool REFILL, bool STK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
     constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
@@ -588,7 +590,7 @@ void decode_kernel(DArgs a) {
         float4v v[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) v[mt] = vin[mt];
-        if (RES && MT == 1 && a.Mp) {
+        if (STK) {
             // stacked residue (MT == 1): output row m += row Mp + m. Row 4 g + e sits
             // in lane group g, element e; Mp >= 4 puts the residue row in lane + 4 Mp.
             const int mp = a.Mp;
@@ -631,7 +633,7 @@ void decode_kernel(DArgs a) {
     if (wave < kCons && nitems > 0) {            // waves without items issue no loads at all
         // independent MFMA chains: even / odd fragments, and (MT == 1; for MT == 2 the
         // registers are not there) the residue columns' own two
-        constexpr bool kSepRes = RES && MT == 1;
+        constexpr bool kSepRes = RES && !STK && MT == 1;
         float4v acc[MT], acc2[MT], accr[1], accr2[1];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) { acc[mt] = float4v{0, 0, 0, 0}; acc2[mt] = float4v{0, 0, 0, 0}; }
@@ -655,7 +657,7 @@ void decode_kernel(DArgs a) {
                 if (it < nitems) {
                     const int ul = uo + KW * bu;
                     const half8 *abase = lds_a + ul * 64 * R + g * R;
-                    const bool res_u = RES && !a.Mp && ul < res_units;   // a separate residue copy
+                    const bool res_u = RES && !STK && ul < res_units;   // a separate residue copy
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t sw = (i < 2) ? ring[s].s.x : ring[s].s.y;
@@ -984,16 +986,19 @@ int cu_count() {
 }
 
 template <bool TILED, bool REFILL>
-const void *kernel_ptr_t(int MT, bool res) {
-    if (MT == 1) return res ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL>)
-                            : reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, REFILL>);
-    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL>)
-               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL>);
+const void *kernel_ptr_t(int MT, bool res, bool stk) {
+    if (MT == 1) {
+        if (!res) return reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, REFILL, false>);
+        return stk ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL, true>)
+                   : reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL, false>);
+    }
+    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL, false>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL, false>);
 }
 
-const void *kernel_ptr(int MT, bool res, bool tiled, bool refill) {
-    if (tiled) return refill ? kernel_ptr_t<true, true>(MT, res) : kernel_ptr_t<true, false>(MT, res);
-    return refill ? kernel_ptr_t<false, true>(MT, res) : kernel_ptr_t<false, false>(MT, res);
+const void *kernel_ptr(int MT, bool res, bool tiled, bool refill, bool stk) {
+    if (tiled) return refill ? kernel_ptr_t<true, true>(MT, res, stk) : kernel_ptr_t<true, false>(MT, res, stk);
+    return refill ? kernel_ptr_t<false, true>(MT, res, stk) : kernel_ptr_t<false, false>(MT, res, stk);
 }
 
 // Work split of one call. A K range of U units (P ranges) costs its operand in
@@ -1153,7 +1158,8 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.partials = static_cast<float *>(g.scratch);
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.KW = pl.KW; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
     a.Rr = pl.Rr; a.Mp = pl.Mp; a.ordered = pl.ordered ? 1 : 0;
-    const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill);
+    // stacking (Mp > 0) exists for MT == 1 with residue columns only
+    const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill, pl.Mp > 0);
     if (pl.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
         if (e != hipSuccess) return e;
