@@ -366,8 +366,9 @@ __device__ inline void zero_unwritten(half8 *lds, const DArgs &a, const Range &r
 }
 
 // ---------------------------------------------------------------- kernel
-// STK: residue rows stacked under the activation rows (RES, MT == 1, M <= 8);
-// an instance of its own, so that its MFMA loop carries no residue branch.
+// STK: residue rows stacked under the activation rows (RES; M <= 8 in one row
+// tile, or M = 9..16 as a second row tile); an instance of its own, so that its
+// MFMA loop carries no residue branch.
 template <int MT, bool RES, bool TILED, bool REFILL, bool STK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
@@ -590,7 +591,10 @@ void decode_kernel(DArgs a) {
         float4v v[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) v[mt] = vin[mt];
-        if (STK) {
+        if constexpr (STK && MT == 2) {
+            // stacked residue, M = 9..16: the residue rows are the second row tile
+            v[0] += v[MT - 1];
+        } else if constexpr (STK) {
             // stacked residue (MT == 1): output row m += row Mp + m. Row 4 g + e sits
             // in lane group g, element e; Mp >= 4 puts the residue row in lane + 4 Mp.
             const int mp = a.Mp;
@@ -992,8 +996,9 @@ const void *kernel_ptr_t(int MT, bool res, bool stk) {
         return stk ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL, true>)
                    : reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL, false>);
     }
-    return res ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL, false>)
-               : reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL, false>);
+    if (!res) return reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL, false>);
+    return stk ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL, true>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL, false>);
 }
 
 const void *kernel_ptr(int MT, bool res, bool tiled, bool refill, bool stk) {
@@ -1011,15 +1016,18 @@ const void *kernel_ptr(int MT, bool res, bool tiled, bool refill, bool stk) {
 // costs three dependent round trips through the memory system.
 Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
     Plan pl;
-    pl.MT = M <= 16 ? 1 : 2;
     const bool res = res_cols > 0;
+    // operand rows: residue rows stacked under the activation rows when M <= 8,
+    // and as a second row tile for M = 9..16 when they cover at least half of K
+    // (below that the stacked tile would multiply mostly zero rows)
+    pl.Mp = 0;
+    if (res && M <= 8) { pl.Mp = 1; while (pl.Mp < M) pl.Mp *= 2; }
+    else if (res && M <= 16 && 2 * res_cols >= K) pl.Mp = 16;
+    pl.MT = (M <= 16 && pl.Mp < 16) ? 1 : 2;
     const int ring = pl.MT == 1 ? 4 : 3;
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
     const int ncu = cu_count();
-    // operand rows: residue rows stacked under the activation rows when M <= 8
-    pl.Mp = 0;
-    if (res && M <= 8) { pl.Mp = 1; while (pl.Mp < M) pl.Mp *= 2; }
     pl.Rr = pl.Mp ? 2 * pl.Mp : (int)M;
     const int64_t op_rows = pl.Mp ? 2 * pl.Mp : (res ? 2 * M : M);   // rows of operand per unit
     double best = 1e30;
@@ -1158,7 +1166,7 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.partials = static_cast<float *>(g.scratch);
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.KW = pl.KW; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
     a.Rr = pl.Rr; a.Mp = pl.Mp; a.ordered = pl.ordered ? 1 : 0;
-    // stacking (Mp > 0) exists for MT == 1 with residue columns only
+    // stacking (Mp > 0) exists with residue columns only
     const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill, pl.Mp > 0);
     if (pl.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);

@@ -142,7 +142,8 @@ def test_prefill_sampled(nv, orc, shape_idx):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 15, 48), (16, 47, 528), (17, 300, 1040), (33, 64, 528),
-                                   (64, 130, 272), (65, 47, 1040), (130, 300, 528), (5, 1000, 4112)])
+                                   (64, 130, 272), (65, 47, 1040), (130, 300, 528), (5, 1000, 4112),
+                                   (12, 200, 512), (12, 300, 1040)])
 @pytest.mark.parametrize("S_frac", [0, 1])
 def test_ragged_products(nv, orc, M, N, K, S_frac):
     x = inputs.small_random(M * 7 + K, M, K)
