@@ -1083,7 +1083,11 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     const int64_t kc = (int64_t)pl.U * 512 < K ? (int64_t)pl.U * 512 : K;
     const int64_t step = M > 0 ? kPThreads / M : 1;   // chunk positions per pass (prod_map)
     const int64_t per_thread = ((kc + 31) / 32 + step - 1) / step;
-    pl.mode = (raw_x && !norm_or_perm && per_thread <= kLocalChunks && M * K <= kLocalMaxElems)
+    // The quantization arithmetic of LOCAL runs on the four producer waves of
+    // every workgroup; residue columns double it (a second block encoded per
+    // block), so they count twice against the same bound.
+    const int64_t local_work = per_thread * (res_cols > 0 ? 2 : 1);
+    pl.mode = (raw_x && !norm_or_perm && local_work <= kLocalChunks && M * K <= kLocalMaxElems)
                   ? MODE_LOCAL : MODE_PRE;
     // PRE producers with more than one chunk per thread put enough loads in the
     // CU's queue that the operand lands late behind the consumers' first items;
