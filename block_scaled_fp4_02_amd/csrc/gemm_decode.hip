@@ -369,7 +369,7 @@ __device__ inline void zero_unwritten(half8 *lds, const DArgs &a, const Range &r
 // STK: residue rows stacked under the activation rows (RES; M <= 8 in one row
 // tile, or M = 9..16 as a second row tile); an instance of its own, so that its
 // MFMA loop carries no residue branch.
-template <int MT, bool RES, bool TILED, bool REFILL, bool STK>
+template <int MT, bool RES, bool TILED, bool STK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
     constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
@@ -413,15 +413,18 @@ void decode_kernel(DArgs a) {
     const int nitems = ntw * nuw;
     // Item it = (tile i_t = it / nuw, unit i_u = it % nuw); tiles and rows are
     // clamped into W, so loads never leave it.
-    auto load_item = [&](int it, WLoad &w) {
+    // spare: a ring slot past the wave's last item still takes the same five
+    // loads (so vmcnt counts stay exact), every lane from W's first bytes: one
+    // line per load, a cache hit after the first
+    auto load_item = [&](int it, WLoad &w, bool spare) {
         const int at = it / nuw, bu = it - at * nuw;
         const int64_t t = t_lo + tg + (int64_t)TW * at;
         const int64_t ul = uo + (int64_t)KW * bu;
         if (TILED) {
-            load_w_tiled(a, t < a.NT ? t : a.NT - 1, kbeg / 512 + ul, lane, w);
+            load_w_tiled(a, spare ? 0 : (t < a.NT ? t : a.NT - 1), spare ? 0 : kbeg / 512 + ul, spare ? 0 : lane, w);
         } else {
             const int64_t n = 16 * t + r16;
-            load_w(a, n < a.N ? n : a.N - 1, kbeg + 512 * ul, g, w);
+            load_w(a, spare ? 0 : (n < a.N ? n : a.N - 1), spare ? 0 : kbeg + 512 * ul, spare ? 0 : g, w);
         }
     };
 
@@ -440,7 +443,7 @@ void decode_kernel(DArgs a) {
         if (a.ordered) __syncthreads();
         if (nitems > 0) {
 #pragma unroll
-            for (int s = 0; s < kPre; ++s) load_item(s < nitems ? s : nitems - 1, ring[s]);
+            for (int s = 0; s < kPre; ++s) load_item(s < nitems ? s : 0, ring[s], s >= nitems);
         }
         TL(1);
         __syncthreads();                       // operand complete
@@ -644,14 +647,14 @@ void decode_kernel(DArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 1; ++mt) { accr[mt] = float4v{0, 0, 0, 0}; accr2[mt] = float4v{0, 0, 0, 0}; }
 #pragma unroll
-        for (int s = kPre; s < kRing; ++s) load_item(s < nitems ? s : nitems - 1, ring[s]);
-        // Fully unrolled over NI items (no loop back-edge), NI = kRing when the
-        // plan's items per wave fit the ring (no refills at all; a kernel of its
-        // own, so the two loop shapes never share a register allocation) and
-        // kMaxItems otherwise: each slot is consumed in place and refilled right
-        // after, always with the same five loads (past the last item -- only in
-        // ragged waves -- it re-reads the current one), so vmcnt is tracked
-        // exactly and the common plans issue no redundant loads.
+        for (int s = kPre; s < kRing; ++s) load_item(s < nitems ? s : 0, ring[s], s >= nitems);
+        // Fully unrolled over NI = kMaxItems items (no loop back-edge): each slot
+        // is consumed in place and refilled right after, always with the same
+        // five loads (spare ones past the wave's last item), so vmcnt is tracked
+        // exactly. One loop shape serves every plan: a second instance for plans
+        // whose items fit the ring saved its spare loads but cost ~2 us at every
+        // switch between the two instances in a sequence of calls (their code is
+        // fetched again), more than it saved.
         auto run = [&](auto ni) {
             constexpr int NI = decltype(ni)::value;
             int at = 0, bu = 0;                    // tile and unit of the current item (wave-uniform)
@@ -713,13 +716,13 @@ void decode_kernel(DArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);   // items stay in order (no hoisted decodes)
                 if (it + kRing < NI) {
-                    const int nx = it + kRing < nitems ? it + kRing : (it < nitems ? it : nitems - 1);
-                    load_item(nx, ring[s]);          // consume slot s, then refill it
+                    const bool spare = it + kRing >= nitems;
+                    load_item(spare ? 0 : it + kRing, ring[s], spare);   // consume slot s, then refill it
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
-        run(std::integral_constant<int, REFILL ? kMaxItems : kRing>{});
+        run(std::integral_constant<int, kMaxItems>{});
     }
 
     // ---- tiles shared by KW waves: their parts are added in LDS, in wave order
@@ -971,7 +974,7 @@ void decode_win_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------- planning
-struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool refill, ordered; int64_t NT, Q; size_t lds; };
+struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool ordered; int64_t NT, Q; size_t lds; };
 
 constexpr size_t kLdsPerCu = 160 * 1024;       // gfx950
 constexpr size_t kLdsStatic = 256;             // the kernel's own __shared__ words, rounded up
@@ -989,21 +992,20 @@ int cu_count() {
     return cus;
 }
 
-template <bool TILED, bool REFILL>
+template <bool TILED>
 const void *kernel_ptr_t(int MT, bool res, bool stk) {
     if (MT == 1) {
-        if (!res) return reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, REFILL, false>);
-        return stk ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL, true>)
-                   : reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, REFILL, false>);
+        if (!res) return reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, false>);
+        return stk ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, true>)
+                   : reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, false>);
     }
-    if (!res) return reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, REFILL, false>);
-    return stk ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL, true>)
-               : reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, REFILL, false>);
+    if (!res) return reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, false>);
+    return stk ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, true>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, false>);
 }
 
-const void *kernel_ptr(int MT, bool res, bool tiled, bool refill, bool stk) {
-    if (tiled) return refill ? kernel_ptr_t<true, true>(MT, res, stk) : kernel_ptr_t<true, false>(MT, res, stk);
-    return refill ? kernel_ptr_t<false, true>(MT, res, stk) : kernel_ptr_t<false, false>(MT, res, stk);
+const void *kernel_ptr(int MT, bool res, bool tiled, bool stk) {
+    return tiled ? kernel_ptr_t<true>(MT, res, stk) : kernel_ptr_t<false>(MT, res, stk);
 }
 
 // Work split of one call. A K range of U units (P ranges) costs its operand in
@@ -1024,7 +1026,6 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     if (res && M <= 8) { pl.Mp = 1; while (pl.Mp < M) pl.Mp *= 2; }
     else if (res && M <= 16 && 2 * res_cols >= K) pl.Mp = 16;
     pl.MT = (M <= 16 && pl.Mp < 16) ? 1 : 2;
-    const int ring = pl.MT == 1 ? 4 : 3;
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
     const int ncu = cu_count();
@@ -1077,7 +1078,6 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
         const size_t red = pl.KW > 1 ? (size_t)8192 * pl.MT : 0;
         pl.lds = ((lds_a > red ? lds_a : red) + 255) / 256 * 256;
     }
-    pl.refill = (int64_t)pl.tw * ((pl.U + pl.KW - 1) / pl.KW) > ring;
     // Raw activations are quantized in the kernel only when every workgroup can
     // read all of X and each producer thread holds at most kLocalChunks chunks.
     const int64_t kc = (int64_t)pl.U * 512 < K ? (int64_t)pl.U * 512 : K;
@@ -1097,8 +1097,8 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     pl.ordered = pl.mode == MODE_LOCAL || pre_per_thread > 1;
     if (std::getenv("NVFP4_DEBUG_PLAN"))
         std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d KW=%d T=%d G=%d "
-                     "lds=%zu refill=%d mode=%d ordered=%d cost=%.2f\n", (long long)M, (long long)N, (long long)K,
-                     (long long)res_cols, pl.MT, pl.U, pl.P, pl.KW, pl.T, pl.G, pl.lds, (int)pl.refill, pl.mode, (int)pl.ordered, best);
+                     "lds=%zu mode=%d ordered=%d cost=%.2f\n", (long long)M, (long long)N, (long long)K,
+                     (long long)res_cols, pl.MT, pl.U, pl.P, pl.KW, pl.T, pl.G, pl.lds, pl.mode, (int)pl.ordered, best);
     return pl;
 }
 
@@ -1171,7 +1171,7 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.KW = pl.KW; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
     a.Rr = pl.Rr; a.Mp = pl.Mp; a.ordered = pl.ordered ? 1 : 0;
     // stacking (Mp > 0) exists with residue columns only
-    const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.refill, pl.Mp > 0);
+    const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.Mp > 0);
     if (pl.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
         if (e != hipSuccess) return e;
