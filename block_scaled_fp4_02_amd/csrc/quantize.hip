@@ -275,7 +275,9 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(QArgs a) {
 // (slots l >= G repeat a real partial). The wait is bounded; a workgroup whose
 // wait gives up recomputes amax(X) itself (same result), and it has still
 // written its slots, so the epochs stay in step.
-constexpr int kSmallPer = 4;
+constexpr int kSmallPer = 2;                   // blocks per thread: 2 keeps the kernel's code small
+                                               // (it alternates with the decode kernel in a call, and
+                                               // 4 cost ~4 us per 15-call sweep in code fetches)
 constexpr int kSmallMaxG = 64;
 constexpr int64_t kRowsMaxK = 16384;           // row kernel: the row (f32) in LDS
 
