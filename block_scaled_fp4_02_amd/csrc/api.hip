@@ -31,9 +31,13 @@ constexpr size_t kAlign = 256;
 inline size_t up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// The skinny (decode) path takes M up to this many rows; larger M is tiled.
+// The skinny (decode) path takes M up to this many rows; larger M is tiled, and
+// so are products with residue columns when K is not a multiple of 32 (the
+// decode kernels load the residue part in 16-byte chunks from column K).
 constexpr int64_t kSkinnyMaxM = 64;
-inline bool skinny_rows(int64_t M, int64_t K, int64_t) { return K > 0 && M <= kSkinnyMaxM; }
+inline bool skinny_rows(int64_t M, int64_t K, int64_t S) {
+    return K > 0 && M <= kSkinnyMaxM && (S == 0 || K % 32 == 0);
+}
 
 int64_t ldc_for(int64_t K) { return (int64_t)up((size_t)(K / 2), 16); }
 int64_t lds_for(int64_t K) { return (int64_t)up((size_t)(K / 16), 8); }

@@ -214,42 +214,29 @@ __device__ inline ChunkPos chunk_at(const DArgs &a, const Range &r, int m, int p
 
 // A chunk of the quantized-activation buffer: 16 bytes of codes (low nibble =
 // even column) and the two block scales.
-struct QChunk { uint4 c; uint16_t s; uint8_t s1; int key; };   // s: both scales (no residue), else the first; s1: the second
+struct QChunk { uint4 c; uint16_t s; int key; };   // s: the two block scales
 
-// Without residue columns every chunk starts at a multiple of 32 columns: one
-// 16-byte and one 2-byte load. Row-major rows hold at least K/2 bytes of codes
-// and K/16 of scales, padded to multiples of 16 and 8, so both stay inside the
-// row's pitch even where the second block lies past the data (those bytes are
-// dropped when stored). Residue chunks start at column K + kc, only 8-byte
-// aligned when K is an odd multiple of 16, so with residue columns every chunk
-// takes two 8-byte and two 1-byte loads, the second of each only inside the
-// data (one code path: a branch on alignment would diverge within a wave).
-// Past the list it reads the row's start (dropped when stored).
-template <bool RES>
+// Every chunk starts at a multiple of 32 columns -- residue chunks at column
+// K + kc, and the host sends residue columns here only when K is a multiple of
+// 32 -- so a chunk is one 16-byte and one 2-byte load. Row-major rows hold at
+// least as many bytes as their columns need, padded to multiples of 16 (codes)
+// and 8 (scales), so both loads stay inside the row's pitch even where the
+// second block lies past the data (those bytes are dropped when stored). Past
+// the list it reads the row's start (dropped when stored).
 __device__ inline QChunk qchunk_load(const uint8_t *crow, const uint8_t *srow, const ChunkPos &f) {
     QChunk q;
     q.key = f.key;
-    if (!RES) {
-        q.c = *reinterpret_cast<const uint4 *>(crow + (f.col >> 1));
-        q.s = *reinterpret_cast<const uint16_t *>(srow + (f.col >> 4));
-    } else {
-        const bool v1 = f.key >= 0 && (f.key & kV1);
-        const uint2 lo = *reinterpret_cast<const uint2 *>(crow + (f.col >> 1));
-        const uint2 hi = *reinterpret_cast<const uint2 *>(crow + (f.col >> 1) + (v1 ? 8 : 0));
-        q.c = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        q.s = srow[f.col >> 4];            // combined only when stored: no wait here
-        q.s1 = srow[(f.col >> 4) + (v1 ? 1 : 0)];
-    }
+    q.c = *reinterpret_cast<const uint4 *>(crow + (f.col >> 1));
+    q.s = *reinterpret_cast<const uint16_t *>(srow + (f.col >> 4));
     return q;
 }
 
 // Decode a chunk into its four fragments (j stride js = 4 R slots).
-template <bool RES>
 __device__ inline void qchunk_store(half8 *lds, int js, const QChunk &q) {
     if (q.key < 0) return;
     const bool v1 = q.key & kV1;
     const int slot = q.key & (kV1 - 1);
-    const uint32_t s0 = RES ? (uint32_t)q.s : q.s & 0xFFu, s1 = RES ? (uint32_t)q.s1 : (uint32_t)q.s >> 8;
+    const uint32_t s0 = q.s & 0xFFu, s1 = (uint32_t)q.s >> 8;
     const half2v d0 = scale_pair(s0), d1 = scale_pair(v1 ? s1 : 0u);
     lds[slot] = decode8(q.c.x, d0);
     lds[slot + js] = decode8(q.c.y, d0);
@@ -465,20 +452,20 @@ void decode_kernel(DArgs a) {
                 QChunk qc[kPreChunks];
 #pragma unroll
                 for (int t = 0; t < kPreChunks; ++t)
-                    qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * t, slots));
+                    qc[t] = qchunk_load(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * t, slots));
                 if (a.ordered) __syncthreads();    // loads out: consumers may issue theirs
                 // the two tensor scales (lane 0 of the first producer wave, which
                 // always holds chunks), after the batch is out
                 if (ptid == 0) { S = load_vmem(a.q_S); wS = load_vmem(a.w_S); }
                 zero_unwritten(lds_a, a, rg, slots);
 #pragma unroll
-                for (int t = 0; t < kPreChunks; ++t) qchunk_store<RES>(lds_a, 4 * R, qc[t]);
+                for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
                 for (int b = kPreChunks; pm.p0 + pm.step * b < npos; b += kPreChunks) {
 #pragma unroll
                     for (int t = 0; t < kPreChunks; ++t)
-                        qc[t] = qchunk_load<RES>(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * (b + t), slots));
+                        qc[t] = qchunk_load(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * (b + t), slots));
 #pragma unroll
-                    for (int t = 0; t < kPreChunks; ++t) qchunk_store<RES>(lds_a, 4 * R, qc[t]);
+                    for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
                 }
             } else {
                 if (a.ordered) __syncthreads();
@@ -827,7 +814,6 @@ __device__ inline QChunk win_chunk_load(const DArgs &a, int v, int KU, int c) {
     q.key = -1;
     q.c = make_uint4(0, 0, 0, 0);
     q.s = 0;
-    q.s1 = 0;
     const int m = c >> 4, p = c & 15;
     const bool resv = RES && v >= KU;
     const int64_t u = resv ? v - KU : v;
@@ -837,7 +823,7 @@ __device__ inline QChunk win_chunk_load(const DArgs &a, int v, int KU, int c) {
     if (m >= a.M) return q;
     if (kc < cend) {
         const ChunkPos f{(resv ? a.K : 0) + kc, ((p & 3) * 16 + (p >> 2)) * kWinRows + m + (kc + 16 < cend ? kV1 : 0)};
-        q = qchunk_load<RES>(a.q_codes + (int64_t)m * a.q_ldc, a.q_scales + (int64_t)m * a.q_lds, f);
+        q = qchunk_load(a.q_codes + (int64_t)m * a.q_ldc, a.q_scales + (int64_t)m * a.q_lds, f);
     } else {
         q.key = ((p & 3) * 16 + (p >> 2)) * kWinRows + m;               // past the data: a zero chunk
     }
@@ -945,7 +931,7 @@ void decode_win_kernel(DArgs a) {
         auto store_unit = [&](int v, const QChunk *q) {
             half8 *dst = lds_a + (v & 1) * SLOT;
 #pragma unroll
-            for (int i = 0; i < kWinChunks; ++i) qchunk_store<RES>(dst, 4 * R, q[i]);
+            for (int i = 0; i < kWinChunks; ++i) qchunk_store(dst, 4 * R, q[i]);
         };
         load_unit(0, q0);
         if (NV > 1) load_unit(1, q1);
@@ -1154,6 +1140,7 @@ hipError_t launch_decode_win(const DecodeLaunch &g, hipStream_t st) {
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     const bool raw = g.x != nullptr;
     if (g.M < 1 || g.M > 64 || g.N < 1 || g.K < 1) return hipErrorInvalidValue;   // the kernels' row bound
+    if (g.res_cols > 0 && g.K % 32 != 0) return hipErrorInvalidValue;          // residue chunks 16-byte aligned
     if (g.M > 32) return launch_decode_win(g, st);
     const Plan pl = plan_for(g.M, g.N, g.K, g.res_cols, raw, false);
     if (!plan_ok(pl) || (raw && pl.mode != MODE_LOCAL)) return hipErrorInvalidValue;
