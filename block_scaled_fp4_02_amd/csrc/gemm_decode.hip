@@ -14,15 +14,18 @@
 //  * a workgroup owns a K range of U 512-column units and T 16-row weight
 //    tiles; it has four consumer waves and four producer waves;
 //  * producer waves issue their (small) activation loads first; after one
-//    barrier the consumer waves issue the loads of their (tile, unit) items at
-//    once (a ring of up to 4 items: 4 x 16 B codes + 8 B scales per lane
-//    each), so the activation data is ahead of the weights in the CU's memory
-//    queue and the operand is ready long before the weights have landed;
+//    barrier (when producers hold more than one chunk per thread) the
+//    consumer waves issue the loads of their first (tile, unit) items (a ring
+//    of 4 items: 4 x 16 B codes + 8 B scales per lane each), so the
+//    activation data is ahead of the weights in the CU's memory queue;
 //  * producers write the K range's operand into LDS as exact f16 e*d values
 //    in A-operand lane order; consumers then decode each weight item in
 //    registers (v_cvt_scalef32_pk_f16_fp4 + v_pk_mul_f16, exact) and issue 16
 //    v_mfma_f32_16x16x32_f16 per item as items land, refilling the ring;
-//    residue columns reuse the decoded weight registers for a second MFMA;
+//    residue columns reuse the decoded weight registers: their rows are
+//    stacked under the activation rows (M <= 8, or M <= 16 when they cover at
+//    least half of K; the same MFMAs) or else multiplied by a separate operand
+//    copy in a second MFMA;
 //  * with more than one K range, partial tiles go to the workspace through
 //    device-coherent stores and the last workgroup of each tile group sums
 //    them in fixed order (deterministic) and writes y.
@@ -393,18 +396,25 @@ void decode_kernel(DArgs a) {
     // Consumer wave w takes tiles t_lo + w / KW + TW i_t (i_t < ntw) and units
     // w % KW + KW i_u (i_u < nuw) of the range: KW waves share each tile, each
     // summing its own units, and their parts are added in LDS at the end.
-    const int KW = a.KW, TW = kCons / KW;
-    const int tg = wave / KW, uo = wave % KW;
-    const int ntw = (wave < kCons && t_lo + tg < t_hi) ? (int)((t_hi - t_lo - tg + TW - 1) / TW) : 0;
-    const int nuw = (wave < kCons && uo < units) ? (units - uo + KW - 1) / KW : 0;
+    // KW is 1, 2 or 4: shifts and masks instead of divisions (a 64-bit
+    // division alone is ~130 scalar instructions ahead of the first load)
+    const int KW = a.KW, kwl = KW >> 1, TW = kCons >> kwl;
+    const int tg = wave >> kwl, uo = wave & (KW - 1);
+    const int nt_wg = (int)(t_hi - t_lo);
+    const int ntw = (wave < kCons && tg < nt_wg) ? (nt_wg - tg + TW - 1) >> (2 - kwl) : 0;
+    const int nuw = (wave < kCons && uo < units) ? (units - uo + KW - 1) >> kwl : 0;
     const int nitems = ntw * nuw;
-    // Item it = (tile i_t = it / nuw, unit i_u = it % nuw); tiles and rows are
-    // clamped into W, so loads never leave it.
+    // Item it = (tile i_t = it / nuw, unit i_u = it % nuw), it < kMaxItems (the
+    // quotient by comparisons: no division); tiles and rows are clamped into
+    // W, so loads never leave it.
     // spare: a ring slot past the wave's last item still takes the same five
     // loads (so vmcnt counts stay exact), every lane from W's first bytes: one
     // line per load, a cache hit after the first
     auto load_item = [&](int it, WLoad &w, bool spare) {
-        const int at = it / nuw, bu = it - at * nuw;
+        int at = 0;
+#pragma unroll
+        for (int k = 1; k < kMaxItems; ++k) at += it >= k * nuw ? 1 : 0;
+        const int bu = it - at * nuw;
         const int64_t t = t_lo + tg + (int64_t)TW * at;
         const int64_t ul = uo + (int64_t)KW * bu;
         if (TILED) {
