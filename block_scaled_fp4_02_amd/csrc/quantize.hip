@@ -576,6 +576,13 @@ int amax_grid(int64_t rows, int64_t K) {
 
 }  // namespace
 
+// A row staged in LDS takes K_in floats (up to 64 KiB): above 48 KiB of
+// dynamic LDS the kernel's limit is raised first (gfx950 has 160 KiB per CU).
+static hipError_t allow_lds(const void *fn, size_t lds) {
+    if (lds <= 48 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
     const bool norm = q.gamma != nullptr, perm = q.perm != nullptr;
     const int64_t nb = q.rows * (q.K_in / 16);
@@ -587,7 +594,12 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
         a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps;
         const size_t lds = (size_t)q.K_in * sizeof(float);
         const int g = (int)q.rows;
-#define QR(XT, NM, PM) quantize_rows_kernel<XT, NM, PM><<<g, kThreads, lds, st>>>(a, q.slots, q.spin)
+#define QR(XT, NM, PM)                                                                              \
+    do {                                                                                            \
+        const hipError_t e_ = allow_lds(reinterpret_cast<const void *>(&quantize_rows_kernel<XT, NM, PM>), lds); \
+        if (e_ != hipSuccess) return e_;                                                            \
+        quantize_rows_kernel<XT, NM, PM><<<g, kThreads, lds, st>>>(a, q.slots, q.spin);             \
+    } while (0)
         if (q.xt == IN_BF16) {
             if (norm && perm) QR(IN_BF16, true, true); else if (norm) QR(IN_BF16, true, false); else QR(IN_BF16, false, true);
         } else {
@@ -645,7 +657,12 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
     if (perm) {
         const int g = (int)(q.rows < 2048 ? (q.rows > 0 ? q.rows : 1) : 2048);
         const size_t lds = (size_t)q.K_in * sizeof(float);
-#define QP(XT, NM) quantize_perm_kernel<XT, NM><<<g, kThreads, lds, st>>>(a)
+#define QP(XT, NM)                                                                                  \
+    do {                                                                                            \
+        const hipError_t e_ = allow_lds(reinterpret_cast<const void *>(&quantize_perm_kernel<XT, NM>), lds); \
+        if (e_ != hipSuccess) return e_;                                                            \
+        quantize_perm_kernel<XT, NM><<<g, kThreads, lds, st>>>(a);                                  \
+    } while (0)
         if (q.xt == IN_BF16) { if (norm) QP(IN_BF16, true); else QP(IN_BF16, false); }
         else { if (norm) QP(IN_F32, true); else QP(IN_F32, false); }
 #undef QP

@@ -203,3 +203,23 @@ def test_rows_quantizer_wait_fallback(nv, orc, rows, norm, use_perm, S, monkeypa
     torch.cuda.synchronize()
     monkeypatch.delenv("NVFP4_SPIN_LIMIT")
     assert_qtensor_equal(q1, ref, "fallback")
+
+
+@pytest.mark.parametrize("rows,norm", [(4, True), (70, False)])
+def test_row_staging_at_k_16384(nv, orc, rows, norm):
+    """The reorder kernels stage a whole row (K floats) in LDS: at K = 16384 that
+    is 64 KiB plus the kernel's own words. 4 rows take the one-launch row
+    quantizer (RMSNorm + reorder + residue), 70 rows the two-pass gather path."""
+    K = 16384
+    x = inputs.small_random(400 + rows, rows, K)
+    g = inputs.gamma(9, 0, K)
+    perm = np.random.default_rng([0, 102, rows]).permutation(K).astype(np.int32)
+    S = 512 if norm else 0
+    kw = dict(perm=torch.from_numpy(perm).to(DEV), residue_cols=S)
+    if norm:
+        kw.update(gamma=g.to(DEV), eps=1e-6)
+    note(f"row staging rows={rows} K={K} norm={norm} S={S}")
+    q = nv.quantize(x.to(DEV), **kw)
+    torch.cuda.synchronize()
+    ref = orc.quantize_aug(x, gamma=g if norm else None, eps=1e-6, perm=perm, S_cols=S)
+    assert_qtensor_equal(q, ref, f"rows={rows}")
