@@ -458,29 +458,55 @@ void decode_kernel(DArgs a) {
             // two paths share no values (each meets the barrier itself), so nothing
             // loaded has to be settled where they join.
             float S = 0.0f, wS = 0.0f;
-            if (__builtin_amdgcn_readfirstlane(pm.p0) < npos) {
-                QChunk qc[kPreChunks];
+            // Chunk t of the thread is position p0 + step t. Without residue
+            // columns and with step a multiple of 16 (M divides 16) its unit and
+            // 32-column step advance by constants: the addresses and the LDS key
+            // are affine in t and need no per-chunk branch (`affine`); otherwise
+            // chunk_at places every position. The two forms are separate paths
+            // around the whole batch loop, so no load is settled where they join.
+            const int klen = (int)(rg.kend - rg.kbeg);
+            const int w0 = pm.p0 & 15;
+            const int key0 = (((pm.p0 >> 4) * 4 + (w0 & 3)) * 16 + (w0 >> 2)) * R + pm.m;
+            const int dkey = (pm.step >> 4) * 64 * R;
+            const int cbase = (int)(rg.kbeg >> 1), sbase = (int)(rg.kbeg >> 4);
+            auto chunk = [&](int tt, auto affine) {
+                if constexpr (decltype(affine)::value) {
+                    const int pos = pm.p0 + pm.step * tt;
+                    const bool ok = pos < rg.npm;
+                    QChunk q;
+                    q.c = *reinterpret_cast<const uint4 *>(crow + (ok ? cbase + 16 * pos : 0));
+                    q.s = *reinterpret_cast<const uint16_t *>(srow + (ok ? sbase + 2 * pos : 0));
+                    q.key = ok ? key0 + dkey * tt + (32 * pos + 16 < klen ? kV1 : 0) : -1;
+                    return q;
+                } else {
+                    return qchunk_load(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * tt, slots));
+                }
+            };
+            auto pre_body = [&](auto affine) {
+                if (__builtin_amdgcn_readfirstlane(pm.p0) < npos) {
+                    QChunk qc[kPreChunks];
 #pragma unroll
-                for (int t = 0; t < kPreChunks; ++t)
-                    qc[t] = qchunk_load(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * t, slots));
-                if (a.ordered) __syncthreads();    // loads out: consumers may issue theirs
-                // the two tensor scales (lane 0 of the first producer wave, which
-                // always holds chunks), after the batch is out
-                if (ptid == 0) { S = load_vmem(a.q_S); wS = load_vmem(a.w_S); }
-                zero_unwritten(lds_a, a, rg, slots);
-#pragma unroll
-                for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
-                for (int b = kPreChunks; pm.p0 + pm.step * b < npos; b += kPreChunks) {
-#pragma unroll
-                    for (int t = 0; t < kPreChunks; ++t)
-                        qc[t] = qchunk_load(crow, srow, chunk_at(a, rg, pm.m, pm.p0 + pm.step * (b + t), slots));
+                    for (int t = 0; t < kPreChunks; ++t) qc[t] = chunk(t, affine);
+                    if (a.ordered) __syncthreads();    // loads out: consumers may issue theirs
+                    // the two tensor scales (lane 0 of the first producer wave, which
+                    // always holds chunks), after the batch is out
+                    if (ptid == 0) { S = load_vmem(a.q_S); wS = load_vmem(a.w_S); }
+                    zero_unwritten(lds_a, a, rg, slots);
 #pragma unroll
                     for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
+                    for (int b = kPreChunks; pm.p0 + pm.step * b < npos; b += kPreChunks) {
+#pragma unroll
+                        for (int t = 0; t < kPreChunks; ++t) qc[t] = chunk(b + t, affine);
+#pragma unroll
+                        for (int t = 0; t < kPreChunks; ++t) qchunk_store(lds_a, 4 * R, qc[t]);
+                    }
+                } else {
+                    if (a.ordered) __syncthreads();
+                    zero_unwritten(lds_a, a, rg, slots);
                 }
-            } else {
-                if (a.ordered) __syncthreads();
-                zero_unwritten(lds_a, a, rg, slots);
-            }
+            };
+            if (!RES && (pm.step & 15) == 0) pre_body(std::true_type{});
+            else pre_body(std::false_type{});
             if (ptid == 0) { sh_S = S; sh_wS = wS; }
             TL(1);
             __syncthreads();                   // operand complete
