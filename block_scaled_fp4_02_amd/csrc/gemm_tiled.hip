@@ -270,9 +270,9 @@ __device__ inline RowChunk load_chunk2_tiled(const uint8_t *codes, int64_t ldc, 
 // M x NW/2 along N), each wave a BM/2 x 2 BN/NW block of 16 x 16 tiles, so
 // every fragment read from LDS feeds 4 to 8 MFMAs (against 4 for the 64 x 64
 // wave tile above). 256 x 256 runs 8 waves (two per SIMD, 128 accumulator
-// registers each), 128 x 256 runs 4, 128 x 128 runs 4 with two workgroups per
-// CU. Two LDS stages; within a wave the stages overlap as a software
-// pipeline, in source order:
+// registers each), 128 x 128 runs 4 with two workgroups per CU. Two LDS
+// stages; within a wave the stages overlap as a software pipeline, in source
+// order:
 //  * a 2-deep register queue: the global loads of step s + 2 go out at the
 //    start of step s and are decoded during step s + 1;
 //  * the decode and LDS stores of step s + 1 (into the other stage) are spread
@@ -518,10 +518,12 @@ hipError_t launch_prefill_impl(const PrefillLaunch &g, hipStream_t st) {
         a.part = static_cast<float *>(g.scratch);
         return run2<256, 256, 8, 2>(a, st);
     }
-    // large tiles when they still give the chip a workgroup per CU or more
+    // 256 x 256 tiles whenever they fill ~3/8 of the CUs or more: measured at
+    // M = 512, K = 8192, N = 28672 (112 such tiles), they beat 128 x 128 tiles
+    // at two workgroups per CU (0.34 vs 0.26 of peak) and 128 x 256 tiles on
+    // four waves (0.19)
     const int64_t tn = (g.N + 255) / 256;
-    if (((g.M + 255) / 256) * tn >= 192) return run2<256, 256, 8, 2>(a, st);
-    if (((g.M + 127) / 128) * tn >= 192) return run2<128, 256, 4, 1>(a, st);
+    if (((g.M + 255) / 256) * tn >= 96) return run2<256, 256, 8, 2>(a, st);
     return run2<128, 128, 4, 2>(a, st);             // 128 x 128 tiles, two workgroups per CU
 }
 
