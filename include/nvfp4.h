@@ -131,11 +131,11 @@ nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, i
  * dtype xt, leading dimension ldx, quantized inside the call with a dynamic
  * tensor scale) is non-NULL. w is N x K. y is M x N with leading dimension ldy,
  * dtype yt (FP32, or BF16 rounded to nearest even).
- * w may be row-major or tiled; a_q must be row-major.
- * Small M (<= 32) runs as one decode launch that streams the weights once
- * (x small enough: quantized inside that launch; else by the quantize kernels
- * first). Larger M quantizes x first and uses the matrix-core tile path, which
- * takes row-major weights only (NVFP4_ERR_UNSUPPORTED for tiled ones).
+ * w may be row-major or tiled (every path reads both); a_q must be row-major.
+ * M <= 64 runs as one decode launch that streams the weights once (for
+ * M <= 32 a small enough x is quantized inside that launch; otherwise the
+ * quantize kernels run first). Larger M quantizes x first and uses the
+ * matrix-core tile path.
  * K == 0 gives y = 0. Workspace: nvfp4_workspace_size(1, M, N, K, 0). */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
                         int64_t M, int64_t K, int64_t ldx,
@@ -150,6 +150,8 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
  * already be in the channel order of opts->perm. S = opts->residue_cols in
  * [0, K]; S = 0 gives the plain product of the normalized/reordered input.
  * a_aug_out (optional, M x (K + S)) receives the quantized X_aug.
+ * The decode launches take residue columns when K is a multiple of 32; other
+ * K run on the matrix-core tile path at any M.
  * Workspace: nvfp4_workspace_size(2, M, N, K, S). */
 nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int64_t ldx,
                                 const nvfp4_quant_opts *opts, const nvfp4_tensor *w,
