@@ -836,10 +836,13 @@ void decode_kernel(DArgs a) {
 // rows, their weights W's first units again (read a second time: S / K more
 // weight bytes, against twice the LDS for a second operand copy).
 //
-// Barriers: both kinds of wave pass exactly NV = KU + RU of them. Barrier 0:
-// units 0 and 1 are in their slots. Barrier k >= 1: the consumers are done with
-// unit k - 1, and the producers have stored unit k (k >= 2) into the slot unit
-// k - 2 left. Consumers work on unit k between barriers k and k + 1.
+// Barriers: both kinds of wave pass exactly NV + 1 = KU + RU + 1 of them. The
+// first: the producers' loads of units 0..2 are out, so the consumers' weight
+// loads queue behind them (measured: the first units land ~1.9 us earlier, the
+// M = 64 product 4% faster). Barrier 0: units 0 and 1 are in their slots.
+// Barrier k >= 1: the consumers are done with unit k - 1, and the producers
+// have stored unit k (k >= 2) into the slot unit k - 2 left. Consumers work on
+// unit k between barriers k and k + 1.
 constexpr int kWinChunks = 4;                  // operand chunks per producer thread and unit (64 x 16)
 constexpr int kWinRows = 64;                   // operand rows of a window slot: fixed, so every fragment
                                                // offset is an immediate of the LDS read
@@ -900,6 +903,7 @@ void decode_win_kernel(DArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
         WLoad ring0, ring1, ring2;             // units v, v + 1, v + 2 in flight (v mod 3)
+        __syncthreads();                       // the producers' first activation loads are out
         if (has) {
             issue(0, ring0);
             if (NV > 1) issue(1, ring1);
@@ -972,6 +976,7 @@ void decode_win_kernel(DArgs a) {
         load_unit(0, q0);
         if (NV > 1) load_unit(1, q1);
         if (NV > 2) load_unit(2, q2);
+        __syncthreads();                       // loads out: the consumers issue theirs behind them
         store_unit(0, q0);
         if (NV > 1) store_unit(1, q1);
         if (NV > 3) load_unit(3, q0);
