@@ -847,26 +847,49 @@ constexpr int kWinChunks = 4;                  // operand chunks per producer th
 constexpr int kWinRows = 64;                   // operand rows of a window slot: fixed, so every fragment
                                                // offset is an immediate of the LDS read
 
-template <bool RES>
-__device__ inline QChunk win_chunk_load(const DArgs &a, int v, int KU, int c) {
-    QChunk q;
-    q.key = -1;
-    q.c = make_uint4(0, 0, 0, 0);
-    q.s = 0;
-    const int m = c >> 4, p = c & 15;
-    const bool resv = RES && v >= KU;
-    const int64_t u = resv ? v - KU : v;
-    const int64_t kc = 512 * u + 32 * p;                              // operand column
-    const int64_t cend = resv ? (a.res_cols < 512 * u + 512 ? a.res_cols : 512 * u + 512)
-                              : (a.K < 512 * u + 512 ? a.K : 512 * u + 512);
-    if (m >= a.M) return q;
-    if (kc < cend) {
-        const ChunkPos f{(resv ? a.K : 0) + kc, ((p & 3) * 16 + (p >> 2)) * kWinRows + m + (kc + 16 < cend ? kV1 : 0)};
-        q = qchunk_load(a.q_codes + (int64_t)m * a.q_ldc, a.q_scales + (int64_t)m * a.q_lds, f);
-    } else {
-        q.key = ((p & 3) * 16 + (p >> 2)) * kWinRows + m;               // past the data: a zero chunk
+// A producer thread's chunks of a unit: rows m_i = ptid / 16 + 16 i (i <
+// kWinChunks), 32-column position p = ptid % 16 in every unit. Their row
+// addresses and LDS keys are fixed; a unit only adds its byte offsets, so a
+// chunk costs two address adds, its two loads and a few selects. Rows >= M
+// read row 0 and are not stored (key -1); a position past the data (the last,
+// partial unit) reads the unit's start and stores a zero chunk (scale 0).
+struct WinRows {
+    const uint8_t *c[kWinChunks], *s[kWinChunks];
+    int key[kWinChunks];                       // LDS key of the chunk, -1 for rows >= M
+    int p;
+};
+
+__device__ inline WinRows win_rows(const DArgs &a, int ptid) {
+    WinRows w;
+    w.p = ptid & 15;
+#pragma unroll
+    for (int i = 0; i < kWinChunks; ++i) {
+        const int m = (ptid >> 4) + 16 * i;
+        const bool ok = m < a.M;
+        w.c[i] = a.q_codes + (int64_t)(ok ? m : 0) * a.q_ldc + 16 * w.p;
+        w.s[i] = a.q_scales + (int64_t)(ok ? m : 0) * a.q_lds + 2 * w.p;
+        w.key[i] = ok ? ((w.p & 3) * 16 + (w.p >> 2)) * kWinRows + m : -1;
     }
-    return q;
+    return w;
+}
+
+template <bool RES>
+__device__ inline void win_unit_load(const DArgs &a, const WinRows &w, int v, int KU, QChunk *q) {
+    const bool resv = RES && v >= KU;
+    const int u = resv ? v - KU : v;
+    const int64_t lim = resv ? a.res_cols : a.K;
+    const int64_t cend = lim < 512 * (int64_t)u + 512 ? lim : 512 * (int64_t)u + 512;
+    const int64_t kc = 512 * (int64_t)u + 32 * w.p;               // operand column of the chunk
+    const bool in = kc < cend, v1 = kc + 16 < cend;
+    const int64_t coff = in ? (resv ? a.K / 2 : 0) + 256 * (int64_t)u : 0;
+    const int64_t soff = in ? (resv ? a.K / 16 : 0) + 32 * (int64_t)u : 0;
+#pragma unroll
+    for (int i = 0; i < kWinChunks; ++i) {
+        q[i].c = *reinterpret_cast<const uint4 *>(w.c[i] + coff);
+        const uint16_t sv = *reinterpret_cast<const uint16_t *>(w.s[i] + soff);
+        q[i].s = in ? sv : (uint16_t)0;
+        q[i].key = w.key[i] < 0 ? -1 : w.key[i] + (v1 ? kV1 : 0);
+    }
 }
 
 template <bool TILED, bool RES>
@@ -964,10 +987,8 @@ void decode_win_kernel(DArgs a) {
         // from register set v mod 3; the loads of unit k + 2 go out while unit k is stored
         const int ptid = tid - 64 * kCons;
         QChunk q0[kWinChunks], q1[kWinChunks], q2[kWinChunks];
-        auto load_unit = [&](int v, QChunk *q) {
-#pragma unroll
-            for (int i = 0; i < kWinChunks; ++i) q[i] = win_chunk_load<RES>(a, v, KU, ptid + kPThreads * i);
-        };
+        const WinRows wr = win_rows(a, ptid);
+        auto load_unit = [&](int v, QChunk *q) { win_unit_load<RES>(a, wr, v, KU, q); };
         auto store_unit = [&](int v, const QChunk *q) {
             half8 *dst = lds_a + (v & 1) * SLOT;
 #pragma unroll
