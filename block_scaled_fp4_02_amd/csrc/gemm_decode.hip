@@ -853,6 +853,14 @@ constexpr int kWinRows = 64;                   // operand rows of a window slot:
 // chunk costs two address adds, its two loads and a few selects. Rows >= M
 // read row 0 and are not stored (key -1); a position past the data (the last,
 // partial unit) reads the unit's start and stores a zero chunk (scale 0).
+//
+// Row swizzle: in the slot group of position p = (32-column step s, lane
+// quarter g), row m sits at row (m + g + 4 s) mod 64. The 16 lanes of a store
+// phase hold one row at the 16 positions of a unit; unswizzled their slots lie
+// 1 KiB apart, all in the same LDS banks (counters: a third of the kernel's
+// cycles were bank conflicts); swizzled they are 16 consecutive slots. The
+// consumers read row r of their fragments at (r + g + 4 s) mod 64, still 16
+// consecutive slots per read phase.
 struct WinRows {
     const uint8_t *c[kWinChunks], *s[kWinChunks];
     int key[kWinChunks];                       // LDS key of the chunk, -1 for rows >= M
@@ -868,7 +876,8 @@ __device__ inline WinRows win_rows(const DArgs &a, int ptid) {
         const bool ok = m < a.M;
         w.c[i] = a.q_codes + (int64_t)(ok ? m : 0) * a.q_ldc + 16 * w.p;
         w.s[i] = a.q_scales + (int64_t)(ok ? m : 0) * a.q_lds + 2 * w.p;
-        w.key[i] = ok ? ((w.p & 3) * 16 + (w.p >> 2)) * kWinRows + m : -1;
+        const int sw = (w.p >> 2) + 4 * (w.p & 3);
+        w.key[i] = ok ? ((w.p & 3) * 16 + (w.p >> 2)) * kWinRows + ((m + sw) & (kWinRows - 1)) : -1;
     }
     return w;
 }
@@ -893,7 +902,7 @@ __device__ inline void win_unit_load(const DArgs &a, const WinRows &w, int v, in
 }
 
 template <bool TILED, bool RES>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))   // 128 KiB of LDS: one per CU
 void decode_win_kernel(DArgs a) {
     constexpr int MT = 4;
     constexpr int R = kWinRows, SLOT = 64 * kWinRows;
@@ -919,9 +928,12 @@ void decode_win_kernel(DArgs a) {
                 load_w(a, n < a.N ? n : a.N - 1, 512 * wu, g, w);
             }
         };
-        int arow[MT];
+        int arow[MT][4];                       // swizzled row of row tile mt in 32-column step i
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) arow[mt] = 16 * mt + r16 < M ? 16 * mt + r16 : M - 1;
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                arow[mt][i] = ((16 * mt + r16 < M ? 16 * mt + r16 : M - 1) + g + 4 * i) & (kWinRows - 1);
         float4v acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
@@ -949,7 +961,7 @@ void decode_win_kernel(DArgs a) {
                         const int fo = (4 * i + j) * 4 * R;
 #pragma unroll
                         for (int mt = 0; mt < MT; ++mt)
-                            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt]], b, acc[mt], 0, 0, 0);
+                            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt][i]], b, acc[mt], 0, 0, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);   // one 32-column step's fragments live at a time
                 }
