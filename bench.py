@@ -138,6 +138,10 @@ def main():
     ap.add_argument("--prefill-case", default="",
                     help="M,K,N: run only the prefill product on pre-quantized activations, --reps launches "
                          "(for profiling the MFMA kernel; prints one line with its time)")
+    ap.add_argument("--augmented-case", type=int, default=-1,
+                    help="S: run only the M=64, K=4096, N=14336 augmented call (RMSNorm, channel reorder, "
+                         "S residue columns, quantization in the call) on a weight ring, --reps graph replays "
+                         "(for profiling the windowed decode kernel; prints one line with its time)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -160,6 +164,9 @@ def main():
 
     if args.prefill_case:
         prefill_case(nvfp4, dev, args.layout == "tiled", [int(v) for v in args.prefill_case.split(",")], args.reps)
+        return
+    if args.augmented_case >= 0:
+        augmented_case(nvfp4, dev, args.layout == "tiled", args.augmented_case, args.reps)
         return
 
     # ---------------- inputs, resident in HBM
@@ -395,6 +402,25 @@ def prefill_case(nvfp4, dev, tiled, mkn, reps):
     print(json.dumps({"prefill_case": [M, K, N], "reps": reps, "us_per_call": round(us, 1),
                       "TFLOPs": round(flops / us / 1e6, 1),
                       "frac_f16_mfma": round(flops / us / 1e6 / F16_MFMA_PEAK_TFLOPS, 4)}), flush=True)
+
+
+def augmented_case(nvfp4, dev, tiled, S, reps):
+    """The M = 64 augmented-channel call alone (the extra-detail leg's inputs), `reps` graph replays."""
+    prep = nvfp4.pack_tiled if tiled else (lambda t: t)
+    x, g, xcal, w = inputs.outlier_aug()
+    xd, gd = x.to(dev), g.to(dev)
+    perm = nvfp4.calibrate_perm(xcal.to(dev), gd)
+    wq = prep(nvfp4.quantize(w.to(dev)[:, perm.long()].contiguous()))
+    ring = Ring(wq, max(2, -(-RING_BYTES // wbytes(14336, 4096))))
+    n = len(ring.items)
+    y = torch.empty((64, 14336), dtype=torch.float32, device=dev)
+
+    def aug():
+        for _ in range(n):
+            nvfp4.gemm_residue(xd, ring.next(), S, gamma=gd, eps=1e-6, perm=perm, out=y)
+    t, _ = graph_time(aug, reps, n)
+    print(json.dumps({"augmented_case": [64, 4096, S, 14336], "reps": reps, "calls_per_replay": n,
+                      "us_per_call": round(t * 1e6, 2)}), flush=True)
 
 
 def cpu_baseline(budget_s: float):
