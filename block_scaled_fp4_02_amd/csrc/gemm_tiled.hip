@@ -519,7 +519,7 @@ hipError_t launch_prefill_impl(const PrefillLaunch &g, hipStream_t st) {
         return run2<256, 256, 8, 2>(a, st);
     }
     // 256 x 256 tiles whenever they fill ~3/8 of the CUs or more: measured at
-    // M = 512, K = 8192, N = 28672 (112 such tiles), they beat 128 x 128 tiles
+    // M = 512, K = 8192, N = 28672 (224 such tiles), they beat 128 x 128 tiles
     // at two workgroups per CU (0.34 vs 0.26 of peak) and 128 x 256 tiles on
     // four waves (0.19)
     const int64_t tn = (g.N + 255) / 256;
