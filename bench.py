@@ -263,7 +263,7 @@ def main():
     achieved = kern_bytes_total / kern_time_total / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
-                "kernel": "decode_kernel<1,false,true> (M<=16 W4A4 decode product, pre-quantized "
+                "kernel": "decode_kernel<1,false,true,false> (M<=16 W4A4 decode product, pre-quantized "
                           "activations, tiled weights)" if args.layout == "tiled" else
                           "decode_kernel<1,false,false> (row-major weights)",
                 "per_launch_bytes": round(kern_bytes_total / len(detail["decode"])),
