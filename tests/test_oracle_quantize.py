@@ -9,7 +9,11 @@ Each test checks the oracle against something other than itself:
   with sup alpha = 1.125 (section 4.2), plus the tighter half-step bound;
 * the augmented-tensor identities of the ARCQuant article, section 3.1
   (one scale s_aug for [Q(X) | Q(R)]);
-* RMSNorm against a closed form and against numpy float64;
+* RMSNorm against a closed form, against numpy float64, and bit for bit against
+  its two-rounding FP32 order written out in numpy;
+* the FP32 dequantization order fl(fl(e d) S) that feeds the residue, and the
+  residue columns themselves, written out in numpy float32 (torch's E4M3
+  decoder and the golden codebook, no oracle call);
 * the calibration order against numpy's stable argsort.
 """
 import json
@@ -264,3 +268,78 @@ def test_fused_quantizer_composition(orc):
     # identity permutation reduces to the plain quantizer
     xi = orc.quantize_aug(x, perm=np.arange(K, dtype=np.int32))
     assert np.array_equal(xi.codes, orc.quantize(x).codes)
+
+
+# ---------------------------------------------------------------------------
+# Rounding orders pinned by arithmetic written out here in numpy float32 (one
+# rounding per operation), independently of the oracle's C code. Each test also
+# checks that the plausible alternative order gives a different result on its
+# input, so a slip to that order fails it.
+# ---------------------------------------------------------------------------
+
+def _e4m3_values(bytes_u8: np.ndarray) -> np.ndarray:
+    """E4M3 byte -> value through torch's float8_e4m3fn decoder (a library routine)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bytes_u8, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.float().numpy()
+
+
+def _deq32_numpy(q):
+    """fl(fl(e * d) * S) for every element: e from the golden codebook, d from torch."""
+    e = code_values(unpack_codes(q.codes)).astype(np.float32)
+    d = np.repeat(_e4m3_values(q.scales), 16, axis=1)
+    ed = (e * d).astype(np.float32)          # exact: at most 2 + 4 significant bits
+    return (ed * np.float32(q.S)).astype(np.float32), e, d
+
+
+def test_dequantize_f32_order(orc):
+    """The FP32 dequantization feeding the residue is fl(fl(e d) S) (ARCQuant article,
+    section 3.1: R = X - deq(Q(X)), computed in FP32); not fl(e fl(d S))."""
+    x = inputs.small_random(31, 16, 1024).float().numpy()
+    q = orc.quantize(x)
+    want, e, d = _deq32_numpy(q)
+    got = orc.dequantize_f32(q)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    alt = (e * (d * np.float32(q.S)).astype(np.float32)).astype(np.float32)
+    assert np.count_nonzero(alt.view(np.uint32) != want.view(np.uint32)) > 0
+
+
+def test_residue_tail_from_numpy_dequant(orc):
+    """X_aug's residue columns are Q(fl(x - fl(fl(e d) S))) against S_X, with the
+    subtraction and the dequantization written out in numpy (config 3's input, K -> 2K)."""
+    x, _ = inputs.residue_8192(16)
+    x = x.float().numpy()
+    K = x.shape[1]
+    xa = orc.quantize_aug(x, S_cols=K)
+    q = orc.quantize(x)
+    deq, e, d = _deq32_numpy(q)
+    R = (x - deq).astype(np.float32)
+    qr = orc.quantize(R, static_S=float(q.S))
+    assert np.array_equal(xa.codes[:, K // 2:], qr.codes)
+    assert np.array_equal(xa.scales[:, K // 16:], qr.scales)
+    # the other multiplication order changes at least one residue code on this input
+    alt = (e * (d * np.float32(q.S)).astype(np.float32)).astype(np.float32)
+    qa = orc.quantize((x - alt).astype(np.float32), static_S=float(q.S))
+    assert not (np.array_equal(qa.codes, qr.codes) and np.array_equal(qa.scales, qr.scales))
+
+
+def test_rmsnorm_two_roundings(orc):
+    """RMSNorm y = fl(fl(x r) gamma) with r = fl32(1 / sqrt(sum(x^2)/K + eps)) and the sum
+    of squares accumulated in FP64 in column order (fused RMSNorm of the ARCQuant article,
+    section 3.2; FP32 output fed to the quantizer), compared bit for bit."""
+    x, g, _, _ = inputs.outlier_aug(rows=8, N=16, cal_rows=4)
+    x = x.float().numpy()
+    g = g.float().numpy()
+    K = x.shape[1]
+    eps = np.float64(np.float32(1e-6))
+    xd = x.astype(np.float64)
+    ss = np.cumsum(xd * xd, axis=1)[:, -1]              # sequential FP64 sum (squares of bf16 are exact)
+    r = (1.0 / np.sqrt(ss / K + eps)).astype(np.float32)[:, None]
+    want = ((x * r).astype(np.float32) * g).astype(np.float32)
+    got = orc.rmsnorm(x, g, 1e-6)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # one rounding of the exact product, or gamma folded into r first, differ on this input
+    once = (xd * r.astype(np.float64) * g.astype(np.float64)).astype(np.float32)
+    folded = (x * (r * g).astype(np.float32)).astype(np.float32)
+    assert np.count_nonzero(once.view(np.uint32) != want.view(np.uint32)) > 0
+    assert np.count_nonzero(folded.view(np.uint32) != want.view(np.uint32)) > 0
