@@ -115,7 +115,7 @@ nvfp4_status check_opts(const nvfp4_quant_opts *o, int64_t K_in) {
     if (o->residue_cols < 0 || o->residue_cols > K_in || o->residue_cols % 16) return NVFP4_ERR_SHAPE;
     if (o->gamma && !aligned(o->gamma, 16)) return NVFP4_ERR_ALIGN;
     if (o->perm && K_in > 16384) return NVFP4_ERR_UNSUPPORTED;
-    if (o->perm && !aligned(o->perm, 4)) return NVFP4_ERR_ALIGN;
+    if (o->perm && !aligned(o->perm, 16)) return NVFP4_ERR_ALIGN;   // read as 16-byte vectors
     if (o->gamma && !(o->eps >= 0.0f)) return NVFP4_ERR_SHAPE;
     return NVFP4_OK;
 }

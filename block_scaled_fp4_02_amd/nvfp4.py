@@ -14,7 +14,7 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("NVFP4_LIB") or os.path.join(_HERE, "libnvfp4.so")  # override: alternative build
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
 
 BF16, FP32 = 0, 1
 _STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "misaligned", 4: "bad dtype",
@@ -164,16 +164,22 @@ def pack_tiled(w: NVFP4Tensor) -> NVFP4Tensor:
 
 
 _ws = {}
+_ws_retired = []
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
     """A per-(device, stream) workspace, grown on demand (plumbing, not compute).
 
     Zero-filled when allocated: its first 8 KiB hold the library's split-K
-    counters, which must start at zero and which every call leaves at zero."""
+    counters, which must start at zero and which every call leaves at zero.
+    A workspace that is outgrown is kept alive, never returned to torch's
+    allocator: a HIP graph captured earlier on the stream still holds its
+    address and writes its counters and partials there on every replay."""
     key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
     buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
+        if buf is not None:
+            _ws_retired.append(buf)
         buf = torch.zeros(max(nbytes, 16384), dtype=torch.uint8, device=device)
         _ws[key] = buf
     return buf

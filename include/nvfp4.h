@@ -109,7 +109,9 @@ typedef struct {
     const int32_t *perm;           /* device [K_in] channel order x'[:, j] = y[:, perm[j]],
                                       or NULL (ARCQuant article, section 3.1: outliers
                                       ranked by calibration absmax come first). Must be a
-                                      permutation of [0, K_in); other values are clamped */
+                                      permutation of [0, K_in); other values are clamped.
+                                      16-byte aligned, else NVFP4_ERR_ALIGN (read as
+                                      16-byte vectors)                                      */
     int64_t        residue_cols;   /* S: residue of columns [0, S) appended after column
                                       K_in, quantized against the same tensor scale
                                       (ARCQuant section 3.1; ResServe abstract). 0 = none,

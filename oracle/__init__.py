@@ -198,6 +198,22 @@ def gemm(a: QTensor, w: QTensor) -> np.ndarray:
     return y
 
 
+def dequantize_unscaled(q: QTensor) -> np.ndarray:
+    """e(c) * d in FP64 (exact), without the tensor scale."""
+    return dequantize(QTensor(q.codes, q.scales, 1.0, q.K))
+
+
+def gemm_blas(a: QTensor, w: QTensor) -> np.ndarray:
+    """The product of ``gemm`` with numpy's float64 matmul as its summation step,
+    for references at full workload sizes. Every e(c)d is an integer multiple of
+    2^-10 and every product of two a multiple of 2^-20; while the partial sums stay
+    below 2^33 in magnitude (as on every workload here) each of them is exact in
+    FP64 in any order, so this equals ``gemm`` bit for bit (a test pins that)."""
+    assert a.K == w.K
+    y = dequantize_unscaled(a) @ dequantize_unscaled(w).T
+    return y * (np.float64(a.S) * np.float64(w.S))
+
+
 def gemm_pairs(a: QTensor, w: QTensor, ms, ns) -> np.ndarray:
     ms = np.ascontiguousarray(ms, dtype=np.int64)
     ns = np.ascontiguousarray(ns, dtype=np.int64)

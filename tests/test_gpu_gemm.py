@@ -21,11 +21,20 @@ def nv():
     return nvfp4
 
 
-def test_gemv_4096(nv, orc):
+LAYOUTS = ["rowmajor", "tiled"]
+
+
+def _layout(nv, wq, layout):
+    """The weight in the layout under test (the bench times the tiled one)."""
+    return nv.pack_tiled(wq) if layout == "tiled" else wq
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemv_4096(nv, orc, layout):
     x, w = inputs.gemv_4096()
-    note("gemm gemv 1x4096x4096")
+    note(f"gemm gemv 1x4096x4096 {layout}")
     wq = nv.quantize(w.to(DEV))
-    y = nv.gemm(x.to(DEV), wq)
+    y = nv.gemm(x.to(DEV), _layout(nv, wq, layout))
     torch.cuda.synchronize()
     ow = orc.quantize(w)
     assert_qtensor_equal(wq, ow, "W")
@@ -34,23 +43,33 @@ def test_gemv_4096(nv, orc):
     assert err <= TOL, err
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("shape_idx", [0, 1, 2])
-def test_decode_sweep(nv, orc, shape_idx):
+def test_decode_sweep(nv, orc, shape_idx, layout):
+    """Every output of the fused call (activation quantized in the call) and of the
+    product on pre-quantized activations (the kernel the bench's roofline times)."""
     K, N = inputs.DECODE_SHAPES[shape_idx]
     x, w = inputs.decode_sweep(shape_idx)
-    note(f"gemm decode sweep K={K} N={N}: quantize W")
+    note(f"gemm decode sweep K={K} N={N} {layout}: quantize W")
     wq = nv.quantize(w.to(DEV))
     torch.cuda.synchronize()
     ow = orc.quantize(w)
     assert_qtensor_equal(wq, ow, "W")
+    wl = _layout(nv, wq, layout)
     xd = x.to(DEV)
     for M in inputs.DECODE_MS:
-        note(f"gemm decode M={M} K={K} N={N}")
-        y = nv.gemm(xd[:M], wq)
+        note(f"gemm decode M={M} K={K} N={N} {layout}")
+        y = nv.gemm(xd[:M], wl)
+        aq = nv.quantize(xd[:M])
+        yk = nv.gemm(aq, wl)
         torch.cuda.synchronize()
-        ref = orc.gemm(orc.quantize(x[:M]), ow)
+        ox = orc.quantize(x[:M])
+        assert_qtensor_equal(aq, ox, "X")
+        ref = orc.gemm_blas(ox, ow)
         err = gemm_error(y.cpu().numpy(), ref)
         assert err <= TOL, (M, err)
+        err = gemm_error(yk.cpu().numpy(), ref)
+        assert err <= TOL, (M, "pre-quantized", err)
 
 
 def test_prequantized_activation_path(nv, orc):
@@ -64,81 +83,152 @@ def test_prequantized_activation_path(nv, orc):
     assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("M", inputs.RESIDUE_MS)
-def test_residue_k_to_2k(nv, orc, M):
+@pytest.fixture(scope="module")
+def residue_case(orc):
     x, w = inputs.residue_8192(16)
+    return x, w, orc.quantize(w), orc.weight_aug(w, 8192)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M", inputs.RESIDUE_MS)
+def test_residue_k_to_2k(nv, orc, residue_case, M, layout):
+    x, w, ow, wa = residue_case
     x = x[:M]
-    note(f"gemm_residue K->2K M={M}")
-    wq = nv.quantize(w.to(DEV))
+    note(f"gemm_residue K->2K M={M} {layout}")
+    wq = _layout(nv, nv.quantize(w.to(DEV)), layout)
     y, aug = nv.gemm_residue(x.to(DEV), wq, 8192, return_aug=True)
     y0 = nv.gemm(x.to(DEV), wq)
     torch.cuda.synchronize()
-    ref, xa, wa = orc.gemm_residue(x, w, 8192)
+    xa = orc.quantize_aug(x, S_cols=8192)
     assert_qtensor_equal(aug, xa, "X_aug")
+    ref = orc.gemm_blas(xa, wa)
     err = gemm_error(y.cpu().numpy(), ref)
     assert err <= TOL, err
     # the compensated product is closer to the product with unquantized activations
-    exact = x.float().numpy().astype(np.float64) @ orc.dequantize(orc.quantize(w)).T
+    exact = x.float().numpy().astype(np.float64) @ orc.dequantize(ow).T
     e_res = np.linalg.norm(y.cpu().numpy() - exact)
     e_base = np.linalg.norm(y0.cpu().numpy() - exact)
     assert e_res <= 0.25 * e_base, (e_res, e_base)
 
 
-@pytest.mark.parametrize("S", inputs.AUG_S)
-def test_outlier_augmented(nv, orc, S):
-    """RMSNorm + calibrated reorder + residue of the top S channels, M=64, N=14336."""
+@pytest.fixture(scope="module")
+def aug_case(orc):
     x, g, xcal, w = inputs.outlier_aug()
     perm = orc.calibrate_perm(xcal, g)
-    pd = torch.from_numpy(perm).to(DEV)
     w_perm = w[:, torch.from_numpy(perm).long()]
-    note(f"gemm_residue augmented S={S}")
-    wq = nv.quantize(w_perm.to(DEV))
+    return x, g, perm, w_perm, orc.quantize(w_perm)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("S", inputs.AUG_S)
+def test_outlier_augmented(nv, orc, aug_case, S, layout):
+    """RMSNorm + calibrated reorder + residue of the top S channels, M=64, N=14336:
+    X_aug bit for bit, every output against the oracle."""
+    x, g, perm, w_perm, ow = aug_case
+    pd = torch.from_numpy(perm).to(DEV)
+    note(f"gemm_residue augmented S={S} {layout}")
+    wq = _layout(nv, nv.quantize(w_perm.to(DEV)), layout)
     y, aug = nv.gemm_residue(x.to(DEV), wq, S, gamma=g.to(DEV), eps=1e-6, perm=pd, return_aug=True)
     torch.cuda.synchronize()
     xa = orc.quantize_aug(x, gamma=g, eps=1e-6, perm=perm, S_cols=S)
     assert_qtensor_equal(aug, xa, "X_aug")
-    wa = orc.weight_aug(w_perm, S)
-    cols = np.sort(np.random.default_rng(S).choice(14336, 1024, replace=False))
-    sub = orc.QTensor(np.ascontiguousarray(wa.codes[cols]), np.ascontiguousarray(wa.scales[cols]), wa.S, wa.K)
-    ref = orc.gemm(xa, sub)
-    err = gemm_error(y.cpu().numpy()[:, cols], ref)
+    # W_aug = [W' | W'[:, :S]]: its tail codes and scales are the head's
+    K = 4096
+    wa = orc.QTensor(np.ascontiguousarray(np.concatenate([ow.codes, ow.codes[:, :S // 2]], axis=1)),
+                     np.ascontiguousarray(np.concatenate([ow.scales, ow.scales[:, :S // 16]], axis=1)), ow.S, K + S)
+    ref = orc.gemm_blas(xa, wa)
+    err = gemm_error(y.cpu().numpy(), ref)
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("shape_idx", [0, 1])
-def test_prefill_sampled(nv, orc, shape_idx):
-    K, N = inputs.PREFILL_SHAPES[shape_idx]
-    xall, w = inputs.prefill(shape_idx, 8192)
-    note(f"prefill K={K} N={N}: quantize W")
-    wq = nv.quantize(w.to(DEV))
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,N,K,S", [(4, 300, 1024, 256), (12, 300, 1024, 256), (24, 300, 1024, 256),
+                                     (8, 14336, 4096, 256), (16, 4096, 14336, 512), (1, 8192, 8192, 2048),
+                                     (48, 700, 2048, 512), (16, 1000, 4096, 2048)])
+def test_residue_partial_columns(nv, orc, M, N, K, S, layout):
+    """Residue columns over a part of K (0 < S < K, K a multiple of 32): the decode
+    paths with a separate residue operand, the stacked rows with S < K, the two-row-tile
+    instance and the windowed kernel. Every output against the oracle."""
+    x = inputs.small_random(300 + M + S, M, K)
+    w = inputs.small_random(301 + N, N, K, scale=0.02)
+    note(f"gemm_residue partial M={M} N={N} K={K} S={S} {layout}")
+    wq = _layout(nv, nv.quantize(w.to(DEV)), layout)
+    y, aug = nv.gemm_residue(x.to(DEV), wq, S, return_aug=True)
     torch.cuda.synchronize()
-    ow_S = orc.tensor_scale(w)
+    xa = orc.quantize_aug(x, S_cols=S)
+    assert_qtensor_equal(aug, xa, "X_aug")
+    ref = orc.gemm_blas(xa, orc.weight_aug(w, S))
+    err = gemm_error(y.cpu().numpy(), ref)
+    assert err <= TOL, (err, M, N, K, S)
+
+
+def _tile_lines(n: int, rng) -> np.ndarray:
+    """Indices below n covering every 128- and 256-wide tile of the prefill plans: both
+    edges of each 128 band and one interior index per band."""
+    idx = []
+    for b in range(0, n, 128):
+        hi = min(b + 128, n) - 1
+        idx += [b, hi, int(rng.integers(b, hi + 1))]
+    return np.unique(np.array(idx, dtype=np.int64))
+
+
+@pytest.fixture(scope="module")
+def prefill_case(orc):
+    cache = {}
+
+    def get(shape_idx):
+        if shape_idx not in cache:
+            cache.clear()
+            xall, w = inputs.prefill(shape_idx, 8192)
+            cache[shape_idx] = (xall, w, orc.tensor_scale(w))
+        return cache[shape_idx]
+    return get
+
+
+@pytest.mark.parametrize("M", inputs.PREFILL_MS)
+@pytest.mark.parametrize("shape_idx", [0, 1])
+def test_prefill_tiles(nv, orc, prefill_case, shape_idx, M):
+    """Prefill products at the bench's sizes (tiled weights, as timed): the outputs at
+    every output tile's four corners and an interior point, plus 128 random rows and
+    columns -- the whole cross product of the chosen rows and columns -- against the
+    oracle, for the FP32 accumulator (P2) and the bf16 store of the fused call (half a
+    bf16 ulp more). Quantized activations are compared bit for bit: every code at the
+    sizes where the oracle quantizes the whole tensor in seconds, else the chosen rows."""
+    K, N = inputs.PREFILL_SHAPES[shape_idx]
+    xall, w, ow_S = prefill_case(shape_idx)
+    rng = np.random.default_rng(1000 * shape_idx + M)
+    note(f"prefill K={K} N={N} M={M}: quantize W, tile")
+    wq = nv.quantize(w.to(DEV))
+    wt = nv.pack_tiled(wq)
+    torch.cuda.synchronize()
     assert float(wq.scale.cpu()[0]) == ow_S
-    xd = xall.to(DEV)
-    wc, ws_, _ = wq.host()
-    rng = np.random.default_rng(shape_idx)
-    for M in inputs.PREFILL_MS:
-        note(f"prefill gemm M={M} K={K} N={N}")
-        yb = nv.gemm(xd[:M], wq, out_dtype=torch.bfloat16)
-        y32 = nv.gemm(xd[:M], wq, out_dtype=torch.float32) if M == 512 else None
-        torch.cuda.synchronize()
-        ms = rng.integers(0, M, 384)
-        ns = rng.integers(0, N, 384)
-        S_x = orc.tensor_scale(xall[:M])
-        rows = np.unique(ms)
+    xd = xall[:M].to(DEV)
+    note(f"prefill gemm K={K} N={N} M={M}")
+    aq = nv.quantize(xd)
+    y32 = nv.gemm(aq, wt, out_dtype=torch.float32)
+    yb = nv.gemm(xd, wt, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([_tile_lines(M, rng), rng.integers(0, M, 128)]))
+    cols = np.unique(np.concatenate([_tile_lines(N, rng), rng.integers(0, N, 128)]))
+    S_x = orc.tensor_scale(xall[:M])
+    assert float(aq.scale.cpu()[0]) == S_x
+    ac, as_, _ = aq.host()
+    if M * K <= 2048 * 8192:
+        ox = orc.quantize(xall[:M])
+        assert np.array_equal(ac, ox.codes) and np.array_equal(as_, ox.scales), "X codes differ"
+        xq = orc.QTensor(np.ascontiguousarray(ox.codes[rows]), np.ascontiguousarray(ox.scales[rows]), ox.S, K)
+    else:
         xq = orc.quantize(xall[rows], static_S=float(S_x))
-        pos = {r: i for i, r in enumerate(rows)}
-        wrows = np.unique(ns)
-        wsub = orc.quantize(w[wrows], static_S=float(ow_S))
-        wpos = {r: i for i, r in enumerate(wrows)}
-        # weight rows must match the device codes too
-        assert np.array_equal(wsub.codes, wc[wrows]) and np.array_equal(wsub.scales, ws_[wrows])
-        ref = orc.gemm_pairs(xq, wsub, np.array([pos[m] for m in ms]), np.array([wpos[n] for n in ns]))
-        got = yb.float().cpu().numpy()[ms, ns]
-        assert bf16_bound_ok(got, ref), (M, gemm_error(got, ref))
-        if y32 is not None:
-            err = gemm_error(y32.cpu().numpy()[ms, ns], ref)
-            assert err <= TOL, err
+        assert np.array_equal(ac[rows], xq.codes) and np.array_equal(as_[rows], xq.scales), "X codes differ"
+    wsub = orc.quantize(w[cols], static_S=float(ow_S))
+    wc, ws_, _ = wq.host()
+    assert np.array_equal(wc[cols], wsub.codes) and np.array_equal(ws_[cols], wsub.scales), "W codes differ"
+    ref = orc.gemm_blas(xq, wsub)
+    got32 = y32.cpu().numpy()[np.ix_(rows, cols)]
+    err = gemm_error(got32, ref)
+    assert err <= TOL, (M, err)
+    gotb = yb.float().cpu().numpy()[np.ix_(rows, cols)]
+    assert bf16_bound_ok(gotb, ref), (M, gemm_error(gotb, ref))
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 15, 48), (16, 47, 528), (17, 300, 1040), (33, 64, 528),

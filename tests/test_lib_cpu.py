@@ -117,6 +117,10 @@ def test_argument_errors_before_launch(L):
     assert L.nvfp4_gemm_residue(fake, 0, 4, 64, 64, C.byref(o), C.byref(w), fake, 1, 32, None, ws, wsn, None) == 2
     o = _COpts(None, C.c_float(1e-6), None, 80, None)
     assert L.nvfp4_gemm_residue(fake, 0, 4, 64, 64, C.byref(o), C.byref(w), fake, 1, 32, None, ws, wsn, None) == 2
+    # permutation pointer not 16-byte aligned (the quantizer reads it as 16-byte vectors)
+    o = _COpts(None, C.c_float(1e-6), vp((1 << 20) + 4), 0, None)
+    assert L.nvfp4_quantize(fake, 0, 4, 64, 64, C.byref(o), C.byref(out), ws, wsn, None) == 3
+    assert L.nvfp4_gemm_residue(fake, 0, 4, 64, 64, C.byref(o), C.byref(w), fake, 1, 32, None, ws, wsn, None) == 3
     # permutation beyond the staged-row limit
     o = _COpts(None, C.c_float(1e-6), fake, 0, None)
     assert L.nvfp4_quantize(fake, 0, 4, 32768, 32768, C.byref(o),

@@ -30,6 +30,17 @@ def test_gemm_fp64_equals_exact_and_numpy(orc):
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+def test_gemm_blas_equals_gemm(orc):
+    """The library-matmul form used for full-size references is the same product,
+    bit for bit (all partial sums exact), on a decode-sweep-shaped slice."""
+    x, w = inputs.decode_sweep(1)
+    a, b = orc.quantize(x[:, :2048]), orc.quantize(w[:300, :2048])
+    assert np.array_equal(orc.gemm_blas(a, b), orc.gemm(a, b))
+    a = orc.quantize(inputs.small_random(7, 9, 528))
+    b = orc.quantize(inputs.small_random(8, 77, 528, scale=0.02))
+    assert np.array_equal(orc.gemm_blas(a, b), orc.gemm(a, b))
+
+
 def test_gemm_workload_exact(orc):
     x, w = inputs.gemv_4096()
     a, b = orc.quantize(x), orc.quantize(w[:512])
