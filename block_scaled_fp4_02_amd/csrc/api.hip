@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/nvfp4.h"
@@ -219,10 +220,13 @@ nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, i
                             static_cast<hipStream_t>(stream));
 }
 
-nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
-                        int64_t M, int64_t K, int64_t ldx,
-                        const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
-                        void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of nvfp4_gemm that do not involve the workspace.
+nvfp4_status check_gemm(const nvfp4_tensor *a_q, const void *x, int xt, int64_t M, int64_t K, int64_t ldx,
+                        const nvfp4_tensor *w, const void *y, int yt, int64_t ldy) {
     if (!w) return NVFP4_ERR_NULL;
     if (a_q == nullptr && x == nullptr && !(M == 0 || K == 0)) return NVFP4_ERR_NULL;
     if (a_q != nullptr && x != nullptr) return NVFP4_ERR_NULL;
@@ -230,14 +234,17 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
     if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
     if (M < 0 || K < 0 || K % 16) return NVFP4_ERR_SHAPE;
     CHECK(check_tensor(w, w->rows, K, true));
-    const int64_t N = w->rows;
-    if (ldy < N) return NVFP4_ERR_SHAPE;
+    if (ldy < w->rows) return NVFP4_ERR_SHAPE;
     if (a_q) CHECK(check_tensor(a_q, M, K));
     else CHECK(check_x(x, xt, M, K, ldx));
-    const size_t need = nvfp4_workspace_size(1, M, N, K, 0);
-    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
-    if (M == 0 || N == 0) return NVFP4_OK;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    return NVFP4_OK;
+}
+
+// The product of nvfp4_gemm on a validated call and a large enough workspace.
+nvfp4_status gemm_enqueue(const nvfp4_tensor *a_q, const void *x, int xt, int64_t M, int64_t K, int64_t ldx,
+                          const nvfp4_tensor *w, void *y, int yt, int64_t ldy, void *ws, size_t ws_bytes,
+                          hipStream_t st) {
+    const int64_t N = w->rows;
     unsigned *header = static_cast<unsigned *>(ws);
     Carver c{static_cast<uint8_t *>(ws) + kHeaderBytes, ws_bytes - kHeaderBytes};
     nvfp4_tensor aq;
@@ -259,6 +266,82 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
         return enqueue_fused(x, xt, ldx, nullptr, aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
     if (!a_q) CHECK(enqueue_quantize(x, xt, M, K, ldx, nullptr, aq, partials, rscale, header, st));
     return enqueue_gemm(aq, *w, M, K, 0, y, yt, ldy, header, scratch, sb, st);
+}
+
+// ---- Workspace of nvfp4_gemm_noalloc: a static device array, one copy per GPU,
+// held until the process ends. In host code the array's name is only a host-side
+// stand-in: its device address (per device) comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is used.
+__device__ __align__(256) static uint8_t g_static_scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+__global__ void zero_words_kernel(unsigned *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+    std::once_flag once;
+    uint8_t *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+StaticScratch g_dev_scratch[kMaxDevices];
+
+// This device's copy of the static scratch. The first call on a device takes its
+// address and clears its counter header with a fill kernel on `st` (a kernel, so a
+// caller's graph capture may hold it; the array also starts zeroed at load).
+hipError_t static_scratch(hipStream_t st, uint8_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    StaticScratch &s = g_dev_scratch[dev];
+    std::call_once(s.once, [&] {
+        void *p = nullptr;
+        s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(g_static_scratch));
+        if (s.err != hipSuccess) return;
+        s.ptr = static_cast<uint8_t *>(p);
+        const int words = (int)(kHeaderBytes / sizeof(unsigned));
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st,
+                           reinterpret_cast<unsigned *>(s.ptr), words);
+        s.err = hipGetLastError();
+    });
+    *out = s.ptr;
+    return s.err;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_gemm_noalloc(const nvfp4_tensor *a_q, const void *x, int xt,
+                                int64_t M, int64_t K, int64_t ldx,
+                                const nvfp4_tensor *w, void *y, int yt, int64_t ldy, void *stream) {
+    CHECK(check_gemm(a_q, x, xt, M, K, ldx, w, y, yt, ldy));
+    const size_t need = nvfp4_workspace_size(1, M, w->rows, K, 0);
+    if (need > (size_t)NVFP4_NOALLOC_SCRATCH_BYTES) {
+        std::snprintf(g_last_error, sizeof(g_last_error),
+                      "nvfp4_gemm_noalloc: this product needs %zu bytes of scratch; the static scratch holds %zu",
+                      need, (size_t)NVFP4_NOALLOC_SCRATCH_BYTES);
+        return NVFP4_ERR_WORKSPACE;
+    }
+    if (M == 0 || w->rows == 0) return NVFP4_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t *ws = nullptr;
+    const hipError_t e = static_scratch(st, &ws);
+    if (e != hipSuccess) return hip_fail(e);
+    return gemm_enqueue(a_q, x, xt, M, K, ldx, w, y, yt, ldy, ws, NVFP4_NOALLOC_SCRATCH_BYTES, st);
+}
+
+nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
+                        int64_t M, int64_t K, int64_t ldx,
+                        const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
+                        void *ws, size_t ws_bytes, void *stream) {
+    CHECK(check_gemm(a_q, x, xt, M, K, ldx, w, y, yt, ldy));
+    const size_t need = nvfp4_workspace_size(1, M, w->rows, K, 0);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (M == 0 || w->rows == 0) return NVFP4_OK;
+    return gemm_enqueue(a_q, x, xt, M, K, ldx, w, y, yt, ldy, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int64_t ldx,

@@ -44,7 +44,7 @@ class _COpts(C.Structure):
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
+EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
            "nvfp4_perm_from_absmax", "nvfp4_workspace_size", "nvfp4_status_string",
            "nvfp4_last_error", "nvfp4_version", "nvfp4_host_e4m3_encode", "nvfp4_host_e2m1_encode"]
 
@@ -59,6 +59,7 @@ def lib():
             vp, i64, sz = C.c_void_p, C.c_int64, C.c_size_t
             L.nvfp4_quantize.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, sz, vp]
             L.nvfp4_gemm.argtypes = [vp, vp, C.c_int, i64, i64, i64, vp, vp, C.c_int, i64, vp, sz, vp]
+            L.nvfp4_gemm_noalloc.argtypes = [vp, vp, C.c_int, i64, i64, i64, vp, vp, C.c_int, i64, vp]
             L.nvfp4_gemm_residue.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, C.c_int, i64, vp,
                                              vp, sz, vp]
             L.nvfp4_pack_tiled.argtypes = [vp, vp, vp]
@@ -71,7 +72,7 @@ def lib():
             L.nvfp4_last_error.restype = C.c_char_p
             L.nvfp4_host_e4m3_encode.argtypes = [C.c_float]
             L.nvfp4_host_e2m1_encode.argtypes = [C.c_float]
-            for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_residue", "nvfp4_pack_tiled",
+            for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_pack_tiled",
                          "nvfp4_channel_absmax", "nvfp4_perm_from_absmax"):
                 getattr(L, name).restype = C.c_int
             _lib = L
@@ -244,6 +245,25 @@ def gemm(a, w: NVFP4Tensor, out_dtype=torch.float32, out: torch.Tensor | None = 
         ws = workspace(n, dev)
         _check(lib().nvfp4_gemm(None, _ptr(a), _dtype_code(a), M, K, a.stride(0), C.byref(w.c()), _ptr(out),
                                 yt, out.stride(0), _ptr(ws), ws.numel(), _stream()), "nvfp4_gemm")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def gemm_noalloc(a, w: NVFP4Tensor, out: torch.Tensor) -> torch.Tensor:
+    """nvfp4_gemm_noalloc: y = Q(a) Q(w)^T into the caller's `out` with no workspace
+    (the library's static per-GPU scratch); a is an NVFP4Tensor or a raw bf16/f32 tensor."""
+    N, K = w.rows, w.K
+    yt = _dtype_code(out)
+    if isinstance(a, NVFP4Tensor):
+        ac = a.c()
+        _check(lib().nvfp4_gemm_noalloc(C.byref(ac), None, 0, a.rows, K, 0, C.byref(w.c()), _ptr(out), yt,
+                                        out.stride(0), _stream()), "nvfp4_gemm_noalloc")
+    else:
+        assert a.dim() == 2 and a.stride(1) == 1
+        _check(lib().nvfp4_gemm_noalloc(None, _ptr(a), _dtype_code(a), a.shape[0], K, a.stride(0), C.byref(w.c()),
+                                        _ptr(out), yt, out.stride(0), _stream()), "nvfp4_gemm_noalloc")
     return out
 
 

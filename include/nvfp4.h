@@ -144,6 +144,22 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor *a_q, const void *x, int xt,
                         const nvfp4_tensor *w, void *y, int yt, int64_t ldy,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* nvfp4_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, kernels and results as nvfp4_gemm.
+ * Its workspace is a static device array of NVFP4_NOALLOC_SCRATCH_BYTES, one
+ * copy per GPU, held until the process ends; the call allocates nothing. The
+ * first call on a device takes the array's address and clears its counters
+ * (a fill kernel on `stream`). Every call on one GPU shares that array, so
+ * calls that overlap on one GPU (other streams, other threads) race: order
+ * them. A product whose workspace (nvfp4_workspace_size(1, M, N, K, 0))
+ * exceeds the array returns NVFP4_ERR_WORKSPACE before anything is enqueued,
+ * and nvfp4_last_error() says how much it needs. */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (32u << 20)
+nvfp4_status nvfp4_gemm_noalloc(const nvfp4_tensor *a_q, const void *x, int xt,
+                                int64_t M, int64_t K, int64_t ldx,
+                                const nvfp4_tensor *w, void *y, int yt, int64_t ldy, void *stream);
+
 /* Residue-compensated product (ARCQuant article, sections 3.1-3.2; ResServe abstract):
  *   X' = perm/RMSNorm(x) per opts, R = X' - deq(Q(X')) on columns [0, S),
  *   Y  = s_aug [Q(X') | Q(R)] [Q(W) | Q(W[:, :S])]^T,  s_aug = S_x S_w,

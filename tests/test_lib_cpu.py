@@ -163,3 +163,17 @@ def test_perm_from_absmax_host(L, orc):
     p = np.zeros(500, np.int32)
     assert L.nvfp4_perm_from_absmax(C.c_void_p(v.ctypes.data), 500, C.c_void_p(p.ctypes.data)) == 0
     assert np.array_equal(p, orc.perm_from_absmax(v))
+
+
+def test_noalloc_rejects_oversized_before_launch(L):
+    """nvfp4_gemm_noalloc refuses a product whose workspace exceeds the static scratch,
+    before touching the device, and says how much it needs (fake pointers)."""
+    vp = C.c_void_p
+    fake = vp(1 << 20)
+    M, N, K = 512, 8192, 28672
+    assert L.nvfp4_workspace_size(1, M, N, K, 0) > (32 << 20)
+    w = _tensor(N, K, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    assert L.nvfp4_gemm_noalloc(None, fake, 0, M, K, K, C.byref(w), fake, 1, N, None) == 5
+    assert b"static scratch" in L.nvfp4_last_error()
+    # argument errors come first, as in nvfp4_gemm
+    assert L.nvfp4_gemm_noalloc(None, None, 0, M, K, K, C.byref(w), fake, 1, N, None) == 1
