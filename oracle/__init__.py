@@ -51,7 +51,7 @@ def lib():
         L.or_rmsnorm.argtypes = [f32p, i64, i64, i64, f32p, C.c_float, f32p, i64]
         L.or_channel_absmax.argtypes = [f32p, i64, i64, i64, vp, C.c_float, f32p]
         L.or_perm_from_absmax.argtypes = [f32p, i64, i32p]
-        L.or_quantize_aug.argtypes = [f32p, i64, i64, i64, vp, C.c_float, vp, i64, vp,
+        L.or_quantize_aug.argtypes = [f32p, i64, i64, i64, vp, C.c_float, vp, vp, i64, vp,
                                       u8p, i64, u8p, i64, vp]
         L.or_quantize_aug.restype = i64
         L.or_gemm.argtypes = [u8p, i64, u8p, i64, C.c_float, u8p, i64, u8p, i64, C.c_float,
@@ -125,7 +125,9 @@ def quantize(x, static_S=None) -> QTensor:
 
 
 def quantize_aug(x, gamma=None, eps: float = 1e-6, perm=None, S_cols: int = 0,
-                 static_S=None) -> QTensor:
+                 static_S=None, smooth=None) -> QTensor:
+    """X_aug of the fused quantizer: RMSNorm (gamma), diagonal smoothing (per input
+    channel), channel gather (perm), NVFP4 quantization and S_cols residue columns."""
     x = _f32(x)
     rows, K = x.shape
     Ka = K + S_cols
@@ -133,10 +135,12 @@ def quantize_aug(x, gamma=None, eps: float = 1e-6, perm=None, S_cols: int = 0,
     codes, scales = _alloc(rows, Ka)
     S = np.zeros(1, np.float32)
     g = _f32(gamma) if gamma is not None else None
+    sm = _f32(smooth) if smooth is not None else None
     p = np.ascontiguousarray(perm, dtype=np.int32) if perm is not None else None
     sp = np.array([static_S], np.float32) if static_S is not None else None
     near = lib().or_quantize_aug(x, rows, K, K, g.ctypes.data if g is not None else None,
-                                 np.float32(eps), p.ctypes.data if p is not None else None,
+                                 np.float32(eps), sm.ctypes.data if sm is not None else None,
+                                 p.ctypes.data if p is not None else None,
                                  S_cols, sp.ctypes.data if sp is not None else None,
                                  codes, Ka // 2, scales, Ka // 16, S.ctypes.data)
     q = QTensor(codes, scales, S[0], Ka)

@@ -28,7 +28,11 @@
  *    q = fl(x * fl(1 / s)) (r = 0 when s = 0), code = E2M1(|q|) with the sign
  *    bit of x; every rounding is to nearest, ties to the even code, saturating;
  *  - the residue uses the FP32 dequantization fl(fl(e * d) * S);
- *  - RMSNorm sums squares in FP64 and rounds r to FP32.
+ *  - RMSNorm sums squares in FP64 and rounds r to FP32;
+ *  - the optional diagonal smoothing (abstract of "OSFP4: Joint Optimization of
+ *    Diagonal Smoothing and Block Scales for NVFP4 Quantization": one diagonal
+ *    matrix per linear projection, its inverse folded into the weight) multiplies
+ *    each input channel by its entry in FP32 after RMSNorm, before the reorder.
  */
 #include "nvfp4_oracle.h"
 
@@ -221,7 +225,7 @@ void or_perm_from_absmax(const float *v, int64_t K, int32_t *perm)
 }
 
 int64_t or_quantize_aug(const float *x, int64_t rows, int64_t K_in, int64_t ldx,
-                        const float *gamma, float eps, const int32_t *perm,
+                        const float *gamma, float eps, const float *smooth, const int32_t *perm,
                         int64_t S_cols, const float *static_S,
                         uint8_t *codes, int64_t ldc, uint8_t *scales, int64_t lds,
                         float *S_out)
@@ -230,9 +234,13 @@ int64_t or_quantize_aug(const float *x, int64_t rows, int64_t K_in, int64_t ldx,
     float *y = (float *)malloc(sizeof(float) * (size_t)(rows * K_in + 1));
     float *xa = (float *)malloc(sizeof(float) * (size_t)(rows * Ka + 1));
 
-    /* RMSNorm, then gather */
+    /* RMSNorm, then the diagonal smoothing multiply (one FP32 rounding per
+     * element; its inverse belongs to the weight, OSFP4 abstract), then gather */
     if (gamma) or_rmsnorm(x, rows, K_in, ldx, gamma, eps, y, K_in);
     else for (int64_t r = 0; r < rows; ++r) memcpy(y + r * K_in, x + r * ldx, sizeof(float) * (size_t)K_in);
+    if (smooth)
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t k = 0; k < K_in; ++k) y[r * K_in + k] = y[r * K_in + k] * smooth[k];
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t j = 0; j < K_in; ++j)
             xa[r * Ka + j] = y[r * K_in + (perm ? perm[j] : j)];

@@ -65,13 +65,14 @@ void or_channel_absmax(const float *x, int64_t rows, int64_t K, int64_t ldx,
 /* Channel order: channels sorted by v descending, ties by ascending index. */
 void or_perm_from_absmax(const float *v, int64_t K, int32_t *perm);
 
-/* Fused-quantizer reference: optional RMSNorm (gamma != NULL), optional channel
+/* Fused-quantizer reference: optional RMSNorm (gamma != NULL), optional diagonal
+ * smoothing y[:, k] *= smooth[k] in FP32 (smooth != NULL), optional channel
  * gather x'[:, j] = y[:, perm[j]] (perm != NULL), then NVFP4 quantization of
  * X_aug = [x' | R] with R = fl(x' - deq32(Q(x'))) on columns [0, S_cols).
  * X_aug is quantized as one tensor (one tensor scale). Output has K_in + S_cols
  * columns. S_cols == 0 gives the plain quantization of x'. */
 int64_t or_quantize_aug(const float *x, int64_t rows, int64_t K_in, int64_t ldx,
-                        const float *gamma, float eps, const int32_t *perm,
+                        const float *gamma, float eps, const float *smooth, const int32_t *perm,
                         int64_t S_cols, const float *static_S,
                         uint8_t *codes, int64_t ldc, uint8_t *scales, int64_t lds,
                         float *S_out);

@@ -343,3 +343,45 @@ def test_rmsnorm_two_roundings(orc):
     folded = (x * (r * g).astype(np.float32)).astype(np.float32)
     assert np.count_nonzero(once.view(np.uint32) != want.view(np.uint32)) > 0
     assert np.count_nonzero(folded.view(np.uint32) != want.view(np.uint32)) > 0
+
+
+# ---------------------------------------------------------------------------
+# Diagonal smoothing (abstract of "OSFP4: Joint Optimization of Diagonal Smoothing
+# and Block Scales for NVFP4 Quantization": one diagonal matrix per linear
+# projection; at run time the activation is multiplied by it and the weight holds
+# its inverse). Reading: each input channel k is multiplied by smooth[k] in FP32
+# after RMSNorm and before the channel reorder.
+# ---------------------------------------------------------------------------
+
+def test_smoothing_identity_and_power_of_two(orc):
+    x = inputs.small_random(61, 6, 512).float().numpy()
+    q = orc.quantize(x)
+    one = orc.quantize_aug(x, smooth=np.ones(512, np.float32))
+    assert np.array_equal(one.codes, q.codes) and np.array_equal(one.scales, q.scales) and one.S == q.S
+    # a constant power of two scales S exactly and leaves every code and block scale
+    for k in (-7, 3):
+        qk = orc.quantize_aug(x, smooth=np.full(512, 2.0 ** k, np.float32))
+        assert np.array_equal(qk.codes, q.codes) and np.array_equal(qk.scales, q.scales)
+        assert qk.S == np.float32(q.S * np.float32(2.0 ** k))
+
+
+def test_smoothing_matches_numpy_multiply(orc):
+    """Smoothing, RMSNorm and the reorder written out in numpy float32, then the
+    (separately pinned) plain quantizer, equal the fused reference bit for bit."""
+    x, g, xcal, _ = inputs.outlier_aug(rows=8, N=16, cal_rows=16)
+    K = 4096
+    sm = np.random.default_rng(62).uniform(0.25, 4.0, K).astype(np.float32)
+    perm = orc.calibrate_perm(xcal, g)
+    xf, gf = x.float().numpy(), g.float().numpy()
+    xd = xf.astype(np.float64)
+    ss = np.cumsum(xd * xd, axis=1)[:, -1]
+    r = (1.0 / np.sqrt(ss / K + np.float64(np.float32(1e-6)))).astype(np.float32)[:, None]
+    y = ((xf * r).astype(np.float32) * gf).astype(np.float32)
+    ys = (y * sm).astype(np.float32)[:, perm]
+    for S_cols in (0, 256):
+        fused = orc.quantize_aug(x, gamma=g, perm=perm, S_cols=S_cols, smooth=sm)
+        plain = orc.quantize_aug(np.ascontiguousarray(ys), S_cols=S_cols)
+        assert fused.S == plain.S
+        assert np.array_equal(fused.codes, plain.codes) and np.array_equal(fused.scales, plain.scales)
+    # smoothing changes the result on this input (the multiply is not skipped)
+    assert not np.array_equal(orc.quantize_aug(x, gamma=g, perm=perm).codes, fused.codes)
