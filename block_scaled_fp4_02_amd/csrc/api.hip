@@ -115,9 +115,10 @@ nvfp4_status check_opts(const nvfp4_quant_opts *o, int64_t K_in) {
     if (!o) return NVFP4_OK;
     if (o->residue_cols < 0 || o->residue_cols > K_in || o->residue_cols % 16) return NVFP4_ERR_SHAPE;
     if (o->gamma && !aligned(o->gamma, 16)) return NVFP4_ERR_ALIGN;
-    if (o->perm && K_in > 16384) return NVFP4_ERR_UNSUPPORTED;
+    if (o->perm && K_in > 32768) return NVFP4_ERR_UNSUPPORTED;   // the row staged in LDS (128 KiB)
     if (o->perm && !aligned(o->perm, 16)) return NVFP4_ERR_ALIGN;   // read as 16-byte vectors
     if (o->gamma && !(o->eps >= 0.0f)) return NVFP4_ERR_SHAPE;
+    if (o->smooth && !aligned(o->smooth, 16)) return NVFP4_ERR_ALIGN;   // read as 16-byte vectors
     return NVFP4_OK;
 }
 
@@ -134,6 +135,7 @@ nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in,
     q.perm = opts ? opts->perm : nullptr;
     q.res_cols = opts ? opts->residue_cols : 0;
     q.static_S = opts ? opts->static_tensor_scale : nullptr;
+    q.smooth = opts ? opts->smooth : nullptr;
     q.codes = out.codes; q.ldc = out.ld_codes; q.scales = out.scales; q.lds = out.ld_scales;
     q.S_out = out.tensor_scale;
     q.partials = partials; q.rscale = rscale;
@@ -379,7 +381,7 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
     const size_t sb = gemm_ws(M, N, K, S);
     uint8_t *scratch = sb ? c.take(sb) : nullptr;
     if (!c.ok) return NVFP4_ERR_WORKSPACE;
-    const bool plain = !opts || (!opts->gamma && !opts->perm);
+    const bool plain = !opts || (!opts->gamma && !opts->perm && !opts->smooth);
     const bool skinny = skinny_rows(M, K, S);
     if (N > 0 && plain && skinny && decode_can_fuse(M, N, K, S, xt == NVFP4_BF16))
         return enqueue_fused(x, xt, ldx, opts ? opts->static_tensor_scale : nullptr, aq, *w, M, K, S, y, yt, ldy,
@@ -448,7 +450,7 @@ const char *nvfp4_status_string(nvfp4_status s) {
 }
 
 const char *nvfp4_last_error(void) { return g_last_error; }
-int nvfp4_version(void) { return 10000; }
+int nvfp4_version(void) { return 10100; }
 
 int nvfp4_host_e4m3_encode(float v) { return (int)e4m3_rne_sat(v); }
 int nvfp4_host_e2m1_encode(float q) { return (int)(e2m1_rne_sat(std::fabs(q)) | ((f2u(q) >> 31) << 3)); }

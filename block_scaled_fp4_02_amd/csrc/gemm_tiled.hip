@@ -266,7 +266,7 @@ __device__ inline RowChunk load_chunk2_tiled(const uint8_t *codes, int64_t ldc, 
     return rc;
 }
 
-// Large tiles (no residue columns): BM x BN per workgroup of NW waves (2 along
+// Large tiles: BM x BN per workgroup of NW waves (2 along
 // M x NW/2 along N), each wave a BM/2 x 2 BN/NW block of 16 x 16 tiles, so
 // every fragment read from LDS feeds 4 to 8 MFMAs (against 4 for the 64 x 64
 // wave tile above). 256 x 256 runs 8 waves (two per SIMD, 128 accumulator
@@ -279,6 +279,13 @@ __device__ inline RowChunk load_chunk2_tiled(const uint8_t *codes, int64_t ldc, 
 //    over the MFMA groups of step s;
 //  * A fragments are read from LDS four MFMA groups ahead, the second
 //    k-chunk's B fragments during the last groups of the first.
+// Residue columns (the augmented K + S product of the ARCQuant article,
+// sections 3.1-3.2; selective compensation of prompts in the ResServe
+// abstract) are further k-steps after the K / BK main ones: step K / BK + r
+// multiplies the activation's columns K + BK r.. (the quantized residue) with
+// the weight's columns BK r.. (the W_aug tail is W's own first S columns, read
+// again, never materialized). They run through the same pipeline and split-K
+// ranges; K must be a multiple of 32 so their chunks stay 16-byte aligned.
 template <int BM, int BN, int NW, int WPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void tiled2_kernel(TArgs a) {
@@ -300,8 +307,10 @@ void tiled2_kernel(TArgs a) {
     if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
     const int tn = bid / a.tiles_m, tm = bid % a.tiles_m;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    // this workgroup's k-steps [s0, s0 + ksteps) (split-K: range blockIdx.y)
-    const int64_t kall = (a.K + BK - 1) / BK;
+    // this workgroup's k-steps [s0, s0 + ksteps) of the main and residue steps
+    // (split-K: range blockIdx.y)
+    const int64_t kmain = (a.K + BK - 1) / BK;
+    const int64_t kall = kmain + (a.res_cols + BK - 1) / BK;
     const int64_t s0 = (int64_t)blockIdx.y * a.kchunk;
     const int64_t ksteps = (s0 + a.kchunk < kall ? s0 + a.kchunk : kall) - s0;
 
@@ -314,15 +323,18 @@ void tiled2_kernel(TArgs a) {
     };
     RowChunk rq0[NCH], rq1[NCH];
     auto gload = [&](int64_t s, RowChunk *q) {
-        const int64_t k = (s0 + s) * BK;
+        const bool res = s0 + s >= kmain;      // a residue step (wave-uniform)
+        const int64_t kw = (res ? s0 + s - kmain : s0 + s) * BK;      // weight column
+        const int64_t ka = res ? a.K + kw : kw;                        // activation column
+        const int64_t wend = res ? a.res_cols : a.K, aend = res ? a.K + a.res_cols : a.K;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int r = crow(c), h = chalf(c);
             if (c < A_ITERS)
-                q[c] = load_chunk2(a.a_codes, a.a_ldc, a.a_scales, a.a_lds, m0 + r, a.M, k + 32 * h, a.K);
+                q[c] = load_chunk2(a.a_codes, a.a_ldc, a.a_scales, a.a_lds, m0 + r, a.M, ka + 32 * h, aend);
             else
-                q[c] = a.w_tiled ? load_chunk2_tiled(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K)
-                                 : load_chunk2(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, k + 32 * h, a.K);
+                q[c] = a.w_tiled ? load_chunk2_tiled(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, kw + 32 * h, wend)
+                                 : load_chunk2(a.w_codes, a.w_ldc, a.w_scales, a.w_lds, n0 + r, a.N, kw + 32 * h, wend);
         }
     };
     // decode unit u = fragment (u & 3) of chunk (u >> 2) into stage st
@@ -482,13 +494,17 @@ hipError_t run(const TArgs &a0, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The pipelined large-tile kernel takes residue columns when K is a multiple of
+// 32; otherwise (and at M <= 64) the 64 x 64-per-wave tile kernel does.
+inline bool large_tiles(int64_t M, int64_t K, int64_t S) { return M > 64 && (S == 0 || K % 32 == 0); }
+
 // Split-K ranges for the large-tile product: only when even 256 x 256 tiles
-// leave most of the chip idle and K is long; P ranges of at least 32 k-steps
-// until the chip holds ~one workgroup per CU.
+// leave most of the chip idle and K (+ S residue columns) is long; P ranges of
+// at least 32 k-steps until the chip holds ~one workgroup per CU.
 int prefill_splits(int64_t M, int64_t N, int64_t K, int64_t S) {
-    if (S > 0 || M <= 64) return 1;
+    if (!large_tiles(M, K, S)) return 1;
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    const int64_t ksteps = (K + BK - 1) / BK;
+    const int64_t ksteps = (K + BK - 1) / BK + (S + BK - 1) / BK;
     if (tiles * 2 >= 192 || ksteps < 256) return 1;     // large enough for the unsplit plans
     int P = 1;
     while (P < 8 && tiles * P < 224 && ksteps / (2 * P) >= 32) P *= 2;
@@ -503,18 +519,21 @@ hipError_t launch_prefill_impl(const PrefillLaunch &g, hipStream_t st) {
     a.M = g.M; a.N = g.N; a.K = g.K; a.res_cols = g.res_cols;
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
     a.tiles_m = a.tiles_n = 0;
-    a.P = 1; a.kchunk = (g.K + BK - 1) / BK; a.part = nullptr;
-    if (g.res_cols > 0) {
-        if (g.M <= 64) return run<64, 128, true>(a, st);
-        return run<128, 128, true>(a, st);
+    const int64_t ktot = (g.K + BK - 1) / BK + (g.res_cols + BK - 1) / BK;
+    a.P = 1; a.kchunk = ktot; a.part = nullptr;
+    if (!large_tiles(g.M, g.K, g.res_cols)) {
+        if (g.res_cols > 0) {
+            if (g.M <= 64) return run<64, 128, true>(a, st);
+            return run<128, 128, true>(a, st);
+        }
+        return run<64, 128, false>(a, st);
     }
-    if (g.M <= 64) return run<64, 128, false>(a, st);
     const int P = prefill_splits(g.M, g.N, g.K, g.res_cols);
     if (P > 1) {
         if (!g.scratch || g.scratch_bytes < (size_t)P * (size_t)g.M * (size_t)g.N * sizeof(float))
             return hipErrorInvalidValue;
         a.P = P;
-        a.kchunk = ((g.K + BK - 1) / BK + P - 1) / P;
+        a.kchunk = (ktot + P - 1) / P;
         a.part = static_cast<float *>(g.scratch);
         return run2<256, 256, 8, 2>(a, st);
     }

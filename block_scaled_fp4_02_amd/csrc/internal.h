@@ -17,6 +17,7 @@ struct QuantLaunch {
     const int32_t *perm;                    // or nullptr
     int64_t res_cols;                       // residue columns appended at K_in
     const float *static_S;                  // or nullptr
+    const float *smooth;                    // per input channel multiplier (FP32 [K_in]) or nullptr
     uint8_t *codes; int64_t ldc;
     uint8_t *scales; int64_t lds;
     float *S_out;

@@ -58,6 +58,19 @@ __device__ inline void gamma16(const uint16_t *g, int64_t off, float *v) {
     }
 }
 
+// Diagonal smoothing (OSFP4 abstract: one diagonal matrix per linear projection,
+// multiplied into the activation at run time; its inverse lives in the weight):
+// v[i] *= s[off + i] for 16 consecutive input channels, one FP32 rounding each.
+__device__ inline void smooth16(const float *s, int64_t off, float *v) {
+    const float4 *p = reinterpret_cast<const float4 *>(s + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 q = p[i];
+        v[4 * i] = v[4 * i] * q.x; v[4 * i + 1] = v[4 * i + 1] * q.y;
+        v[4 * i + 2] = v[4 * i + 2] * q.z; v[4 * i + 3] = v[4 * i + 3] * q.w;
+    }
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -99,7 +112,7 @@ __device__ inline double block_sum_d(double v, double *sh) {
 
 template <int XT>
 __global__ __launch_bounds__(kThreads) void amax_plain_kernel(const void *x, int64_t rows, int64_t K,
-                                                             int64_t ldx, float *partials) {
+                                                             int64_t ldx, const float *smooth, float *partials) {
     __shared__ float sh[kThreads / 64];
     const int64_t nb = K / 16, total = rows * nb;
     float m = 0.0f;
@@ -108,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void amax_plain_kernel(const void *x, int
         const int64_t r = c / nb, b = c - r * nb;
         float v[16];
         load16<XT>(x, r * ldx + 16 * b, v);
+        if (smooth) smooth16(smooth, 16 * b, v);
 #pragma unroll
         for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
     }
@@ -134,7 +148,8 @@ __device__ inline float row_rms_scale(const void *x, int64_t row, int64_t K, int
 template <int XT>
 __global__ __launch_bounds__(kThreads) void amax_rmsnorm_kernel(const void *x, int64_t rows, int64_t K,
                                                                int64_t ldx, const uint16_t *gamma,
-                                                               float eps, float *rscale, float *partials) {
+                                                               float eps, const float *smooth, float *rscale,
+                                                               float *partials) {
     __shared__ float sh[kThreads / 64];
     __shared__ double shd[kThreads / 64];
     float m = 0.0f;
@@ -148,9 +163,11 @@ __global__ __launch_bounds__(kThreads) void amax_rmsnorm_kernel(const void *x, i
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float y = v[i] * r;
-                y = y * g[i];
-                m = fmaxf(m, fabsf(y));
+                v[i] = y * g[i];
             }
+            if (smooth) smooth16(smooth, 16 * b, v);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
         }
     }
     m = block_max(m, sh);
@@ -171,6 +188,7 @@ struct QArgs {
     const float *partials; int npart;
     const float *rscale;
     float eps;
+    const float *smooth;                      // per input channel, or nullptr
 };
 
 __device__ inline float tensor_scale(const QArgs &a, float *sh) {
@@ -251,6 +269,7 @@ __global__ __launch_bounds__(kThreads) void quantize_flat_kernel(QArgs a) {
                         v[16 * b + i] = y * gm[i];
                     }
                 }
+                if (a.smooth) smooth16(a.smooth, col0 + 16 * b, v + 16 * b);
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[16 * b + i] = 0.0f;
@@ -409,10 +428,15 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QArgs a, unsign
     for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
         float v[16];
         load16<XT>(a.x, row * a.ldx + 16 * b, v);
+        if (NORM) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ss += (double)v[i] * (double)v[i];
+        } else if (a.smooth) {
+            smooth16(a.smooth, 16 * b, v);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            if (NORM) ss += (double)v[i] * (double)v[i];
-            else m = fmaxf(m, fabsf(v[i]));
+            if (!NORM) m = fmaxf(m, fabsf(v[i]));
             rowbuf[i * KB + b] = v[i];
         }
     }
@@ -420,14 +444,18 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QArgs a, unsign
         ss = block_sum_d(ss, shd);
         const float r = (float)(1.0 / sqrt(ss / (double)K + (double)a.eps));
         for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
-            float g[16];
+            float g[16], y[16];
             gamma16(a.gamma, 16 * b, g);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float y = rowbuf[i * KB + b] * r;
-                y = y * g[i];
-                rowbuf[i * KB + b] = y;
-                m = fmaxf(m, fabsf(y));
+                const float t = rowbuf[i * KB + b] * r;
+                y[i] = t * g[i];
+            }
+            if (a.smooth) smooth16(a.smooth, 16 * b, y);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                rowbuf[i * KB + b] = y[i];
+                m = fmaxf(m, fabsf(y[i]));
             }
         }
     }
@@ -446,13 +474,14 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QArgs a, unsign
                     for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
                         float v[16], g[16];
                         load16<XT>(a.x, rr * a.ldx + 16 * b, v);
-                        if (NORM) gamma16(a.gamma, 16 * b, g);
+                        if (NORM) {
+                            gamma16(a.gamma, 16 * b, g);
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            float y = v[i];
-                            if (NORM) { y = y * rs; y = y * g[i]; }
-                            mm = fmaxf(mm, fabsf(y));
+                            for (int i = 0; i < 16; ++i) { const float t = v[i] * rs; v[i] = t * g[i]; }
                         }
+                        if (a.smooth) smooth16(a.smooth, 16 * b, v);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) mm = fmaxf(mm, fabsf(v[i]));
                     }
                 }
             }
@@ -507,6 +536,7 @@ __global__ __launch_bounds__(kThreads) void quantize_perm_kernel(QArgs a) {
                     v[i] = y * gm[i];
                 }
             }
+            if (a.smooth) smooth16(a.smooth, 16 * b, v);
 #pragma unroll
             for (int i = 0; i < 16; ++i) rowbuf[16 * b + i] = v[i];
         }
@@ -584,14 +614,14 @@ static hipError_t allow_lds(const void *fn, size_t lds) {
 }
 
 hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
-    const bool norm = q.gamma != nullptr, perm = q.perm != nullptr;
+    const bool norm = q.gamma != nullptr, perm = q.perm != nullptr, smooth = q.smooth != nullptr;
     const int64_t nb = q.rows * (q.K_in / 16);
-    if ((norm || perm) && q.slots && q.rows >= 1 && q.rows <= kSmallMaxG && q.K_in > 0 && q.K_in <= kRowsMaxK) {
+    if ((norm || perm || smooth) && q.slots && q.rows >= 1 && q.rows <= kSmallMaxG && q.K_in > 0 && q.K_in <= kRowsMaxK) {
         QArgs a;
         a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
         a.gamma = q.gamma; a.perm = q.perm; a.res_cols = q.res_cols; a.static_S = q.static_S;
         a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
-        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps;
+        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps; a.smooth = q.smooth;
         const size_t lds = (size_t)q.K_in * sizeof(float);
         const int g = (int)q.rows;
 #define QR(XT, NM, PM)                                                                              \
@@ -601,21 +631,23 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
         quantize_rows_kernel<XT, NM, PM><<<g, kThreads, lds, st>>>(a, q.slots, q.spin);             \
     } while (0)
         if (q.xt == IN_BF16) {
-            if (norm && perm) QR(IN_BF16, true, true); else if (norm) QR(IN_BF16, true, false); else QR(IN_BF16, false, true);
+            if (norm && perm) QR(IN_BF16, true, true); else if (norm) QR(IN_BF16, true, false);
+            else if (perm) QR(IN_BF16, false, true); else QR(IN_BF16, false, false);
         } else {
-            if (norm && perm) QR(IN_F32, true, true); else if (norm) QR(IN_F32, true, false); else QR(IN_F32, false, true);
+            if (norm && perm) QR(IN_F32, true, true); else if (norm) QR(IN_F32, true, false);
+            else if (perm) QR(IN_F32, false, true); else QR(IN_F32, false, false);
         }
 #undef QR
         return hipGetLastError();
     }
-    if (!norm && !perm && q.slots && q.rows <= 32 && nb > 0 && nb <= (int64_t)kSmallMaxG * kThreads * kSmallPer) {
+    if (!norm && !perm && !smooth && q.slots && q.rows <= 32 && nb > 0 && nb <= (int64_t)kSmallMaxG * kThreads * kSmallPer) {
         int G = (int)((nb + kThreads - 1) / kThreads);
         if (G > kSmallMaxG) G = kSmallMaxG;
         QArgs a;
         a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
         a.gamma = nullptr; a.perm = nullptr; a.res_cols = q.res_cols; a.static_S = q.static_S;
         a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
-        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps;
+        a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps; a.smooth = nullptr;
         if (q.xt == IN_BF16)
             quantize_small_kernel<IN_BF16><<<G, kThreads, 0, st>>>(a, q.slots, G, q.spin);
         else
@@ -628,15 +660,15 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
             npart = (int)(q.rows < kAmaxPartials ? q.rows : kAmaxPartials);
             if (npart < 1) npart = 1;
             if (q.xt == IN_BF16)
-                amax_rmsnorm_kernel<IN_BF16><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.gamma, q.eps, q.rscale, q.partials);
+                amax_rmsnorm_kernel<IN_BF16><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.gamma, q.eps, q.smooth, q.rscale, q.partials);
             else
-                amax_rmsnorm_kernel<IN_F32><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.gamma, q.eps, q.rscale, q.partials);
+                amax_rmsnorm_kernel<IN_F32><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.gamma, q.eps, q.smooth, q.rscale, q.partials);
         } else {
             npart = amax_grid(q.rows, q.K_in);
             if (q.xt == IN_BF16)
-                amax_plain_kernel<IN_BF16><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.partials);
+                amax_plain_kernel<IN_BF16><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.smooth, q.partials);
             else
-                amax_plain_kernel<IN_F32><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.partials);
+                amax_plain_kernel<IN_F32><<<npart, kThreads, 0, st>>>(q.x, q.rows, q.K_in, q.ldx, q.smooth, q.partials);
         }
     } else if (norm) {
         const int g = (int)(q.rows < 4096 ? (q.rows > 0 ? q.rows : 1) : 4096);
@@ -652,7 +684,7 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
     a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
     a.gamma = q.gamma; a.perm = q.perm; a.res_cols = q.res_cols; a.static_S = q.static_S;
     a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
-    a.partials = q.partials; a.npart = npart; a.rscale = q.rscale; a.eps = q.eps;
+    a.partials = q.partials; a.npart = npart; a.rscale = q.rscale; a.eps = q.eps; a.smooth = q.smooth;
 
     if (perm) {
         const int g = (int)(q.rows < 2048 ? (q.rows > 0 ? q.rows : 1) : 2048);

@@ -38,7 +38,7 @@ class _CTensor(C.Structure):
 
 class _COpts(C.Structure):
     _fields_ = [("gamma", C.c_void_p), ("eps", C.c_float), ("perm", C.c_void_p),
-                ("residue_cols", C.c_int64), ("static_tensor_scale", C.c_void_p)]
+                ("residue_cols", C.c_int64), ("static_tensor_scale", C.c_void_p), ("smooth", C.c_void_p)]
 
 
 _lib = None
@@ -186,10 +186,13 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return buf
 
 
-def _opts(gamma, eps, perm, residue_cols, static_scale):
-    if gamma is None and perm is None and not residue_cols and static_scale is None:
+def _opts(gamma, eps, perm, residue_cols, static_scale, smooth=None):
+    if gamma is None and perm is None and not residue_cols and static_scale is None and smooth is None:
         return None, []
     keep = []
+    if smooth is not None:
+        assert smooth.dtype == torch.float32 and smooth.is_contiguous()
+        keep.append(smooth)
     if gamma is not None:
         assert gamma.dtype == torch.bfloat16 and gamma.is_contiguous()
         keep.append(gamma)
@@ -202,18 +205,18 @@ def _opts(gamma, eps, perm, residue_cols, static_scale):
                                         device=(gamma if gamma is not None else perm).device
                                         if (gamma is not None or perm is not None) else "cuda")
         keep.append(static_scale)
-    o = _COpts(_ptr(gamma), C.c_float(eps), _ptr(perm), int(residue_cols), _ptr(static_scale))
+    o = _COpts(_ptr(gamma), C.c_float(eps), _ptr(perm), int(residue_cols), _ptr(static_scale), _ptr(smooth))
     return o, keep
 
 
 def quantize(x: torch.Tensor, gamma=None, eps: float = 1e-6, perm=None, residue_cols: int = 0,
-             static_scale=None) -> NVFP4Tensor:
-    """NVFP4-quantize rows of x (bf16/f32, 2-D), optionally fused with RMSNorm, a channel
-    gather and residue columns; returns rows x (K + residue_cols)."""
+             static_scale=None, smooth=None) -> NVFP4Tensor:
+    """NVFP4-quantize rows of x (bf16/f32, 2-D), optionally fused with RMSNorm, a diagonal
+    smoothing multiply, a channel gather and residue columns; returns rows x (K + residue_cols)."""
     assert x.dim() == 2 and x.stride(1) == 1
     rows, K = x.shape
     out = NVFP4Tensor.empty(rows, K + residue_cols, x.device)
-    o, keep = _opts(gamma, eps, perm, residue_cols, static_scale)
+    o, keep = _opts(gamma, eps, perm, residue_cols, static_scale, smooth)
     n = lib().nvfp4_workspace_size(0, rows, 0, K, residue_cols)
     ws = workspace(n, x.device)
     ct = out.c()
@@ -269,7 +272,7 @@ def gemm_noalloc(a, w: NVFP4Tensor, out: torch.Tensor) -> torch.Tensor:
 
 def gemm_residue(x: torch.Tensor, w: NVFP4Tensor, residue_cols: int, gamma=None, eps: float = 1e-6,
                  perm=None, static_scale=None, out_dtype=torch.float32, return_aug: bool = False,
-                 out: torch.Tensor | None = None):
+                 out: torch.Tensor | None = None, smooth=None):
     """Y = s_aug [Q(X') | Q(R)] [Q(W) | Q(W[:, :S])]^T with X' = perm/RMSNorm(x), R its residue
     on columns [0, S). w must already be in the channel order of perm."""
     assert x.dim() == 2 and x.stride(1) == 1
@@ -277,9 +280,9 @@ def gemm_residue(x: torch.Tensor, w: NVFP4Tensor, residue_cols: int, gamma=None,
     N = w.rows
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    o, keep = _opts(gamma, eps, perm, residue_cols, static_scale)
+    o, keep = _opts(gamma, eps, perm, residue_cols, static_scale, smooth)
     if o is None:
-        o = _COpts(None, C.c_float(eps), None, 0, None)
+        o = _COpts(None, C.c_float(eps), None, 0, None, None)
     aug = NVFP4Tensor.empty(M, K + residue_cols, x.device) if return_aug else None
     augc = aug.c() if aug is not None else None
     n = lib().nvfp4_workspace_size(2, M, N, K, residue_cols)

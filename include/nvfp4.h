@@ -117,12 +117,19 @@ typedef struct {
                                       (ARCQuant section 3.1; ResServe abstract). 0 = none,
                                       S = K_in gives K -> 2K. Multiple of 16.             */
     const float   *static_tensor_scale; /* device float, or NULL = dynamic amax / 2688   */
+    const float   *smooth;         /* diagonal smoothing: device FP32 [K_in], or NULL. Input
+                                      channel k (before the reorder, after RMSNorm) is
+                                      multiplied by smooth[k] in FP32 before quantization;
+                                      the caller folds 1/smooth into the weight (abstract of
+                                      "OSFP4: Joint Optimization of Diagonal Smoothing and
+                                      Block Scales for NVFP4 Quantization"). 16-byte aligned,
+                                      else NVFP4_ERR_ALIGN                                   */
 } nvfp4_quant_opts;
 
 /* Quantize x (rows x K_in, dtype xt, leading dimension ldx elements) into
  * `out`, which must have rows == rows and K == K_in + opts->residue_cols.
  * opts may be NULL (plain quantization with a dynamic tensor scale). K_in with
- * a permutation is limited to 16384. Workspace: nvfp4_workspace_size(0, rows, 0, K_in, S). */
+ * a permutation is limited to 32768 (a row is staged in LDS). Workspace: nvfp4_workspace_size(0, rows, 0, K_in, S). */
 nvfp4_status nvfp4_quantize(const void *x, int xt, int64_t rows, int64_t K_in, int64_t ldx,
                             const nvfp4_quant_opts *opts, const nvfp4_tensor *out,
                             void *ws, size_t ws_bytes, void *stream);

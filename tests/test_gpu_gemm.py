@@ -389,3 +389,75 @@ def test_prefill_large_tiles_ragged(nv, orc, M, N, K):
     ref = orc.gemm_pairs(xq, wsub, ms, np.array([wpos[n] for n in ns]))
     err = gemm_error(y.cpu().numpy()[ms, ns], ref)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("M,S", [(64, 256), (8, 0), (300, 128)])
+def test_smoothed_product(nv, orc, aug_case, M, S, layout):
+    """Runtime diagonal smoothing with its inverse folded into the weight (OSFP4 abstract):
+    Y = Q(smooth(RMSNorm(X))[:, perm]) Q((W diag(1/s))[:, perm])^T, with residue columns;
+    every output against the oracle, X_aug bit for bit."""
+    x, g, perm, w_perm, _ = aug_case
+    K = 4096
+    if M > x.shape[0]:
+        x = inputs.activations(4, 1, M, K, 0.01, 50.0)
+    else:
+        x = x[:M]
+    sm = np.random.default_rng(M + S).uniform(0.5, 2.0, K).astype(np.float32)
+    w = inputs.weights(4, 0, 14336, K, 0.02)
+    ws = (w.float() / torch.from_numpy(sm)[None, :]).to(torch.bfloat16)   # the inverse, folded offline
+    ws_perm = ws[:, torch.from_numpy(perm).long()]
+    note(f"smoothed product M={M} S={S} {layout}")
+    wq = _layout(nv, nv.quantize(ws_perm.to(DEV)), layout)
+    y, aug = nv.gemm_residue(x.to(DEV), wq, S, gamma=g.to(DEV), eps=1e-6, perm=torch.from_numpy(perm).to(DEV),
+                             smooth=torch.from_numpy(sm).to(DEV), return_aug=True)
+    torch.cuda.synchronize()
+    xa = orc.quantize_aug(x, gamma=g, eps=1e-6, perm=perm, S_cols=S, smooth=sm)
+    assert_qtensor_equal(aug, xa, "X_aug")
+    ref = orc.gemm_blas(xa, orc.weight_aug(ws_perm, S))
+    err = gemm_error(y.cpu().numpy(), ref)
+    assert err <= TOL, err
+
+
+def _waug(q, S):
+    """W_aug = [W' | W'[:, :S]] from the quantized W': the tail's codes and block scales
+    are the head's (same blocks, same tensor scale)."""
+    import oracle
+    return oracle.QTensor(np.ascontiguousarray(np.concatenate([q.codes, q.codes[:, :S // 2]], axis=1)),
+                          np.ascontiguousarray(np.concatenate([q.scales, q.scales[:, :S // 16]], axis=1)),
+                          q.S, q.K + S)
+
+
+@pytest.mark.parametrize("M,N,K,S,layouts", [(520, 3000, 4096, 256, LAYOUTS), (2048, 28672, 8192, 512, ["tiled"]),
+                                             (512, 8192, 28672, 1024, ["tiled"]), (300, 1000, 2048, 2048, LAYOUTS)])
+def test_prefill_selective_residue(nv, orc, M, N, K, S, layouts):
+    """Selective compensation at prompt sizes (ResServe abstract; ARCQuant article, sections
+    3.1-3.2): RMSNorm, calibrated reorder and the residue of the top S channels, in the
+    pipelined matrix-core product (split K at 512 x 8192 x 28672). X_aug bit for bit; the
+    outputs at every tile's corners and an interior point against the oracle."""
+    rng = np.random.default_rng(M + S)
+    x = inputs.activations(5, 2, M, K, 0.01, 50.0)
+    g = inputs.gamma(5, 2, K)
+    xcal = inputs.activations(5, 2, 512, K, 0.01, 50.0, tensor=inputs.T_XCAL)
+    perm = orc.calibrate_perm(xcal, g)
+    w = inputs.weights(5, 2, N, K, 0.015)[:, torch.from_numpy(perm).long()]
+    note(f"prefill selective residue M={M} N={N} K={K} S={S}: quantize")
+    wq = nv.quantize(w.to(DEV))
+    pd = torch.from_numpy(perm).to(DEV)
+    xa = orc.quantize_aug(x, gamma=g, eps=1e-6, perm=perm, S_cols=S)
+    rows = np.unique(np.concatenate([_tile_lines(M, rng), rng.integers(0, M, 64)]))
+    cols = np.unique(np.concatenate([_tile_lines(N, rng), rng.integers(0, N, 64)]))
+    S_w = orc.tensor_scale(w)
+    wsub = _waug(orc.quantize(w[cols], static_S=float(S_w)), S)
+    xsub = orc.QTensor(np.ascontiguousarray(xa.codes[rows]), np.ascontiguousarray(xa.scales[rows]), xa.S, K + S)
+    ref = orc.gemm_blas(xsub, wsub)
+    for layout in layouts:
+        note(f"prefill selective residue M={M} N={N} K={K} S={S} {layout}")
+        wl = _layout(nv, wq, layout)
+        y, aug = nv.gemm_residue(x.to(DEV), wl, S, gamma=g.to(DEV), eps=1e-6, perm=pd, return_aug=True)
+        yb = nv.gemm_residue(x.to(DEV), wl, S, gamma=g.to(DEV), eps=1e-6, perm=pd, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert_qtensor_equal(aug, xa, "X_aug")
+        err = gemm_error(y.cpu().numpy()[np.ix_(rows, cols)], ref)
+        assert err <= TOL, (err, layout)
+        assert bf16_bound_ok(yb.float().cpu().numpy()[np.ix_(rows, cols)], ref), layout

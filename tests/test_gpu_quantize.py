@@ -205,12 +205,12 @@ def test_rows_quantizer_wait_fallback(nv, orc, rows, norm, use_perm, S, monkeypa
     assert_qtensor_equal(q1, ref, "fallback")
 
 
-@pytest.mark.parametrize("rows,norm", [(4, True), (70, False)])
-def test_row_staging_at_k_16384(nv, orc, rows, norm):
+@pytest.mark.parametrize("rows,norm,K", [(4, True, 16384), (70, False, 16384), (4, True, 28672), (70, True, 32768)])
+def test_row_staging_at_large_k(nv, orc, rows, norm, K):
     """The reorder kernels stage a whole row (K floats) in LDS: at K = 16384 that
-    is 64 KiB plus the kernel's own words. 4 rows take the one-launch row
-    quantizer (RMSNorm + reorder + residue), 70 rows the two-pass gather path."""
-    K = 16384
+    is 64 KiB plus the kernel's own words, at 32768 (the limit) 128 KiB. Up to
+    K = 16384, 4 rows take the one-launch row quantizer (RMSNorm + reorder +
+    residue); 70 rows, and longer rows, the two-pass gather path."""
     x = inputs.small_random(400 + rows, rows, K)
     g = inputs.gamma(9, 0, K)
     perm = np.random.default_rng([0, 102, rows]).permutation(K).astype(np.int32)
@@ -223,3 +223,24 @@ def test_row_staging_at_k_16384(nv, orc, rows, norm):
     torch.cuda.synchronize()
     ref = orc.quantize_aug(x, gamma=g if norm else None, eps=1e-6, perm=perm, S_cols=S)
     assert_qtensor_equal(q, ref, f"rows={rows}")
+
+
+@pytest.mark.parametrize("rows,K,norm,perm,S", [(4, 4096, False, False, 0), (64, 4096, True, True, 256),
+                                                 (7, 1040, True, False, 64), (33, 2048, False, True, 0),
+                                                 (130, 4096, True, True, 512), (300, 1024, False, False, 0),
+                                                 (130, 528, True, False, 528), (20, 20000, False, False, 0)])
+def test_smoothing_fused(nv, orc, rows, K, norm, perm, S):
+    """Diagonal smoothing inside the fused quantizer (per input channel, after RMSNorm,
+    before the reorder): every kernel path -- one workgroup per row (rows <= 64,
+    K <= 16384), the two-pass amax + encode and the row-gather path -- bit for bit."""
+    x = inputs.small_random(900 + rows + K, rows, K)
+    sm = np.random.default_rng(K + rows).uniform(0.125, 8.0, K).astype(np.float32)
+    g = inputs.gamma(9, rows, K) if norm else None
+    p = np.random.default_rng(rows).permutation(K).astype(np.int32) if perm else None
+    note(f"quantize smoothing rows={rows} K={K} norm={norm} perm={perm} S={S}")
+    q = nv.quantize(x.to(DEV), gamma=g.to(DEV) if norm else None, eps=1e-6,
+                    perm=torch.from_numpy(p).to(DEV) if perm else None, residue_cols=S,
+                    smooth=torch.from_numpy(sm).to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.quantize_aug(x, gamma=g, eps=1e-6, perm=p, S_cols=S, smooth=sm)
+    assert_qtensor_equal(q, ref, "smoothed")

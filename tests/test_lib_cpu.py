@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.nvfp4_version() == 10000
+    assert L.nvfp4_version() == 10100
     assert L.nvfp4_status_string(0) == b"ok"
     assert L.nvfp4_status_string(5) == b"workspace too small"
 
@@ -121,10 +121,13 @@ def test_argument_errors_before_launch(L):
     o = _COpts(None, C.c_float(1e-6), vp((1 << 20) + 4), 0, None)
     assert L.nvfp4_quantize(fake, 0, 4, 64, 64, C.byref(o), C.byref(out), ws, wsn, None) == 3
     assert L.nvfp4_gemm_residue(fake, 0, 4, 64, 64, C.byref(o), C.byref(w), fake, 1, 32, None, ws, wsn, None) == 3
+    # smoothing vector not 16-byte aligned
+    o = _COpts(None, C.c_float(1e-6), None, 0, None, vp((1 << 20) + 8))
+    assert L.nvfp4_quantize(fake, 0, 4, 64, 64, C.byref(o), C.byref(out), ws, wsn, None) == 3
     # permutation beyond the staged-row limit
     o = _COpts(None, C.c_float(1e-6), fake, 0, None)
-    assert L.nvfp4_quantize(fake, 0, 4, 32768, 32768, C.byref(o),
-                            C.byref(_tensor(4, 32768, codes=1 << 20, scales=1 << 21, scale=1 << 22)),
+    assert L.nvfp4_quantize(fake, 0, 4, 32784, 32784, C.byref(o),
+                            C.byref(_tensor(4, 32784, codes=1 << 20, scales=1 << 21, scale=1 << 22)),
                             ws, 1 << 30, None) == 6
 
 
