@@ -61,6 +61,12 @@ def lib():
         L.or_gemm_exact.argtypes = [u8p, i64, u8p, i64, C.c_float, u8p, i64, u8p, i64, C.c_float,
                                     i64, i64, i64, f64p, i64]
         L.or_gemm_exact.restype = C.c_int
+        L.or_e8m0_value.argtypes = [C.c_int]; L.or_e8m0_value.restype = C.c_double
+        L.or_mx_block_exponent.argtypes = [f32p]; L.or_mx_block_exponent.restype = C.c_int
+        L.or_mx_quantize.argtypes = [f32p, i64, i64, i64, u8p, i64, u8p, i64]
+        L.or_mx_dequantize.argtypes = [u8p, i64, u8p, i64, i64, i64, f64p, i64]
+        L.or_mx_quantize_aug.argtypes = [f32p, i64, i64, i64, i64, u8p, i64, u8p, i64]
+        L.or_mx_gemm.argtypes = [u8p, i64, u8p, i64, u8p, i64, u8p, i64, i64, i64, i64, f64p, i64]
         _lib = L
     return _lib
 
@@ -263,3 +269,73 @@ def gemm_error(y, y_ref) -> float:
     floor = 1e-3 * np.max(np.abs(y_ref))
     den = np.maximum(np.abs(y_ref), floor if floor > 0 else 1e-30)
     return float(np.max(np.abs(y - y_ref) / den))
+
+
+# ---------------------------------------------------------------------- MXFP4
+# E2M1 codes (the same packing) with one E8M0 scale byte per 32 elements along K
+# and no tensor scale; the rule is stated in nvfp4_oracle.c.
+
+class MXTensor:
+    """An MXFP4 tensor in the canonical layout: codes [rows][K/2], scales [rows][K/32]."""
+
+    def __init__(self, codes: np.ndarray, scales: np.ndarray, K: int):
+        self.codes, self.scales, self.K = codes, scales, K
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+
+def e8m0_value(byte: int) -> float:
+    return lib().or_e8m0_value(byte)
+
+
+def mx_block_exponent(v32) -> int:
+    v = np.ascontiguousarray(v32, dtype=np.float32)
+    assert v.shape == (32,)
+    return int(lib().or_mx_block_exponent(v))
+
+
+def mx_quantize(x, S_cols: int = 0) -> MXTensor:
+    """MXFP4 quantization of x (rows x K, K % 32 == 0); with S_cols > 0, X_aug = [Q(x) | Q(R)]
+    with R = x - deq(Q(x)) on columns [0, S_cols)."""
+    x = _f32(x)
+    rows, K = x.shape
+    assert K % 32 == 0 and S_cols % 32 == 0 and 0 <= S_cols <= K
+    Ka = K + S_cols
+    codes, scales = np.zeros((rows, Ka // 2), np.uint8), np.zeros((rows, Ka // 32), np.uint8)
+    if S_cols:
+        lib().or_mx_quantize_aug(x, rows, K, K, S_cols, codes, Ka // 2, scales, Ka // 32)
+    else:
+        lib().or_mx_quantize(x, rows, K, K, codes, K // 2, scales, K // 32)
+    return MXTensor(codes, scales, Ka)
+
+
+def mx_dequantize(q: MXTensor) -> np.ndarray:
+    out = np.zeros((q.rows, q.K), np.float64)
+    lib().or_mx_dequantize(q.codes, q.codes.shape[1], q.scales, q.scales.shape[1], q.rows, q.K, out, q.K)
+    return out
+
+
+def mx_gemm(a: MXTensor, w: MXTensor) -> np.ndarray:
+    assert a.K == w.K
+    y = np.zeros((a.rows, w.rows), np.float64)
+    lib().or_mx_gemm(a.codes, a.codes.shape[1], a.scales, a.scales.shape[1],
+                     w.codes, w.codes.shape[1], w.scales, w.scales.shape[1], a.rows, w.rows, a.K, y, w.rows)
+    return y
+
+
+def mx_gemm_blas(a: MXTensor, w: MXTensor) -> np.ndarray:
+    """mx_gemm with numpy's float64 matmul as the summation step (sums in another order),
+    for references at full workload sizes; a test bounds its distance to mx_gemm."""
+    assert a.K == w.K
+    return mx_dequantize(a) @ mx_dequantize(w).T
+
+
+def mx_weight_aug(w: MXTensor, S_cols: int) -> MXTensor:
+    """W_aug = [W | W[:, :S]] of an MXFP4 weight: the tail repeats the head's first S
+    columns (their codes and block scales)."""
+    return MXTensor(np.ascontiguousarray(np.concatenate([w.codes, w.codes[:, :S_cols // 2]], axis=1)),
+                    np.ascontiguousarray(np.concatenate([w.scales, w.scales[:, :S_cols // 32]], axis=1)),
+                    w.K + S_cols)
+

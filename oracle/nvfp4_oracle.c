@@ -343,3 +343,116 @@ int or_gemm_exact(const uint8_t *ac, int64_t ldac, const uint8_t *as, int64_t ld
         }
     return 0;
 }
+
+/* ---------------------------------------------------------------- MXFP4
+ * MXFP4: E2M1 elements (the element format of section 1 of the ARCQuant
+ * article) sharing one power-of-two E8M0 scale per 32 consecutive elements
+ * along K (the 32-element blocks and E8M0 scales of the MX formats, ARCQuant
+ * article sections 2.2 and 4.2; MXFP4 is the second format of the ResServe
+ * abstract). The pages give no scale rule; this follows the published MX
+ * definition: shared exponent e = floor(log2(amax)) - 2 (2 = the exponent of
+ * E2M1's largest value, 6 = 1.5 * 2^2), clamped to E8M0's range [-127, 127];
+ * element q = x * 2^-e rounded to nearest E2M1 (ties even), saturating at 6,
+ * sign of x. An all-zero block takes e = -127. There is no tensor scale. */
+
+double or_e8m0_value(int byte)
+{
+    if (byte == 255) return NAN;
+    return ldexp(1.0, byte - 127);
+}
+
+int or_mx_block_exponent(const float *v)
+{
+    float amax = 0.0f;
+    int ex;
+    for (int i = 0; i < 32; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) return -127;
+    (void)frexp((double)amax, &ex);      /* amax = f 2^ex, f in [0.5, 1): floor(log2) = ex - 1 */
+    ex = ex - 1 - 2;
+    return ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+}
+
+void or_mx_quantize(const float *x, int64_t rows, int64_t K, int64_t ldx,
+                    uint8_t *codes, int64_t ldc, uint8_t *scales, int64_t lds)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const float *v = x + r * ldx + 32 * b;
+            int e = or_mx_block_exponent(v);
+            scales[r * lds + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i) {
+                double q = ldexp((double)v[i], -e);            /* exact */
+                int c = or_e2m1_encode((float)q) & 7;          /* (float) exact: |q| < 8, >= 2^-22 or 0 */
+                if (signbit(v[i])) c |= 8;
+                int64_t k = 32 * b + i;
+                uint8_t *byte = &codes[r * ldc + k / 2];
+                if ((k & 1) == 0) *byte = (uint8_t)((*byte & 0xF0) | c);
+                else              *byte = (uint8_t)((*byte & 0x0F) | (c << 4));
+            }
+        }
+}
+
+void or_mx_dequantize(const uint8_t *codes, int64_t ldc, const uint8_t *scales, int64_t lds,
+                      int64_t rows, int64_t K, double *out, int64_t ldo)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            out[r * ldo + k] = or_e2m1_value(code_at(codes, ldc, r, k)) * or_e8m0_value(scales[r * lds + k / 32]);
+}
+
+/* X_aug = [Q(x) | Q(R)] in MXFP4, R = fl(x - deq(Q(x))) on columns [0, S_cols):
+ * the two-stage residue of section 3.1 of the ARCQuant article in the MX format.
+ * deq(Q(x)) = e(c) 2^e is exact in FP32 here, so R rounds once. Each 32-block
+ * of R takes its own shared exponent (MX has no tensor-wide scale). */
+void or_mx_quantize_aug(const float *x, int64_t rows, int64_t K, int64_t ldx, int64_t S_cols,
+                        uint8_t *codes, int64_t ldc, uint8_t *scales, int64_t lds)
+{
+    float *res = (float *)malloc(sizeof(float) * (size_t)(rows * (S_cols > 0 ? S_cols : 1) + 1));
+    or_mx_quantize(x, rows, K, ldx, codes, ldc, scales, lds);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < S_cols; ++k) {
+            float deq = (float)(or_e2m1_value(code_at(codes, ldc, r, k)) * or_e8m0_value(scales[r * lds + k / 32]));
+            res[r * S_cols + k] = x[r * ldx + k] - deq;
+        }
+    if (S_cols > 0) {
+        /* the residue columns start at column K of the output rows */
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t b = 0; b < S_cols / 32; ++b) {
+                const float *v = res + r * S_cols + 32 * b;
+                int e = or_mx_block_exponent(v);
+                scales[r * lds + K / 32 + b] = (uint8_t)(e + 127);
+                for (int i = 0; i < 32; ++i) {
+                    double q = ldexp((double)v[i], -e);
+                    int c = or_e2m1_encode((float)q) & 7;
+                    if (signbit(v[i])) c |= 8;
+                    int64_t k = K + 32 * b + i;
+                    uint8_t *byte = &codes[r * ldc + k / 2];
+                    if ((k & 1) == 0) *byte = (uint8_t)((*byte & 0xF0) | c);
+                    else              *byte = (uint8_t)((*byte & 0x0F) | (c << 4));
+                }
+            }
+    }
+    free(res);
+}
+
+/* y[m][n] = sum_k deq(a)[m][k] deq(w)[n][k] in FP64 (every product is exact). */
+void or_mx_gemm(const uint8_t *ac, int64_t ldac, const uint8_t *as, int64_t ldas,
+                const uint8_t *wc, int64_t ldwc, const uint8_t *ws, int64_t ldws,
+                int64_t M, int64_t N, int64_t K, double *y, int64_t ldy)
+{
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * K + 1));
+    double *w = (double *)malloc(sizeof(double) * (size_t)(K + 1));
+    or_mx_dequantize(ac, ldac, as, ldas, M, K, a, K);
+    for (int64_t n = 0; n < N; ++n) {
+        or_mx_dequantize(wc + n * ldwc, ldwc, ws + n * ldws, ldws, 1, K, w, K);
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += a[m * K + k] * w[k];
+            y[m * ldy + n] = acc;
+        }
+    }
+    free(a); free(w);
+}

@@ -93,7 +93,22 @@ int or_gemm_exact(const uint8_t *ac, int64_t ldac, const uint8_t *as, int64_t ld
                   const uint8_t *wc, int64_t ldwc, const uint8_t *ws, int64_t ldws, float Sw,
                   int64_t M, int64_t N, int64_t K, double *y, int64_t ldy);
 
+/* ---- MXFP4: E2M1 codes (same packing) with one E8M0 scale byte per 32 elements
+ * along K (scales [rows][K/32], value 2^(byte - 127)); no tensor scale. */
+double  or_e8m0_value(int byte);
+int     or_mx_block_exponent(const float *v32);
+void    or_mx_quantize(const float *x, int64_t rows, int64_t K, int64_t ldx,
+                       uint8_t *codes, int64_t ldc, uint8_t *scales, int64_t lds);
+void    or_mx_dequantize(const uint8_t *codes, int64_t ldc, const uint8_t *scales, int64_t lds,
+                         int64_t rows, int64_t K, double *out, int64_t ldo);
+void    or_mx_quantize_aug(const float *x, int64_t rows, int64_t K, int64_t ldx, int64_t S_cols,
+                           uint8_t *codes, int64_t ldc, uint8_t *scales, int64_t lds);
+void    or_mx_gemm(const uint8_t *ac, int64_t ldac, const uint8_t *as, int64_t ldas,
+                   const uint8_t *wc, int64_t ldwc, const uint8_t *ws, int64_t ldws,
+                   int64_t M, int64_t N, int64_t K, double *y, int64_t ldy);
+
 #ifdef __cplusplus
 }
 #endif
 #endif
+
