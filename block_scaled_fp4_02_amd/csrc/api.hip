@@ -201,6 +201,7 @@ size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S) 
         case 1: return kHeaderBytes + tensor_ws(M, K) + quant_ws(M) + gemm_ws(M, N, K, 0);
         case 2: return kHeaderBytes + tensor_ws(M, K + S) + quant_ws(M) + gemm_ws(M, N, K, S);
         case 3: return kHeaderBytes + up((size_t)std::max<int64_t>(M, 1) * sizeof(float), kAlign);
+        case 4: return mx_workspace_bytes(M, N, K, S);
         default: return 0;
     }
 }
@@ -389,6 +390,60 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
     CHECK(enqueue_quantize(x, xt, M, K, ldx, opts, aq, partials, rscale, header, st));
     if (N == 0) return NVFP4_OK;
     return enqueue_gemm(aq, *w, M, K, S, y, yt, ldy, header, scratch, sb, st);
+}
+
+}  // extern "C"
+
+namespace {
+
+nvfp4_status check_mx(const nvfp4_mx_tensor *t, int64_t rows, int64_t K) {
+    if (!t) return NVFP4_ERR_NULL;
+    if (t->rows != rows || t->K != K || rows < 0 || K < 0 || K % 32) return NVFP4_ERR_SHAPE;
+    if (rows == 0 || K == 0) return NVFP4_OK;
+    if (!t->codes || !t->scales) return NVFP4_ERR_NULL;
+    if (t->ld_codes < K / 2 || t->ld_scales < K / 32) return NVFP4_ERR_SHAPE;
+    if (t->ld_codes % 16 || !aligned(t->codes, 16)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_mx_quantize(const void *x, int xt, int64_t rows, int64_t K_in, int64_t ldx,
+                               int64_t residue_cols, const nvfp4_mx_tensor *out, void *stream) {
+    CHECK(check_x(x, xt, rows, K_in, ldx));
+    if (K_in % 32 || residue_cols < 0 || residue_cols > K_in || residue_cols % 32) return NVFP4_ERR_SHAPE;
+    CHECK(check_mx(out, rows, K_in + residue_cols));
+    if (rows == 0 || K_in == 0) return NVFP4_OK;
+    MXQuantLaunch q;
+    q.x = x; q.xt = xt; q.rows = rows; q.K = K_in; q.ldx = ldx; q.res_cols = residue_cols;
+    q.codes = out->codes; q.ldc = out->ld_codes; q.scales = out->scales; q.lds = out->ld_scales;
+    const hipError_t e = launch_mx_quantize(q, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, int64_t residue_cols,
+                           void *y, int yt, int64_t ldy, void *ws, size_t ws_bytes, void *stream) {
+    if (!a || !w) return NVFP4_ERR_NULL;
+    if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
+    const int64_t M = a->rows, N = w->rows, K = w->K, S = residue_cols;
+    if (S < 0 || S > K || S % 32) return NVFP4_ERR_SHAPE;
+    CHECK(check_mx(w, N, K));
+    CHECK(check_mx(a, M, K + S));
+    if (!y && M > 0 && N > 0) return NVFP4_ERR_NULL;
+    if (ldy < N) return NVFP4_ERR_SHAPE;
+    const size_t need = mx_workspace_bytes(M, N, K, S);
+    if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (M == 0 || N == 0) return NVFP4_OK;
+    MXGemmLaunch g;
+    g.a_codes = a->codes; g.a_ldc = a->ld_codes; g.a_scales = a->scales; g.a_lds = a->ld_scales;
+    g.w_codes = w->codes; g.w_ldc = w->ld_codes; g.w_scales = w->scales; g.w_lds = w->ld_scales;
+    g.M = M; g.N = N; g.K = K; g.res_cols = S;
+    g.y = y; g.yt = yt; g.ldy = ldy;
+    g.scratch = ws; g.scratch_bytes = ws_bytes;
+    const hipError_t e = launch_mx_gemm(g, static_cast<hipStream_t>(stream));   // K == 0 stores zeros
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
 nvfp4_status nvfp4_pack_tiled(const nvfp4_tensor *src, const nvfp4_tensor *dst, void *stream) {

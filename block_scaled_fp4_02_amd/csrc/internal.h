@@ -102,4 +102,27 @@ struct PackLaunch {
 };
 hipError_t launch_pack_tiled(const PackLaunch &g, hipStream_t st);
 
+// MXFP4 (E2M1 codes, one E8M0 byte per 32 elements along K, no tensor scale).
+struct MXQuantLaunch {
+    const void *x; int xt; int64_t rows, K, ldx;
+    int64_t res_cols;                       // residue of columns [0, res_cols) after column K
+    uint8_t *codes; int64_t ldc;
+    uint8_t *scales; int64_t lds;
+};
+hipError_t launch_mx_quantize(const MXQuantLaunch &q, hipStream_t st);
+
+// y = A W^T over the K (+ res_cols residue) columns: A is M x (K + res_cols),
+// W is N x K; the residue columns meet W's first res_cols columns.
+struct MXGemmLaunch {
+    const uint8_t *a_codes; int64_t a_ldc;
+    const uint8_t *a_scales; int64_t a_lds;
+    const uint8_t *w_codes; int64_t w_ldc;
+    const uint8_t *w_scales; int64_t w_lds;
+    int64_t M, N, K, res_cols;
+    void *y; int yt; int64_t ldy;
+    void *scratch; size_t scratch_bytes;    // mx_workspace_bytes()
+};
+size_t mx_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t S);
+hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st);
+
 }  // namespace nvfp4

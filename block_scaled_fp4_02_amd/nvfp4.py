@@ -44,7 +44,8 @@ class _COpts(C.Structure):
 _lib = None
 _lock = threading.Lock()
 
-EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
+EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_mx_quantize",
+           "nvfp4_mx_gemm", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
            "nvfp4_perm_from_absmax", "nvfp4_workspace_size", "nvfp4_status_string",
            "nvfp4_last_error", "nvfp4_version", "nvfp4_host_e4m3_encode", "nvfp4_host_e2m1_encode"]
 
@@ -63,6 +64,8 @@ def lib():
             L.nvfp4_gemm_residue.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, C.c_int, i64, vp,
                                              vp, sz, vp]
             L.nvfp4_pack_tiled.argtypes = [vp, vp, vp]
+            L.nvfp4_mx_quantize.argtypes = [vp, C.c_int, i64, i64, i64, i64, vp, vp]
+            L.nvfp4_mx_gemm.argtypes = [vp, vp, i64, vp, C.c_int, i64, vp, sz, vp]
             L.nvfp4_channel_absmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, C.c_float, vp, vp, sz, vp]
             L.nvfp4_perm_from_absmax.argtypes = [vp, i64, vp]
             L.nvfp4_workspace_size.argtypes = [C.c_int, i64, i64, i64, i64]
@@ -73,6 +76,7 @@ def lib():
             L.nvfp4_host_e4m3_encode.argtypes = [C.c_float]
             L.nvfp4_host_e2m1_encode.argtypes = [C.c_float]
             for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_pack_tiled",
+                         "nvfp4_mx_quantize", "nvfp4_mx_gemm",
                          "nvfp4_channel_absmax", "nvfp4_perm_from_absmax"):
                 getattr(L, name).restype = C.c_int
             _lib = L
@@ -317,3 +321,64 @@ def perm_from_absmax(v: torch.Tensor) -> torch.Tensor:
 
 def calibrate_perm(x_cal: torch.Tensor, gamma=None, eps: float = 1e-6) -> torch.Tensor:
     return perm_from_absmax(channel_absmax(x_cal, gamma, eps))
+
+
+# ---------------------------------------------------------------------- MXFP4
+
+class _CMXTensor(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("ld_codes", C.c_int64), ("scales", C.c_void_p),
+                ("ld_scales", C.c_int64), ("rows", C.c_int64), ("K", C.c_int64)]
+
+
+class MXTensor:
+    """Device MXFP4 tensor: codes [rows, ld_codes] u8 (E2M1 nibbles), scales [rows, ld_scales]
+    u8 (E8M0, one per 32 columns); no tensor scale."""
+
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, K: int):
+        self.codes, self.scales, self.K = codes, scales, K
+
+    @staticmethod
+    def empty(rows: int, K: int, device="cuda") -> "MXTensor":
+        ldc, lds = _round_up(max(K // 2, 1), 16), _round_up(max(K // 32, 1), 16)
+        return MXTensor(torch.empty((rows, ldc), dtype=torch.uint8, device=device),
+                        torch.empty((rows, lds), dtype=torch.uint8, device=device), K)
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    def c(self) -> _CMXTensor:
+        return _CMXTensor(self.codes.data_ptr(), self.codes.stride(0), self.scales.data_ptr(), self.scales.stride(0),
+                          self.rows, self.K)
+
+    def host(self):
+        """(codes [rows, K/2], scales [rows, K/32]) as numpy arrays on the host."""
+        return self.codes[:, : self.K // 2].cpu().numpy(), self.scales[:, : self.K // 32].cpu().numpy()
+
+
+def mx_quantize(x: torch.Tensor, residue_cols: int = 0) -> MXTensor:
+    """MXFP4-quantize rows of x (bf16/f32, 2-D, K % 32 == 0); residue_cols > 0 appends the
+    quantized residue of the first residue_cols columns."""
+    assert x.dim() == 2 and (x.stride(1) == 1 or x.numel() == 0)
+    rows, K = x.shape
+    out = MXTensor.empty(rows, K + residue_cols, x.device)
+    ct = out.c()
+    _check(lib().nvfp4_mx_quantize(_ptr(x), _dtype_code(x), rows, K, max(x.stride(0), K), int(residue_cols), C.byref(ct),
+                                   _stream()), "nvfp4_mx_quantize")
+    return out
+
+
+def mx_gemm(a: MXTensor, w: MXTensor, residue_cols: int = 0, out_dtype=torch.float32,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = A W^T in MXFP4; A has K + residue_cols columns, W has K."""
+    M, N = a.rows, w.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    n = lib().nvfp4_workspace_size(4, M, N, w.K, residue_cols)
+    ws = workspace(n, a.codes.device) if n else None
+    ac, wc = a.c(), w.c()
+    _check(lib().nvfp4_mx_gemm(C.byref(ac), C.byref(wc), int(residue_cols), _ptr(out), _dtype_code(out),
+                               out.stride(0), _ptr(ws), ws.numel() if ws is not None else 0, _stream()),
+           "nvfp4_mx_gemm")
+    return out
+

@@ -183,6 +183,43 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
                                 void *y, int yt, int64_t ldy, const nvfp4_tensor *a_aug_out,
                                 void *ws, size_t ws_bytes, void *stream);
 
+/* ---- MXFP4 (the second block format of the ResServe abstract; the 32-element
+ * blocks and E8M0 scales of the MX formats, ARCQuant article, sections 2.2 and
+ * 4.2). Each value is an E2M1 code (the same nibbles and packing as above) and
+ * every 32 consecutive values along K share one E8M0 byte b, scale 2^(b - 127).
+ * There is no tensor scale. Quantization rule (the pages name the format, not
+ * its rounding; this is the MX definition): shared exponent e =
+ * floor(log2(block amax)) - 2, clamped to [-127, 127] (-127 for an all-zero
+ * block); code = E2M1(x * 2^-e) round to nearest even, saturating at 6, sign
+ * of x. gfx950's scaled FP4 matrix instructions consume these blocks as they
+ * are stored.
+ * Canonical storage: codes rows x ld_codes bytes (ld_codes >= K/2, multiple
+ * of 16, 16-byte aligned pointer); scales rows x ld_scales bytes (>= K/32). */
+typedef struct {
+    uint8_t *codes;  int64_t ld_codes;
+    uint8_t *scales; int64_t ld_scales;
+    int64_t  rows, K;      /* K % 32 == 0 */
+} nvfp4_mx_tensor;
+
+/* MXFP4-quantize x (rows x K_in, dtype xt, ldx) into `out` (rows x (K_in + S)).
+ * S = residue_cols (multiple of 32, <= K_in): the residue R = x - deq(Q(x)) of
+ * columns [0, S), computed in FP32 (exact dequantization, one rounding) and
+ * quantized in the same format with its own block scales, is stored after
+ * column K_in (the two-stage residue of the ARCQuant article, section 3.1).
+ * K_in % 32 == 0. No workspace: every block is independent. */
+nvfp4_status nvfp4_mx_quantize(const void *x, int xt, int64_t rows, int64_t K_in, int64_t ldx,
+                               int64_t residue_cols, const nvfp4_mx_tensor *out, void *stream);
+
+/* MXFP4 product y = A W^T (ARCQuant article, section 3.1 formula; ResServe
+ * abstract for MXFP4 with residue compensation): A is M x (K + S) (its last S
+ * columns the quantized residue of its first S), W is N x K; the residue
+ * columns meet W's own first S columns (never materialized). FP32 accumulation
+ * in the scaled FP4 matrix cores; y dtype yt (FP32 or BF16 round to nearest
+ * even), leading dimension ldy. Workspace: nvfp4_workspace_size(4, M, N, K, S)
+ * bytes (may be 0, then ws may be NULL). */
+nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, int64_t residue_cols,
+                           void *y, int yt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
+
 /* Rewrite the row-major weight `src` into the tiled layout `dst` (same rows
  * and K; dst->ld_codes = KU*4096, dst->ld_scales = KU*512; its codes and
  * scales buffers hold ceil(rows/16) strips). The tensor scale is copied.
@@ -202,7 +239,8 @@ nvfp4_status nvfp4_channel_absmax(const void *x, int xt, int64_t rows, int64_t K
 nvfp4_status nvfp4_perm_from_absmax(const float *absmax_host, int64_t K, int32_t *perm_host);
 
 /* Bytes of workspace an operation needs: op 0 = quantize (M = rows), 1 = gemm,
- * 2 = gemm_residue, 3 = channel_absmax (M = rows). S is the residue column count. */
+ * 2 = gemm_residue, 3 = channel_absmax (M = rows), 4 = mx_gemm. S is the residue
+ * column count. */
 size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S);
 
 const char *nvfp4_status_string(nvfp4_status s);
