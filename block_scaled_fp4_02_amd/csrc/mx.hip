@@ -15,6 +15,8 @@
 // Residue columns (ARCQuant article, sections 3.1-3.2; ResServe abstract: the
 // residue is kept in the same format) follow column K of the activation and
 // meet the weight's first S columns again.
+#include <type_traits>
+
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -292,6 +294,239 @@ hipError_t run_small(const MXDArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ large M (tiles)
+// BM x BN = 256 x 256 output tiles on 4 waves, one per SIMD with the whole
+// register file (2 x 2 waves of 128 x 128: 8 x 8 MFMAs of 16 x 16 per
+// 128-column step, every fragment read from LDS feeding 8 of them).
+// A step's codes and E8M0 bytes go from memory straight into LDS with gfx950's
+// direct-to-LDS loads (global_load_lds_dwordx4 / _ubyte: no staging registers,
+// no decode -- the matrix cores take them as stored): codes at row * 64 + 16 q
+// (a fragment read is 1 KiB contiguous per wave); a scale byte lands as a
+// zero-extended dword (the ubyte form writes lane l at base + 4 l), entry
+// row * 4 + block.
+// Three LDS stages: the loads of step s + 2 go out during step s, after step s's
+// fragments are in registers, and step s + 1's are waited for at its end. A
+// 32-block past the data is loaded from its row's start and then overwritten in
+// LDS by the thread that loaded it (codes 0, scale 127). Residue columns are
+// further steps, as in the small-M kernel. Split-K writes FP32 partial tiles
+// for a combine in fixed order.
+// Direct-to-LDS loads, issued from asm blocks that have no output registers: the
+// hardware writes lane l's 16 bytes at M0 + 16 l (dwordx4), its byte zero-extended
+// at M0 + 4 l (ubyte), M0 = the wave's LDS address
+// (set in the same block). The compiler does not see these as LDS writes, so it
+// adds no waits of its own between them and reads of other stages; the kernel
+// waits for them itself (vmcnt) before the barrier that publishes a stage.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is named as clobbered on purpose
+__device__ inline void dma16(const void *src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
+}
+__device__ inline void dma1(const void *src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ubyte %1, off"
+                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ inline uint32_t lds_addr_of(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p);
+}
+
+constexpr int MX_BM = 256, MX_BN = 256, MX_NW = 4, MX_NT = 64 * MX_NW;
+constexpr int MX_ACODE = MX_BM * 64, MX_BCODE = MX_BN * 64;          // bytes per stage
+constexpr int MX_ASC = MX_BM * 4 * 4, MX_BSC = MX_BN * 4 * 4;        // a dword per scale byte
+constexpr int MX_STAGE = MX_ACODE + MX_BCODE + MX_ASC + MX_BSC;       // 40 KiB
+constexpr int MX_CH = MX_BM * 4 / MX_NT;                              // chunks per thread and operand (4)
+constexpr int MX_LOADS = 4 * MX_CH;                                   // direct-to-LDS loads per thread and step
+
+struct MXTArgs {
+    const uint8_t *a_codes; int64_t a_ldc;
+    const uint8_t *a_scales; int64_t a_lds;
+    const uint8_t *w_codes; int64_t w_ldc;
+    const uint8_t *w_scales; int64_t w_lds;
+    int64_t M, N, K, res;
+    void *y; int yt; int64_t ldy;
+    int tiles_m, tiles_n;
+    int64_t kchunk;                            // k-steps per split-K range (blockIdx.y)
+    float *part;                               // split-K partials [P][M][N], or nullptr
+};
+
+// s_waitcnt with vmcnt <= n (n < 64) and the other counters left alone, and with
+// lgkmcnt == 0 and the others left alone (gfx9 encoding)
+#define MX_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+#define MX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
+
+__global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mx_tile_kernel(MXTArgs a) {
+    // one object per stage: with the loop unrolled by three every access names its
+    // stage, so the compiler can tell in-flight loads into one stage from reads of another
+    __shared__ __attribute__((aligned(16))) uint8_t st0[MX_STAGE], st1[MX_STAGE], st2[MX_STAGE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, g = lane >> 4;
+    const int nblk = a.tiles_m * a.tiles_n;
+    int bid = blockIdx.x;
+    if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;        // tiles sharing a weight column on one XCD
+    const int tn = bid / a.tiles_m, tm = bid % a.tiles_m;
+    const int64_t m0 = (int64_t)tm * MX_BM, n0 = (int64_t)tn * MX_BN;
+    const int64_t kmain = (a.K + 127) / 128, kall = kmain + (a.res + 127) / 128;
+    const int64_t s0 = (int64_t)blockIdx.y * a.kchunk;
+    const int64_t ksteps = (s0 + a.kchunk < kall ? s0 + a.kchunk : kall) - s0;
+    const int q4 = lane & 3;                   // this thread's quarter of a row (every chunk)
+
+    // chunk i of this thread: c = 256 i + 64 wave + lane, row c / 4 of the tile
+    int ra[MX_CH], rb[MX_CH];
+#pragma unroll
+    for (int i = 0; i < MX_CH; ++i) {
+        const int row = (MX_NT * i + tid) >> 2;
+        const int64_t ma = m0 + row, nb = n0 + row;
+        ra[i] = (int)(ma < a.M ? ma : a.M - 1);
+        rb[i] = (int)(nb < a.N ? nb : a.N - 1);
+    }
+    // step s of this range: weight columns kw.. and activation columns ka.. ; whether
+    // this thread's 32-block of the step holds data
+    auto cols = [&](int64_t s, int64_t &kw, int64_t &ka, bool &ok) {
+        const bool main = s0 + s < kmain;
+        kw = (main ? s0 + s : s0 + s - kmain) * 128;
+        ka = main ? kw : a.K + kw;
+        ok = kw + 32 * q4 < (main ? a.K : a.res);
+    };
+    // the MX_LOADS direct-to-LDS loads of step s into stage st (each wave writes
+    // 1 KiB of codes or 64 scale bytes per instruction, lane l at base + 16 l / l)
+    auto dma = [&](int64_t s, uint8_t *st) {
+        int64_t kw, ka;
+        bool ok;
+        cols(s, kw, ka, ok);
+        const int64_t cw = ok ? kw / 2 + 16 * q4 : 0, ca = ok ? ka / 2 + 16 * q4 : 0;
+        const int64_t bw = ok ? kw / 32 + q4 : 0, ba = ok ? ka / 32 + q4 : 0;
+        const uint32_t sbase = lds_addr_of(st);
+#pragma unroll
+        for (int i = 0; i < MX_CH; ++i) {
+            const uint32_t cbase = (uint32_t)(MX_NT * i + 64 * wave);  // first chunk of this wave's instruction
+            dma16(a.a_codes + (int64_t)ra[i] * a.a_ldc + ca, sbase + 16 * cbase);
+            dma16(a.w_codes + (int64_t)rb[i] * a.w_ldc + cw, sbase + MX_ACODE + 16 * cbase);
+            dma1(a.a_scales + (int64_t)ra[i] * a.a_lds + ba, sbase + MX_ACODE + MX_BCODE + 4 * cbase);
+            dma1(a.w_scales + (int64_t)rb[i] * a.w_lds + bw, sbase + MX_ACODE + MX_BCODE + MX_ASC + 4 * cbase);
+        }
+    };
+    // after this thread's loads of step s have landed: blocks past the data become
+    // zero codes with a unit scale (the loads read the row's first bytes instead)
+    auto fixup = [&](int64_t s, uint8_t *st) {
+        int64_t kw, ka;
+        bool ok;
+        cols(s, kw, ka, ok);
+        if (ok) return;
+#pragma unroll
+        for (int i = 0; i < MX_CH; ++i) {
+            const int c = MX_NT * i + tid;
+            *reinterpret_cast<uint4 *>(st + 16 * c) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(st + MX_ACODE + 16 * c) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint32_t *>(st + MX_ACODE + MX_BCODE + 4 * c) = 127u;
+            *reinterpret_cast<uint32_t *>(st + MX_ACODE + MX_BCODE + MX_ASC + 4 * c) = 127u;
+        }
+    };
+
+    float4v acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = float4v{0, 0, 0, 0};
+
+    if (ksteps > 0) dma(0, st0);
+    if (ksteps > 1) dma(1, st1);
+    if (ksteps > 1) MX_WAIT_VM(MX_LOADS); else MX_WAIT_VM(0);
+    if (ksteps > 0) fixup(0, st0);
+    MX_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+
+    // step s computes from `cur`, loads step s + 2 into `far` and patches step s + 1 in `nxt`
+    auto step = [&](int64_t s, const uint8_t *cur, uint8_t *nxt, uint8_t *far) {
+        // every fragment of the step, read before any further load goes out
+        v8i bf[8], af[8];
+        int bs[8], as[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = wn * 128 + 16 * j + r16;
+            const uint4 v = *reinterpret_cast<const uint4 *>(cur + MX_ACODE + row * 64 + 16 * g);
+            bf[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            bs[j] = cur[MX_ACODE + MX_BCODE + MX_ASC + 4 * (row * 4 + g)];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = wm * 128 + 16 * i + r16;
+            const uint4 v = *reinterpret_cast<const uint4 *>(cur + row * 64 + 16 * g);
+            af[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            as[i] = cur[MX_ACODE + MX_BCODE + 4 * (row * 4 + g)];
+        }
+        const bool more = s + 2 < ksteps;
+        if (more) dma(s + 2, far);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, as[i], 0,
+                                                                             bs[j]);
+        // Step s + 1's loads have landed (only step s + 2's may still be in flight),
+        // its patches are written, and this wave's reads of stage s are done. The
+        // barrier is a bare s_barrier: __syncthreads would also wait for step s + 2.
+        if (more) MX_WAIT_VM(MX_LOADS); else MX_WAIT_VM(0);
+        if (s + 1 < ksteps) fixup(s + 1, nxt);
+        MX_WAIT_LGKM0();
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int64_t s = 0; s < ksteps; s += 3) {
+        step(s, st0, st1, st2);
+        if (s + 1 < ksteps) step(s + 1, st1, st2, st0);
+        if (s + 2 < ksteps) step(s + 2, st2, st0, st1);
+    }
+
+    // epilogue: one fully unrolled store nest per output kind, so every
+    // accumulator index is a constant (a runtime loop here would keep the
+    // accumulators in memory instead of registers)
+    float *part = a.part ? a.part + (int64_t)blockIdx.y * a.M * a.N : nullptr;
+    const int64_t mrow = m0 + wm * 128 + 4 * g, ncol = n0 + wn * 128 + r16;
+    auto store_all = [&](auto kind) {
+        constexpr int KIND = decltype(kind)::value;   // 2: partial, 1: FP32, 0: BF16
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t m = mrow + 16 * i + e, n = ncol + 16 * j;
+                    if (m < a.M && n < a.N) {
+                        if constexpr (KIND == 2) part[m * a.N + n] = acc[i][j][e];
+                        else if constexpr (KIND == 1) static_cast<float *>(a.y)[m * a.ldy + n] = acc[i][j][e];
+                        else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(acc[i][j][e]);
+                    }
+                }
+    };
+    if (part) store_all(std::integral_constant<int, 2>{});
+    else if (a.yt == 1) store_all(std::integral_constant<int, 1>{});
+    else store_all(std::integral_constant<int, 0>{});
+}
+
+// y[m][n] = sum_p part[p][m][n] in order p = 0, 1, ... (deterministic).
+__global__ __launch_bounds__(256) void mx_combine_kernel(const float *part, int P, int64_t M, int64_t N, void *y,
+                                                         int yt, int64_t ldy) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * N) return;
+    const int64_t m = idx / N, n = idx - m * N;
+    float s = 0.0f;
+    for (int p = 0; p < P; ++p) s += part[(int64_t)p * M * N + idx];
+    if (yt == 1) static_cast<float *>(y)[m * ldy + n] = s;
+    else static_cast<uint16_t *>(y)[m * ldy + n] = f32_to_bf16_rne(s);
+}
+
+// Split-K ranges of the tile kernel: when its 256 x 256 tiles leave most CUs idle
+// and the steps are many, P ranges of at least 16 steps until ~one tile per CU.
+int mx_splits(int64_t M, int64_t N, int64_t K, int64_t S) {
+    if (M <= 64) return 1;
+    const int64_t tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
+    const int64_t steps = (K + 127) / 128 + (S + 127) / 128;
+    int P = 1;
+    while (P < 8 && tiles * P < 192 && steps / (2 * P) >= 16) P *= 2;
+    return P;
+}
+
 }  // namespace
 
 hipError_t launch_mx_quantize(const MXQuantLaunch &q, hipStream_t st) {
@@ -308,8 +543,8 @@ hipError_t launch_mx_quantize(const MXQuantLaunch &q, hipStream_t st) {
 }
 
 size_t mx_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t S) {
-    (void)M; (void)N; (void)K; (void)S;
-    return 0;
+    const int P = mx_splits(M, N, K, S);
+    return P > 1 ? (size_t)P * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st) {
@@ -324,18 +559,28 @@ hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st) {
     if (g.M <= 16) return wide ? run_small<2, 1>(a, st) : run_small<1, 1>(a, st);
     if (g.M <= 32) return wide ? run_small<2, 2>(a, st) : run_small<1, 2>(a, st);
     if (g.M <= 64) return run_small<1, 4>(a, st);
-    // larger M: the same kernel over 64-row slices of the activation
-    for (int64_t m0 = 0; m0 < g.M; m0 += 64) {
-        MXDArgs s = a;
-        s.a_codes = g.a_codes + m0 * g.a_ldc;
-        s.a_scales = g.a_scales + m0 * g.a_lds;
-        s.M = g.M - m0 < 64 ? g.M - m0 : 64;
-        s.y = g.yt == 1 ? static_cast<void *>(static_cast<float *>(g.y) + m0 * g.ldy)
-                        : static_cast<void *>(static_cast<uint16_t *>(g.y) + m0 * g.ldy);
-        const hipError_t e = run_small<1, 4>(s, st);
-        if (e != hipSuccess) return e;
+    // larger M: 256 x 256 tiles on the matrix cores, split K when the tiles are few
+    MXTArgs t;
+    t.a_codes = g.a_codes; t.a_ldc = g.a_ldc; t.a_scales = g.a_scales; t.a_lds = g.a_lds;
+    t.w_codes = g.w_codes; t.w_ldc = g.w_ldc; t.w_scales = g.w_scales; t.w_lds = g.w_lds;
+    t.M = g.M; t.N = g.N; t.K = g.K; t.res = g.res_cols;
+    t.y = g.y; t.yt = g.yt; t.ldy = g.ldy;
+    t.tiles_m = (int)((g.M + MX_BM - 1) / MX_BM);
+    t.tiles_n = (int)((g.N + MX_BN - 1) / MX_BN);
+    const int P = mx_splits(g.M, g.N, g.K, g.res_cols);
+    const int64_t kall = (g.K + 127) / 128 + (g.res_cols + 127) / 128;
+    t.kchunk = (kall + P - 1) / P;
+    t.part = nullptr;
+    if (P > 1) {
+        if (!g.scratch || g.scratch_bytes < mx_workspace_bytes(g.M, g.N, g.K, g.res_cols)) return hipErrorInvalidValue;
+        t.part = static_cast<float *>(g.scratch);
     }
-    return hipSuccess;
+    mx_tile_kernel<<<dim3((unsigned)(t.tiles_m * t.tiles_n), (unsigned)P), MX_NT, 0, st>>>(t);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || P == 1) return e;
+    const int64_t total = g.M * g.N;
+    mx_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(t.part, P, g.M, g.N, g.y, g.yt, g.ldy);
+    return hipGetLastError();
 }
 
 }  // namespace nvfp4

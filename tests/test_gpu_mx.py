@@ -122,3 +122,40 @@ def test_mx_residue_compensation(nv, orc, M):
     e_res = np.linalg.norm(y.cpu().numpy() - exact)
     e_base = np.linalg.norm(y0.cpu().numpy() - exact)
     assert e_res <= 0.25 * e_base, (e_res, e_base)
+
+
+def _lines(n, rng):
+    idx = []
+    for b in range(0, n, 128):
+        hi = min(b + 128, n) - 1
+        idx += [b, hi, int(rng.integers(b, hi + 1))]
+    return np.unique(np.array(idx, dtype=np.int64))
+
+
+@pytest.mark.parametrize("M,N,K,S", [(300, 3000, 2048, 0), (520, 1000, 1056, 96), (2048, 28672, 8192, 0),
+                                     (512, 8192, 28672, 0), (8192, 8192, 28672, 0), (2048, 8192, 8192, 1024)])
+def test_mx_prefill_tiles(nv, orc, M, N, K, S):
+    """The large-M MXFP4 product (256 x 256 tiles, split K where the tiles are few, residue
+    columns as further steps): every tile's corners and an interior point, plus random rows
+    and columns -- the whole cross product -- against the oracle, FP32 and BF16 outputs."""
+    rng = np.random.default_rng(M + N + S)
+    x = inputs.activations(5, 3, M, K, 0.01, 50.0)
+    w = inputs.weights(5, 3, N, K, 0.015)
+    note(f"mx prefill M={M} N={N} K={K} S={S}")
+    aq = nv.mx_quantize(x.to(DEV), residue_cols=S)
+    wq = nv.mx_quantize(w.to(DEV))
+    y = nv.mx_gemm(aq, wq, residue_cols=S)
+    yb = nv.mx_gemm(aq, wq, residue_cols=S, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([_lines(M, rng), rng.integers(0, M, 64)]))
+    cols = np.unique(np.concatenate([_lines(N, rng), rng.integers(0, N, 64)]))
+    xr = orc.mx_quantize(x[rows], S_cols=S)
+    wr = orc.mx_quantize(w[cols])
+    ac, as_ = aq.host()
+    wc, ws_ = wq.host()
+    assert np.array_equal(ac[rows], xr.codes) and np.array_equal(as_[rows], xr.scales), "X codes"
+    assert np.array_equal(wc[cols], wr.codes) and np.array_equal(ws_[cols], wr.scales), "W codes"
+    ref = orc.mx_gemm_blas(xr, orc.mx_weight_aug(wr, S))
+    err = gemm_error(y.cpu().numpy()[np.ix_(rows, cols)], ref)
+    assert err <= TOL, err
+    assert bf16_bound_ok(yb.float().cpu().numpy()[np.ix_(rows, cols)], ref)
