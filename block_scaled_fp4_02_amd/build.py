@@ -16,6 +16,7 @@ FLAGS = [
     "-ffp-contract=off",                       # every product/sum rounds once
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    "-Wno-inline-asm",                          # direct-to-LDS loads name M0 as clobbered on purpose
 ]
 
 

@@ -316,7 +316,6 @@ hipError_t run_small(const MXDArgs &a, hipStream_t st) {
 // (set in the same block). The compiler does not see these as LDS writes, so it
 // adds no waits of its own between them and reads of other stages; the kernel
 // waits for them itself (vmcnt) before the barrier that publishes a stage.
-#pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 is named as clobbered on purpose
 __device__ inline void dma16(const void *src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -326,7 +325,15 @@ __device__ inline void dma1(const void *src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ubyte %1, off"
                  :: "s"(lds_addr), "v"(src) : "memory", "m0");
 }
-#pragma clang diagnostic pop
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
+__device__ inline void dma16s(const void *base, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
+}
+__device__ inline void dma1s(const void *base, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ubyte %1, %2"
+                 :: "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
+}
 __device__ inline uint32_t lds_addr_of(const void *p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p);
 }
@@ -335,6 +342,7 @@ constexpr int MX_BM = 256, MX_BN = 256, MX_NW = 4, MX_NT = 64 * MX_NW;
 constexpr int MX_ACODE = MX_BM * 64, MX_BCODE = MX_BN * 64;          // bytes per stage
 constexpr int MX_ASC = MX_BM * 4 * 4, MX_BSC = MX_BN * 4 * 4;        // a dword per scale byte
 constexpr int MX_STAGE = MX_ACODE + MX_BCODE + MX_ASC + MX_BSC;       // 40 KiB
+constexpr int MX_GROUP_M = 8;                                         // row tiles per group of the tile order
 constexpr int MX_CH = MX_BM * 4 / MX_NT;                              // chunks per thread and operand (4)
 constexpr int MX_LOADS = 4 * MX_CH;                                   // direct-to-LDS loads per thread and step
 
@@ -357,29 +365,45 @@ struct MXTArgs {
 
 __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mx_tile_kernel(MXTArgs a) {
-    // one object per stage: with the loop unrolled by three every access names its
-    // stage, so the compiler can tell in-flight loads into one stage from reads of another
-    __shared__ __attribute__((aligned(16))) uint8_t st0[MX_STAGE], st1[MX_STAGE], st2[MX_STAGE];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_mx[];   // [3][MX_STAGE]
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, g = lane >> 4;
+    // Tile order. Workgroups are dealt to the 8 XCDs round robin; renumber them so
+    // each XCD takes a contiguous range, and walk that range in groups of
+    // MX_GROUP_M row tiles sweeping the columns together: the tiles resident on
+    // one XCD then share activation and weight panels in its L2.
     const int nblk = a.tiles_m * a.tiles_n;
     int bid = blockIdx.x;
-    if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;        // tiles sharing a weight column on one XCD
-    const int tn = bid / a.tiles_m, tm = bid % a.tiles_m;
+    if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+    const int in_group = MX_GROUP_M * a.tiles_n, first_m = (bid / in_group) * MX_GROUP_M;
+    const int gsize = a.tiles_m - first_m < MX_GROUP_M ? a.tiles_m - first_m : MX_GROUP_M;
+    const int tm = first_m + (bid % in_group) % gsize, tn = (bid % in_group) / gsize;
     const int64_t m0 = (int64_t)tm * MX_BM, n0 = (int64_t)tn * MX_BN;
     const int64_t kmain = (a.K + 127) / 128, kall = kmain + (a.res + 127) / 128;
     const int64_t s0 = (int64_t)blockIdx.y * a.kchunk;
     const int64_t ksteps = (s0 + a.kchunk < kall ? s0 + a.kchunk : kall) - s0;
-    const int q4 = lane & 3;                   // this thread's quarter of a row (every chunk)
+    // Row r's four 32-blocks of a step sit in LDS in the order p = block ^ f(r),
+    // f(r) = ((r >> 1) ^ (r >> 2)) & 3: a fragment read (16 rows x one block per
+    // 16 lanes) then spreads over every bank group, with 32 or with 64 banks.
+    // Chunk c of a stage is row c / 4, position c % 4; this thread fetches the
+    // block that belongs at its position (every chunk: the row's low bits are
+    // those of tid / 4).
+    const int q4 = (lane & 3) ^ (((lane >> 3) ^ (lane >> 4)) & 3);
+    const int gp = g ^ (((r16 >> 1) ^ (r16 >> 2)) & 3);   // position of block g in this lane's rows
 
-    // chunk i of this thread: c = 256 i + 64 wave + lane, row c / 4 of the tile
-    int ra[MX_CH], rb[MX_CH];
+    // chunk i of this thread: c = 256 i + 64 wave + lane, row c / 4 of the tile;
+    // byte offsets of this thread's rows from the tile's first row (rows past the
+    // matrix repeat its last row); 32 bits hold them (launcher-checked)
+    const uint8_t *abase = a.a_codes + m0 * a.a_ldc, *wbase = a.w_codes + n0 * a.w_ldc;
+    const uint8_t *asbase = a.a_scales + m0 * a.a_lds, *wsbase = a.w_scales + n0 * a.w_lds;
+    uint32_t ra[MX_CH], rb[MX_CH], rsa[MX_CH], rsb[MX_CH];
 #pragma unroll
     for (int i = 0; i < MX_CH; ++i) {
         const int row = (MX_NT * i + tid) >> 2;
         const int64_t ma = m0 + row, nb = n0 + row;
-        ra[i] = (int)(ma < a.M ? ma : a.M - 1);
-        rb[i] = (int)(nb < a.N ? nb : a.N - 1);
+        const int64_t la = (ma < a.M ? ma : a.M - 1) - m0, lb = (nb < a.N ? nb : a.N - 1) - n0;
+        ra[i] = (uint32_t)(la * a.a_ldc); rsa[i] = (uint32_t)(la * a.a_lds);
+        rb[i] = (uint32_t)(lb * a.w_ldc); rsb[i] = (uint32_t)(lb * a.w_lds);
     }
     // step s of this range: weight columns kw.. and activation columns ka.. ; whether
     // this thread's 32-block of the step holds data
@@ -395,16 +419,16 @@ void mx_tile_kernel(MXTArgs a) {
         int64_t kw, ka;
         bool ok;
         cols(s, kw, ka, ok);
-        const int64_t cw = ok ? kw / 2 + 16 * q4 : 0, ca = ok ? ka / 2 + 16 * q4 : 0;
-        const int64_t bw = ok ? kw / 32 + q4 : 0, ba = ok ? ka / 32 + q4 : 0;
+        const uint32_t cw = ok ? (uint32_t)(kw / 2 + 16 * q4) : 0u, ca = ok ? (uint32_t)(ka / 2 + 16 * q4) : 0u;
+        const uint32_t bw = ok ? (uint32_t)(kw / 32 + q4) : 0u, ba = ok ? (uint32_t)(ka / 32 + q4) : 0u;
         const uint32_t sbase = lds_addr_of(st);
 #pragma unroll
         for (int i = 0; i < MX_CH; ++i) {
             const uint32_t cbase = (uint32_t)(MX_NT * i + 64 * wave);  // first chunk of this wave's instruction
-            dma16(a.a_codes + (int64_t)ra[i] * a.a_ldc + ca, sbase + 16 * cbase);
-            dma16(a.w_codes + (int64_t)rb[i] * a.w_ldc + cw, sbase + MX_ACODE + 16 * cbase);
-            dma1(a.a_scales + (int64_t)ra[i] * a.a_lds + ba, sbase + MX_ACODE + MX_BCODE + 4 * cbase);
-            dma1(a.w_scales + (int64_t)rb[i] * a.w_lds + bw, sbase + MX_ACODE + MX_BCODE + MX_ASC + 4 * cbase);
+            dma16s(abase, ra[i] + ca, sbase + 16 * cbase);
+            dma16s(wbase, rb[i] + cw, sbase + MX_ACODE + 16 * cbase);
+            dma1s(asbase, rsa[i] + ba, sbase + MX_ACODE + MX_BCODE + 4 * cbase);
+            dma1s(wsbase, rsb[i] + bw, sbase + MX_ACODE + MX_BCODE + MX_ASC + 4 * cbase);
         }
     };
     // after this thread's loads of step s have landed: blocks past the data become
@@ -430,52 +454,78 @@ void mx_tile_kernel(MXTArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = float4v{0, 0, 0, 0};
 
-    if (ksteps > 0) dma(0, st0);
-    if (ksteps > 1) dma(1, st1);
-    if (ksteps > 1) MX_WAIT_VM(MX_LOADS); else MX_WAIT_VM(0);
-    if (ksteps > 0) fixup(0, st0);
-    MX_WAIT_LGKM0();
-    __builtin_amdgcn_s_barrier();
-
-    // step s computes from `cur`, loads step s + 2 into `far` and patches step s + 1 in `nxt`
-    auto step = [&](int64_t s, const uint8_t *cur, uint8_t *nxt, uint8_t *far) {
-        // every fragment of the step, read before any further load goes out
-        v8i bf[8], af[8];
-        int bs[8], as[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row = wn * 128 + 16 * j + r16;
-            const uint4 v = *reinterpret_cast<const uint4 *>(cur + MX_ACODE + row * 64 + 16 * g);
-            bf[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            bs[j] = cur[MX_ACODE + MX_BCODE + MX_ASC + 4 * (row * 4 + g)];
+    // Software pipeline inside the wave (one wave per SIMD, so nothing else hides
+    // its waits): step s's 64 MFMAs run from fragment registers F[s % 2] while the
+    // 32 LDS reads of step s + 1's fragments into F[(s + 1) % 2] are interleaved
+    // between them; then step s + 3's loads go out into the stage step s left,
+    // step s + 2's are waited for, patched and published at the barrier.
+    // At the top of step s: stage s + 1 is published, step s + 2's loads are in flight.
+    struct Frags { v8i a[8], b[8]; int sa[8], sb[8]; };
+    Frags F0, F1;
+    auto stage = [&](int64_t s) { return lds_mx + (int)(s % 3) * MX_STAGE; };
+    auto frag_read = [&](const uint8_t *cur, Frags &F, int r) {      // read r of 32
+        const bool isb = r < 16, sc = (r & 1) != 0;
+        const int idx = (r & 15) >> 1;
+        const int row = (isb ? wn : wm) * 128 + 16 * idx + r16;
+        const uint8_t *base = cur + (isb ? MX_ACODE : 0);
+        if (!sc) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(base + row * 64 + 16 * gp);
+            (isb ? F.b[idx] : F.a[idx]) = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        } else {
+            const int v = cur[MX_ACODE + MX_BCODE + (isb ? MX_ASC : 0) + 4 * (row * 4 + gp)];
+            (isb ? F.sb[idx] : F.sa[idx]) = v;
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = wm * 128 + 16 * i + r16;
-            const uint4 v = *reinterpret_cast<const uint4 *>(cur + row * 64 + 16 * g);
-            af[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            as[i] = cur[MX_ACODE + MX_BCODE + 4 * (row * 4 + g)];
-        }
-        const bool more = s + 2 < ksteps;
-        if (more) dma(s + 2, far);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, as[i], 0,
-                                                                             bs[j]);
-        // Step s + 1's loads have landed (only step s + 2's may still be in flight),
-        // its patches are written, and this wave's reads of stage s are done. The
-        // barrier is a bare s_barrier: __syncthreads would also wait for step s + 2.
+    };
+    auto publish = [&](int64_t s, bool more) {       // step s's loads landed, patched, visible
         if (more) MX_WAIT_VM(MX_LOADS); else MX_WAIT_VM(0);
-        if (s + 1 < ksteps) fixup(s + 1, nxt);
+        fixup(s, stage(s));
         MX_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
     };
-    for (int64_t s = 0; s < ksteps; s += 3) {
-        step(s, st0, st1, st2);
-        if (s + 1 < ksteps) step(s + 1, st1, st2, st0);
-        if (s + 2 < ksteps) step(s + 2, st2, st0, st1);
+
+    if (ksteps > 0) dma(0, stage(0));
+    if (ksteps > 1) dma(1, stage(1));
+    if (ksteps > 2) dma(2, stage(2));
+    if (ksteps > 0) {
+        if (ksteps > 2) MX_WAIT_VM(2 * MX_LOADS); else if (ksteps > 1) MX_WAIT_VM(MX_LOADS); else MX_WAIT_VM(0);
+        fixup(0, stage(0));
+        MX_WAIT_LGKM0();
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int r = 0; r < 32; ++r) frag_read(stage(0), F0, r);
+    }
+    if (ksteps > 1) publish(1, ksteps > 2);
+
+    auto step = [&](int64_t s, Frags &Fc, Frags &Fn) {
+        // unconditional, so that they can sit between the MFMAs; after the last step
+        // they read a stale (in-bounds) stage whose values are never used
+        const uint8_t *nst = stage(s + 1);
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            const int i0 = (2 * q) >> 3, j0 = (2 * q) & 7, j1 = j0 + 1;
+            // An empty asm statement pins the order (the compiler would otherwise put
+            // the 64 MFMAs first and the reads after them): it takes the previous
+            // pair's last result and hands this pair its scale, and as a volatile
+            // statement it stays between the previous read and this one.
+            int sa = Fc.sa[i0];
+            if (q > 0) {
+                const int pi = (2 * q - 1) >> 3, pj = (2 * q - 1) & 7;
+                asm volatile("" : "+v"(sa) : "a"(acc[pi][pj]));
+            }
+            acc[i0][j0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Fc.a[i0], Fc.b[j0], acc[i0][j0], 4, 4, 0,
+                                                                           sa, 0, Fc.sb[j0]);
+            acc[i0][j1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Fc.a[i0], Fc.b[j1], acc[i0][j1], 4, 4, 0,
+                                                                           sa, 0, Fc.sb[j1]);
+            frag_read(nst, Fn, q);
+        }
+        MX_WAIT_LGKM0();                               // this wave's reads of stage s + 1 are done
+        const bool more = s + 3 < ksteps;
+        if (more) dma(s + 3, stage(s));                // stage s was read during step s - 1
+        if (s + 2 < ksteps) publish(s + 2, more);
+    };
+    for (int64_t s = 0; s < ksteps; s += 2) {
+        step(s, F0, F1);
+        if (s + 1 < ksteps) step(s + 1, F1, F0);
     }
 
     // epilogue: one fully unrolled store nest per output kind, so every
@@ -560,6 +610,11 @@ hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st) {
     if (g.M <= 32) return wide ? run_small<2, 2>(a, st) : run_small<1, 2>(a, st);
     if (g.M <= 64) return run_small<1, 4>(a, st);
     // larger M: 256 x 256 tiles on the matrix cores, split K when the tiles are few
+    // the tile kernel addresses a tile's rows by 32-bit offsets from its first row
+    int64_t stride = g.a_ldc > g.w_ldc ? g.a_ldc : g.w_ldc;
+    stride = stride > g.a_lds ? stride : g.a_lds;
+    stride = stride > g.w_lds ? stride : g.w_lds;
+    if ((int64_t)MX_BM * stride >= ((int64_t)1 << 32)) return hipErrorInvalidValue;
     MXTArgs t;
     t.a_codes = g.a_codes; t.a_ldc = g.a_ldc; t.a_scales = g.a_scales; t.a_lds = g.a_lds;
     t.w_codes = g.w_codes; t.w_ldc = g.w_ldc; t.w_scales = g.w_scales; t.w_lds = g.w_lds;
@@ -575,7 +630,15 @@ hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st) {
         if (!g.scratch || g.scratch_bytes < mx_workspace_bytes(g.M, g.N, g.K, g.res_cols)) return hipErrorInvalidValue;
         t.part = static_cast<float *>(g.scratch);
     }
-    mx_tile_kernel<<<dim3((unsigned)(t.tiles_m * t.tiles_n), (unsigned)P), MX_NT, 0, st>>>(t);
+    const size_t lds = 3 * (size_t)MX_STAGE;
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mx_tile_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    mx_tile_kernel<<<dim3((unsigned)(t.tiles_m * t.tiles_n), (unsigned)P), MX_NT, lds, st>>>(t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P == 1) return e;
     const int64_t total = g.M * g.N;
