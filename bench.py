@@ -42,6 +42,8 @@ from block_scaled_fp4_02_amd import inputs  # noqa: E402
 METRIC = "NVFP4 GEMM µs & HBM GB/s at M=1–16; prefill TFLOP/s; % of roofline"
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0
+FP4_MFMA_PEAK_TFLOPS = 10100.0
+QUANT_BYTES_PER_ELEM = 2.5625      # bf16 read + codes + E4M3 scales
 RING_BYTES = 640 << 20
 
 
@@ -294,8 +296,34 @@ def main():
 
 def extra_detail(nvfp4, dev, tiled):
     """Residue K->2K overhead, M=64 augmented product, prefill TFLOP/s (one number each)."""
-    res = {"residue": [], "augmented": [], "prefill": []}
+    res = {"gemv": [], "residue": [], "augmented": [], "quantizer": [], "prefill": [],
+           "prefill_selective_residue": [], "mx_decode": [], "mx_prefill": []}
     prep = nvfp4.pack_tiled if tiled else (lambda t: t)
+    # the single GEMV x[1 x 4096] W[4096 x 4096]^T: activation quantized in the call
+    x, w = inputs.gemv_4096()
+    xd = x.to(dev)
+    wq = prep(nvfp4.quantize(w.to(dev)))
+    ring = Ring(wq, max(2, -(-RING_BYTES // wbytes(4096, 4096))))
+    n = len(ring.items)
+    y = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+    aq = nvfp4.quantize(xd)
+
+    def gemv_call():
+        for _ in range(n):
+            nvfp4.gemm(xd, ring.next(), out=y)
+
+    def gemv_kern():
+        for _ in range(n):
+            nvfp4.gemm(aq, ring.next(), out=y)
+
+    tf, _ = graph_time(gemv_call, 20, n)
+    tk, _ = graph_time(gemv_kern, 20, n)
+    res["gemv"].append({"M": 1, "K": 4096, "N": 4096, "us_call": round(tf * 1e6, 3),
+                        "GBs_call": round(call_bytes(1, 4096, 4096) / tf / 1e9, 1),
+                        "frac_hbm_call": round(call_bytes(1, 4096, 4096) / tf / 1e9 / HBM_PEAK_GBS, 4),
+                        "us_kernel": round(tk * 1e6, 3),
+                        "frac_hbm_kernel": round(kernel_bytes(1, 4096, 4096) / tk / 1e9 / HBM_PEAK_GBS, 4)})
+    del ring
     # residue-compensated decode, K = N = 8192
     x, w = inputs.residue_8192(16)
     xd = x.to(dev)
@@ -318,7 +346,8 @@ def extra_detail(nvfp4, dev, tiled):
         tc, _ = graph_time(comp, 20, n)
         res["residue"].append({"M": M, "K": 8192, "N": 8192, "us_plain": round(tb * 1e6, 3),
                                "us_residue": round(tc * 1e6, 3), "overhead": round(tc / tb - 1, 4),
-                               "GBs_residue": round(call_bytes(M, 8192, 8192) / tc / 1e9, 1)})
+                               "GBs_residue": round(call_bytes(M, 8192, 8192) / tc / 1e9, 1),
+                               "frac_hbm_residue": round(call_bytes(M, 8192, 8192) / tc / 1e9 / HBM_PEAK_GBS, 4)})
     del ring
     # augmented channels, M = 64, K = 4096, N = 14336
     x, g, xcal, w = inputs.outlier_aug()
@@ -339,6 +368,7 @@ def extra_detail(nvfp4, dev, tiled):
         res["augmented"].append({"M": 64, "K": 4096, "S": S, "N": 14336, "us_call": round(t * 1e6, 3),
                                  "overhead_vs_S0": round(t / t0 - 1, 4),
                                  "GBs": round(call_bytes(64, 14336, 4096) / t / 1e9, 1),
+                                 "frac_hbm": round(call_bytes(64, 14336, 4096) / t / 1e9 / HBM_PEAK_GBS, 4),
                                  "TFLOPs": round(flops / t / 1e12, 2)})
     del ring
     # prefill: bf16 out, activation quantize in the call
@@ -372,9 +402,70 @@ def extra_detail(nvfp4, dev, tiled):
                                    "TFLOPs_call": round(flops / tf / 1e12, 1),
                                    "us_kernel": round(tk * 1e6, 1), "TFLOPs_kernel": round(flops / tk / 1e12, 1),
                                    "frac_f16_mfma_kernel": round(flops / tk / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
+            # the activation quantizer alone (amax pass + quantize pass): 2.5625 B per element
+            tq, _ = graph_time(lambda: nvfp4.quantize(xm), reps, 1)
+            qb = QUANT_BYTES_PER_ELEM * M * K
+            res["quantizer"].append({"M": M, "K": K, "us": round(tq * 1e6, 1), "GBs": round(qb / tq / 1e9, 1),
+                                     "frac_hbm": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4)})
+            if M == 2048:
+                # selective residue on the prefill product: top S = 512 columns (activation
+                # quantized in the call, residue columns appended)
+                S = 512
+                ts, _ = graph_time(lambda: nvfp4.gemm_residue(xm, wq, S, out=y), reps, 1)
+                fl = 2.0 * M * N * (K + S)
+                res["prefill_selective_residue"].append({
+                    "M": M, "K": K, "S": S, "N": N, "us_call": round(ts * 1e6, 1),
+                    "overhead_vs_plain_call": round(ts / tf - 1, 4), "TFLOPs_call": round(fl / ts / 1e12, 1),
+                    "frac_f16_mfma_call": round(fl / ts / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)})
         del xall, wq, aq_cache
         torch.cuda.empty_cache()
+    res.update(mx_detail(nvfp4, dev))
     return res
+
+
+def mx_detail(nvfp4, dev):
+    """MXFP4 on the scaled FP4 matrix cores: decode sweep (kernel alone, weight ring) and
+    prefill (kernel alone), against 8 TB/s and the 10.1 PFLOP/s dense FP4 peak."""
+    out = {"mx_decode": [], "mx_prefill": []}
+    for si, (K, N) in enumerate(inputs.DECODE_SHAPES):
+        x, w = inputs.decode_sweep(si)
+        wq = nvfp4.mx_quantize(w.to(dev))
+        wb = N * K // 2 + N * K // 32
+        copies = max(2, -(-RING_BYTES // wb))
+        ring = [wq] + [nvfp4.MXTensor(wq.codes.clone(), wq.scales.clone(), K) for _ in range(copies - 1)]
+        for M in inputs.DECODE_MS:
+            aq = nvfp4.mx_quantize(x[:M].to(dev))
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+            def kern():
+                for r in ring:
+                    nvfp4.mx_gemm(aq, r, out=y)
+
+            t, _ = graph_time(kern, 20, len(ring))
+            b = wb + M * K // 2 + M * K // 32 + 4 * M * N
+            out["mx_decode"].append({"M": M, "K": K, "N": N, "us_kernel": round(t * 1e6, 3),
+                                     "GBs_kernel": round(b / t / 1e9, 1),
+                                     "frac_hbm_kernel": round(b / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del ring, wq
+    torch.manual_seed(0)
+    for (K, N) in inputs.PREFILL_SHAPES:
+        w = (torch.randn((N, K), device=dev, dtype=torch.float32) * 0.015).to(torch.bfloat16)
+        wq = nvfp4.mx_quantize(w)
+        del w
+        for M in inputs.PREFILL_MS:
+            x = torch.randn((M, K), device=dev, dtype=torch.float32).to(torch.bfloat16)
+            aq = nvfp4.mx_quantize(x)
+            del x
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            t, _ = graph_time(lambda: nvfp4.mx_gemm(aq, wq, out=y), 10 if M < 8192 else 4, 1)
+            fl = 2.0 * M * N * K
+            out["mx_prefill"].append({"M": M, "K": K, "N": N, "us_kernel": round(t * 1e6, 1),
+                                      "TFLOPs_kernel": round(fl / t / 1e12, 1),
+                                      "frac_fp4_mfma_kernel": round(fl / t / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4)})
+            del aq, y
+        del wq
+        torch.cuda.empty_cache()
+    return out
 
 
 def prefill_case(nvfp4, dev, tiled, mkn, reps):

@@ -201,7 +201,7 @@ size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S) 
         case 1: return kHeaderBytes + tensor_ws(M, K) + quant_ws(M) + gemm_ws(M, N, K, 0);
         case 2: return kHeaderBytes + tensor_ws(M, K + S) + quant_ws(M) + gemm_ws(M, N, K, S);
         case 3: return kHeaderBytes + up((size_t)std::max<int64_t>(M, 1) * sizeof(float), kAlign);
-        case 4: return mx_workspace_bytes(M, N, K, S);
+        case 4: return kHeaderBytes + mx_workspace_bytes(M, N, K, S);
         default: return 0;
     }
 }
@@ -433,15 +433,18 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, i
     CHECK(check_mx(a, M, K + S));
     if (!y && M > 0 && N > 0) return NVFP4_ERR_NULL;
     if (ldy < N) return NVFP4_ERR_SHAPE;
+    // the partials go after the header, which this product leaves untouched (the
+    // workspace may be shared with the NVFP4 entry points and their counters)
     const size_t need = mx_workspace_bytes(M, N, K, S);
-    if (need > 0 && (!ws || ws_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (need > 0 && (!ws || ws_bytes < kHeaderBytes + need)) return NVFP4_ERR_WORKSPACE;
     if (M == 0 || N == 0) return NVFP4_OK;
     MXGemmLaunch g;
     g.a_codes = a->codes; g.a_ldc = a->ld_codes; g.a_scales = a->scales; g.a_lds = a->ld_scales;
     g.w_codes = w->codes; g.w_ldc = w->ld_codes; g.w_scales = w->scales; g.w_lds = w->ld_scales;
     g.M = M; g.N = N; g.K = K; g.res_cols = S;
     g.y = y; g.yt = yt; g.ldy = ldy;
-    g.scratch = ws; g.scratch_bytes = ws_bytes;
+    g.scratch = need > 0 ? static_cast<uint8_t *>(ws) + kHeaderBytes : nullptr;
+    g.scratch_bytes = need > 0 ? ws_bytes - kHeaderBytes : 0;
     const hipError_t e = launch_mx_gemm(g, static_cast<hipStream_t>(stream));   // K == 0 stores zeros
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }

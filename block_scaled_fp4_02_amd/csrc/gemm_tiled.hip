@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "lds_dma.h"
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
@@ -437,6 +438,230 @@ void tiled2_kernel(TArgs a) {
     }
 }
 
+// ------------------------------------------------- FP4 operands staged in LDS
+// The large-M product with the operands kept in LDS as stored (FP4 codes and
+// E4M3 bytes, a quarter of the f16 bytes) and decoded to f16 per fragment in
+// registers, right before the MFMAs that use it.
+//
+// A step is 128 columns of K. Its codes and scale bytes go from memory into one
+// of three LDS stages by direct-to-LDS loads (no staging registers): row r's
+// 32-column chunk b (16 code bytes) at r * 64 + 16 p, its two E4M3 bytes
+// zero-extended into the dword at r * 4 + p, p = b ^ f(r) with
+// f(r) = ((r >> 1) ^ (r >> 2)) & 3, so that the fragment reads below (16 rows x
+// one chunk per 16 lanes) hit every bank group. The loads of step s + 3 go out
+// at the end of step s into the stage step s read; step s + 1's are waited for
+// there. A chunk past the data is loaded from its row's start and then
+// overwritten (zero codes and scales) by the thread that loaded it.
+//
+// 256 x 256 output tiles on 8 waves, two per SIMD (one's LDS reads and decode
+// run under the other's MFMAs), each a 128 x 64 block: 8 x 4 accumulators of
+// v_mfma_f32_16x16x32_f16. Per step a lane reads the 16 code bytes of chunk g
+// (its lane group) of each of its 12 rows, and MFMA k-substep j takes their
+// dword j: the MFMA's k-slot (g, e) is column 32 g + 8 j + e of the step, for
+// both operands, so the four substeps cover the 128 columns once. Dwords 0-1
+// take the chunk's first E4M3 byte, 2-3 its second. The decode is exact
+// (decode8: e(c) d in f16), the accumulation FP32, as in the other kernels.
+//
+// Residue columns are further steps (activation columns K + kw.., weight
+// columns kw..), as in tiled2_kernel. Tiled weights are read in place: a
+// chunk's 16 bytes and two scale bytes sit at offsets that split into a
+// per-lane part fixed for the kernel and a per-step part.
+constexpr int PF_BM = 256, PF_BN = 256;
+constexpr int PF_ACODE = PF_BM * 64, PF_BCODE = PF_BN * 64;          // code bytes per stage
+constexpr int PF_ASC = PF_BM * 16, PF_BSC = PF_BN * 16;              // a dword per chunk
+constexpr int PF_STAGE = PF_ACODE + PF_BCODE + PF_ASC + PF_BSC;       // 40 KiB
+constexpr int PF_GROUP_M = 8;                                         // row tiles per group of the tile order
+
+// 8 waves, 2 along M x 4 along N, two per SIMD. (Four waves of 128 x 128, one per
+// SIMD with the whole register file, decode a third less but measured half as fast:
+// nothing hides one wave's decode and LDS waits.)
+constexpr int PF_NW = 8;
+
+__global__ __launch_bounds__(64 * PF_NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fp4lds_kernel(TArgs a) {
+    constexpr int NW = PF_NW, PF_NT = 64 * NW;
+    constexpr int PF_CH = PF_BM * 4 / PF_NT;                          // chunks per thread and operand
+    constexpr int PF_LOADS = 4 * PF_CH;                               // direct-to-LDS loads per thread and step
+    constexpr int WN = NW / 2, CT = PF_BN / WN / 16;                  // waves along N, 16-column tiles per wave
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_pf[];   // [3][PF_STAGE]
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN, r16 = lane & 15, g = lane >> 4;
+    // tile order: each XCD takes a contiguous range of tiles (workgroups are dealt
+    // to the 8 XCDs round robin), walked in groups of PF_GROUP_M row tiles that
+    // sweep the columns together and so share panels in that XCD's L2
+    const int nblk = a.tiles_m * a.tiles_n;
+    int bid = blockIdx.x;
+    if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+    const int in_group = PF_GROUP_M * a.tiles_n, first_m = (bid / in_group) * PF_GROUP_M;
+    const int gsize = a.tiles_m - first_m < PF_GROUP_M ? a.tiles_m - first_m : PF_GROUP_M;
+    const int tm = first_m + (bid % in_group) % gsize, tn = (bid % in_group) / gsize;
+    const int64_t m0 = (int64_t)tm * PF_BM, n0 = (int64_t)tn * PF_BN;
+    const int64_t kmain = (a.K + 127) / 128, kall = kmain + (a.res_cols + 127) / 128;
+    const int64_t s0 = (int64_t)blockIdx.y * a.kchunk;
+    const int64_t ksteps = (s0 + a.kchunk < kall ? s0 + a.kchunk : kall) - s0;
+
+    // chunk i of this thread: c = PF_NT i + tid, row c / 4 of the tile, position
+    // c % 4; it fetches the chunk that belongs there (the row's low four bits are
+    // those of tid / 4 for every i)
+    const int q4 = (lane & 3) ^ (((lane >> 3) ^ (lane >> 4)) & 3);
+    const int gp = g ^ (((r16 >> 1) ^ (r16 >> 2)) & 3);     // position of chunk g in this lane's rows
+    // per-lane byte offsets from the tile's first row (rows past the matrix repeat
+    // its last row); 32 bits hold them (launcher-checked)
+    const uint8_t *abase = a.a_codes + m0 * a.a_ldc, *asbase = a.a_scales + m0 * a.a_lds;
+    const int64_t wrow0 = a.w_tiled ? n0 / 16 : n0;
+    const uint8_t *wbase = a.w_codes + wrow0 * a.w_ldc, *wsbase = a.w_scales + wrow0 * a.w_lds;
+    uint32_t ra[PF_CH], rsa[PF_CH], rb[PF_CH], rsb[PF_CH];
+#pragma unroll
+    for (int i = 0; i < PF_CH; ++i) {
+        const int row = (PF_NT * i + tid) >> 2;
+        const int64_t ma = m0 + row, nb = n0 + row;
+        const int64_t la = (ma < a.M ? ma : a.M - 1) - m0, n = nb < a.N ? nb : a.N - 1;
+        ra[i] = (uint32_t)(la * a.a_ldc);
+        rsa[i] = (uint32_t)(la * a.a_lds);
+        if (a.w_tiled) {          // 16 x 512 items: strip n / 16, lane 16 (k / 128 % 4) + n % 16, k / 32 % 4
+            rb[i] = (uint32_t)((n / 16 - n0 / 16) * a.w_ldc + 16 * (n & 15) + 1024 * q4);
+            rsb[i] = (uint32_t)((n / 16 - n0 / 16) * a.w_lds + 8 * (n & 15) + 2 * q4);
+        } else {
+            rb[i] = (uint32_t)((n - n0) * a.w_ldc + 16 * q4);
+            rsb[i] = (uint32_t)((n - n0) * a.w_lds + 2 * q4);
+        }
+    }
+    // step s of this range: weight columns kw.., activation columns ka.., and
+    // whether this thread's chunk of the step holds data
+    auto cols = [&](int64_t s, int64_t &kw, int64_t &ka, bool &ok) {
+        const bool main = s0 + s < kmain;
+        kw = (main ? s0 + s : s0 + s - kmain) * 128;
+        ka = main ? kw : a.K + kw;
+        ok = kw + 32 * q4 < (main ? a.K : a.res_cols);
+    };
+    auto dma = [&](int64_t s, uint8_t *st) {
+        int64_t kw, ka;
+        bool ok;
+        cols(s, kw, ka, ok);
+        const uint32_t ca = ok ? (uint32_t)(ka / 2 + 16 * q4) : 0u, sa = ok ? (uint32_t)(ka / 16 + 2 * q4) : 0u;
+        uint32_t cw = 0, sw = 0;
+        if (ok) {
+            if (a.w_tiled) {
+                cw = (uint32_t)((kw >> 9) * 4096 + 256 * ((kw >> 7) & 3));
+                sw = (uint32_t)((kw >> 9) * 512 + 128 * ((kw >> 7) & 3));
+            } else {
+                cw = (uint32_t)(kw / 2);
+                sw = (uint32_t)(kw / 16);
+            }
+        }
+        const uint32_t sbase = lds_addr_of(st);
+#pragma unroll
+        for (int i = 0; i < PF_CH; ++i) {
+            const uint32_t cbase = (uint32_t)(PF_NT * i + 64 * wave);   // first chunk of this wave's instruction
+            dma16s(abase, ra[i] + ca, sbase + 16 * cbase);
+            dma16s(wbase, rb[i] + cw, sbase + PF_ACODE + 16 * cbase);
+            dma2s(asbase, rsa[i] + sa, sbase + PF_ACODE + PF_BCODE + 4 * cbase);
+            dma2s(wsbase, rsb[i] + sw, sbase + PF_ACODE + PF_BCODE + PF_ASC + 4 * cbase);
+        }
+    };
+    // after this thread's loads of step s have landed: chunks past the data become
+    // zero codes and zero scales (the loads read the row's first bytes instead)
+    auto fixup = [&](int64_t s, uint8_t *st) {
+        int64_t kw, ka;
+        bool ok;
+        cols(s, kw, ka, ok);
+        if (ok) return;
+#pragma unroll
+        for (int i = 0; i < PF_CH; ++i) {
+            const int c = PF_NT * i + tid;
+            *reinterpret_cast<uint4 *>(st + 16 * c) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(st + PF_ACODE + 16 * c) = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint32_t *>(st + PF_ACODE + PF_BCODE + 4 * c) = 0u;
+            *reinterpret_cast<uint32_t *>(st + PF_ACODE + PF_BCODE + PF_ASC + 4 * c) = 0u;
+        }
+    };
+
+    float4v acc[8][CT];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j) acc[i][j] = float4v{0, 0, 0, 0};
+
+    auto stage = [&](int64_t s) { return lds_pf + (int)(s % 3) * PF_STAGE; };
+    // one step: this wave's 12 rows of codes and scales from LDS, then four
+    // k-substeps of 32 MFMAs, each operand fragment decoded right before use
+    auto compute = [&](const uint8_t *st) {
+        uint4 ca[8], cb[CT];
+        uint32_t sa[8], sb[CT];
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            const int row = wn * 16 * CT + 16 * j + r16;
+            cb[j] = *reinterpret_cast<const uint4 *>(st + PF_ACODE + row * 64 + 16 * gp);
+            sb[j] = *reinterpret_cast<const uint32_t *>(st + PF_ACODE + PF_BCODE + PF_ASC + 4 * (row * 4 + gp));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = wm * 128 + 16 * i + r16;
+            ca[i] = *reinterpret_cast<const uint4 *>(st + row * 64 + 16 * gp);
+            sa[i] = *reinterpret_cast<const uint32_t *>(st + PF_ACODE + PF_BCODE + 4 * (row * 4 + gp));
+        }
+        auto word = [](const uint4 &v, int k) { return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w; };
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            half8 bf[CT];
+#pragma unroll
+            for (int j = 0; j < CT; ++j) bf[j] = decode8(word(cb[j], k), scale_pair(sb[j] >> (8 * (k >> 1))));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const half8 af = decode8(word(ca[i], k), scale_pair(sa[i] >> (8 * (k >> 1))));
+#pragma unroll
+                for (int j = 0; j < CT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    if (ksteps > 0) dma(0, stage(0));
+    if (ksteps > 1) dma(1, stage(1));
+    if (ksteps > 2) dma(2, stage(2));
+    if (ksteps > 0) {
+        if (ksteps > 2) DMA_WAIT_VM(2 * PF_LOADS); else if (ksteps > 1) DMA_WAIT_VM(PF_LOADS); else DMA_WAIT_VM(0);
+        fixup(0, stage(0));
+        DMA_WAIT_LGKM0();
+        __builtin_amdgcn_s_barrier();
+    }
+    for (int64_t s = 0; s < ksteps; ++s) {
+        compute(stage(s));
+        if (s + 1 < ksteps) {
+            // step s + 1's loads landed (step s + 2's may still be in flight), patched, visible;
+            // past this barrier no wave reads stage s any more
+            if (s + 2 < ksteps) DMA_WAIT_VM(PF_LOADS); else DMA_WAIT_VM(0);
+            fixup(s + 1, stage(s + 1));
+            DMA_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();
+            if (s + 3 < ksteps) dma(s + 3, stage(s));
+        }
+    }
+
+    // epilogue: fully unrolled per output kind (constant accumulator indices)
+    float *part = a.part ? a.part + (int64_t)blockIdx.y * a.M * a.N : nullptr;
+    const float scale = part ? 1.0f : a.a_S[0] * a.w_S[0];
+    const int64_t mrow = m0 + wm * 128 + 4 * g, ncol = n0 + wn * 16 * CT + r16;
+    auto store_all = [&](auto kind) {
+        constexpr int KIND = decltype(kind)::value;   // 2: partial, 1: FP32, 0: BF16
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < CT; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t m = mrow + 16 * i + e, n = ncol + 16 * j;
+                    if (m < a.M && n < a.N) {
+                        if constexpr (KIND == 2) part[m * a.N + n] = acc[i][j][e];
+                        else if constexpr (KIND == 1) static_cast<float *>(a.y)[m * a.ldy + n] = acc[i][j][e] * scale;
+                        else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f2bf(acc[i][j][e] * scale);
+                    }
+                }
+    };
+    if (part) store_all(std::integral_constant<int, 2>{});
+    else if (a.yt == 1) store_all(std::integral_constant<int, 1>{});
+    else store_all(std::integral_constant<int, 0>{});
+}
+
 // Split-K combine: y[m][n] = S_a S_w sum_p part[p][m][n], in order p = 0, 1, ...
 // (deterministic); one thread per element.
 __global__ __launch_bounds__(256) void prefill_combine_kernel(const float *part, int P, int64_t M, int64_t N,
@@ -511,6 +736,71 @@ int prefill_splits(int64_t M, int64_t N, int64_t K, int64_t S) {
     return P;
 }
 
+// Split-K ranges of fp4lds_kernel: when its 256 x 256 tiles leave most CUs idle
+// and the 128-column steps are many, P ranges of at least 16 steps until the
+// chip holds about one workgroup per CU.
+int fp4lds_splits(int64_t M, int64_t N, int64_t K, int64_t S) {
+    if (M <= 64) return 1;
+    const int64_t tiles = ((M + PF_BM - 1) / PF_BM) * ((N + PF_BN - 1) / PF_BN);
+    const int64_t steps = (K + 127) / 128 + (S + 127) / 128;
+    int P = 1;
+    while (P < 8 && tiles * P < 192 && steps / (2 * P) >= 16) P *= 2;
+    return P;
+}
+
+inline bool aligned_to(const void *p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
+// fp4lds_kernel takes the long-K products: measured against tiled2_kernel at
+// M = 512 / 2048 / 8192 (bf16 out, tiled weights), it is ahead at K = 28672,
+// N = 8192 (0.39 / 0.47 / 0.48 of the f16 peak against 0.40 / 0.46 / 0.44) and
+// behind at K = 8192, N = 28672 for M <= 2048 (0.35 / 0.36 against 0.38 / 0.40;
+// level at M = 8192). Its other conditions: K and S multiples of 32 (whole
+// 32-column chunks), code rows 16-byte aligned and scale rows 2-byte aligned,
+// and a tile's rows within 32-bit offsets of its first row.
+constexpr int64_t kFp4ldsMinK = 16384;
+
+bool fp4lds_fits(const PrefillLaunch &g) {
+    if (g.M <= 64 || g.K % 32 != 0 || g.res_cols % 32 != 0) return false;
+    if (g.K + g.res_cols < kFp4ldsMinK) return false;
+    if (!aligned_to(g.a_codes, 16) || g.a_ldc % 16 != 0 || !aligned_to(g.a_scales, 2) || g.a_lds % 2 != 0) return false;
+    if (!aligned_to(g.w_codes, 16) || g.w_ldc % 16 != 0 || !aligned_to(g.w_scales, 2) || g.w_lds % 2 != 0) return false;
+    const int64_t wrows = g.w_tiled ? PF_BN / 16 : PF_BN;
+    const int64_t span_a = (int64_t)PF_BM * (g.a_ldc > g.a_lds ? g.a_ldc : g.a_lds);
+    const int64_t span_w = wrows * (g.w_ldc > g.w_lds ? g.w_ldc : g.w_lds);
+    return span_a < ((int64_t)1 << 32) && span_w < ((int64_t)1 << 32);
+}
+
+hipError_t run_fp4lds(const TArgs &a0, hipStream_t st, void *scratch, size_t scratch_bytes) {
+    TArgs a = a0;
+    a.tiles_m = (int)((a.M + PF_BM - 1) / PF_BM);
+    a.tiles_n = (int)((a.N + PF_BN - 1) / PF_BN);
+    const int P = fp4lds_splits(a.M, a.N, a.K, a.res_cols);
+    const int64_t kall = (a.K + 127) / 128 + (a.res_cols + 127) / 128;
+    a.P = P;
+    a.kchunk = (kall + P - 1) / P;
+    a.part = nullptr;
+    if (P > 1) {
+        if (!scratch || scratch_bytes < (size_t)P * (size_t)a.M * (size_t)a.N * sizeof(float))
+            return hipErrorInvalidValue;
+        a.part = static_cast<float *>(scratch);
+    }
+    const size_t lds = 3 * (size_t)PF_STAGE;
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&fp4lds_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    fp4lds_kernel<<<dim3((unsigned)(a.tiles_m * a.tiles_n), (unsigned)P), 64 * PF_NW, lds, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || P == 1) return e;
+    const int64_t total = a.M * a.N;
+    prefill_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a.part, P, a.M, a.N, a.a_S, a.w_S, a.y,
+                                                                            a.yt, a.ldy);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_impl(const PrefillLaunch &g, hipStream_t st) {
     TArgs a;
     a.a_codes = g.a_codes; a.a_ldc = g.a_ldc; a.a_scales = g.a_scales; a.a_lds = g.a_lds; a.a_S = g.a_S;
@@ -521,6 +811,7 @@ hipError_t launch_prefill_impl(const PrefillLaunch &g, hipStream_t st) {
     a.tiles_m = a.tiles_n = 0;
     const int64_t ktot = (g.K + BK - 1) / BK + (g.res_cols + BK - 1) / BK;
     a.P = 1; a.kchunk = ktot; a.part = nullptr;
+    if (fp4lds_fits(g)) return run_fp4lds(a, st, g.scratch, g.scratch_bytes);
     if (!large_tiles(g.M, g.K, g.res_cols)) {
         if (g.res_cols > 0) {
             if (g.M <= 64) return run<64, 128, true>(a, st);
@@ -548,8 +839,11 @@ hipError_t launch_prefill_impl(const PrefillLaunch &g, hipStream_t st) {
 
 }  // namespace
 
+// covers whichever kernel the call's strides select
 size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t S) {
-    const int P = prefill_splits(M, N, K, S);
+    const int P1 = prefill_splits(M, N, K, S);
+    const int P2 = (K % 32 == 0 && S % 32 == 0 && K + S >= kFp4ldsMinK) ? fp4lds_splits(M, N, K, S) : 1;
+    const int P = P1 > P2 ? P1 : P2;
     return P > 1 ? (size_t)P * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 

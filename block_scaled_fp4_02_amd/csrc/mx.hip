@@ -18,6 +18,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "lds_dma.h"
 #include "nvfp4_device.h"
 
 #pragma clang fp contract(off)
@@ -300,44 +301,16 @@ hipError_t run_small(const MXDArgs &a, hipStream_t st) {
 // 128-column step, every fragment read from LDS feeding 8 of them).
 // A step's codes and E8M0 bytes go from memory straight into LDS with gfx950's
 // direct-to-LDS loads (global_load_lds_dwordx4 / _ubyte: no staging registers,
-// no decode -- the matrix cores take them as stored): codes at row * 64 + 16 q
-// (a fragment read is 1 KiB contiguous per wave); a scale byte lands as a
+// no decode -- the matrix cores take them as stored): a row's 32-block b at
+// row * 64 + 16 p, p its swizzled position (below); a scale byte lands as a
 // zero-extended dword (the ubyte form writes lane l at base + 4 l), entry
-// row * 4 + block.
-// Three LDS stages: the loads of step s + 2 go out during step s, after step s's
-// fragments are in registers, and step s + 1's are waited for at its end. A
+// row * 4 + p.
+// Three LDS stages: the loads of step s + 3 go out at the end of step s, into
+// the stage step s - 1 read, and step s + 2's are waited for there. A
 // 32-block past the data is loaded from its row's start and then overwritten in
 // LDS by the thread that loaded it (codes 0, scale 127). Residue columns are
 // further steps, as in the small-M kernel. Split-K writes FP32 partial tiles
 // for a combine in fixed order.
-// Direct-to-LDS loads, issued from asm blocks that have no output registers: the
-// hardware writes lane l's 16 bytes at M0 + 16 l (dwordx4), its byte zero-extended
-// at M0 + 4 l (ubyte), M0 = the wave's LDS address
-// (set in the same block). The compiler does not see these as LDS writes, so it
-// adds no waits of its own between them and reads of other stages; the kernel
-// waits for them itself (vmcnt) before the barrier that publishes a stage.
-#pragma clang diagnostic ignored "-Winline-asm"   // M0 is named as clobbered on purpose
-__device__ inline void dma16(const void *src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
-}
-__device__ inline void dma1(const void *src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ubyte %1, off"
-                 :: "s"(lds_addr), "v"(src) : "memory", "m0");
-}
-// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane offset.
-__device__ inline void dma16s(const void *base, uint32_t off, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
-}
-__device__ inline void dma1s(const void *base, uint32_t off, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ubyte %1, %2"
-                 :: "s"(lds_addr), "v"(off), "s"(base) : "memory", "m0");
-}
-__device__ inline uint32_t lds_addr_of(const void *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p);
-}
-
 constexpr int MX_BM = 256, MX_BN = 256, MX_NW = 4, MX_NT = 64 * MX_NW;
 constexpr int MX_ACODE = MX_BM * 64, MX_BCODE = MX_BN * 64;          // bytes per stage
 constexpr int MX_ASC = MX_BM * 4 * 4, MX_BSC = MX_BN * 4 * 4;        // a dword per scale byte
@@ -357,11 +330,6 @@ struct MXTArgs {
     int64_t kchunk;                            // k-steps per split-K range (blockIdx.y)
     float *part;                               // split-K partials [P][M][N], or nullptr
 };
-
-// s_waitcnt with vmcnt <= n (n < 64) and the other counters left alone, and with
-// lgkmcnt == 0 and the others left alone (gfx9 encoding)
-#define MX_WAIT_VM(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
-#define MX_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4))
 
 __global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mx_tile_kernel(MXTArgs a) {
@@ -477,9 +445,9 @@ void mx_tile_kernel(MXTArgs a) {
         }
     };
     auto publish = [&](int64_t s, bool more) {       // step s's loads landed, patched, visible
-        if (more) MX_WAIT_VM(MX_LOADS); else MX_WAIT_VM(0);
+        if (more) DMA_WAIT_VM(MX_LOADS); else DMA_WAIT_VM(0);
         fixup(s, stage(s));
-        MX_WAIT_LGKM0();
+        DMA_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
     };
 
@@ -487,9 +455,9 @@ void mx_tile_kernel(MXTArgs a) {
     if (ksteps > 1) dma(1, stage(1));
     if (ksteps > 2) dma(2, stage(2));
     if (ksteps > 0) {
-        if (ksteps > 2) MX_WAIT_VM(2 * MX_LOADS); else if (ksteps > 1) MX_WAIT_VM(MX_LOADS); else MX_WAIT_VM(0);
+        if (ksteps > 2) DMA_WAIT_VM(2 * MX_LOADS); else if (ksteps > 1) DMA_WAIT_VM(MX_LOADS); else DMA_WAIT_VM(0);
         fixup(0, stage(0));
-        MX_WAIT_LGKM0();
+        DMA_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int r = 0; r < 32; ++r) frag_read(stage(0), F0, r);
@@ -518,7 +486,7 @@ void mx_tile_kernel(MXTArgs a) {
                                                                            sa, 0, Fc.sb[j1]);
             frag_read(nst, Fn, q);
         }
-        MX_WAIT_LGKM0();                               // this wave's reads of stage s + 1 are done
+        DMA_WAIT_LGKM0();                               // this wave's reads of stage s + 1 are done
         const bool more = s + 3 < ksteps;
         if (more) dma(s + 3, stage(s));                // stage s was read during step s - 1
         if (s + 2 < ksteps) publish(s + 2, more);

@@ -216,7 +216,9 @@ nvfp4_status nvfp4_mx_quantize(const void *x, int xt, int64_t rows, int64_t K_in
  * columns meet W's own first S columns (never materialized). FP32 accumulation
  * in the scaled FP4 matrix cores; y dtype yt (FP32 or BF16 round to nearest
  * even), leading dimension ldy. Workspace: nvfp4_workspace_size(4, M, N, K, S)
- * bytes (may be 0, then ws may be NULL). */
+ * bytes; its first 8 KiB (the counter header the NVFP4 entry points keep) are
+ * never written, so one workspace can serve both formats. When the product needs
+ * no split-K partials, ws may be NULL. */
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, int64_t residue_cols,
                            void *y, int yt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 

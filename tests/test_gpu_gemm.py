@@ -364,11 +364,13 @@ def test_in_launch_quantization_shapes(nv, orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(700, 16400, 1040), (300, 16400, 1040), (520, 12304, 2064), (100, 300, 1040),
-                                   (300, 3000, 16400), (520, 8960, 1040)])
+                                   (300, 3000, 16400), (520, 8960, 1040), (300, 3000, 16416), (700, 1040, 20000)])
 def test_prefill_large_tiles_ragged(nv, orc, M, N, K):
-    """Shapes that take the pipelined product (256 x 256 and 128 x 128 tiles, and
-    256 x 256 with K split four ways): ragged M, N, and a K ending in a half chunk.
-    Sampled outputs against the oracle; row-major and tiled weights give identical bits."""
+    """Shapes that take the pipelined products (256 x 256 and 128 x 128 tiles, and
+    256 x 256 with K split four ways; FP4 operands in LDS at K >= 16384 with K a
+    multiple of 32): ragged M, N, a K ending in a half chunk, and K ending one or
+    few chunks into a 128-column step. Sampled outputs against the oracle; row-major
+    and tiled weights give identical bits."""
     x = inputs.small_random(800 + M, M, K)
     w = inputs.small_random(801 + N, N, K, scale=0.02)
     note(f"large-tile prefill M={M} N={N} K={K}")

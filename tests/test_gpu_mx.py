@@ -159,3 +159,32 @@ def test_mx_prefill_tiles(nv, orc, M, N, K, S):
     err = gemm_error(y.cpu().numpy()[np.ix_(rows, cols)], ref)
     assert err <= TOL, err
     assert bf16_bound_ok(yb.float().cpu().numpy()[np.ix_(rows, cols)], ref)
+
+
+def test_mx_split_k_keeps_workspace_header(nv, orc):
+    """An MXFP4 product with split-K partials shares the stream's workspace with the
+    NVFP4 entry points: its partials must land after the 8 KiB counter header, which
+    the NVFP4 split-K decode plans rely on staying as they left it. Regression: the
+    partials once started at the workspace's first byte, and a later split-K NVFP4
+    decode call on the same workspace then returned wrong outputs."""
+    M, N, K = 512, 8192, 28672
+    assert nv.lib().nvfp4_workspace_size(4, M, N, K, 0) > 8192      # this shape splits K
+    x = inputs.activations(5, 4, M, K, 0.01, 50.0)
+    w = inputs.weights(5, 4, N, K, 0.015)
+    aq, wq = nv.mx_quantize(x.to(DEV)), nv.mx_quantize(w.to(DEV))
+    # an NVFP4 call first, so the workspace exists and its header holds live state
+    xs, ws = inputs.decode_sweep(1)
+    wn = nv.quantize(ws.to(DEV))
+    y0 = nv.gemm(xs[:16].to(DEV), wn)
+    torch.cuda.synchronize()
+    n = nv.lib().nvfp4_workspace_size(4, M, N, K, 0)
+    buf = nv.workspace(n, DEV)
+    head = buf[:8192].clone()
+    note("mx split-K product on the shared workspace")
+    nv.mx_gemm(aq, wq)
+    torch.cuda.synchronize()
+    assert torch.equal(nv.workspace(n, DEV)[:8192], head), "MX product wrote into the counter header"
+    note("NVFP4 split-K decode call after it")
+    y1 = nv.gemm(xs[:16].to(DEV), wn)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
