@@ -7,8 +7,9 @@
 //                as one partial maximum per workgroup -- no atomics, so the
 //                result does not depend on scheduling;
 //   quant pass   every workgroup folds the partials into S, then quantizes
-//                groups of 64 columns (4 blocks of 16) per thread: block absmax,
-//                E4M3 block scale, E2M1 codes, nibble packing, and the residue
+//                16-element blocks (two lanes per block without a reorder, one
+//                thread per block group with it): block absmax, E4M3 block
+//                scale, E2M1 codes, nibble packing, and the residue
 //                R = x - fl(fl(e d) S) of columns below res_cols, quantized
 //                against the same S and stored after column K_in.
 // All rounding follows the FP32 order of nvfp4.h; contraction into FMA is off
@@ -241,41 +242,148 @@ __device__ inline void process_group(const QArgs &a, const float *v, int nb, int
     }
 }
 
+// ------------------------------------------ large activations, lane pairs
+// The flat quantizer (no reorder): two lanes per 16-element block, each loading
+// 8 consecutive elements, so a wave's load is 1 KiB contiguous (32 blocks). The
+// two lanes exchange their half maxima, then each encodes its own 8 codes (one
+// dword) with the block's E4M3 scale -- the same FP32 steps as encode_block --
+// and the even lane stores the scale byte. Grid-stride over blocks with two
+// blocks per lane pair in flight.
+
+template <int XT>
+__device__ inline void load8(const void *base, int64_t off, float *v) {
+    if constexpr (XT == IN_BF16) {
+        const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = u2f(w[i] << 16);
+            v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+        const float4 q0 = p[0], q1 = p[1];
+        v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+        v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+    }
+}
+
+__device__ inline void gamma8(const uint16_t *g, int64_t off, float *v) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(g + off);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = u2f(w[i] << 16);
+        v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+    }
+}
+
+__device__ inline void smooth8(const float *s, int64_t off, float *v) {
+    const float4 *p = reinterpret_cast<const float4 *>(s + off);
+    const float4 q0 = p[0], q1 = p[1];
+    v[0] = v[0] * q0.x; v[1] = v[1] * q0.y; v[2] = v[2] * q0.z; v[3] = v[3] * q0.w;
+    v[4] = v[4] * q1.x; v[5] = v[5] * q1.y; v[6] = v[6] * q1.z; v[7] = v[7] * q1.w;
+}
+
+// This lane's half of a block (the partner lane, lane ^ 1, holds the other half):
+// returns the block's E4M3 byte, the 8 codes in cw (low nibble first) and d.
+__device__ inline uint32_t encode_half(const float *v, float S, float t, uint32_t &cw, float &d) {
+    float ab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ab = fmaxf(ab, fabsf(v[i]));
+    ab = fmaxf(ab, __shfl_xor(ab, 1));
+    const float sf = ab / t;
+    const uint32_t db = e4m3_rne_sat(sf);
+    d = e4m3_to_float(db);
+    const float s = d * S;
+    const float rcp = (s > 0.0f) ? 1.0f / s : 0.0f;
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * rcp, v[1] * rcp, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * rcp, v[3] * rcp, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * rcp, v[5] * rcp, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * rcp, v[7] * rcp, 1.0f, 3);
+    cw = w;
+    return db;
+}
+
+// Residue of this lane's half: R = x - fl(fl(e d) S), as block_residue.
+__device__ inline void residue_half(const float *v, uint32_t cw, float d, float S, float *r) {
+    typedef float float2v __attribute__((ext_vector_type(2)));
+    float2v e[4];
+    e[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+    e[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+    e[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+    e[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float ed = e[i >> 1][i & 1] * d;
+        const float deq = ed * S;
+        r[i] = v[i] - deq;
+    }
+}
+
 template <int XT, bool NORM>
-__global__ __launch_bounds__(kThreads) void quantize_flat_kernel(QArgs a) {
+__global__ __launch_bounds__(kThreads) void quantize_pairs_kernel(QArgs a) {
     __shared__ float sh[kThreads / 64];
     const float S = tensor_scale(a, sh);
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.S_out = S;
     const float t = 6.0f * S;
-    const int64_t ng = (a.K_in + 63) / 64, total = a.rows * ng;
-    for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total;
-         g += (int64_t)gridDim.x * kThreads) {
-        const int64_t row = g / ng, gi = g - row * ng, col0 = 64 * gi;
-        const int64_t rem = a.K_in - col0;
-        const int nb = rem >= 64 ? 4 : (int)(rem / 16);
-        float v[64];
-        float r = 1.0f;
-        if (NORM) r = a.rscale[row];
+    const int h = threadIdx.x & 1;
+    const int64_t nb = a.K_in / 16, total = a.rows * nb;
+    const int64_t stride = (int64_t)gridDim.x * (kThreads / 2);
+    // block p of the flattened (row, block) order: load, RMSNorm / smoothing, encode, store
+    auto where = [&](int64_t p, int64_t &row, int64_t &b) {
+        row = p / nb;
+        b = p - row * nb;
+    };
+    auto prep = [&](int64_t row, int64_t col, float *v) {
+        if (NORM) {
+            const float r = a.rscale[row];
+            float g[8];
+            gamma8(a.gamma, col, g);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (b < nb) {
-                load16<XT>(a.x, row * a.ldx + col0 + 16 * b, v + 16 * b);
-                if (NORM) {
-                    float gm[16];
-                    gamma16(a.gamma, col0 + 16 * b, gm);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float y = v[16 * b + i] * r;
-                        v[16 * b + i] = y * gm[i];
-                    }
-                }
-                if (a.smooth) smooth16(a.smooth, col0 + 16 * b, v + 16 * b);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[16 * b + i] = 0.0f;
+            for (int i = 0; i < 8; ++i) {
+                const float y = v[i] * r;
+                v[i] = y * g[i];
             }
         }
-        process_group(a, v, nb, row, col0, S, t);
+        if (a.smooth) smooth8(a.smooth, col, v);
+    };
+    auto emit = [&](int64_t row, int64_t b, const float *v) {
+        const int64_t col = 16 * b + 8 * h;
+        uint32_t cw;
+        float d;
+        const uint32_t db = encode_half(v, S, t, cw, d);
+        *reinterpret_cast<uint32_t *>(a.codes + row * a.ldc + col / 2) = cw;
+        if (h == 0) a.scales[row * a.lds + b] = (uint8_t)db;
+        if (16 * b < a.res_cols) {                 // the same for both lanes of the pair
+            float rv[8];
+            residue_half(v, cw, d, S, rv);
+            uint32_t rc;
+            float dr;
+            const uint32_t rdb = encode_half(rv, S, t, rc, dr);
+            const int64_t rcol = a.K_in + col;
+            *reinterpret_cast<uint32_t *>(a.codes + row * a.ldc + rcol / 2) = rc;
+            if (h == 0) a.scales[row * a.lds + rcol / 16] = (uint8_t)rdb;
+        }
+    };
+    for (int64_t p = (int64_t)blockIdx.x * (kThreads / 2) + (threadIdx.x >> 1); p < total; p += 2 * stride) {
+        const int64_t p1 = p + stride;
+        const bool two = p1 < total;               // the same for both lanes of the pair
+        int64_t r0, b0, r1 = 0, b1 = 0;
+        where(p, r0, b0);
+        float v0[8], v1[8];
+        load8<XT>(a.x, r0 * a.ldx + 16 * b0 + 8 * h, v0);
+        if (two) {
+            where(p1, r1, b1);
+            load8<XT>(a.x, r1 * a.ldx + 16 * b1 + 8 * h, v1);
+        }
+        prep(r0, 16 * b0 + 8 * h, v0);
+        emit(r0, b0, v0);
+        if (two) {
+            prep(r1, 16 * b1 + 8 * h, v1);
+            emit(r1, b1, v1);
+        }
     }
 }
 
@@ -699,11 +807,12 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
         else { if (norm) QP(IN_F32, true); else QP(IN_F32, false); }
 #undef QP
     } else {
-        const int64_t groups = q.rows * ((q.K_in + 63) / 64);
-        int64_t g = (groups + kThreads - 1) / kThreads;
-        if (g > 8192) g = 8192;
+        // two lanes per block, two blocks per lane pair in flight; up to 8 workgroups per CU
+        const int64_t blocks = q.rows * (q.K_in / 16);
+        int64_t g = (blocks + kThreads - 1) / kThreads;
+        if (g > 2048) g = 2048;
         if (g < 1) g = 1;
-#define QF(XT, NM) quantize_flat_kernel<XT, NM><<<(int)g, kThreads, 0, st>>>(a)
+#define QF(XT, NM) quantize_pairs_kernel<XT, NM><<<(int)g, kThreads, 0, st>>>(a)
         if (q.xt == IN_BF16) { if (norm) QF(IN_BF16, true); else QF(IN_BF16, false); }
         else { if (norm) QF(IN_F32, true); else QF(IN_F32, false); }
 #undef QF
