@@ -140,6 +140,12 @@ def main():
     ap.add_argument("--prefill-case", default="",
                     help="M,K,N: run only the prefill product on pre-quantized activations, --reps launches "
                          "(for profiling the MFMA kernel; prints one line with its time)")
+    ap.add_argument("--mx-prefill-case", default="",
+                    help="M,K,N: run only the MXFP4 product on pre-quantized operands, --reps launches "
+                         "(for profiling the scaled-FP4 tile kernel; prints one line with its time)")
+    ap.add_argument("--quantize-case", default="",
+                    help="M,K: run only the activation quantizer on bf16 X [M x K], --reps launches "
+                         "(for profiling the quantizer passes; prints one line with its time)")
     ap.add_argument("--augmented-case", type=int, default=-1,
                     help="S: run only the M=64, K=4096, N=14336 augmented call (RMSNorm, channel reorder, "
                          "S residue columns, quantization in the call) on a weight ring, --reps graph replays "
@@ -166,6 +172,12 @@ def main():
 
     if args.prefill_case:
         prefill_case(nvfp4, dev, args.layout == "tiled", [int(v) for v in args.prefill_case.split(",")], args.reps)
+        return
+    if args.mx_prefill_case:
+        mx_prefill_case(nvfp4, dev, [int(v) for v in args.mx_prefill_case.split(",")], args.reps)
+        return
+    if args.quantize_case:
+        quantize_case(nvfp4, dev, [int(v) for v in args.quantize_case.split(",")], args.reps)
         return
     if args.augmented_case >= 0:
         augmented_case(nvfp4, dev, args.layout == "tiled", args.augmented_case, args.reps)
@@ -493,6 +505,47 @@ def prefill_case(nvfp4, dev, tiled, mkn, reps):
     print(json.dumps({"prefill_case": [M, K, N], "reps": reps, "us_per_call": round(us, 1),
                       "TFLOPs": round(flops / us / 1e6, 1),
                       "frac_f16_mfma": round(flops / us / 1e6 / F16_MFMA_PEAK_TFLOPS, 4)}), flush=True)
+
+
+def timed_launches(fn, reps):
+    """fn() once untimed, then `reps` launches between HIP events; seconds per launch."""
+    fn()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / 1e3 / max(reps, 1)
+
+
+def mx_prefill_case(nvfp4, dev, mkn, reps):
+    """One MXFP4 product shape, kernel alone (both operands quantized before), `reps` launches."""
+    M, K, N = mkn
+    torch.manual_seed(0)
+    x = torch.randn((M, K), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn((N, K), device=dev, dtype=torch.float32) * 0.015).to(torch.bfloat16)
+    aq, wq = nvfp4.mx_quantize(x), nvfp4.mx_quantize(w)
+    del x, w
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t = timed_launches(lambda: nvfp4.mx_gemm(aq, wq, out=y), reps)
+    fl = 2.0 * M * N * K
+    print(json.dumps({"mx_prefill_case": [M, K, N], "reps": reps, "us_per_call": round(t * 1e6, 1),
+                      "TFLOPs": round(fl / t / 1e12, 1),
+                      "frac_fp4_mfma": round(fl / t / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4)}), flush=True)
+
+
+def quantize_case(nvfp4, dev, mk, reps):
+    """The activation quantizer alone on bf16 X [M x K] (amax pass + quantize pass), `reps` launches."""
+    M, K = mk
+    torch.manual_seed(0)
+    x = torch.randn((M, K), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    t = timed_launches(lambda: nvfp4.quantize(x), reps)
+    b = QUANT_BYTES_PER_ELEM * M * K
+    print(json.dumps({"quantize_case": [M, K], "reps": reps, "us_per_call": round(t * 1e6, 1),
+                      "GBs": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}),
+          flush=True)
 
 
 def augmented_case(nvfp4, dev, tiled, S, reps):

@@ -38,7 +38,9 @@
 // round trip queues behind the weight stream.
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
+#include <unordered_map>
 
 #include "internal.h"
 #include "nvfp4_device.h"
@@ -1076,7 +1078,7 @@ const void *kernel_ptr(int MT, bool res, bool tiled, bool stk) {
 // -- plus ~2 us for each further round of workgroups (a workgroup's start-up:
 // arguments, operand, first items), plus ~1.5 us for a split-K combine, which
 // costs three dependent round trips through the memory system.
-Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
+Plan plan_compute(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm, int ncu) {
     Plan pl;
     const bool res = res_cols > 0;
     // operand rows: residue rows stacked under the activation rows when M <= 8,
@@ -1088,7 +1090,6 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     pl.MT = (M <= 16 && pl.Mp < 16) ? 1 : 2;
     pl.NT = (N + 15) / 16;
     const int64_t ku = (K + 511) / 512 > 0 ? (K + 511) / 512 : 1;
-    const int ncu = cu_count();
     pl.Rr = pl.Mp ? 2 * pl.Mp : (int)M;
     const int64_t op_rows = pl.Mp ? 2 * pl.Mp : (res ? 2 * M : M);   // rows of operand per unit
     double best = 1e30;
@@ -1115,14 +1116,6 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
                                     (P > 1 ? 1.5 + 0.1 * (double)P : 0.0) + (KW > 1 ? 0.1 : 0.0);
                 if (cost < best) { best = cost; bU = (int)U; bKW = KW; bntw = ntw; found = true; }
             }
-        }
-    }
-    if (const char *e = std::getenv("NVFP4_DECODE_FORCE")) {         // tuning override "U,KW,ntw"
-        int fu = 0, fk = 0, ft = 0;
-        if (std::sscanf(e, "%d,%d,%d", &fu, &fk, &ft) == 3 && fu >= 1 && (fk == 1 || fk == 2 || fk == 4) &&
-            ft >= 1 && ft * ((fu + fk - 1) / fk) <= kMaxItems && (fk == 1 || ft <= 2) &&
-            (size_t)fu * 1024 * (size_t)op_rows + kLdsStatic <= kLdsPerCu) {
-            bU = fu; bKW = fk; bntw = ft; found = true;
         }
     }
     if (!found) { bU = 1; bKW = 1; bntw = 1; }
@@ -1155,10 +1148,44 @@ Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, boo
     // per thread on, racing wins at one).
     const int64_t pre_per_thread = (((kc + 31) / 32) * (res_cols > 0 ? 2 : 1) + step - 1) / step;
     pl.ordered = pl.mode == MODE_LOCAL || pre_per_thread > 1;
-    if (std::getenv("NVFP4_DEBUG_PLAN"))
-        std::fprintf(stderr, "[nvfp4] decode plan M=%lld N=%lld K=%lld S=%lld: MT=%d U=%d P=%d KW=%d T=%d G=%d "
-                     "lds=%zu mode=%d ordered=%d cost=%.2f\n", (long long)M, (long long)N, (long long)K,
-                     (long long)res_cols, pl.MT, pl.U, pl.P, pl.KW, pl.T, pl.G, pl.lds, pl.mode, (int)pl.ordered, best);
+    return pl;
+}
+
+// Plans are computed once per (shape, mode, CU count) and kept: a call asks for
+// its plan up to three times (workspace size, fusion check, launch), and the
+// search above walks a few hundred candidates. Thread-safe; the table is
+// dropped wholesale if it ever holds 4096 shapes.
+struct PlanKey {
+    int64_t M, N, K, S;
+    int flags, ncu;
+    bool operator==(const PlanKey &o) const {
+        return M == o.M && N == o.N && K == o.K && S == o.S && flags == o.flags && ncu == o.ncu;
+    }
+};
+struct PlanKeyHash {
+    size_t operator()(const PlanKey &k) const {
+        uint64_t h = 1469598103934665603ull;
+        for (uint64_t v : {(uint64_t)k.M, (uint64_t)k.N, (uint64_t)k.K, (uint64_t)k.S, (uint64_t)k.flags,
+                           (uint64_t)k.ncu})
+            h = (h ^ v) * 1099511628211ull;
+        return (size_t)h;
+    }
+};
+
+Plan plan_for(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x, bool norm_or_perm) {
+    static std::mutex mu;
+    static std::unordered_map<PlanKey, Plan, PlanKeyHash> table;
+    const int ncu = cu_count();
+    const PlanKey key{M, N, K, res_cols, (raw_x ? 1 : 0) | (norm_or_perm ? 2 : 0), ncu};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        const auto it = table.find(key);
+        if (it != table.end()) return it->second;
+    }
+    const Plan pl = plan_compute(M, N, K, res_cols, raw_x, norm_or_perm, ncu);
+    std::lock_guard<std::mutex> lock(mu);
+    if (table.size() >= 4096) table.clear();
+    table.emplace(key, pl);
     return pl;
 }
 
