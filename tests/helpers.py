@@ -1,4 +1,5 @@
 """Shared helpers for the GPU parity tests (no NVFP4 arithmetic here)."""
+import os
 import sys
 
 import numpy as np
@@ -26,15 +27,28 @@ def assert_qtensor_equal(gpu_t, ref, what: str):
                              f"{codes[r, j]:#x} != {ref.codes[r, j]:#x}")
 
 
+# every gemm_error comparison of the session: (test, floored error, normwise error,
+# floor-clamped elements, elements); conftest prints a summary at the end
+P2_RECORDS = []
+
+
 def gemm_error(y, y_ref) -> float:
-    """max |y - y*| / max(|y*|, 1e-3 max|y*|) -- the floored relative error."""
+    """max |y - y*| / max(|y*|, 1e-3 max|y*|) -- the floored relative error. Also records
+    the plain normwise max|y - y*| / max|y*| and how many elements sit below the floor."""
     y = np.asarray(y, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     if y_ref.size == 0:
         return 0.0
-    floor = 1e-3 * np.max(np.abs(y_ref))
+    amax = np.max(np.abs(y_ref))
+    floor = 1e-3 * amax
     den = np.maximum(np.abs(y_ref), floor if floor > 0 else 1e-30)
-    return float(np.max(np.abs(y - y_ref) / den))
+    diff = np.abs(y - y_ref)
+    err = float(np.max(diff / den))
+    normwise = float(np.max(diff) / amax) if amax > 0 else float(np.max(diff))
+    clamped = int(np.count_nonzero(np.abs(y_ref) < floor))
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    P2_RECORDS.append((test, err, normwise, clamped, int(y_ref.size)))
+    return err
 
 
 def bf16_bound_ok(y_bf16, y_ref, tol=2e-3) -> bool:
