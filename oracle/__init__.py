@@ -339,3 +339,52 @@ def mx_weight_aug(w: MXTensor, S_cols: int) -> MXTensor:
                     np.ascontiguousarray(np.concatenate([w.scales, w.scales[:, :S_cols // 32]], axis=1)),
                     w.K + S_cols)
 
+
+
+# ------------------------------------------------- decode attention (compensated)
+# ResServe abstract: the FP4 activation base plus FP4-quantized residue is applied
+# "to linear layers and decode attention". Reading (the pages give no attention
+# formula; this is scaled dot-product attention for one decode query per head):
+# the KV cache is stored in NVFP4 like a weight -- K as [H*T, D] (row h*T + t,
+# blocks along D), V transposed as [H*D, T] (row h*D + j, blocks along T), one
+# tensor scale each -- and the two activation operands of the step, the query
+# q_h and the probabilities p_h, carry the base + residue of the linear layers:
+#   s_h = ( [Q(q_h) | Q(R_q)] . [K_h | K_h]^T ) / sqrt(D)       (the residue product)
+#   p_h = softmax(s_h)                  in FP32: m = max s, e = exp(s - m), p = e / sum(e)
+#   o_h =   [Q(p_h) | Q(R_p)] . [Vt_h | Vt_h]^T
+# with each q_h and p_h quantized as its own tensor (its own tensor scale), and
+# compensate=False dropping the residue columns. Products are FP64 (gemm).
+
+def _rows(q: QTensor, r0: int, r1: int, dup: bool) -> QTensor:
+    """Rows [r0, r1) of a quantized tensor, with its codes and scales repeated once
+    along K when dup (W_aug = [W | W]: the tail is W's own columns)."""
+    c, s = q.codes[r0:r1, : q.K // 2], q.scales[r0:r1, : q.K // 16]
+    if dup:
+        c, s = np.concatenate([c, c], axis=1), np.concatenate([s, s], axis=1)
+    return QTensor(np.ascontiguousarray(c), np.ascontiguousarray(s), q.S, q.K * (2 if dup else 1))
+
+
+def softmax_f32(s) -> np.ndarray:
+    """p = e / sum(e), e = exp(s - max s), every step in FP32 (numpy float32 ops)."""
+    s = np.asarray(s, np.float32)
+    e = np.exp(s - np.max(s)).astype(np.float32)
+    return (e / np.float32(np.sum(e, dtype=np.float32))).astype(np.float32)
+
+
+def decode_attention(q, k_cache: QTensor, vt_cache: QTensor, H: int, T: int, D: int,
+                     compensate: bool = True, return_p: bool = False):
+    """o [H, D] (FP64) of the compensated decode attention above; q is [H, D]."""
+    q = _f32(q)
+    assert q.shape == (H, D) and k_cache.K == D and k_cache.rows == H * T
+    assert vt_cache.K == T and vt_cache.rows == H * D and D % 16 == 0 and T % 16 == 0
+    o = np.zeros((H, D), np.float64)
+    ps = np.zeros((H, T), np.float32)
+    inv = 1.0 / np.sqrt(np.float64(D))
+    for h in range(H):
+        qa = quantize_aug(q[h:h + 1], S_cols=D if compensate else 0)
+        y = gemm(qa, _rows(k_cache, h * T, (h + 1) * T, compensate))[0]
+        p = softmax_f32((y * inv).astype(np.float32))
+        ps[h] = p
+        pa = quantize_aug(p[None, :], S_cols=T if compensate else 0)
+        o[h] = gemm(pa, _rows(vt_cache, h * D, (h + 1) * D, compensate))[0]
+    return (o, ps) if return_p else o
