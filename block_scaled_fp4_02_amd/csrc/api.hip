@@ -202,6 +202,7 @@ size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S) 
         case 2: return kHeaderBytes + tensor_ws(M, K + S) + quant_ws(M) + gemm_ws(M, N, K, S);
         case 3: return kHeaderBytes + up((size_t)std::max<int64_t>(M, 1) * sizeof(float), kAlign);
         case 4: return kHeaderBytes + mx_workspace_bytes(M, N, K, S);
+        case 5: return K > 0 ? kHeaderBytes + attention_workspace_bytes(M, N, K) : kHeaderBytes;
         default: return 0;
     }
 }
@@ -423,6 +424,37 @@ nvfp4_status nvfp4_mx_quantize(const void *x, int xt, int64_t rows, int64_t K_in
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
+nvfp4_status nvfp4_decode_attention(const void *q, int qt, int64_t H, int64_t D, int64_t ldq,
+                                    const nvfp4_tensor *k_cache, const nvfp4_tensor *vt_cache, int64_t T,
+                                    int compensate, float *out, int64_t ldo, void *ws, size_t ws_bytes,
+                                    void *stream) {
+    if (qt != NVFP4_BF16 && qt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
+    if (H < 0 || D < 32 || D > 256 || D % 32 || T <= 0 || T % 16) return NVFP4_ERR_SHAPE;
+    if (compensate != 0 && compensate != 1) return NVFP4_ERR_SHAPE;
+    CHECK(check_tensor(k_cache, H * T, D));
+    CHECK(check_tensor(vt_cache, H * D, T));
+    if (H == 0) return NVFP4_OK;
+    if (!q || !out) return NVFP4_ERR_NULL;
+    if (ldq < D || ldo < D) return NVFP4_ERR_SHAPE;
+    if (!aligned(q, 16) || (ldq * elem_size(qt)) % 16 || !aligned(out, 4)) return NVFP4_ERR_ALIGN;
+    const size_t need = kHeaderBytes + attention_workspace_bytes(H, D, T);
+    if (!ws || ws_bytes < need) return NVFP4_ERR_WORKSPACE;
+    AttentionLaunch g;
+    g.q = q; g.qt = qt == NVFP4_BF16 ? IN_BF16 : IN_F32; g.ldq = ldq;
+    g.H = H; g.D = D; g.T = T;
+    g.k_codes = k_cache->codes; g.k_ldc = k_cache->ld_codes;
+    g.k_scales = k_cache->scales; g.k_lds = k_cache->ld_scales; g.k_S = k_cache->tensor_scale;
+    g.v_codes = vt_cache->codes; g.v_ldc = vt_cache->ld_codes;
+    g.v_scales = vt_cache->scales; g.v_lds = vt_cache->ld_scales; g.v_S = vt_cache->tensor_scale;
+    g.compensate = compensate;
+    g.out = out; g.ldo = ldo;
+    // after the counter header, which this operation leaves untouched
+    g.scratch = static_cast<uint8_t *>(ws) + kHeaderBytes;
+    g.scratch_bytes = ws_bytes - kHeaderBytes;
+    const hipError_t e = launch_attention(g, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, int64_t residue_cols,
                            void *y, int yt, int64_t ldy, void *ws, size_t ws_bytes, void *stream) {
     if (!a || !w) return NVFP4_ERR_NULL;
@@ -508,7 +540,7 @@ const char *nvfp4_status_string(nvfp4_status s) {
 }
 
 const char *nvfp4_last_error(void) { return g_last_error; }
-int nvfp4_version(void) { return 10100; }
+int nvfp4_version(void) { return 10200; }
 
 int nvfp4_host_e4m3_encode(float v) { return (int)e4m3_rne_sat(v); }
 int nvfp4_host_e2m1_encode(float q) { return (int)(e2m1_rne_sat(std::fabs(q)) | ((f2u(q) >> 31) << 3)); }

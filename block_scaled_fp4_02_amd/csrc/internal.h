@@ -125,4 +125,22 @@ struct MXGemmLaunch {
 size_t mx_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t S);
 hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st);
 
+// Decode attention over an NVFP4 KV cache with residue-compensated query and
+// probabilities: K cache [H*T, D], V cache transposed [H*D, T] (row-major).
+struct AttentionLaunch {
+    const void *q; int qt; int64_t ldq;     // [H][D] bf16 or f32
+    int64_t H, D, T;                        // D % 32 == 0, D <= 256, T % 16 == 0, T > 0
+    const uint8_t *k_codes; int64_t k_ldc;
+    const uint8_t *k_scales; int64_t k_lds;
+    const float *k_S;
+    const uint8_t *v_codes; int64_t v_ldc;
+    const uint8_t *v_scales; int64_t v_lds;
+    const float *v_S;
+    int compensate;
+    float *out; int64_t ldo;                // [H][D] FP32
+    void *scratch; size_t scratch_bytes;    // attention_workspace_bytes()
+};
+size_t attention_workspace_bytes(int64_t H, int64_t D, int64_t T);
+hipError_t launch_attention(const AttentionLaunch &g, hipStream_t st);
+
 }  // namespace nvfp4

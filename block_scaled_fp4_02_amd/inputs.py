@@ -122,3 +122,19 @@ def small_random(seed: int, rows: int, K: int, scale: float = 1.0, outlier_frac:
         cols = np.random.default_rng([0, 101, seed]).choice(K, max(1, int(round(outlier_frac * K))), replace=False)
         x[:, cols] *= np.float32(mult)
     return _bf16(x)
+
+
+# decode attention: 32 heads of dimension 128 over 4096 cached tokens (the
+# Llama-3.1-8B query geometry, one KV head per query head)
+ATTN_SHAPE = (32, 4096, 128)
+
+
+def attention(H: int, T: int, D: int, sub: int = 0):
+    """Decode attention inputs (config 6 streams): q [H x D], K [H*T x D] (row h*T + t)
+    and V transposed, Vt [H*D x T] (row h*D + j), all N(0, 1) in bf16; the query has
+    1% outlier channels x 50 like the other activations."""
+    q = activations(6, sub, H, D, 0.01, 50.0)
+    k = _bf16(_rng(6, sub, T_W).standard_normal((H * T, D), dtype=np.float32))
+    v = _rng(6, sub, T_XCAL).standard_normal((H, T, D), dtype=np.float32)
+    vt = _bf16(np.ascontiguousarray(v.transpose(0, 2, 1)).reshape(H * D, T))
+    return q, k, vt

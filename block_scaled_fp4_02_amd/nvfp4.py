@@ -45,7 +45,7 @@ _lib = None
 _lock = threading.Lock()
 
 EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_mx_quantize",
-           "nvfp4_mx_gemm", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
+           "nvfp4_mx_gemm", "nvfp4_decode_attention", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
            "nvfp4_perm_from_absmax", "nvfp4_workspace_size", "nvfp4_status_string",
            "nvfp4_last_error", "nvfp4_version", "nvfp4_host_e4m3_encode", "nvfp4_host_e2m1_encode"]
 
@@ -66,6 +66,8 @@ def lib():
             L.nvfp4_pack_tiled.argtypes = [vp, vp, vp]
             L.nvfp4_mx_quantize.argtypes = [vp, C.c_int, i64, i64, i64, i64, vp, vp]
             L.nvfp4_mx_gemm.argtypes = [vp, vp, i64, vp, C.c_int, i64, vp, sz, vp]
+            L.nvfp4_decode_attention.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, i64, C.c_int, vp, i64,
+                                                 vp, sz, vp]
             L.nvfp4_channel_absmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, C.c_float, vp, vp, sz, vp]
             L.nvfp4_perm_from_absmax.argtypes = [vp, i64, vp]
             L.nvfp4_workspace_size.argtypes = [C.c_int, i64, i64, i64, i64]
@@ -76,7 +78,7 @@ def lib():
             L.nvfp4_host_e4m3_encode.argtypes = [C.c_float]
             L.nvfp4_host_e2m1_encode.argtypes = [C.c_float]
             for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_pack_tiled",
-                         "nvfp4_mx_quantize", "nvfp4_mx_gemm",
+                         "nvfp4_mx_quantize", "nvfp4_mx_gemm", "nvfp4_decode_attention",
                          "nvfp4_channel_absmax", "nvfp4_perm_from_absmax"):
                 getattr(L, name).restype = C.c_int
             _lib = L
@@ -382,3 +384,20 @@ def mx_gemm(a: MXTensor, w: MXTensor, residue_cols: int = 0, out_dtype=torch.flo
            "nvfp4_mx_gemm")
     return out
 
+
+def decode_attention(q: torch.Tensor, k_cache: NVFP4Tensor, vt_cache: NVFP4Tensor, T: int,
+                     compensate: bool = True, out: torch.Tensor | None = None) -> torch.Tensor:
+    """nvfp4_decode_attention: q [H, D] (bf16/f32); k_cache NVFP4 [H*T, D]; vt_cache NVFP4
+    [H*D, T] (V transposed); returns o [H, D] FP32. compensate adds the residue columns of
+    the query and of the probabilities."""
+    assert q.dim() == 2 and q.stride(1) == 1
+    H, D = q.shape
+    if out is None:
+        out = torch.empty((H, D), dtype=torch.float32, device=q.device)
+    n = lib().nvfp4_workspace_size(5, H, D, T, 0)
+    ws = workspace(n, q.device)
+    kc, vc = k_cache.c(), vt_cache.c()
+    _check(lib().nvfp4_decode_attention(_ptr(q), _dtype_code(q), H, D, q.stride(0), C.byref(kc), C.byref(vc),
+                                        int(T), 1 if compensate else 0, _ptr(out), out.stride(0), _ptr(ws),
+                                        ws.numel(), _stream()), "nvfp4_decode_attention")
+    return out

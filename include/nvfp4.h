@@ -222,6 +222,31 @@ nvfp4_status nvfp4_mx_quantize(const void *x, int xt, int64_t rows, int64_t K_in
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, int64_t residue_cols,
                            void *y, int yt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
+/* Decode attention over an NVFP4 KV cache with residue compensation of its
+ * activation operands (ResServe abstract: the FP4 base plus FP4-quantized
+ * residue of the linear layers, applied to decode attention). The pages give no
+ * attention formula; the reading is scaled dot-product attention of one decode
+ * query per head, the cache stored like a weight and the two activation operands
+ * of the step -- the query and the probabilities -- carrying residue columns as
+ * in nvfp4_gemm_residue:
+ *   s_h = ([Q(q_h) | Q(R(q_h))] . [K_h | K_h]^T) / sqrt(D)
+ *   p_h = softmax(s_h)        FP32: m = max s, e = exp(s - m), p = e / sum(e)
+ *   o_h = [Q(p_h) | Q(R(p_h))] . [Vt_h | Vt_h]^T
+ * q_h and p_h are each quantized as one tensor (own tensor scale); compensate = 0
+ * drops the residue columns (plain W4A4 attention).
+ *   q        H x D activations (dtype qt, leading dimension ldq), one row per head
+ *   k_cache  row-major NVFP4, H*T rows of D columns: row h*T + t is token t of head h
+ *   vt_cache row-major NVFP4, H*D rows of T columns: row h*D + j is dimension j of
+ *            head h over the tokens (V transposed, blocks of 16 along the tokens)
+ *   out      H x D FP32 (leading dimension ldo)
+ * 32 <= D <= 256 with D % 32 == 0, T > 0 with T % 16 == 0 (else NVFP4_ERR_SHAPE);
+ * H == 0 does nothing. Workspace: nvfp4_workspace_size(5, H, D, T, 0) bytes; its
+ * first 8 KiB (the NVFP4 counter header) are never written. */
+nvfp4_status nvfp4_decode_attention(const void *q, int qt, int64_t H, int64_t D, int64_t ldq,
+                                    const nvfp4_tensor *k_cache, const nvfp4_tensor *vt_cache, int64_t T,
+                                    int compensate, float *out, int64_t ldo, void *ws, size_t ws_bytes,
+                                    void *stream);
+
 /* Rewrite the row-major weight `src` into the tiled layout `dst` (same rows
  * and K; dst->ld_codes = KU*4096, dst->ld_scales = KU*512; its codes and
  * scales buffers hold ceil(rows/16) strips). The tensor scale is copied.
@@ -241,7 +266,8 @@ nvfp4_status nvfp4_channel_absmax(const void *x, int xt, int64_t rows, int64_t K
 nvfp4_status nvfp4_perm_from_absmax(const float *absmax_host, int64_t K, int32_t *perm_host);
 
 /* Bytes of workspace an operation needs: op 0 = quantize (M = rows), 1 = gemm,
- * 2 = gemm_residue, 3 = channel_absmax (M = rows), 4 = mx_gemm. S is the residue
+ * 2 = gemm_residue, 3 = channel_absmax (M = rows), 4 = mx_gemm, 5 = decode_attention
+ * (M = H, N = D, K = T). S is the residue
  * column count. */
 size_t nvfp4_workspace_size(int op, int64_t M, int64_t N, int64_t K, int64_t S);
 

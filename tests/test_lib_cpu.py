@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.nvfp4_version() == 10100
+    assert L.nvfp4_version() == 10200
     assert L.nvfp4_status_string(0) == b"ok"
     assert L.nvfp4_status_string(5) == b"workspace too small"
 
@@ -180,3 +180,32 @@ def test_noalloc_rejects_oversized_before_launch(L):
     assert b"static scratch" in L.nvfp4_last_error()
     # argument errors come first, as in nvfp4_gemm
     assert L.nvfp4_gemm_noalloc(None, None, 0, M, K, K, C.byref(w), fake, 1, N, None) == 1
+
+
+def test_decode_attention_argument_errors(L):
+    """nvfp4_decode_attention rejects bad sizes, dtypes, caches and workspaces before
+    anything is enqueued (fake, never dereferenced pointers)."""
+    vp = C.c_void_p
+    fake = vp(1 << 20)
+    H, D, T = 2, 64, 32
+    kc = _tensor(H * T, D, codes=1 << 20, scales=1 << 21, scale=1 << 22)
+    vt = _tensor(H * D, T, codes=1 << 23, scales=1 << 24, scale=1 << 25)
+    n = L.nvfp4_workspace_size(5, H, D, T, 0)
+    assert n > 8192
+    ws = fake
+
+    def call(q=fake, qt=0, h=H, d=D, ldq=D, k=kc, v=vt, t=T, comp=1, out=fake, ldo=D, wsn=n):
+        return L.nvfp4_decode_attention(q, qt, h, d, ldq, C.byref(k), C.byref(v), t, comp, out, ldo, ws, wsn, None)
+
+    assert call(qt=5) == 4                                        # dtype
+    assert call(d=48) == 2 and call(d=16) == 2 and call(d=288) == 2   # D % 32, 32 <= D <= 256
+    assert call(t=0) == 2 and call(t=24) == 2                     # T > 0, T % 16
+    assert call(comp=2) == 2
+    assert call(k=_tensor(H * T + 1, D, codes=1 << 20, scales=1 << 21, scale=1 << 22)) == 2
+    assert call(v=_tensor(H * D, T + 16, codes=1 << 23, scales=1 << 24, scale=1 << 25)) == 2
+    assert call(q=None) == 1 and call(out=None) == 1
+    assert call(ldq=32) == 2 and call(ldo=32) == 2
+    assert call(q=vp((1 << 20) + 2)) == 3
+    assert call(wsn=n - 1) == 5
+    assert call(h=0, k=_tensor(0, D, codes=1 << 20, scales=1 << 21, scale=1 << 22),
+                v=_tensor(0, T, codes=1 << 23, scales=1 << 24, scale=1 << 25)) == 0   # nothing to do
