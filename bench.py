@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--quantize-case", default="",
                     help="M,K: run only the activation quantizer on bf16 X [M x K], --reps launches "
                          "(for profiling the quantizer passes; prints one line with its time)")
+    ap.add_argument("--attention-case", type=int, default=-1,
+                    help="0/1: run only decode attention (32 heads x 4096 tokens x 128) without/with "
+                         "compensation on a ring of caches, --reps graph replays (for profiling)")
     ap.add_argument("--augmented-case", type=int, default=-1,
                     help="S: run only the M=64, K=4096, N=14336 augmented call (RMSNorm, channel reorder, "
                          "S residue columns, quantization in the call) on a weight ring, --reps graph replays "
@@ -178,6 +181,9 @@ def main():
         return
     if args.quantize_case:
         quantize_case(nvfp4, dev, [int(v) for v in args.quantize_case.split(",")], args.reps)
+        return
+    if args.attention_case >= 0:
+        attention_case(nvfp4, dev, bool(args.attention_case), args.reps)
         return
     if args.augmented_case >= 0:
         augmented_case(nvfp4, dev, args.layout == "tiled", args.augmented_case, args.reps)
@@ -432,7 +438,43 @@ def extra_detail(nvfp4, dev, tiled):
         del xall, wq, aq_cache
         torch.cuda.empty_cache()
     res.update(mx_detail(nvfp4, dev))
+    res.update(attention_detail(nvfp4, dev))
     return res
+
+
+def attention_bytes(H, T, D):
+    """Algorithmic bytes of one decode-attention call: both caches once (codes and
+    E4M3 scales), the bf16 query and the FP32 output."""
+    return 2 * (H * T * D // 2 + H * T * D // 16) + 2 * H * D + 4 * H * D
+
+
+def attention_ring(nvfp4, dev, H, T, D):
+    q, k, vt = inputs.attention(H, T, D)
+    kq, vq = nvfp4.quantize(k.to(dev)), nvfp4.quantize(vt.to(dev))
+    copies = max(2, -(-RING_BYTES // attention_bytes(H, T, D)))
+    return q.to(dev), [(kq, vq)] + [(kq.clone(), vq.clone()) for _ in range(copies - 1)]
+
+
+def attention_detail(nvfp4, dev):
+    """Decode attention over the NVFP4 KV cache (32 heads x 4096 tokens x 128), plain and
+    with residue compensation, on a ring of cache copies (kernels alone, HIP graph)."""
+    H, T, D = inputs.ATTN_SHAPE
+    qd, ring = attention_ring(nvfp4, dev, H, T, D)
+    out = torch.empty((H, D), dtype=torch.float32, device=dev)
+    rows, t_plain = [], None
+    for comp in (False, True):
+        def run():
+            for kq, vq in ring:
+                nvfp4.decode_attention(qd, kq, vq, T, compensate=comp, out=out)
+
+        t, _ = graph_time(run, 20, len(ring))
+        t_plain = t if not comp else t_plain
+        b = attention_bytes(H, T, D)
+        rows.append({"H": H, "T": T, "D": D, "compensate": comp, "us_call": round(t * 1e6, 3),
+                     "GBs": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "overhead_vs_plain": round(t / t_plain - 1, 4)})
+    del ring
+    return {"decode_attention": rows}
 
 
 def mx_detail(nvfp4, dev):
@@ -546,6 +588,23 @@ def quantize_case(nvfp4, dev, mk, reps):
     print(json.dumps({"quantize_case": [M, K], "reps": reps, "us_per_call": round(t * 1e6, 1),
                       "GBs": round(b / t / 1e9, 1), "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}),
           flush=True)
+
+
+def attention_case(nvfp4, dev, comp, reps):
+    """Decode attention alone on a ring of cache copies, `reps` graph replays."""
+    H, T, D = inputs.ATTN_SHAPE
+    qd, ring = attention_ring(nvfp4, dev, H, T, D)
+    out = torch.empty((H, D), dtype=torch.float32, device=dev)
+
+    def run():
+        for kq, vq in ring:
+            nvfp4.decode_attention(qd, kq, vq, T, compensate=comp, out=out)
+
+    t, _ = graph_time(run, reps, len(ring))
+    b = attention_bytes(H, T, D)
+    print(json.dumps({"attention_case": [H, T, D], "compensate": comp, "reps": reps, "calls_per_replay": len(ring),
+                      "us_per_call": round(t * 1e6, 2), "GBs": round(b / t / 1e9, 1),
+                      "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
 
 
 def augmented_case(nvfp4, dev, tiled, S, reps):

@@ -54,8 +54,7 @@ constexpr int kThreads = 64 * (kCons + kProd);
 constexpr int kPThreads = 64 * kProd;
 constexpr int kMaxItems = 8;                   // (tile, unit) items per consumer wave
 constexpr int kPreItems = 2;                   // items each consumer issues before the operand barrier
-constexpr size_t kTileCntOffset = 4096;        // header bytes before the tile counters
-constexpr int64_t kMaxTileCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
+constexpr int64_t kMaxTileCounters = kMaxCounters;
 constexpr int64_t kLocalMaxElems = 32768;      // LOCAL: X read by every workgroup
 constexpr int kLocalLoads = 4;                 // LOCAL: amax loads per lane and batch (K split over workgroups)
 constexpr int kLocalChunks = 4;                // LOCAL: raw 32-column chunks per producer thread

@@ -45,6 +45,8 @@ hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 // first call on a workspace; calls keep it valid (counts return to zero, all
 // slots advance to the same epoch), so it never needs clearing again.
 constexpr size_t kHeaderBytes = 8192;
+constexpr size_t kTileCntOffset = 4096;         // header bytes before the arrival counters
+constexpr int64_t kMaxCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
 constexpr size_t kSlotsOffset = 512;
 
 // Decode-shaped (M <= 64) product in one launch. With x != nullptr (bf16, and
@@ -138,6 +140,7 @@ struct AttentionLaunch {
     const float *v_S;
     int compensate;
     float *out; int64_t ldo;                // [H][D] FP32
+    unsigned *counters;                     // H <= kMaxCounters arrival counters in the zero-kept header
     void *scratch; size_t scratch_bytes;    // attention_workspace_bytes()
 };
 size_t attention_workspace_bytes(int64_t H, int64_t D, int64_t T);

@@ -239,9 +239,10 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, i
  *   vt_cache row-major NVFP4, H*D rows of T columns: row h*D + j is dimension j of
  *            head h over the tokens (V transposed, blocks of 16 along the tokens)
  *   out      H x D FP32 (leading dimension ldo)
- * 32 <= D <= 256 with D % 32 == 0, T > 0 with T % 16 == 0 (else NVFP4_ERR_SHAPE);
- * H == 0 does nothing. Workspace: nvfp4_workspace_size(5, H, D, T, 0) bytes; its
- * first 8 KiB (the NVFP4 counter header) are never written. */
+ * 32 <= D <= 256 with D % 32 == 0, T > 0 with T % 16 == 0, H <= 1024 (else
+ * NVFP4_ERR_SHAPE); H == 0 does nothing. Workspace: nvfp4_workspace_size(5, H, D, T, 0)
+ * bytes, the same zero-kept counter header as the products (H of its arrival
+ * counters are used and returned to zero), so it can be shared with them. */
 nvfp4_status nvfp4_decode_attention(const void *q, int qt, int64_t H, int64_t D, int64_t ldq,
                                     const nvfp4_tensor *k_cache, const nvfp4_tensor *vt_cache, int64_t T,
                                     int compensate, float *out, int64_t ldo, void *ws, size_t ws_bytes,
