@@ -296,9 +296,7 @@ hipError_t run_small(const MXDArgs &a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------ large M (tiles)
-// BM x BN = 256 x 256 output tiles on 4 waves, one per SIMD with the whole
-// register file (2 x 2 waves of 128 x 128: 8 x 8 MFMAs of 16 x 16 per
-// 128-column step, every fragment read from LDS feeding 8 of them).
+// BM x BN = 256 x 256 output tiles, 16 x 16 MFMAs over 128-column steps.
 // A step's codes and E8M0 bytes go from memory straight into LDS with gfx950's
 // direct-to-LDS loads (global_load_lds_dwordx4 / _ubyte: no staging registers,
 // no decode -- the matrix cores take them as stored): a row's 32-block b at
@@ -311,13 +309,11 @@ hipError_t run_small(const MXDArgs &a, hipStream_t st) {
 // LDS by the thread that loaded it (codes 0, scale 127). Residue columns are
 // further steps, as in the small-M kernel. Split-K writes FP32 partial tiles
 // for a combine in fixed order.
-constexpr int MX_BM = 256, MX_BN = 256, MX_NW = 4, MX_NT = 64 * MX_NW;
+constexpr int MX_BM = 256, MX_BN = 256;
 constexpr int MX_ACODE = MX_BM * 64, MX_BCODE = MX_BN * 64;          // bytes per stage
 constexpr int MX_ASC = MX_BM * 4 * 4, MX_BSC = MX_BN * 4 * 4;        // a dword per scale byte
 constexpr int MX_STAGE = MX_ACODE + MX_BCODE + MX_ASC + MX_BSC;       // 40 KiB
 constexpr int MX_GROUP_M = 8;                                         // row tiles per group of the tile order
-constexpr int MX_CH = MX_BM * 4 / MX_NT;                              // chunks per thread and operand (4)
-constexpr int MX_LOADS = 4 * MX_CH;                                   // direct-to-LDS loads per thread and step
 
 struct MXTArgs {
     const uint8_t *a_codes; int64_t a_ldc;
@@ -331,15 +327,22 @@ struct MXTArgs {
     float *part;                               // split-K partials [P][M][N], or nullptr
 };
 
-__global__ __launch_bounds__(MX_NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mx_tile_kernel(MXTArgs a) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_mx[];   // [3][MX_STAGE]
+// 8 waves, two per SIMD (2 along M x 4 along N, 128 x 64 each, 128 accumulator
+// registers): one wave's LDS reads and waits run under the other's MFMAs (a probe
+// of back-to-back scaled FP4 MFMAs: 7.6 PF with one wave per SIMD, 8.9 PF with
+// two). Per step a wave reads its 12 rows' chunks and scale bytes and issues 32
+// MFMAs. (Four waves of 128 x 128, one per SIMD, with the fragments double-
+// buffered in registers and the next step's reads placed between the MFMAs:
+// 10% slower at prefill sizes.)
+constexpr int MX8_NW = 8, MX8_NT = 64 * MX8_NW;
+constexpr int MX8_CH = MX_BM * 4 / MX8_NT;                            // chunks per thread and operand (2)
+constexpr int MX8_LOADS = 4 * MX8_CH;
+
+__global__ __launch_bounds__(MX8_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mx_tile8_kernel(MXTArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_m8[];   // [3][MX_STAGE]
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, g = lane >> 4;
-    // Tile order. Workgroups are dealt to the 8 XCDs round robin; renumber them so
-    // each XCD takes a contiguous range, and walk that range in groups of
-    // MX_GROUP_M row tiles sweeping the columns together: the tiles resident on
-    // one XCD then share activation and weight panels in its L2.
+    const int wm = wave >> 2, wn = wave & 3, r16 = lane & 15, g = lane >> 4;
     const int nblk = a.tiles_m * a.tiles_n;
     int bid = blockIdx.x;
     if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
@@ -350,39 +353,27 @@ void mx_tile_kernel(MXTArgs a) {
     const int64_t kmain = (a.K + 127) / 128, kall = kmain + (a.res + 127) / 128;
     const int64_t s0 = (int64_t)blockIdx.y * a.kchunk;
     const int64_t ksteps = (s0 + a.kchunk < kall ? s0 + a.kchunk : kall) - s0;
-    // Row r's four 32-blocks of a step sit in LDS in the order p = block ^ f(r),
-    // f(r) = ((r >> 1) ^ (r >> 2)) & 3: a fragment read (16 rows x one block per
-    // 16 lanes) then spreads over every bank group, with 32 or with 64 banks.
-    // Chunk c of a stage is row c / 4, position c % 4; this thread fetches the
-    // block that belongs at its position (every chunk: the row's low bits are
-    // those of tid / 4).
+    // chunk i of this thread: c = MX8_NT i + tid, row c / 4, position c % 4 (the
+    // row's low four bits are those of tid / 4 for every i)
     const int q4 = (lane & 3) ^ (((lane >> 3) ^ (lane >> 4)) & 3);
-    const int gp = g ^ (((r16 >> 1) ^ (r16 >> 2)) & 3);   // position of block g in this lane's rows
-
-    // chunk i of this thread: c = 256 i + 64 wave + lane, row c / 4 of the tile;
-    // byte offsets of this thread's rows from the tile's first row (rows past the
-    // matrix repeat its last row); 32 bits hold them (launcher-checked)
+    const int gp = g ^ (((r16 >> 1) ^ (r16 >> 2)) & 3);
     const uint8_t *abase = a.a_codes + m0 * a.a_ldc, *wbase = a.w_codes + n0 * a.w_ldc;
     const uint8_t *asbase = a.a_scales + m0 * a.a_lds, *wsbase = a.w_scales + n0 * a.w_lds;
-    uint32_t ra[MX_CH], rb[MX_CH], rsa[MX_CH], rsb[MX_CH];
+    uint32_t ra[MX8_CH], rb[MX8_CH], rsa[MX8_CH], rsb[MX8_CH];
 #pragma unroll
-    for (int i = 0; i < MX_CH; ++i) {
-        const int row = (MX_NT * i + tid) >> 2;
+    for (int i = 0; i < MX8_CH; ++i) {
+        const int row = (MX8_NT * i + tid) >> 2;
         const int64_t ma = m0 + row, nb = n0 + row;
         const int64_t la = (ma < a.M ? ma : a.M - 1) - m0, lb = (nb < a.N ? nb : a.N - 1) - n0;
         ra[i] = (uint32_t)(la * a.a_ldc); rsa[i] = (uint32_t)(la * a.a_lds);
         rb[i] = (uint32_t)(lb * a.w_ldc); rsb[i] = (uint32_t)(lb * a.w_lds);
     }
-    // step s of this range: weight columns kw.. and activation columns ka.. ; whether
-    // this thread's 32-block of the step holds data
     auto cols = [&](int64_t s, int64_t &kw, int64_t &ka, bool &ok) {
         const bool main = s0 + s < kmain;
         kw = (main ? s0 + s : s0 + s - kmain) * 128;
         ka = main ? kw : a.K + kw;
         ok = kw + 32 * q4 < (main ? a.K : a.res);
     };
-    // the MX_LOADS direct-to-LDS loads of step s into stage st (each wave writes
-    // 1 KiB of codes or 64 scale bytes per instruction, lane l at base + 16 l / l)
     auto dma = [&](int64_t s, uint8_t *st) {
         int64_t kw, ka;
         bool ok;
@@ -391,24 +382,23 @@ void mx_tile_kernel(MXTArgs a) {
         const uint32_t bw = ok ? (uint32_t)(kw / 32 + q4) : 0u, ba = ok ? (uint32_t)(ka / 32 + q4) : 0u;
         const uint32_t sbase = lds_addr_of(st);
 #pragma unroll
-        for (int i = 0; i < MX_CH; ++i) {
-            const uint32_t cbase = (uint32_t)(MX_NT * i + 64 * wave);  // first chunk of this wave's instruction
+        for (int i = 0; i < MX8_CH; ++i) {
+            const uint32_t cbase = (uint32_t)(MX8_NT * i + 64 * wave);
             dma16s(abase, ra[i] + ca, sbase + 16 * cbase);
             dma16s(wbase, rb[i] + cw, sbase + MX_ACODE + 16 * cbase);
             dma1s(asbase, rsa[i] + ba, sbase + MX_ACODE + MX_BCODE + 4 * cbase);
             dma1s(wsbase, rsb[i] + bw, sbase + MX_ACODE + MX_BCODE + MX_ASC + 4 * cbase);
         }
     };
-    // after this thread's loads of step s have landed: blocks past the data become
-    // zero codes with a unit scale (the loads read the row's first bytes instead)
+    // chunks past the data become zero codes with a unit scale (127)
     auto fixup = [&](int64_t s, uint8_t *st) {
         int64_t kw, ka;
         bool ok;
         cols(s, kw, ka, ok);
         if (ok) return;
 #pragma unroll
-        for (int i = 0; i < MX_CH; ++i) {
-            const int c = MX_NT * i + tid;
+        for (int i = 0; i < MX8_CH; ++i) {
+            const int c = MX8_NT * i + tid;
             *reinterpret_cast<uint4 *>(st + 16 * c) = make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(st + MX_ACODE + 16 * c) = make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint32_t *>(st + MX_ACODE + MX_BCODE + 4 * c) = 127u;
@@ -416,97 +406,67 @@ void mx_tile_kernel(MXTArgs a) {
         }
     };
 
-    float4v acc[8][8];
+    float4v acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = float4v{0, 0, 0, 0};
-
-    // Software pipeline inside the wave (one wave per SIMD, so nothing else hides
-    // its waits): step s's 64 MFMAs run from fragment registers F[s % 2] while the
-    // 32 LDS reads of step s + 1's fragments into F[(s + 1) % 2] are interleaved
-    // between them; then step s + 3's loads go out into the stage step s left,
-    // step s + 2's are waited for, patched and published at the barrier.
-    // At the top of step s: stage s + 1 is published, step s + 2's loads are in flight.
-    struct Frags { v8i a[8], b[8]; int sa[8], sb[8]; };
-    Frags F0, F1;
-    auto stage = [&](int64_t s) { return lds_mx + (int)(s % 3) * MX_STAGE; };
-    auto frag_read = [&](const uint8_t *cur, Frags &F, int r) {      // read r of 32
-        const bool isb = r < 16, sc = (r & 1) != 0;
-        const int idx = (r & 15) >> 1;
-        const int row = (isb ? wn : wm) * 128 + 16 * idx + r16;
-        const uint8_t *base = cur + (isb ? MX_ACODE : 0);
-        if (!sc) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(base + row * 64 + 16 * gp);
-            (isb ? F.b[idx] : F.a[idx]) = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        } else {
-            const int v = cur[MX_ACODE + MX_BCODE + (isb ? MX_ASC : 0) + 4 * (row * 4 + gp)];
-            (isb ? F.sb[idx] : F.sa[idx]) = v;
+        for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0, 0, 0, 0};
+    auto stage = [&](int64_t s) { return lds_m8 + (int)(s % 3) * MX_STAGE; };
+    auto compute = [&](const uint8_t *st) {
+        v8i fa[8], fb[4];
+        int sa[8], sb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = wn * 64 + 16 * j + r16;
+            const uint4 v = *reinterpret_cast<const uint4 *>(st + MX_ACODE + row * 64 + 16 * gp);
+            fb[j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            sb[j] = st[MX_ACODE + MX_BCODE + MX_ASC + 4 * (row * 4 + gp)];
         }
-    };
-    auto publish = [&](int64_t s, bool more) {       // step s's loads landed, patched, visible
-        if (more) DMA_WAIT_VM(MX_LOADS); else DMA_WAIT_VM(0);
-        fixup(s, stage(s));
-        DMA_WAIT_LGKM0();
-        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = wm * 128 + 16 * i + r16;
+            const uint4 v = *reinterpret_cast<const uint4 *>(st + row * 64 + 16 * gp);
+            fa[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+            sa[i] = st[MX_ACODE + MX_BCODE + 4 * (row * 4 + gp)];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb[j], acc[i][j], 4, 4, 0, sa[i],
+                                                                             0, sb[j]);
     };
 
     if (ksteps > 0) dma(0, stage(0));
     if (ksteps > 1) dma(1, stage(1));
     if (ksteps > 2) dma(2, stage(2));
     if (ksteps > 0) {
-        if (ksteps > 2) DMA_WAIT_VM(2 * MX_LOADS); else if (ksteps > 1) DMA_WAIT_VM(MX_LOADS); else DMA_WAIT_VM(0);
+        if (ksteps > 2) DMA_WAIT_VM(2 * MX8_LOADS); else if (ksteps > 1) DMA_WAIT_VM(MX8_LOADS); else DMA_WAIT_VM(0);
         fixup(0, stage(0));
         DMA_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
-#pragma unroll
-        for (int r = 0; r < 32; ++r) frag_read(stage(0), F0, r);
     }
-    if (ksteps > 1) publish(1, ksteps > 2);
-
-    auto step = [&](int64_t s, Frags &Fc, Frags &Fn) {
-        // unconditional, so that they can sit between the MFMAs; after the last step
-        // they read a stale (in-bounds) stage whose values are never used
-        const uint8_t *nst = stage(s + 1);
-#pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            const int i0 = (2 * q) >> 3, j0 = (2 * q) & 7, j1 = j0 + 1;
-            // An empty asm statement pins the order (the compiler would otherwise put
-            // the 64 MFMAs first and the reads after them): it takes the previous
-            // pair's last result and hands this pair its scale, and as a volatile
-            // statement it stays between the previous read and this one.
-            int sa = Fc.sa[i0];
-            if (q > 0) {
-                const int pi = (2 * q - 1) >> 3, pj = (2 * q - 1) & 7;
-                asm volatile("" : "+v"(sa) : "a"(acc[pi][pj]));
-            }
-            acc[i0][j0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Fc.a[i0], Fc.b[j0], acc[i0][j0], 4, 4, 0,
-                                                                           sa, 0, Fc.sb[j0]);
-            acc[i0][j1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Fc.a[i0], Fc.b[j1], acc[i0][j1], 4, 4, 0,
-                                                                           sa, 0, Fc.sb[j1]);
-            frag_read(nst, Fn, q);
+    for (int64_t s = 0; s < ksteps; ++s) {
+        compute(stage(s));
+        if (s + 1 < ksteps) {
+            // step s + 1's loads landed (step s + 2's may still be in flight), patched, visible;
+            // past this barrier no wave reads stage s any more
+            if (s + 2 < ksteps) DMA_WAIT_VM(MX8_LOADS); else DMA_WAIT_VM(0);
+            fixup(s + 1, stage(s + 1));
+            DMA_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();
+            if (s + 3 < ksteps) dma(s + 3, stage(s));
         }
-        DMA_WAIT_LGKM0();                               // this wave's reads of stage s + 1 are done
-        const bool more = s + 3 < ksteps;
-        if (more) dma(s + 3, stage(s));                // stage s was read during step s - 1
-        if (s + 2 < ksteps) publish(s + 2, more);
-    };
-    for (int64_t s = 0; s < ksteps; s += 2) {
-        step(s, F0, F1);
-        if (s + 1 < ksteps) step(s + 1, F1, F0);
     }
 
-    // epilogue: one fully unrolled store nest per output kind, so every
-    // accumulator index is a constant (a runtime loop here would keep the
-    // accumulators in memory instead of registers)
     float *part = a.part ? a.part + (int64_t)blockIdx.y * a.M * a.N : nullptr;
-    const int64_t mrow = m0 + wm * 128 + 4 * g, ncol = n0 + wn * 128 + r16;
+    const int64_t mrow = m0 + wm * 128 + 4 * g, ncol = n0 + wn * 64 + r16;
     auto store_all = [&](auto kind) {
         constexpr int KIND = decltype(kind)::value;   // 2: partial, 1: FP32, 0: BF16
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t m = mrow + 16 * i + e, n = ncol + 16 * j;
@@ -601,12 +561,12 @@ hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st) {
     const size_t lds = 3 * (size_t)MX_STAGE;
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mx_tile_kernel),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mx_tile8_kernel),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    mx_tile_kernel<<<dim3((unsigned)(t.tiles_m * t.tiles_n), (unsigned)P), MX_NT, lds, st>>>(t);
+    mx_tile8_kernel<<<dim3((unsigned)(t.tiles_m * t.tiles_n), (unsigned)P), MX8_NT, lds, st>>>(t);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || P == 1) return e;
     const int64_t total = g.M * g.N;
