@@ -429,7 +429,7 @@ nvfp4_status nvfp4_decode_attention(const void *q, int qt, int64_t H, int64_t D,
                                     int compensate, float *out, int64_t ldo, void *ws, size_t ws_bytes,
                                     void *stream) {
     if (qt != NVFP4_BF16 && qt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
-    if (H < 0 || H > kMaxCounters || D < 32 || D > 256 || D % 32 || T <= 0 || T % 16) return NVFP4_ERR_SHAPE;
+    if (H < 0 || H > 65535 || D < 32 || D > 256 || D % 32 || T <= 0 || T % 16) return NVFP4_ERR_SHAPE;
     if (compensate != 0 && compensate != 1) return NVFP4_ERR_SHAPE;
     CHECK(check_tensor(k_cache, H * T, D));
     CHECK(check_tensor(vt_cache, H * D, T));
@@ -448,9 +448,7 @@ nvfp4_status nvfp4_decode_attention(const void *q, int qt, int64_t H, int64_t D,
     g.v_scales = vt_cache->scales; g.v_lds = vt_cache->ld_scales; g.v_S = vt_cache->tensor_scale;
     g.compensate = compensate;
     g.out = out; g.ldo = ldo;
-    // one arrival counter per head in the header (returned to zero by each call);
-    // the rest after the header
-    g.counters = reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ws) + kTileCntOffset);
+    // scores and statistics after the header, which this call leaves untouched
     g.scratch = static_cast<uint8_t *>(ws) + kHeaderBytes;
     g.scratch_bytes = ws_bytes - kHeaderBytes;
     const hipError_t e = launch_attention(g, static_cast<hipStream_t>(stream));

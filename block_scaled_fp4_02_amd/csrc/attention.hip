@@ -14,21 +14,31 @@
 // The residue columns meet the cache's own columns again, so the cache is read
 // once and the two terms are added in registers ("combined on-chip").
 //
+// The residue columns meet the cache's own columns again, so each cache element
+// is read once and multiplies the sum of the base and residue values of its
+// operand element: (e_q d_q + e_r d_r) e_k d_k, the augmented product written
+// per element ("combined on-chip").
+//
 // The step is HBM-bound (one query per head: nothing to share between tokens
-// but the query), so it runs on the vector units with exact products
-// (e(c) d from the hardware convert, times the E4M3 value) and FP32 sums:
-//   attn_scores_kernel  (chunk of 256 tokens, head): quantizes q_h (+ residue),
-//                       D / 32 lanes per token stream its K row (a slice each,
-//                       the query's slice in registers), and it writes s plus
-//                       the chunk's (max, sum of exp);
-//   attn_pv_kernel      (chunk, head): folds the chunks' statistics into the
-//                       head's (m, l), quantizes its 256 probabilities (+ residue)
-//                       into LDS, one output dimension per thread streams its
-//                       Vt row segment and stores an unscaled partial o; the last
-//                       workgroup of the head (a counter in the workspace header)
-//                       adds the partials in chunk order and applies S_p S_V.
-// Every thread issues all of its loads before it uses any (a loop with a load per
-// step waited for each round trip in turn: 8.5 and 14.3 us per kernel).
+// but the query), so it runs on the vector units: e(c) from the hardware
+// convert, products accumulated by FMA per 16-block and scaled once by the
+// block's E4M3 value. Two launches; the softmax needs the head's max and sum
+// before any probability can be quantized (its tensor scale is 1 / sum):
+//   attn_scores_kernel  (64 tokens, head), one wave: quantizes q_h (+ residue),
+//                       D / 32 lanes per token stream its K row (a 16-byte slice
+//                       each, the query's slice in registers), writes s and the
+//                       wave's (max, sum of exp(s - max)). No barrier but the one
+//                       that hands the quantized query across the wave.
+//   attn_pv_kernel      (16 output dimensions, head): every workgroup folds the
+//                       head's statistics (the same fixed order everywhere),
+//                       quantizes the head's probabilities (+ residue) into LDS,
+//                       one block of 16 per thread, and streams its 16 Vt rows
+//                       (a wave reads 1 KiB of one row per load); the slices'
+//                       sums meet by cross-lane adds. The workgroup covers all
+//                       tokens, so no partial outputs cross workgroups.
+// Every thread issues its loads in the order their data is used, all before the
+// first use: loads return in order, so waiting for the first does not wait for
+// the cache stream behind it.
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -37,15 +47,9 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kAT = 256;                       // threads per workgroup = tokens per chunk
-
-template <typename T>
-__device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-template <typename T>
-__device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-template <typename T>
-__device__ inline T add_dev(T *p, T v) { return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ inline void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+constexpr int kPR = 16;                        // Vt rows (output dimensions) per PV workgroup
+constexpr int kPT = 256;                       // PV threads: 2 x 128 slices of 32 tokens
+constexpr int kTT = 4096;                      // tokens per LDS tile of probabilities
 
 struct AArgs {
     const void *q; int qt; int64_t ldq;
@@ -58,11 +62,9 @@ struct AArgs {
     const float *v_S;
     int comp;
     float *scores;                             // [H][T]
-    float *stats;                              // [H][NC][2]: chunk max, chunk sum of exp(s - max)
-    float *partial;                            // [H][NC][D]
+    float *stats;                              // [H][NW][2]: a wave's max and sum of exp(s - max)
     float *out; int64_t ldo;
-    unsigned *cnt;                             // [H] arrival counters (workspace header), zero-kept
-    int NC;
+    int NW;                                    // waves (64 tokens each) per head
 };
 
 __device__ inline float warp_max(float v) {
@@ -87,115 +89,127 @@ __device__ inline void decode8_f32(uint32_t w, float d, float *o) {
     o[4] = e2[0] * d; o[5] = e2[1] * d; o[6] = e3[0] * d; o[7] = e3[1] * d;
 }
 
-// Quantize the 16 values of one block against S (and its residue when comp)
-// and leave e(c) d (without S) of the base and of the residue in b[16], r[16].
-__device__ inline void quant_block(const float *v, float S, bool comp, float *b, float *r) {
+// acc + sum of x[i] e(c_i) over the 8 codes of one dword, by FMA.
+__device__ inline float dot8(uint32_t w, const float *x, float acc) {
+    typedef float float2v __attribute__((ext_vector_type(2)));
+    const float2v e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const float2v e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const float2v e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const float2v e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    acc = __builtin_fmaf(x[0], e0[0], acc); acc = __builtin_fmaf(x[1], e0[1], acc);
+    acc = __builtin_fmaf(x[2], e1[0], acc); acc = __builtin_fmaf(x[3], e1[1], acc);
+    acc = __builtin_fmaf(x[4], e2[0], acc); acc = __builtin_fmaf(x[5], e2[1], acc);
+    acc = __builtin_fmaf(x[6], e3[0], acc); acc = __builtin_fmaf(x[7], e3[1], acc);
+    return acc;
+}
+
+// sum of x[i] e(c_i) d over 32 codes (16 bytes) and their two E4M3 bytes.
+__device__ inline float dot32(const uint4 c, uint32_t s2, const float *x) {
+    const float d0 = e4m3_to_float(s2 & 0xFFu), d1 = e4m3_to_float((s2 >> 8) & 0xFFu);
+    const float a0 = dot8(c.y, x + 8, dot8(c.x, x, 0.0f));
+    const float a1 = dot8(c.w, x + 24, dot8(c.z, x + 16, 0.0f));
+    return a0 * d0 + a1 * d1;
+}
+
+// Quantize the 16 values of one block against S (and its residue when comp) and
+// leave, per element, e(c) d + e(c_r) d_r (without S): the base plus the residue.
+__device__ inline void quant_block_aug(const float *v, float S, bool comp, float *o) {
     uint32_t cw[2];
     float d;
     encode_block(v, S, 6.0f * S, cw, d);
-    decode8_f32(cw[0], d, b);
-    decode8_f32(cw[1], d, b + 8);
-    if (!comp) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) r[i] = 0.0f;
-        return;
-    }
+    decode8_f32(cw[0], d, o);
+    decode8_f32(cw[1], d, o + 8);
+    if (!comp) return;
     float res[16];
     block_residue(v, cw, d, S, res);
     uint32_t rw[2];
-    float dr;
+    float dr, r[16];
     encode_block(res, S, 6.0f * S, rw, dr);
     decode8_f32(rw[0], dr, r);
     decode8_f32(rw[1], dr, r + 8);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = o[i] + r[i];
 }
 
-// 32 codes (16 bytes) and their two E4M3 bytes: e(c) d of the 32 values, by pairs.
-__device__ inline void decode32(const uint4 c, uint32_t s2, float *o) {
-    const float d0 = e4m3_to_float(s2 & 0xFFu), d1 = e4m3_to_float((s2 >> 8) & 0xFFu);
-    decode8_f32(c.x, d0, o);
-    decode8_f32(c.y, d0, o + 8);
-    decode8_f32(c.z, d1, o + 16);
-    decode8_f32(c.w, d1, o + 24);
-}
-
-// LPT lanes per token (D / 32 rounded up to a power of two): lane group g holds
-// the query's dimensions 32 g .. 32 g + 31 (base and residue, in registers) and
-// loads that 16-byte slice of its token's K row, so LPT lanes read a row and a
-// wave reads 64 / LPT rows (1 KiB at D = 128) per load; the partial dot products
-// meet by cross-lane adds.
+// One wave per 64 tokens of a head. LPT lanes per token (D / 32 rounded up to a
+// power of two): lane group g holds the query's dimensions 32 g .. 32 g + 31 and
+// loads that 16-byte slice of its token's K row, so a wave reads 64 / LPT rows
+// (1 KiB at D = 128) per load; the partial dot products meet by cross-lane adds.
 template <int XT, int LPT>
-__global__ __launch_bounds__(kAT) void attn_scores_kernel(AArgs a) {
-    __shared__ __attribute__((aligned(16))) float qb[256], qr[256];
-    __shared__ float red[kAT / 64];
-    const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t h = blockIdx.y;
+__global__ __launch_bounds__(64) void attn_scores_kernel(AArgs a) {
+    __shared__ __attribute__((aligned(16))) float qa[256];
+    const int lane = threadIdx.x;
+    const int64_t w = blockIdx.x, h = blockIdx.y;
     const int D = (int)a.D, nb = D / 16;
-    constexpr int TPW = 64 / LPT;                // tokens per wave and load
+    constexpr int TPW = 64 / LPT;                // tokens per load
     const int g = lane % LPT, tl = lane / LPT;
     const bool gv = 32 * g < D;
-    // this lane's K slices of its LPT tokens, all loads first
+    // the query block of lane b < nb first (used first; lanes past nb load block 0
+    // and drop it), then the K slices
+    // (raw words here, converted after the K loads are out)
+    uint4 qw[XT == IN_BF16 ? 2 : 4];
+    {
+        const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.q) +
+                                                          (h * a.ldq + 16 * (lane < nb ? lane : 0)) *
+                                                              (XT == IN_BF16 ? 2 : 4));
+#pragma unroll
+        for (int i = 0; i < (XT == IN_BF16 ? 2 : 4); ++i) qw[i] = qp[i];
+    }
+    const float kS = a.k_S[0];
+    asm volatile("" ::: "memory");
     uint4 cw[LPT];
     uint32_t s2[LPT];
     int64_t tok[LPT];
 #pragma unroll
     for (int it = 0; it < LPT; ++it) {
-        tok[it] = (int64_t)c * kAT + 64 * wave + TPW * it + tl;
+        tok[it] = 64 * w + TPW * it + tl;
         const bool ok = gv && tok[it] < a.T;
         const int64_t row = h * a.T + (ok ? tok[it] : 0);
         cw[it] = *reinterpret_cast<const uint4 *>(a.k_codes + row * a.k_ldc + (ok ? 16 * g : 0));
         s2[it] = *reinterpret_cast<const uint16_t *>(a.k_scales + row * a.k_lds + (ok ? 2 * g : 0));
     }
-    // q_h and its residue, quantized as one tensor of D values: lane b < nb of wave 0
-    // owns block b
-    if (wave == 0) {
-        float v[16];
-        float m = 0.0f;
-        if (lane < nb) {
+    __builtin_amdgcn_sched_barrier(0);         // every K load is out before q is used
+    // q_h quantized as one tensor of D values (its residue against the same S)
+    float v[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int64_t off = h * a.ldq + 16 * lane + i;
-                v[i] = XT == IN_BF16 ? u2f((uint32_t)static_cast<const uint16_t *>(a.q)[off] << 16)
-                                     : static_cast<const float *>(a.q)[off];
-                m = fmaxf(m, fabsf(v[i]));
-            }
+    for (int i = 0; i < 8; ++i) {
+        if (XT == IN_BF16) {
+            const uint32_t wd = (&qw[i / 4].x)[i % 4];
+            v[2 * i] = u2f(wd << 16);
+            v[2 * i + 1] = u2f(wd & 0xFFFF0000u);
+        } else {
+            v[2 * i] = u2f((&qw[i / 2].x)[2 * (i % 2)]);
+            v[2 * i + 1] = u2f((&qw[i / 2].x)[2 * (i % 2) + 1]);
         }
-        m = warp_max(m);
-        const float S = m > 0.0f ? m / 2688.0f : 1.0f;
-        if (lane < nb) {
-            float b[16], r[16];
-            quant_block(v, S, a.comp != 0, b, r);
+    }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                qb[16 * lane + i] = b[i];
-                qr[16 * lane + i] = r[i];
-            }
-        }
-        if (lane == 0) red[0] = S;
+    for (int i = 0; i < 16; ++i) v[i] = lane < nb ? v[i] : 0.0f;
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = warp_max(am);
+    const float S = am > 0.0f ? am / 2688.0f : 1.0f;
+    if (lane < nb) {
+        float o[16];
+        quant_block_aug(v, S, a.comp != 0, o);
+#pragma unroll
+        for (int i = 0; i < 16; i += 4)
+            *reinterpret_cast<float4 *>(qa + 16 * lane + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
     }
     __syncthreads();
-    const float scale = red[0] * a.k_S[0];
-    const float inv = 1.0f / sqrtf((float)D);
-    float q_b[32], q_r[32];
+    float x[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        q_b[i] = gv ? qb[32 * g + i] : 0.0f;
-        q_r[i] = gv ? qr[32 * g + i] : 0.0f;
+    for (int i = 0; i < 32; i += 4) {
+        const float4 t = gv ? *reinterpret_cast<const float4 *>(qa + 32 * g + i) : make_float4(0, 0, 0, 0);
+        x[i] = t.x; x[i + 1] = t.y; x[i + 2] = t.z; x[i + 3] = t.w;
     }
-    __syncthreads();                           // red[] is reused below
-
+    const float scale = S * kS;
+    const float inv = 1.0f / sqrtf((float)D);
     float mx = -INFINITY;
     float sv[LPT];
 #pragma unroll
     for (int it = 0; it < LPT; ++it) {
-        float kd[32];
-        decode32(cw[it], s2[it], kd);
-        float sb = 0.0f, sr = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            sb += q_b[j] * kd[j];
-            sr += q_r[j] * kd[j];
-        }
-        float sum = sb + sr;
+        float sum = dot32(cw[it], s2[it], x);
 #pragma unroll
         for (int o = 1; o < LPT; o <<= 1) sum += __shfl_xor(sum, o);
         const float sc = (sum * scale) * inv;
@@ -204,146 +218,167 @@ __global__ __launch_bounds__(kAT) void attn_scores_kernel(AArgs a) {
         sv[it] = ok ? sc : -INFINITY;
         mx = fmaxf(mx, sv[it]);
     }
-    // the chunk's max and sum of exp(s - max) (every lane of a token holds its score)
+    // the wave's max and sum of exp(s - max) (every lane of a token holds its score)
     mx = warp_max(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
     float e = 0.0f;
     if (g == 0) {
 #pragma unroll
-        for (int it = 0; it < LPT; ++it) e += tok[it] < a.T ? expf(sv[it] - m) : 0.0f;
+        for (int it = 0; it < LPT; ++it) e += tok[it] < a.T ? expf(sv[it] - mx) : 0.0f;
     }
     e = warp_sum(e);
-    if (lane == 0) red[wave] = e;
-    __syncthreads();
-    if (tid == 0) {
-        float *st = a.stats + (h * a.NC + c) * 2;
-        st[0] = m;
-        st[1] = (red[0] + red[1]) + (red[2] + red[3]);
-    }
+    if (lane == 0) *reinterpret_cast<float2 *>(a.stats + (h * a.NW + w) * 2) = make_float2(mx, e);
 }
 
-__global__ __launch_bounds__(kAT) void attn_pv_kernel(AArgs a) {
-    __shared__ float pb[kAT], pr[kAT], pv[kAT], sh[2];
-    __shared__ int sh_last;
-    const int c = blockIdx.x, tid = threadIdx.x;
+// One workgroup per 16 output dimensions of a head, over all of its tokens.
+// Thread t takes slice t % 128 (32 tokens) of rows 8 (t / 128) .. + 7 per tile of
+// 4096 tokens, so the lanes of a wave read 64 consecutive 16-byte slices of one
+// row per load; and block t of the tile's probabilities for the quantization.
+__global__ __launch_bounds__(kPT) void attn_pv_kernel(AArgs a) {
+    __shared__ __attribute__((aligned(16))) float pa[kTT];
+    __shared__ float red[kPT / 64][8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t h = blockIdx.y;
-    const int64_t t0 = (int64_t)c * kAT;
-    const int nt = (int)(a.T - t0 < kAT ? a.T - t0 : kAT);   // a multiple of 16
-    // this thread's Vt row segment (dimension tid of head h), all loads first
-    constexpr int NG = kAT / 32;
-    const bool has_row = tid < a.D;
-    const int64_t row = h * a.D + (has_row ? tid : 0);
-    const uint8_t *cp = a.v_codes + row * a.v_ldc + t0 / 2;
-    const uint16_t *sp2 = reinterpret_cast<const uint16_t *>(a.v_scales + row * a.v_lds + t0 / 16);
-    uint4 cw[NG];
-    uint32_t s2[NG];
+    const int sl = tid & 127;
+    const int64_t row0 = h * a.D + (int64_t)blockIdx.x * kPR + 8 * (tid >> 7);
+    const float *st = a.stats + h * a.NW * 2;
+    // loads in the order of use: the statistics (entries lane + 64 k of a batch of
+    // 256), then the first tile's scores block and Vt slices
+    auto stats_at = [&](int i0, float2 *e) {
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-        const bool ok = 32 * i + 32 <= nt;     // a whole group of 32 tokens (else its start, unused)
-        cw[i] = *reinterpret_cast<const uint4 *>(cp + (ok ? 16 * i : 0));
-        s2[i] = sp2[ok ? i : 0];
-    }
-    const float s_own = tid < nt ? a.scores[h * a.T + t0 + tid] : 0.0f;   // this thread's token
-    const int g16 = nt & ~31;                  // a last block of 16 tokens starts here when nt % 32 == 16
-    const uint2 tw = *reinterpret_cast<const uint2 *>(cp + (nt & 16 ? g16 / 2 : 0));
-    const uint32_t ts = a.v_scales[row * a.v_lds + (t0 + (nt & 16 ? g16 : 0)) / 16];
-    // the head's max and normalizer from the chunks' statistics: wave 0's lanes take
-    // the chunks (the same fixed reduction in every workgroup of the head)
-    if (tid < 64) {
-        const float *st = a.stats + h * a.NC * 2;
-        float mloc = -INFINITY;
-        for (int i = tid; i < a.NC; i += 64) mloc = fmaxf(mloc, st[2 * i]);
-        const float mh = warp_max(mloc);
-        float lloc = 0.0f;
-        for (int i = tid; i < a.NC; i += 64) lloc += st[2 * i + 1] * expf(st[2 * i] - mh);
-        const float lh = warp_sum(lloc);
-        if (tid == 0) {
-            sh[0] = mh;
-            sh[1] = lh;
+        for (int k = 0; k < 4; ++k) {
+            const int i = i0 + 64 * k + lane;
+            e[k] = *reinterpret_cast<const float2 *>(st + 2 * (i < a.NW ? i : 0));
         }
+    };
+    float sc[16];
+    uint4 cw[8];
+    uint16_t s2[8];                            // widened where used (not ahead of the tile loop)
+    auto tile_loads = [&](int64_t t0, int nt) {
+        const float4 *sp = reinterpret_cast<const float4 *>(a.scores + h * a.T + t0 + (16 * tid < nt ? 16 * tid : 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 t = sp[i];
+            sc[4 * i] = t.x; sc[4 * i + 1] = t.y; sc[4 * i + 2] = t.z; sc[4 * i + 3] = t.w;
+        }
+        asm volatile("" ::: "memory");          // keep the scores ahead of the Vt stream
+        const int64_t tf = t0 + (32 * sl + 32 <= nt ? 32 * sl : 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            cw[i] = *reinterpret_cast<const uint4 *>(a.v_codes + (row0 + i) * a.v_ldc + tf / 2);
+            s2[i] = *reinterpret_cast<const uint16_t *>(a.v_scales + (row0 + i) * a.v_lds + tf / 16);
+        }
+    };
+    // the head's max and normalizer from the waves' statistics: every wave folds
+    // them in the same fixed order (lane i takes entries i, i + 64, ...). Up to 256
+    // entries (T <= 16384) they stay in registers from one batch of loads issued
+    // ahead of the scores and the Vt stream; beyond, a loop folds them first.
+    float2 e0[4];
+    stats_at(0, e0);
+    const float vS = a.v_S[0];
+    float m = -INFINITY, l = 0.0f;
+    if (a.NW > 256) {
+        float mloc = -INFINITY;
+        for (int i0 = 0; i0 < a.NW; i0 += 256) {
+            float2 e[4];
+            stats_at(i0, e);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (i0 + 64 * k + lane < a.NW) mloc = fmaxf(mloc, e[k].x);
+        }
+        m = warp_max(mloc);
+        float lloc = 0.0f;
+        for (int i0 = 0; i0 < a.NW; i0 += 256) {
+            float2 e[4];
+            stats_at(i0, e);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (i0 + 64 * k + lane < a.NW) lloc += e[k].y * expf(e[k].x - m);
+        }
+        l = warp_sum(lloc);
     }
-    __syncthreads();
-    const float m = sh[0], l = sh[1];
+    asm volatile("" ::: "memory");
+    tile_loads(0, (int)(a.T < kTT ? a.T : kTT));
+    if (a.NW <= 256) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (64 * k + lane < a.NW) mloc = fmaxf(mloc, e0[k].x);
+        m = warp_max(mloc);
+        float lloc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (64 * k + lane < a.NW) lloc += e0[k].y * expf(e0[k].x - m);
+        l = warp_sum(lloc);
+    }
     // p's tensor scale: max p = exp(0) / l
     const float pmax = 1.0f / l;
     const float Sp = pmax > 0.0f ? pmax / 2688.0f : 1.0f;
-    // every thread its token's probability, then thread b < nt / 16 quantizes the
-    // block of tokens t0 + 16 b ..
-    if (tid < nt) pv[tid] = expf(s_own - m) / l;
-    __syncthreads();
-    if (tid < nt / 16) {
-        float v[16];
+    float acc[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = pv[16 * tid + i];
-        float b[16], r[16];
-        quant_block(v, Sp, a.comp != 0, b, r);
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int64_t t0 = 0; t0 < a.T; t0 += kTT) {
+        const int nt = (int)(a.T - t0 < kTT ? a.T - t0 : kTT);   // a multiple of 16
+        if (t0 > 0) tile_loads(t0, nt);
+        // this thread's block of 16 probabilities (+ residue) into LDS
+        if (16 * tid < nt) {
+            float p[16], o[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            pb[16 * tid + i] = b[i];
-            pr[16 * tid + i] = r[i];
+            for (int i = 0; i < 16; ++i) p[i] = expf(sc[i] - m) / l;
+            quant_block_aug(p, Sp, a.comp != 0, o);
+#pragma unroll
+            for (int i = 0; i < 16; i += 4)
+                *reinterpret_cast<float4 *>(pa + 16 * tid + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
         }
-    }
-    __syncthreads();
-    // one output dimension per thread over the chunk's tokens
-    float* part = a.partial + (h * a.NC + c) * a.D;
-    if (has_row) {
-        float ob = 0.0f, orr = 0.0f;
+        __syncthreads();
+        if (32 * sl + 32 <= nt) {
+            float x[32];
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            if (32 * i + 32 <= nt) {
-                float vd[32];
-                decode32(cw[i], s2[i], vd);
+            for (int i = 0; i < 32; i += 4) {
+                const float4 t = *reinterpret_cast<const float4 *>(pa + 32 * sl + i);
+                x[i] = t.x; x[i + 1] = t.y; x[i + 2] = t.z; x[i + 3] = t.w;
+            }
 #pragma unroll
-                for (int j = 0; j < 32; ++j) {
-                    ob += pb[32 * i + j] * vd[j];
-                    orr += pr[32 * i + j] * vd[j];
-                }
+            for (int i = 0; i < 8; ++i) acc[i] += dot32(cw[i], s2[i], x);
+        } else if (32 * sl + 16 == nt) {
+            // the tile ends with half a slice: 16 tokens, one scale byte
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; i += 4) {
+                const float4 t = *reinterpret_cast<const float4 *>(pa + 32 * sl + i);
+                x[i] = t.x; x[i + 1] = t.y; x[i + 2] = t.z; x[i + 3] = t.w;
+            }
+            const int64_t hc = (t0 + 32 * sl) / 2, hs = (t0 + 32 * sl) / 16;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint2 c = *reinterpret_cast<const uint2 *>(a.v_codes + (row0 + i) * a.v_ldc + hc);
+                const float d = e4m3_to_float(a.v_scales[(row0 + i) * a.v_lds + hs]);
+                acc[i] += dot8(c.y, x + 8, dot8(c.x, x, 0.0f)) * d;
             }
         }
-        if (nt & 16) {
-            const float d = e4m3_to_float(ts);
-            float vd[16];
-            decode8_f32(tw.x, d, vd);
-            decode8_f32(tw.y, d, vd + 8);
-            for (int j = 0; j < 16; ++j) {
-                ob += pb[g16 + j] * vd[j];
-                orr += pr[g16 + j] * vd[j];
-            }
-        }
-        st_dev(part + tid, ob + orr);
+        if (t0 + kTT < a.T) __syncthreads();    // the next tile overwrites pa
     }
-    // the last workgroup of the head adds the partials in chunk order (device-scope
-    // stores, acknowledged before the arrival; device-scope loads after it)
-    wait_own_stores();
-    __syncthreads();
-    if (tid == 0) sh_last = add_dev(&a.cnt[h], 1u) == (unsigned)a.NC - 1;
-    __syncthreads();
-    if (sh_last && has_row) {
-        // sixteen device-scope loads in flight at a time, added in chunk order
-        const float *src = a.partial + h * a.NC * a.D + tid;
-        float s = 0.0f;
-        for (int i0 = 0; i0 < a.NC; i0 += 16) {
-            float v[16];
+    // the 128 slices of each row: across the wave, then the wave pair
 #pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = i0 + k < a.NC ? ld_dev(src + (int64_t)(i0 + k) * a.D) : 0.0f;
+    for (int i = 0; i < 8; ++i) acc[i] = warp_sum(acc[i]);
+    if (lane == 0) {
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                if (i0 + k < a.NC) s += v[k];
-        }
-        a.out[h * a.ldo + tid] = s * (Sp * a.v_S[0]);
+        for (int i = 0; i < 8; ++i) red[wave][i] = acc[i];
     }
-    if (sh_last && tid == 0) st_dev(&a.cnt[h], 0u);
+    __syncthreads();
+    if (tid < kPR) {
+        const int hh = tid >> 3, i = tid & 7;
+        const float o = red[2 * hh][i] + red[2 * hh + 1][i];
+        a.out[h * a.ldo + (int64_t)blockIdx.x * kPR + tid] = o * (Sp * vS);
+    }
 }
 
 }  // namespace
 
 size_t attention_workspace_bytes(int64_t H, int64_t D, int64_t T) {
-    const int64_t NC = (T + kAT - 1) / kAT;
+    (void)D;
+    const int64_t NW = (T + 63) / 64;
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
-    return up((size_t)(H * T) * 4) + up((size_t)(H * NC * 2) * 4) + up((size_t)(H * NC * D) * 4);
+    return up((size_t)(H * T) * 4) + up((size_t)(H * NW * 2) * 4);
 }
 
 hipError_t launch_attention(const AttentionLaunch &g, hipStream_t st) {
@@ -354,21 +389,18 @@ hipError_t launch_attention(const AttentionLaunch &g, hipStream_t st) {
     a.k_codes = g.k_codes; a.k_ldc = g.k_ldc; a.k_scales = g.k_scales; a.k_lds = g.k_lds; a.k_S = g.k_S;
     a.v_codes = g.v_codes; a.v_ldc = g.v_ldc; a.v_scales = g.v_scales; a.v_lds = g.v_lds; a.v_S = g.v_S;
     a.comp = g.compensate;
-    a.NC = (int)((g.T + kAT - 1) / kAT);
+    a.NW = (int)((g.T + 63) / 64);
     auto up = [](size_t n) { return (n + 255) / 256 * 256; };
     uint8_t *w = static_cast<uint8_t *>(g.scratch);
     a.scores = reinterpret_cast<float *>(w);
     w += up((size_t)(g.H * g.T) * 4);
     a.stats = reinterpret_cast<float *>(w);
-    w += up((size_t)(g.H * a.NC * 2) * 4);
-    a.partial = reinterpret_cast<float *>(w);
     a.out = g.out; a.ldo = g.ldo;
-    a.cnt = g.counters;
-    const dim3 grid((unsigned)a.NC, (unsigned)g.H);
+    const dim3 sgrid((unsigned)a.NW, (unsigned)g.H);
 #define AS(LPT)                                                                                    \
     do {                                                                                           \
-        if (g.qt == IN_BF16) attn_scores_kernel<IN_BF16, LPT><<<grid, kAT, 0, st>>>(a);            \
-        else attn_scores_kernel<IN_F32, LPT><<<grid, kAT, 0, st>>>(a);                             \
+        if (g.qt == IN_BF16) attn_scores_kernel<IN_BF16, LPT><<<sgrid, 64, 0, st>>>(a);            \
+        else attn_scores_kernel<IN_F32, LPT><<<sgrid, 64, 0, st>>>(a);                             \
     } while (0)
     const int64_t nd = g.D / 32;               // 32-column slices per row: 1..8
     if (nd == 1) AS(1);
@@ -376,7 +408,7 @@ hipError_t launch_attention(const AttentionLaunch &g, hipStream_t st) {
     else if (nd <= 4) AS(4);
     else AS(8);
 #undef AS
-    attn_pv_kernel<<<grid, kAT, 0, st>>>(a);
+    attn_pv_kernel<<<dim3((unsigned)(g.D / kPR), (unsigned)g.H), kPT, 0, st>>>(a);
     return hipGetLastError();
 }
 

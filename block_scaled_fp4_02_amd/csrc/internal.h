@@ -131,7 +131,7 @@ hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st);
 // probabilities: K cache [H*T, D], V cache transposed [H*D, T] (row-major).
 struct AttentionLaunch {
     const void *q; int qt; int64_t ldq;     // [H][D] bf16 or f32
-    int64_t H, D, T;                        // D % 32 == 0, D <= 256, T % 16 == 0, T > 0
+    int64_t H, D, T;                        // H <= 65535, D % 32 == 0, D <= 256, T % 16 == 0, T > 0
     const uint8_t *k_codes; int64_t k_ldc;
     const uint8_t *k_scales; int64_t k_lds;
     const float *k_S;
@@ -140,7 +140,6 @@ struct AttentionLaunch {
     const float *v_S;
     int compensate;
     float *out; int64_t ldo;                // [H][D] FP32
-    unsigned *counters;                     // H <= kMaxCounters arrival counters in the zero-kept header
     void *scratch; size_t scratch_bytes;    // attention_workspace_bytes()
 };
 size_t attention_workspace_bytes(int64_t H, int64_t D, int64_t T);

@@ -239,10 +239,14 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, i
  *   vt_cache row-major NVFP4, H*D rows of T columns: row h*D + j is dimension j of
  *            head h over the tokens (V transposed, blocks of 16 along the tokens)
  *   out      H x D FP32 (leading dimension ldo)
- * 32 <= D <= 256 with D % 32 == 0, T > 0 with T % 16 == 0, H <= 1024 (else
+ * Each cache element meets the sum of the base and residue values of its operand
+ * element, (e_q d_q + e_r d_r) e_k d_k, as in the augmented product's definition;
+ * sums are FP32 in a fixed order (the output is the same bits on every call).
+ * 32 <= D <= 256 with D % 32 == 0, T > 0 with T % 16 == 0, H <= 65535 (else
  * NVFP4_ERR_SHAPE); H == 0 does nothing. Workspace: nvfp4_workspace_size(5, H, D, T, 0)
- * bytes, the same zero-kept counter header as the products (H of its arrival
- * counters are used and returned to zero), so it can be shared with them. */
+ * bytes; the scores and softmax statistics go after the 8 KiB counter header,
+ * which this call leaves untouched, so the workspace can be shared with the
+ * products. */
 nvfp4_status nvfp4_decode_attention(const void *q, int qt, int64_t H, int64_t D, int64_t ldq,
                                     const nvfp4_tensor *k_cache, const nvfp4_tensor *vt_cache, int64_t T,
                                     int compensate, float *out, int64_t ldo, void *ws, size_t ws_bytes,
