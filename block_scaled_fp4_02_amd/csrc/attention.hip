@@ -47,6 +47,7 @@
 namespace nvfp4 {
 namespace {
 
+constexpr int kST = 256;                       // scores threads: four waves of 64 tokens
 constexpr int kPR = 16;                        // Vt rows (output dimensions) per PV workgroup
 constexpr int kPT = 256;                       // PV threads: 2 x 128 slices of 32 tokens
 constexpr int kTT = 4096;                      // tokens per LDS tile of probabilities
@@ -103,12 +104,19 @@ __device__ inline float dot8(uint32_t w, const float *x, float acc) {
     return acc;
 }
 
+// Both E4M3 bytes of s2's low half as floats, exact: the OCP FP8 convert (scale 1).
+__device__ inline float2 e4m3_pair(uint32_t s2) {
+    typedef float float2v __attribute__((ext_vector_type(2)));
+    const float2v d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s2, 1.0f, false);
+    return make_float2(d[0], d[1]);
+}
+
 // sum of x[i] e(c_i) d over 32 codes (16 bytes) and their two E4M3 bytes.
 __device__ inline float dot32(const uint4 c, uint32_t s2, const float *x) {
-    const float d0 = e4m3_to_float(s2 & 0xFFu), d1 = e4m3_to_float((s2 >> 8) & 0xFFu);
+    const float2 d = e4m3_pair(s2);
     const float a0 = dot8(c.y, x + 8, dot8(c.x, x, 0.0f));
     const float a1 = dot8(c.w, x + 24, dot8(c.z, x + 16, 0.0f));
-    return a0 * d0 + a1 * d1;
+    return a0 * d.x + a1 * d.y;
 }
 
 // Quantize the 16 values of one block against S (and its residue when comp) and
@@ -131,32 +139,69 @@ __device__ inline void quant_block_aug(const float *v, float S, bool comp, float
     for (int i = 0; i < 16; ++i) o[i] = o[i] + r[i];
 }
 
-// One wave per 64 tokens of a head. LPT lanes per token (D / 32 rounded up to a
-// power of two): lane group g holds the query's dimensions 32 g .. 32 g + 31 and
-// loads that 16-byte slice of its token's K row, so a wave reads 64 / LPT rows
-// (1 KiB at D = 128) per load; the partial dot products meet by cross-lane adds.
+// The same quantization with a block spread over an aligned group of four lanes
+// (quarter j = lane & 3 holds elements 4 j .. 4 j + 3): every step and rounding
+// of encode_block and block_residue per element, the block's absmax by two
+// cross-lane maxima (a maximum does not round).
+__device__ inline void enc4(const float *v, float S, float *ed, uint32_t &w, float &d) {
+    typedef float float2v __attribute__((ext_vector_type(2)));
+    float ab = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    ab = fmaxf(ab, __shfl_xor(ab, 1));
+    ab = fmaxf(ab, __shfl_xor(ab, 2));
+    const float sf = ab / (6.0f * S);
+    d = e4m3_to_float(e4m3_rne_sat(sf));
+    const float sc = d * S;
+    const float rcp = (sc > 0.0f) ? 1.0f / sc : 0.0f;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * rcp, v[1] * rcp, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * rcp, v[3] * rcp, 1.0f, 1);
+    const float2v e01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const float2v e23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    ed[0] = e01[0] * d; ed[1] = e01[1] * d; ed[2] = e23[0] * d; ed[3] = e23[1] * d;
+}
+__device__ inline void quant4_aug(const float *v, float S, bool comp, float *o) {
+    uint32_t w;
+    float d;
+    enc4(v, S, o, w, d);
+    if (!comp) return;
+    float r[4], er[4], dr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = v[i] - o[i] * S;
+    enc4(r, S, er, w, dr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = o[i] + er[i];
+}
+
+// Four waves of 64 tokens per workgroup. Wave 0 quantizes q_h (four lanes per
+// block) into LDS once for the workgroup; each wave then works alone. LPT lanes
+// per token (D / 32 rounded up to a power of two): lane group g holds the
+// query's dimensions 32 g .. 32 g + 31 and loads that 16-byte slice of its
+// token's K row, so a wave reads 64 / LPT rows (1 KiB at D = 128) per load; the
+// partial dot products meet by cross-lane adds. Statistics are per wave.
 template <int XT, int LPT>
-__global__ __launch_bounds__(64) void attn_scores_kernel(AArgs a) {
+__global__ __launch_bounds__(kST) void attn_scores_kernel(AArgs a) {
     __shared__ __attribute__((aligned(16))) float qa[256];
-    const int lane = threadIdx.x;
-    const int64_t w = blockIdx.x, h = blockIdx.y;
-    const int D = (int)a.D, nb = D / 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t h = blockIdx.y, w = (int64_t)blockIdx.x * (kST / 64) + wave;
+    const int D = (int)a.D;
     constexpr int TPW = 64 / LPT;                // tokens per load
     const int g = lane % LPT, tl = lane / LPT;
     const bool gv = 32 * g < D;
-    // the query block of lane b < nb first (used first; lanes past nb load block 0
-    // and drop it), then the K slices
-    // (raw words here, converted after the K loads are out)
-    uint4 qw[XT == IN_BF16 ? 2 : 4];
+    // the query first (used first: dimensions 4 lane .. 4 lane + 3, raw words;
+    // lanes past D load dimension 0 and drop it), then the K slices
+    constexpr int QB = XT == IN_BF16 ? 2 : 4;   // bytes per query element
+    const bool qv = 4 * lane < D;
+    uint32_t qw[QB];
     {
-        const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint8_t *>(a.q) +
-                                                          (h * a.ldq + 16 * (lane < nb ? lane : 0)) *
-                                                              (XT == IN_BF16 ? 2 : 4));
-#pragma unroll
-        for (int i = 0; i < (XT == IN_BF16 ? 2 : 4); ++i) qw[i] = qp[i];
+        const uint8_t *qp = static_cast<const uint8_t *>(a.q) + (h * a.ldq + (qv ? 4 * lane : 0)) * QB;
+        if (XT == IN_BF16) {
+            const uint2 t = *reinterpret_cast<const uint2 *>(qp);
+            qw[0] = t.x; qw[1] = t.y;
+        } else {
+            const uint4 t = *reinterpret_cast<const uint4 *>(qp);
+            qw[0] = t.x; qw[1] = t.y; qw[2] = t.z; qw[3] = t.w;
+        }
     }
     const float kS = a.k_S[0];
-    asm volatile("" ::: "memory");
     uint4 cw[LPT];
     uint32_t s2[LPT];
     int64_t tok[LPT];
@@ -170,32 +215,23 @@ __global__ __launch_bounds__(64) void attn_scores_kernel(AArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);         // every K load is out before q is used
     // q_h quantized as one tensor of D values (its residue against the same S)
-    float v[16];
+    float am;
+    {
+        float v[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (XT == IN_BF16) {
-            const uint32_t wd = (&qw[i / 4].x)[i % 4];
-            v[2 * i] = u2f(wd << 16);
-            v[2 * i + 1] = u2f(wd & 0xFFFF0000u);
-        } else {
-            v[2 * i] = u2f((&qw[i / 2].x)[2 * (i % 2)]);
-            v[2 * i + 1] = u2f((&qw[i / 2].x)[2 * (i % 2) + 1]);
+        for (int i = 0; i < 4; ++i) {
+            const float f = XT == IN_BF16 ? u2f(i & 1 ? qw[i >> 1] & 0xFFFF0000u : qw[i >> 1] << 16) : u2f(qw[i]);
+            v[i] = qv ? f : 0.0f;
+        }
+        am = warp_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        const float S = am > 0.0f ? am / 2688.0f : 1.0f;
+        if (wave == 0) {
+            float o[4];
+            quant4_aug(v, S, a.comp != 0, o);
+            if (qv) *reinterpret_cast<float4 *>(qa + 4 * lane) = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = lane < nb ? v[i] : 0.0f;
-    float am = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
-    am = warp_max(am);
     const float S = am > 0.0f ? am / 2688.0f : 1.0f;
-    if (lane < nb) {
-        float o[16];
-        quant_block_aug(v, S, a.comp != 0, o);
-#pragma unroll
-        for (int i = 0; i < 16; i += 4)
-            *reinterpret_cast<float4 *>(qa + 16 * lane + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
-    }
     __syncthreads();
     float x[32];
 #pragma unroll
@@ -226,7 +262,7 @@ __global__ __launch_bounds__(64) void attn_scores_kernel(AArgs a) {
         for (int it = 0; it < LPT; ++it) e += tok[it] < a.T ? expf(sv[it] - mx) : 0.0f;
     }
     e = warp_sum(e);
-    if (lane == 0) *reinterpret_cast<float2 *>(a.stats + (h * a.NW + w) * 2) = make_float2(mx, e);
+    if (lane == 0 && w < a.NW) *reinterpret_cast<float2 *>(a.stats + (h * a.NW + w) * 2) = make_float2(mx, e);
 }
 
 // One workgroup per 16 output dimensions of a head, over all of its tokens.
@@ -396,11 +432,11 @@ hipError_t launch_attention(const AttentionLaunch &g, hipStream_t st) {
     w += up((size_t)(g.H * g.T) * 4);
     a.stats = reinterpret_cast<float *>(w);
     a.out = g.out; a.ldo = g.ldo;
-    const dim3 sgrid((unsigned)a.NW, (unsigned)g.H);
+    const dim3 sgrid((unsigned)((a.NW + kST / 64 - 1) / (kST / 64)), (unsigned)g.H);
 #define AS(LPT)                                                                                    \
     do {                                                                                           \
-        if (g.qt == IN_BF16) attn_scores_kernel<IN_BF16, LPT><<<sgrid, 64, 0, st>>>(a);            \
-        else attn_scores_kernel<IN_F32, LPT><<<sgrid, 64, 0, st>>>(a);                             \
+        if (g.qt == IN_BF16) attn_scores_kernel<IN_BF16, LPT><<<sgrid, kST, 0, st>>>(a);           \
+        else attn_scores_kernel<IN_F32, LPT><<<sgrid, kST, 0, st>>>(a);                            \
     } while (0)
     const int64_t nd = g.D / 32;               // 32-column slices per row: 1..8
     if (nd == 1) AS(1);

@@ -75,6 +75,32 @@ def test_attention_closed_forms(nv, orc, comp):
     np.testing.assert_allclose(o, vd[:, :, hot], rtol=2e-6, atol=1e-6)
 
 
+def test_attention_one_hot_small_scales(nv, orc):
+    """One dominant token whose V block is scaled down row by row (factors 2^0 ..
+    2^-19), so its E4M3 block scales run from normal through the subnormal codes to
+    zero: o equals that token's dequantized V column to FP32 rounding, element by
+    element and without an absolute floor (a wrong scale decode at any code shows)."""
+    H, T, D = 2, 64, 128
+    hot = 21
+    g = np.random.default_rng(12)
+    vt = g.standard_normal((H * D, T)).astype(np.float32)
+    blk = slice(16 * (hot // 16), 16 * (hot // 16) + 16)
+    for r in range(H * D):
+        vt[r, blk] *= np.float32(2.0 ** -(r % 20))
+    vt = torch.from_numpy(vt)
+    q = torch.zeros((H, D), dtype=torch.float32)
+    q[:, 0] = 64.0
+    k = torch.zeros((H * T, D), dtype=torch.float32)
+    k[[h * T + hot for h in range(H)], 0] = 64.0
+    codes = orc.quantize(vt)
+    sb = np.asarray(codes.scales)[:, hot // 16]
+    assert ((sb > 0) & (sb < 8)).any() and (sb >= 8).any()      # subnormal and normal codes
+    vd = orc.dequantize(codes).reshape(H, D, T)
+    for comp in (True, False):
+        o, _ = _run(nv, orc, q, k, vt, H, T, D, comp, q_f32=True)
+        np.testing.assert_allclose(o, vd[:, :, hot], rtol=2e-6, atol=0)
+
+
 def test_attention_repeat_and_graph(nv):
     """Deterministic across calls, and a captured graph replays to the same bits."""
     H, T, D = 4, 512, 64
