@@ -828,8 +828,12 @@ void decode_kernel(DArgs a) {
 // ---------------------------------------------------------------- M = 33..64
 // Four row tiles take 64 rows x 1 KiB of operand per 512-column unit, so a
 // whole K range does not fit in LDS. Here the operand streams through a window
-// of two unit slots instead: every consumer wave owns one 16-row weight tile
-// over all of K (no split-K, no combine), producers fill the slot of unit k + 2
+// of two unit slots instead: a workgroup owns four 16-row weight tiles over all
+// of K (no split-K, no combine) and each consumer wave one quadrant of its
+// 64 x 64 output block -- two row tiles times two weight tiles, so an operand
+// fragment read from LDS feeds two weight tiles (LDS reads per CU halve against
+// a wave per weight tile: 35.4 -> 32.9 us for the M = 64 augmented call), each
+// weight item loaded by the two waves of its column pair; producers fill the slot of unit k + 2
 // as soon as the consumers are done with unit k, one workgroup barrier per
 // unit (loads run three units ahead on both sides). Residue columns (ARCQuant
 // article, sections 3.1-3.2) are further
@@ -905,7 +909,6 @@ __device__ inline void win_unit_load(const DArgs &a, const WinRows &w, int v, in
 template <bool TILED, bool RES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))   // 128 KiB of LDS: one per CU
 void decode_win_kernel(DArgs a) {
-    constexpr int MT = 4;
     constexpr int R = kWinRows, SLOT = 64 * kWinRows;
     extern __shared__ half8 lds_a[];           // [2 slots][64 R]: rows >= M are never read
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -915,30 +918,40 @@ void decode_win_kernel(DArgs a) {
 
     TL(0);
     if (wave < kCons) {
-        // ---- consumer: tile t over all (virtual) units
-        const int64_t t = 4 * (int64_t)blockIdx.x + wave;
-        const bool has = t < a.NT;
-        const int64_t tc = has ? t : a.NT - 1;
+        // ---- consumer: one quadrant of the workgroup's 64 x 64 output block over all
+        // (virtual) units -- row tiles 2 qa, 2 qa + 1 times weight tiles t0, t0 + 1 --
+        // so every operand fragment read from LDS feeds the MFMAs of two weight tiles
+        const int qa = wave >> 1, qb = wave & 1;
+        const int64_t t0 = 4 * (int64_t)blockIdx.x + 2 * qb;
+        const bool has = t0 < a.NT;            // (t0 + 1 past the tiles: loads clamped, nothing stored)
+        const int64_t tc[2] = {has ? t0 : a.NT - 1, t0 + 1 < a.NT ? t0 + 1 : a.NT - 1};
         const float qS = load_vmem(a.q_S), wS = load_vmem(a.w_S);   // first: no wait holds a weight load on them
-        auto issue = [&](int v, WLoad &w) {
+        auto issue = [&](int v, WLoad *w) {
             const int64_t wu = v < KU ? v : v - KU;
-            if (TILED) {
-                load_w_tiled(a, tc, wu, lane, w);
-            } else {
-                const int64_t n = 16 * tc + r16;
-                load_w(a, n < a.N ? n : a.N - 1, 512 * wu, g, w);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                if (TILED) {
+                    load_w_tiled(a, tc[tt], wu, lane, w[tt]);
+                } else {
+                    const int64_t n = 16 * tc[tt] + r16;
+                    load_w(a, n < a.N ? n : a.N - 1, 512 * wu, g, w[tt]);
+                }
             }
         };
-        int arow[MT][4];                       // swizzled row of row tile mt in 32-column step i
+        int arow[2][4];                        // swizzled row of row tile 2 qa + m in 32-column step i
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                arow[mt][i] = ((16 * mt + r16 < M ? 16 * mt + r16 : M - 1) + g + 4 * i) & (kWinRows - 1);
-        float4v acc[MT];
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * (2 * qa + m) + r16;
+                arow[m][i] = ((row < M ? row : M - 1) + g + 4 * i) & (kWinRows - 1);
+            }
+        float4v acc[2][2];                     // [weight tile][row tile]
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = float4v{0, 0, 0, 0};
-        WLoad ring0, ring1, ring2;             // units v, v + 1, v + 2 in flight (v mod 3)
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) acc[tt][m] = float4v{0, 0, 0, 0};
+        WLoad ring0[2], ring1[2], ring2[2];    // units v, v + 1, v + 2 in flight (v mod 3)
         __syncthreads();                       // the producers' first activation loads are out
         if (has) {
             issue(0, ring0);
@@ -947,22 +960,32 @@ void decode_win_kernel(DArgs a) {
         }
         __syncthreads();                       // barrier 0: units 0 and 1 are in their slots
         TL(1);
-        auto step = [&](int v, WLoad &w) {
+        auto step = [&](int v, WLoad *w) {
             if (has) {
                 const half8 *abase = lds_a + (v & 1) * SLOT + g * R;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t sw = (i < 2) ? w.s.x : w.s.y;
-                    const half2v d0 = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
-                    const half2v d1 = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
-                    const uint32_t cws[4] = {w.c[i].x, w.c[i].y, w.c[i].z, w.c[i].w};
+                    half2v d[2][2];
+                    uint32_t cws[2][4];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const uint32_t sw = (i < 2) ? w[tt].s.x : w[tt].s.y;
+                        d[tt][0] = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
+                        d[tt][1] = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
+                        cws[tt][0] = w[tt].c[i].x; cws[tt][1] = w[tt].c[i].y;
+                        cws[tt][2] = w[tt].c[i].z; cws[tt][3] = w[tt].c[i].w;
+                    }
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const half8 b = decode8(cws[j], j < 2 ? d0 : d1);
+                        const half8 b0 = decode8(cws[0][j], d[0][j >> 1]);
+                        const half8 b1 = decode8(cws[1][j], d[1][j >> 1]);
                         const int fo = (4 * i + j) * 4 * R;
 #pragma unroll
-                        for (int mt = 0; mt < MT; ++mt)
-                            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(abase[fo + arow[mt][i]], b, acc[mt], 0, 0, 0);
+                        for (int m = 0; m < 2; ++m) {
+                            const half8 av = abase[fo + arow[m][i]];
+                            acc[0][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b0, acc[0][m], 0, 0, 0);
+                            acc[1][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b1, acc[1][m], 0, 0, 0);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);   // one 32-column step's fragments live at a time
                 }
@@ -980,19 +1003,22 @@ void decode_win_kernel(DArgs a) {
         TL(4);
         if (has) {
             const float scale = qS * wS;
-            const int64_t n = 16 * t + r16;
-            if (n < a.N) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+            for (int tt = 0; tt < 2; ++tt) {
+                const int64_t n = 16 * (t0 + tt) + r16;
+                if (n < a.N) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t m = 16 * mt + 4 * g + e;
-                        if (m < a.M) {
-                            const float val = acc[mt][e] * scale;
-                            if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n] = val;
-                            else static_cast<uint16_t *>(a.y)[m * a.ldy + n] = f32_to_bf16_rne(val);
+                    for (int m = 0; m < 2; ++m)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int64_t row = 16 * (2 * qa + m) + 4 * g + e;
+                            if (row < a.M) {
+                                const float val = acc[tt][m][e] * scale;
+                                if (a.yt == 1) static_cast<float *>(a.y)[row * a.ldy + n] = val;
+                                else static_cast<uint16_t *>(a.y)[row * a.ldy + n] = f32_to_bf16_rne(val);
+                            }
                         }
-                    }
+                }
             }
         }
     } else {
@@ -1210,8 +1236,9 @@ extern "C" int nvfp4_debug_timeline(void *host, size_t bytes) {
 }
 #endif
 
-// M = 33..64: the windowed kernel, one 16-row weight tile per consumer wave
-// over all of K (and the residue units), quantized activations only.
+// M = 33..64: the windowed kernel, four weight tiles per workgroup over all of K
+// (and the residue units), each consumer wave one quadrant of the 64 x 64 output
+// block; quantized activations only.
 hipError_t launch_decode_win(const DecodeLaunch &g, hipStream_t st) {
     if (g.x != nullptr || !g.header) return hipErrorInvalidValue;
     DArgs a{};
