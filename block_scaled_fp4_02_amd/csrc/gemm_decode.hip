@@ -197,6 +197,7 @@ __device__ inline PMap prod_map(int ptid, int M) {
 // fragment j = 0, plus kV1 when the chunk's second 16-column block is inside
 // the data; -1 past the list.
 constexpr int kV1 = 1 << 30;
+constexpr int kZS = 1 << 29;                   // key flag: the chunk lies past the data, store zeros
 struct ChunkPos {
     int64_t col;   // stored column of the chunk start (residue columns follow column K)
     int key;
@@ -239,8 +240,9 @@ __device__ inline QChunk qchunk_load(const uint8_t *crow, const uint8_t *srow, c
 __device__ inline void qchunk_store(half8 *lds, int js, const QChunk &q) {
     if (q.key < 0) return;
     const bool v1 = q.key & kV1;
-    const int slot = q.key & (kV1 - 1);
-    const uint32_t s0 = q.s & 0xFFu, s1 = (uint32_t)q.s >> 8;
+    const int slot = q.key & (kZS - 1);
+    const uint32_t sv = (q.key & kZS) ? 0u : q.s;   // applied here, not at the load: no early wait
+    const uint32_t s0 = sv & 0xFFu, s1 = sv >> 8;
     const half2v d0 = scale_pair(s0), d1 = scale_pair(v1 ? s1 : 0u);
     lds[slot] = decode8(q.c.x, d0);
     lds[slot + js] = decode8(q.c.y, d0);
@@ -900,9 +902,8 @@ __device__ inline void win_unit_load(const DArgs &a, const WinRows &w, int v, in
 #pragma unroll
     for (int i = 0; i < kWinChunks; ++i) {
         q[i].c = *reinterpret_cast<const uint4 *>(w.c[i] + coff);
-        const uint16_t sv = *reinterpret_cast<const uint16_t *>(w.s[i] + soff);
-        q[i].s = in ? sv : (uint16_t)0;
-        q[i].key = w.key[i] < 0 ? -1 : w.key[i] + (v1 ? kV1 : 0);
+        q[i].s = *reinterpret_cast<const uint16_t *>(w.s[i] + soff);
+        q[i].key = w.key[i] < 0 ? -1 : w.key[i] + (v1 ? kV1 : 0) + (in ? 0 : kZS);
     }
 }
 
