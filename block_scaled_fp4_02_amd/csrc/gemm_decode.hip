@@ -837,7 +837,7 @@ void decode_kernel(DArgs a) {
 // a wave per weight tile: 35.4 -> 32.9 us for the M = 64 augmented call), each
 // weight item loaded by the two waves of its column pair; producers fill the slot of unit k + 2
 // as soon as the consumers are done with unit k, one workgroup barrier per
-// unit (loads run three units ahead on both sides). Residue columns (ARCQuant
+// unit (weight loads run four units ahead, operand loads three). Residue columns (ARCQuant
 // article, sections 3.1-3.2) are further
 // "virtual units" after the K / 512 main ones: their operand is the residue
 // rows, their weights W's first units again (read a second time: S / K more
@@ -952,12 +952,13 @@ void decode_win_kernel(DArgs a) {
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int m = 0; m < 2; ++m) acc[tt][m] = float4v{0, 0, 0, 0};
-        WLoad ring0[2], ring1[2], ring2[2];    // units v, v + 1, v + 2 in flight (v mod 3)
+        WLoad ring0[2], ring1[2], ring2[2], ring3[2];   // units v .. v + 3 in flight (v mod 4)
         __syncthreads();                       // the producers' first activation loads are out
         if (has) {
             issue(0, ring0);
             if (NV > 1) issue(1, ring1);
             if (NV > 2) issue(2, ring2);
+            if (NV > 3) issue(3, ring3);
         }
         __syncthreads();                       // barrier 0: units 0 and 1 are in their slots
         TL(1);
@@ -990,16 +991,17 @@ void decode_win_kernel(DArgs a) {
                     }
                     __builtin_amdgcn_sched_barrier(0);   // one 32-column step's fragments live at a time
                 }
-                if (v + 3 < NV) issue(v + 3, w);
+                if (v + 4 < NV) issue(v + 4, w);
             }
             if (v + 1 < NV) __syncthreads();   // barrier v + 1: done with unit v
             if (v == 2) TL(2);
             if (v == 5) TL(3);
         };
-        for (int v = 0; v < NV; v += 3) {
+        for (int v = 0; v < NV; v += 4) {
             step(v, ring0);
             if (v + 1 < NV) step(v + 1, ring1);
             if (v + 2 < NV) step(v + 2, ring2);
+            if (v + 3 < NV) step(v + 3, ring3);
         }
         TL(4);
         if (has) {
