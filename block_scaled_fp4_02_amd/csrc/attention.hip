@@ -269,13 +269,16 @@ __global__ __launch_bounds__(kST) void attn_scores_kernel(AArgs a) {
 // Thread t takes slice t % 128 (32 tokens) of rows 8 (t / 128) .. + 7 per tile of
 // 4096 tokens, so the lanes of a wave read 64 consecutive 16-byte slices of one
 // row per load; and block t of the tile's probabilities for the quantization.
+// Workgroup i takes head i % H and dimension group i / H: workgroups go to the
+// eight XCDs in turn by their index, so with H a multiple of 8 all groups of a
+// head share one XCD and its L2 fetches the head's scores once (not once per XCD).
 __global__ __launch_bounds__(kPT) void attn_pv_kernel(AArgs a) {
     __shared__ __attribute__((aligned(16))) float pa[kTT];
     __shared__ float red[kPT / 64][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t h = blockIdx.y;
+    const int64_t h = blockIdx.x % a.H, dg = blockIdx.x / a.H;
     const int sl = tid & 127;
-    const int64_t row0 = h * a.D + (int64_t)blockIdx.x * kPR + 8 * (tid >> 7);
+    const int64_t row0 = h * a.D + dg * kPR + 8 * (tid >> 7);
     const float *st = a.stats + h * a.NW * 2;
     // loads in the order of use: the statistics (entries lane + 64 k of a batch of
     // 256), then the first tile's scores block and Vt slices
@@ -404,7 +407,7 @@ __global__ __launch_bounds__(kPT) void attn_pv_kernel(AArgs a) {
     if (tid < kPR) {
         const int hh = tid >> 3, i = tid & 7;
         const float o = red[2 * hh][i] + red[2 * hh + 1][i];
-        a.out[h * a.ldo + (int64_t)blockIdx.x * kPR + tid] = o * (Sp * vS);
+        a.out[h * a.ldo + dg * kPR + tid] = o * (Sp * vS);
     }
 }
 
@@ -444,7 +447,7 @@ hipError_t launch_attention(const AttentionLaunch &g, hipStream_t st) {
     else if (nd <= 4) AS(4);
     else AS(8);
 #undef AS
-    attn_pv_kernel<<<dim3((unsigned)(g.D / kPR), (unsigned)g.H), kPT, 0, st>>>(a);
+    attn_pv_kernel<<<dim3((unsigned)(g.D / kPR * g.H)), kPT, 0, st>>>(a);
     return hipGetLastError();
 }
 
