@@ -831,11 +831,12 @@ void decode_kernel(DArgs a) {
 // Four row tiles take 64 rows x 1 KiB of operand per 512-column unit, so a
 // whole K range does not fit in LDS. Here the operand streams through a window
 // of two unit slots instead: a workgroup owns four 16-row weight tiles over all
-// of K (no split-K, no combine) and each consumer wave one quadrant of its
-// 64 x 64 output block -- two row tiles times two weight tiles, so an operand
-// fragment read from LDS feeds two weight tiles (LDS reads per CU halve against
-// a wave per weight tile: 35.4 -> 32.9 us for the M = 64 augmented call), each
-// weight item loaded by the two waves of its column pair; producers fill the slot of unit k + 2
+// of K (no split-K across workgroups) and consumer wave w takes the 32-column
+// step w of every unit for all four weight tiles and all four row tiles, so each
+// weight item is loaded and decoded once and each operand fragment read once per
+// CU (against a wave per weight tile: operand reads / 4, the M = 64 augmented
+// call 35.4 -> 28.3 us with the deeper weight ring); the four waves' partial
+// tiles are added in LDS in wave order at the end; producers fill the slot of unit k + 2
 // as soon as the consumers are done with unit k, one workgroup barrier per
 // unit (weight loads run four units ahead, operand loads three). Residue columns (ARCQuant
 // article, sections 3.1-3.2) are further
@@ -843,7 +844,8 @@ void decode_kernel(DArgs a) {
 // rows, their weights W's first units again (read a second time: S / K more
 // weight bytes, against twice the LDS for a second operand copy).
 //
-// Barriers: both kinds of wave pass exactly NV + 1 = KU + RU + 1 of them. The
+// Barriers: both kinds of wave pass exactly NV + 3 = KU + RU + 3 of them (the
+// last two around the consumers' partial sums). The
 // first: the producers' loads of units 0..2 are out, so the consumers' weight
 // loads queue behind them (measured: the first units land ~1.9 us earlier, the
 // M = 64 product 4% faster). Barrier 0: units 0 and 1 are in their slots.
@@ -907,6 +909,12 @@ __device__ inline void win_unit_load(const DArgs &a, const WinRows &w, int v, in
     }
 }
 
+// A consumer's share of one unit: 32-column step iw of each of four weight tiles.
+struct WStep {
+    uint4 c[4];
+    uint16_t s[4];                             // the step's two E4M3 bytes per tile
+};
+
 template <bool TILED, bool RES>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))   // 128 KiB of LDS: one per CU
 void decode_win_kernel(DArgs a) {
@@ -919,80 +927,79 @@ void decode_win_kernel(DArgs a) {
 
     TL(0);
     if (wave < kCons) {
-        // ---- consumer: one quadrant of the workgroup's 64 x 64 output block over all
-        // (virtual) units -- row tiles 2 qa, 2 qa + 1 times weight tiles t0, t0 + 1 --
-        // so every operand fragment read from LDS feeds the MFMAs of two weight tiles
-        const int qa = wave >> 1, qb = wave & 1;
-        const int64_t t0 = 4 * (int64_t)blockIdx.x + 2 * qb;
-        const bool has = t0 < a.NT;            // (t0 + 1 past the tiles: loads clamped, nothing stored)
-        const int64_t tc[2] = {has ? t0 : a.NT - 1, t0 + 1 < a.NT ? t0 + 1 : a.NT - 1};
+        // ---- consumer: 32-column step iw = wave of every (virtual) unit, for the
+        // workgroup's four weight tiles and four row tiles: each weight item is loaded
+        // and decoded once per workgroup and each operand fragment read once per CU;
+        // the waves' partial tiles are added in LDS at the end
+        const int iw = wave;
+        const int64_t tb = 4 * (int64_t)blockIdx.x;
+        int64_t tcl[4];                        // tiles clamped into W (tiles past it are not stored)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) tcl[tt] = tb + tt < a.NT ? tb + tt : a.NT - 1;
         const float qS = load_vmem(a.q_S), wS = load_vmem(a.w_S);   // first: no wait holds a weight load on them
-        auto issue = [&](int v, WLoad *w) {
+        auto issue = [&](int v, WStep &w) {
             const int64_t wu = v < KU ? v : v - KU;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
+            for (int tt = 0; tt < 4; ++tt) {
                 if (TILED) {
-                    load_w_tiled(a, tc[tt], wu, lane, w[tt]);
+                    // step iw of the item is its own contiguous KiB; its two scale bytes
+                    // sit at 2 iw in the lane's eight
+                    w.c[tt] = *reinterpret_cast<const uint4 *>(a.w_codes + tcl[tt] * a.w_ldc + wu * 4096 +
+                                                               1024 * iw + 16 * lane);
+                    w.s[tt] = *reinterpret_cast<const uint16_t *>(a.w_scales + tcl[tt] * a.w_lds + wu * 512 +
+                                                                   8 * lane + 2 * iw);
                 } else {
-                    const int64_t n = 16 * tc[tt] + r16;
-                    load_w(a, n < a.N ? n : a.N - 1, 512 * wu, g, w[tt]);
+                    const int64_t n0 = 16 * tcl[tt] + r16, n = n0 < a.N ? n0 : a.N - 1;
+                    const int64_t ki = 512 * wu + 128 * g + 32 * iw;
+                    w.c[tt] = *reinterpret_cast<const uint4 *>(a.w_codes + n * a.w_ldc + (ki < a.K ? ki / 2 : 0));
+                    w.s[tt] = *reinterpret_cast<const uint16_t *>(a.w_scales + n * a.w_lds + (ki < a.K ? ki / 16 : 0));
                 }
             }
         };
-        int arow[2][4];                        // swizzled row of row tile 2 qa + m in 32-column step i
+        int arow[4];                           // swizzled row of row tile mt in step iw
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int mt = 0; mt < 4; ++mt)
+            arow[mt] = ((16 * mt + r16 < M ? 16 * mt + r16 : M - 1) + g + 4 * iw) & (kWinRows - 1);
+        float4v acc[4][4];                     // [weight tile][row tile]
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * (2 * qa + m) + r16;
-                arow[m][i] = ((row < M ? row : M - 1) + g + 4 * i) & (kWinRows - 1);
-            }
-        float4v acc[2][2];                     // [weight tile][row tile]
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) acc[tt][m] = float4v{0, 0, 0, 0};
-        WLoad ring0[2], ring1[2], ring2[2], ring3[2];   // units v .. v + 3 in flight (v mod 4)
+            for (int mt = 0; mt < 4; ++mt) acc[tt][mt] = float4v{0, 0, 0, 0};
+        WStep ring0, ring1, ring2, ring3;      // units v .. v + 3 in flight (v mod 4)
         __syncthreads();                       // the producers' first activation loads are out
-        if (has) {
-            issue(0, ring0);
-            if (NV > 1) issue(1, ring1);
-            if (NV > 2) issue(2, ring2);
-            if (NV > 3) issue(3, ring3);
-        }
+        issue(0, ring0);
+        if (NV > 1) issue(1, ring1);
+        if (NV > 2) issue(2, ring2);
+        if (NV > 3) issue(3, ring3);
         __syncthreads();                       // barrier 0: units 0 and 1 are in their slots
         TL(1);
-        auto step = [&](int v, WLoad *w) {
-            if (has) {
-                const half8 *abase = lds_a + (v & 1) * SLOT + g * R;
+        auto step = [&](int v, WStep &w) {
+            const half8 *abase = lds_a + (v & 1) * SLOT + g * R;
+            half2v d[4][2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    half2v d[2][2];
-                    uint32_t cws[2][4];
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const uint32_t sw = (i < 2) ? w[tt].s.x : w[tt].s.y;
-                        d[tt][0] = scale_pair((sw >> (16 * (i & 1))) & 0xFFu);
-                        d[tt][1] = scale_pair((sw >> (16 * (i & 1) + 8)) & 0xFFu);
-                        cws[tt][0] = w[tt].c[i].x; cws[tt][1] = w[tt].c[i].y;
-                        cws[tt][2] = w[tt].c[i].z; cws[tt][3] = w[tt].c[i].w;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const half8 b0 = decode8(cws[0][j], d[0][j >> 1]);
-                        const half8 b1 = decode8(cws[1][j], d[1][j >> 1]);
-                        const int fo = (4 * i + j) * 4 * R;
-#pragma unroll
-                        for (int m = 0; m < 2; ++m) {
-                            const half8 av = abase[fo + arow[m][i]];
-                            acc[0][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b0, acc[0][m], 0, 0, 0);
-                            acc[1][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b1, acc[1][m], 0, 0, 0);
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);   // one 32-column step's fragments live at a time
-                }
-                if (v + 4 < NV) issue(v + 4, w);
+            for (int tt = 0; tt < 4; ++tt) {
+                d[tt][0] = scale_pair(w.s[tt] & 0xFFu);
+                d[tt][1] = scale_pair((uint32_t)w.s[tt] >> 8);
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                half8 b[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const uint32_t cw = j == 0 ? w.c[tt].x : j == 1 ? w.c[tt].y : j == 2 ? w.c[tt].z : w.c[tt].w;
+                    b[tt] = decode8(cw, d[tt][j >> 1]);
+                }
+                const int fo = (4 * iw + j) * 4 * R;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const half8 av = abase[fo + arow[mt]];
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        acc[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[tt], acc[tt][mt], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // one 8-column fragment's operands live at a time
+            }
+            if (v + 4 < NV) issue(v + 4, w);
             if (v + 1 < NV) __syncthreads();   // barrier v + 1: done with unit v
             if (v == 2) TL(2);
             if (v == 5) TL(3);
@@ -1004,23 +1011,31 @@ void decode_win_kernel(DArgs a) {
             if (v + 3 < NV) step(v + 3, ring3);
         }
         TL(4);
-        if (has) {
+        // the four waves' partial tiles, parked in the operand slots and added in wave order
+        float4v *park = reinterpret_cast<float4v *>(lds_a);   // [wave][tt * 4 + mt][lane]: 64 KiB
+        __syncthreads();                       // every wave is done with the operand
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) park[(wave * 16 + tt * 4 + mt) * 64 + lane] = acc[tt][mt];
+        __syncthreads();
+        const int tt = wave;                   // wave w sums and stores weight tile w
+        const int64_t n = 16 * (tb + tt) + r16;
+        if (tb + tt < a.NT && n < a.N) {
             const float scale = qS * wS;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int64_t n = 16 * (t0 + tt) + r16;
-                if (n < a.N) {
+            for (int mt = 0; mt < 4; ++mt) {
+                float4v sum = park[(tt * 4 + mt) * 64 + lane];
 #pragma unroll
-                    for (int m = 0; m < 2; ++m)
+                for (int w2 = 1; w2 < kCons; ++w2) sum += park[(w2 * 16 + tt * 4 + mt) * 64 + lane];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int64_t row = 16 * (2 * qa + m) + 4 * g + e;
-                            if (row < a.M) {
-                                const float val = acc[tt][m][e] * scale;
-                                if (a.yt == 1) static_cast<float *>(a.y)[row * a.ldy + n] = val;
-                                else static_cast<uint16_t *>(a.y)[row * a.ldy + n] = f32_to_bf16_rne(val);
-                            }
-                        }
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t row = 16 * mt + 4 * g + e;
+                    if (row < a.M) {
+                        const float val = sum[e] * scale;
+                        if (a.yt == 1) static_cast<float *>(a.y)[row * a.ldy + n] = val;
+                        else static_cast<uint16_t *>(a.y)[row * a.ldy + n] = f32_to_bf16_rne(val);
+                    }
                 }
             }
         }
@@ -1060,6 +1075,8 @@ void decode_win_kernel(DArgs a) {
             if (k + 1 < NV) pstep(k + 1, q2, q1);
             if (k + 2 < NV) pstep(k + 2, q0, q2);
         }
+        __syncthreads();                       // the consumers' two barriers around their partial sums
+        __syncthreads();
     }
 }
 
@@ -1240,8 +1257,8 @@ extern "C" int nvfp4_debug_timeline(void *host, size_t bytes) {
 #endif
 
 // M = 33..64: the windowed kernel, four weight tiles per workgroup over all of K
-// (and the residue units), each consumer wave one quadrant of the 64 x 64 output
-// block; quantized activations only.
+// (and the residue units), each consumer wave one 32-column step of every unit;
+// quantized activations only.
 hipError_t launch_decode_win(const DecodeLaunch &g, hipStream_t st) {
     if (g.x != nullptr || !g.header) return hipErrorInvalidValue;
     DArgs a{};
