@@ -24,15 +24,17 @@
 // convert, products accumulated by FMA per 16-block and scaled once by the
 // block's E4M3 value. Two launches; the softmax needs the head's max and sum
 // before any probability can be quantized (its tensor scale is 1 / sum):
-//   attn_scores_kernel  (64 tokens, head), one wave: quantizes q_h (+ residue),
-//                       D / 32 lanes per token stream its K row (a 16-byte slice
-//                       each, the query's slice in registers), writes s and the
-//                       wave's (max, sum of exp(s - max)). No barrier but the one
-//                       that hands the quantized query across the wave.
+//   attn_scores_kernel  (256 tokens, head), four waves: wave 0 quantizes q_h
+//                       (+ residue) once for the workgroup; D / 32 lanes per token
+//                       stream its K row (a 16-byte slice each, the query's slice
+//                       in registers); each wave writes u = exp(s - m_w) for its 64
+//                       tokens and its (m_w, sum of u), m_w the max of its scores.
 //   attn_pv_kernel      (16 output dimensions, head): every workgroup folds the
-//                       head's statistics (the same fixed order everywhere),
-//                       quantizes the head's probabilities (+ residue) into LDS,
-//                       one block of 16 per thread, and streams its 16 Vt rows
+//                       head's statistics into (m, l) (the same fixed order
+//                       everywhere), forms p = u exp(m_w - m) / l (the softmax's
+//                       exp(s - m) / l taken per 64-token group: one multiply per
+//                       token), quantizes the head's probabilities (+ residue) into
+//                       LDS, one block of 16 per thread, and streams its 16 Vt rows
 //                       (a wave reads 1 KiB of one row per load); the slices'
 //                       sums meet by cross-lane adds. The workgroup covers all
 //                       tokens, so no partial outputs cross workgroups.
@@ -62,7 +64,7 @@ struct AArgs {
     const uint8_t *v_scales; int64_t v_lds;
     const float *v_S;
     int comp;
-    float *scores;                             // [H][T]
+    float *scores;                             // [H][T]: u = exp(s - m_w), m_w the max of the token's wave
     float *stats;                              // [H][NW][2]: a wave's max and sum of exp(s - max)
     float *out; int64_t ldo;
     int NW;                                    // waves (64 tokens each) per head
@@ -250,16 +252,22 @@ __global__ __launch_bounds__(kST) void attn_scores_kernel(AArgs a) {
         for (int o = 1; o < LPT; o <<= 1) sum += __shfl_xor(sum, o);
         const float sc = (sum * scale) * inv;
         const bool ok = tok[it] < a.T;
-        if (ok && g == 0) a.scores[h * a.T + tok[it]] = sc;
         sv[it] = ok ? sc : -INFINITY;
         mx = fmaxf(mx, sv[it]);
     }
-    // the wave's max and sum of exp(s - max) (every lane of a token holds its score)
+    // the wave's max m_w and sum of u = exp(s - m_w) (every lane of a token holds its
+    // score); u is what the P.V kernel needs of a token: p = u exp(m_w - m) / l
     mx = warp_max(mx);
     float e = 0.0f;
     if (g == 0) {
 #pragma unroll
-        for (int it = 0; it < LPT; ++it) e += tok[it] < a.T ? expf(sv[it] - mx) : 0.0f;
+        for (int it = 0; it < LPT; ++it) {
+            if (tok[it] < a.T) {
+                const float u = expf(sv[it] - mx);
+                a.scores[h * a.T + tok[it]] = u;
+                e += u;
+            }
+        }
     }
     e = warp_sum(e);
     if (lane == 0 && w < a.NW) *reinterpret_cast<float2 *>(a.stats + (h * a.NW + w) * 2) = make_float2(mx, e);
@@ -289,16 +297,18 @@ __global__ __launch_bounds__(kPT) void attn_pv_kernel(AArgs a) {
             e[k] = *reinterpret_cast<const float2 *>(st + 2 * (i < a.NW ? i : 0));
         }
     };
-    float sc[16];
+    float sc[16], mw;                          // the block's u values and its wave's max
     uint4 cw[8];
     uint16_t s2[8];                            // widened where used (not ahead of the tile loop)
     auto tile_loads = [&](int64_t t0, int nt) {
-        const float4 *sp = reinterpret_cast<const float4 *>(a.scores + h * a.T + t0 + (16 * tid < nt ? 16 * tid : 0));
+        const int64_t b0 = t0 + (16 * tid < nt ? 16 * tid : 0);
+        const float4 *sp = reinterpret_cast<const float4 *>(a.scores + h * a.T + b0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float4 t = sp[i];
             sc[4 * i] = t.x; sc[4 * i + 1] = t.y; sc[4 * i + 2] = t.z; sc[4 * i + 3] = t.w;
         }
+        mw = st[2 * (b0 / 64)];
         asm volatile("" ::: "memory");          // keep the scores ahead of the Vt stream
         const int64_t tf = t0 + (32 * sl + 32 <= nt ? 32 * sl : 0);
 #pragma unroll
@@ -360,9 +370,11 @@ __global__ __launch_bounds__(kPT) void attn_pv_kernel(AArgs a) {
         if (t0 > 0) tile_loads(t0, nt);
         // this thread's block of 16 probabilities (+ residue) into LDS
         if (16 * tid < nt) {
+            // p = exp(s - m) / l, evaluated as u exp(m_w - m) / l: the factor once per block
+            const float cwl = expf(mw - m) / l;
             float p[16], o[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) p[i] = expf(sc[i] - m) / l;
+            for (int i = 0; i < 16; ++i) p[i] = sc[i] * cwl;
             quant_block_aug(p, Sp, a.comp != 0, o);
 #pragma unroll
             for (int i = 0; i < 16; i += 4)
