@@ -397,11 +397,21 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
 
 namespace {
 
-nvfp4_status check_mx(const nvfp4_mx_tensor *t, int64_t rows, int64_t K) {
+int64_t mx_tiled_ldc(int64_t K) { return (K + 511) / 512 * 4096; }
+int64_t mx_tiled_lds(int64_t K) { return (K + 511) / 512 * 256; }
+
+nvfp4_status check_mx(const nvfp4_mx_tensor *t, int64_t rows, int64_t K, bool allow_tiled = false) {
     if (!t) return NVFP4_ERR_NULL;
+    if (t->layout != NVFP4_LAYOUT_ROWMAJOR && t->layout != NVFP4_LAYOUT_TILED) return NVFP4_ERR_SHAPE;
+    if (t->layout == NVFP4_LAYOUT_TILED && !allow_tiled) return NVFP4_ERR_UNSUPPORTED;
     if (t->rows != rows || t->K != K || rows < 0 || K < 0 || K % 32) return NVFP4_ERR_SHAPE;
     if (rows == 0 || K == 0) return NVFP4_OK;
     if (!t->codes || !t->scales) return NVFP4_ERR_NULL;
+    if (t->layout == NVFP4_LAYOUT_TILED) {
+        if (t->ld_codes != mx_tiled_ldc(K) || t->ld_scales != mx_tiled_lds(K)) return NVFP4_ERR_SHAPE;
+        if (!aligned(t->codes, 16)) return NVFP4_ERR_ALIGN;
+        return NVFP4_OK;
+    }
     if (t->ld_codes < K / 2 || t->ld_scales < K / 32) return NVFP4_ERR_SHAPE;
     if (t->ld_codes % 16 || !aligned(t->codes, 16)) return NVFP4_ERR_ALIGN;
     return NVFP4_OK;
@@ -461,8 +471,9 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, i
     if (yt != NVFP4_BF16 && yt != NVFP4_FP32) return NVFP4_ERR_DTYPE;
     const int64_t M = a->rows, N = w->rows, K = w->K, S = residue_cols;
     if (S < 0 || S > K || S % 32) return NVFP4_ERR_SHAPE;
-    CHECK(check_mx(w, N, K));
+    CHECK(check_mx(w, N, K, true));
     CHECK(check_mx(a, M, K + S));
+    if (w->layout == NVFP4_LAYOUT_TILED && M > 64) return NVFP4_ERR_UNSUPPORTED;   // the tile kernel reads rows
     if (!y && M > 0 && N > 0) return NVFP4_ERR_NULL;
     if (ldy < N) return NVFP4_ERR_SHAPE;
     // the partials go after the header, which this product leaves untouched (the
@@ -473,11 +484,27 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, i
     MXGemmLaunch g;
     g.a_codes = a->codes; g.a_ldc = a->ld_codes; g.a_scales = a->scales; g.a_lds = a->ld_scales;
     g.w_codes = w->codes; g.w_ldc = w->ld_codes; g.w_scales = w->scales; g.w_lds = w->ld_scales;
+    g.w_tiled = w->layout == NVFP4_LAYOUT_TILED;
     g.M = M; g.N = N; g.K = K; g.res_cols = S;
     g.y = y; g.yt = yt; g.ldy = ldy;
     g.scratch = need > 0 ? static_cast<uint8_t *>(ws) + kHeaderBytes : nullptr;
     g.scratch_bytes = need > 0 ? ws_bytes - kHeaderBytes : 0;
     const hipError_t e = launch_mx_gemm(g, static_cast<hipStream_t>(stream));   // K == 0 stores zeros
+    return e == hipSuccess ? NVFP4_OK : hip_fail(e);
+}
+
+nvfp4_status nvfp4_mx_pack_tiled(const nvfp4_mx_tensor *src, const nvfp4_mx_tensor *dst, void *stream) {
+    if (!src || !dst) return NVFP4_ERR_NULL;
+    CHECK(check_mx(src, src->rows, src->K));
+    if (dst->layout != NVFP4_LAYOUT_TILED) return NVFP4_ERR_SHAPE;
+    CHECK(check_mx(dst, src->rows, src->K, true));
+    if (src->rows > 0 && src->K > 0 && (src->codes == dst->codes || src->scales == dst->scales))
+        return NVFP4_ERR_SHAPE;
+    MXPackLaunch g;
+    g.src_codes = src->codes; g.src_ldc = src->ld_codes; g.src_scales = src->scales; g.src_lds = src->ld_scales;
+    g.dst_codes = dst->codes; g.dst_ldc = dst->ld_codes; g.dst_scales = dst->scales; g.dst_lds = dst->ld_scales;
+    g.rows = src->rows; g.K = src->K;
+    const hipError_t e = launch_mx_pack_tiled(g, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);
 }
 
@@ -540,7 +567,7 @@ const char *nvfp4_status_string(nvfp4_status s) {
 }
 
 const char *nvfp4_last_error(void) { return g_last_error; }
-int nvfp4_version(void) { return 10200; }
+int nvfp4_version(void) { return 10300; }
 
 int nvfp4_host_e4m3_encode(float v) { return (int)e4m3_rne_sat(v); }
 int nvfp4_host_e2m1_encode(float q) { return (int)(e2m1_rne_sat(std::fabs(q)) | ((f2u(q) >> 31) << 3)); }

@@ -104,6 +104,16 @@ struct PackLaunch {
 };
 hipError_t launch_pack_tiled(const PackLaunch &g, hipStream_t st);
 
+// Row-major MXFP4 -> tiled MX layout (items of 16 rows x 512 columns).
+struct MXPackLaunch {
+    const uint8_t *src_codes; int64_t src_ldc;
+    const uint8_t *src_scales; int64_t src_lds;
+    uint8_t *dst_codes; int64_t dst_ldc;
+    uint8_t *dst_scales; int64_t dst_lds;
+    int64_t rows, K;
+};
+hipError_t launch_mx_pack_tiled(const MXPackLaunch &g, hipStream_t st);
+
 // MXFP4 (E2M1 codes, one E8M0 byte per 32 elements along K, no tensor scale).
 struct MXQuantLaunch {
     const void *x; int xt; int64_t rows, K, ldx;
@@ -120,6 +130,7 @@ struct MXGemmLaunch {
     const uint8_t *a_scales; int64_t a_lds;
     const uint8_t *w_codes; int64_t w_ldc;
     const uint8_t *w_scales; int64_t w_lds;
+    int w_tiled;                            // W in the tiled MX layout (M <= 64 only)
     int64_t M, N, K, res_cols;
     void *y; int yt; int64_t ldy;
     void *scratch; size_t scratch_bytes;    // mx_workspace_bytes()

@@ -162,6 +162,7 @@ struct MXDArgs {
     int64_t M, N, K, res;
     void *y; int yt; int64_t ldy;
     int64_t NT;
+    int w_tiled;                               // W in the tiled MX layout
 };
 
 template <int TW, int MT>
@@ -171,7 +172,7 @@ struct MXStep {
     uint32_t mask;                             // ~0: the lane's block holds data; 0: masked
 };
 
-template <int TW, int MT, int D, int NS>
+template <int TW, int MT, int D, int NS, bool TILED>
 __global__ __launch_bounds__(256) void mx_small_kernel(MXDArgs a) {
     __shared__ float4v red[4][TW * MT][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,10 +189,18 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MXDArgs a) {
     const uint8_t *wrow_c[TW], *wrow_s[TW], *arow_c[MT], *arow_s[MT];
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
-        int64_t n = 16 * (t0 + t) + r16;
-        n = n < a.N ? n : a.N - 1;
-        wrow_c[t] = a.w_codes + n * a.w_ldc;
-        wrow_s[t] = a.w_scales + n * a.w_lds;
+        if (TILED) {
+            // tile t0 + t (clamped: tiles past N are never stored); this lane's
+            // 16 bytes and E8M0 byte of every step sit at fixed offsets in it
+            const int64_t tile = t0 + t < a.NT ? t0 + t : a.NT - 1;
+            wrow_c[t] = a.w_codes + tile * a.w_ldc + 16 * lane;
+            wrow_s[t] = a.w_scales + tile * a.w_lds + lane;
+        } else {
+            int64_t n = 16 * (t0 + t) + r16;
+            n = n < a.N ? n : a.N - 1;
+            wrow_c[t] = a.w_codes + n * a.w_ldc;
+            wrow_s[t] = a.w_scales + n * a.w_lds;
+        }
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -209,10 +218,14 @@ __global__ __launch_bounds__(256) void mx_small_kernel(MXDArgs a) {
         const bool ok = kw < (main ? a.K : a.res);
         const int64_t cw = ok ? kw / 2 : 0, ca = ok ? ka / 2 : 0, bw = ok ? kw / 32 : 0, ba = ok ? ka / 32 : 0;
         st.mask = ok ? ~0u : 0u;
+        // tiled: weight step sw = kw / 128 of the lane's tile, in lane order (steps
+        // past the data read the tile's first step; the mask zeroes them)
+        const int64_t sw = ok ? (kw - 32 * g) / 128 : 0;
+        const int64_t tc = (sw >> 2) * 4096 + 1024 * (sw & 3), ts = (sw >> 2) * 256 + 64 * (sw & 3);
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
-            st.b[t] = *reinterpret_cast<const uint4 *>(wrow_c[t] + cw);
-            st.sb[t] = wrow_s[t][bw];
+            st.b[t] = *reinterpret_cast<const uint4 *>(wrow_c[t] + (TILED ? tc : cw));
+            st.sb[t] = wrow_s[t][TILED ? ts : bw];
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -289,9 +302,17 @@ template <int TW, int MT>
 hipError_t run_small(const MXDArgs &a, hipStream_t st) {
     const int64_t G = (a.NT + TW - 1) / TW;
     const int64_t per = ((a.K + 127) / 128 + (a.res + 127) / 128 + 3) / 4;
-    if (per <= 8) mx_small_kernel<TW, MT, 4, 8><<<dim3((unsigned)G), dim3(256), 0, st>>>(a);
-    else if (per <= 16) mx_small_kernel<TW, MT, 4, 16><<<dim3((unsigned)G), dim3(256), 0, st>>>(a);
-    else mx_small_kernel<TW, MT, 4, 32><<<dim3((unsigned)G), dim3(256), 0, st>>>(a);
+#define MXS(NS, TL) mx_small_kernel<TW, MT, 4, NS, TL><<<dim3((unsigned)G), dim3(256), 0, st>>>(a)
+    if (a.w_tiled) {
+        if (per <= 8) MXS(8, true);
+        else if (per <= 16) MXS(16, true);
+        else MXS(32, true);
+    } else {
+        if (per <= 8) MXS(8, false);
+        else if (per <= 16) MXS(16, false);
+        else MXS(32, false);
+    }
+#undef MXS
     return hipGetLastError();
 }
 
@@ -533,6 +554,7 @@ hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st) {
     a.M = g.M; a.N = g.N; a.K = g.K; a.res = g.res_cols;
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
     a.NT = (g.N + 15) / 16;
+    a.w_tiled = g.w_tiled;
     const bool wide = a.NT >= 512;          // two tiles per workgroup once there are enough of them
     if (g.M <= 16) return wide ? run_small<2, 1>(a, st) : run_small<1, 1>(a, st);
     if (g.M <= 32) return wide ? run_small<2, 2>(a, st) : run_small<1, 2>(a, st);

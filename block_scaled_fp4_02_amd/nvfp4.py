@@ -45,7 +45,7 @@ _lib = None
 _lock = threading.Lock()
 
 EXPORTS = ["nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_mx_quantize",
-           "nvfp4_mx_gemm", "nvfp4_decode_attention", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
+           "nvfp4_mx_gemm", "nvfp4_mx_pack_tiled", "nvfp4_decode_attention", "nvfp4_pack_tiled", "nvfp4_channel_absmax",
            "nvfp4_perm_from_absmax", "nvfp4_workspace_size", "nvfp4_status_string",
            "nvfp4_last_error", "nvfp4_version", "nvfp4_host_e4m3_encode", "nvfp4_host_e2m1_encode"]
 
@@ -66,6 +66,7 @@ def lib():
             L.nvfp4_pack_tiled.argtypes = [vp, vp, vp]
             L.nvfp4_mx_quantize.argtypes = [vp, C.c_int, i64, i64, i64, i64, vp, vp]
             L.nvfp4_mx_gemm.argtypes = [vp, vp, i64, vp, C.c_int, i64, vp, sz, vp]
+            L.nvfp4_mx_pack_tiled.argtypes = [vp, vp, vp]
             L.nvfp4_decode_attention.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, i64, C.c_int, vp, i64,
                                                  vp, sz, vp]
             L.nvfp4_channel_absmax.argtypes = [vp, C.c_int, i64, i64, i64, vp, C.c_float, vp, vp, sz, vp]
@@ -78,7 +79,7 @@ def lib():
             L.nvfp4_host_e4m3_encode.argtypes = [C.c_float]
             L.nvfp4_host_e2m1_encode.argtypes = [C.c_float]
             for name in ("nvfp4_quantize", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvfp4_gemm_residue", "nvfp4_pack_tiled",
-                         "nvfp4_mx_quantize", "nvfp4_mx_gemm", "nvfp4_decode_attention",
+                         "nvfp4_mx_quantize", "nvfp4_mx_gemm", "nvfp4_mx_pack_tiled", "nvfp4_decode_attention",
                          "nvfp4_channel_absmax", "nvfp4_perm_from_absmax"):
                 getattr(L, name).restype = C.c_int
             _lib = L
@@ -329,15 +330,19 @@ def calibrate_perm(x_cal: torch.Tensor, gamma=None, eps: float = 1e-6) -> torch.
 
 class _CMXTensor(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("ld_codes", C.c_int64), ("scales", C.c_void_p),
-                ("ld_scales", C.c_int64), ("rows", C.c_int64), ("K", C.c_int64)]
+                ("ld_scales", C.c_int64), ("rows", C.c_int64), ("K", C.c_int64), ("layout", C.c_int32)]
 
 
 class MXTensor:
     """Device MXFP4 tensor: codes [rows, ld_codes] u8 (E2M1 nibbles), scales [rows, ld_scales]
-    u8 (E8M0, one per 32 columns); no tensor scale."""
+    u8 (E8M0, one per 32 columns); no tensor scale. A tiled tensor (layout 1, weights of the
+    M <= 64 product) stores ceil(rows/16) strips of ld_codes / ld_scales bytes and keeps its
+    logical row count in `nrows`."""
 
-    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, K: int):
-        self.codes, self.scales, self.K = codes, scales, K
+    def __init__(self, codes: torch.Tensor, scales: torch.Tensor, K: int, layout: int = ROWMAJOR,
+                 nrows: int | None = None):
+        self.codes, self.scales, self.K, self.layout = codes, scales, K, layout
+        self.nrows = codes.shape[0] if nrows is None else nrows
 
     @staticmethod
     def empty(rows: int, K: int, device="cuda") -> "MXTensor":
@@ -345,16 +350,23 @@ class MXTensor:
         return MXTensor(torch.empty((rows, ldc), dtype=torch.uint8, device=device),
                         torch.empty((rows, lds), dtype=torch.uint8, device=device), K)
 
+    @staticmethod
+    def empty_tiled(rows: int, K: int, device="cuda") -> "MXTensor":
+        ku, nt = max((K + 511) // 512, 1), max((rows + 15) // 16, 1)
+        return MXTensor(torch.empty((nt, ku * 4096), dtype=torch.uint8, device=device),
+                        torch.empty((nt, ku * 256), dtype=torch.uint8, device=device), K, TILED, rows)
+
     @property
     def rows(self) -> int:
-        return self.codes.shape[0]
+        return self.nrows
 
     def c(self) -> _CMXTensor:
         return _CMXTensor(self.codes.data_ptr(), self.codes.stride(0), self.scales.data_ptr(), self.scales.stride(0),
-                          self.rows, self.K)
+                          self.rows, self.K, self.layout)
 
     def host(self):
-        """(codes [rows, K/2], scales [rows, K/32]) as numpy arrays on the host."""
+        """(codes [rows, K/2], scales [rows, K/32]) as numpy arrays on the host (row-major only)."""
+        assert self.layout == ROWMAJOR, "host() reads the row-major layout"
         return self.codes[:, : self.K // 2].cpu().numpy(), self.scales[:, : self.K // 32].cpu().numpy()
 
 
@@ -367,6 +379,14 @@ def mx_quantize(x: torch.Tensor, residue_cols: int = 0) -> MXTensor:
     ct = out.c()
     _check(lib().nvfp4_mx_quantize(_ptr(x), _dtype_code(x), rows, K, max(x.stride(0), K), int(residue_cols), C.byref(ct),
                                    _stream()), "nvfp4_mx_quantize")
+    return out
+
+
+def mx_pack_tiled(w: MXTensor) -> MXTensor:
+    """The tiled copy of a row-major MXFP4 weight (nvfp4_mx_pack_tiled), on the current stream."""
+    out = MXTensor.empty_tiled(w.rows, w.K, device=w.codes.device)
+    src, dst = w.c(), out.c()
+    _check(lib().nvfp4_mx_pack_tiled(C.byref(src), C.byref(dst), _stream()), "nvfp4_mx_pack_tiled")
     return out
 
 

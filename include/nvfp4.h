@@ -193,12 +193,24 @@ nvfp4_status nvfp4_gemm_residue(const void *x, int xt, int64_t M, int64_t K, int
  * block); code = E2M1(x * 2^-e) round to nearest even, saturating at 6, sign
  * of x. gfx950's scaled FP4 matrix instructions consume these blocks as they
  * are stored.
- * Canonical storage: codes rows x ld_codes bytes (ld_codes >= K/2, multiple
- * of 16, 16-byte aligned pointer); scales rows x ld_scales bytes (>= K/32). */
+ * Canonical storage (layout = NVFP4_LAYOUT_ROWMAJOR): codes rows x ld_codes
+ * bytes (ld_codes >= K/2, multiple of 16, 16-byte aligned pointer); scales
+ * rows x ld_scales bytes (>= K/32).
+ * Tiled storage (weights of the M <= 64 product; layout = NVFP4_LAYOUT_TILED),
+ * the order in which that product reads them, so that each of its loads is one
+ * contiguous run: items of 16 rows x 512 columns; item (t, u) lives at
+ * codes + t*ld_codes + u*4096 and scales + t*ld_scales + u*256, with
+ * ld_codes = KU*4096, ld_scales = KU*256, KU = ceil(K/512). Inside an item, for
+ * the 128-column step i < 4 and p = 0..63 with r = p % 16, g = p / 16:
+ *   codes  byte 1024*i + 16*p + j  (j < 16) = byte j of the canonical codes of
+ *          row 16t+r starting at column 512u + 128i + 32g;
+ *   scales byte 64*i + p = the E8M0 byte of that 32-column block.
+ * Rows >= rows and columns >= K hold zero codes (and zero scale bytes). */
 typedef struct {
     uint8_t *codes;  int64_t ld_codes;
     uint8_t *scales; int64_t ld_scales;
     int64_t  rows, K;      /* K % 32 == 0 */
+    int32_t  layout;       /* nvfp4_layout; only W of nvfp4_mx_gemm at M <= 64 may be tiled */
 } nvfp4_mx_tensor;
 
 /* MXFP4-quantize x (rows x K_in, dtype xt, ldx) into `out` (rows x (K_in + S)).
@@ -218,7 +230,8 @@ nvfp4_status nvfp4_mx_quantize(const void *x, int xt, int64_t rows, int64_t K_in
  * even), leading dimension ldy. Workspace: nvfp4_workspace_size(4, M, N, K, S)
  * bytes; its first 8 KiB (the counter header the NVFP4 entry points keep) are
  * never written, so one workspace can serve both formats. When the product needs
- * no split-K partials, ws may be NULL. */
+ * no split-K partials, ws may be NULL. W may be tiled (nvfp4_mx_pack_tiled) when
+ * M <= 64; a tiled W at M > 64, or a tiled A, is NVFP4_ERR_UNSUPPORTED. */
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor *a, const nvfp4_mx_tensor *w, int64_t residue_cols,
                            void *y, int yt, int64_t ldy, void *ws, size_t ws_bytes, void *stream);
 
@@ -257,6 +270,13 @@ nvfp4_status nvfp4_decode_attention(const void *q, int qt, int64_t H, int64_t D,
  * scales buffers hold ceil(rows/16) strips). The tensor scale is copied.
  * A one-time layout change of static weights: values are not touched. */
 nvfp4_status nvfp4_pack_tiled(const nvfp4_tensor *src, const nvfp4_tensor *dst, void *stream);
+
+/* Rewrite the row-major MXFP4 weight `src` into the tiled MX layout `dst` (same
+ * rows and K; dst->layout = NVFP4_LAYOUT_TILED, dst->ld_codes = KU*4096,
+ * dst->ld_scales = KU*256; its buffers hold ceil(rows/16) strips). A one-time
+ * layout change of static weights for the M <= 64 MXFP4 product; values are not
+ * touched. Shape or layout errors: NVFP4_ERR_SHAPE; misaligned: NVFP4_ERR_ALIGN. */
+nvfp4_status nvfp4_mx_pack_tiled(const nvfp4_mx_tensor *src, const nvfp4_mx_tensor *dst, void *stream);
 
 /* Calibration statistic for the outlier reorder (ARCQuant article, sections 3.1
  * and 6.1): absmax_out[j] = max over rows of |RMSNorm(x)[:, j]| (|x| when

@@ -103,6 +103,65 @@ def test_mx_gemm_ragged(nv, orc, M, N, K, S):
     assert bf16_bound_ok(yb.float().cpu().numpy(), ref)
 
 
+def _mx_tiled_host(codes, scales, rows, K):
+    """The tiled MX weight layout as nvfp4.h defines it, written out on the host from
+    the row-major bytes: item (t, u), step i, lane p = 16 g + r."""
+    ku, nt = (K + 511) // 512, (rows + 15) // 16
+    tc = np.zeros((nt, ku * 4096), np.uint8)
+    ts = np.zeros((nt, ku * 256), np.uint8)
+    for t in range(nt):
+        for u in range(ku):
+            for i in range(4):
+                for p in range(64):
+                    n, k = 16 * t + p % 16, 512 * u + 128 * i + 32 * (p // 16)
+                    if n < rows and k < K:
+                        o = u * 4096 + 1024 * i + 16 * p
+                        tc[t, o:o + 16] = codes[n, k // 2:k // 2 + 16]
+                        ts[t, u * 256 + 64 * i + p] = scales[n, k // 32]
+    return tc, ts
+
+
+@pytest.mark.parametrize("rows,K", [(1, 32), (16, 512), (40, 1056), (3, 4128)])
+def test_mx_tiled_layout(nv, rows, K):
+    """nvfp4_mx_pack_tiled writes the bytes of the tiled MX layout, zeros past the tensor."""
+    w = inputs.small_random(900 + rows + K, rows, K, scale=0.02)
+    note(f"mx pack tiled rows={rows} K={K}")
+    wq = nv.mx_quantize(w.to(DEV))
+    wt = nv.mx_pack_tiled(wq)
+    torch.cuda.synchronize()
+    c, sc = wq.host()
+    tc, ts = _mx_tiled_host(c, sc, rows, K)
+    assert np.array_equal(wt.codes.cpu().numpy(), tc), "tiled codes"
+    assert np.array_equal(wt.scales.cpu().numpy(), ts), "tiled scales"
+
+
+@pytest.mark.parametrize("M,N,K,S", [(1, 300, 1056, 0), (8, 47, 544, 32), (16, 8192, 4096, 0), (2, 14336, 4096, 0),
+                                     (4, 4096, 14336, 0), (16, 1000, 4128, 2048), (17, 300, 1056, 64),
+                                     (33, 130, 160, 32), (64, 700, 4096, 256)])
+def test_mx_tiled_same_result(nv, M, N, K, S):
+    """The M <= 64 product on tiled MX weights gives the row-major weights' result bit
+    for bit (the same steps in the same order; only the load addresses differ)."""
+    x = inputs.small_random(800 + M, M, K)
+    w = inputs.small_random(801 + N, N, K, scale=0.02)
+    note(f"mx tiled product M={M} N={N} K={K} S={S}")
+    aq = nv.mx_quantize(x.to(DEV), residue_cols=S)
+    wq = nv.mx_quantize(w.to(DEV))
+    wt = nv.mx_pack_tiled(wq)
+    y = nv.mx_gemm(aq, wq, residue_cols=S)
+    yt = nv.mx_gemm(aq, wt, residue_cols=S)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yt)
+
+
+def test_mx_tiled_needs_small_m(nv):
+    """A tiled MX weight is refused above M = 64 (the tile kernel reads row-major weights)."""
+    wt = nv.mx_pack_tiled(nv.mx_quantize(inputs.small_random(3, 32, 256, scale=0.02).to(DEV)))
+    aq = nv.mx_quantize(inputs.small_random(4, 65, 256).to(DEV))
+    with pytest.raises(nv.NVFP4Error) as e:
+        nv.mx_gemm(aq, wt)
+    assert e.value.status == 6
+
+
 @pytest.mark.parametrize("M", [1, 8, 16])
 def test_mx_residue_compensation(nv, orc, M):
     """The residue-compensated MXFP4 product (K -> 2K, config 3's law) against the oracle,

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.nvfp4_version() == 10200
+    assert L.nvfp4_version() == 10300
     assert L.nvfp4_status_string(0) == b"ok"
     assert L.nvfp4_status_string(5) == b"workspace too small"
 
@@ -209,3 +209,36 @@ def test_decode_attention_argument_errors(L):
     assert call(wsn=n - 1) == 5
     assert call(h=0, k=_tensor(0, D, codes=1 << 20, scales=1 << 21, scale=1 << 22),
                 v=_tensor(0, T, codes=1 << 23, scales=1 << 24, scale=1 << 25)) == 0   # nothing to do
+
+
+def _mx(rows, K, codes=1 << 20, scales=1 << 21, ldc=None, lds=None, layout=0):
+    from block_scaled_fp4_02_amd.nvfp4 import _CMXTensor
+    if layout == 1:
+        ku = (K + 511) // 512
+        dl, ds = ku * 4096, ku * 256
+    else:
+        dl, ds = max(16, (K // 2 + 15) // 16 * 16), max(1, K // 32)
+    return _CMXTensor(codes, ldc if ldc is not None else dl, scales, lds if lds is not None else ds, rows, K, layout)
+
+
+def test_mx_tiled_argument_errors(L):
+    """nvfp4_mx_pack_tiled and the tiled MX weight of nvfp4_mx_gemm: layouts, strides, rows,
+    alignment and the M <= 64 limit are checked before anything is enqueued (fake pointers)."""
+    vp = C.c_void_p
+    src = _mx(40, 1024)
+    dst = _mx(40, 1024, codes=1 << 22, scales=1 << 23, layout=1)
+    pack = lambda s, d: L.nvfp4_mx_pack_tiled(C.byref(s), C.byref(d), None)
+    assert pack(src, _mx(40, 1024, codes=1 << 22, scales=1 << 23)) == 2               # dst not tiled
+    assert pack(src, _mx(40, 1024, codes=1 << 22, scales=1 << 23, layout=1, ldc=4096)) == 2   # KU = 2: 8192
+    assert pack(src, _mx(40, 1024, codes=1 << 22, scales=1 << 23, layout=1, lds=256)) == 2
+    assert pack(src, _mx(41, 1024, codes=1 << 22, scales=1 << 23, layout=1)) == 2      # rows differ
+    assert pack(src, _mx(40, 1024, codes=(1 << 22) + 8, scales=1 << 23, layout=1)) == 3
+    assert pack(_mx(40, 1024, layout=1), dst) == 6                                   # src must be row-major
+    assert pack(src, _mx(40, 1024, codes=1 << 20, scales=1 << 23, layout=1)) == 2      # in place
+    assert pack(src, _mx(40, 1024, codes=1 << 22, scales=1 << 23, layout=2)) == 2      # no such layout
+    y = vp(1 << 26)
+    gemm = lambda a, w: L.nvfp4_mx_gemm(C.byref(a), C.byref(w), 0, y, 1, 40, None, 0, None)
+    assert gemm(_mx(65, 1024, codes=1 << 24, scales=1 << 25), dst) == 6               # tiled W at M > 64
+    assert gemm(_mx(8, 1024, codes=1 << 24, scales=1 << 25, layout=1), dst) == 6      # tiled A
+    assert gemm(_mx(8, 1024, codes=1 << 24, scales=1 << 25), _mx(40, 1024, codes=1 << 22, scales=1 << 23,
+                                                                   layout=1, ldc=4096)) == 2
