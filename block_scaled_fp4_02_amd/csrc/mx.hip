@@ -555,7 +555,11 @@ hipError_t launch_mx_gemm(const MXGemmLaunch &g, hipStream_t st) {
     a.y = g.y; a.yt = g.yt; a.ldy = g.ldy;
     a.NT = (g.N + 15) / 16;
     a.w_tiled = g.w_tiled;
-    const bool wide = a.NT >= 512;          // two tiles per workgroup once there are enough of them
+    // two tiles per workgroup (one activation load feeds both) once there are enough
+    // tiles: from 512, or from 384 when M > 2 (measured on the N = 6144 sweep shape:
+    // M = 16 9.1 -> 7.4 us, M = 1 5.7 -> 6.3 us; at N = 4096 the halved workgroup
+    // count loses)
+    const bool wide = a.NT >= 512 || (g.M > 2 && a.NT >= 384);
     if (g.M <= 16) return wide ? run_small<2, 1>(a, st) : run_small<1, 1>(a, st);
     if (g.M <= 32) return wide ? run_small<2, 2>(a, st) : run_small<1, 2>(a, st);
     if (g.M <= 64) return run_small<1, 4>(a, st);

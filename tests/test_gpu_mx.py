@@ -136,6 +136,7 @@ def test_mx_tiled_layout(nv, rows, K):
 
 
 @pytest.mark.parametrize("M,N,K,S", [(1, 300, 1056, 0), (8, 47, 544, 32), (16, 8192, 4096, 0), (2, 14336, 4096, 0),
+                                     (8, 6144, 4096, 0), (3, 6150, 1056, 64),
                                      (4, 4096, 14336, 0), (16, 1000, 4128, 2048), (17, 300, 1056, 64),
                                      (33, 130, 160, 32), (64, 700, 4096, 256)])
 def test_mx_tiled_same_result(nv, M, N, K, S):
