@@ -102,16 +102,6 @@ __device__ inline T add_dev(T *p, T v) { return __hip_atomic_fetch_add(p, v, __A
 
 __device__ inline void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Wait until a workgroup count in LDS reaches n. Bounded, so that a count that
-// never arrives cannot keep the kernel from ending.
-__device__ inline void wait_count(const unsigned *c, unsigned n) {
-#pragma clang loop unroll(disable)
-    for (unsigned it = 0; it < (1u << 24); ++it) {
-        if (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= n) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 // ------------------------------------------------------------ weight items
 struct WLoad {
     uint4 c[4];
@@ -372,10 +362,7 @@ __device__ inline void zero_unwritten(half8 *lds, const DArgs &a, const Range &r
 // STK: residue rows stacked under the activation rows (RES; M <= 8 in one row
 // tile, or M = 9..16 as a second row tile); an instance of its own, so that its
 // MFMA loop carries no residue branch.
-// STG: LOCAL plans whose producer threads take two or more chunk steps publish
-// the operand step by step (an instance of its own: the per-item readiness test
-// slows the item loop of the other plans).
-template <int MT, bool RES, bool TILED, bool STK, bool STG>
+template <int MT, bool RES, bool TILED, bool STK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_kernel(DArgs a) {
     constexpr int kRing = MT == 1 ? 4 : 3;       // weight items in flight per consumer wave
@@ -383,12 +370,10 @@ void decode_kernel(DArgs a) {
     // after it, so that computing on landed items overlaps the (throttled)
     // issue of later loads.
     constexpr int kPre = kPreItems < kRing ? kPreItems : kRing;
-    const bool staged = STG && a.mode == MODE_LOCAL;
     extern __shared__ half8 lds_a[];          // operand [U][4 i][4 j][4 g][M] (+ residue copy); then tile sums
     __shared__ float sh_S, sh_wS;             // activation and weight tensor scales
     __shared__ float sh_part[kProd];
     __shared__ unsigned sh_cnt;
-    __shared__ unsigned sh_step[kLocalChunks];   // LOCAL: producer waves done with chunk step t
     __shared__ int sh_last;
     // wave index as a scalar: branches on it are uniform (barriers inside them stay per wave)
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -449,11 +434,7 @@ void decode_kernel(DArgs a) {
     // flight.
     TL(0);
     WLoad ring[kRing];
-    if (tid == 0) {
-        sh_cnt = 0;
-#pragma unroll
-        for (int t = 0; t < kLocalChunks; ++t) sh_step[t] = 0;
-    }
+    if (tid == 0) sh_cnt = 0;
     if (wave < kCons) {
         // Ordered launches wait until the producers' loads are out, so that the
         // operand lands ahead of the weight stream (LOCAL always: the barrier
@@ -465,7 +446,7 @@ void decode_kernel(DArgs a) {
             for (int s = 0; s < kPre; ++s) load_item(s < nitems ? s : 0, ring[s], s >= nitems);
         }
         TL(1);
-        if (!staged) __syncthreads();          // operand complete (else published step by step, below)
+        __syncthreads();                       // operand complete
     } else {
         const int ptid = tid - 64 * kCons, pw = wave - kCons;
         if (a.mode == MODE_PRE) {
@@ -616,9 +597,6 @@ void decode_kernel(DArgs a) {
             }
             if (blockIdx.x == 0 && ptid == 0) *a.q_S = S;
             if (ptid == 0) { sh_S = S; sh_wS = wS; }
-            // Step t (chunk t of every thread: positions step t .. step (t + 1) - 1 of
-            // every row) is published on its own, so the consumers start on the
-            // first units while later ones are still being encoded.
 #pragma unroll
             for (int t = 0; t < kLocalChunks; ++t) {
                 const int pos = pm.p0 + pm.step * t;
@@ -627,21 +605,14 @@ void decode_kernel(DArgs a) {
                     xchunk_quantize<RES>(a, lds_a, slots, kbeg, rg.rend, pm.m, f.col, (f.key & kV1) != 0, xc[t], S,
                                          q == 0);
                 }
-                // every producer wave counts every step, with or without chunks
-                if (lane == 0) __hip_atomic_fetch_add(&sh_step[t], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
             TL(1);
-            if (!staged) __syncthreads();      // operand complete
+            __syncthreads();                   // operand complete
         }
     }
     TL(2);
 
     // ---- consumers: decode weights, MFMA
-    // LOCAL: the operand arrives in steps; step 0 also carries the tensor scales.
-    // A wave needs step t once an item's unit reaches positions step t and up.
-    const int pstep = kPThreads / M;
-    int ready = 0;                             // steps known complete
-    if (staged && wave < kCons && nitems > 0) wait_count(&sh_step[0], kProd);
     const float scale = sh_S * sh_wS;
     // Output tile t of this workgroup: lane holds rows 16 mt + 4 g + e of column
     // 16 t + r16; only rows < M are stored.
@@ -718,12 +689,6 @@ void decode_kernel(DArgs a) {
                 const int s = it % kRing;
                 if (it < nitems) {
                     const int ul = uo + KW * bu;
-                    if (staged && ready + 1 < kLocalChunks && 16 * ul + 15 >= (ready + 1) * pstep) {
-                        // steps complete in order in every producer wave: the last one needed suffices
-                        const int need = min((16 * ul + 15) / pstep, kLocalChunks - 1);
-                        wait_count(&sh_step[need], kProd);
-                        ready = need;
-                    }
                     const half8 *abase = lds_a + ul * 64 * R + g * R;
                     const bool res_u = RES && !STK && ul < res_units;   // a separate residue copy
 #pragma unroll
@@ -851,7 +816,7 @@ void decode_kernel(DArgs a) {
                         if (p0 + k < a.P) { s0 += v0[k]; s1 += v1[k]; }
                 }
                 for (int c = 0; c < 2 && n + c < a.N; ++c) {
-                    const float v = (c ? s1 : s0) * (sh_S * sh_wS);   // after the barriers: every wave
+                    const float v = (c ? s1 : s0) * scale;
                     if (a.yt == 1) static_cast<float *>(a.y)[m * a.ldy + n + c] = v;
                     else static_cast<uint16_t *>(a.y)[m * a.ldy + n + c] = f32_to_bf16_rne(v);
                 }
@@ -1116,7 +1081,7 @@ void decode_win_kernel(DArgs a) {
 }
 
 // ---------------------------------------------------------------- planning
-struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool ordered, staged; int64_t NT, Q; size_t lds; };
+struct Plan { int MT, U, P, T, tw, KW, G, mode, Rr, Mp; bool ordered; int64_t NT, Q; size_t lds; };
 
 constexpr size_t kLdsPerCu = 160 * 1024;       // gfx950
 constexpr size_t kLdsStatic = 256;             // the kernel's own __shared__ words, rounded up
@@ -1135,20 +1100,19 @@ int cu_count() {
 }
 
 template <bool TILED>
-const void *kernel_ptr_t(int MT, bool res, bool stk, bool stg) {
+const void *kernel_ptr_t(int MT, bool res, bool stk) {
     if (MT == 1) {
-        if (!res) return stg ? reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, false, true>)
-                             : reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, false, false>);
-        return stk ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, true, false>)
-                   : reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, false, false>);
+        if (!res) return reinterpret_cast<const void *>(&decode_kernel<1, false, TILED, false>);
+        return stk ? reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, true>)
+                   : reinterpret_cast<const void *>(&decode_kernel<1, true, TILED, false>);
     }
-    if (!res) return reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, false, false>);
-    return stk ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, true, false>)
-               : reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, false, false>);
+    if (!res) return reinterpret_cast<const void *>(&decode_kernel<2, false, TILED, false>);
+    return stk ? reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, true>)
+               : reinterpret_cast<const void *>(&decode_kernel<2, true, TILED, false>);
 }
 
-const void *kernel_ptr(int MT, bool res, bool tiled, bool stk, bool stg) {
-    return tiled ? kernel_ptr_t<true>(MT, res, stk, stg) : kernel_ptr_t<false>(MT, res, stk, stg);
+const void *kernel_ptr(int MT, bool res, bool tiled, bool stk) {
+    return tiled ? kernel_ptr_t<true>(MT, res, stk) : kernel_ptr_t<false>(MT, res, stk);
 }
 
 // Work split of one call. A K range of U units (P ranges) costs its operand in
@@ -1229,10 +1193,6 @@ Plan plan_compute(int64_t M, int64_t N, int64_t K, int64_t res_cols, bool raw_x,
     // per thread on, racing wins at one).
     const int64_t pre_per_thread = (((kc + 31) / 32) * (res_cols > 0 ? 2 : 1) + step - 1) / step;
     pl.ordered = pl.mode == MODE_LOCAL || pre_per_thread > 1;
-    // LOCAL with two or more chunk steps per producer thread: the consumers start
-    // on the first step's units while later steps are encoded (one row tile, no
-    // residue columns: the instance that exists)
-    pl.staged = pl.mode == MODE_LOCAL && pl.MT == 1 && !res && per_thread >= 2;
     return pl;
 }
 
@@ -1345,7 +1305,7 @@ hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
     a.U = pl.U; a.P = pl.P; a.T = pl.T; a.tw = pl.tw; a.KW = pl.KW; a.G = pl.G; a.mode = pl.mode; a.NT = pl.NT;
     a.Rr = pl.Rr; a.Mp = pl.Mp; a.ordered = pl.ordered ? 1 : 0;
     // stacking (Mp > 0) exists with residue columns only
-    const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.Mp > 0, pl.staged);
+    const void *fn = kernel_ptr(pl.MT, g.res_cols > 0, g.w_tiled != 0, pl.Mp > 0);
     if (pl.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pl.lds);
         if (e != hipSuccess) return e;
