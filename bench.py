@@ -137,6 +137,9 @@ def main():
     ap.add_argument("--roofline-only", action="store_true",
                     help="run only the kernel-alone leg behind the roofline figure (for profiling: then every "
                          "decode-kernel launch of the process belongs to that figure, equally per case)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="run only the timed headline steps and print their line (for a kernel trace of the "
+                         "fused calls as the headline replays them)")
     ap.add_argument("--prefill-case", default="",
                     help="M,K,N: run only the prefill product on pre-quantized activations, --reps launches "
                          "(for profiling the MFMA kernel; prints one line with its time)")
@@ -246,6 +249,11 @@ def main():
         value = step_bytes / sec_per_step / 1e9
         del graphs
         log(f"timed {args.steps} steps: {sec_per_step * 1e6:.1f} us/step, {value:.1f} GB/s")
+        if args.headline_only:
+            print(json.dumps({"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+                              "steps": args.steps, "warmup": args.warmup,
+                              "ms_per_step": round(sec_per_step * 1e3, 5), "mode": "headline-only"}))
+            return
 
     # ---------------- per-case detail: whole call and kernel alone. The kernel-alone leg
     # (pre-quantized activations) launches only the decode kernel, the same number of times

@@ -64,11 +64,11 @@ constexpr int kMaxP = 8;                       // split-K partials loaded at onc
 enum Mode { MODE_PRE = 0, MODE_LOCAL = 1 };
 
 #ifdef NVFP4_TIMELINE
-// Profiling builds only: per (workgroup, wave, point) s_memrealtime stamps (100 MHz).
+// Profiling builds only: per (workgroup, wave < 16, point) s_memrealtime stamps (100 MHz).
 // Internal linkage: the kernel addresses it PC-relative, with no load of its address.
-static __device__ unsigned long long g_timeline[1024 * 8 * 8];
+static __device__ unsigned long long g_timeline[1024 * 16 * 8];
 #define TL(point) do { if ((threadIdx.x & 63) == 0 && blockIdx.x < 1024) \
-    g_timeline[(blockIdx.x * 8 + (threadIdx.x >> 6)) * 8 + (point)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+    g_timeline[(blockIdx.x * 16 + (threadIdx.x >> 6)) * 8 + (point)] = __builtin_amdgcn_s_memrealtime(); } while (0)
 #else
 #define TL(point) do { } while (0)
 #endif
@@ -831,12 +831,13 @@ void decode_kernel(DArgs a) {
 // Four row tiles take 64 rows x 1 KiB of operand per 512-column unit, so a
 // whole K range does not fit in LDS. Here the operand streams through a window
 // of two unit slots instead: a workgroup owns four 16-row weight tiles over all
-// of K (no split-K across workgroups) and consumer wave w takes the 32-column
-// step w of every unit for all four weight tiles and all four row tiles, so each
-// weight item is loaded and decoded once and each operand fragment read once per
-// CU (against a wave per weight tile: operand reads / 4, the M = 64 augmented
-// call 35.4 -> 28.3 us with the deeper weight ring); the four waves' partial
-// tiles are added in LDS in wave order at the end; producers fill the slot of unit k + 2
+// of K (no split-K across workgroups). Its eight consumer waves, two per SIMD,
+// split each unit by 32-column step (wave w % 4) and weight-tile pair (w / 4),
+// for all four row tiles, so each weight item is loaded and decoded once and each
+// operand fragment read twice per CU (against a wave per weight tile: operand
+// reads / 2, the M = 64 augmented call 35.4 -> 28.3 us with the deeper weight
+// ring; eight waves instead of four one step each: 28.5 -> 28.0 us); the waves'
+// partial tiles are added in LDS in step order at the end; producers fill the slot of unit k + 2
 // as soon as the consumers are done with unit k, one workgroup barrier per
 // unit (weight loads run four units ahead, operand loads three). Residue columns (ARCQuant
 // article, sections 3.1-3.2) are further
@@ -909,14 +910,20 @@ __device__ inline void win_unit_load(const DArgs &a, const WinRows &w, int v, in
     }
 }
 
-// A consumer's share of one unit: 32-column step iw of each of four weight tiles.
+// Eight consumer waves (two per SIMD, so that one's MFMAs run while the other
+// decodes or waits) and the four producer waves: twelve waves, 170 VGPRs each.
+constexpr int kWinCons = 8;
+constexpr int kWinTW = 4 * kCons / kWinCons;   // weight tiles per consumer wave
+constexpr int kWinThreads = 64 * (kWinCons + kProd);
+
+// A consumer's share of one unit: 32-column step iw of each of its weight tiles.
 struct WStep {
-    uint4 c[4];
-    uint16_t s[4];                             // the step's two E4M3 bytes per tile
+    uint4 c[kWinTW];
+    uint16_t s[kWinTW];                        // the step's two E4M3 bytes per tile
 };
 
 template <bool TILED, bool RES>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))   // 128 KiB of LDS: one per CU
+__global__ __launch_bounds__(kWinThreads) __attribute__((amdgpu_waves_per_eu(3)))   // 128 KiB of LDS: one per CU
 void decode_win_kernel(DArgs a) {
     constexpr int R = kWinRows, SLOT = 64 * kWinRows;
     extern __shared__ half8 lds_a[];           // [2 slots][64 R]: rows >= M are never read
@@ -926,21 +933,22 @@ void decode_win_kernel(DArgs a) {
     const int KU = (int)((a.K + 511) / 512), RU = RES ? (int)((a.res_cols + 511) / 512) : 0, NV = KU + RU;
 
     TL(0);
-    if (wave < kCons) {
-        // ---- consumer: 32-column step iw = wave of every (virtual) unit, for the
-        // workgroup's four weight tiles and four row tiles: each weight item is loaded
-        // and decoded once per workgroup and each operand fragment read once per CU;
-        // the waves' partial tiles are added in LDS at the end
-        const int iw = wave;
-        const int64_t tb = 4 * (int64_t)blockIdx.x;
-        int64_t tcl[4];                        // tiles clamped into W (tiles past it are not stored)
+    if (wave < kWinCons) {
+        // ---- consumer: 32-column step iw = wave % 4 of every (virtual) unit, for
+        // weight tiles kWinTW (wave / 4) .. of the workgroup's four and all four row
+        // tiles: each weight item is loaded and decoded once per workgroup and each
+        // operand fragment read by 4 / kWinTW waves; the waves' partial tiles are added
+        // in LDS at the end
+        const int iw = wave & 3;
+        const int64_t tb = 4 * (int64_t)blockIdx.x + kWinTW * (wave >> 2);
+        int64_t tcl[kWinTW];                   // tiles clamped into W (tiles past it are not stored)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) tcl[tt] = tb + tt < a.NT ? tb + tt : a.NT - 1;
+        for (int tt = 0; tt < kWinTW; ++tt) tcl[tt] = tb + tt < a.NT ? tb + tt : a.NT - 1;
         const float qS = load_vmem(a.q_S), wS = load_vmem(a.w_S);   // first: no wait holds a weight load on them
         auto issue = [&](int v, WStep &w) {
             const int64_t wu = v < KU ? v : v - KU;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int tt = 0; tt < kWinTW; ++tt) {
                 if (TILED) {
                     // step iw of the item is its own contiguous KiB; its two scale bytes
                     // sit at 2 iw in the lane's eight
@@ -960,9 +968,9 @@ void decode_win_kernel(DArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
             arow[mt] = ((16 * mt + r16 < M ? 16 * mt + r16 : M - 1) + g + 4 * iw) & (kWinRows - 1);
-        float4v acc[4][4];                     // [weight tile][row tile]
+        float4v acc[kWinTW][4];                // [weight tile][row tile]
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < kWinTW; ++tt)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) acc[tt][mt] = float4v{0, 0, 0, 0};
         WStep ring0, ring1, ring2, ring3;      // units v .. v + 3 in flight (v mod 4)
@@ -975,17 +983,17 @@ void decode_win_kernel(DArgs a) {
         TL(1);
         auto step = [&](int v, WStep &w) {
             const half8 *abase = lds_a + (v & 1) * SLOT + g * R;
-            half2v d[4][2];
+            half2v d[kWinTW][2];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int tt = 0; tt < kWinTW; ++tt) {
                 d[tt][0] = scale_pair(w.s[tt] & 0xFFu);
                 d[tt][1] = scale_pair((uint32_t)w.s[tt] >> 8);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                half8 b[4];
+                half8 b[kWinTW];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
+                for (int tt = 0; tt < kWinTW; ++tt) {
                     const uint32_t cw = j == 0 ? w.c[tt].x : j == 1 ? w.c[tt].y : j == 2 ? w.c[tt].z : w.c[tt].w;
                     b[tt] = decode8(cw, d[tt][j >> 1]);
                 }
@@ -994,7 +1002,7 @@ void decode_win_kernel(DArgs a) {
                 for (int mt = 0; mt < 4; ++mt) {
                     const half8 av = abase[fo + arow[mt]];
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
+                    for (int tt = 0; tt < kWinTW; ++tt)
                         acc[tt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[tt], acc[tt][mt], 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);   // one 8-column fragment's operands live at a time
@@ -1011,23 +1019,27 @@ void decode_win_kernel(DArgs a) {
             if (v + 3 < NV) step(v + 3, ring3);
         }
         TL(4);
-        // the four waves' partial tiles, parked in the operand slots and added in wave order
+        // the waves' partial tiles, parked in the operand slots and added in step order:
+        // tile t's parts are held by waves 4 (t / kWinTW) + iw, iw = 0..3, at index
+        // (t % kWinTW) 4 + mt
         float4v *park = reinterpret_cast<float4v *>(lds_a);   // [wave][tt * 4 + mt][lane]: 64 KiB
         __syncthreads();                       // every wave is done with the operand
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < kWinTW; ++tt)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) park[(wave * 16 + tt * 4 + mt) * 64 + lane] = acc[tt][mt];
+            for (int mt = 0; mt < 4; ++mt) park[(wave * 4 * kWinTW + tt * 4 + mt) * 64 + lane] = acc[tt][mt];
         __syncthreads();
-        const int tt = wave;                   // wave w sums and stores weight tile w
-        const int64_t n = 16 * (tb + tt) + r16;
-        if (tb + tt < a.NT && n < a.N) {
+        const int tt = wave;                   // wave w < 4 sums and stores weight tile w
+        const int64_t t4 = 4 * (int64_t)blockIdx.x + tt;
+        const int64_t n = 16 * t4 + r16;
+        const int pw0 = 4 * (tt / kWinTW), pi = (tt % kWinTW) * 4;
+        if (wave < 4 && t4 < a.NT && n < a.N) {
             const float scale = qS * wS;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                float4v sum = park[(tt * 4 + mt) * 64 + lane];
+                float4v sum = park[(pw0 * 4 * kWinTW + pi + mt) * 64 + lane];
 #pragma unroll
-                for (int w2 = 1; w2 < kCons; ++w2) sum += park[(w2 * 16 + tt * 4 + mt) * 64 + lane];
+                for (int w2 = 1; w2 < 4; ++w2) sum += park[((pw0 + w2) * 4 * kWinTW + pi + mt) * 64 + lane];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t row = 16 * mt + 4 * g + e;
@@ -1042,7 +1054,7 @@ void decode_win_kernel(DArgs a) {
     } else {
         // ---- producers: unit v's chunks (row c / 16, position c % 16) into slot v & 1,
         // from register set v mod 3; the loads of unit k + 2 go out while unit k is stored
-        const int ptid = tid - 64 * kCons;
+        const int ptid = tid - 64 * kWinCons;
         QChunk q0[kWinChunks], q1[kWinChunks], q2[kWinChunks];
         const WinRows wr = win_rows(a, ptid);
         auto load_unit = [&](int v, QChunk *q) { win_unit_load<RES>(a, wr, v, KU, q); };
@@ -1257,8 +1269,8 @@ extern "C" int nvfp4_debug_timeline(void *host, size_t bytes) {
 #endif
 
 // M = 33..64: the windowed kernel, four weight tiles per workgroup over all of K
-// (and the residue units), each consumer wave one 32-column step of every unit;
-// quantized activations only.
+// (and the residue units), each of its eight consumer waves one 32-column step of
+// every unit for two of them; quantized activations only.
 hipError_t launch_decode_win(const DecodeLaunch &g, hipStream_t st) {
     if (g.x != nullptr || !g.header) return hipErrorInvalidValue;
     DArgs a{};
@@ -1281,7 +1293,7 @@ hipError_t launch_decode_win(const DecodeLaunch &g, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     void *args[] = {&a};
-    return hipLaunchKernel(fn, dim3((unsigned)a.G), dim3(kThreads), args, lds, st);
+    return hipLaunchKernel(fn, dim3((unsigned)a.G), dim3(kWinThreads), args, lds, st);
 }
 
 hipError_t launch_decode(const DecodeLaunch &g, hipStream_t st) {
