@@ -140,6 +140,7 @@ nvfp4_status enqueue_quantize(const void *x, int xt, int64_t rows, int64_t K_in,
     q.S_out = out.tensor_scale;
     q.partials = partials; q.rscale = rscale;
     q.slots = reinterpret_cast<unsigned long long *>(header) + kSlotsOffset / 8;   // header bytes 512..1023
+    q.grid_slots = reinterpret_cast<unsigned long long *>(header) + kGridSlotsOffset / 8;   // 1024..3071
     q.spin = spin_limit();
     hipError_t e = launch_quantize(q, st);
     return e == hipSuccess ? NVFP4_OK : hip_fail(e);

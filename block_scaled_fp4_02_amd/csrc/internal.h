@@ -25,6 +25,7 @@ struct QuantLaunch {
     float *partials;                        // kAmaxPartials floats
     float *rscale;                          // rows floats (RMSNorm factors)
     unsigned long long *slots;              // 64 arrival slots of the small quantizer (header), or nullptr
+    unsigned long long *grid_slots;         // 256 arrival slots of the grid quantizer (header), or nullptr
     unsigned spin;                          // bound on the arrival wait (polls)
 };
 
@@ -40,14 +41,16 @@ struct ChannelAbsmaxLaunch {
 hipError_t launch_channel_absmax(const ChannelAbsmaxLaunch &c, hipStream_t st);
 
 // Every workspace starts with a header of counters: the small quantizer's 64
-// arrival slots (bytes 512..1023: partial maximum and epoch) and the decode
-// product's split-K tile counters (from byte 4096). It must be zero before the
+// arrival slots (bytes 512..1023: partial maximum and epoch), the grid
+// quantizer's 256 (bytes 1024..3071) and the decode product's split-K tile
+// counters (from byte 4096). It must be zero before the
 // first call on a workspace; calls keep it valid (counts return to zero, all
 // slots advance to the same epoch), so it never needs clearing again.
 constexpr size_t kHeaderBytes = 8192;
 constexpr size_t kTileCntOffset = 4096;         // header bytes before the arrival counters
 constexpr int64_t kMaxCounters = (int64_t)((kHeaderBytes - kTileCntOffset) / sizeof(unsigned));
 constexpr size_t kSlotsOffset = 512;
+constexpr size_t kGridSlotsOffset = 1024;
 
 // Decode-shaped (M <= 64) product in one launch. With x != nullptr (bf16, and
 // decode_can_fuse true) the raw activations are quantized inside the kernel and

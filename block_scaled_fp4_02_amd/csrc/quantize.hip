@@ -11,9 +11,14 @@
 //                thread per block group with it): block absmax, E4M3 block
 //                scale, E2M1 codes, nibble packing, and the residue
 //                R = x - fl(fl(e d) S) of columns below res_cols, quantized
-//                against the same S and stored after column K_in.
+//                against the same S and stored after column K_in;
+//   one launch   decode-sized activations (the small quantizer) and mid-size
+//                ones up to 16 M elements (the grid quantizer) keep X in
+//                registers across one grid-wide arrival for amax(X) instead.
 // All rounding follows the FP32 order of nvfp4.h; contraction into FMA is off
 // so every product and difference rounds exactly once.
+#include <algorithm>
+
 #include "internal.h"
 #include "nvfp4_device.h"
 
@@ -511,6 +516,163 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
     }
 }
 
+// ------------------------------------------- mid-size activations, one launch
+// Activations of up to kGridMaxG * kGridThreads * kGridPer 16-element blocks (16 M
+// elements; bf16, no RMSNorm, reorder
+// or smoothing; the smaller prefill activations) in one launch of G <= kGridMaxG
+// workgroups of kGridThreads threads, at most one per CU, so that all of them are
+// resident: each thread keeps its (up to kGridPer) blocks in registers as loaded,
+// the workgroups' partial maxima meet in a grid-wide arrival on kGridMaxG slots
+// (the small quantizer's epoch scheme, four slots per lane of wave 0), and every
+// block is then encoded from its registers. X is read once, where the two-pass
+// path reads it twice and launches twice. A workgroup whose wait gives up
+// recomputes amax(X) from memory (same result), having written its slots, so
+// the epochs stay in step.
+constexpr int kGridThreads = 1024;
+constexpr int kGridPer = 4;
+constexpr int kGridMaxG = 256;
+static_assert(kGridSlotsOffset + 8 * kGridMaxG <= kTileCntOffset, "grid slots overlap the tile counters");
+
+__device__ inline float block_max_grid(float v, float *sh) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) sh[w] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int i = 1; i < kGridThreads / 64; ++i) r = fmaxf(r, sh[i]);
+    return r;
+}
+
+// Arrival of workgroup blockIdx.x < G <= kGridMaxG with partial m (the same in
+// every thread): lane l of wave 0 owns slots l + 64 j; slot s carries the partial
+// of workgroup s mod G.
+__device__ inline float slot_max_grid(unsigned long long *slot, int G, unsigned ep, float m, unsigned spin,
+                                      float *sh, int *sh_ok) {
+    if (threadIdx.x < 64) {
+        const int l = threadIdx.x;
+        const unsigned long long mine = (unsigned long long)ep << 32 | __float_as_uint(m);
+        unsigned long long sv[kGridMaxG / 64];
+#pragma unroll
+        for (int j = 0; j < kGridMaxG / 64; ++j)
+            if ((l + 64 * j) % G == (int)blockIdx.x) st_dev(&slot[l + 64 * j], mine);
+#pragma unroll
+        for (int j = 0; j < kGridMaxG / 64; ++j) sv[j] = ld_dev(&slot[l + 64 * j]);
+        auto arrived = [&]() {
+            bool in = true;
+#pragma unroll
+            for (int j = 0; j < kGridMaxG / 64; ++j) in = in && (unsigned)(sv[j] >> 32) == ep;
+            return __all(in);
+        };
+        unsigned it = 0;
+        int ok = 1;
+        while (!arrived()) {
+            if (++it > spin) { ok = 0; break; }
+            __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+            for (int j = 0; j < kGridMaxG / 64; ++j) sv[j] = ld_dev(&slot[l + 64 * j]);
+        }
+        float pm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kGridMaxG / 64; ++j) pm = fmaxf(pm, __uint_as_float((unsigned)sv[j]));
+        pm = wave_max(pm);
+        if (l == 0) { *sh_ok = ok; sh[0] = pm; }
+    }
+    __syncthreads();
+    return sh[0];
+}
+
+__global__ __launch_bounds__(kGridThreads) void quantize_grid_kernel(QArgs a, unsigned long long *slot, int G,
+                                                                     unsigned spin) {
+    __shared__ float sh[kGridThreads / 64];
+    __shared__ int sh_ok;
+    const uint32_t KB = (uint32_t)(a.K_in / 16);
+    const int64_t NB = a.rows * (int64_t)KB;
+    const int64_t b0 = (int64_t)blockIdx.x * NB / G, b1 = ((int64_t)blockIdx.x + 1) * NB / G;
+    const bool arrive = !a.static_S && G > 1;
+    unsigned ep = 0;
+    if (arrive && threadIdx.x < 64) ep = (unsigned)(ld_dev(&slot[blockIdx.x]) >> 32) + 1u;   // ahead of the data
+    // block b = b0 + tid + kGridThreads t of this thread: 16 bf16 (two 16-byte words each)
+    uint4 raw[kGridPer][2];
+#pragma unroll
+    for (int t = 0; t < kGridPer; ++t) {
+        const int64_t b = b0 + threadIdx.x + (int64_t)kGridThreads * t;
+        if (b < b1) {
+            const uint32_t row = (uint32_t)(b / KB), blk = (uint32_t)(b - (int64_t)row * KB);
+            const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + row * a.ldx + 16 * (int64_t)blk);
+            raw[t][0] = p[0];
+            raw[t][1] = p[1];
+        } else {
+            raw[t][0] = make_uint4(0, 0, 0, 0);
+            raw[t][1] = make_uint4(0, 0, 0, 0);
+        }
+    }
+    // for finite values the order of |bf16| bit patterns is that of the magnitudes
+    auto to_f32 = [](const uint4 *q, float *v) {
+        const uint32_t w[8] = {q[0].x, q[0].y, q[0].z, q[0].w, q[1].x, q[1].y, q[1].z, q[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = u2f(w[i] << 16);
+            v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+        }
+    };
+    float S;
+    if (a.static_S) {
+        S = *a.static_S;
+    } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kGridPer; ++t) {
+            float v[16];
+            to_f32(raw[t], v);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+        }
+        m = block_max_grid(m, sh);
+        if (arrive) {
+            float mm = slot_max_grid(slot, G, ep, m, spin, sh, &sh_ok);
+            if (!sh_ok) {
+                mm = 0.0f;                           // the wait gave up: all of X here
+                for (int64_t b = threadIdx.x; b < NB; b += kGridThreads) {
+                    const uint32_t row = (uint32_t)(b / KB), blk = (uint32_t)(b - (int64_t)row * KB);
+                    float w[16];
+                    load16<IN_BF16>(a.x, row * a.ldx + 16 * (int64_t)blk, w);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) mm = fmaxf(mm, fabsf(w[i]));
+                }
+            }
+            m = block_max_grid(mm, sh);
+        }
+        S = m > 0.0f ? m / 2688.0f : 1.0f;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.S_out = S;
+    const float t6 = 6.0f * S;
+#pragma unroll
+    for (int t = 0; t < kGridPer; ++t) {
+        const int64_t b = b0 + threadIdx.x + (int64_t)kGridThreads * t;
+        if (b < b1) {
+            const uint32_t row = (uint32_t)(b / KB), blk = (uint32_t)(b - (int64_t)row * KB);
+            float v[16];
+            to_f32(raw[t], v);
+            uint32_t cw[2];
+            float d;
+            const uint32_t db = encode_block(v, S, t6, cw, d);
+            *reinterpret_cast<uint2 *>(a.codes + row * a.ldc + 8 * (int64_t)blk) = make_uint2(cw[0], cw[1]);
+            a.scales[row * a.lds + blk] = (uint8_t)db;
+            if (16 * (int64_t)blk < a.res_cols) {
+                float rv[16];
+                block_residue(v, cw, d, S, rv);
+                uint32_t rc[2];
+                float dr;
+                const uint32_t rdb = encode_block(rv, S, t6, rc, dr);
+                *reinterpret_cast<uint2 *>(a.codes + row * a.ldc + a.K_in / 2 + 8 * (int64_t)blk) = make_uint2(rc[0], rc[1]);
+                a.scales[row * a.lds + KB + blk] = (uint8_t)rdb;
+            }
+        }
+    }
+}
+
 // ------------------------------------------- few rows with RMSNorm / reorder
 // Rows <= 64 with RMSNorm and/or the calibration reorder, in one launch of one
 // workgroup per row: the row, normalized, goes to LDS (the FP64 sum of squares
@@ -714,6 +876,20 @@ int amax_grid(int64_t rows, int64_t K) {
 
 }  // namespace
 
+// CUs of the current device (the grid quantizer launches at most one workgroup per CU).
+static int grid_cus() {
+    static int cus = 0;
+    if (cus <= 0) {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0)
+            cus = c;
+        else
+            return 1;
+    }
+    return cus;
+}
+
 // A row staged in LDS takes K_in floats (up to 64 KiB): above 48 KiB of
 // dynamic LDS the kernel's limit is raised first (gfx950 has 160 KiB per CU).
 static hipError_t allow_lds(const void *fn, size_t lds) {
@@ -761,6 +937,19 @@ hipError_t launch_quantize(const QuantLaunch &q, hipStream_t st) {
         else
             quantize_small_kernel<IN_F32><<<G, kThreads, 0, st>>>(a, q.slots, G, q.spin);
         return hipGetLastError();
+    }
+    if (!norm && !perm && !smooth && q.grid_slots && q.xt == IN_BF16 && nb > 0) {
+        const int cus = grid_cus();
+        const int64_t G = std::min<int64_t>(std::min<int64_t>(kGridMaxG, cus), (nb + kGridThreads - 1) / kGridThreads);
+        if (G >= 1 && nb <= G * kGridThreads * kGridPer) {
+            QArgs a;
+            a.x = q.x; a.rows = q.rows; a.K_in = q.K_in; a.ldx = q.ldx;
+            a.gamma = nullptr; a.perm = nullptr; a.res_cols = q.res_cols; a.static_S = q.static_S;
+            a.codes = q.codes; a.ldc = q.ldc; a.scales = q.scales; a.lds = q.lds; a.S_out = q.S_out;
+            a.partials = q.partials; a.npart = 0; a.rscale = q.rscale; a.eps = q.eps; a.smooth = nullptr;
+            quantize_grid_kernel<<<(int)G, kGridThreads, 0, st>>>(a, q.grid_slots, (int)G, q.spin);
+            return hipGetLastError();
+        }
     }
     int npart = 0;
     if (!q.static_S) {

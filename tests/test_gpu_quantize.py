@@ -177,6 +177,29 @@ def test_small_quantizer_wait_fallback(nv, orc, rows, K, S, monkeypatch):
     assert_qtensor_equal(q1, ox, "fallback")
 
 
+@pytest.mark.parametrize("rows,K,S", [(512, 8192, 0), (130, 4112, 2048), (2048, 8192, 512), (40, 28672, 0)])
+def test_grid_quantizer(nv, orc, rows, K, S, monkeypatch):
+    """The one-launch quantizer of mid-size activations (up to 16 M elements, X held in
+    registers over a grid-wide arrival for amax(X)), at prefill and ragged shapes, with and
+    without residue columns, then with the arrival forced to give up at once (spin limit 0,
+    set from the host): every workgroup recomputes amax(X) itself. Codes must equal the
+    oracle's both times, and a second call (the slots' next epoch) again."""
+    x = inputs.small_random(700 + rows, rows, K)
+    ox = orc.quantize_aug(x, S_cols=S) if S else orc.quantize(x)
+    xd = x.to(DEV)
+    for i in range(2):
+        note(f"grid quantizer rows={rows} K={K} S={S}: call {i}")
+        q0 = nv.quantize(xd, residue_cols=S)
+        torch.cuda.synchronize()
+        assert_qtensor_equal(q0, ox, f"call {i}")
+    monkeypatch.setenv("NVFP4_SPIN_LIMIT", "0")
+    note(f"grid quantizer rows={rows} K={K} S={S}: fallback")
+    q1 = nv.quantize(xd, residue_cols=S)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("NVFP4_SPIN_LIMIT")
+    assert_qtensor_equal(q1, ox, "fallback")
+
+
 @pytest.mark.parametrize("rows,norm,use_perm,S", [(64, True, True, 256), (7, True, True, 0), (1, True, False, 64),
                                                   (33, False, True, 512)])
 def test_rows_quantizer_wait_fallback(nv, orc, rows, norm, use_perm, S, monkeypatch):
