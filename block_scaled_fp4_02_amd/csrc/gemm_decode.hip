@@ -836,7 +836,8 @@ void decode_kernel(DArgs a) {
 // for all four row tiles, so each weight item is loaded and decoded once and each
 // operand fragment read twice per CU (against a wave per weight tile: operand
 // reads / 2, the M = 64 augmented call 35.4 -> 28.3 us with the deeper weight
-// ring; eight waves instead of four one step each: 28.5 -> 28.0 us); the waves'
+// ring; eight waves instead of four one step each: 28.5 -> 28.0 us; eight producer
+// waves instead of four, each two chunks of a unit: 27.7 -> 27.0 us); the waves'
 // partial tiles are added in LDS in step order at the end; producers fill the slot of unit k + 2
 // as soon as the consumers are done with unit k, one workgroup barrier per
 // unit (weight loads run four units ahead, operand loads three). Residue columns (ARCQuant
@@ -853,12 +854,14 @@ void decode_kernel(DArgs a) {
 // Barrier k >= 1: the consumers are done with unit k - 1, and the producers
 // have stored unit k (k >= 2) into the slot unit k - 2 left. Consumers work on
 // unit k between barriers k and k + 1.
-constexpr int kWinChunks = 4;                  // operand chunks per producer thread and unit (64 x 16)
+constexpr int kWinProd = 8;                    // producer waves of the windowed kernel
+constexpr int kWinPThreads = 64 * kWinProd;
+constexpr int kWinChunks = 64 * 16 / kWinPThreads;   // operand chunks per producer thread and unit (64 x 16 in all)
 constexpr int kWinRows = 64;                   // operand rows of a window slot: fixed, so every fragment
                                                // offset is an immediate of the LDS read
 
-// A producer thread's chunks of a unit: rows m_i = ptid / 16 + 16 i (i <
-// kWinChunks), 32-column position p = ptid % 16 in every unit. Their row
+// A producer thread's chunks of a unit: rows m_i = ptid / 16 + (kWinPThreads /
+// 16) i (i < kWinChunks), 32-column position p = ptid % 16 in every unit. Their row
 // addresses and LDS keys are fixed; a unit only adds its byte offsets, so a
 // chunk costs two address adds, its two loads and a few selects. Rows >= M
 // read row 0 and are not stored (key -1); a position past the data (the last,
@@ -882,7 +885,7 @@ __device__ inline WinRows win_rows(const DArgs &a, int ptid) {
     w.p = ptid & 15;
 #pragma unroll
     for (int i = 0; i < kWinChunks; ++i) {
-        const int m = (ptid >> 4) + 16 * i;
+        const int m = (ptid >> 4) + (kWinPThreads / 16) * i;
         const bool ok = m < a.M;
         w.c[i] = a.q_codes + (int64_t)(ok ? m : 0) * a.q_ldc + 16 * w.p;
         w.s[i] = a.q_scales + (int64_t)(ok ? m : 0) * a.q_lds + 2 * w.p;
@@ -911,10 +914,10 @@ __device__ inline void win_unit_load(const DArgs &a, const WinRows &w, int v, in
 }
 
 // Eight consumer waves (two per SIMD, so that one's MFMAs run while the other
-// decodes or waits) and the four producer waves: twelve waves, 170 VGPRs each.
+// decodes or waits) and eight producer waves: sixteen waves, 128 VGPRs each.
 constexpr int kWinCons = 8;
 constexpr int kWinTW = 4 * kCons / kWinCons;   // weight tiles per consumer wave
-constexpr int kWinThreads = 64 * (kWinCons + kProd);
+constexpr int kWinThreads = 64 * (kWinCons + kWinProd);
 
 // A consumer's share of one unit: 32-column step iw of each of its weight tiles.
 struct WStep {
@@ -923,7 +926,7 @@ struct WStep {
 };
 
 template <bool TILED, bool RES>
-__global__ __launch_bounds__(kWinThreads) __attribute__((amdgpu_waves_per_eu(3)))   // 128 KiB of LDS: one per CU
+__global__ __launch_bounds__(kWinThreads) __attribute__((amdgpu_waves_per_eu(4)))   // 128 KiB of LDS: one per CU
 void decode_win_kernel(DArgs a) {
     constexpr int R = kWinRows, SLOT = 64 * kWinRows;
     extern __shared__ half8 lds_a[];           // [2 slots][64 R]: rows >= M are never read
