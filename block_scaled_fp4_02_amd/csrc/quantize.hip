@@ -31,26 +31,44 @@ constexpr int kThreads = 256;
 
 __device__ inline float bf16f(uint32_t h) { return u2f(h << 16); }
 
-// 16 consecutive elements starting at element `off` of a bf16 or f32 array.
+// 16 consecutive elements of a bf16 or f32 array as loaded (32 or 64 bytes).
 template <int XT>
-__device__ inline void load16(const void *base, int64_t off, float *v) {
+struct Raw16 {
+    uint4 q[XT == IN_BF16 ? 2 : 4];
+};
+
+template <int XT>
+__device__ inline void load_raw16(const void *base, int64_t off, Raw16<XT> &r) {
+    const uint4 *p = XT == IN_BF16 ? reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off)
+                                   : reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + off);
+#pragma unroll
+    for (int i = 0; i < (XT == IN_BF16 ? 2 : 4); ++i) r.q[i] = p[i];
+}
+
+template <int XT>
+__device__ inline void raw16_to_f32(const Raw16<XT> &r, float *v) {
     if constexpr (XT == IN_BF16) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
-        uint4 a = p[0], b = p[1];
-        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint32_t w[8] = {r.q[0].x, r.q[0].y, r.q[0].z, r.q[0].w, r.q[1].x, r.q[1].y, r.q[1].z, r.q[1].w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             v[2 * i] = u2f(w[i] << 16);
             v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
         }
     } else {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float4 q = p[i];
-            v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+            v[4 * i] = u2f(r.q[i].x); v[4 * i + 1] = u2f(r.q[i].y);
+            v[4 * i + 2] = u2f(r.q[i].z); v[4 * i + 3] = u2f(r.q[i].w);
         }
     }
+}
+
+// 16 consecutive elements starting at element `off` of a bf16 or f32 array.
+template <int XT>
+__device__ inline void load16(const void *base, int64_t off, float *v) {
+    Raw16<XT> r;
+    load_raw16<XT>(base, off, r);
+    raw16_to_f32<XT>(r, v);
 }
 
 __device__ inline void gamma16(const uint16_t *g, int64_t off, float *v) {
@@ -418,19 +436,29 @@ __device__ inline void st_dev(T *p, T v) { __hip_atomic_store(p, v, __ATOMIC_REL
 template <typename T>
 __device__ inline T ld_dev(const T *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
-// This call's epoch, read by wave 0 at the start of the kernel.
-__device__ inline unsigned slot_epoch(const unsigned long long *slot) {
-    return (unsigned)(ld_dev(&slot[blockIdx.x]) >> 32) + 1u;
+// The epoch half (the high 32 bits) of this workgroup's own slot as the call
+// finds it, read by every thread at the start of the kernel, before the data.
+// Nothing is computed from it until the arrival: arithmetic on a load inside a
+// branch makes the compiler wait for that load there, and so does a 64-bit
+// load whose unused half the register allocator hands out again; either way
+// the data loads would start one memory round trip later.
+__device__ inline unsigned slot_word(const unsigned long long *slot) {
+    return ld_dev(reinterpret_cast<const unsigned *>(&slot[blockIdx.x]) + 1);
 }
 
+// This call's epoch: one past the one the slot carries.
+__device__ inline unsigned slot_epoch(unsigned word) { return word + 1u; }
+
 // Arrival of workgroup blockIdx.x < G <= 64 with partial m (after block_max:
-// the same in every thread). Wave 0 writes the slots and waits; the grid
-// maximum is returned in every thread, and *sh_ok says whether the wait
-// completed (0: it gave up after `spin` polls, the caller recomputes).
-__device__ inline float slot_max(unsigned long long *slot, int G, unsigned ep, float m, unsigned spin,
+// the same in every thread); `word` is slot_word() from the start of the
+// kernel. Wave 0 writes the slots and waits; the grid maximum is returned in
+// every thread, and *sh_ok says whether the wait completed (0: it gave up
+// after `spin` polls, the caller recomputes).
+__device__ inline float slot_max(unsigned long long *slot, int G, unsigned word, float m, unsigned spin,
                                  float *sh, int *sh_ok) {
     if (threadIdx.x < 64) {                    // wave 0: lane l owns slot l
         const int l = threadIdx.x;
+        const unsigned ep = slot_epoch(word);
         if (l % G == (int)blockIdx.x) st_dev(&slot[l], (unsigned long long)ep << 32 | __float_as_uint(m));
         unsigned long long sv = ld_dev(&slot[l]);
         unsigned it = 0;
@@ -452,23 +480,32 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
                                                                    unsigned spin) {
     __shared__ float sh[kThreads / 64];
     __shared__ int sh_ok;
-    const int64_t KB = a.K_in / 16, NB = a.rows * KB;
-    const int64_t b0 = (int64_t)blockIdx.x * NB / G, b1 = ((int64_t)blockIdx.x + 1) * NB / G;
-    // this call's epoch, read ahead of the data (its latency overlaps theirs)
+    // NB <= kSmallMaxG * kThreads * kSmallPer blocks: block indices fit 32 bits
+    const uint32_t KB = (uint32_t)(a.K_in / 16), NB = (uint32_t)a.rows * KB;
+    const uint32_t b0 = blockIdx.x * NB / G, b1 = (blockIdx.x + 1) * NB / G;
     const bool arrive = !a.static_S && G > 1;
-    unsigned ep = 0;
-    if (arrive && threadIdx.x < 64) ep = slot_epoch(slot);
+    const unsigned word = slot_word(slot);   // in flight beside the data loads
+    // every block's load is issued before any is used (one memory round trip);
+    // the raw words are converted after the branches, which then hold no use of them
+    Raw16<XT> raw[kSmallPer];
+#pragma unroll
+    for (int t = 0; t < kSmallPer; ++t) {
+        const uint32_t b = b0 + threadIdx.x + kThreads * t;
+        if (b < b1) {
+            const uint32_t row = b / KB, blk = b - row * KB;
+            load_raw16<XT>(a.x, row * a.ldx + 16 * (int64_t)blk, raw[t]);
+        } else {
+#pragma unroll
+            for (auto &q : raw[t].q) q = make_uint4(0, 0, 0, 0);
+        }
+    }
     float v[kSmallPer][16];
     float m = 0.0f;
 #pragma unroll
     for (int t = 0; t < kSmallPer; ++t) {
-        const int64_t b = b0 + threadIdx.x + (int64_t)kThreads * t;
-        if (b < b1) {
-            const int64_t row = b / KB, blk = b - row * KB;
-            load16<XT>(a.x, row * a.ldx + 16 * blk, v[t]);
+        raw16_to_f32<XT>(raw[t], v[t]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[t][i]));
-        }
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[t][i]));
     }
     float S;
     if (a.static_S) {
@@ -476,18 +513,18 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
     } else {
         m = block_max(m, sh);
         if (arrive) {
-            float mm = slot_max(slot, G, ep, m, spin, sh, &sh_ok);
+            m = slot_max(slot, G, word, m, spin, sh, &sh_ok);   // the same in every thread
             if (!sh_ok) {
-                mm = 0.0f;                           // the wait gave up: all of X here
-                for (int64_t b = threadIdx.x; b < NB; b += kThreads) {
-                    const int64_t row = b / KB, blk = b - row * KB;
+                float mm = 0.0f;                     // the wait gave up: all of X here
+                for (uint32_t b = threadIdx.x; b < NB; b += kThreads) {
+                    const uint32_t row = b / KB, blk = b - row * KB;
                     float w[16];
-                    load16<XT>(a.x, row * a.ldx + 16 * blk, w);
+                    load16<XT>(a.x, row * a.ldx + 16 * (int64_t)blk, w);
 #pragma unroll
                     for (int i = 0; i < 16; ++i) mm = fmaxf(mm, fabsf(w[i]));
                 }
+                m = block_max(mm, sh);
             }
-            m = block_max(mm, sh);
         }
         S = m > 0.0f ? m / 2688.0f : 1.0f;
     }
@@ -495,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void quantize_small_kernel(QArgs a, unsig
     const float t6 = 6.0f * S;
 #pragma unroll
     for (int t = 0; t < kSmallPer; ++t) {
-        const int64_t b = b0 + threadIdx.x + (int64_t)kThreads * t;
+        const uint32_t b = b0 + threadIdx.x + kThreads * t;
         if (b < b1) {
             const int64_t row = b / KB, blk = b - row * KB;
             uint32_t cw[2];
@@ -548,10 +585,11 @@ __device__ inline float block_max_grid(float v, float *sh) {
 // Arrival of workgroup blockIdx.x < G <= kGridMaxG with partial m (the same in
 // every thread): lane l of wave 0 owns slots l + 64 j; slot s carries the partial
 // of workgroup s mod G.
-__device__ inline float slot_max_grid(unsigned long long *slot, int G, unsigned ep, float m, unsigned spin,
-                                      float *sh, int *sh_ok) {
+__device__ inline float slot_max_grid(unsigned long long *slot, int G, unsigned word, float m,
+                                      unsigned spin, float *sh, int *sh_ok) {
     if (threadIdx.x < 64) {
         const int l = threadIdx.x;
+        const unsigned ep = slot_epoch(word);
         const unsigned long long mine = (unsigned long long)ep << 32 | __float_as_uint(m);
         unsigned long long sv[kGridMaxG / 64];
 #pragma unroll
@@ -591,8 +629,7 @@ __global__ __launch_bounds__(kGridThreads) void quantize_grid_kernel(QArgs a, un
     const int64_t NB = a.rows * (int64_t)KB;
     const int64_t b0 = (int64_t)blockIdx.x * NB / G, b1 = ((int64_t)blockIdx.x + 1) * NB / G;
     const bool arrive = !a.static_S && G > 1;
-    unsigned ep = 0;
-    if (arrive && threadIdx.x < 64) ep = (unsigned)(ld_dev(&slot[blockIdx.x]) >> 32) + 1u;   // ahead of the data
+    const unsigned word = slot_word(slot);   // in flight beside the data loads
     // block b = b0 + tid + kGridThreads t of this thread: 16 bf16 (two 16-byte words each)
     uint4 raw[kGridPer][2];
 #pragma unroll
@@ -631,9 +668,9 @@ __global__ __launch_bounds__(kGridThreads) void quantize_grid_kernel(QArgs a, un
         }
         m = block_max_grid(m, sh);
         if (arrive) {
-            float mm = slot_max_grid(slot, G, ep, m, spin, sh, &sh_ok);
+            m = slot_max_grid(slot, G, word, m, spin, sh, &sh_ok);   // the same in every thread
             if (!sh_ok) {
-                mm = 0.0f;                           // the wait gave up: all of X here
+                float mm = 0.0f;                     // the wait gave up: all of X here
                 for (int64_t b = threadIdx.x; b < NB; b += kGridThreads) {
                     const uint32_t row = (uint32_t)(b / KB), blk = (uint32_t)(b - (int64_t)row * KB);
                     float w[16];
@@ -641,8 +678,8 @@ __global__ __launch_bounds__(kGridThreads) void quantize_grid_kernel(QArgs a, un
 #pragma unroll
                     for (int i = 0; i < 16; ++i) mm = fmaxf(mm, fabsf(w[i]));
                 }
+                m = block_max_grid(mm, sh);
             }
-            m = block_max_grid(mm, sh);
         }
         S = m > 0.0f ? m / 2688.0f : 1.0f;
     }
@@ -691,8 +728,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QArgs a, unsign
     const int G = (int)gridDim.x;
     const int64_t row = blockIdx.x, K = a.K_in, KB = K / 16;
     const bool arrive = !a.static_S && G > 1;
-    unsigned ep = 0;
-    if (arrive && threadIdx.x < 64) ep = slot_epoch(slot);
+    const unsigned word = slot_word(slot);   // in flight beside the data loads
     double ss = 0.0;
     float m = 0.0f;
     for (int64_t b = threadIdx.x; b < KB; b += kThreads) {
@@ -735,7 +771,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QArgs a, unsign
         S = *a.static_S;
     } else {
         if (arrive) {
-            float mm = slot_max(slot, G, ep, m, spin, sh, &sh_ok);
+            float mm = slot_max(slot, G, word, m, spin, sh, &sh_ok);
             if (!sh_ok) {                      // the wait gave up: every row here
                 mm = 0.0f;
                 for (int64_t rr = 0; rr < a.rows; ++rr) {
