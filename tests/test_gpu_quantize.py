@@ -158,12 +158,17 @@ def test_deterministic(nv):
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales) and torch.equal(a.scale, b.scale)
 
 
-@pytest.mark.parametrize("rows,K,S", [(16, 14336, 0), (7, 4112, 2048), (32, 8192, 8192)])
-def test_small_quantizer_wait_fallback(nv, orc, rows, K, S, monkeypatch):
+@pytest.mark.parametrize("rows,K,S,dt", [(16, 14336, 0, "bf16"), (7, 4112, 2048, "bf16"), (32, 8192, 8192, "bf16"),
+                                        # 32768 and 21504 blocks on 64 workgroups: two blocks per thread
+                                        # (all threads, then the first 80 of each workgroup)
+                                        (32, 16384, 0, "bf16"), (24, 14336, 4096, "bf16"), (24, 14336, 4096, "f32")])
+def test_small_quantizer_wait_fallback(nv, orc, rows, K, S, dt, monkeypatch):
     """The one-launch quantizer of decode-sized activations, with its grid-wide
     arrival forced to give up at once (spin limit 0, set from the host): every
     workgroup then recomputes amax(X) itself. Codes must equal the oracle's."""
     x = inputs.small_random(300 + rows, rows, K)
+    if dt == "f32":
+        x = x.float()
     ox = orc.quantize_aug(x, S_cols=S) if S else orc.quantize(x)
     note(f"small quantizer rows={rows} K={K} S={S}: normal")
     q0 = nv.quantize(x.to(DEV), residue_cols=S)
